@@ -1,0 +1,107 @@
+"""Seeded workload generator: shapes, ranges, determinism (CPU)."""
+import numpy as np
+import pytest
+
+from non_cartesian_mri_fhd_amd import inputs
+
+
+@pytest.mark.parametrize("name", ["random16", "spiral32", "radial64"])
+def test_shapes_and_dtypes(name):
+    w = inputs.make_workload(name)
+    spec = inputs.WORKLOADS[name]
+    for a in ("kx", "ky", "kz", "Dr", "Di"):
+        assert w[a].shape == (spec.M,) and w[a].dtype == np.float32 and w[a].flags.c_contiguous
+    for a in ("x", "y", "z"):
+        assert w[a].shape == (spec.N,) and w[a].dtype == np.float32
+    assert np.all(np.isfinite(np.concatenate([w[a] for a in ("kx", "ky", "kz", "Dr", "Di")])))
+
+
+def test_large_workload_shapes():
+    for name, M in (("spiral128", 100_000), ("vdrandom256", 100_000)):
+        k = inputs.make_kspace(name)
+        assert k["kx"].shape == (M,)
+    assert inputs.WORKLOADS["spiral128"].terms == 128 ** 3 * 100_000
+
+
+def test_deterministic():
+    a, b = inputs.make_kspace("spiral32"), inputs.make_kspace("spiral32")
+    for key in a:
+        assert np.array_equal(a[key], b[key])
+
+
+def test_grid_coords_exact_and_ordered():
+    L = 16
+    x, y, z = inputs.grid_coords(L)
+    ax = (np.arange(L) - L // 2) / L
+    assert np.array_equal(x.astype(np.float64)[:L], ax)          # x fastest
+    assert np.array_equal(y.astype(np.float64)[::L][:L], ax)
+    assert np.array_equal(z.astype(np.float64)[::L * L], ax)
+    assert x.min() == -0.5 and x.max() < 0.5
+    n = np.array([0, 1, L, L * L, L ** 3 - 1])
+    ix, iy, iz = inputs.grid_index(n, L)
+    assert np.array_equal(x[n], ax[ix].astype(np.float32))
+    assert np.array_equal(y[n], ax[iy].astype(np.float32))
+    assert np.array_equal(z[n], ax[iz].astype(np.float32))
+
+
+def test_random16_ranges():
+    k = inputs.make_kspace("random16")
+    for a in ("kx", "ky", "kz"):
+        assert k[a].min() >= -8 and k[a].max() < 8
+    d = np.concatenate([k["Dr"], k["Di"]])
+    assert abs(d.mean()) < 0.1 and abs(d.std() - 1) < 0.05
+
+
+def test_spiral32_structure():
+    k = inputs.make_kspace("spiral32")
+    kz = k["kz"].reshape(16, 4, 256)
+    assert np.array_equal(np.unique(k["kz"]), np.arange(-16, 16, 2, dtype=np.float32))
+    assert np.all(kz == kz[:, :1, :1])
+    r = np.hypot(k["kx"], k["ky"]).reshape(16, 4, 256)
+    assert np.allclose(r, 16 * np.arange(256) / 256, atol=1e-5)
+    # interleave j starts at angle 2 pi j/4 (t = 0 has r = 0; check s = 1)
+    th = np.arctan2(k["ky"], k["kx"]).reshape(16, 4, 256)[0, :, 1]
+    expect = 2 * np.pi * (8 / 256 + np.arange(4) / 4)
+    assert np.allclose(np.angle(np.exp(1j * (th - expect))), 0, atol=1e-5)
+
+
+def test_spiral128_structure():
+    k = inputs.make_kspace("spiral128")
+    planes = np.unique(k["kz"])
+    assert planes.size == 25
+    assert np.allclose(planes, -64 + 5.12 * np.arange(25), atol=1e-5)
+    r = np.hypot(k["kx"], k["ky"]).reshape(25, 8, 500)
+    assert np.allclose(r, 64 * np.arange(500) / 500, atol=1e-4)
+
+
+def test_radial64_structure():
+    k = inputs.make_kspace("radial64")
+    K = np.stack([k["kx"], k["ky"], k["kz"]], 1).astype(np.float64).reshape(256, 256, 3)
+    r = np.linalg.norm(K, axis=2)
+    assert np.allclose(r, np.abs(-32 + 0.25 * np.arange(256))[None, :], atol=1e-4)
+    d = inputs.fibonacci_directions(256)
+    assert np.allclose(np.linalg.norm(d, axis=1), 1)
+    # D is the FT of positive blobs: largest magnitude at k = 0 (s = 128)
+    mag = np.hypot(k["Dr"], k["Di"]).reshape(256, 256)
+    assert np.all(mag.argmax(axis=1) == 128)
+
+
+def test_vdrandom256_density():
+    k = inputs.make_kspace("vdrandom256")
+    for a in ("kx", "ky", "kz"):
+        assert k[a].min() >= -128 and k[a].max() <= 128
+    # k = 128 u|u|: P(|k| < 32) = P(|u| < 1/2) = 1/2
+    frac = np.mean(np.abs(k["kx"]) < 32)
+    assert abs(frac - 0.5) < 0.01
+
+
+def test_voxel_subset():
+    s = inputs.voxel_subset(256 ** 3)
+    assert s.size == 4096 and np.all(np.diff(s) > 0)
+    assert np.array_equal(s, inputs.voxel_subset(256 ** 3))
+
+
+def test_cartesian_case():
+    c = inputs.cartesian_case(4, seed=0)
+    assert c["M"] == c["N"] == 64
+    assert set(np.unique(c["kx"]).tolist()) == {-2.0, -1.0, 0.0, 1.0}
