@@ -1,0 +1,187 @@
+"""Benchmark of the F^H D hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: the
+loop-fission pre-pass (fhd_pack) and the gather kernel (fhd_gather) through
+the C ABI, on the 128^3-voxel x 100,000-sample stack-of-spirals workload by
+default, with every input already resident in device memory.
+
+Prints one JSON line (rank 0, N = 1) with the throughput in voxel-sample
+terms per second, the gather kernel's ALU roofline figures (per-launch HIP
+event timing on the launch stream), the sampled parity against the fp64
+oracle and the oracle's own CPU throughput on that sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "F^H D voxel-sample terms/s at 128^3 x 100k; % of FP32 VALU/trans roofline"
+
+# gfx950 ALU ceiling of the gather kernel, from unit counts and clock:
+# 256 CUs x 4 SIMDs at 2.4 GHz. FP32 vector peak 157.3 TFLOP/s (AMD's
+# figure). v_sin_f32 / v_cos_f32 issue one wave64 instruction per 8 SIMD
+# cycles, i.e. 8 lanes per cycle per SIMD (measured by the issue-rate
+# micro-benchmarks; a quarter of the FP32 FMA rate), so the
+# transcendental peak is 256 * 4 * 8 * 2.4e9 = 1.97e13 /s. With 13 FLOP
+# and 2 transcendentals per voxel-sample term the roofline is
+# R = min(P_fp32 / 13, P_trans / 2) terms/s.
+CUS, SIMDS_PER_CU, TRANS_LANES_PER_CYCLE, CLOCK_HZ = 256, 4, 8, 2.4e9
+P_FP32 = 157.3e12
+P_TRANS = CUS * SIMDS_PER_CU * TRANS_LANES_PER_CYCLE * CLOCK_HZ
+FLOP_PER_TERM = 13
+ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / 2)
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="spiral128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args(argv)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w: dict, name: str, target_s: float, rho_r, rho_i) -> tuple[dict, dict]:
+    """Time the fp64 oracle on a seeded voxel sample of the full workload
+    and compare the GPU result on the same voxels."""
+    import oracle
+    from non_cartesian_mri_fhd_amd import inputs, metrics
+    threads = oracle.default_threads()
+    N, M = w["N"], w["M"]
+    probe = inputs.voxel_subset(N, 64, seed=4242)
+    t0 = time.perf_counter()
+    oracle.fhd_subset(w, probe, threads=threads)
+    rate = probe.size * M / (time.perf_counter() - t0)
+    count = int(np.clip(target_s * rate / M, 256, min(N, 262144)))
+    idx = inputs.voxel_subset(N, count, seed=inputs.WORKLOADS[name].seed + 2000
+                              if name in inputs.WORKLOADS else 2000)
+    t0 = time.perf_counter()
+    ref_r, ref_i = oracle.fhd_subset(w, idx, threads=threads)
+    dt = time.perf_counter() - t0
+    g_r, g_i = rho_r[idx], rho_i[idx]
+    parity = dict(voxels=int(idx.size), rel_l2=metrics.rel_l2(g_r, g_i, ref_r, ref_i),
+                  psnr_db=metrics.psnr_db(g_r, g_i, ref_r, ref_i), tolerance=5e-4)
+    base = dict(value=idx.size * M / dt, unit="terms/s", cores=threads, kind="oracle",
+                sample="%d seeded voxels x all %d samples of %s (%.1f s, fp64, %s)"
+                       % (idx.size, M, name, dt, cpu_model()))
+    return base, parity
+
+
+def main(argv=None) -> int:
+    args = parse(argv)
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: the F^H D path shards over voxels "
+              "with no exchange, and this build measures one GPU's share only "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from non_cartesian_mri_fhd_amd import binding, build, inputs
+
+    build.ensure_built()
+    binding.load()
+    assert torch.cuda.is_available(), "no GPU visible"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = inputs.make_workload(args.workload)
+    N, M = w["N"], w["M"]
+    t = {k: torch.from_numpy(w[k]).to(dev) for k in ("kx", "ky", "kz", "Dr", "Di", "x", "y", "z")}
+    packed = binding.new_packed(M, dev)
+    rho_r = torch.empty(N, dtype=torch.float32, device=dev)
+    rho_i = torch.empty(N, dtype=torch.float32, device=dev)
+
+    def step():
+        binding.fhd_pack(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], packed)
+        binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], rho_r, rho_i)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        binding.fhd_pack(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], packed)
+        e[1].record(stream)
+        binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], rho_r, rho_i)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    gather_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    terms = float(N) * float(M)
+    value = terms / (ms_step * 1e-3)
+
+    achieved = FLOP_PER_TERM * terms / (gather_ms * 1e-3) / 1e12
+    peak = FLOP_PER_TERM * ROOF_TERMS / 1e12
+    cfg = binding.gather_config()
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "terms/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: F^H D over %d^3 voxels x %d samples (%s)"
+                        % (args.workload, w["L"], M, inputs.WORKLOADS[args.workload].trajectory),
+            "N": N, "M": M, "terms": terms, **cfg,
+        },
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+        },
+        "kernel_ms": {"fhd_gather_kernel": gather_ms, "fhd_pack_kernel": pack_ms},
+        "gflops_13_per_term": FLOP_PER_TERM * value / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline(w, args.workload, args.cpu_seconds,
+                                    rho_r.cpu().numpy(), rho_i.cpu().numpy())
+        out["cpu_baseline"] = base
+        out["parity"] = parity
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,121 @@
+/*
+ * fhd.h -- C ABI of the MI355X (gfx950) F^H D library, libfhd.so.
+ *
+ * F^H D is the adjoint non-uniform discrete Fourier transform at the heart
+ * of iterative non-Cartesian MRI reconstruction (page "Case study --
+ * iterative MRI reconstruction", section 17.3, the F^H D equation):
+ *
+ *     rho_n = sum_{m < M} D_m * exp(+i * 2*pi * (kx_m*x_n + ky_m*y_n + kz_m*z_n))
+ *
+ * for every voxel n < N. k is in cycles per field of view and (x, y, z) in
+ * field-of-view units. D_m = Dr[m] + i*Di[m] and rho_n = rho_r[n] +
+ * i*rho_i[n]. There is no weighting and no normalisation. The argument
+ * names and order follow the gather kernel on that page (section 17.3.1),
+ * with a HIP stream added.
+ *
+ * Conventions shared by every entry point:
+ *   - All arrays are fp32 (or the packed buffer, see fhd_pack), contiguous,
+ *     4-byte aligned, in device memory of the current HIP device (or in
+ *     pinned host memory the device can access). They are owned by the
+ *     caller; the library never frees or retains them.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *     stream) and the call returns without synchronising. Calls on one
+ *     stream run in order.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Return value: FHD_OK (0) or a negative FHD_ERR_* status. Argument
+ *     checks that need no device (null pointers, negative sizes, overlaps,
+ *     alignment) run before any HIP call; then pointers are checked to be
+ *     device-accessible, on the current device and large enough for the
+ *     stated sizes. fhd_last_error() gives a message for the calling
+ *     thread's last failure.
+ */
+#ifndef FHD_H
+#define FHD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FHD_OK 0
+#define FHD_ERR_INVALID_ARG (-1) /* bad pointer, size, alignment or overlap */
+#define FHD_ERR_HIP (-2)         /* a HIP runtime or launch error */
+#define FHD_ERR_ALLOC (-3)       /* the library could not get its workspace */
+
+/*
+ * rho = F^H D over N voxels and M samples (section 17.3, F^H D equation).
+ * Runs the loop-fission pre-pass (fhd_pack, section 17.3.2) into a
+ * stream-ordered workspace of fhd_packed_bytes(M) bytes that the library
+ * allocates and frees on `stream`, then the gather kernel (fhd_gather,
+ * one lane per voxel with no atomics, section 17.3.1).
+ *   kx, ky, kz, Dr, Di : M fp32 values each (read only)
+ *   x, y, z            : N fp32 values each (read only)
+ *   rho_r, rho_i       : N fp32 values each (written); they must not
+ *                        overlap each other or any input
+ *   M >= 0, N >= 0     : M = 0 writes zeros (an empty sum); N = 0 does
+ *                        nothing. Pointers may be NULL only when the
+ *                        matching size is 0.
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
+ */
+int fhd_compute(const float *kx, const float *ky, const float *kz,
+                const float *Dr, const float *Di,
+                const float *x, const float *y, const float *z,
+                float *rho_r, float *rho_i, int M, int N, void *stream);
+
+/*
+ * Size in bytes of the packed k-space that fhd_pack writes for M samples,
+ * or -1 if M < 0. M is padded up to a whole chunk of samples.
+ */
+int64_t fhd_packed_bytes(int M);
+
+/*
+ * Loop-fission pre-pass (section 17.3.2: move per-sample work out of the
+ * voxel loop; section 17.3.4: keep a sample's values together). Packs the
+ * SoA k-space into `packed`, chunk-interleaved records of (kx, ky, kz,
+ * arg(D) in revolutions, |D|), zero-padded to a whole chunk. The padding
+ * records have |D| = 0 and add exactly nothing.
+ *   kx..Di       : M fp32 values each (read only)
+ *   packed       : device buffer of at least packed_bytes bytes (written),
+ *                  16-byte aligned, packed_bytes >= fhd_packed_bytes(M); it
+ *                  must not overlap any input
+ * M = 0 does nothing. Errors: FHD_ERR_INVALID_ARG, FHD_ERR_HIP.
+ */
+int fhd_pack(const float *kx, const float *ky, const float *kz,
+             const float *Dr, const float *Di, int M,
+             void *packed, int64_t packed_bytes, void *stream);
+
+/*
+ * Gather kernel over packed k-space (section 17.3.1, gather form; 17.3.3,
+ * accumulators in registers; 17.3.4, every lane reads the same sample at
+ * once; 17.3.5, hardware sin/cos). rho = F^H D for the M samples that
+ * fhd_pack wrote into `packed` (same M).
+ *   packed       : fhd_packed_bytes(M) bytes written by fhd_pack (read only),
+ *                  16-byte aligned
+ *   x, y, z      : N fp32 values each (read only)
+ *   rho_r, rho_i : N fp32 values each (written), not overlapping any input
+ * M = 0 writes zeros; N = 0 does nothing. The per-voxel summation order is
+ * fixed, so repeated calls give bitwise identical results.
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_HIP.
+ */
+int fhd_gather(const void *packed, int M,
+               const float *x, const float *y, const float *z,
+               float *rho_r, float *rho_i, int N, void *stream);
+
+/*
+ * Launch shape of the gather kernel: voxels per lane, samples per packed
+ * chunk and workgroup size (threads). Any pointer may be NULL.
+ */
+void fhd_gather_config(int *voxels_per_lane, int *samples_per_chunk, int *block_threads);
+
+/* Static description of a status code. Never NULL. */
+const char *fhd_status_string(int status);
+
+/* Message for the calling thread's most recent failure ("" if none). */
+const char *fhd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FHD_H */

@@ -1,0 +1,167 @@
+"""Python binding of libfhd.so (the C ABI in include/fhd.h).
+
+Argument marshalling only: every step of F^H D runs in the library's HIP
+kernels. torch supplies device memory and the current stream. There is no
+CPU fallback: if the library is missing or a tensor is not on the GPU, the
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from .build import lib_path
+
+FHD_OK = 0
+FHD_ERR_INVALID_ARG = -1
+FHD_ERR_HIP = -2
+FHD_ERR_ALLOC = -3
+
+LIBRARY = lib_path("libfhd.so")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FhdError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__("%s failed: status %d (%s)" % (where, status, message))
+        self.status = status
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libfhd.so; raises FileNotFoundError if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None or path is not None:
+            p = path or LIBRARY
+            if not os.path.exists(p):
+                raise FileNotFoundError(
+                    "%s is not built; run __graft_entry__.build() or "
+                    "python -m non_cartesian_mri_fhd_amd.build" % p)
+            lib = ctypes.CDLL(p)
+            _declare(lib)
+            if path is not None:
+                return lib
+            _lib = lib
+        return _lib
+
+
+def _declare(lib: ctypes.CDLL) -> None:
+    fp, vp, i32, i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.fhd_compute.argtypes = [fp] * 10 + [i32, i32, vp]
+    lib.fhd_compute.restype = i32
+    lib.fhd_packed_bytes.argtypes = [i32]
+    lib.fhd_packed_bytes.restype = i64
+    lib.fhd_pack.argtypes = [fp] * 5 + [i32, vp, i64, vp]
+    lib.fhd_pack.restype = i32
+    lib.fhd_gather.argtypes = [vp, i32] + [fp] * 5 + [i32, vp]
+    lib.fhd_gather.restype = i32
+    lib.fhd_gather_config.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
+    lib.fhd_gather_config.restype = None
+    lib.fhd_status_string.argtypes = [i32]
+    lib.fhd_status_string.restype = ctypes.c_char_p
+    lib.fhd_last_error.argtypes = []
+    lib.fhd_last_error.restype = ctypes.c_char_p
+
+
+def _check(lib, status: int, where: str) -> None:
+    if status != FHD_OK:
+        msg = lib.fhd_last_error().decode() or lib.fhd_status_string(status).decode()
+        raise FhdError(status, where, msg)
+
+
+def _vec(t: torch.Tensor, name: str, n: int, device) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU, got %s" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if not t.is_contiguous() or t.dim() != 1 or t.numel() != n:
+        raise ValueError("%s must be a contiguous 1-D tensor of %d elements" % (name, n))
+    return t.data_ptr() if n > 0 else 0
+
+
+def _stream(device, stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def gather_config() -> dict:
+    lib = load()
+    v, u, b = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lib.fhd_gather_config(ctypes.byref(v), ctypes.byref(u), ctypes.byref(b))
+    return dict(voxels_per_lane=v.value, samples_per_chunk=u.value, block_threads=b.value)
+
+
+def fhd_packed_bytes(M: int) -> int:
+    n = load().fhd_packed_bytes(int(M))
+    if n < 0:
+        raise ValueError("M must be >= 0")
+    return int(n)
+
+
+def fhd_compute(kx, ky, kz, Dr, Di, x, y, z, rho_r=None, rho_i=None, stream=None):
+    """rho = F^H D; returns (rho_r, rho_i), float32 tensors on x's device."""
+    lib = load()
+    M, N = kx.numel(), x.numel()
+    dev = x.device
+    if rho_r is None:
+        rho_r = torch.empty(N, dtype=torch.float32, device=dev)
+    if rho_i is None:
+        rho_i = torch.empty(N, dtype=torch.float32, device=dev)
+    ptrs = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"),
+                                               (Dr, "Dr"), (Di, "Di"))]
+    ptrs += [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"),
+                                               (rho_r, "rho_r"), (rho_i, "rho_i"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_compute(*ptrs, M, N, _stream(dev, stream)), "fhd_compute")
+    return rho_r, rho_i
+
+
+def fhd_pack(kx, ky, kz, Dr, Di, packed: torch.Tensor, stream=None) -> torch.Tensor:
+    """Pre-pass into ``packed`` (a uint8 or float32 device tensor)."""
+    lib = load()
+    M = kx.numel()
+    dev = packed.device
+    ptrs = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"),
+                                               (Dr, "Dr"), (Di, "Di"))]
+    if packed.device.type != "cuda" or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous GPU tensor")
+    nbytes = packed.numel() * packed.element_size()
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_pack(*ptrs, M, packed.data_ptr(), nbytes, _stream(dev, stream)),
+               "fhd_pack")
+    return packed
+
+
+def fhd_gather(packed: torch.Tensor, M: int, x, y, z, rho_r=None, rho_i=None, stream=None):
+    """Gather over a packed k-space of M samples; returns (rho_r, rho_i)."""
+    lib = load()
+    N = x.numel()
+    dev = x.device
+    if rho_r is None:
+        rho_r = torch.empty(N, dtype=torch.float32, device=dev)
+    if rho_i is None:
+        rho_i = torch.empty(N, dtype=torch.float32, device=dev)
+    if packed.device != dev or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous tensor on %s" % dev)
+    if packed.numel() * packed.element_size() < (fhd_packed_bytes(M) if M > 0 else 0):
+        raise ValueError("packed is smaller than fhd_packed_bytes(M)")
+    ptrs = [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"),
+                                               (rho_r, "rho_r"), (rho_i, "rho_i"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_gather(packed.data_ptr(), int(M), *ptrs, N, _stream(dev, stream)),
+               "fhd_gather")
+    return rho_r, rho_i
+
+
+def new_packed(M: int, device) -> torch.Tensor:
+    """Device buffer of fhd_packed_bytes(M) bytes for fhd_pack / fhd_gather."""
+    return torch.empty(max(fhd_packed_bytes(M), 4), dtype=torch.uint8, device=device)

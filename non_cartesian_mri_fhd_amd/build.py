@@ -1,0 +1,66 @@
+"""Compile the HIP sources of this package into in-tree shared libraries.
+
+``python -m non_cartesian_mri_fhd_amd.build`` (or ``build_all()``) runs hipcc
+for gfx950 on every source below. It needs no GPU: hipcc cross-compiles.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+CSRC = os.path.join(PKG, "csrc")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+# -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
+HIP_FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Wall", "-Wno-unused-result",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + INCLUDE,
+]
+
+# library name -> source files
+LIBRARIES = {
+    "libfhd.so": ["fhd.hip"],
+    "libfhd_microbench.so": ["microbench.hip"],
+}
+
+
+def lib_path(name: str) -> str:
+    return os.path.join(PKG, name)
+
+
+def build_library(name: str, verbose: bool = False) -> str:
+    out = lib_path(name)
+    srcs = [os.path.join(CSRC, s) for s in LIBRARIES[name]]
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *HIP_FLAGS, "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (name, res.stdout, res.stderr))
+    os.replace(tmp, out)
+    return out
+
+
+def build_all(verbose: bool = False) -> list[str]:
+    return [build_library(n, verbose) for n in LIBRARIES]
+
+
+def ensure_built() -> None:
+    """Build only the libraries that are missing (never rebuilds)."""
+    for n in LIBRARIES:
+        if not os.path.exists(lib_path(n)):
+            build_library(n)
+
+
+if __name__ == "__main__":
+    for p in build_all(verbose="-v" in sys.argv):
+        print(p)

@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: exports, sizes and argument checks.
+
+Every case here fails (or returns) before the library makes any HIP call,
+so it runs on a host with no device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from non_cartesian_mri_fhd_amd import build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fhd.h")
+
+FHD_OK, FHD_ERR_INVALID_ARG = 0, -1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    build.ensure_built()
+    lib = ctypes.CDLL(build.lib_path("libfhd.so"))
+    vp = ctypes.c_void_p
+    lib.fhd_compute.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
+    lib.fhd_pack.argtypes = [vp] * 5 + [ctypes.c_int, vp, ctypes.c_int64, vp]
+    lib.fhd_gather.argtypes = [vp, ctypes.c_int] + [vp] * 5 + [ctypes.c_int, vp]
+    lib.fhd_packed_bytes.argtypes = [ctypes.c_int]
+    lib.fhd_packed_bytes.restype = ctypes.c_int64
+    lib.fhd_last_error.restype = ctypes.c_char_p
+    lib.fhd_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fhd_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fhd_compute", "fhd_pack", "fhd_gather", "fhd_packed_bytes",
+              "fhd_status_string", "fhd_last_error", "fhd_gather_config"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_microbench_library_loads():
+    build.ensure_built()
+    mb = ctypes.CDLL(build.lib_path("libfhd_microbench.so"))
+    assert mb.fhdmb_mix_count() >= 8
+
+
+def test_packed_bytes(lib):
+    assert lib.fhd_packed_bytes(-1) == -1
+    assert lib.fhd_packed_bytes(0) == 0
+    # chunks of 8 samples x 5 fp32 fields
+    assert lib.fhd_packed_bytes(1) == 8 * 5 * 4
+    assert lib.fhd_packed_bytes(8) == 8 * 5 * 4
+    assert lib.fhd_packed_bytes(9) == 2 * 8 * 5 * 4
+    assert lib.fhd_packed_bytes(100_000) == 100_000 * 20
+    assert lib.fhd_packed_bytes(2 ** 31 - 1) == ((2 ** 31 - 1 + 7) // 8) * 160
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, 7):
+        assert lib.fhd_status_string(s)
+    assert b"INVALID" in lib.fhd_status_string(-1)
+
+
+def _last(lib):
+    return lib.fhd_last_error().decode()
+
+
+def test_negative_sizes_rejected(lib):
+    assert lib.fhd_compute(*[None] * 10, -1, 4, None) == FHD_ERR_INVALID_ARG
+    assert "M < 0" in _last(lib)
+    assert lib.fhd_compute(*[None] * 10, 4, -1, None) == FHD_ERR_INVALID_ARG
+    assert "N < 0" in _last(lib)
+    assert lib.fhd_gather(None, -3, *[None] * 5, 4, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_pack(*[None] * 5, -2, None, 0, None) == FHD_ERR_INVALID_ARG
+
+
+def test_empty_calls_succeed_without_device(lib):
+    # N = 0: nothing to do; M = 0 pack: nothing to do
+    assert lib.fhd_compute(*[None] * 10, 5, 0, None) == FHD_OK
+    assert lib.fhd_gather(None, 5, *[None] * 5, 0, None) == FHD_OK
+    assert lib.fhd_pack(*[None] * 5, 0, None, 0, None) == FHD_OK
+
+
+def test_null_pointers_rejected(lib):
+    fake = [0x10000 * (i + 1) for i in range(10)]
+    for i, name in enumerate(["kx", "ky", "kz", "Dr", "Di", "x", "y", "z", "rho_r", "rho_i"]):
+        args = list(fake)
+        args[i] = None
+        assert lib.fhd_compute(*args, 16, 16, None) == FHD_ERR_INVALID_ARG
+        assert name in _last(lib)
+
+
+def test_misaligned_rejected(lib):
+    fake = [0x100000 * (i + 1) for i in range(10)]
+    fake[6] += 2
+    assert lib.fhd_compute(*fake, 16, 16, None) == FHD_ERR_INVALID_ARG
+    assert "aligned" in _last(lib)
+
+
+def test_overlapping_output_rejected(lib):
+    fake = [0x100000 * (i + 1) for i in range(10)]
+    fake[9] = fake[8] + 8            # rho_i overlaps rho_r
+    assert lib.fhd_compute(*fake, 16, 16, None) == FHD_ERR_INVALID_ARG
+    assert "overlaps" in _last(lib)
+    fake = [0x100000 * (i + 1) for i in range(10)]
+    fake[8] = fake[5]                # rho_r aliases x
+    assert lib.fhd_compute(*fake, 16, 16, None) == FHD_ERR_INVALID_ARG
+
+
+def test_packed_buffer_alignment(lib):
+    fake = [0x100000 * (i + 1) for i in range(6)]
+    assert lib.fhd_pack(*fake[:5], 8, fake[5] + 4, 160, None) == FHD_ERR_INVALID_ARG
+    assert "16-byte" in _last(lib)
+    assert lib.fhd_gather(fake[5] + 8, 8, *fake[:5], 16, None) == FHD_ERR_INVALID_ARG
+
+
+def test_pack_buffer_too_small_rejected(lib):
+    fake = [0x100000 * (i + 1) for i in range(6)]
+    assert lib.fhd_pack(*fake[:5], 9, fake[5], 160, None) == FHD_ERR_INVALID_ARG
+    assert "packed_bytes" in _last(lib)
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from non_cartesian_mri_fhd_amd import binding
+    with pytest.raises(FileNotFoundError):
+        binding.load(str(tmp_path / "libfhd.so"))
