@@ -41,6 +41,27 @@ P_TRANS = CUS * SIMDS_PER_CU * TRANS_LANES_PER_CYCLE * CLOCK_HZ
 FLOP_PER_TERM = 13
 ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / 2)
 
+# HBM bytes per gather launch at 128^3 x 100k, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes scaled by a 1 GiB copy's readings (factors 2.0 and 1.0):
+# 40.3 MiB read + 16.0 MiB written. Valid only for the kernel source they
+# were taken on (its SHA-256 below); any later edit reports null until the
+# counters are taken again.
+TRAFFIC = {
+    "workload": "spiral128",
+    "kernel_source_sha256": "54a44be2b4904c33c7c2f2752d8c38a1c00c29f4752efb1a145e000598a75fe3",
+    "bytes_per_launch": (20150 * 2.0 + 16384 * 1.0) * 1024,
+}
+KERNEL_SOURCE = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc", "fhd.hip")
+
+
+def measured_traffic(workload: str):
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if workload != TRAFFIC["workload"] or sha != TRAFFIC["kernel_source_sha256"]:
+        return None
+    return TRAFFIC["bytes_per_launch"]
+
 
 def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
@@ -169,7 +190,7 @@ def main(argv=None) -> int:
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
         },
         "kernel_ms": {"fhd_gather_kernel": gather_ms, "fhd_pack_kernel": pack_ms},
         "gflops_13_per_term": FLOP_PER_TERM * value / 1e9,

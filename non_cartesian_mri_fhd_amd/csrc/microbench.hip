@@ -15,6 +15,14 @@
 // blocking issue, time ~ A*t_fma + B*t_trans; with side-by-side issue, time
 // ~ max(A*t_fma, B*t_trans).
 //
+// form_kernel<F> times one exact VALU instruction form, written as inline
+// assembly so the compiler can neither reorder, fuse nor re-encode it: eight
+// independent accumulator chains per lane, so every instruction has seven
+// independent neighbours. The forms separate what decides the FP32 issue
+// rate on gfx950: operand source (VGPR, inline constant, literal, SGPR),
+// encoding (VOP2, VOP3), v_fract_f32, the transcendental unit, and the
+// gather kernel's own mix of 2 transcendentals and 5 FMAs.
+//
 // The kernels also read the shader clock counter (clock64) and the constant
 // wall clock (wall_clock64) at the start and end of each workgroup, so the
 // host can report the clock the SIMDs actually ran at.
@@ -96,6 +104,102 @@ const MixEntry kMixes[] = {
     {16, 2, mix_kernel<16, 2>}, {6, 1, mix_kernel<6, 1>},
 };
 
+
+// ---------------------------------------------------------------------------
+// instruction forms (inline assembly; VALU only)
+// ---------------------------------------------------------------------------
+#define FHDMB_R8(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7)
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void form_kernel(float *__restrict__ out,
+                                                      long long *__restrict__ clocks, int iters,
+                                                      float sv)
+{
+    float a0 = threadIdx.x, a1 = a0 + 1, a2 = a0 + 2, a3 = a0 + 3, a4 = a0 + 4, a5 = a0 + 5,
+          a6 = a0 + 6, a7 = a0 + 7;
+    float t0 = 0, t1 = 0, t2 = 0, t3 = 0, t4 = 0, t5 = 0, t6 = 0, t7 = 0;
+    const float x = threadIdx.x * 0.001f, y = x + 0.5f;
+    const long long c0 = clock64(), w0 = wall_clock64();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (F == 0) {   // v_fmac_f32_e32, VGPR operands
+#define FHDMB_I(i) asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a##i) : "v"(y), "v"(x));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 1) {   // v_fmac_f32_e32, SGPR src0
+#define FHDMB_I(i) asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a##i) : "s"(sv), "v"(x));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 2) {   // v_fmac_f32_e32, inline constant
+#define FHDMB_I(i) asm volatile("v_fmac_f32_e32 %0, 0.5, %1" : "+v"(a##i) : "v"(x));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 3) {   // v_fma_f32 (VOP3), VGPR operands
+#define FHDMB_I(i) asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(a##i) : "v"(y), "v"(x));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 4) {   // v_fma_f32 (VOP3), SGPR operand
+#define FHDMB_I(i) asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(a##i) : "s"(sv), "v"(x));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 5) {   // v_fmamk_f32, literal constant
+#define FHDMB_I(i) asm volatile("v_fmamk_f32 %0, %1, 0x3f000000, %0" : "+v"(a##i) : "v"(x));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 6) {   // v_fract_f32
+#define FHDMB_I(i) asm volatile("v_fract_f32_e32 %0, %0" : "+v"(a##i));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 7) {   // v_sin_f32 into distinct live registers
+#define FHDMB_I(i) asm volatile("v_sin_f32_e32 %0, %1" : "+v"(t##i) : "v"(a##i));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 8) {   // gather mix, grouped: sin, cos, 5 VGPR FMAs
+                asm volatile("v_sin_f32_e32 %0, %1" : "+v"(t0) : "v"(x));
+                asm volatile("v_cos_f32_e32 %0, %1" : "+v"(t1) : "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a0) : "v"(y), "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a1) : "v"(y), "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a2) : "v"(y), "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a3) : "v"(y), "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a4) : "v"(y), "v"(x));
+            } else if constexpr (F == 9) {   // gather mix with SGPR operands
+                asm volatile("v_sin_f32_e32 %0, %1" : "+v"(t0) : "v"(x));
+                asm volatile("v_cos_f32_e32 %0, %1" : "+v"(t1) : "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a0) : "s"(sv), "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a1) : "s"(sv), "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a2) : "s"(sv), "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a3) : "s"(sv), "v"(x));
+                asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a4) : "s"(sv), "v"(x));
+            }
+        }
+    }
+    const long long c1 = clock64(), w1 = wall_clock64();
+    out[(size_t)blockIdx.x * kBlock + threadIdx.x] =
+        a0 + a1 + a2 + a3 + a4 + a5 + a6 + a7 + t0 + t1 + t2 + t3 + t4 + t5 + t6 + t7;
+    if (threadIdx.x == 0) {
+        clocks[4 * blockIdx.x + 0] = c0;
+        clocks[4 * blockIdx.x + 1] = c1;
+        clocks[4 * blockIdx.x + 2] = w0;
+        clocks[4 * blockIdx.x + 3] = w1;
+    }
+}
+#undef FHDMB_R8
+
+struct FormEntry {
+    const char *name;
+    int instrs_per_group;   // instructions per unrolled group (4 groups per iteration)
+    MixFn fn;
+};
+
+const FormEntry kForms[] = {
+    {"fmac_vop2_vgpr", 8, form_kernel<0>}, {"fmac_vop2_sgpr", 8, form_kernel<1>},
+    {"fmac_vop2_inline_const", 8, form_kernel<2>}, {"fma_vop3_vgpr", 8, form_kernel<3>},
+    {"fma_vop3_sgpr", 8, form_kernel<4>}, {"fmamk_literal", 8, form_kernel<5>},
+    {"fract", 8, form_kernel<6>}, {"sin", 8, form_kernel<7>},
+    {"mix_2trans_5fma_vgpr", 7, form_kernel<8>}, {"mix_2trans_5fma_sgpr", 7, form_kernel<9>},
+};
+
 }  // namespace
 
 // Number of (A, B) pairs and the pair at index i.
@@ -109,19 +213,15 @@ extern "C" int fhdmb_mix_pair(int i, int *a, int *b)
     return 0;
 }
 
-// Runs mix_kernel<a, b> on `blocks` workgroups of 256 lanes for `iters`
-// iterations of 8 streams: one untimed launch, then one launch timed with
-// HIP events on a private stream. Writes the elapsed milliseconds, the mean
-// shader clock in MHz over the workgroups, and a checksum of the outputs.
-// Returns 0, -1 for an unknown pair or bad size, -2 on a HIP error.
-extern "C" int fhdmb_mix(int a, int b, int blocks, int iters, double *ms, double *sclk_mhz,
-                         double *checksum)
-{
-    MixFn fn = nullptr;
-    for (const MixEntry &e : kMixes)
-        if (e.a == a && e.b == b) fn = e.fn;
-    if (!fn || blocks <= 0 || iters <= 0) return -1;
+namespace {
 
+// One untimed launch, then one launch timed with HIP events on a private
+// stream. Writes the elapsed milliseconds, the mean shader clock (MHz) over
+// the workgroups and a checksum of the outputs. 0 on success, -2 on a HIP
+// error.
+int time_kernel(MixFn fn, int blocks, int iters, float arg, double *ms, double *sclk_mhz,
+                double *checksum)
+{
     float *out = nullptr;
     long long *clocks = nullptr;
     hipStream_t stream = nullptr;
@@ -137,20 +237,22 @@ extern "C" int fhdmb_mix(int a, int b, int blocks, int iters, double *ms, double
         rc = -2;
     }
     if (rc == 0) {
-        fn<<<blocks, kBlock, 0, stream>>>(out, clocks, iters, 0.25f);
-        hipEventRecord(e0, stream);
-        fn<<<blocks, kBlock, 0, stream>>>(out, clocks, iters, 0.25f);
-        hipEventRecord(e1, stream);
+        fn<<<blocks, kBlock, 0, stream>>>(out, clocks, iters, arg);
+        (void)hipEventRecord(e0, stream);
+        fn<<<blocks, kBlock, 0, stream>>>(out, clocks, iters, arg);
+        (void)hipEventRecord(e1, stream);
         if (hipStreamSynchronize(stream) != hipSuccess || hipGetLastError() != hipSuccess) rc = -2;
     }
     if (rc == 0) {
         float f = 0.0f;
-        hipEventElapsedTime(&f, e0, e1);
+        (void)hipEventElapsedTime(&f, e0, e1);
         *ms = f;
         std::vector<long long> c((size_t)blocks * 4);
         std::vector<float> o(nout);
-        hipMemcpy(c.data(), clocks, c.size() * sizeof(long long), hipMemcpyDeviceToHost);
-        hipMemcpy(o.data(), out, o.size() * sizeof(float), hipMemcpyDeviceToHost);
+        if (hipMemcpy(c.data(), clocks, c.size() * sizeof(long long), hipMemcpyDeviceToHost) !=
+                hipSuccess ||
+            hipMemcpy(o.data(), out, o.size() * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess)
+            rc = -2;
         double cyc = 0.0, wall = 0.0, sum = 0.0;
         for (int i = 0; i < blocks; ++i) {
             cyc += (double)(c[4 * i + 1] - c[4 * i + 0]);
@@ -160,10 +262,48 @@ extern "C" int fhdmb_mix(int a, int b, int blocks, int iters, double *ms, double
         *sclk_mhz = wall > 0 ? cyc / wall * (wall_khz / 1000.0) : 0.0;
         *checksum = sum;
     }
-    if (e0) hipEventDestroy(e0);
-    if (e1) hipEventDestroy(e1);
-    if (stream) hipStreamDestroy(stream);
-    if (out) hipFree(out);
-    if (clocks) hipFree(clocks);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (stream) (void)hipStreamDestroy(stream);
+    if (out) (void)hipFree(out);
+    if (clocks) (void)hipFree(clocks);
     return rc;
+}
+
+}  // namespace
+
+// Runs mix_kernel<a, b> on `blocks` workgroups of 256 lanes for `iters`
+// iterations of 8 streams (see time_kernel). Returns 0, -1 for an unknown
+// pair or bad size, -2 on a HIP error.
+extern "C" int fhdmb_mix(int a, int b, int blocks, int iters, double *ms, double *sclk_mhz,
+                         double *checksum)
+{
+    MixFn fn = nullptr;
+    for (const MixEntry &e : kMixes)
+        if (e.a == a && e.b == b) fn = e.fn;
+    if (!fn || blocks <= 0 || iters <= 0) return -1;
+    return time_kernel(fn, blocks, iters, 0.25f, ms, sclk_mhz, checksum);
+}
+
+// Number of instruction forms, and the name and instructions per group of
+// form i (each iteration runs 4 groups per lane).
+extern "C" int fhdmb_form_count(void) { return (int)(sizeof(kForms) / sizeof(kForms[0])); }
+
+extern "C" const char *fhdmb_form_name(int i)
+{
+    return (i >= 0 && i < fhdmb_form_count()) ? kForms[i].name : nullptr;
+}
+
+extern "C" int fhdmb_form_instrs(int i)
+{
+    return (i >= 0 && i < fhdmb_form_count()) ? kForms[i].instrs_per_group : -1;
+}
+
+// Times form i (see time_kernel). Returns 0, -1 for a bad index or size,
+// -2 on a HIP error.
+extern "C" int fhdmb_form(int i, int blocks, int iters, double *ms, double *sclk_mhz,
+                          double *checksum)
+{
+    if (i < 0 || i >= fhdmb_form_count() || blocks <= 0 || iters <= 0) return -1;
+    return time_kernel(kForms[i].fn, blocks, iters, 1.0001f, ms, sclk_mhz, checksum);
 }
