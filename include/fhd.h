@@ -103,6 +103,71 @@ int fhd_gather(const void *packed, int M,
                float *rho_r, float *rho_i, int N, void *stream);
 
 /*
+ * Forward operator F (image to k-space; page "Case study -- iterative MRI
+ * reconstruction", section 17.2, with F^H of section 17.3 its adjoint):
+ *
+ *     D_m = sum_{n < N} rho_n * exp(-i * 2*pi * (kx_m*x_n + ky_m*y_n + kz_m*z_n))
+ *
+ * for every sample m < M. Runs a per-voxel pre-pass (fhd_forward_pack) into
+ * a stream-ordered workspace of fhd_packed_bytes(N) bytes, then the gather
+ * kernel with one lane per sample (fhd_forward_gather), no atomics.
+ *   kx, ky, kz         : M fp32 values each (read only)
+ *   x, y, z, rho_r/_i  : N fp32 values each (read only)
+ *   Dr, Di             : M fp32 values each (written), not overlapping any
+ *                        input
+ *   M = 0 does nothing; N = 0 writes zeros (an empty sum).
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
+ */
+int fhd_forward(const float *kx, const float *ky, const float *kz,
+                const float *x, const float *y, const float *z,
+                const float *rho_r, const float *rho_i,
+                float *Dr, float *Di, int M, int N, void *stream);
+
+/*
+ * Pre-pass of F: packs the voxels and the image into `packed` in the record
+ * format of fhd_pack (x, y, z, -arg(rho) in revolutions, |rho|), N padded to
+ * a whole chunk; the size is fhd_packed_bytes(N).
+ *   x, y, z, rho_r, rho_i : N fp32 values each (read only)
+ *   packed                : device buffer, 16-byte aligned, packed_bytes >=
+ *                           fhd_packed_bytes(N), not overlapping any input
+ * N = 0 does nothing. Errors: FHD_ERR_INVALID_ARG, FHD_ERR_HIP.
+ */
+int fhd_forward_pack(const float *x, const float *y, const float *z,
+                     const float *rho_r, const float *rho_i, int N,
+                     void *packed, int64_t packed_bytes, void *stream);
+
+/*
+ * Gather of F over packed voxels (written by fhd_forward_pack with the same
+ * N): D = F rho for the M samples.
+ *   packed     : fhd_packed_bytes(N) bytes, 16-byte aligned (read only)
+ *   kx, ky, kz : M fp32 values each (read only)
+ *   Dr, Di     : M fp32 values each (written), not overlapping any input
+ * M = 0 does nothing; N = 0 writes zeros. Repeated calls are bitwise
+ * identical. Errors: FHD_ERR_INVALID_ARG, FHD_ERR_HIP.
+ */
+int fhd_forward_gather(const void *packed, int N,
+                       const float *kx, const float *ky, const float *kz,
+                       float *Dr, float *Di, int M, void *stream);
+
+/*
+ * Normal operator q = F^H F p, the product inside each conjugate-gradient
+ * iteration (section 17.2; split by loop fission into F and F^H, section
+ * 17.3.2). Runs F into a k-space temporary and F^H back, all in one
+ * stream-ordered workspace of fhd_packed_bytes(N) + fhd_packed_bytes(M) +
+ * 8*M bytes.
+ *   kx, ky, kz       : M fp32 values each (read only)
+ *   x, y, z, p_r/_i  : N fp32 values each (read only)
+ *   q_r, q_i         : N fp32 values each (written), not overlapping any
+ *                      input
+ *   N = 0 does nothing; M = 0 writes zeros.
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
+ */
+int fhd_normal(const float *kx, const float *ky, const float *kz,
+               const float *x, const float *y, const float *z,
+               const float *p_r, const float *p_i,
+               float *q_r, float *q_i, int M, int N, void *stream);
+
+/*
  * Launch shape of the gather kernel: voxels per lane, samples per packed
  * chunk and workgroup size (threads). Any pointer may be NULL.
  */

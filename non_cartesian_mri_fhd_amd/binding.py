@@ -60,6 +60,14 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_pack.restype = i32
     lib.fhd_gather.argtypes = [vp, i32] + [fp] * 5 + [i32, vp]
     lib.fhd_gather.restype = i32
+    lib.fhd_forward.argtypes = [fp] * 10 + [i32, i32, vp]
+    lib.fhd_forward.restype = i32
+    lib.fhd_forward_pack.argtypes = [fp] * 5 + [i32, vp, i64, vp]
+    lib.fhd_forward_pack.restype = i32
+    lib.fhd_forward_gather.argtypes = [vp, i32] + [fp] * 5 + [i32, vp]
+    lib.fhd_forward_gather.restype = i32
+    lib.fhd_normal.argtypes = [fp] * 10 + [i32, i32, vp]
+    lib.fhd_normal.restype = i32
     lib.fhd_gather_config.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
     lib.fhd_gather_config.restype = None
     lib.fhd_status_string.argtypes = [i32]
@@ -160,6 +168,78 @@ def fhd_gather(packed: torch.Tensor, M: int, x, y, z, rho_r=None, rho_i=None, st
         _check(lib, lib.fhd_gather(packed.data_ptr(), int(M), *ptrs, N, _stream(dev, stream)),
                "fhd_gather")
     return rho_r, rho_i
+
+
+def fhd_forward(kx, ky, kz, x, y, z, rho_r, rho_i, Dr=None, Di=None, stream=None):
+    """D = F rho; returns (Dr, Di), float32 tensors on kx's device."""
+    lib = load()
+    M, N = kx.numel(), x.numel()
+    dev = kx.device
+    if Dr is None:
+        Dr = torch.empty(M, dtype=torch.float32, device=dev)
+    if Di is None:
+        Di = torch.empty(M, dtype=torch.float32, device=dev)
+    ptrs = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"))]
+    ptrs += [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"),
+                                               (rho_r, "rho_r"), (rho_i, "rho_i"))]
+    ptrs += [_vec(t, nm, M, dev) for t, nm in ((Dr, "Dr"), (Di, "Di"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_forward(*ptrs, M, N, _stream(dev, stream)), "fhd_forward")
+    return Dr, Di
+
+
+def fhd_forward_pack(x, y, z, rho_r, rho_i, packed: torch.Tensor, stream=None) -> torch.Tensor:
+    """Pre-pass of F into ``packed`` (fhd_packed_bytes(N) bytes)."""
+    lib = load()
+    N = x.numel()
+    dev = packed.device
+    ptrs = [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"),
+                                               (rho_r, "rho_r"), (rho_i, "rho_i"))]
+    if packed.device.type != "cuda" or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous GPU tensor")
+    nbytes = packed.numel() * packed.element_size()
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_forward_pack(*ptrs, N, packed.data_ptr(), nbytes,
+                                         _stream(dev, stream)), "fhd_forward_pack")
+    return packed
+
+
+def fhd_forward_gather(packed: torch.Tensor, N: int, kx, ky, kz, Dr=None, Di=None, stream=None):
+    """Gather of F over packed voxels; returns (Dr, Di)."""
+    lib = load()
+    M = kx.numel()
+    dev = kx.device
+    if Dr is None:
+        Dr = torch.empty(M, dtype=torch.float32, device=dev)
+    if Di is None:
+        Di = torch.empty(M, dtype=torch.float32, device=dev)
+    if packed.device != dev or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous tensor on %s" % dev)
+    if packed.numel() * packed.element_size() < (fhd_packed_bytes(N) if N > 0 else 0):
+        raise ValueError("packed is smaller than fhd_packed_bytes(N)")
+    ptrs = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"),
+                                               (Dr, "Dr"), (Di, "Di"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_forward_gather(packed.data_ptr(), int(N), *ptrs, M,
+                                           _stream(dev, stream)), "fhd_forward_gather")
+    return Dr, Di
+
+
+def fhd_normal(kx, ky, kz, x, y, z, p_r, p_i, q_r=None, q_i=None, stream=None):
+    """q = F^H F p; returns (q_r, q_i), float32 tensors on x's device."""
+    lib = load()
+    M, N = kx.numel(), x.numel()
+    dev = x.device
+    if q_r is None:
+        q_r = torch.empty(N, dtype=torch.float32, device=dev)
+    if q_i is None:
+        q_i = torch.empty(N, dtype=torch.float32, device=dev)
+    ptrs = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"))]
+    ptrs += [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"), (p_r, "p_r"),
+                                               (p_i, "p_i"), (q_r, "q_r"), (q_i, "q_i"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_normal(*ptrs, M, N, _stream(dev, stream)), "fhd_normal")
+    return q_r, q_i
 
 
 def new_packed(M: int, device) -> torch.Tensor:

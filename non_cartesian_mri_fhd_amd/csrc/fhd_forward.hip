@@ -1,0 +1,298 @@
+// fhd_forward.hip -- the forward operator F (image to k-space) for gfx950.
+//
+// D_m = sum_n rho_n exp(-i 2 pi k_m . x_n)   (page "Case study -- iterative
+// MRI reconstruction", section 17.2: F maps the image to k-space and F^H,
+// section 17.3, is its adjoint; section 17.3.2 names F^H F, whose first
+// half this is)
+//
+// The same two-kernel split as F^H D with the roles of voxels and samples
+// swapped:
+//
+//  * fhd_forward_pack_kernel -- per-voxel pre-pass. Writes each voxel as the
+//    record (x, y, z, s, a) with a = |rho| and s = -arg(rho) / (2 pi), so
+//    that rho e^{-i 2 pi k.x} = a e^{-i 2 pi (k.x + s)}.
+//
+//  * fhd_forward_gather_kernel -- one lane per kSamp consecutive samples,
+//    no atomics; every lane walks the same voxel stream through LDS
+//    (stream_chunks). Per term: p = kx x + ky y + kz z + s (3 FMA; 2 + 1/kSamp
+//    when all of a lane's samples share kz, as within a plane of a stack of
+//    spirals -- bitwise identical), v_cos_f32, v_sin_f32, 2 FMA. The
+//    accumulated sine sum is negated once at the end (exact).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "fhd_internal.h"
+
+namespace fhd {
+namespace {
+
+constexpr int kSamp = 8;   // consecutive samples per lane
+
+__global__ __launch_bounds__(kPackBlock) void fhd_forward_pack_kernel(
+    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
+    const float *__restrict__ rho_r, const float *__restrict__ rho_i,
+    float *__restrict__ packed, int N, int64_t N_pad)
+{
+    const int64_t n = (int64_t)blockIdx.x * kPackBlock + threadIdx.x;
+    if (n >= N_pad) return;
+    float fx = 0.0f, fy = 0.0f, fz = 0.0f, s = 0.0f, amp = 0.0f;
+    if (n < N) {
+        fx = x[n];
+        fy = y[n];
+        fz = z[n];
+        const double re = rho_r[n], im = rho_i[n];
+        amp = (float)hypot(re, im);
+        s = (float)(-atan2(im, re) * (0.5 / M_PI));   // [-0.5, 0.5] revolutions
+    }
+    store_record(packed, n, fx, fy, fz, s, amp);
+}
+
+// Accumulate one chunk of kChunk voxels into a lane's S samples.
+// SHARED: all S samples have the same kz (checked by the caller).
+template <int S, bool SHARED>
+__device__ __forceinline__ void accumulate_voxels(const float4 *ch, const float (&kx)[S],
+                                                  const float (&ky)[S], const float (&kz)[S],
+                                                  float (&acc_r)[S], float (&acc_i)[S])
+{
+    float f[kFields][kChunk];
+    load_chunk(ch, f);
+    const float(&vx)[kChunk] = f[0];
+    const float(&vy)[kChunk] = f[1];
+    const float(&vz)[kChunk] = f[2];
+    const float(&vs)[kChunk] = f[3];
+    const float(&amp)[kChunk] = f[4];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+        float p[S], c[S], sn[S];
+        if constexpr (SHARED) {
+            const float q = __builtin_fmaf(kz[0], vz[u], vs[u]);
+#pragma unroll
+            for (int j = 0; j < S; ++j) p[j] = __builtin_fmaf(kx[j], vx[u], __builtin_fmaf(ky[j], vy[u], q));
+        } else {
+#pragma unroll
+            for (int j = 0; j < S; ++j)
+                p[j] = __builtin_fmaf(kx[j], vx[u],
+                                      __builtin_fmaf(ky[j], vy[u], __builtin_fmaf(kz[j], vz[u], vs[u])));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < S; ++j) c[j] = __builtin_amdgcn_cosf(p[j]);
+#pragma unroll
+        for (int j = 0; j < S; ++j) sn[j] = __builtin_amdgcn_sinf(p[j]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            acc_r[j] = __builtin_fmaf(amp[u], c[j], acc_r[j]);
+            acc_i[j] = __builtin_fmaf(amp[u], sn[j], acc_i[j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int S>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void fhd_forward_gather_kernel(
+    const float *__restrict__ packed, int nchunks,
+    const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
+    float *__restrict__ Dr, float *__restrict__ Di, int M)
+{
+    __shared__ float4 stage[2][kStageVec4];
+    const float4 *src = reinterpret_cast<const float4 *>(packed);
+
+    // lane l of workgroup b owns samples (b*kBlock + l)*S + j, j < S
+    const int64_t m0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * S;
+    float sx[S], sy[S], sz[S], acc_r[S], acc_i[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const int64_t m = m0 + j;
+        const bool live = m < M;
+        sx[j] = live ? kx[m] : 0.0f;
+        sy[j] = live ? ky[m] : 0.0f;
+        sz[j] = live ? kz[m] : 0.0f;
+        acc_r[j] = 0.0f;
+        acc_i[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 1; j < S; ++j)
+        if (m0 + j >= M) {
+            sx[j] = sx[0];
+            sy[j] = sy[0];
+            sz[j] = sz[0];
+        }
+    bool same_kz = true;
+#pragma unroll
+    for (int j = 1; j < S; ++j) same_kz = same_kz && __float_as_uint(sz[j]) == __float_as_uint(sz[0]);
+    const bool shared = __syncthreads_and(same_kz);
+
+    if (shared)
+        stream_chunks(src, nchunks, stage, [&](const float4 *ch) {
+            accumulate_voxels<S, true>(ch, sx, sy, sz, acc_r, acc_i);
+        });
+    else
+        stream_chunks(src, nchunks, stage, [&](const float4 *ch) {
+            accumulate_voxels<S, false>(ch, sx, sy, sz, acc_r, acc_i);
+        });
+
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const int64_t m = m0 + j;
+        if (m < M) {
+            Dr[m] = acc_r[j];
+            Di[m] = -acc_i[j];
+        }
+    }
+}
+
+}  // namespace
+
+int launch_forward_pack(const float *x, const float *y, const float *z, const float *rho_r,
+                        const float *rho_i, int N, float *packed, hipStream_t stream)
+{
+    if (N == 0) return FHD_OK;
+    const int64_t N_pad = (int64_t)((N + kChunk - 1) / kChunk) * kChunk;
+    const int64_t blocks = (N_pad + kPackBlock - 1) / kPackBlock;
+    fhd_forward_pack_kernel<<<dim3((unsigned)blocks), dim3(kPackBlock), 0, stream>>>(
+        x, y, z, rho_r, rho_i, packed, N, N_pad);
+    return launch_status("fhd_forward_pack_kernel launch");
+}
+
+int launch_forward_gather(const float *packed, int N, const float *kx, const float *ky,
+                          const float *kz, float *Dr, float *Di, int M, hipStream_t stream)
+{
+    if (M == 0) return FHD_OK;
+    const int nchunks = (int)(((int64_t)N + kChunk - 1) / kChunk);
+    const int64_t per_block = (int64_t)kBlock * kSamp;
+    const int64_t blocks = ((int64_t)M + per_block - 1) / per_block;
+    fhd_forward_gather_kernel<kSamp><<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
+        packed, nchunks, kx, ky, kz, Dr, Di, M);
+    return launch_status("fhd_forward_gather_kernel launch");
+}
+
+}  // namespace fhd
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+using namespace fhd;
+
+extern "C" int fhd_forward_pack(const float *x, const float *y, const float *z, const float *rho_r,
+                                const float *rho_i, int N, void *packed, int64_t packed_bytes,
+                                void *stream)
+{
+    clear_error();
+    if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
+    if (N == 0) return FHD_OK;
+    const int64_t need = packed_bytes_for(N), nb = (int64_t)N * 4;
+    if (packed_bytes < need)
+        return fail(FHD_ERR_INVALID_ARG, "packed_bytes " + std::to_string(packed_bytes) + " < " +
+                                             std::to_string(need));
+    const Span all[] = {{x, nb, "x"}, {y, nb, "y"}, {z, nb, "z"}, {rho_r, nb, "rho_r"},
+                        {rho_i, nb, "rho_i"}, {packed, need, "packed", 16}};
+    int rc = check_host_side(all, 6);
+    if (rc == FHD_OK) rc = check_no_overlap(all, 6, 5);
+    if (rc == FHD_OK) rc = check_device_spans(all, 6);
+    if (rc != FHD_OK) return rc;
+    return launch_forward_pack(x, y, z, rho_r, rho_i, N, (float *)packed, (hipStream_t)stream);
+}
+
+extern "C" int fhd_forward_gather(const void *packed, int N, const float *kx, const float *ky,
+                                  const float *kz, float *Dr, float *Di, int M, void *stream)
+{
+    clear_error();
+    if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
+    if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
+    if (M == 0) return FHD_OK;
+    const int64_t mb = (int64_t)M * 4;
+    const Span all[] = {{packed, N > 0 ? packed_bytes_for(N) : 0, "packed", 16},
+                        {kx, mb, "kx"}, {ky, mb, "ky"}, {kz, mb, "kz"},
+                        {Dr, mb, "Dr"}, {Di, mb, "Di"}};
+    int rc = check_host_side(all, 6);
+    if (rc == FHD_OK) rc = check_no_overlap(all, 6, 4);
+    if (rc == FHD_OK) rc = check_device_spans(all, 6);
+    if (rc != FHD_OK) return rc;
+    return launch_forward_gather((const float *)packed, N, kx, ky, kz, Dr, Di, M,
+                                 (hipStream_t)stream);
+}
+
+extern "C" int fhd_forward(const float *kx, const float *ky, const float *kz, const float *x,
+                           const float *y, const float *z, const float *rho_r, const float *rho_i,
+                           float *Dr, float *Di, int M, int N, void *stream)
+{
+    clear_error();
+    if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
+    if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
+    if (M == 0) return FHD_OK;
+    const int64_t mb = (int64_t)M * 4, nb = (int64_t)N * 4;
+    const Span all[] = {{kx, mb, "kx"}, {ky, mb, "ky"}, {kz, mb, "kz"},
+                        {x, nb, "x"},   {y, nb, "y"},   {z, nb, "z"},
+                        {rho_r, nb, "rho_r"}, {rho_i, nb, "rho_i"},
+                        {Dr, mb, "Dr"}, {Di, mb, "Di"}};
+    int rc = check_host_side(all, 10);
+    if (rc == FHD_OK) rc = check_no_overlap(all, 10, 8);
+    if (rc == FHD_OK) rc = check_device_spans(all, 10);
+    if (rc != FHD_OK) return rc;
+
+    hipStream_t s = (hipStream_t)stream;
+    float *packed = nullptr;
+    if (N > 0) {
+        const hipError_t e = hipMallocAsync((void **)&packed, (size_t)packed_bytes_for(N), s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+        }
+        rc = launch_forward_pack(x, y, z, rho_r, rho_i, N, packed, s);
+    }
+    if (rc == FHD_OK) rc = launch_forward_gather(packed, N, kx, ky, kz, Dr, Di, M, s);
+    if (packed) {
+        const hipError_t e = hipFreeAsync(packed, s);
+        if (e != hipSuccess && rc == FHD_OK)
+            rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
+    }
+    return rc;
+}
+
+// q = F^H F p: F into a k-space temporary, then F^H (loop fission of the
+// normal operator into its two halves, page "Case study -- iterative MRI
+// reconstruction", section 17.3.2).
+extern "C" int fhd_normal(const float *kx, const float *ky, const float *kz, const float *x,
+                          const float *y, const float *z, const float *p_r, const float *p_i,
+                          float *q_r, float *q_i, int M, int N, void *stream)
+{
+    clear_error();
+    if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
+    if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
+    if (N == 0) return FHD_OK;
+    const int64_t mb = (int64_t)M * 4, nb = (int64_t)N * 4;
+    const Span all[] = {{kx, mb, "kx"}, {ky, mb, "ky"}, {kz, mb, "kz"},
+                        {x, nb, "x"},   {y, nb, "y"},   {z, nb, "z"},
+                        {p_r, nb, "p_r"}, {p_i, nb, "p_i"},
+                        {q_r, nb, "q_r"}, {q_i, nb, "q_i"}};
+    int rc = check_host_side(all, 10);
+    if (rc == FHD_OK) rc = check_no_overlap(all, 10, 8);
+    if (rc == FHD_OK) rc = check_device_spans(all, 10);
+    if (rc != FHD_OK) return rc;
+
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) return launch_gather(nullptr, 0, x, y, z, q_r, q_i, N, s);   // empty sum
+    // one workspace: packed voxels | packed samples | D (real, imaginary)
+    const int64_t vox_bytes = packed_bytes_for(N), smp_bytes = packed_bytes_for(M);
+    const int64_t d_bytes = 2 * mb;
+    char *ws = nullptr;
+    const hipError_t e = hipMallocAsync((void **)&ws, (size_t)(vox_bytes + smp_bytes + d_bytes), s);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+    }
+    float *vox = (float *)ws, *smp = (float *)(ws + vox_bytes);
+    float *d_r = (float *)(ws + vox_bytes + smp_bytes), *d_i = d_r + M;
+    rc = launch_forward_pack(x, y, z, p_r, p_i, N, vox, s);
+    if (rc == FHD_OK) rc = launch_forward_gather(vox, N, kx, ky, kz, d_r, d_i, M, s);
+    if (rc == FHD_OK) rc = launch_pack(kx, ky, kz, d_r, d_i, M, smp, s);
+    if (rc == FHD_OK) rc = launch_gather(smp, M, x, y, z, q_r, q_i, N, s);
+    const hipError_t f = hipFreeAsync(ws, s);
+    if (f != hipSuccess && rc == FHD_OK)
+        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
+    return rc;
+}

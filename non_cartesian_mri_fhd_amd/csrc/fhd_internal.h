@@ -1,0 +1,154 @@
+// fhd_internal.h -- shared pieces of libfhd.so's kernels and C ABI (not
+// installed; the public interface is include/fhd.h).
+//
+// Both non-uniform DFT directions use one record format and one broadcast
+// machine:
+//
+//  * A "packed" stream holds records of five fp32 fields -- three
+//    coordinates, a phase offset in revolutions and an amplitude -- in
+//    chunks of kChunk records, field-major inside a chunk
+//    ([f0 x8][f1 x8][f2 x8][f3 x8][f4 x8], 160 B = ten float4). The tail
+//    chunk is padded with amplitude-0 records, which add exactly 0.
+//    F^H D streams k-space samples (kx, ky, kz, arg D / 2pi, |D|); the
+//    forward F streams voxels (x, y, z, -arg rho / 2pi, |rho|).
+//
+//  * stream_chunks() walks a packed stream through LDS in stages of
+//    kStageChunks chunks, double buffered: while a workgroup works on one
+//    stage, each lane holds three float4 of the next stage in registers and
+//    writes them to the other buffer before the stage barrier. Every lane
+//    then reads each chunk with same-address ds_read_b128, which the LDS
+//    broadcasts, so the stream's values reach the FMAs in VGPRs (on gfx950
+//    an FP32 FMA with an SGPR operand issues at half rate and never pairs).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "fhd.h"
+
+namespace fhd {
+
+constexpr int kBlock = 256;        // gather workgroup: 4 wave64
+constexpr int kChunk = 8;          // records per packed chunk
+constexpr int kFields = 5;         // three coordinates, phase offset, amplitude
+constexpr int kChunkVec4 = kChunk * kFields / 4;        // 10 float4 per chunk
+constexpr int kStageChunks = 64;   // chunks per LDS stage (512 records, 10 KB)
+constexpr int kStageVec4 = kStageChunks * kChunkVec4;   // 640 float4
+constexpr int kStageLoads = (kStageVec4 + kBlock - 1) / kBlock;   // 3 per lane
+constexpr int kPackBlock = 256;
+
+static_assert(kBlock % 64 == 0, "workgroup must be whole wave64s");
+static_assert(kChunk * kFields % 4 == 0, "chunks must be whole float4s");
+static_assert(kStageLoads == 3, "stream_chunks holds three float4 per lane");
+
+inline int64_t packed_bytes_for(int64_t count)
+{
+    const int64_t chunks = (count + kChunk - 1) / kChunk;
+    return chunks * kChunk * kFields * (int64_t)sizeof(float);
+}
+
+// Writes record r of a packed stream (one lane per padded record).
+__device__ __forceinline__ void store_record(float *__restrict__ packed, int64_t r, float f0,
+                                             float f1, float f2, float f3, float f4)
+{
+    float *c = packed + (r / kChunk) * (kFields * kChunk) + (r % kChunk);
+    c[0 * kChunk] = f0;
+    c[1 * kChunk] = f1;
+    c[2 * kChunk] = f2;
+    c[3 * kChunk] = f3;
+    c[4 * kChunk] = f4;
+}
+
+// Unpacks one chunk's float4s (read from LDS) into per-field arrays.
+__device__ __forceinline__ void load_chunk(const float4 *ch, float (&f)[kFields][kChunk])
+{
+#pragma unroll
+    for (int q = 0; q < kChunkVec4; ++q) {
+        const float4 t = ch[q];
+        const int field = (4 * q) / kChunk, at = (4 * q) % kChunk;
+        f[field][at + 0] = t.x;
+        f[field][at + 1] = t.y;
+        f[field][at + 2] = t.z;
+        f[field][at + 3] = t.w;
+    }
+}
+
+// Streams the nchunks chunks of `src` through the workgroup's LDS stage
+// buffers and calls body(chunk) for each chunk in order, in every lane.
+// Every lane of the workgroup must call it (it holds workgroup barriers).
+template <typename Body>
+__device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, int nchunks,
+                                              float4 (*stage)[kStageVec4], Body &&body)
+{
+    const int64_t total_vec4 = (int64_t)nchunks * kChunkVec4;
+    const int nstages = (nchunks + kStageChunks - 1) / kStageChunks;
+    for (int i = threadIdx.x; i < kStageVec4 && i < total_vec4; i += kBlock) stage[0][i] = src[i];
+    __syncthreads();
+
+    for (int st = 0; st < nstages; ++st) {
+        // prefetch the next stage into registers (indices clamped in bounds;
+        // the clamped copies are never written to LDS)
+        const bool more = st + 1 < nstages;
+        const int64_t next = (int64_t)(st + 1) * kStageVec4 + threadIdx.x;
+        float4 r0, r1, r2;
+        if (more) {
+            r0 = src[min(next, total_vec4 - 1)];
+            r1 = src[min(next + kBlock, total_vec4 - 1)];
+            r2 = src[min(next + 2 * kBlock, total_vec4 - 1)];
+        }
+        const int chunks_here = min(kStageChunks, nchunks - st * kStageChunks);
+        const float4 *buf = stage[st & 1];
+        for (int c = 0; c < chunks_here; ++c) body(buf + c * kChunkVec4);
+        if (more) {
+            // the other buffer was last read before the previous barrier
+            float4 *dst = stage[(st + 1) & 1];
+            const int i0 = threadIdx.x;
+            if (next < total_vec4) dst[i0] = r0;
+            if (i0 + kBlock < kStageVec4 && next + kBlock < total_vec4) dst[i0 + kBlock] = r1;
+            if (i0 + 2 * kBlock < kStageVec4 && next + 2 * kBlock < total_vec4)
+                dst[i0 + 2 * kBlock] = r2;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side (abi_checks.hip)
+// ---------------------------------------------------------------------------
+struct Span {
+    const void *p;
+    int64_t bytes;
+    const char *name;
+    unsigned align = 4;   // required alignment in bytes
+};
+
+// Records msg as the calling thread's last error and returns status.
+int fail(int status, const std::string &msg);
+void clear_error();
+
+// NULL and alignment of every span with bytes > 0; no HIP call.
+int check_host_side(const Span *spans, int count);
+// Spans [first_out, count) are outputs: none may overlap any other span.
+int check_no_overlap(const Span *spans, int count, int first_out);
+// Every span with bytes > 0 is device-accessible memory of the current
+// device and, for device allocations, ends inside the allocation holding
+// its first byte.
+int check_device_spans(const Span *spans, int count);
+// FHD_ERR_HIP with `what` if the last launch failed.
+int launch_status(const char *what);
+
+// Kernel launches without argument checks (callers have checked).
+// fhd.hip: adjoint F^H D
+int launch_pack(const float *kx, const float *ky, const float *kz, const float *Dr, const float *Di,
+                int M, float *packed, hipStream_t stream);
+int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
+                  float *rho_r, float *rho_i, int N, hipStream_t stream);
+// fhd_forward.hip: forward F
+int launch_forward_pack(const float *x, const float *y, const float *z, const float *rho_r,
+                        const float *rho_i, int N, float *packed, hipStream_t stream);
+int launch_forward_gather(const float *packed, int N, const float *kx, const float *ky,
+                          const float *kz, float *Dr, float *Di, int M, hipStream_t stream);
+
+}  // namespace fhd

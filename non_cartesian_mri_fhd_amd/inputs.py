@@ -244,3 +244,10 @@ def cartesian_case(L: int, seed: int) -> dict:
     Dr, Di = _f32(rng.standard_normal(M), rng.standard_normal(M))
     x, y, z = grid_coords(L)
     return dict(kx=kx, ky=ky, kz=kz, Dr=Dr, Di=Di, x=x, y=y, z=z, M=M, N=L ** 3, L=L)
+
+
+def random_image(N: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Seeded complex image, Re and Im i.i.d. N(0,1), as fp32 (re, im)."""
+    rng = np.random.default_rng(seed)
+    re, im = _f32(rng.standard_normal(N), rng.standard_normal(N))
+    return re, im
