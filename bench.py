@@ -11,6 +11,12 @@ event timing on the launch stream), the sampled parity against the fp64
 oracle and the oracle's own CPU throughput on that sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--op fhd|forward|normal|cg]
+
+--op selects the operator timed (default fhd, the headline F^H D):
+forward = D = F rho; normal = F^H F rho (2 N M terms per step); cg = one
+conjugate-gradient iteration (F^H F plus two inner products and the vector
+updates; 2 N M terms per step).
 """
 from __future__ import annotations
 
@@ -69,6 +75,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="spiral128")
+    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -119,6 +126,9 @@ def main(argv=None) -> int:
               "with no exchange, and this build measures one GPU's share only "
               "(got --gpus %d)" % args.gpus, file=sys.stderr)
         return 2
+
+    if args.op != "fhd":
+        return bench_other(args)
 
     import torch
     from non_cartesian_mri_fhd_amd import binding, build, inputs
@@ -200,6 +210,69 @@ def main(argv=None) -> int:
                                     rho_r.cpu().numpy(), rho_i.cpu().numpy())
         out["cpu_baseline"] = base
         out["parity"] = parity
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_other(args) -> int:
+    """Times F, F^H F or one CG iteration on the workload (one JSON line)."""
+    import torch
+    from non_cartesian_mri_fhd_amd import binding, build, inputs
+    build.ensure_built()
+    binding.load()
+    assert torch.cuda.is_available(), "no GPU visible"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.make_workload(args.workload)
+    N, M = w["N"], w["M"]
+    t = {k: torch.from_numpy(w[k]).to(dev) for k in ("kx", "ky", "kz", "Dr", "Di", "x", "y", "z")}
+    img = [torch.from_numpy(a).to(dev) for a in inputs.random_image(N, seed=77)]
+    if args.op == "forward":
+        Dr = torch.empty(M, device=dev)
+        Di = torch.empty(M, device=dev)
+
+        def step():
+            binding.fhd_forward(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], img[0], img[1],
+                                Dr, Di)
+        terms_per_step = float(N) * M
+    elif args.op == "normal":
+        qr = torch.empty(N, device=dev)
+        qi = torch.empty(N, device=dev)
+
+        def step():
+            binding.fhd_normal(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], img[0], img[1],
+                               qr, qi)
+        terms_per_step = 2.0 * N * M
+    else:
+        rr = torch.empty(N, device=dev)
+        ri = torch.empty(N, device=dev)
+        k_iters = 3
+
+        def step():
+            binding.fhd_cg(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], t["x"], t["y"], t["z"],
+                           k_iters, 0.0, rr, ri)
+        # F^H D once plus k_iters applications of F^H F
+        terms_per_step = float(N) * M * (1 + 2 * k_iters)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    value = terms_per_step / (ms * 1e-3)
+    out = {
+        "metric": "%s voxel-sample terms/s (%s)" % (args.op, args.workload),
+        "value": value, "unit": "terms/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "op": args.op, "N": N, "M": M,
+                   "terms_per_step": terms_per_step},
+        "roofline": {"bound": "alu", "achieved": FLOP_PER_TERM * value / 1e12,
+                     "peak": FLOP_PER_TERM * ROOF_TERMS / 1e12, "unit": "TFLOP/s",
+                     "frac": value / ROOF_TERMS, "traffic": None},
+    }
     print(json.dumps(out), flush=True)
     return 0
 

@@ -168,6 +168,38 @@ int fhd_normal(const float *kx, const float *ky, const float *kz,
                float *q_r, float *q_i, int M, int N, void *stream);
 
 /*
+ * Conjugate-gradient reconstruction (page "Case study -- iterative MRI
+ * reconstruction", section 17.2 and its CG skeleton after section 17.3.6)
+ * with the regulariser left out (the pages do not specify R or lambda):
+ * solves F^H F rho = F^H D from rho = 0. Each iteration applies F^H F once
+ * (fhd_normal) and two inner products (fp64 accumulation, fixed reduction
+ * order: bitwise repeatable). As on the pages, the inner products return to
+ * the host every iteration, so this call synchronises `stream` and blocks
+ * the calling thread.
+ *   kx, ky, kz, Dr, Di : M fp32 values each (read only)
+ *   x, y, z            : N fp32 values each (read only)
+ *   rho_r, rho_i       : N fp32 values each (written: the last iterate),
+ *                        not overlapping any input
+ *   max_iter >= 0      : iteration limit
+ *   tol >= 0           : stop once the squared residual norm ||r||^2 falls
+ *                        below tol (absolute, as on the pages)
+ *   iters_done         : host int, set to the iterations run
+ *   residuals          : host array of max_iter + 1 floats or NULL; entry k
+ *                        is ||r_k||^2 (entry 0 is ||F^H D||^2)
+ * The workspace of fhd_cg_workspace_bytes(M, N) bytes is allocated and
+ * freed on `stream`. Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
+ */
+int fhd_cg(const float *kx, const float *ky, const float *kz,
+           const float *Dr, const float *Di,
+           const float *x, const float *y, const float *z,
+           float *rho_r, float *rho_i, int M, int N, int max_iter, float tol,
+           int *iters_done, float *residuals, void *stream);
+
+/* Workspace bytes fhd_cg allocates for M samples and N voxels (-1 if
+ * either is negative). */
+int64_t fhd_cg_workspace_bytes(int M, int N);
+
+/*
  * Launch shape of the gather kernel: voxels per lane, samples per packed
  * chunk and workgroup size (threads). Any pointer may be NULL.
  */

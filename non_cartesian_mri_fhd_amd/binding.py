@@ -68,6 +68,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_forward_gather.restype = i32
     lib.fhd_normal.argtypes = [fp] * 10 + [i32, i32, vp]
     lib.fhd_normal.restype = i32
+    lib.fhd_cg.argtypes = [fp] * 10 + [i32, i32, i32, ctypes.c_float,
+                                       ctypes.POINTER(ctypes.c_int), ctypes.c_void_p, vp]
+    lib.fhd_cg.restype = i32
+    lib.fhd_cg_workspace_bytes.argtypes = [i32, i32]
+    lib.fhd_cg_workspace_bytes.restype = i64
     lib.fhd_gather_config.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
     lib.fhd_gather_config.restype = None
     lib.fhd_status_string.argtypes = [i32]
@@ -240,6 +245,33 @@ def fhd_normal(kx, ky, kz, x, y, z, p_r, p_i, q_r=None, q_i=None, stream=None):
     with torch.cuda.device(dev):
         _check(lib, lib.fhd_normal(*ptrs, M, N, _stream(dev, stream)), "fhd_normal")
     return q_r, q_i
+
+
+def fhd_cg(kx, ky, kz, Dr, Di, x, y, z, max_iter: int, tol: float = 0.0,
+           rho_r=None, rho_i=None, stream=None):
+    """CG on F^H F rho = F^H D from rho = 0 (synchronises the stream).
+
+    Returns (rho_r, rho_i, iterations, residuals) with residuals the numpy
+    array of squared residual norms ||r_k||^2, k = 0..iterations.
+    """
+    import numpy as np
+    lib = load()
+    M, N = kx.numel(), x.numel()
+    dev = x.device
+    if rho_r is None:
+        rho_r = torch.empty(N, dtype=torch.float32, device=dev)
+    if rho_i is None:
+        rho_i = torch.empty(N, dtype=torch.float32, device=dev)
+    ptrs = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"),
+                                               (Dr, "Dr"), (Di, "Di"))]
+    ptrs += [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"),
+                                               (rho_r, "rho_r"), (rho_i, "rho_i"))]
+    res = np.zeros(int(max_iter) + 1, dtype=np.float32)
+    done = ctypes.c_int(0)
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_cg(*ptrs, M, N, int(max_iter), float(tol), ctypes.byref(done),
+                               res.ctypes.data, _stream(dev, stream)), "fhd_cg")
+    return rho_r, rho_i, done.value, res[:done.value + 1].copy()
 
 
 def new_packed(M: int, device) -> torch.Tensor:

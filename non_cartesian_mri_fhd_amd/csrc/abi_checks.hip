@@ -97,6 +97,60 @@ int check_device_spans(const Span *spans, int count)
     return FHD_OK;
 }
 
+int split_count(int64_t blocks, int nchunks)
+{
+    static int cus_cached[64] = {0};
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= 64) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    if (cus_cached[device] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+            cus <= 0) {
+            (void)hipGetLastError();
+            return 1;
+        }
+        cus_cached[device] = cus;
+    }
+    const int64_t resident = 4LL * cus_cached[device];
+    if (blocks <= 0 || blocks >= resident) return 1;
+    const int64_t stages = (nchunks + kStageChunks - 1) / kStageChunks;
+    int64_t splits = resident / blocks;
+    if (splits > stages) splits = stages;
+    return splits < 1 ? 1 : (int)splits;
+}
+
+namespace {
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float *__restrict__ part_r,
+                                                            const float *__restrict__ part_i,
+                                                            int splits, int64_t n,
+                                                            float *__restrict__ out_r,
+                                                            float *__restrict__ out_i)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float sr = 0.0f, si = 0.0f;
+    for (int s = 0; s < splits; ++s) {
+        sr += part_r[(int64_t)s * n + i];
+        si += part_i[(int64_t)s * n + i];
+    }
+    out_r[i] = sr;
+    out_i[i] = si;
+}
+
+}  // namespace
+
+int launch_reduce(const float *part_r, const float *part_i, int splits, int64_t n, float *out_r,
+                  float *out_i, hipStream_t stream)
+{
+    if (n == 0) return FHD_OK;
+    reduce_splits_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(
+        part_r, part_i, splits, n, out_r, out_i);
+    return launch_status("reduce_splits_kernel launch");
+}
+
 int launch_status(const char *what)
 {
     const hipError_t e = hipGetLastError();

@@ -112,11 +112,13 @@ __device__ __forceinline__ void accumulate_chunk(const float4 *ch, const float (
 
 // At least 4 waves per SIMD (<= 128 VGPRs): a 128^3 grid at 8 voxels per
 // lane is exactly 4 waves per SIMD, so all of them are resident at once.
+// Split s = blockIdx.y of `splits` takes its share of the sample stream and
+// writes rho (splits == 1) or its partial sums at out + s*N.
 template <int V>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void fhd_gather_kernel(
-    const float *__restrict__ packed, int nchunks,
+    const float *__restrict__ packed, int nchunks, int splits,
     const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
-    float *__restrict__ rho_r, float *__restrict__ rho_i, int N)
+    float *__restrict__ out_r, float *__restrict__ out_i, int N)
 {
     __shared__ float4 stage[2][kStageVec4];
     const float4 *src = reinterpret_cast<const float4 *>(packed);
@@ -152,21 +154,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     // reached by every wave of the workgroup
     const bool shared = __syncthreads_and(same_yz);
 
+    int c0, c1;
+    split_range(nchunks, splits, blockIdx.y, &c0, &c1);
     if (shared)
-        stream_chunks(src, nchunks, stage, [&](const float4 *ch) {
+        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
             accumulate_chunk<V, true>(ch, px, py, pz, acc_r, acc_i);
         });
     else
-        stream_chunks(src, nchunks, stage, [&](const float4 *ch) {
+        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
             accumulate_chunk<V, false>(ch, px, py, pz, acc_r, acc_i);
         });
 
+    float *dst_r = out_r + (int64_t)blockIdx.y * N, *dst_i = out_i + (int64_t)blockIdx.y * N;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int64_t n = n0 + v;
         if (n < N) {
-            rho_r[n] = acc_r[v];
-            rho_i[n] = acc_i[v];
+            dst_r[n] = acc_r[v];
+            dst_i[n] = acc_i[v];
         }
     }
 }
@@ -192,9 +197,28 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
     const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
     const int64_t per_block = (int64_t)kBlock * kVox;
     const int64_t blocks = ((int64_t)N + per_block - 1) / per_block;
-    fhd_gather_kernel<kVox><<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
-        packed, nchunks, x, y, z, rho_r, rho_i, N);
-    return launch_status("fhd_gather_kernel launch");
+    const int splits = split_count(blocks, nchunks);
+    if (splits == 1) {
+        fhd_gather_kernel<kVox><<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
+            packed, nchunks, 1, x, y, z, rho_r, rho_i, N);
+        return launch_status("fhd_gather_kernel launch");
+    }
+    float *part = nullptr;
+    const hipError_t e = hipMallocAsync((void **)&part, (size_t)splits * 2 * N * sizeof(float), stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (split partials): ") +
+                                       hipGetErrorString(e));
+    }
+    float *part_r = part, *part_i = part + (int64_t)splits * N;
+    fhd_gather_kernel<kVox><<<dim3((unsigned)blocks, (unsigned)splits), dim3(kBlock), 0, stream>>>(
+        packed, nchunks, splits, x, y, z, part_r, part_i, N);
+    int rc = launch_status("fhd_gather_kernel launch");
+    if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, N, rho_r, rho_i, stream);
+    const hipError_t f = hipFreeAsync(part, stream);
+    if (f != hipSuccess && rc == FHD_OK)
+        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
+    return rc;
 }
 
 int adjoint_gather_vox_per_lane() { return kVox; }

@@ -92,11 +92,13 @@ __device__ __forceinline__ void accumulate_voxels(const float4 *ch, const float 
     }
 }
 
+// Split s = blockIdx.y of `splits` takes its share of the voxel stream and
+// writes D (splits == 1) or its partial sums at out + s*M.
 template <int S>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void fhd_forward_gather_kernel(
-    const float *__restrict__ packed, int nchunks,
+    const float *__restrict__ packed, int nchunks, int splits,
     const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
-    float *__restrict__ Dr, float *__restrict__ Di, int M)
+    float *__restrict__ out_r, float *__restrict__ out_i, int M)
 {
     __shared__ float4 stage[2][kStageVec4];
     const float4 *src = reinterpret_cast<const float4 *>(packed);
@@ -126,21 +128,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     for (int j = 1; j < S; ++j) same_kz = same_kz && __float_as_uint(sz[j]) == __float_as_uint(sz[0]);
     const bool shared = __syncthreads_and(same_kz);
 
+    int c0, c1;
+    split_range(nchunks, splits, blockIdx.y, &c0, &c1);
     if (shared)
-        stream_chunks(src, nchunks, stage, [&](const float4 *ch) {
+        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
             accumulate_voxels<S, true>(ch, sx, sy, sz, acc_r, acc_i);
         });
     else
-        stream_chunks(src, nchunks, stage, [&](const float4 *ch) {
+        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
             accumulate_voxels<S, false>(ch, sx, sy, sz, acc_r, acc_i);
         });
 
+    float *dst_r = out_r + (int64_t)blockIdx.y * M, *dst_i = out_i + (int64_t)blockIdx.y * M;
 #pragma unroll
     for (int j = 0; j < S; ++j) {
         const int64_t m = m0 + j;
         if (m < M) {
-            Dr[m] = acc_r[j];
-            Di[m] = -acc_i[j];
+            dst_r[m] = acc_r[j];
+            dst_i[m] = -acc_i[j];
         }
     }
 }
@@ -165,9 +170,29 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
     const int nchunks = (int)(((int64_t)N + kChunk - 1) / kChunk);
     const int64_t per_block = (int64_t)kBlock * kSamp;
     const int64_t blocks = ((int64_t)M + per_block - 1) / per_block;
-    fhd_forward_gather_kernel<kSamp><<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
-        packed, nchunks, kx, ky, kz, Dr, Di, M);
-    return launch_status("fhd_forward_gather_kernel launch");
+    const int splits = split_count(blocks, nchunks);
+    if (splits == 1) {
+        fhd_forward_gather_kernel<kSamp><<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
+            packed, nchunks, 1, kx, ky, kz, Dr, Di, M);
+        return launch_status("fhd_forward_gather_kernel launch");
+    }
+    float *part = nullptr;
+    const hipError_t e = hipMallocAsync((void **)&part, (size_t)splits * 2 * M * sizeof(float), stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (split partials): ") +
+                                       hipGetErrorString(e));
+    }
+    float *part_r = part, *part_i = part + (int64_t)splits * M;
+    fhd_forward_gather_kernel<kSamp>
+        <<<dim3((unsigned)blocks, (unsigned)splits), dim3(kBlock), 0, stream>>>(
+            packed, nchunks, splits, kx, ky, kz, part_r, part_i, M);
+    int rc = launch_status("fhd_forward_gather_kernel launch");
+    if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, M, Dr, Di, stream);
+    const hipError_t f = hipFreeAsync(part, stream);
+    if (f != hipSuccess && rc == FHD_OK)
+        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
+    return rc;
 }
 
 }  // namespace fhd

@@ -75,13 +75,16 @@ __device__ __forceinline__ void load_chunk(const float4 *ch, float (&f)[kFields]
     }
 }
 
-// Streams the nchunks chunks of `src` through the workgroup's LDS stage
-// buffers and calls body(chunk) for each chunk in order, in every lane.
-// Every lane of the workgroup must call it (it holds workgroup barriers).
+// Streams chunks [c_begin, c_end) of `src` through the workgroup's LDS
+// stage buffers and calls body(chunk) for each chunk in order, in every
+// lane. Every lane of the workgroup must call it (it holds workgroup
+// barriers). Chunks past the end of `src` are never read.
 template <typename Body>
-__device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, int nchunks,
-                                              float4 (*stage)[kStageVec4], Body &&body)
+__device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, int c_begin,
+                                              int c_end, float4 (*stage)[kStageVec4], Body &&body)
 {
+    const int nchunks = c_end > c_begin ? c_end - c_begin : 0;
+    src += (int64_t)c_begin * kChunkVec4;
     const int64_t total_vec4 = (int64_t)nchunks * kChunkVec4;
     const int nstages = (nchunks + kStageChunks - 1) / kStageChunks;
     for (int i = threadIdx.x; i < kStageVec4 && i < total_vec4; i += kBlock) stage[0][i] = src[i];
@@ -114,6 +117,18 @@ __device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, in
     }
 }
 
+// Chunk range of split `s` when nchunks chunks are cut into `splits` parts
+// of whole stages.
+__device__ __forceinline__ void split_range(int nchunks, int splits, int s, int *c_begin,
+                                            int *c_end)
+{
+    const int stages = (nchunks + kStageChunks - 1) / kStageChunks;
+    const int per = (stages + splits - 1) / splits;   // stages per split
+    const int b = s * per * kStageChunks;
+    *c_begin = min(b, nchunks);
+    *c_end = min(b + per * kStageChunks, nchunks);
+}
+
 // ---------------------------------------------------------------------------
 // host side (abi_checks.hip)
 // ---------------------------------------------------------------------------
@@ -139,7 +154,20 @@ int check_device_spans(const Span *spans, int count);
 // FHD_ERR_HIP with `what` if the last launch failed.
 int launch_status(const char *what);
 
-// Kernel launches without argument checks (callers have checked).
+// How many parts to cut a stream of `nchunks` chunks into, for a gather
+// whose output needs `blocks` workgroups: enough for one full round of
+// resident workgroups (4 per CU at the gathers' occupancy), at least one
+// stage per part, never a second partial round.
+int split_count(int64_t blocks, int nchunks);
+
+// out[i] = sum_{s < splits} part[s*n + i] in increasing s, for the real
+// and the imaginary parts (stream-ordered launch, no checks).
+int launch_reduce(const float *part_r, const float *part_i, int splits, int64_t n, float *out_r,
+                  float *out_i, hipStream_t stream);
+
+// Kernel launches without argument checks (callers have checked). A gather
+// whose output is too small to fill the chip splits the stream, with a
+// stream-ordered partial-sum workspace it allocates and frees itself.
 // fhd.hip: adjoint F^H D
 int launch_pack(const float *kx, const float *ky, const float *kz, const float *Dr, const float *Di,
                 int M, float *packed, hipStream_t stream);

@@ -120,3 +120,45 @@ def fhd_subset(inputs: dict, voxels, threads: int | None = None):
     idx = np.asarray(voxels, dtype=np.int64)
     return fhd(inputs["kx"], inputs["ky"], inputs["kz"], inputs["Dr"], inputs["Di"],
                inputs["x"][idx], inputs["y"][idx], inputs["z"][idx], threads=threads)
+
+
+def cg(kx, ky, kz, Dr, Di, x, y, z, iters: int, tol: float = 0.0, threads: int | None = None):
+    """fp64 conjugate gradients on F^H F rho = F^H D from rho = 0.
+
+    The loop the page "Case study -- iterative MRI reconstruction" sketches
+    after section 17.3.6, without its unspecified regulariser, applied with
+    this module's own F^H (fhd) and F (forward). Inner products are
+    Re sum conj(u) v. Stops after `iters` iterations or once ||r||^2 < tol.
+    Returns (rho complex128, residuals list of ||r_k||^2 for k = 0..done).
+    """
+    X = (np.asarray(x, np.float64), np.asarray(y, np.float64), np.asarray(z, np.float64))
+    K = (np.asarray(kx, np.float64), np.asarray(ky, np.float64), np.asarray(kz, np.float64))
+
+    def normal_op(v):
+        fr, fi = forward(*K, v.real, v.imag, *X, threads=threads)
+        hr, hi = fhd(*K, fr, fi, *X, threads=threads)
+        return hr + 1j * hi
+
+    br, bi = fhd(*K, Dr, Di, *X, threads=threads)
+    r = br + 1j * bi
+    rho = np.zeros_like(r)
+    p = r.copy()
+    rs = float(np.vdot(r, r).real)
+    residuals = [rs]
+    for _ in range(iters):
+        if not rs > 0.0 or rs < tol:
+            break
+        ap = normal_op(p)
+        pap = float(np.vdot(p, ap).real)
+        if not pap > 0.0:
+            break
+        alpha = rs / pap
+        rho = rho + alpha * p
+        r = r - alpha * ap
+        rs_new = float(np.vdot(r, r).real)
+        residuals.append(rs_new)
+        if rs_new < tol:
+            break
+        p = r + (rs_new / rs) * p
+        rs = rs_new
+    return rho, residuals

@@ -27,6 +27,12 @@ def lib():
     lib.fhd_gather.argtypes = [vp, ctypes.c_int] + [vp] * 5 + [ctypes.c_int, vp]
     lib.fhd_packed_bytes.argtypes = [ctypes.c_int]
     lib.fhd_packed_bytes.restype = ctypes.c_int64
+    lib.fhd_cg.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                       vp, vp, vp]
+    lib.fhd_cg_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.fhd_cg_workspace_bytes.restype = ctypes.c_int64
+    lib.fhd_forward.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
+    lib.fhd_normal.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
     lib.fhd_last_error.restype = ctypes.c_char_p
     lib.fhd_status_string.restype = ctypes.c_char_p
     return lib
@@ -41,7 +47,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fhd_compute", "fhd_pack", "fhd_gather", "fhd_packed_bytes",
-              "fhd_status_string", "fhd_last_error", "fhd_gather_config"):
+              "fhd_status_string", "fhd_last_error", "fhd_gather_config",
+              "fhd_forward", "fhd_forward_pack", "fhd_forward_gather", "fhd_normal",
+              "fhd_cg", "fhd_cg_workspace_bytes"):
         assert n in names
 
 
@@ -136,3 +144,34 @@ def test_binding_fails_loudly_without_library(tmp_path):
     from non_cartesian_mri_fhd_amd import binding
     with pytest.raises(FileNotFoundError):
         binding.load(str(tmp_path / "libfhd.so"))
+
+
+def test_forward_and_normal_argument_checks(lib):
+    fake = [0x100000 * (i + 1) for i in range(10)]
+    assert lib.fhd_forward(*[None] * 10, -1, 3, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_forward(*[None] * 10, 0, 3, None) == FHD_OK          # no samples: nothing
+    args = list(fake)
+    args[8] = fake[6]                                                  # Dr aliases rho_r
+    assert lib.fhd_forward(*args, 16, 16, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_normal(*[None] * 10, 3, -1, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_normal(*[None] * 10, 3, 0, None) == FHD_OK          # no voxels: nothing
+    args = list(fake)
+    args[3] = None                                                     # x
+    assert lib.fhd_normal(*args, 16, 16, None) == FHD_ERR_INVALID_ARG
+
+
+def test_cg_argument_checks(lib):
+    done = ctypes.c_int(7)
+    fake = [0x100000 * (i + 1) for i in range(10)]
+    assert lib.fhd_cg(*fake, 16, 16, 3, 0.0, None, None, None) == FHD_ERR_INVALID_ARG
+    assert "iters_done" in _last(lib)
+    assert lib.fhd_cg(*fake, 16, 16, -1, 0.0, ctypes.addressof(done), None, None) == \
+        FHD_ERR_INVALID_ARG
+    assert lib.fhd_cg(*fake, 16, 16, 3, -1.0, ctypes.addressof(done), None, None) == \
+        FHD_ERR_INVALID_ARG
+    assert lib.fhd_cg(*fake, 16, 16, 3, float("nan"), ctypes.addressof(done), None, None) == \
+        FHD_ERR_INVALID_ARG
+    assert lib.fhd_cg(*[None] * 10, 16, 0, 3, 0.0, ctypes.addressof(done), None, None) == FHD_OK
+    assert done.value == 0
+    assert lib.fhd_cg_workspace_bytes(-1, 4) == -1
+    assert lib.fhd_cg_workspace_bytes(100, 1000) >= 6 * 4000 + 2 * 400

@@ -1,0 +1,79 @@
+"""GPU conjugate-gradient reconstruction (fhd_cg) against the oracle's fp64
+CG and the closed form on a full Cartesian grid."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from non_cartesian_mri_fhd_amd import binding, build, inputs, metrics
+
+from test_gpu_parity import check, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    build.ensure_built()
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def run(case, dev, iters, tol=0.0):
+    d = to_dev(case, dev)
+    rr, ri, done, res = binding.fhd_cg(d["kx"], d["ky"], d["kz"], d["Dr"], d["Di"],
+                                       d["x"], d["y"], d["z"], iters, tol)
+    torch.cuda.synchronize(dev)
+    return rr.cpu().numpy(), ri.cpu().numpy(), done, res
+
+
+def test_cg_one_step_recovers_image_on_full_grid(dev):
+    L = 16
+    kx, ky, kz = inputs.cartesian_kgrid(L)
+    x, y, z = inputs.grid_coords(L)
+    tr, ti = inputs.random_image(L ** 3, seed=71)
+    Dr, Di = oracle.forward(kx, ky, kz, tr, ti, x, y, z)
+    case = dict(kx=kx, ky=ky, kz=kz, Dr=Dr.astype(np.float32), Di=Di.astype(np.float32),
+                x=x, y=y, z=z)
+    rs0 = float(L ** 6 * np.sum(tr.astype(np.float64) ** 2 + ti.astype(np.float64) ** 2))
+    rr, ri, done, res = run(case, dev, iters=5, tol=1e-8 * rs0)
+    assert done == 1, res
+    check("cg full grid", rr, ri, tr.astype(np.float64), ti.astype(np.float64))
+
+
+def test_cg_matches_oracle_cg(dev):
+    L = 8
+    rng = np.random.default_rng(72)
+    M = 3000
+    k = rng.uniform(-3.5, 3.5, (3, M)).astype(np.float32)
+    D = rng.standard_normal((2, M)).astype(np.float32)
+    x, y, z = inputs.grid_coords(L)
+    case = dict(kx=k[0], ky=k[1], kz=k[2], Dr=D[0], Di=D[1], x=x, y=y, z=z)
+    iters = 6
+    rr, ri, done, res = run(case, dev, iters)
+    ref, ref_res = oracle.cg(k[0], k[1], k[2], D[0], D[1], x, y, z, iters=iters)
+    assert done == iters and len(ref_res) == iters + 1
+    check("cg vs oracle cg", rr, ri, ref.real, ref.imag)
+    assert np.allclose(res, ref_res, rtol=1e-3, atol=0), (res, ref_res)
+
+
+def test_cg_zero_iterations_and_repeatable(dev):
+    c = inputs.random_case(N=700, M=900, seed=73, kmax=4.0)
+    rr, ri, done, res = run(c, dev, iters=0)
+    assert done == 0 and np.all(rr == 0) and np.all(ri == 0) and len(res) == 1
+    bref = oracle.fhd(c["kx"], c["ky"], c["kz"], c["Dr"], c["Di"], c["x"], c["y"], c["z"])
+    assert abs(res[0] - np.sum(bref[0] ** 2 + bref[1] ** 2)) <= 1e-4 * res[0]
+    a = run(c, dev, iters=4)
+    b = run(c, dev, iters=4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2] == 4
+    assert np.array_equal(a[3], b[3])
+
+
+def test_cg_without_samples(dev):
+    c = inputs.random_case(N=50, M=4, seed=74)
+    d = to_dev(c, dev)
+    e = torch.empty(0, dtype=torch.float32, device=dev)
+    rr, ri, done, res = binding.fhd_cg(e, e, e, e, e, d["x"], d["y"], d["z"], 5, 0.0)
+    torch.cuda.synchronize(dev)
+    assert done == 0 and torch.count_nonzero(rr).item() == 0 and res[0] == 0
