@@ -11,12 +11,15 @@ event timing on the launch stream), the sampled parity against the fp64
 oracle and the oracle's own CPU throughput on that sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--op fhd|forward|normal|cg]
+                    [--op fhd|forward|normal|cg|grid]
 
 --op selects the operator timed (default fhd, the headline F^H D):
-forward = D = F rho; normal = F^H F rho (2 N M terms per step); cg = one
-conjugate-gradient iteration (F^H F plus two inner products and the vector
-updates; 2 N M terms per step).
+forward = D = F rho; normal = F^H F rho (2 N M terms per step); cg = a
+3-iteration conjugate-gradient reconstruction (F^H D, then per iteration
+F^H F, two inner products and the vector updates; 7 N M terms per step);
+grid = F^H D with the voxels on the workload's Cartesian grid, as a
+complex matrix product on the fp32 matrix cores (fhd_pack +
+fhd_grid_gather; N M terms per step, priced against the fp32 MFMA peak).
 """
 from __future__ import annotations
 
@@ -45,6 +48,10 @@ CUS, SIMDS_PER_CU, TRANS_LANES_PER_CYCLE, CLOCK_HZ = 256, 4, 8, 2.4e9
 P_FP32 = 157.3e12
 P_TRANS = CUS * SIMDS_PER_CU * TRANS_LANES_PER_CYCLE * CLOCK_HZ
 FLOP_PER_TERM = 13
+# the separable grid form: one complex multiply-add (4 real FMAs) per term
+# on the matrix cores, whose dense fp32 peak is 157.3 TFLOP/s
+MFMA_FLOP_PER_TERM = 8
+P_MFMA_FP32 = 157.3e12
 ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / 2)
 
 # HBM bytes per gather launch at 128^3 x 100k, from rocprofv3 FETCH_SIZE and
@@ -75,7 +82,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="spiral128")
-    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg"])
+    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -243,6 +250,17 @@ def bench_other(args) -> int:
             binding.fhd_normal(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], img[0], img[1],
                                qr, qi)
         terms_per_step = 2.0 * N * M
+    elif args.op == "grid":
+        L = inputs.WORKLOADS[args.workload].L
+        axis = inputs.grid_axis_of(L)
+        packed = binding.new_packed(M, dev)
+        rr = torch.empty(N, device=dev)
+        ri = torch.empty(N, device=dev)
+
+        def step():
+            binding.fhd_pack(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], packed)
+            binding.fhd_grid_gather(packed, M, (L, L, L), axis, rr, ri)
+        terms_per_step = float(N) * M
     else:
         rr = torch.empty(N, device=dev)
         ri = torch.empty(N, device=dev)
@@ -273,6 +291,12 @@ def bench_other(args) -> int:
                      "peak": FLOP_PER_TERM * ROOF_TERMS / 1e12, "unit": "TFLOP/s",
                      "frac": value / ROOF_TERMS, "traffic": None},
     }
+    if args.op == "grid":
+        # one complex multiply-add per term on the fp32 matrix cores
+        achieved = MFMA_FLOP_PER_TERM * value
+        out["roofline"] = {"bound": "mfma", "achieved": achieved / 1e12,
+                           "peak": P_MFMA_FP32 / 1e12, "unit": "TFLOP/s",
+                           "frac": achieved / P_MFMA_FP32, "traffic": None}
     print(json.dumps(out), flush=True)
     return 0
 

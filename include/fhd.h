@@ -168,6 +168,37 @@ int fhd_normal(const float *kx, const float *ky, const float *kz,
                float *q_r, float *q_i, int M, int N, void *stream);
 
 /*
+ * F^H D for voxels on a Cartesian grid, as a complex matrix product on the
+ * matrix cores (the exponential of section 17.3's F^H D equation factors
+ * over the axes). Voxel n = ix + nx*(iy + ny*iz) has coordinates
+ * (x0 + ix*dx, y0 + iy*dy, z0 + iz*dz), each computed in double and rounded
+ * once to fp32; with explicit coordinate arrays holding those values, the
+ * result equals fhd_compute's up to fp32 rounding.
+ *   kx, ky, kz, Dr, Di : M fp32 values each (read only)
+ *   nx, ny, nz >= 0    : grid size, nx*ny*nz < 2^31
+ *   axis               : HOST array of 6 floats {x0, dx, y0, dy, z0, dz},
+ *                        finite, read during the call
+ *   rho_r, rho_i       : nx*ny*nz fp32 values each (written), not
+ *                        overlapping any input
+ * Runs fhd_pack into a stream-ordered workspace, then fhd_grid_gather.
+ * M = 0 writes zeros; an empty grid does nothing.
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
+ */
+int fhd_compute_grid(const float *kx, const float *ky, const float *kz,
+                     const float *Dr, const float *Di, int M,
+                     int nx, int ny, int nz, const float *axis,
+                     float *rho_r, float *rho_i, void *stream);
+
+/*
+ * The matrix-core gather of fhd_compute_grid over k-space packed by
+ * fhd_pack (same M; 16-byte aligned). Same grid arguments and outputs.
+ * Repeated calls are bitwise identical. Errors: FHD_ERR_INVALID_ARG,
+ * FHD_ERR_ALLOC (split partial sums), FHD_ERR_HIP.
+ */
+int fhd_grid_gather(const void *packed, int M, int nx, int ny, int nz,
+                    const float *axis, float *rho_r, float *rho_i, void *stream);
+
+/*
  * Conjugate-gradient reconstruction (page "Case study -- iterative MRI
  * reconstruction", section 17.2 and its CG skeleton after section 17.3.6)
  * with the regulariser left out (the pages do not specify R or lambda):

@@ -73,6 +73,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_cg.restype = i32
     lib.fhd_cg_workspace_bytes.argtypes = [i32, i32]
     lib.fhd_cg_workspace_bytes.restype = i64
+    fpp = ctypes.POINTER(ctypes.c_float)
+    lib.fhd_compute_grid.argtypes = [fp] * 5 + [i32] * 4 + [fpp, fp, fp, vp]
+    lib.fhd_compute_grid.restype = i32
+    lib.fhd_grid_gather.argtypes = [vp] + [i32] * 4 + [fpp, fp, fp, vp]
+    lib.fhd_grid_gather.restype = i32
     lib.fhd_gather_config.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
     lib.fhd_gather_config.restype = None
     lib.fhd_status_string.argtypes = [i32]
@@ -272,6 +277,54 @@ def fhd_cg(kx, ky, kz, Dr, Di, x, y, z, max_iter: int, tol: float = 0.0,
         _check(lib, lib.fhd_cg(*ptrs, M, N, int(max_iter), float(tol), ctypes.byref(done),
                                res.ctypes.data, _stream(dev, stream)), "fhd_cg")
     return rho_r, rho_i, done.value, res[:done.value + 1].copy()
+
+
+def _axis(axis):
+    a = (ctypes.c_float * 6)(*[float(v) for v in axis])
+    if len(axis) != 6:
+        raise ValueError("axis must hold x0, dx, y0, dy, z0, dz")
+    return a
+
+
+def fhd_compute_grid(kx, ky, kz, Dr, Di, shape, axis, rho_r=None, rho_i=None, stream=None):
+    """F^H D on the grid shape = (nx, ny, nz), axis = (x0, dx, y0, dy, z0, dz);
+    voxel n = ix + nx*(iy + ny*iz). Returns (rho_r, rho_i) on kx's device."""
+    lib = load()
+    nx, ny, nz = (int(v) for v in shape)
+    M, N = kx.numel(), nx * ny * nz
+    dev = kx.device
+    if rho_r is None:
+        rho_r = torch.empty(N, dtype=torch.float32, device=dev)
+    if rho_i is None:
+        rho_i = torch.empty(N, dtype=torch.float32, device=dev)
+    ptrs = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"),
+                                               (Dr, "Dr"), (Di, "Di"))]
+    outs = [_vec(t, nm, N, dev) for t, nm in ((rho_r, "rho_r"), (rho_i, "rho_i"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_compute_grid(*ptrs, M, nx, ny, nz, _axis(axis), *outs,
+                                         _stream(dev, stream)), "fhd_compute_grid")
+    return rho_r, rho_i
+
+
+def fhd_grid_gather(packed, M: int, shape, axis, rho_r=None, rho_i=None, stream=None):
+    """Matrix-core gather over k-space packed by fhd_pack; see fhd_compute_grid."""
+    lib = load()
+    nx, ny, nz = (int(v) for v in shape)
+    N = nx * ny * nz
+    dev = packed.device
+    if rho_r is None:
+        rho_r = torch.empty(N, dtype=torch.float32, device=dev)
+    if rho_i is None:
+        rho_i = torch.empty(N, dtype=torch.float32, device=dev)
+    if packed.device.type != "cuda" or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous GPU tensor")
+    if packed.numel() * packed.element_size() < (fhd_packed_bytes(M) if M > 0 else 0):
+        raise ValueError("packed is smaller than fhd_packed_bytes(M)")
+    outs = [_vec(t, nm, N, dev) for t, nm in ((rho_r, "rho_r"), (rho_i, "rho_i"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_grid_gather(packed.data_ptr(), int(M), nx, ny, nz, _axis(axis),
+                                        *outs, _stream(dev, stream)), "fhd_grid_gather")
+    return rho_r, rho_i
 
 
 def new_packed(M: int, device) -> torch.Tensor:

@@ -97,7 +97,7 @@ int check_device_spans(const Span *spans, int count)
     return FHD_OK;
 }
 
-int split_count(int64_t blocks, int nchunks)
+int split_count(int64_t blocks, int nchunks, int per_cu)
 {
     static int cus_cached[64] = {0};
     int device = 0;
@@ -114,12 +114,26 @@ int split_count(int64_t blocks, int nchunks)
         }
         cus_cached[device] = cus;
     }
-    const int64_t resident = 4LL * cus_cached[device];
-    if (blocks <= 0 || blocks >= resident) return 1;
+    if (per_cu < 1) per_cu = 1;
+    const int64_t resident = (int64_t)per_cu * cus_cached[device];
     const int64_t stages = (nchunks + kStageChunks - 1) / kStageChunks;
-    int64_t splits = resident / blocks;
-    if (splits > stages) splits = stages;
-    return splits < 1 ? 1 : (int)splits;
+    if (blocks <= 0 || stages <= 1) return 1;
+    if (blocks < resident) {
+        int64_t splits = resident / blocks;
+        if (splits > stages) splits = stages;
+        return splits < 1 ? 1 : (int)splits;
+    }
+    // Enough workgroups for one round: split only where it evens out the
+    // last, partly filled round (up to 4 ways, and only for a gain of more
+    // than a tenth).
+    auto fill = [&](int64_t s) {
+        const int64_t n = blocks * s, rounds = (n + resident - 1) / resident;
+        return (double)n / (double)(rounds * resident);
+    };
+    int best = 1;
+    for (int64_t s = 2; s <= 4 && s <= stages; ++s)
+        if (fill(s) > 1.1 * fill(best)) best = (int)s;
+    return best;
 }
 
 namespace {

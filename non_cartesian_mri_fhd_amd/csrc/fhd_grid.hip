@@ -1,0 +1,264 @@
+// fhd_grid.hip -- F^H D on a Cartesian voxel grid as a complex GEMM on the
+// gfx950 matrix cores.
+//
+// rho_n = sum_m D_m exp(+i 2 pi k_m . x_n)   (page "Case study -- iterative
+// MRI reconstruction", section 17.3, F^H D equation) with the voxels on a
+// grid, x = x0 + ix dx, y = y0 + iy dy, z = z0 + iz dz, n = ix + nx (iy +
+// ny iz). The exponential factors, exp(i 2 pi k.x) = exp(i 2 pi kx x) *
+// exp(i 2 pi (ky y + kz z)), so with D_m = a_m exp(i 2 pi psi_m):
+//
+//     rho[(iy, iz), ix] = sum_m A[(iy, iz), m] B[m, ix]
+//     A[(iy, iz), m] = a_m exp(i 2 pi (ky_m y + kz_m z + psi_m))
+//     B[m, ix]       = exp(i 2 pi kx_m x)
+//
+// a complex (nyz x M) by (M x nx) product. Each term then costs one complex
+// multiply-add on the matrix cores (4 real v_mfma_f32_32x32x2_f32 per 2
+// samples and 32 x 32 outputs) instead of two transcendentals and ~3 FMAs
+// on the vector ALUs; the operands are generated on the fly from the packed
+// samples (fhd_pack's format), amortised over a 32 x 64 output tile per
+// wave: per lane and 2 samples, one A element (2 FMA, 2 transcendentals,
+// 3 multiplies) and two B elements (1 multiply, 2 transcendentals each)
+// feed 8 MFMAs. The voxel coordinates are the grid's, rounded once to fp32
+// from their double values. Rows and columns past the grid's edge are
+// computed like the others and never stored: in C = A B a row of A only
+// reaches its own row of C and a column of B its own column.
+//
+// v_mfma_f32_32x32x2_f32 operand layout (measured): lane l supplies
+// A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator register r of lane l
+// holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]. Both operands of a lane
+// therefore belong to the same sample, m0 + l / 32.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "fhd_internal.h"
+
+namespace fhd {
+namespace {
+
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+constexpr int kTileYZ = 32;           // A rows per wave
+constexpr int kTilesX = 2;            // 32-column B tiles per wave
+constexpr int kWaves = kBlock / 64;   // 4 waves per workgroup, stacked along yz
+
+struct GridAxis {
+    float x0, dx, y0, dy, z0, dz;
+};
+
+__device__ __forceinline__ float grid_coord(float c0, float d, int64_t i)
+{
+    return (float)((double)c0 + (double)i * (double)d);
+}
+
+// Workgroup b covers ix tile bx = b % tiles_x (64 columns) and yz rows
+// (b / tiles_x) * 128 .. + 127, one 32-row slab per wave; split s =
+// blockIdx.y takes its share of the sample stream.
+__global__ __launch_bounds__(kBlock) void fhd_grid_kernel(
+    const float *__restrict__ packed, int nchunks, int splits, int nx, int ny, int64_t nyz,
+    int tiles_x, GridAxis g, float *__restrict__ out_r, float *__restrict__ out_i)
+{
+    __shared__ float4 stage[2][kStageVec4];
+    const float4 *src = reinterpret_cast<const float4 *>(packed);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+
+    const int bx = blockIdx.x % tiles_x;
+    const int64_t yz0 = (int64_t)(blockIdx.x / tiles_x) * (kTileYZ * kWaves) + (int64_t)wave * kTileYZ;
+
+    // this lane's A row (yz) and B columns (ix)
+    const int64_t yz = yz0 + col;
+    const float ry = grid_coord(g.y0, g.dy, yz % ny);
+    const float rz = grid_coord(g.z0, g.dz, yz / ny);
+    float cx[kTilesX];
+#pragma unroll
+    for (int t = 0; t < kTilesX; ++t) cx[t] = grid_coord(g.x0, g.dx, bx * (32 * kTilesX) + 32 * t + col);
+
+    float16v acc_r[kTilesX], acc_i[kTilesX];
+#pragma unroll
+    for (int t = 0; t < kTilesX; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc_r[t][r] = 0.0f;
+            acc_i[t][r] = 0.0f;
+        }
+
+    int c0, c1;
+    split_range(nchunks, splits, blockIdx.y, &c0, &c1);
+    stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
+        const float *f = reinterpret_cast<const float *>(ch);
+        // 8 samples = 4 k-steps of 2; this lane's sample of step j is
+        // 2 j + half
+#pragma unroll
+        for (int j = 0; j < kChunk / 2; ++j) {
+            const int u = 2 * j + half;
+            const float skx = f[0 * kChunk + u], sky = f[1 * kChunk + u];
+            const float skz = f[2 * kChunk + u], psi = f[3 * kChunk + u];
+            const float amp = f[4 * kChunk + u];
+            // A element: a e^{i 2 pi (ky y + kz z + psi)}
+            const float q = __builtin_fmaf(sky, ry, __builtin_fmaf(skz, rz, psi));
+            const float a_r = amp * __builtin_amdgcn_cosf(q);
+            const float a_i = amp * __builtin_amdgcn_sinf(q);
+            const float na_i = -a_i;
+#pragma unroll
+            for (int t = 0; t < kTilesX; ++t) {
+                // B element: e^{i 2 pi kx x}
+                const float p = skx * cx[t];
+                const float b_r = __builtin_amdgcn_cosf(p);
+                const float b_i = __builtin_amdgcn_sinf(p);
+                // (a_r + i a_i)(b_r + i b_i)
+                acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a_r, b_r, acc_r[t], 0, 0, 0);
+                acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(na_i, b_i, acc_r[t], 0, 0, 0);
+                acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a_r, b_i, acc_i[t], 0, 0, 0);
+                acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a_i, b_r, acc_i[t], 0, 0, 0);
+            }
+        }
+    });
+
+    const int64_t N = nyz * nx;
+    float *dst_r = out_r + (int64_t)blockIdx.y * N, *dst_i = out_i + (int64_t)blockIdx.y * N;
+#pragma unroll
+    for (int t = 0; t < kTilesX; ++t) {
+        const int ix = bx * (32 * kTilesX) + 32 * t + col;
+        if (ix >= nx) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = yz0 + 8 * (r / 4) + 4 * half + (r % 4);
+            if (row < nyz) {
+                dst_r[row * nx + ix] = acc_r[t][r];
+                dst_i[row * nx + ix] = acc_i[t][r];
+            }
+        }
+    }
+}
+
+// Workgroups of fhd_grid_kernel that fit on one CU at once (its register
+// budget allows 3 waves per SIMD); asked of the runtime once per device.
+int grid_blocks_per_cu()
+{
+    static int cached[64] = {0};
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= 64) {
+        (void)hipGetLastError();
+        return 3;
+    }
+    if (cached[device] == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fhd_grid_kernel, kBlock, 0) != hipSuccess ||
+            n <= 0) {
+            (void)hipGetLastError();
+            n = 3;
+        }
+        cached[device] = n;
+    }
+    return cached[device];
+}
+
+}  // namespace
+
+int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const float *axis,
+                       float *rho_r, float *rho_i, hipStream_t stream)
+{
+    const int64_t nyz = (int64_t)ny * nz, N = nyz * nx;
+    if (N == 0) return FHD_OK;
+    const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
+    const int tiles_x = (nx + 32 * kTilesX - 1) / (32 * kTilesX);
+    const int64_t slabs = (nyz + kTileYZ * kWaves - 1) / (kTileYZ * kWaves);
+    const int64_t blocks = slabs * tiles_x;
+    const GridAxis g{axis[0], axis[1], axis[2], axis[3], axis[4], axis[5]};
+    const int splits = split_count(blocks, nchunks, grid_blocks_per_cu());
+    if (splits == 1) {
+        fhd_grid_kernel<<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
+            packed, nchunks, 1, nx, ny, nyz, tiles_x, g, rho_r, rho_i);
+        return launch_status("fhd_grid_kernel launch");
+    }
+    float *part = nullptr;
+    const hipError_t e = hipMallocAsync((void **)&part, (size_t)splits * 2 * N * sizeof(float), stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (split partials): ") +
+                                       hipGetErrorString(e));
+    }
+    float *part_r = part, *part_i = part + (int64_t)splits * N;
+    fhd_grid_kernel<<<dim3((unsigned)blocks, (unsigned)splits), dim3(kBlock), 0, stream>>>(
+        packed, nchunks, splits, nx, ny, nyz, tiles_x, g, part_r, part_i);
+    int rc = launch_status("fhd_grid_kernel launch");
+    if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, N, rho_r, rho_i, stream);
+    const hipError_t f = hipFreeAsync(part, stream);
+    if (f != hipSuccess && rc == FHD_OK)
+        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
+    return rc;
+}
+
+}  // namespace fhd
+
+using namespace fhd;
+
+namespace {
+int check_grid_args(int M, int nx, int ny, int nz, const float *axis, int64_t *N)
+{
+    if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
+    if (nx < 0 || ny < 0 || nz < 0) return fail(FHD_ERR_INVALID_ARG, "negative grid size");
+    const int64_t n = (int64_t)nx * ny * nz;
+    if (n > INT32_MAX) return fail(FHD_ERR_INVALID_ARG, "nx*ny*nz exceeds 2^31 - 1");
+    if (!axis) return fail(FHD_ERR_INVALID_ARG, "axis is NULL");
+    for (int i = 0; i < 6; ++i)
+        if (!std::isfinite(axis[i])) return fail(FHD_ERR_INVALID_ARG, "axis holds a non-finite value");
+    *N = n;
+    return FHD_OK;
+}
+}  // namespace
+
+extern "C" int fhd_grid_gather(const void *packed, int M, int nx, int ny, int nz, const float *axis,
+                               float *rho_r, float *rho_i, void *stream)
+{
+    clear_error();
+    int64_t N = 0;
+    int rc = check_grid_args(M, nx, ny, nz, axis, &N);
+    if (rc != FHD_OK || N == 0) return rc;
+    const int64_t nb = N * 4;
+    const Span all[] = {{packed, M > 0 ? packed_bytes_for(M) : 0, "packed", 16},
+                        {rho_r, nb, "rho_r"}, {rho_i, nb, "rho_i"}};
+    rc = check_host_side(all, 3);
+    if (rc == FHD_OK) rc = check_no_overlap(all, 3, 1);
+    if (rc == FHD_OK) rc = check_device_spans(all, 3);
+    if (rc != FHD_OK) return rc;
+    return launch_grid_gather((const float *)packed, M, nx, ny, nz, axis, rho_r, rho_i,
+                              (hipStream_t)stream);
+}
+
+extern "C" int fhd_compute_grid(const float *kx, const float *ky, const float *kz, const float *Dr,
+                                const float *Di, int M, int nx, int ny, int nz, const float *axis,
+                                float *rho_r, float *rho_i, void *stream)
+{
+    clear_error();
+    int64_t N = 0;
+    int rc = check_grid_args(M, nx, ny, nz, axis, &N);
+    if (rc != FHD_OK || N == 0) return rc;
+    const int64_t mb = (int64_t)M * 4, nb = N * 4;
+    const Span all[] = {{kx, mb, "kx"}, {ky, mb, "ky"}, {kz, mb, "kz"}, {Dr, mb, "Dr"},
+                        {Di, mb, "Di"}, {rho_r, nb, "rho_r"}, {rho_i, nb, "rho_i"}};
+    rc = check_host_side(all, 7);
+    if (rc == FHD_OK) rc = check_no_overlap(all, 7, 5);
+    if (rc == FHD_OK) rc = check_device_spans(all, 7);
+    if (rc != FHD_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    float *packed = nullptr;
+    if (M > 0) {
+        const hipError_t e = hipMallocAsync((void **)&packed, (size_t)packed_bytes_for(M), s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+        }
+        rc = launch_pack(kx, ky, kz, Dr, Di, M, packed, s);
+    }
+    if (rc == FHD_OK) rc = launch_grid_gather(packed, M, nx, ny, nz, axis, rho_r, rho_i, s);
+    if (packed) {
+        const hipError_t e = hipFreeAsync(packed, s);
+        if (e != hipSuccess && rc == FHD_OK)
+            rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
+    }
+    return rc;
+}

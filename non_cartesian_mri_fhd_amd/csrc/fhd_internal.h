@@ -155,10 +155,11 @@ int check_device_spans(const Span *spans, int count);
 int launch_status(const char *what);
 
 // How many parts to cut a stream of `nchunks` chunks into, for a gather
-// whose output needs `blocks` workgroups: enough for one full round of
-// resident workgroups (4 per CU at the gathers' occupancy), at least one
-// stage per part, never a second partial round.
-int split_count(int64_t blocks, int nchunks);
+// whose output needs `blocks` workgroups of which `per_cu` fit on a CU at
+// once: below one round, enough parts to fill it (at least one stage per
+// part); above, up to 4 parts where that evens out a partly filled last
+// round.
+int split_count(int64_t blocks, int nchunks, int per_cu = 4);
 
 // out[i] = sum_{s < splits} part[s*n + i] in increasing s, for the real
 // and the imaginary parts (stream-ordered launch, no checks).
@@ -178,5 +179,8 @@ int launch_forward_pack(const float *x, const float *y, const float *z, const fl
                         const float *rho_i, int N, float *packed, hipStream_t stream);
 int launch_forward_gather(const float *packed, int N, const float *kx, const float *ky,
                           const float *kz, float *Dr, float *Di, int M, hipStream_t stream);
+// fhd_grid.hip: F^H D on a Cartesian grid (axis = x0, dx, y0, dy, z0, dz)
+int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const float *axis,
+                       float *rho_r, float *rho_i, hipStream_t stream);
 
 }  // namespace fhd

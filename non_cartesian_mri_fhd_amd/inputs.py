@@ -91,6 +91,24 @@ def grid_coords(L: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
             np.ascontiguousarray(z.reshape(-1)))
 
 
+def grid_axis_of(L: int) -> tuple[float, ...]:
+    """(x0, dx, y0, dy, z0, dz) of the L^3 grid grid_coords(L) lays out."""
+    return (-0.5, 1.0 / L) * 3
+
+
+def coords_from_axis(nx: int, ny: int, nz: int, axis) -> tuple[np.ndarray, ...]:
+    """fp32 x, y, z of an nx x ny x nz grid given (x0, dx, y0, dy, z0, dz):
+    coordinate c0 + i d in double from the fp32 c0 and d, rounded once to
+    fp32; voxel n = ix + nx*(iy + ny*iz)."""
+    a = [float(np.float32(v)) for v in axis]
+    ax = (a[0] + np.arange(nx, dtype=np.float64) * a[1]).astype(F32)
+    ay = (a[2] + np.arange(ny, dtype=np.float64) * a[3]).astype(F32)
+    az = (a[4] + np.arange(nz, dtype=np.float64) * a[5]).astype(F32)
+    z, y, x = np.meshgrid(az, ay, ax, indexing="ij")
+    return (np.ascontiguousarray(x.reshape(-1)), np.ascontiguousarray(y.reshape(-1)),
+            np.ascontiguousarray(z.reshape(-1)))
+
+
 def grid_index(n: np.ndarray, L: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """(ix, iy, iz) of voxel indices n on an L^3 grid."""
     n = np.asarray(n, dtype=np.int64)

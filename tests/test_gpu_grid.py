@@ -1,0 +1,146 @@
+"""GPU parity of the matrix-core F^H D on a Cartesian voxel grid
+(fhd_compute_grid / fhd_grid_gather) against the fp64 oracle, the numpy FFT
+on a full integer k-grid, and the direct gather.
+
+The voxel coordinates handed to the oracle are the grid's, built as the
+library defines them (c0 + i d in double, rounded once to fp32). Same gate as
+the direct path: relative L2 <= 5e-4 and every element within 10x that bound
+times the reference's rms magnitude.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from non_cartesian_mri_fhd_amd import binding, build, inputs
+
+from pins import cartesian_fft_reference
+from test_gpu_parity import check
+
+pytestmark = pytest.mark.gpu
+
+ODD_AXIS = (0.3, 0.013, -0.2, 0.021, 0.11, -0.017)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    build.ensure_built()
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def t(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def gpu_grid(case, shape, axis, dev, out=None):
+    k = [t(case[a], dev) for a in ("kx", "ky", "kz", "Dr", "Di")]
+    rr, ri = binding.fhd_compute_grid(*k, shape, axis, *(out or (None, None)))
+    torch.cuda.synchronize(dev)
+    return rr.cpu().numpy(), ri.cpu().numpy()
+
+
+def oracle_on_grid(case, shape, axis, idx=None):
+    x, y, z = inputs.coords_from_axis(*shape, axis)
+    if idx is not None:
+        x, y, z = x[idx], y[idx], z[idx]
+    return oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"], x, y, z)
+
+
+@pytest.mark.parametrize("name", ["random16", "spiral32"])
+def test_grid_workload_all_voxels(dev, name):
+    w = inputs.make_workload(name)
+    L = inputs.WORKLOADS[name].L
+    rr, ri = gpu_grid(w, (L, L, L), inputs.grid_axis_of(L), dev)
+    ref = oracle.fhd(w["kx"], w["ky"], w["kz"], w["Dr"], w["Di"], w["x"], w["y"], w["z"])
+    check("grid " + name, rr, ri, *ref)
+
+
+@pytest.mark.parametrize("name,count", [("radial64", 8192), ("spiral128", 4096),
+                                        ("vdrandom256", inputs.SUBSET_SIZE)])
+def test_grid_workload_sampled_voxels(dev, name, count):
+    """Full-size run in the benchmark's launch shape; the oracle computes a
+    seeded voxel subset."""
+    w = inputs.make_workload(name)
+    L = inputs.WORKLOADS[name].L
+    rr, ri = gpu_grid(w, (L, L, L), inputs.grid_axis_of(L), dev)
+    if name == "vdrandom256":
+        idx = inputs.voxel_subset(w["N"])
+    else:
+        idx = inputs.voxel_subset(w["N"], count, seed=inputs.WORKLOADS[name].seed + 1000)
+    ref_r, ref_i = oracle.fhd_subset(w, idx)
+    check("grid " + name, rr[idx], ri[idx], ref_r, ref_i)
+
+
+@pytest.mark.parametrize("shape,M", [((1, 1, 1), 1), ((70, 5, 27), 1000), ((130, 3, 2), 7),
+                                     ((64, 128, 1), 4097), ((33, 17, 9), 513),
+                                     ((7, 129, 2), 2049), ((1, 300, 1), 64)])
+def test_grid_ragged(dev, shape, M):
+    """Grids whose edges cut the 64-column and 128-row tiles, sample counts
+    off the 8-sample chunk and 512-sample stage, non-dyadic axis steps of
+    either sign."""
+    c = inputs.random_case(1, M, seed=M + shape[0])
+    rr, ri = gpu_grid(c, shape, ODD_AXIS, dev)
+    check("grid ragged %s M=%d" % (shape, M), rr, ri, *oracle_on_grid(c, shape, ODD_AXIS))
+
+
+def test_grid_one_round_no_split(dev):
+    """768 workgroups and 2 stages: the unsplit launch (one full round)."""
+    shape, M = (64, 384, 256), 600
+    c = inputs.random_case(1, M, seed=77)
+    rr, ri = gpu_grid(c, shape, ODD_AXIS, dev)
+    idx = inputs.voxel_subset(int(np.prod(shape)), 2048, seed=78)
+    check("grid unsplit", rr[idx], ri[idx], *oracle_on_grid(c, shape, ODD_AXIS, idx))
+
+
+@pytest.mark.parametrize("L", [16, 32])
+def test_grid_cartesian_matches_fft(dev, L):
+    c = inputs.cartesian_case(L, seed=500 + L)
+    rr, ri = gpu_grid(c, (L, L, L), inputs.grid_axis_of(L), dev)
+    ref = cartesian_fft_reference(c)
+    check("grid cartesian L=%d" % L, rr, ri, ref.real, ref.imag)
+
+
+def test_grid_no_samples_writes_zeros(dev):
+    shape = (40, 9, 3)
+    N = int(np.prod(shape))
+    out = (torch.full((N,), 7.0, device=dev), torch.full((N,), -7.0, device=dev))
+    e = np.zeros(0, np.float32)
+    case = dict(kx=e, ky=e, kz=e, Dr=e, Di=e)
+    rr, ri = gpu_grid(case, shape, ODD_AXIS, dev, out)
+    assert not rr.any() and not ri.any()
+
+
+def test_grid_empty_grid(dev):
+    c = inputs.random_case(1, 64, seed=5)
+    for shape in ((0, 2, 2), (3, 0, 5), (4, 4, 0)):
+        rr, ri = gpu_grid(c, shape, ODD_AXIS, dev)
+        assert rr.shape == (0,) and ri.shape == (0,)
+
+
+def test_grid_repeatable_and_two_stage_equal(dev):
+    w = inputs.make_workload("spiral32")
+    L = inputs.WORKLOADS["spiral32"].L
+    axis = inputs.grid_axis_of(L)
+    a = gpu_grid(w, (L, L, L), axis, dev)
+    b = gpu_grid(w, (L, L, L), axis, dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    k = [t(w[n], dev) for n in ("kx", "ky", "kz", "Dr", "Di")]
+    packed = binding.new_packed(w["M"], dev)
+    binding.fhd_pack(*k, packed)
+    rr, ri = binding.fhd_grid_gather(packed, w["M"], (L, L, L), axis)
+    torch.cuda.synchronize(dev)
+    assert np.array_equal(rr.cpu().numpy(), a[0]) and np.array_equal(ri.cpu().numpy(), a[1])
+
+
+def test_grid_agrees_with_direct_gather(dev):
+    shape = (70, 5, 27)
+    c = inputs.random_case(1, 3000, seed=91)
+    x, y, z = inputs.coords_from_axis(*shape, ODD_AXIS)
+    k = [t(c[n], dev) for n in ("kx", "ky", "kz", "Dr", "Di")]
+    dr, di = binding.fhd_compute(*k, t(x, dev), t(y, dev), t(z, dev))
+    gr, gi = binding.fhd_compute_grid(*k, shape, ODD_AXIS)
+    torch.cuda.synchronize(dev)
+    check("grid vs direct", gr.cpu().numpy(), gi.cpu().numpy(),
+          dr.cpu().numpy().astype(np.float64), di.cpu().numpy().astype(np.float64))

@@ -105,3 +105,14 @@ def test_cartesian_case():
     c = inputs.cartesian_case(4, seed=0)
     assert c["M"] == c["N"] == 64
     assert set(np.unique(c["kx"]).tolist()) == {-2.0, -1.0, 0.0, 1.0}
+
+
+def test_coords_from_axis_matches_grid_coords():
+    for L in (4, 16, 32):
+        got = inputs.coords_from_axis(L, L, L, inputs.grid_axis_of(L))
+        for a, b in zip(got, inputs.grid_coords(L)):
+            assert np.array_equal(a, b)
+    x, y, z = inputs.coords_from_axis(3, 2, 2, (0.25, 0.5, -1.0, 2.0, 4.0, -0.125))
+    assert x.tolist() == [0.25, 0.75, 1.25] * 4
+    assert y.tolist() == [-1.0] * 3 + [1.0] * 3 + [-1.0] * 3 + [1.0] * 3
+    assert z.tolist() == [4.0] * 6 + [3.875] * 6
