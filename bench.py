@@ -54,26 +54,36 @@ MFMA_FLOP_PER_TERM = 8
 P_MFMA_FP32 = 157.3e12
 ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / 2)
 
-# HBM bytes per gather launch at 128^3 x 100k, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE passes scaled by a 1 GiB copy's readings (factors 2.0 and 1.0):
-# 40.3 MiB read + 16.0 MiB written. Valid only for the kernel source they
-# were taken on (its SHA-256 below); any later edit reports null until the
-# counters are taken again.
+# HBM bytes per launch of each operator's dominant kernel at 128^3 x 100k,
+# from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by a 1 GiB copy's
+# readings (factors 2.0 and 1.0). Valid only for the sources they were taken
+# on (SHA-256 over the listed files, in order); any later edit reports null
+# until the counters are taken again.
+#   fhd  (fhd_gather_kernel): 39.4 MiB read (x, y, z and the packed samples
+#        once per XCD L2) + 16.0 MiB written (rho)
+#   grid (fhd_grid_kernel):   15.4 MiB read (packed samples once per XCD L2)
+#        + 48.0 MiB written (3 split partial sums of rho)
+CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
-    "workload": "spiral128",
-    "kernel_source_sha256": "54a44be2b4904c33c7c2f2752d8c38a1c00c29f4752efb1a145e000598a75fe3",
-    "bytes_per_launch": (20150 * 2.0 + 16384 * 1.0) * 1024,
+    "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
+            "sha256": "286ee91accce82c6e8dd770012e75c744090a233e5e0524d17a8be8113482122",
+            "bytes_per_launch": (20156.5 * 2.0 + 16384 * 1.0) * 1024},
+    "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
+             "sha256": "0a8ad465bb80819b79ba4384d16fd32ac84a1c79f953e5f75d8d4edbe53a2d60",
+             "bytes_per_launch": (7875.5 * 2.0 + 49152 * 1.0) * 1024},
 }
-KERNEL_SOURCE = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc", "fhd.hip")
 
 
-def measured_traffic(workload: str):
+def measured_traffic(op: str, workload: str):
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if workload != TRAFFIC["workload"] or sha != TRAFFIC["kernel_source_sha256"]:
+    entry = TRAFFIC.get(op)
+    if entry is None or workload != entry["workload"]:
         return None
-    return TRAFFIC["bytes_per_launch"]
+    h = hashlib.sha256()
+    for name in entry["sources"]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return entry["bytes_per_launch"] if h.hexdigest() == entry["sha256"] else None
 
 
 def parse(argv=None):
@@ -207,7 +217,7 @@ def main(argv=None) -> int:
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic("fhd", args.workload),
         },
         "kernel_ms": {"fhd_gather_kernel": gather_ms, "fhd_pack_kernel": pack_ms},
         "gflops_13_per_term": FLOP_PER_TERM * value / 1e9,
@@ -296,7 +306,8 @@ def bench_other(args) -> int:
         achieved = MFMA_FLOP_PER_TERM * value
         out["roofline"] = {"bound": "mfma", "achieved": achieved / 1e12,
                            "peak": P_MFMA_FP32 / 1e12, "unit": "TFLOP/s",
-                           "frac": achieved / P_MFMA_FP32, "traffic": None}
+                           "frac": achieved / P_MFMA_FP32,
+                           "traffic": measured_traffic("grid", args.workload)}
     print(json.dumps(out), flush=True)
     return 0
 
