@@ -185,7 +185,8 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - t0
 
     ms_step = wall * 1e3 / args.steps
-    gather_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    gather_all = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    gather_ms = float(np.mean(gather_all))
     pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     terms = float(N) * float(M)
     value = terms / (ms_step * 1e-3)
@@ -219,7 +220,9 @@ def main(argv=None) -> int:
             "frac": achieved / peak,
             "traffic": measured_traffic("fhd", args.workload),
         },
-        "kernel_ms": {"fhd_gather_kernel": gather_ms, "fhd_pack_kernel": pack_ms},
+        "kernel_ms": {"fhd_gather_kernel": gather_ms, "fhd_pack_kernel": pack_ms,
+                      "fhd_gather_kernel_median": float(np.median(gather_all)),
+                      "fhd_gather_kernel_min": float(np.min(gather_all))},
         "gflops_13_per_term": FLOP_PER_TERM * value / 1e9,
     }
     if not args.no_cpu_baseline:
@@ -231,8 +234,36 @@ def main(argv=None) -> int:
     return 0
 
 
+def oracle_forward_sample(w: dict, name: str, target_s: float, Dr, Di, img):
+    """Time the fp64 oracle's F on a seeded subset of the samples (all
+    voxels each) and compare the GPU's D on those samples."""
+    import oracle
+    from non_cartesian_mri_fhd_amd import inputs, metrics
+    threads = oracle.default_threads()
+    N, M = w["N"], w["M"]
+    probe = inputs.voxel_subset(M, 16, seed=4243)
+    t0 = time.perf_counter()
+    oracle.forward(w["kx"][probe], w["ky"][probe], w["kz"][probe], img[0], img[1],
+                   w["x"], w["y"], w["z"], threads=threads)
+    rate = probe.size * N / (time.perf_counter() - t0)
+    count = int(np.clip(target_s * rate / N, 64, min(M, 65536)))
+    seed = inputs.WORKLOADS[name].seed + 3000 if name in inputs.WORKLOADS else 3000
+    idx = inputs.voxel_subset(M, count, seed=seed)
+    t0 = time.perf_counter()
+    ref_r, ref_i = oracle.forward(w["kx"][idx], w["ky"][idx], w["kz"][idx], img[0], img[1],
+                                  w["x"], w["y"], w["z"], threads=threads)
+    dt = time.perf_counter() - t0
+    parity = dict(samples=int(idx.size), rel_l2=metrics.rel_l2(Dr[idx], Di[idx], ref_r, ref_i),
+                  psnr_db=metrics.psnr_db(Dr[idx], Di[idx], ref_r, ref_i), tolerance=5e-4)
+    base = dict(value=idx.size * N / dt, unit="terms/s", cores=threads, kind="oracle",
+                sample="%d seeded samples x all %d voxels of %s (%.1f s, fp64, %s)"
+                       % (idx.size, N, name, dt, cpu_model()))
+    return base, parity
+
+
 def bench_other(args) -> int:
-    """Times F, F^H F or one CG iteration on the workload (one JSON line)."""
+    """Times F, F^H F, a CG reconstruction or the grid form of F^H D on the
+    workload (one JSON line)."""
     import torch
     from non_cartesian_mri_fhd_amd import binding, build, inputs
     build.ensure_built()
@@ -240,26 +271,27 @@ def bench_other(args) -> int:
     assert torch.cuda.is_available(), "no GPU visible"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
     w = inputs.make_workload(args.workload)
     N, M = w["N"], w["M"]
     t = {k: torch.from_numpy(w[k]).to(dev) for k in ("kx", "ky", "kz", "Dr", "Di", "x", "y", "z")}
-    img = [torch.from_numpy(a).to(dev) for a in inputs.random_image(N, seed=77)]
+    img_np = inputs.random_image(N, seed=77)
+    img = [torch.from_numpy(a).to(dev) for a in img_np]
+    # step(): the whole operator; timed(): the same with HIP events on the
+    # launch stream around its dominant kernel (None where one call covers it)
+    dominant = None
     if args.op == "forward":
         Dr = torch.empty(M, device=dev)
         Di = torch.empty(M, device=dev)
+        vox = binding.new_packed(N, dev)
 
-        def step():
-            binding.fhd_forward(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], img[0], img[1],
-                                Dr, Di)
+        def pre():
+            binding.fhd_forward_pack(t["x"], t["y"], t["z"], img[0], img[1], vox)
+
+        def main_kernel():
+            binding.fhd_forward_gather(vox, N, t["kx"], t["ky"], t["kz"], Dr, Di)
+        dominant = "fhd_forward_gather_kernel"
         terms_per_step = float(N) * M
-    elif args.op == "normal":
-        qr = torch.empty(N, device=dev)
-        qi = torch.empty(N, device=dev)
-
-        def step():
-            binding.fhd_normal(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], img[0], img[1],
-                               qr, qi)
-        terms_per_step = 2.0 * N * M
     elif args.op == "grid":
         L = inputs.WORKLOADS[args.workload].L
         axis = inputs.grid_axis_of(L)
@@ -267,29 +299,53 @@ def bench_other(args) -> int:
         rr = torch.empty(N, device=dev)
         ri = torch.empty(N, device=dev)
 
-        def step():
+        def pre():
             binding.fhd_pack(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], packed)
+
+        def main_kernel():
             binding.fhd_grid_gather(packed, M, (L, L, L), axis, rr, ri)
+        dominant = "fhd_grid_kernel + reduce_splits_kernel"
         terms_per_step = float(N) * M
+    elif args.op == "normal":
+        qr = torch.empty(N, device=dev)
+        qi = torch.empty(N, device=dev)
+
+        def pre():
+            pass
+
+        def main_kernel():
+            binding.fhd_normal(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], img[0], img[1],
+                               qr, qi)
+        terms_per_step = 2.0 * N * M
     else:
         rr = torch.empty(N, device=dev)
         ri = torch.empty(N, device=dev)
         k_iters = 3
 
-        def step():
+        def pre():
+            pass
+
+        def main_kernel():
             binding.fhd_cg(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], t["x"], t["y"], t["z"],
                            k_iters, 0.0, rr, ri)
         # F^H D once plus k_iters applications of F^H F
         terms_per_step = float(N) * M * (1 + 2 * k_iters)
     for _ in range(args.warmup):
-        step()
+        pre()
+        main_kernel()
     torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for e in ev:
+        pre()
+        e[0].record(stream)
+        main_kernel()
+        e[1].record(stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     value = terms_per_step / (ms * 1e-3)
+    k_rate = terms_per_step / (float(np.mean(kms)) * 1e-3)
     out = {
         "metric": "%s voxel-sample terms/s (%s)" % (args.op, args.workload),
         "value": value, "unit": "terms/s", "n_gpus": 1, "steps": args.steps,
@@ -297,17 +353,44 @@ def bench_other(args) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "op": args.op, "N": N, "M": M,
                    "terms_per_step": terms_per_step},
-        "roofline": {"bound": "alu", "achieved": FLOP_PER_TERM * value / 1e12,
+        "roofline": {"bound": "alu", "achieved": FLOP_PER_TERM * k_rate / 1e12,
                      "peak": FLOP_PER_TERM * ROOF_TERMS / 1e12, "unit": "TFLOP/s",
-                     "frac": value / ROOF_TERMS, "traffic": None},
+                     "frac": k_rate / ROOF_TERMS, "traffic": None},
+        "kernel_ms": {"timed": dominant or "whole call", "mean": float(np.mean(kms)),
+                      "median": float(np.median(kms)), "min": float(np.min(kms))},
     }
     if args.op == "grid":
         # one complex multiply-add per term on the fp32 matrix cores
-        achieved = MFMA_FLOP_PER_TERM * value
+        achieved = MFMA_FLOP_PER_TERM * k_rate
         out["roofline"] = {"bound": "mfma", "achieved": achieved / 1e12,
                            "peak": P_MFMA_FP32 / 1e12, "unit": "TFLOP/s",
                            "frac": achieved / P_MFMA_FP32,
                            "traffic": measured_traffic("grid", args.workload)}
+    if not args.no_cpu_baseline:
+        if args.op == "grid":
+            base, parity = cpu_baseline(w, args.workload, args.cpu_seconds,
+                                        rr.cpu().numpy(), ri.cpu().numpy())
+        elif args.op == "forward":
+            base, parity = oracle_forward_sample(w, args.workload, args.cpu_seconds,
+                                                 Dr.cpu().numpy(), Di.cpu().numpy(), img_np)
+        else:
+            # F^H F and CG run F then F^H: the oracle's rate for one term of
+            # each, timed on bounded samples, gives its rate per term here
+            half = args.cpu_seconds / 2
+            g = binding.fhd_compute(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"],
+                                    t["x"], t["y"], t["z"])
+            b_adj, parity = cpu_baseline(w, args.workload, half,
+                                         g[0].cpu().numpy(), g[1].cpu().numpy())
+            Dr_, Di_ = binding.fhd_forward(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"],
+                                           img[0], img[1])
+            b_fwd, _ = oracle_forward_sample(w, args.workload, half, Dr_.cpu().numpy(),
+                                             Di_.cpu().numpy(), img_np)
+            rate = 2.0 / (1.0 / b_adj["value"] + 1.0 / b_fwd["value"])
+            base = dict(value=rate, unit="terms/s", cores=b_adj["cores"], kind="oracle",
+                        sample="F^H: %s; F: %s" % (b_adj["sample"], b_fwd["sample"]))
+            parity = {"F^H D": parity}
+        out["cpu_baseline"] = base
+        out["parity"] = parity
     print(json.dumps(out), flush=True)
     return 0
 

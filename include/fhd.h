@@ -204,8 +204,10 @@ int fhd_grid_gather(const void *packed, int M, int nx, int ny, int nz,
  * with the regulariser left out (the pages do not specify R or lambda):
  * solves F^H F rho = F^H D from rho = 0. Each iteration applies F^H F once
  * (fhd_normal) and two inner products (fp64 accumulation, fixed reduction
- * order: bitwise repeatable). As on the pages, the inner products return to
- * the host every iteration, so this call synchronises `stream` and blocks
+ * order: bitwise repeatable). The CG scalars stay in device memory: an
+ * iteration is enqueued with no host round trip, the host checks the stop
+ * flag once per 8 iterations, and reads the iteration count and residual
+ * history back at the end, so this call synchronises `stream` and blocks
  * the calling thread.
  *   kx, ky, kz, Dr, Di : M fp32 values each (read only)
  *   x, y, z            : N fp32 values each (read only)
@@ -217,8 +219,8 @@ int fhd_grid_gather(const void *packed, int M, int nx, int ny, int nz,
  *   iters_done         : host int, set to the iterations run
  *   residuals          : host array of max_iter + 1 floats or NULL; entry k
  *                        is ||r_k||^2 (entry 0 is ||F^H D||^2)
- * The workspace of fhd_cg_workspace_bytes(M, N) bytes is allocated and
- * freed on `stream`. Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
+ * The workspace of fhd_cg_workspace_bytes(M, N, max_iter) bytes is
+ * allocated and freed on `stream`. Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
  */
 int fhd_cg(const float *kx, const float *ky, const float *kz,
            const float *Dr, const float *Di,
@@ -226,9 +228,9 @@ int fhd_cg(const float *kx, const float *ky, const float *kz,
            float *rho_r, float *rho_i, int M, int N, int max_iter, float tol,
            int *iters_done, float *residuals, void *stream);
 
-/* Workspace bytes fhd_cg allocates for M samples and N voxels (-1 if
- * either is negative). */
-int64_t fhd_cg_workspace_bytes(int M, int N);
+/* Workspace bytes fhd_cg allocates for M samples, N voxels and max_iter
+ * iterations (-1 if any is negative). */
+int64_t fhd_cg_workspace_bytes(int M, int N, int max_iter);
 
 /*
  * Launch shape of the gather kernel: voxels per lane, samples per packed

@@ -71,7 +71,7 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_cg.argtypes = [fp] * 10 + [i32, i32, i32, ctypes.c_float,
                                        ctypes.POINTER(ctypes.c_int), ctypes.c_void_p, vp]
     lib.fhd_cg.restype = i32
-    lib.fhd_cg_workspace_bytes.argtypes = [i32, i32]
+    lib.fhd_cg_workspace_bytes.argtypes = [i32, i32, i32]
     lib.fhd_cg_workspace_bytes.restype = i64
     fpp = ctypes.POINTER(ctypes.c_float)
     lib.fhd_compute_grid.argtypes = [fp] * 5 + [i32] * 4 + [fpp, fp, fp, vp]

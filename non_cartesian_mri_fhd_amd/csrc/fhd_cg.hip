@@ -14,9 +14,13 @@
 // Vectors are complex fp32 (separate real and imaginary arrays); inner
 // products are Re sum conj(u) v accumulated in fp64 by a two-stage
 // reduction with a fixed order (per-block partials, then one block), so
-// every run is bitwise repeatable. As on the pages, the scalars come back
-// to the host each iteration (two 8-byte reads), which decides the early
-// stop; F^H F dominates the iteration by orders of magnitude.
+// every run is bitwise repeatable. The scalars (rs, <p, Ap>, alpha, beta,
+// the iteration count and the residual history) live in device memory and
+// are produced and consumed by kernels, so an iteration is a fixed launch
+// sequence with no host round trip. Once the stopping rule fires, a device
+// flag turns the remaining updates into no-ops; the host looks at that flag
+// only between batches of kBatch iterations (skipping batches that would do
+// nothing) and reads the count and history back once at the end.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -51,11 +55,28 @@ __global__ __launch_bounds__(kVecBlock) void dot_partial_kernel(
     if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
 }
 
-// out[0] = sum of partial[0 .. count) in a fixed order
+// Device-resident CG scalars. `active` is 1 while iterating; the kernels of
+// an iteration do nothing once it is 0.
+struct CgState {
+    double rs;        // ||r||^2 of the current residual
+    double pap;       // <p, Ap>
+    float alpha, beta;
+    int active;
+    int iters;        // iterations completed
+};
+
+// Stage 2 of the inner products: sum the partials in a fixed order, then
+// thread 0 applies one step of the CG scalar logic.
+enum class DotUse { kStart, kAlpha, kResidual };
+
+template <DotUse USE>
 __global__ __launch_bounds__(kVecBlock) void dot_final_kernel(const double *__restrict__ partial,
-                                                              int count, double *__restrict__ out)
+                                                              int count, CgState *st,
+                                                              double *__restrict__ history,
+                                                              int max_iter, float tol)
 {
     __shared__ double red[kVecBlock];
+    if (USE != DotUse::kStart && !st->active) return;
     double acc = 0.0;
     for (int i = threadIdx.x; i < count; i += kVecBlock) acc += partial[i];
     red[threadIdx.x] = acc;
@@ -64,15 +85,42 @@ __global__ __launch_bounds__(kVecBlock) void dot_final_kernel(const double *__re
         if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
-    if (threadIdx.x == 0) out[0] = red[0];
+    if (threadIdx.x != 0) return;
+    const double v = red[0];
+    if (USE == DotUse::kStart) {
+        // rs_0 = ||F^H D||^2; iterate unless it is already small enough or zero
+        st->rs = v;
+        st->iters = 0;
+        history[0] = v;
+        st->active = (max_iter > 0 && !(v < (double)tol) && v > 0.0) ? 1 : 0;
+    } else if (USE == DotUse::kAlpha) {
+        st->pap = v;
+        if (v > 0.0) {
+            st->alpha = (float)(st->rs / v);
+        } else {
+            st->active = 0;   // p lies in the null space of F: nothing left to do
+        }
+    } else {
+        const int k = st->iters + 1;
+        st->iters = k;
+        history[k] = v;
+        if (v < (double)tol || !(v > 0.0) || k >= max_iter) {
+            st->active = 0;
+        } else {
+            st->beta = (float)(v / st->rs);
+            st->rs = v;
+        }
+    }
 }
 
 // rho += alpha p;  r -= alpha Ap
 __global__ __launch_bounds__(kVecBlock) void cg_step_kernel(
     float *__restrict__ rho_r, float *__restrict__ rho_i, float *__restrict__ r_r,
     float *__restrict__ r_i, const float *__restrict__ p_r, const float *__restrict__ p_i,
-    const float *__restrict__ ap_r, const float *__restrict__ ap_i, float alpha, int64_t n)
+    const float *__restrict__ ap_r, const float *__restrict__ ap_i, const CgState *st, int64_t n)
 {
+    if (!st->active) return;
+    const float alpha = st->alpha;
     const int64_t i = (int64_t)blockIdx.x * kVecBlock + threadIdx.x;
     if (i >= n) return;
     rho_r[i] = __builtin_fmaf(alpha, p_r[i], rho_r[i]);
@@ -84,8 +132,10 @@ __global__ __launch_bounds__(kVecBlock) void cg_step_kernel(
 // p = r + beta p
 __global__ __launch_bounds__(kVecBlock) void cg_direction_kernel(
     float *__restrict__ p_r, float *__restrict__ p_i, const float *__restrict__ r_r,
-    const float *__restrict__ r_i, float beta, int64_t n)
+    const float *__restrict__ r_i, const CgState *st, int64_t n)
 {
+    if (!st->active) return;
+    const float beta = st->beta;
     const int64_t i = (int64_t)blockIdx.x * kVecBlock + threadIdx.x;
     if (i >= n) return;
     p_r[i] = __builtin_fmaf(beta, p_r[i], r_r[i]);
@@ -108,25 +158,26 @@ __global__ __launch_bounds__(kVecBlock) void cg_start_kernel(
 
 unsigned vec_blocks(int64_t n) { return (unsigned)((n + kVecBlock - 1) / kVecBlock); }
 
+constexpr int kBatch = 8;   // iterations enqueued between looks at the stop flag
+
 struct CgWork {
     float *r_r, *r_i, *p_r, *p_i, *ap_r, *ap_i;   // N each
     float *vox, *smp, *d_r, *d_i;                 // normal-operator temporaries
-    double *partial, *scalar;
+    double *partial;                              // kDotBlocks
+    CgState *state;
+    double *history;                              // max_iter + 1
 };
 
-// <u, v> into host `out` (synchronises the stream)
+// <u, v>, consumed on the device by dot_final_kernel<USE>
+template <DotUse USE>
 int dot(const float *ur, const float *ui, const float *vr, const float *vi, int64_t n,
-        const CgWork &w, hipStream_t s, double *out)
+        const CgWork &w, int max_iter, float tol, hipStream_t s)
 {
     const int blocks = (int)std::min<int64_t>(kDotBlocks, std::max<int64_t>(1, vec_blocks(n)));
     dot_partial_kernel<<<blocks, kVecBlock, 0, s>>>(ur, ui, vr, vi, n, w.partial);
-    dot_final_kernel<<<1, kVecBlock, 0, s>>>(w.partial, blocks, w.scalar);
-    int rc = launch_status("dot kernels launch");
-    if (rc != FHD_OK) return rc;
-    hipError_t e = hipMemcpyAsync(out, w.scalar, sizeof(double), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return fail(FHD_ERR_HIP, std::string("dot readback: ") + hipGetErrorString(e));
-    return FHD_OK;
+    dot_final_kernel<USE><<<1, kVecBlock, 0, s>>>(w.partial, blocks, w.state, w.history, max_iter,
+                                                  tol);
+    return launch_status("dot kernels launch");
 }
 
 // Ap = F^H F p
@@ -140,45 +191,56 @@ int normal(const float *kx, const float *ky, const float *kz, const float *x, co
     return rc;
 }
 
+int read_back(void *dst, const void *src, size_t bytes, hipStream_t s)
+{
+    hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(FHD_ERR_HIP, std::string("CG readback: ") + hipGetErrorString(e));
+    return FHD_OK;
+}
+
 int run_cg(const float *kx, const float *ky, const float *kz, const float *Dr, const float *Di,
            const float *x, const float *y, const float *z, float *rho_r, float *rho_i, int M, int N,
            int max_iter, float tol, int *iters_done, float *residuals, const CgWork &w,
            hipStream_t s)
 {
     const int64_t n = N;
-    // b = F^H D into r; rho = 0; p = r
+    // b = F^H D into r; rho = 0; p = r; rs = <r, r>
     int rc = launch_pack(kx, ky, kz, Dr, Di, M, w.smp, s);
     if (rc == FHD_OK) rc = launch_gather(w.smp, M, x, y, z, w.r_r, w.r_i, N, s);
     if (rc != FHD_OK) return rc;
     cg_start_kernel<<<vec_blocks(n), kVecBlock, 0, s>>>(rho_r, rho_i, w.p_r, w.p_i, w.r_r, w.r_i, n);
     if ((rc = launch_status("cg_start_kernel launch")) != FHD_OK) return rc;
-    double rs = 0.0;
-    if ((rc = dot(w.r_r, w.r_i, w.r_r, w.r_i, n, w, s, &rs)) != FHD_OK) return rc;
-    if (residuals) residuals[0] = (float)rs;
-    int it = 0;
-    while (it < max_iter && !(rs < (double)tol) && rs > 0.0) {
-        if ((rc = normal(kx, ky, kz, x, y, z, M, N, w, s)) != FHD_OK) return rc;
-        double pap = 0.0;
-        if ((rc = dot(w.p_r, w.p_i, w.ap_r, w.ap_i, n, w, s, &pap)) != FHD_OK) return rc;
-        if (!(pap > 0.0)) break;   // p is in the null space of F: nothing left to do
-        const float alpha = (float)(rs / pap);
-        cg_step_kernel<<<vec_blocks(n), kVecBlock, 0, s>>>(rho_r, rho_i, w.r_r, w.r_i, w.p_r, w.p_i,
-                                                           w.ap_r, w.ap_i, alpha, n);
-        if ((rc = launch_status("cg_step_kernel launch")) != FHD_OK) return rc;
-        double rs_new = 0.0;
-        if ((rc = dot(w.r_r, w.r_i, w.r_r, w.r_i, n, w, s, &rs_new)) != FHD_OK) return rc;
-        ++it;
-        if (residuals) residuals[it] = (float)rs_new;
-        if (rs_new < (double)tol) {
-            rs = rs_new;
-            break;
+    if ((rc = dot<DotUse::kStart>(w.r_r, w.r_i, w.r_r, w.r_i, n, w, max_iter, tol, s)) != FHD_OK)
+        return rc;
+    for (int launched = 0; launched < max_iter;) {
+        int active = 0;
+        if ((rc = read_back(&active, &w.state->active, sizeof(int), s)) != FHD_OK) return rc;
+        if (!active) break;
+        const int batch = std::min(kBatch, max_iter - launched);
+        for (int b = 0; b < batch; ++b) {
+            if ((rc = normal(kx, ky, kz, x, y, z, M, N, w, s)) != FHD_OK) return rc;
+            rc = dot<DotUse::kAlpha>(w.p_r, w.p_i, w.ap_r, w.ap_i, n, w, max_iter, tol, s);
+            if (rc != FHD_OK) return rc;
+            cg_step_kernel<<<vec_blocks(n), kVecBlock, 0, s>>>(rho_r, rho_i, w.r_r, w.r_i, w.p_r,
+                                                               w.p_i, w.ap_r, w.ap_i, w.state, n);
+            if ((rc = launch_status("cg_step_kernel launch")) != FHD_OK) return rc;
+            rc = dot<DotUse::kResidual>(w.r_r, w.r_i, w.r_r, w.r_i, n, w, max_iter, tol, s);
+            if (rc != FHD_OK) return rc;
+            cg_direction_kernel<<<vec_blocks(n), kVecBlock, 0, s>>>(w.p_r, w.p_i, w.r_r, w.r_i,
+                                                                    w.state, n);
+            if ((rc = launch_status("cg_direction_kernel launch")) != FHD_OK) return rc;
         }
-        const float beta = (float)(rs_new / rs);
-        cg_direction_kernel<<<vec_blocks(n), kVecBlock, 0, s>>>(w.p_r, w.p_i, w.r_r, w.r_i, beta, n);
-        if ((rc = launch_status("cg_direction_kernel launch")) != FHD_OK) return rc;
-        rs = rs_new;
+        launched += batch;
     }
-    *iters_done = it;
+    CgState st;
+    if ((rc = read_back(&st, w.state, sizeof st, s)) != FHD_OK) return rc;
+    *iters_done = st.iters;
+    if (residuals) {
+        std::vector<double> h((size_t)st.iters + 1);
+        if ((rc = read_back(h.data(), w.history, h.size() * sizeof(double), s)) != FHD_OK) return rc;
+        for (size_t k = 0; k < h.size(); ++k) residuals[k] = (float)h[k];
+    }
     return FHD_OK;
 }
 
@@ -187,13 +249,13 @@ int run_cg(const float *kx, const float *ky, const float *kz, const float *Dr, c
 
 using namespace fhd;
 
-extern "C" int64_t fhd_cg_workspace_bytes(int M, int N)
+extern "C" int64_t fhd_cg_workspace_bytes(int M, int N, int max_iter)
 {
-    if (M < 0 || N < 0) return -1;
+    if (M < 0 || N < 0 || max_iter < 0) return -1;
     const int64_t nb = (int64_t)N * 4, mb = (int64_t)M * 4;
     auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
     return 6 * up(nb) + up(packed_bytes_for(N)) + up(packed_bytes_for(M)) + 2 * up(mb) +
-           up(kDotBlocks * 8) + up(8);
+           up(kDotBlocks * 8) + up(sizeof(CgState)) + up(((int64_t)max_iter + 1) * 8);
 }
 
 extern "C" int fhd_cg(const float *kx, const float *ky, const float *kz, const float *Dr,
@@ -220,7 +282,7 @@ extern "C" int fhd_cg(const float *kx, const float *ky, const float *kz, const f
 
     hipStream_t s = (hipStream_t)stream;
     char *ws = nullptr;
-    const int64_t bytes = fhd_cg_workspace_bytes(M, N);
+    const int64_t bytes = fhd_cg_workspace_bytes(M, N, max_iter);
     hipError_t e = hipMallocAsync((void **)&ws, (size_t)bytes, s);
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -245,7 +307,8 @@ extern "C" int fhd_cg(const float *kx, const float *ky, const float *kz, const f
     w.d_r = (float *)take(mb);
     w.d_i = (float *)take(mb);
     w.partial = (double *)take(kDotBlocks * 8);
-    w.scalar = (double *)take(8);
+    w.state = (CgState *)take(sizeof(CgState));
+    w.history = (double *)take(((int64_t)max_iter + 1) * 8);
     rc = run_cg(kx, ky, kz, Dr, Di, x, y, z, rho_r, rho_i, M, N, max_iter, tol, iters_done,
                 residuals, w, s);
     e = hipFreeAsync(ws, s);

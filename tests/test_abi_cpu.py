@@ -29,7 +29,7 @@ def lib():
     lib.fhd_packed_bytes.restype = ctypes.c_int64
     lib.fhd_cg.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                        vp, vp, vp]
-    lib.fhd_cg_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.fhd_cg_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.fhd_cg_workspace_bytes.restype = ctypes.c_int64
     lib.fhd_forward.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
     lib.fhd_normal.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
@@ -175,8 +175,10 @@ def test_cg_argument_checks(lib):
         FHD_ERR_INVALID_ARG
     assert lib.fhd_cg(*[None] * 10, 16, 0, 3, 0.0, ctypes.addressof(done), None, None) == FHD_OK
     assert done.value == 0
-    assert lib.fhd_cg_workspace_bytes(-1, 4) == -1
-    assert lib.fhd_cg_workspace_bytes(100, 1000) >= 6 * 4000 + 2 * 400
+    assert lib.fhd_cg_workspace_bytes(-1, 4, 3) == -1
+    assert lib.fhd_cg_workspace_bytes(4, 4, -3) == -1
+    assert lib.fhd_cg_workspace_bytes(100, 1000, 50) >= 6 * 4000 + 2 * 400 + 51 * 8
+    assert lib.fhd_cg_workspace_bytes(100, 1000, 1000) > lib.fhd_cg_workspace_bytes(100, 1000, 50)
 
 
 def test_grid_argument_checks(lib):

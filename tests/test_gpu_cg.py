@@ -77,3 +77,46 @@ def test_cg_without_samples(dev):
     rr, ri, done, res = binding.fhd_cg(e, e, e, e, e, d["x"], d["y"], d["z"], 5, 0.0)
     torch.cuda.synchronize(dev)
     assert done == 0 and torch.count_nonzero(rr).item() == 0 and res[0] == 0
+
+
+def _grid_case():
+    L = 8
+    rng = np.random.default_rng(72)
+    M = 3000
+    k = rng.uniform(-3.5, 3.5, (3, M)).astype(np.float32)
+    D = rng.standard_normal((2, M)).astype(np.float32)
+    x, y, z = inputs.grid_coords(L)
+    return dict(kx=k[0], ky=k[1], kz=k[2], Dr=D[0], Di=D[1], x=x, y=y, z=z)
+
+
+def _oracle_cg(c, iters, tol=0.0):
+    return oracle.cg(c["kx"], c["ky"], c["kz"], c["Dr"], c["Di"], c["x"], c["y"], c["z"],
+                     iters=iters, tol=tol)
+
+
+@pytest.mark.parametrize("iters", [8, 9, 17])
+def test_cg_across_check_batches(dev, iters):
+    """Iteration counts at, just past and well past the host's stop-flag
+    check period (8): the device-side scalars carry over between batches."""
+    c = _grid_case()
+    rr, ri, done, res = run(c, dev, iters)
+    ref, ref_res = _oracle_cg(c, iters)
+    assert done == iters == len(ref_res) - 1
+    check("cg %d iterations" % iters, rr, ri, ref.real, ref.imag)
+    assert np.allclose(res, ref_res, rtol=1e-3, atol=0), (res, ref_res)
+
+
+@pytest.mark.parametrize("stop", [3, 11])
+def test_cg_tolerance_stop_inside_a_batch(dev, stop):
+    """A tolerance between ||r||^2 after stop - 1 and after stop iterations
+    ends the run after exactly `stop` iterations; the rest of the batch does
+    nothing to rho."""
+    c = _grid_case()
+    _, ref_res = _oracle_cg(c, 20)
+    assert ref_res[stop - 1] > 1.4 * ref_res[stop]      # well separated
+    tol = float(np.sqrt(ref_res[stop - 1] * ref_res[stop]))
+    rr, ri, done, res = run(c, dev, 20, tol=tol)
+    ref, ref_stop = _oracle_cg(c, 20, tol=tol)
+    assert done == stop == len(ref_stop) - 1 and len(res) == stop + 1
+    assert res[stop] < tol <= res[stop - 1]
+    check("cg stop at %d" % stop, rr, ri, ref.real, ref.imag)
