@@ -66,11 +66,11 @@ ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / 2)
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
     "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
-            "sha256": "286ee91accce82c6e8dd770012e75c744090a233e5e0524d17a8be8113482122",
-            "bytes_per_launch": (20156.5 * 2.0 + 16384 * 1.0) * 1024},
+            "sha256": "78c0746a6d97e29e5deb4c32d1cd8c5cdb1c8c465960d9f2718432a798761791",
+            "bytes_per_launch": (20157.0 * 2.0 + 16384 * 1.0) * 1024},
     "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
-             "sha256": "0a8ad465bb80819b79ba4384d16fd32ac84a1c79f953e5f75d8d4edbe53a2d60",
-             "bytes_per_launch": (7875.5 * 2.0 + 49152 * 1.0) * 1024},
+             "sha256": "52123b52ce807d2bcff36893bc7a982590104eada543d42e2961b7d7621770d0",
+             "bytes_per_launch": (7876.0 * 2.0 + 49152 * 1.0) * 1024},
 }
 
 

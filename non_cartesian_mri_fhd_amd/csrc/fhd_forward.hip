@@ -77,11 +77,15 @@ __device__ __forceinline__ void accumulate_voxels(const float4 *ch, const float 
                 p[j] = __builtin_fmaf(kx[j], vx[u],
                                       __builtin_fmaf(ky[j], vy[u], __builtin_fmaf(kz[j], vz[u], vs[u])));
         }
+        // transcendentals as one group at raised wave priority, so the
+        // waves' FMA runs coincide and pair (as in the F^H D gather)
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < S; ++j) c[j] = __builtin_amdgcn_cosf(p[j]);
 #pragma unroll
         for (int j = 0; j < S; ++j) sn[j] = __builtin_amdgcn_sinf(p[j]);
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < S; ++j) {
