@@ -36,14 +36,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "F^H D voxel-sample terms/s at 128^3 x 100k; % of FP32 VALU/trans roofline"
 
-# gfx950 ALU ceiling of the gather kernel, from unit counts and clock:
+# gfx950 ALU ceiling of the gathers, from unit counts and clock:
 # 256 CUs x 4 SIMDs at 2.4 GHz. FP32 vector peak 157.3 TFLOP/s (AMD's
 # figure). v_sin_f32 / v_cos_f32 issue one wave64 instruction per 8 SIMD
 # cycles, i.e. 8 lanes per cycle per SIMD (measured by the issue-rate
 # micro-benchmarks; a quarter of the FP32 FMA rate), so the
-# transcendental peak is 256 * 4 * 8 * 2.4e9 = 1.97e13 /s. With 13 FLOP
-# and 2 transcendentals per voxel-sample term the roofline is
-# R = min(P_fp32 / 13, P_trans / 2) terms/s.
+# transcendental peak is 256 * 4 * 8 * 2.4e9 = 1.97e13 /s. A term counts
+# 13 FLOP (the fixed convention); the transcendentals a term needs depend
+# on the gather's path: 2 where each term's sin and cos are evaluated
+# (ROOF_TERMS = min(P_fp32 / 13, P_trans / 2), transcendental-bound), 4
+# per 8 terms on the ramp path, whose ceiling is then the FP32 one.
 CUS, SIMDS_PER_CU, TRANS_LANES_PER_CYCLE, CLOCK_HZ = 256, 4, 8, 2.4e9
 P_FP32 = 157.3e12
 P_TRANS = CUS * SIMDS_PER_CU * TRANS_LANES_PER_CYCLE * CLOCK_HZ
@@ -52,7 +54,46 @@ FLOP_PER_TERM = 13
 # on the matrix cores, whose dense fp32 peak is 157.3 TFLOP/s
 MFMA_FLOP_PER_TERM = 8
 P_MFMA_FP32 = 157.3e12
-ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / 2)
+TRANS_PER_TERM_DIRECT = 2.0
+TRANS_PER_TERM_RAMP = 4.0 / 8
+ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / TRANS_PER_TERM_DIRECT)
+
+
+def roof_terms(parts) -> float:
+    """Terms/s ceiling of work made of (terms, transcendentals per term)
+    parts run one after another: total terms over the sum of each part's
+    time at min(P_fp32 / 13, P_trans / t)."""
+    total = sum(n for n, _ in parts)
+    t_min = sum(n / min(P_FP32 / FLOP_PER_TERM, P_TRANS / t) for n, t in parts if n > 0)
+    return total / t_min if t_min > 0 else ROOF_TERMS
+
+
+def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 8) -> float:
+    """Fraction of voxels whose gather workgroup takes the ramp path, by the
+    kernel's own test: every lane's `vox` voxels share y and z bitwise, all
+    exist, and x_v equals x_0 + v (x_1 - x_0) rounded once to fp32."""
+    x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
+    N = x.size
+    full = N // vox * vox
+    lanes = full // vox
+    if lanes == 0:
+        return 0.0
+    X, Y, Z = (a[:full].reshape(lanes, vox) for a in (x, y, z))
+    same = (np.all(Y.view(np.uint32) == Y[:, :1].view(np.uint32), axis=1)
+            & np.all(Z.view(np.uint32) == Z[:, :1].view(np.uint32), axis=1))
+    dx = (X[:, 1] - X[:, 0]).astype(np.float32)
+    v = np.arange(vox, dtype=np.float64)
+    ramp_x = (X[:, :1].astype(np.float64) + v * dx[:, None].astype(np.float64)).astype(np.float32)
+    lane_ok = same & np.isfinite(dx) & np.all(ramp_x == X, axis=1)
+    per_block = block
+    blocks = (lanes + per_block - 1) // per_block
+    ok = np.zeros(blocks * per_block, bool)
+    ok[:lanes] = lane_ok
+    # lanes past N (a partial last workgroup) stay False: such a
+    # workgroup never qualifies
+    block_ok = ok.reshape(blocks, per_block).all(axis=1)
+    voxels = np.minimum(block * vox, N - np.arange(blocks) * block * vox)
+    return float(np.sum(voxels[block_ok]) / N)
 
 # HBM bytes per launch of each operator's dominant kernel at 128^3 x 100k,
 # from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by a 1 GiB copy's
@@ -66,8 +107,8 @@ ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / 2)
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
     "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
-            "sha256": "78c0746a6d97e29e5deb4c32d1cd8c5cdb1c8c465960d9f2718432a798761791",
-            "bytes_per_launch": (20157.0 * 2.0 + 16384 * 1.0) * 1024},
+            "sha256": "df158e35a0a708f15dcaee1449a1251cb99dc05b0e66c26ace6b2f0ec804a81f",
+            "bytes_per_launch": (20164.0 * 2.0 + 16384 * 1.0) * 1024},
     "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
              "sha256": "52123b52ce807d2bcff36893bc7a982590104eada543d42e2961b7d7621770d0",
              "bytes_per_launch": (7876.0 * 2.0 + 49152 * 1.0) * 1024},
@@ -190,10 +231,14 @@ def main(argv=None) -> int:
     pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     terms = float(N) * float(M)
     value = terms / (ms_step * 1e-3)
-
-    achieved = FLOP_PER_TERM * terms / (gather_ms * 1e-3) / 1e12
-    peak = FLOP_PER_TERM * ROOF_TERMS / 1e12
     cfg = binding.gather_config()
+
+    # the ceiling for the paths this voxel layout takes (the x-fastest
+    # grids of the workloads: the ramp path throughout)
+    ramp = ramp_voxel_fraction(w["x"], w["y"], w["z"], cfg["block_threads"], cfg["voxels_per_lane"])
+    roof = roof_terms([(terms * ramp, TRANS_PER_TERM_RAMP), (terms * (1 - ramp), TRANS_PER_TERM_DIRECT)])
+    achieved = FLOP_PER_TERM * terms / (gather_ms * 1e-3) / 1e12
+    peak = FLOP_PER_TERM * roof / 1e12
     out = {
         "metric": METRIC,
         "value": value,
@@ -210,7 +255,7 @@ def main(argv=None) -> int:
         "config": {
             "workload": "%s: F^H D over %d^3 voxels x %d samples (%s)"
                         % (args.workload, w["L"], M, inputs.WORKLOADS[args.workload].trajectory),
-            "N": N, "M": M, "terms": terms, **cfg,
+            "N": N, "M": M, "terms": terms, "ramp_path_voxel_fraction": ramp, **cfg,
         },
         "roofline": {
             "bound": "alu",
@@ -220,6 +265,10 @@ def main(argv=None) -> int:
             "frac": achieved / peak,
             "traffic": measured_traffic("fhd", args.workload),
         },
+        "roofline_direct_form": {
+            "note": "R for 2 transcendentals per term, the pages' direct evaluation",
+            "peak": FLOP_PER_TERM * ROOF_TERMS / 1e12, "unit": "TFLOP/s",
+            "frac": FLOP_PER_TERM * terms / (gather_ms * 1e-3) / (FLOP_PER_TERM * ROOF_TERMS)},
         "kernel_ms": {"fhd_gather_kernel": gather_ms, "fhd_pack_kernel": pack_ms,
                       "fhd_gather_kernel_median": float(np.median(gather_all)),
                       "fhd_gather_kernel_min": float(np.min(gather_all))},
@@ -280,6 +329,7 @@ def bench_other(args) -> int:
     # step(): the whole operator; timed(): the same with HIP events on the
     # launch stream around its dominant kernel (None where one call covers it)
     dominant = None
+    k_iters = 3
     if args.op == "forward":
         Dr = torch.empty(M, device=dev)
         Di = torch.empty(M, device=dev)
@@ -320,7 +370,6 @@ def bench_other(args) -> int:
     else:
         rr = torch.empty(N, device=dev)
         ri = torch.empty(N, device=dev)
-        k_iters = 3
 
         def pre():
             pass
@@ -346,6 +395,14 @@ def bench_other(args) -> int:
     kms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     value = terms_per_step / (ms * 1e-3)
     k_rate = terms_per_step / (float(np.mean(kms)) * 1e-3)
+    # ceiling: F^H terms at the adjoint gather's path mix, F terms direct
+    NM = float(N) * M
+    ramp = ramp_voxel_fraction(w["x"], w["y"], w["z"])
+    adjoint = {"normal": 1, "cg": 1 + k_iters}.get(args.op, 0)
+    forward_terms = {"forward": 1, "normal": 1, "cg": k_iters}.get(args.op, 0)
+    roof = roof_terms([(adjoint * NM * ramp, TRANS_PER_TERM_RAMP),
+                       (adjoint * NM * (1 - ramp), TRANS_PER_TERM_DIRECT),
+                       (forward_terms * NM, TRANS_PER_TERM_DIRECT)])
     out = {
         "metric": "%s voxel-sample terms/s (%s)" % (args.op, args.workload),
         "value": value, "unit": "terms/s", "n_gpus": 1, "steps": args.steps,
@@ -354,8 +411,8 @@ def bench_other(args) -> int:
         "config": {"workload": args.workload, "op": args.op, "N": N, "M": M,
                    "terms_per_step": terms_per_step},
         "roofline": {"bound": "alu", "achieved": FLOP_PER_TERM * k_rate / 1e12,
-                     "peak": FLOP_PER_TERM * ROOF_TERMS / 1e12, "unit": "TFLOP/s",
-                     "frac": k_rate / ROOF_TERMS, "traffic": None},
+                     "peak": FLOP_PER_TERM * roof / 1e12, "unit": "TFLOP/s",
+                     "frac": k_rate / roof, "traffic": None},
         "kernel_ms": {"timed": dominant or "whole call", "mean": float(np.mean(kms)),
                       "median": float(np.median(kms)), "min": float(np.min(kms))},
     }

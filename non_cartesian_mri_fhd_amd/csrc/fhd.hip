@@ -30,8 +30,20 @@
 //    are bitwise identical; workgroups that fail the test take the general
 //    path.
 //
-// Per voxel-sample term: phase 1 + 2/kVox FMA (3 FMA on the general path),
-// v_cos_f32, v_sin_f32, 2 FMA accumulate.
+//    When, in addition, each lane's voxels are equally spaced along x
+//    (x_v = x_0 + v dx to fp32 rounding, checked exactly), the phase is a
+//    ramp p_v = p_0 + v d with d = kx dx, and the phasors follow from two
+//    seeds: a e^{i 2 pi p_0} by v_cos/v_sin, its rotation by e^{i 2 pi d}
+//    (also v_cos/v_sin), then the three-term recurrence
+//    w_{v+1} = 2 cos(2 pi d) w_v - w_{v-1}, which holds for any sinusoid of
+//    step d and is linear, so the amplitude rides along. Four
+//    transcendentals per sample and lane instead of 2 kVox. Rounding in the
+//    recurrence grows at most like v^2 ulp (v < kVox); the seeds carry the
+//    same phase rounding as the direct evaluation.
+//
+// Per voxel-sample term: direct paths, phase 1 + 2/kVox FMA (3 FMA on the
+// general path), v_cos_f32, v_sin_f32, 2 FMA accumulate; ramp path, 4/kVox
+// transcendentals and about 5 VALU operations.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -116,6 +128,52 @@ __device__ __forceinline__ void accumulate_chunk(const float4 *ch, const float (
     }
 }
 
+// Ramp path: a lane's V voxels share y and z and sit at x0 + v dx.
+template <int V>
+__device__ __forceinline__ void accumulate_chunk_ramp(const float4 *ch, float x0, float dx, float y,
+                                                      float z, float (&acc_r)[V], float (&acc_i)[V])
+{
+    float f[kFields][kChunk];
+    load_chunk(ch, f);
+    const float(&skx)[kChunk] = f[0];
+    const float(&sky)[kChunk] = f[1];
+    const float(&skz)[kChunk] = f[2];
+    const float(&psi)[kChunk] = f[3];
+    const float(&amp)[kChunk] = f[4];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+        const float p0 = __builtin_fmaf(skx[u], x0, __builtin_fmaf(sky[u], y, __builtin_fmaf(skz[u], z, psi[u])));
+        const float d = skx[u] * dx;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        const float c0 = __builtin_amdgcn_cosf(p0), s0 = __builtin_amdgcn_sinf(p0);
+        const float cd = __builtin_amdgcn_cosf(d), sd = __builtin_amdgcn_sinf(d);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        // w_0 = a e^{i 2 pi p0}; w_1 = w_0 e^{i 2 pi d}
+        float wr0 = amp[u] * c0, wi0 = amp[u] * s0;
+        float wr1 = __builtin_fmaf(wr0, cd, -wi0 * sd);
+        float wi1 = __builtin_fmaf(wi0, cd, wr0 * sd);
+        const float two_cd = cd + cd;
+        acc_r[0] += wr0;
+        acc_i[0] += wi0;
+        acc_r[1] += wr1;
+        acc_i[1] += wi1;
+#pragma unroll
+        for (int v = 2; v < V; ++v) {
+            const float wr2 = __builtin_fmaf(two_cd, wr1, -wr0);
+            const float wi2 = __builtin_fmaf(two_cd, wi1, -wi0);
+            acc_r[v] += wr2;
+            acc_i[v] += wi2;
+            wr0 = wr1;
+            wi0 = wi1;
+            wr1 = wr2;
+            wi1 = wi2;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // At least 4 waves per SIMD (<= 128 VGPRs): a 128^3 grid at 8 voxels per
 // lane is exactly 4 waves per SIMD, so all of them are resident at once.
 // Split s = blockIdx.y of `splits` takes its share of the sample stream and
@@ -156,13 +214,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     for (int v = 1; v < V; ++v)
         same_yz = same_yz && __float_as_uint(py[v]) == __float_as_uint(py[0]) &&
                   __float_as_uint(pz[v]) == __float_as_uint(pz[0]);
-    // one decision per workgroup, so both branches' stage barriers are
+    // equal spacing along x: every x_v is x0 + v dx rounded once (lanes with
+    // voxels past N never qualify)
+    const float dx = px[1] - px[0];
+    bool ramp = same_yz && n0 + V <= N && __builtin_isfinite(dx);
+#pragma unroll
+    for (int v = 1; v < V; ++v)
+        ramp = ramp && __builtin_fmaf((float)v, dx, px[0]) == px[v];
+    // one decision per workgroup, so every branch's stage barriers are
     // reached by every wave of the workgroup
+    const bool all_ramp = __syncthreads_and(ramp);
     const bool shared = __syncthreads_and(same_yz);
 
     int c0, c1;
     split_range(nchunks, splits, blockIdx.y, &c0, &c1);
-    if (shared)
+    if (all_ramp)
+        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
+            accumulate_chunk_ramp<V>(ch, px[0], dx, py[0], pz[0], acc_r, acc_i);
+        });
+    else if (shared)
         stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
             accumulate_chunk<V, true>(ch, px, py, pz, acc_r, acc_i);
         });

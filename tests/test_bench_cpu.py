@@ -3,6 +3,8 @@ import os
 import subprocess
 import sys
 
+import numpy as np
+
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -25,3 +27,32 @@ def test_roofline_constants():
     # transcendental-bound: 2 per term at 8 lanes per clock per SIMD
     assert abs(bench.ROOF_TERMS - 256 * 4 * 8 * 2.4e9 / 2) / bench.ROOF_TERMS < 1e-9
     assert bench.ROOF_TERMS < bench.P_FP32 / bench.FLOP_PER_TERM
+
+
+def test_ramp_fraction_mirrors_the_kernel_test():
+    from non_cartesian_mri_fhd_amd import inputs
+    L = 32
+    x, y, z = inputs.grid_coords(L)
+    assert bench.ramp_voxel_fraction(x, y, z) == 1.0
+    n = np.arange(L ** 3)
+    zfast = n.reshape(L, L, L).transpose(2, 1, 0).reshape(-1)
+    assert bench.ramp_voxel_fraction(x[zfast], y[zfast], z[zfast]) == 0.0
+    swap = n.copy()
+    swap[1::8], swap[2::8] = n[2::8], n[1::8]
+    assert bench.ramp_voxel_fraction(x[swap], y[swap], z[swap]) == 0.0
+    # one voxel off the grid spoils its workgroup only (2048 voxels of 32768)
+    x2 = x.copy()
+    x2[5000] += np.float32(1e-3)
+    assert bench.ramp_voxel_fraction(x2, y, z) == 1.0 - 2048 / L ** 3
+    # a partial last workgroup takes a direct path
+    m = L ** 3 - 8
+    assert bench.ramp_voxel_fraction(x[:m], y[:m], z[:m]) == (L ** 3 - 2048) / m
+
+
+def test_roof_terms_mixes_paths():
+    r_direct = bench.roof_terms([(1.0, bench.TRANS_PER_TERM_DIRECT)])
+    r_ramp = bench.roof_terms([(1.0, bench.TRANS_PER_TERM_RAMP)])
+    assert r_direct == bench.ROOF_TERMS
+    assert r_ramp == bench.P_FP32 / bench.FLOP_PER_TERM
+    mixed = bench.roof_terms([(1.0, bench.TRANS_PER_TERM_RAMP), (1.0, bench.TRANS_PER_TERM_DIRECT)])
+    assert abs(mixed - 2 / (1 / r_ramp + 1 / r_direct)) < 1e-6 * mixed

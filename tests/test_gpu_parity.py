@@ -217,18 +217,60 @@ def test_large_exact_phases_closed_form(dev):
     assert metrics.rel_l2(rr, ri, ref.real, ref.imag) < 1e-5
 
 
-def test_shared_and_general_paths_bitwise_equal(dev):
-    """The same grid voxels in x-fastest order (each lane's voxels share y and
-    z: the shared-phase path) and in z-fastest order (they do not: the general
-    path) give bitwise identical per-voxel results."""
+def test_ramp_shared_and_general_paths(dev):
+    """One grid, three voxel orders. x fastest: each lane's 8 voxels share y
+    and z and are equally spaced in x (the ramp path). The same with voxels
+    1 and 2 of every 8 swapped: y, z still shared, x no longer a ramp (the
+    shared-phase path). z fastest: nothing shared (the general path). The
+    shared and general paths give bitwise identical per-voxel results; the
+    ramp path meets the oracle gate and agrees with them to rounding."""
     L = 32
     k = inputs.make_kspace("spiral32")
     x, y, z = inputs.grid_coords(L)
-    a = gpu_fhd(dict(k, x=x, y=y, z=z), dev)
-    perm = np.arange(L ** 3).reshape(L, L, L).transpose(2, 1, 0).reshape(-1)   # z fastest
-    b = gpu_fhd(dict(k, x=x[perm], y=y[perm], z=z[perm]), dev)
-    assert not np.array_equal(z[perm][:8], np.full(8, z[perm][0]))   # z varies within a lane
-    assert np.array_equal(a[0][perm], b[0]) and np.array_equal(a[1][perm], b[1])
+    n = np.arange(L ** 3)
+    swap = n.copy()
+    swap[1::8], swap[2::8] = n[2::8], n[1::8]
+    zfast = n.reshape(L, L, L).transpose(2, 1, 0).reshape(-1)
+    ramp = gpu_fhd(dict(k, x=x, y=y, z=z), dev)
+    shared = gpu_fhd(dict(k, x=x[swap], y=y[swap], z=z[swap]), dev)
+    general = gpu_fhd(dict(k, x=x[zfast], y=y[zfast], z=z[zfast]), dev)
+    assert not np.array_equal(z[zfast][:8], np.full(8, z[zfast][0]))   # z varies within a lane
+    sh = (np.empty_like(shared[0]), np.empty_like(shared[1]))
+    sh[0][swap], sh[1][swap] = shared
+    assert np.array_equal(sh[0][zfast], general[0]) and np.array_equal(sh[1][zfast], general[1])
+    ref = oracle.fhd(k["kx"], k["ky"], k["kz"], k["Dr"], k["Di"], x, y, z)
+    check("ramp path", *ramp, *ref)
+    check("shared path", *sh, *ref)
+    assert metrics.rel_l2(*ramp, sh[0].astype(np.float64), sh[1].astype(np.float64)) < 5e-5
+
+
+def test_ramp_path_odd_spacing(dev):
+    """A grid whose fp32 x steps are not all equal (non-dyadic origin and
+    step, negative step in z): lanes whose voxels are not an exact ramp fall
+    back; everything meets the oracle gate."""
+    shape, axis = (72, 5, 27), (0.3, 0.013, -0.2, 0.021, 0.11, -0.017)
+    x, y, z = inputs.coords_from_axis(*shape, axis)
+    c = inputs.random_case(1, 3000, seed=91)
+    w = dict(c, x=x, y=y, z=z)
+    rr, ri = gpu_fhd(w, dev)
+    ref = oracle.fhd(c["kx"], c["ky"], c["kz"], c["Dr"], c["Di"], x, y, z)
+    check("odd spacing", rr, ri, *ref)
+
+
+def test_ramp_path_nyquist_and_zero_steps(dev):
+    """Samples whose x-step phase kx dx is 0, 1/4, 1/2 or -1/2 revolution (the
+    recurrence's degenerate points) on an L = 32 grid."""
+    L = 32
+    x, y, z = inputs.grid_coords(L)
+    rng = np.random.default_rng(12)
+    M = 4096
+    kx = rng.choice(np.array([0.0, 8.0, 16.0, -16.0, 15.5, -0.25], np.float32), M)
+    ky, kz = (rng.uniform(-16, 16, M).astype(np.float32) for _ in range(2))
+    Dr, Di = (rng.standard_normal(M).astype(np.float32) for _ in range(2))
+    w = dict(kx=kx, ky=ky, kz=kz, Dr=Dr, Di=Di, x=x, y=y, z=z)
+    rr, ri = gpu_fhd(w, dev)
+    ref = oracle.fhd(kx, ky, kz, Dr, Di, x, y, z)
+    check("ramp degenerate steps", rr, ri, *ref)
 
 
 def test_mixed_waves(dev):
