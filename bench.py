@@ -68,23 +68,39 @@ def roof_terms(parts) -> float:
     return total / t_min if t_min > 0 else ROOF_TERMS
 
 
-def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 8) -> float:
-    """Fraction of voxels whose gather workgroup takes the ramp path, by the
-    kernel's own test: every lane's `vox` voxels share y and z bitwise, all
-    exist, and x_v equals x_0 + v (x_1 - x_0) rounded once to fp32."""
+def _lane_ramps(x, y, z, vox: int = 8):
+    """Per group of `vox` consecutive voxels (the last partial group
+    dropped): do they share y and z bitwise and sit at x_0 + v (x_1 - x_0)
+    rounded once to fp32 -- the gathers' ramp test."""
     x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
-    N = x.size
-    full = N // vox * vox
+    full = x.size // vox * vox
     lanes = full // vox
     if lanes == 0:
-        return 0.0
+        return np.zeros(0, bool)
     X, Y, Z = (a[:full].reshape(lanes, vox) for a in (x, y, z))
     same = (np.all(Y.view(np.uint32) == Y[:, :1].view(np.uint32), axis=1)
             & np.all(Z.view(np.uint32) == Z[:, :1].view(np.uint32), axis=1))
     dx = (X[:, 1] - X[:, 0]).astype(np.float32)
     v = np.arange(vox, dtype=np.float64)
     ramp_x = (X[:, :1].astype(np.float64) + v * dx[:, None].astype(np.float64)).astype(np.float32)
-    lane_ok = same & np.isfinite(dx) & np.all(ramp_x == X, axis=1)
+    return same & np.isfinite(dx) & np.all(ramp_x == X, axis=1)
+
+
+def ramp_chunk_fraction(x, y, z, vox: int = 8) -> float:
+    """Fraction of voxels that F's pre-pass writes as ramp chunks."""
+    n = np.asarray(x).size
+    return float(np.sum(_lane_ramps(x, y, z, vox)) * vox / n) if n else 0.0
+
+
+def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 8) -> float:
+    """Fraction of voxels whose F^H D gather workgroup takes the ramp path,
+    by the kernel's own test: every lane's `vox` voxels form a ramp (see
+    _lane_ramps) and the workgroup's lanes all exist."""
+    N = np.asarray(x).size
+    lane_ok = _lane_ramps(x, y, z, vox)
+    lanes = lane_ok.size
+    if lanes == 0:
+        return 0.0
     per_block = block
     blocks = (lanes + per_block - 1) // per_block
     ok = np.zeros(blocks * per_block, bool)
@@ -398,11 +414,13 @@ def bench_other(args) -> int:
     # ceiling: F^H terms at the adjoint gather's path mix, F terms direct
     NM = float(N) * M
     ramp = ramp_voxel_fraction(w["x"], w["y"], w["z"])
+    ramp_f = ramp_chunk_fraction(w["x"], w["y"], w["z"])
     adjoint = {"normal": 1, "cg": 1 + k_iters}.get(args.op, 0)
     forward_terms = {"forward": 1, "normal": 1, "cg": k_iters}.get(args.op, 0)
     roof = roof_terms([(adjoint * NM * ramp, TRANS_PER_TERM_RAMP),
                        (adjoint * NM * (1 - ramp), TRANS_PER_TERM_DIRECT),
-                       (forward_terms * NM, TRANS_PER_TERM_DIRECT)])
+                       (forward_terms * NM * ramp_f, TRANS_PER_TERM_RAMP),
+                       (forward_terms * NM * (1 - ramp_f), TRANS_PER_TERM_DIRECT)])
     out = {
         "metric": "%s voxel-sample terms/s (%s)" % (args.op, args.workload),
         "value": value, "unit": "terms/s", "n_gpus": 1, "steps": args.steps,

@@ -10,14 +10,22 @@
 //
 //  * fhd_forward_pack_kernel -- per-voxel pre-pass. Writes each voxel as the
 //    record (x, y, z, s, a) with a = |rho| and s = -arg(rho) / (2 pi), so
-//    that rho e^{-i 2 pi k.x} = a e^{-i 2 pi (k.x + s)}.
+//    that rho e^{-i 2 pi k.x} = a e^{-i 2 pi (k.x + s)}. A chunk of 8
+//    voxels that share y and z and sit at x0 + u dx (checked exactly; every
+//    chunk of an x-fastest grid) is written as a ramp chunk instead:
+//    Re rho_u, -Im rho_u, then (x0, dx, y, z), marked by -1 in the last
+//    slot of the amplitude field (amplitudes are never negative).
 //
 //  * fhd_forward_gather_kernel -- one lane per kSamp consecutive samples,
 //    no atomics; every lane walks the same voxel stream through LDS
-//    (stream_chunks). Per term: p = kx x + ky y + kz z + s (3 FMA; 2 + 1/kSamp
-//    when all of a lane's samples share kz, as within a plane of a stack of
-//    spirals -- bitwise identical), v_cos_f32, v_sin_f32, 2 FMA. The
-//    accumulated sine sum is negated once at the end (exact).
+//    (stream_chunks) and accumulates conj(D). Per term of a general chunk:
+//    p = kx x + ky y + kz z + s (3 FMA; 2 + 1/kSamp when all of a lane's
+//    samples share kz, as within a plane of a stack of spirals -- bitwise
+//    identical), v_cos_f32, v_sin_f32, 2 FMA. A ramp chunk is a polynomial
+//    in z = e^{i 2 pi kx dx}: sum_u conj(rho_u) e^{i 2 pi k.x_u} =
+//    e^{i 2 pi k.x_0} sum_u conj(rho_u) z^u, evaluated by Horner's rule
+//    (4 FMA per voxel) after 4 transcendentals per sample and chunk. The
+//    accumulated imaginary part is negated once at the end (exact).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -36,18 +44,70 @@ __global__ __launch_bounds__(kPackBlock) void fhd_forward_pack_kernel(
     const float *__restrict__ rho_r, const float *__restrict__ rho_i,
     float *__restrict__ packed, int N, int64_t N_pad)
 {
+    // every lane stays to the end: the ramp test exchanges values between
+    // the 8 lanes of a chunk (a chunk never straddles N_pad or a wave)
     const int64_t n = (int64_t)blockIdx.x * kPackBlock + threadIdx.x;
-    if (n >= N_pad) return;
-    float fx = 0.0f, fy = 0.0f, fz = 0.0f, s = 0.0f, amp = 0.0f;
-    if (n < N) {
+    const bool live = n < N;
+    float fx = 0.0f, fy = 0.0f, fz = 0.0f, re = 0.0f, im = 0.0f;
+    if (live) {
         fx = x[n];
         fy = y[n];
         fz = z[n];
-        const double re = rho_r[n], im = rho_i[n];
-        amp = (float)hypot(re, im);
-        s = (float)(-atan2(im, re) * (0.5 / M_PI));   // [-0.5, 0.5] revolutions
+        re = rho_r[n];
+        im = rho_i[n];
     }
-    store_record(packed, n, fx, fy, fz, s, amp);
+    const int lane = threadIdx.x & 63, base = lane & ~(kChunk - 1), u = lane & (kChunk - 1);
+    const float x0 = __shfl(fx, base), x1 = __shfl(fx, base + 1);
+    const float y0 = __shfl(fy, base), z0 = __shfl(fz, base);
+    const float dx = x1 - x0;
+    const bool mine = live && __float_as_uint(fy) == __float_as_uint(y0) &&
+                      __float_as_uint(fz) == __float_as_uint(z0) && __builtin_isfinite(dx) &&
+                      __builtin_fmaf((float)u, dx, x0) == fx;
+    const bool ramp = ((__ballot(mine) >> base) & 0xffull) == 0xffull;
+    if (n >= N_pad) return;
+    if (ramp) {
+        const float geo = u == 0 ? x0 : u == 1 ? dx : u == 2 ? y0 : u == 3 ? z0 : 0.0f;
+        store_record(packed, n, re, -im, geo, 0.0f, u == kChunk - 1 ? -1.0f : 0.0f);
+    } else {
+        float s = 0.0f, amp = 0.0f;
+        if (live) {
+            amp = (float)hypot((double)re, (double)im);
+            s = (float)(-atan2((double)im, (double)re) * (0.5 / M_PI));   // [-0.5, 0.5] revolutions
+        }
+        store_record(packed, n, fx, fy, fz, s, amp);
+    }
+}
+
+// A ramp chunk: acc_j += e^{i 2 pi k_j.x_0} sum_u c_u z_j^u with
+// c_u = conj(rho_u), z_j = e^{i 2 pi kx_j dx} (Horner, highest u first).
+template <int S>
+__device__ __forceinline__ void accumulate_ramp_chunk(const float (&f)[kFields][kChunk],
+                                                      const float (&kx)[S], const float (&ky)[S],
+                                                      const float (&kz)[S], float (&acc_r)[S],
+                                                      float (&acc_i)[S])
+{
+    const float x0 = f[2][0], dx = f[2][1], y = f[2][2], z = f[2][3];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const float p = __builtin_fmaf(kx[j], x0, __builtin_fmaf(ky[j], y, kz[j] * z));
+        const float d = kx[j] * dx;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        const float er = __builtin_amdgcn_cosf(p), ei = __builtin_amdgcn_sinf(p);
+        const float zr = __builtin_amdgcn_cosf(d), zi = __builtin_amdgcn_sinf(d);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        float hr = f[0][kChunk - 1], hi = f[1][kChunk - 1];
+#pragma unroll
+        for (int u = kChunk - 2; u >= 0; --u) {
+            const float tr = __builtin_fmaf(hr, zr, __builtin_fmaf(-hi, zi, f[0][u]));
+            const float ti = __builtin_fmaf(hr, zi, __builtin_fmaf(hi, zr, f[1][u]));
+            hr = tr;
+            hi = ti;
+        }
+        acc_r[j] = __builtin_fmaf(er, hr, __builtin_fmaf(-ei, hi, acc_r[j]));
+        acc_i[j] = __builtin_fmaf(er, hi, __builtin_fmaf(ei, hr, acc_i[j]));
+    }
 }
 
 // Accumulate one chunk of kChunk voxels into a lane's S samples.
@@ -59,6 +119,13 @@ __device__ __forceinline__ void accumulate_voxels(const float4 *ch, const float 
 {
     float f[kFields][kChunk];
     load_chunk(ch, f);
+    // every lane reads the same chunk: a scalar branch
+    const float mark = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                      __builtin_bit_cast(int, f[4][kChunk - 1])));
+    if (mark < 0.0f) {
+        accumulate_ramp_chunk<S>(f, kx, ky, kz, acc_r, acc_i);
+        return;
+    }
     const float(&vx)[kChunk] = f[0];
     const float(&vy)[kChunk] = f[1];
     const float(&vz)[kChunk] = f[2];

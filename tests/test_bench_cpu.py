@@ -56,3 +56,15 @@ def test_roof_terms_mixes_paths():
     assert r_ramp == bench.P_FP32 / bench.FLOP_PER_TERM
     mixed = bench.roof_terms([(1.0, bench.TRANS_PER_TERM_RAMP), (1.0, bench.TRANS_PER_TERM_DIRECT)])
     assert abs(mixed - 2 / (1 / r_ramp + 1 / r_direct)) < 1e-6 * mixed
+
+
+def test_ramp_chunk_fraction():
+    from non_cartesian_mri_fhd_amd import inputs
+    L = 16
+    x, y, z = inputs.grid_coords(L)
+    assert bench.ramp_chunk_fraction(x, y, z) == 1.0
+    x2 = x.copy()
+    x2[[3, 100]] += np.float32(1e-3)          # spoils 2 chunks of 8
+    assert bench.ramp_chunk_fraction(x2, y, z) == 1.0 - 16 / L ** 3
+    m = L ** 3 - 3                            # partial last chunk
+    assert bench.ramp_chunk_fraction(x[:m], y[:m], z[:m]) == (L ** 3 - 8) / m

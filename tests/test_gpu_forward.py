@@ -144,6 +144,13 @@ def test_forward_shared_kz_and_general_paths_bitwise_equal(dev):
     identical per-sample results."""
     w = inputs.make_workload("spiral32")
     img = inputs.random_image(w["N"], seed=10)
+    # voxels 1 and 2 of every 8 swapped: no chunk is a ramp, so every chunk
+    # takes the direct paths under test
+    n = np.arange(w["N"])
+    swap = n.copy()
+    swap[1::8], swap[2::8] = n[2::8], n[1::8]
+    w = dict(w, x=w["x"][swap], y=w["y"][swap], z=w["z"][swap])
+    img = (img[0][swap], img[1][swap])
     a = gpu_forward(w, img, dev)
     M = w["M"]
     perm = np.arange(M).reshape(16, M // 16).T.reshape(-1)     # plane index fastest
@@ -151,3 +158,56 @@ def test_forward_shared_kz_and_general_paths_bitwise_equal(dev):
     assert not np.all(p["kz"][:8] == p["kz"][0])
     b = gpu_forward(p, img, dev)
     assert np.array_equal(a[0][perm], b[0]) and np.array_equal(a[1][perm], b[1])
+
+
+def test_forward_ramp_and_direct_chunks_agree(dev):
+    """The same voxels as ramp chunks (x-fastest grid order) and as direct
+    chunks (voxels 1 and 2 of every 8 swapped): D is a sum over voxels, so
+    both must match the oracle and each other."""
+    w = inputs.make_workload("spiral32")
+    img = inputs.random_image(w["N"], seed=14)
+    n = np.arange(w["N"])
+    swap = n.copy()
+    swap[1::8], swap[2::8] = n[2::8], n[1::8]
+    ramp = gpu_forward(w, img, dev)
+    direct = gpu_forward(dict(w, x=w["x"][swap], y=w["y"][swap], z=w["z"][swap]),
+                         (img[0][swap], img[1][swap]), dev)
+    ref = oracle.forward(w["kx"], w["ky"], w["kz"], img[0], img[1], w["x"], w["y"], w["z"])
+    check("forward ramp chunks", *ramp, *ref)
+    check("forward direct chunks", *direct, *ref)
+    assert metrics.rel_l2(*ramp, direct[0].astype(np.float64), direct[1].astype(np.float64)) < 5e-5
+
+
+def test_forward_ramp_degenerate_steps_and_partial_chunk(dev):
+    """Samples whose x-step phase kx dx is 0, 1/4, 1/2 or -1/2 revolution, on
+    an L = 32 grid cut 5 voxels short (the last chunk is partial and takes
+    the direct path)."""
+    L = 32
+    x, y, z = inputs.grid_coords(L)
+    N = L ** 3 - 5
+    x, y, z = x[:N], y[:N], z[:N]
+    rng = np.random.default_rng(15)
+    M = 3000
+    kx = rng.choice(np.array([0.0, 8.0, 16.0, -16.0, 15.5, -0.25], np.float32), M)
+    ky, kz = (rng.uniform(-16, 16, M).astype(np.float32) for _ in range(2))
+    c = dict(kx=kx, ky=ky, kz=kz, Dr=kx, Di=kx, x=x, y=y, z=z)
+    img = inputs.random_image(N, seed=16)
+    D = gpu_forward(c, img, dev)
+    ref = oracle.forward(kx, ky, kz, img[0], img[1], x, y, z)
+    check("forward ramp degenerate steps", *D, *ref)
+
+
+def test_forward_mixed_chunks(dev):
+    """A grid with some voxels moved off it: their chunks are direct, the
+    rest ramp chunks, in one stream."""
+    L = 24
+    x, y, z = (a.copy() for a in inputs.grid_coords(L))
+    rng = np.random.default_rng(17)
+    moved = rng.choice(L ** 3, 50, replace=False)
+    x[moved] += np.float32(0.002)
+    k = inputs.make_kspace("random16")
+    c = dict(k, x=x, y=y, z=z)
+    img = inputs.random_image(L ** 3, seed=18)
+    D = gpu_forward(c, img, dev)
+    ref = oracle.forward(k["kx"], k["ky"], k["kz"], img[0], img[1], x, y, z)
+    check("forward mixed chunks", *D, *ref)
