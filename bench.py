@@ -123,7 +123,7 @@ def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 8) -> float:
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
     "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
-            "sha256": "df158e35a0a708f15dcaee1449a1251cb99dc05b0e66c26ace6b2f0ec804a81f",
+            "sha256": "5ef3acb66f15cb4557181db1f1a7fcb778c31b9ef15173e79aa71ab81bbbf874",
             "bytes_per_launch": (20164.0 * 2.0 + 16384 * 1.0) * 1024},
     "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
              "sha256": "52123b52ce807d2bcff36893bc7a982590104eada543d42e2961b7d7621770d0",

@@ -55,7 +55,9 @@
 namespace fhd {
 namespace {
 
-constexpr int kVox = 8;   // consecutive voxels per lane
+constexpr int kVox = 8;         // consecutive voxels per lane
+constexpr int kRampGroup = 4;   // samples per transcendental group on the ramp path
+static_assert(kChunk % kRampGroup == 0, "ramp groups tile a chunk");
 
 __global__ __launch_bounds__(kPackBlock) void fhd_pack_kernel(
     const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
@@ -140,35 +142,53 @@ __device__ __forceinline__ void accumulate_chunk_ramp(const float4 *ch, float x0
     const float(&skz)[kChunk] = f[2];
     const float(&psi)[kChunk] = f[3];
     const float(&amp)[kChunk] = f[4];
+    // the transcendentals of kRampGroup samples issue as one group at raised
+    // wave priority (longer groups let more of the other waves' VALU work
+    // pair up; 4 measured best)
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-        const float p0 = __builtin_fmaf(skx[u], x0, __builtin_fmaf(sky[u], y, __builtin_fmaf(skz[u], z, psi[u])));
-        const float d = skx[u] * dx;
+    for (int u0 = 0; u0 < kChunk; u0 += kRampGroup) {
+        float p0[kRampGroup], d[kRampGroup], c0[kRampGroup], s0[kRampGroup], cd[kRampGroup],
+            sd[kRampGroup];
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) {
+            const int u = u0 + t;
+            p0[t] = __builtin_fmaf(skx[u], x0, __builtin_fmaf(sky[u], y, __builtin_fmaf(skz[u], z, psi[u])));
+            d[t] = skx[u] * dx;
+        }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
-        const float c0 = __builtin_amdgcn_cosf(p0), s0 = __builtin_amdgcn_sinf(p0);
-        const float cd = __builtin_amdgcn_cosf(d), sd = __builtin_amdgcn_sinf(d);
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) {
+            c0[t] = __builtin_amdgcn_cosf(p0[t]);
+            s0[t] = __builtin_amdgcn_sinf(p0[t]);
+            cd[t] = __builtin_amdgcn_cosf(d[t]);
+            sd[t] = __builtin_amdgcn_sinf(d[t]);
+        }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
-        // w_0 = a e^{i 2 pi p0}; w_1 = w_0 e^{i 2 pi d}
-        float wr0 = amp[u] * c0, wi0 = amp[u] * s0;
-        float wr1 = __builtin_fmaf(wr0, cd, -wi0 * sd);
-        float wi1 = __builtin_fmaf(wi0, cd, wr0 * sd);
-        const float two_cd = cd + cd;
-        acc_r[0] += wr0;
-        acc_i[0] += wi0;
-        acc_r[1] += wr1;
-        acc_i[1] += wi1;
 #pragma unroll
-        for (int v = 2; v < V; ++v) {
-            const float wr2 = __builtin_fmaf(two_cd, wr1, -wr0);
-            const float wi2 = __builtin_fmaf(two_cd, wi1, -wi0);
-            acc_r[v] += wr2;
-            acc_i[v] += wi2;
-            wr0 = wr1;
-            wi0 = wi1;
-            wr1 = wr2;
-            wi1 = wi2;
+        for (int t = 0; t < kRampGroup; ++t) {
+            const int u = u0 + t;
+            // w_0 = a e^{i 2 pi p0}; w_1 = w_0 e^{i 2 pi d}
+            float wr0 = amp[u] * c0[t], wi0 = amp[u] * s0[t];
+            float wr1 = __builtin_fmaf(wr0, cd[t], -wi0 * sd[t]);
+            float wi1 = __builtin_fmaf(wi0, cd[t], wr0 * sd[t]);
+            const float two_cd = cd[t] + cd[t];
+            acc_r[0] += wr0;
+            acc_i[0] += wi0;
+            acc_r[1] += wr1;
+            acc_i[1] += wi1;
+#pragma unroll
+            for (int v = 2; v < V; ++v) {
+                const float wr2 = __builtin_fmaf(two_cd, wr1, -wr0);
+                const float wi2 = __builtin_fmaf(two_cd, wi1, -wi0);
+                acc_r[v] += wr2;
+                acc_i[v] += wi2;
+                wr0 = wr1;
+                wi0 = wi1;
+                wr1 = wr2;
+                wi1 = wi2;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }

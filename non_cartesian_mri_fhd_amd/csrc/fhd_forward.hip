@@ -37,7 +37,9 @@
 namespace fhd {
 namespace {
 
-constexpr int kSamp = 8;   // consecutive samples per lane
+constexpr int kSamp = 8;        // consecutive samples per lane
+constexpr int kRampGroup = 2;   // samples per transcendental group on ramp chunks
+static_assert(kSamp % kRampGroup == 0, "ramp groups tile a lane's samples");
 
 __global__ __launch_bounds__(kPackBlock) void fhd_forward_pack_kernel(
     const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
@@ -87,26 +89,44 @@ __device__ __forceinline__ void accumulate_ramp_chunk(const float (&f)[kFields][
                                                       float (&acc_i)[S])
 {
     const float x0 = f[2][0], dx = f[2][1], y = f[2][2], z = f[2][3];
+    // the transcendentals of kRampGroup samples issue as one group at raised
+    // wave priority (2 measured best)
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-        const float p = __builtin_fmaf(kx[j], x0, __builtin_fmaf(ky[j], y, kz[j] * z));
-        const float d = kx[j] * dx;
+    for (int j0 = 0; j0 < S; j0 += kRampGroup) {
+        float p[kRampGroup], d[kRampGroup], er[kRampGroup], ei[kRampGroup], zr[kRampGroup],
+            zi[kRampGroup];
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) {
+            const int j = j0 + t;
+            p[t] = __builtin_fmaf(kx[j], x0, __builtin_fmaf(ky[j], y, kz[j] * z));
+            d[t] = kx[j] * dx;
+        }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
-        const float er = __builtin_amdgcn_cosf(p), ei = __builtin_amdgcn_sinf(p);
-        const float zr = __builtin_amdgcn_cosf(d), zi = __builtin_amdgcn_sinf(d);
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) {
+            er[t] = __builtin_amdgcn_cosf(p[t]);
+            ei[t] = __builtin_amdgcn_sinf(p[t]);
+            zr[t] = __builtin_amdgcn_cosf(d[t]);
+            zi[t] = __builtin_amdgcn_sinf(d[t]);
+        }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
-        float hr = f[0][kChunk - 1], hi = f[1][kChunk - 1];
 #pragma unroll
-        for (int u = kChunk - 2; u >= 0; --u) {
-            const float tr = __builtin_fmaf(hr, zr, __builtin_fmaf(-hi, zi, f[0][u]));
-            const float ti = __builtin_fmaf(hr, zi, __builtin_fmaf(hi, zr, f[1][u]));
-            hr = tr;
-            hi = ti;
+        for (int t = 0; t < kRampGroup; ++t) {
+            const int j = j0 + t;
+            float hr = f[0][kChunk - 1], hi = f[1][kChunk - 1];
+#pragma unroll
+            for (int u = kChunk - 2; u >= 0; --u) {
+                const float tr = __builtin_fmaf(hr, zr[t], __builtin_fmaf(-hi, zi[t], f[0][u]));
+                const float ti = __builtin_fmaf(hr, zi[t], __builtin_fmaf(hi, zr[t], f[1][u]));
+                hr = tr;
+                hi = ti;
+            }
+            acc_r[j] = __builtin_fmaf(er[t], hr, __builtin_fmaf(-ei[t], hi, acc_r[j]));
+            acc_i[j] = __builtin_fmaf(er[t], hi, __builtin_fmaf(ei[t], hr, acc_i[j]));
         }
-        acc_r[j] = __builtin_fmaf(er, hr, __builtin_fmaf(-ei, hi, acc_r[j]));
-        acc_i[j] = __builtin_fmaf(er, hi, __builtin_fmaf(ei, hr, acc_i[j]));
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
