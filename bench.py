@@ -11,7 +11,7 @@ event timing on the launch stream), the sampled parity against the fp64
 oracle and the oracle's own CPU throughput on that sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--op fhd|forward|normal|cg|grid]
+                    [--op fhd|forward|normal|cg|grid|grid_bf16x3]
 
 --op selects the operator timed (default fhd, the headline F^H D):
 forward = D = F rho; normal = F^H F rho (2 N M terms per step); cg = a
@@ -19,7 +19,10 @@ forward = D = F rho; normal = F^H F rho (2 N M terms per step); cg = a
 F^H F, two inner products and the vector updates; 7 N M terms per step);
 grid = F^H D with the voxels on the workload's Cartesian grid, as a
 complex matrix product on the fp32 matrix cores (fhd_pack +
-fhd_grid_gather; N M terms per step, priced against the fp32 MFMA peak).
+fhd_grid_gather; N M terms per step, priced against the fp32 MFMA peak);
+grid_bf16x3 = the same product with each fp32 operand split into two bf16
+parts and three bf16 products per real product (priced as 24 FLOP per
+term against the 2.5 PFLOP/s dense bf16 peak).
 """
 from __future__ import annotations
 
@@ -54,6 +57,7 @@ FLOP_PER_TERM = 13
 # on the matrix cores, whose dense fp32 peak is 157.3 TFLOP/s
 MFMA_FLOP_PER_TERM = 8
 P_MFMA_FP32 = 157.3e12
+P_MFMA_BF16 = 2.5e15
 TRANS_PER_TERM_DIRECT = 2.0
 TRANS_PER_TERM_RAMP = 4.0 / 8
 ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / TRANS_PER_TERM_DIRECT)
@@ -149,7 +153,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="spiral128")
-    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid"])
+    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid", "grid_bf16x3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -358,7 +362,8 @@ def bench_other(args) -> int:
             binding.fhd_forward_gather(vox, N, t["kx"], t["ky"], t["kz"], Dr, Di)
         dominant = "fhd_forward_gather_kernel"
         terms_per_step = float(N) * M
-    elif args.op == "grid":
+    elif args.op in ("grid", "grid_bf16x3"):
+        precision = binding.FHD_GRID_BF16X3 if args.op == "grid_bf16x3" else binding.FHD_GRID_FP32
         L = inputs.WORKLOADS[args.workload].L
         axis = inputs.grid_axis_of(L)
         packed = binding.new_packed(M, dev)
@@ -369,8 +374,9 @@ def bench_other(args) -> int:
             binding.fhd_pack(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], packed)
 
         def main_kernel():
-            binding.fhd_grid_gather(packed, M, (L, L, L), axis, rr, ri)
-        dominant = "fhd_grid_kernel + reduce_splits_kernel"
+            binding.fhd_grid_gather(packed, M, (L, L, L), axis, rr, ri, precision=precision)
+        dominant = ("fhd_grid_bf16x3_kernel" if args.op == "grid_bf16x3" else "fhd_grid_kernel") + \
+            " + reduce_splits_kernel"
         terms_per_step = float(N) * M
     elif args.op == "normal":
         qr = torch.empty(N, device=dev)
@@ -441,8 +447,16 @@ def bench_other(args) -> int:
                            "peak": P_MFMA_FP32 / 1e12, "unit": "TFLOP/s",
                            "frac": achieved / P_MFMA_FP32,
                            "traffic": measured_traffic("grid", args.workload)}
+    elif args.op == "grid_bf16x3":
+        # three bf16 products per real product: 3 x 8 FLOP per term on the
+        # bf16 matrix cores (2.5 PFLOP/s dense)
+        achieved = 3 * MFMA_FLOP_PER_TERM * k_rate
+        out["dtype"] = "bf16x3 (fp32 accumulation)"
+        out["roofline"] = {"bound": "mfma", "achieved": achieved / 1e12,
+                           "peak": P_MFMA_BF16 / 1e12, "unit": "TFLOP/s",
+                           "frac": achieved / P_MFMA_BF16, "traffic": None}
     if not args.no_cpu_baseline:
-        if args.op == "grid":
+        if args.op in ("grid", "grid_bf16x3"):
             base, parity = cpu_baseline(w, args.workload, args.cpu_seconds,
                                         rr.cpu().numpy(), ri.cpu().numpy())
         elif args.op == "forward":

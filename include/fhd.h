@@ -43,6 +43,13 @@ extern "C" {
 #define FHD_ERR_HIP (-2)         /* a HIP runtime or launch error */
 #define FHD_ERR_ALLOC (-3)       /* the library could not get its workspace */
 
+/* Arithmetic of the grid form's matrix products (fhd_compute_grid). */
+#define FHD_GRID_FP32 0   /* fp32 matrix-core products, fp32 accumulation */
+#define FHD_GRID_BF16X3 1 /* each fp32 operand split into two bf16 parts,
+                             three bf16 products per fp32 product (the
+                             lo x lo part, under 2^-17 relative, dropped),
+                             fp32 accumulation */
+
 /*
  * rho = F^H D over N voxels and M samples (section 17.3, F^H D equation).
  * Runs the loop-fission pre-pass (fhd_pack, section 17.3.2) into a
@@ -173,11 +180,14 @@ int fhd_normal(const float *kx, const float *ky, const float *kz,
  * over the axes). Voxel n = ix + nx*(iy + ny*iz) has coordinates
  * (x0 + ix*dx, y0 + iy*dy, z0 + iz*dz), each computed in double and rounded
  * once to fp32; with explicit coordinate arrays holding those values, the
- * result equals fhd_compute's up to fp32 rounding.
+ * result equals fhd_compute's up to rounding.
  *   kx, ky, kz, Dr, Di : M fp32 values each (read only)
  *   nx, ny, nz >= 0    : grid size, nx*ny*nz < 2^31
  *   axis               : HOST array of 6 floats {x0, dx, y0, dy, z0, dz},
  *                        finite, read during the call
+ *   precision          : FHD_GRID_FP32 or FHD_GRID_BF16X3 (about 1e-5
+ *                        relative per term, within the same tolerance as
+ *                        fp32 here, and several times faster)
  *   rho_r, rho_i       : nx*ny*nz fp32 values each (written), not
  *                        overlapping any input
  * Runs fhd_pack into a stream-ordered workspace, then fhd_grid_gather.
@@ -186,17 +196,18 @@ int fhd_normal(const float *kx, const float *ky, const float *kz,
  */
 int fhd_compute_grid(const float *kx, const float *ky, const float *kz,
                      const float *Dr, const float *Di, int M,
-                     int nx, int ny, int nz, const float *axis,
+                     int nx, int ny, int nz, const float *axis, int precision,
                      float *rho_r, float *rho_i, void *stream);
 
 /*
  * The matrix-core gather of fhd_compute_grid over k-space packed by
- * fhd_pack (same M; 16-byte aligned). Same grid arguments and outputs.
- * Repeated calls are bitwise identical. Errors: FHD_ERR_INVALID_ARG,
- * FHD_ERR_ALLOC (split partial sums), FHD_ERR_HIP.
+ * fhd_pack (same M; 16-byte aligned). Same grid arguments, precision and
+ * outputs. Repeated calls are bitwise identical. Errors:
+ * FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC (split partial sums), FHD_ERR_HIP.
  */
 int fhd_grid_gather(const void *packed, int M, int nx, int ny, int nz,
-                    const float *axis, float *rho_r, float *rho_i, void *stream);
+                    const float *axis, int precision, float *rho_r, float *rho_i,
+                    void *stream);
 
 /*
  * Conjugate-gradient reconstruction (page "Case study -- iterative MRI

@@ -19,6 +19,8 @@ FHD_OK = 0
 FHD_ERR_INVALID_ARG = -1
 FHD_ERR_HIP = -2
 FHD_ERR_ALLOC = -3
+FHD_GRID_FP32 = 0
+FHD_GRID_BF16X3 = 1
 
 LIBRARY = lib_path("libfhd.so")
 
@@ -74,9 +76,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_cg_workspace_bytes.argtypes = [i32, i32, i32]
     lib.fhd_cg_workspace_bytes.restype = i64
     fpp = ctypes.POINTER(ctypes.c_float)
-    lib.fhd_compute_grid.argtypes = [fp] * 5 + [i32] * 4 + [fpp, fp, fp, vp]
+    lib.fhd_compute_grid.argtypes = [fp] * 5 + [i32] * 4 + [fpp, i32, fp, fp, vp]
     lib.fhd_compute_grid.restype = i32
-    lib.fhd_grid_gather.argtypes = [vp] + [i32] * 4 + [fpp, fp, fp, vp]
+    lib.fhd_grid_gather.argtypes = [vp] + [i32] * 4 + [fpp, i32, fp, fp, vp]
     lib.fhd_grid_gather.restype = i32
     lib.fhd_gather_config.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
     lib.fhd_gather_config.restype = None
@@ -286,7 +288,8 @@ def _axis(axis):
     return a
 
 
-def fhd_compute_grid(kx, ky, kz, Dr, Di, shape, axis, rho_r=None, rho_i=None, stream=None):
+def fhd_compute_grid(kx, ky, kz, Dr, Di, shape, axis, rho_r=None, rho_i=None, stream=None,
+                     precision: int = FHD_GRID_FP32):
     """F^H D on the grid shape = (nx, ny, nz), axis = (x0, dx, y0, dy, z0, dz);
     voxel n = ix + nx*(iy + ny*iz). Returns (rho_r, rho_i) on kx's device."""
     lib = load()
@@ -301,12 +304,13 @@ def fhd_compute_grid(kx, ky, kz, Dr, Di, shape, axis, rho_r=None, rho_i=None, st
                                                (Dr, "Dr"), (Di, "Di"))]
     outs = [_vec(t, nm, N, dev) for t, nm in ((rho_r, "rho_r"), (rho_i, "rho_i"))]
     with torch.cuda.device(dev):
-        _check(lib, lib.fhd_compute_grid(*ptrs, M, nx, ny, nz, _axis(axis), *outs,
+        _check(lib, lib.fhd_compute_grid(*ptrs, M, nx, ny, nz, _axis(axis), int(precision), *outs,
                                          _stream(dev, stream)), "fhd_compute_grid")
     return rho_r, rho_i
 
 
-def fhd_grid_gather(packed, M: int, shape, axis, rho_r=None, rho_i=None, stream=None):
+def fhd_grid_gather(packed, M: int, shape, axis, rho_r=None, rho_i=None, stream=None,
+                    precision: int = FHD_GRID_FP32):
     """Matrix-core gather over k-space packed by fhd_pack; see fhd_compute_grid."""
     lib = load()
     nx, ny, nz = (int(v) for v in shape)
@@ -323,7 +327,8 @@ def fhd_grid_gather(packed, M: int, shape, axis, rho_r=None, rho_i=None, stream=
     outs = [_vec(t, nm, N, dev) for t, nm in ((rho_r, "rho_r"), (rho_i, "rho_i"))]
     with torch.cuda.device(dev):
         _check(lib, lib.fhd_grid_gather(packed.data_ptr(), int(M), nx, ny, nz, _axis(axis),
-                                        *outs, _stream(dev, stream)), "fhd_grid_gather")
+                                        int(precision), *outs, _stream(dev, stream)),
+               "fhd_grid_gather")
     return rho_r, rho_i
 
 

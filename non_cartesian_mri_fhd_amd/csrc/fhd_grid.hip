@@ -39,6 +39,9 @@ namespace fhd {
 namespace {
 
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int kTileYZ = 32;           // A rows per wave
 constexpr int kTilesX = 2;            // 32-column B tiles per wave
@@ -149,22 +152,156 @@ __global__ __launch_bounds__(kBlock) void fhd_grid_kernel(
     }
 }
 
-// Workgroups of fhd_grid_kernel that fit on one CU at once (its register
-// budget allows 3 waves per SIMD); asked of the runtime once per device.
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both rounded to
+// nearest even: hi + lo carries 16 significant bits, x - (hi + lo) is
+// within 2^-17 |x|. Two values per v_cvt_pk_bf16_f32; the bf16 hi parts
+// widen back to fp32 by a shift (low half) or a mask (high half).
+__device__ __forceinline__ void split_bf16(const float (&x)[kChunk], bf16x8 &hi, bf16x8 &lo)
+{
+#pragma unroll
+    for (int i = 0; i < kChunk; i += 2) {
+        const bf16x2 h = __builtin_convertvector((float2v){x[i], x[i + 1]}, bf16x2);
+        const unsigned u = __builtin_bit_cast(unsigned, h);
+        const float h0 = __builtin_bit_cast(float, u << 16);
+        const float h1 = __builtin_bit_cast(float, u & 0xffff0000u);
+        const bf16x2 l = __builtin_convertvector((float2v){x[i] - h0, x[i + 1] - h1}, bf16x2);
+        hi[i] = h[0];
+        hi[i + 1] = h[1];
+        lo[i] = l[0];
+        lo[i + 1] = l[1];
+    }
+}
+
+// The same product with bf16 matrix-core instructions in three passes:
+// a b = a_hi b_hi + a_hi b_lo + a_lo b_hi (a_lo b_lo, below 2^-17 |a b|,
+// dropped), accumulated in fp32 by v_mfma_f32_32x32x16_bf16. One such
+// instruction takes 16 samples; lane l supplies A[l % 32][8 (l / 32) + i]
+// and B[8 (l / 32) + i][l % 32], i < 8 (layout measured), so the two
+// half-waves take one chunk of 8 samples each, and the accumulator layout
+// is the fp32 instruction's. Same workgroup tiling as fhd_grid_kernel.
+__global__ __launch_bounds__(kBlock) void fhd_grid_bf16x3_kernel(
+    const float *__restrict__ packed, int nchunks, int splits, int nx, int ny, int64_t nyz,
+    int tiles_x, GridAxis g, float *__restrict__ out_r, float *__restrict__ out_i)
+{
+    __shared__ float4 stage[2][kStageVec4];
+    const float4 *src = reinterpret_cast<const float4 *>(packed);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+
+    const int bx = blockIdx.x % tiles_x;
+    const int64_t yz0 = (int64_t)(blockIdx.x / tiles_x) * (kTileYZ * kWaves) + (int64_t)wave * kTileYZ;
+    const int64_t yz = yz0 + col;
+    const float ry = grid_coord(g.y0, g.dy, yz % ny);
+    const float rz = grid_coord(g.z0, g.dz, yz / ny);
+    float cx[kTilesX];
+#pragma unroll
+    for (int t = 0; t < kTilesX; ++t) cx[t] = grid_coord(g.x0, g.dx, bx * (32 * kTilesX) + 32 * t + col);
+
+    float16v acc_r[kTilesX], acc_i[kTilesX];
+#pragma unroll
+    for (int t = 0; t < kTilesX; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc_r[t][r] = 0.0f;
+            acc_i[t][r] = 0.0f;
+        }
+
+    int c0, c1;
+    split_range(nchunks, splits, blockIdx.y, &c0, &c1);
+    stream_chunk_groups<2>(src, c0, c1, stage, [&](const float4 *ch, int count) {
+        // half-wave h takes chunk h of the pair; a missing second chunk (odd
+        // stream end) is eight zero-amplitude samples
+        float f[kFields][kChunk];
+        if (half < count) {
+            load_chunk(ch + half * kChunkVec4, f);
+        } else {
+#pragma unroll
+            for (int q = 0; q < kFields; ++q)
+#pragma unroll
+                for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
+        }
+        __builtin_amdgcn_s_setprio(1);
+        // A elements of this lane's row: a e^{i 2 pi (ky y + kz z + psi)}
+        float ar[kChunk], ai[kChunk];
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const float q = __builtin_fmaf(f[1][u], ry, __builtin_fmaf(f[2][u], rz, f[3][u]));
+            ar[u] = f[4][u] * __builtin_amdgcn_cosf(q);
+            ai[u] = f[4][u] * __builtin_amdgcn_sinf(q);
+        }
+        bf16x8 arh, arl, aih, ail;
+        split_bf16(ar, arh, arl);
+        split_bf16(ai, aih, ail);
+        const bf16x8 naih = -aih, nail = -ail;
+#pragma unroll
+        for (int t = 0; t < kTilesX; ++t) {
+            // B elements of this lane's column: e^{i 2 pi kx x}
+            float br[kChunk], bi[kChunk];
+#pragma unroll
+            for (int u = 0; u < kChunk; ++u) {
+                const float p = f[0][u] * cx[t];
+                br[u] = __builtin_amdgcn_cosf(p);
+                bi[u] = __builtin_amdgcn_sinf(p);
+            }
+            bf16x8 brh, brl, bih, bil;
+            split_bf16(br, brh, brl);
+            split_bf16(bi, bih, bil);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+            // real part: a_r b_r - a_i b_i; imaginary part: a_r b_i + a_i b_r
+            acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, brh, acc_r[t], 0, 0, 0);
+            acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bih, acc_i[t], 0, 0, 0);
+            acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, brl, acc_r[t], 0, 0, 0);
+            acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bil, acc_i[t], 0, 0, 0);
+            acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arl, brh, acc_r[t], 0, 0, 0);
+            acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arl, bih, acc_i[t], 0, 0, 0);
+            acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(naih, bih, acc_r[t], 0, 0, 0);
+            acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, brh, acc_i[t], 0, 0, 0);
+            acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(naih, bil, acc_r[t], 0, 0, 0);
+            acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, brl, acc_i[t], 0, 0, 0);
+            acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(nail, bih, acc_r[t], 0, 0, 0);
+            acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ail, brh, acc_i[t], 0, 0, 0);
+            __builtin_amdgcn_s_setprio(1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    });
+
+    const int64_t N = nyz * nx;
+    float *dst_r = out_r + (int64_t)blockIdx.y * N, *dst_i = out_i + (int64_t)blockIdx.y * N;
+#pragma unroll
+    for (int t = 0; t < kTilesX; ++t) {
+        const int ix = bx * (32 * kTilesX) + 32 * t + col;
+        if (ix >= nx) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = yz0 + 8 * (r / 4) + 4 * half + (r % 4);
+            if (row < nyz) {
+                dst_r[row * nx + ix] = acc_r[t][r];
+                dst_i[row * nx + ix] = acc_i[t][r];
+            }
+        }
+    }
+}
+
+// Workgroups of a grid kernel that fit on one CU at once (its register
+// budget), asked of the runtime once per device and kernel.
+template <int PRECISION>
 int grid_blocks_per_cu()
 {
     static int cached[64] = {0};
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= 64) {
         (void)hipGetLastError();
-        return 3;
+        return 2;
     }
     if (cached[device] == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fhd_grid_kernel, kBlock, 0) != hipSuccess ||
-            n <= 0) {
+        const void *kernel = PRECISION == FHD_GRID_BF16X3 ? (const void *)fhd_grid_bf16x3_kernel
+                                                          : (const void *)fhd_grid_kernel;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n <= 0) {
             (void)hipGetLastError();
-            n = 3;
+            n = 2;
         }
         cached[device] = n;
     }
@@ -174,21 +311,29 @@ int grid_blocks_per_cu()
 }  // namespace
 
 int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const float *axis,
-                       float *rho_r, float *rho_i, hipStream_t stream)
+                       int precision, float *rho_r, float *rho_i, hipStream_t stream)
 {
     const int64_t nyz = (int64_t)ny * nz, N = nyz * nx;
     if (N == 0) return FHD_OK;
+    const bool bf16x3 = precision == FHD_GRID_BF16X3;
     const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
     const int tiles_x = (nx + 32 * kTilesX - 1) / (32 * kTilesX);
     const int64_t slabs = (nyz + kTileYZ * kWaves - 1) / (kTileYZ * kWaves);
     const int64_t blocks = slabs * tiles_x;
     const GridAxis g{axis[0], axis[1], axis[2], axis[3], axis[4], axis[5]};
-    const int splits = split_count(blocks, nchunks, grid_blocks_per_cu());
-    if (splits == 1) {
-        fhd_grid_kernel<<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
-            packed, nchunks, 1, nx, ny, nyz, tiles_x, g, rho_r, rho_i);
-        return launch_status("fhd_grid_kernel launch");
-    }
+    const int per_cu = bf16x3 ? grid_blocks_per_cu<FHD_GRID_BF16X3>() : grid_blocks_per_cu<FHD_GRID_FP32>();
+    const int splits = split_count(blocks, nchunks, per_cu);
+    auto launch = [&](int nsplit, float *out_r, float *out_i) {
+        const dim3 grid((unsigned)blocks, (unsigned)nsplit);
+        if (bf16x3)
+            fhd_grid_bf16x3_kernel<<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, nsplit, nx, ny, nyz,
+                                                                     tiles_x, g, out_r, out_i);
+        else
+            fhd_grid_kernel<<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, nsplit, nx, ny, nyz,
+                                                              tiles_x, g, out_r, out_i);
+        return launch_status(bf16x3 ? "fhd_grid_bf16x3_kernel launch" : "fhd_grid_kernel launch");
+    };
+    if (splits == 1) return launch(1, rho_r, rho_i);
     float *part = nullptr;
     const hipError_t e = hipMallocAsync((void **)&part, (size_t)splits * 2 * N * sizeof(float), stream);
     if (e != hipSuccess) {
@@ -197,9 +342,7 @@ int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const
                                        hipGetErrorString(e));
     }
     float *part_r = part, *part_i = part + (int64_t)splits * N;
-    fhd_grid_kernel<<<dim3((unsigned)blocks, (unsigned)splits), dim3(kBlock), 0, stream>>>(
-        packed, nchunks, splits, nx, ny, nyz, tiles_x, g, part_r, part_i);
-    int rc = launch_status("fhd_grid_kernel launch");
+    int rc = launch(splits, part_r, part_i);
     if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, N, rho_r, rho_i, stream);
     const hipError_t f = hipFreeAsync(part, stream);
     if (f != hipSuccess && rc == FHD_OK)
@@ -212,9 +355,11 @@ int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const
 using namespace fhd;
 
 namespace {
-int check_grid_args(int M, int nx, int ny, int nz, const float *axis, int64_t *N)
+int check_grid_args(int M, int nx, int ny, int nz, const float *axis, int precision, int64_t *N)
 {
     if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
+    if (precision != FHD_GRID_FP32 && precision != FHD_GRID_BF16X3)
+        return fail(FHD_ERR_INVALID_ARG, "precision must be FHD_GRID_FP32 or FHD_GRID_BF16X3");
     if (nx < 0 || ny < 0 || nz < 0) return fail(FHD_ERR_INVALID_ARG, "negative grid size");
     const int64_t n = (int64_t)nx * ny * nz;
     if (n > INT32_MAX) return fail(FHD_ERR_INVALID_ARG, "nx*ny*nz exceeds 2^31 - 1");
@@ -227,11 +372,11 @@ int check_grid_args(int M, int nx, int ny, int nz, const float *axis, int64_t *N
 }  // namespace
 
 extern "C" int fhd_grid_gather(const void *packed, int M, int nx, int ny, int nz, const float *axis,
-                               float *rho_r, float *rho_i, void *stream)
+                               int precision, float *rho_r, float *rho_i, void *stream)
 {
     clear_error();
     int64_t N = 0;
-    int rc = check_grid_args(M, nx, ny, nz, axis, &N);
+    int rc = check_grid_args(M, nx, ny, nz, axis, precision, &N);
     if (rc != FHD_OK || N == 0) return rc;
     const int64_t nb = N * 4;
     const Span all[] = {{packed, M > 0 ? packed_bytes_for(M) : 0, "packed", 16},
@@ -240,17 +385,17 @@ extern "C" int fhd_grid_gather(const void *packed, int M, int nx, int ny, int nz
     if (rc == FHD_OK) rc = check_no_overlap(all, 3, 1);
     if (rc == FHD_OK) rc = check_device_spans(all, 3);
     if (rc != FHD_OK) return rc;
-    return launch_grid_gather((const float *)packed, M, nx, ny, nz, axis, rho_r, rho_i,
+    return launch_grid_gather((const float *)packed, M, nx, ny, nz, axis, precision, rho_r, rho_i,
                               (hipStream_t)stream);
 }
 
 extern "C" int fhd_compute_grid(const float *kx, const float *ky, const float *kz, const float *Dr,
                                 const float *Di, int M, int nx, int ny, int nz, const float *axis,
-                                float *rho_r, float *rho_i, void *stream)
+                                int precision, float *rho_r, float *rho_i, void *stream)
 {
     clear_error();
     int64_t N = 0;
-    int rc = check_grid_args(M, nx, ny, nz, axis, &N);
+    int rc = check_grid_args(M, nx, ny, nz, axis, precision, &N);
     if (rc != FHD_OK || N == 0) return rc;
     const int64_t mb = (int64_t)M * 4, nb = N * 4;
     const Span all[] = {{kx, mb, "kx"}, {ky, mb, "ky"}, {kz, mb, "kz"}, {Dr, mb, "Dr"},
@@ -269,7 +414,7 @@ extern "C" int fhd_compute_grid(const float *kx, const float *ky, const float *k
         }
         rc = launch_pack(kx, ky, kz, Dr, Di, M, packed, s);
     }
-    if (rc == FHD_OK) rc = launch_grid_gather(packed, M, nx, ny, nz, axis, rho_r, rho_i, s);
+    if (rc == FHD_OK) rc = launch_grid_gather(packed, M, nx, ny, nz, axis, precision, rho_r, rho_i, s);
     if (packed) {
         const hipError_t e = hipFreeAsync(packed, s);
         if (e != hipSuccess && rc == FHD_OK)

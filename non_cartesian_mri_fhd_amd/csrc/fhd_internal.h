@@ -76,13 +76,18 @@ __device__ __forceinline__ void load_chunk(const float4 *ch, float (&f)[kFields]
 }
 
 // Streams chunks [c_begin, c_end) of `src` through the workgroup's LDS
-// stage buffers and calls body(chunk) for each chunk in order, in every
-// lane. Every lane of the workgroup must call it (it holds workgroup
-// barriers). Chunks past the end of `src` are never read.
-template <typename Body>
-__device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, int c_begin,
-                                              int c_end, float4 (*stage)[kStageVec4], Body &&body)
+// stage buffers and calls body(chunks, count) for every STEP consecutive
+// chunks of a stage, in order, in every lane: `chunks` points at the first
+// of them in LDS and `count` (1..STEP) says how many are valid (fewer only
+// at the end of the stream; the LDS beyond them holds stale data and must
+// not be read). Every lane of the workgroup must call it (it holds
+// workgroup barriers). Chunks past the end of `src` are never read.
+template <int STEP, typename Body>
+__device__ __forceinline__ void stream_chunk_groups(const float4 *__restrict__ src, int c_begin,
+                                                    int c_end, float4 (*stage)[kStageVec4],
+                                                    Body &&body)
 {
+    static_assert(kStageChunks % STEP == 0, "chunk groups tile a stage");
     const int nchunks = c_end > c_begin ? c_end - c_begin : 0;
     src += (int64_t)c_begin * kChunkVec4;
     const int64_t total_vec4 = (int64_t)nchunks * kChunkVec4;
@@ -103,7 +108,7 @@ __device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, in
         }
         const int chunks_here = min(kStageChunks, nchunks - st * kStageChunks);
         const float4 *buf = stage[st & 1];
-        for (int c = 0; c < chunks_here; ++c) body(buf + c * kChunkVec4);
+        for (int c = 0; c < chunks_here; c += STEP) body(buf + c * kChunkVec4, min(STEP, chunks_here - c));
         if (more) {
             // the other buffer was last read before the previous barrier
             float4 *dst = stage[(st + 1) & 1];
@@ -115,6 +120,15 @@ __device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, in
         }
         __syncthreads();
     }
+}
+
+// stream_chunk_groups one chunk at a time: body(chunk).
+template <typename Body>
+__device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, int c_begin,
+                                              int c_end, float4 (*stage)[kStageVec4], Body &&body)
+{
+    stream_chunk_groups<1>(src, c_begin, c_end, stage,
+                           [&](const float4 *ch, int) { body(ch); });
 }
 
 // Chunk range of split `s` when nchunks chunks are cut into `splits` parts
@@ -181,6 +195,6 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
                           const float *kz, float *Dr, float *Di, int M, hipStream_t stream);
 // fhd_grid.hip: F^H D on a Cartesian grid (axis = x0, dx, y0, dy, z0, dz)
 int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const float *axis,
-                       float *rho_r, float *rho_i, hipStream_t stream);
+                       int precision, float *rho_r, float *rho_i, hipStream_t stream);
 
 }  // namespace fhd

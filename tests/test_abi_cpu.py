@@ -33,8 +33,8 @@ def lib():
     lib.fhd_cg_workspace_bytes.restype = ctypes.c_int64
     lib.fhd_forward.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
     lib.fhd_normal.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
-    lib.fhd_compute_grid.argtypes = [vp] * 5 + [ctypes.c_int] * 4 + [vp] * 4
-    lib.fhd_grid_gather.argtypes = [vp] + [ctypes.c_int] * 4 + [vp] * 4
+    lib.fhd_compute_grid.argtypes = [vp] * 5 + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 3
+    lib.fhd_grid_gather.argtypes = [vp] + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 3
     lib.fhd_last_error.restype = ctypes.c_char_p
     lib.fhd_status_string.restype = ctypes.c_char_p
     return lib
@@ -185,31 +185,35 @@ def test_grid_argument_checks(lib):
     axis = (ctypes.c_float * 6)(-0.5, 1 / 16, -0.5, 1 / 16, -0.5, 1 / 16)
     ax = ctypes.addressof(axis)
     fake = [0x100000 * (i + 1) for i in range(7)]
-    assert lib.fhd_compute_grid(*fake[:5], -1, 4, 4, 4, ax, *fake[5:], None) == FHD_ERR_INVALID_ARG
-    assert lib.fhd_compute_grid(*fake[:5], 8, 4, -4, 4, ax, *fake[5:], None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_compute_grid(*fake[:5], -1, 4, 4, 4, ax, 0, *fake[5:], None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_compute_grid(*fake[:5], 8, 4, -4, 4, ax, 0, *fake[5:], None) == FHD_ERR_INVALID_ARG
     assert "negative" in _last(lib)
-    assert lib.fhd_compute_grid(*fake[:5], 8, 2048, 2048, 1024, ax, *fake[5:], None) == \
+    assert lib.fhd_compute_grid(*fake[:5], 8, 2048, 2048, 1024, ax, 0, *fake[5:], None) == \
         FHD_ERR_INVALID_ARG
     assert "2^31" in _last(lib)
-    assert lib.fhd_compute_grid(*fake[:5], 8, 4, 4, 4, None, *fake[5:], None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_compute_grid(*fake[:5], 8, 4, 4, 4, None, 0, *fake[5:], None) == FHD_ERR_INVALID_ARG
     assert "axis" in _last(lib)
     bad = (ctypes.c_float * 6)(-0.5, float("inf"), -0.5, 0.1, -0.5, 0.1)
-    assert lib.fhd_compute_grid(*fake[:5], 8, 4, 4, 4, ctypes.addressof(bad), *fake[5:], None) == \
+    assert lib.fhd_compute_grid(*fake[:5], 8, 4, 4, 4, ctypes.addressof(bad), 0, *fake[5:], None) == \
         FHD_ERR_INVALID_ARG
     assert "finite" in _last(lib)
     # an empty grid does nothing, even with NULL buffers
-    assert lib.fhd_compute_grid(*[None] * 5, 8, 0, 4, 4, ax, None, None, None) == FHD_OK
-    assert lib.fhd_grid_gather(None, 8, 4, 4, 0, ax, None, None, None) == FHD_OK
+    assert lib.fhd_compute_grid(*[None] * 5, 8, 0, 4, 4, ax, 0, None, None, None) == FHD_OK
+    assert lib.fhd_grid_gather(None, 8, 4, 4, 0, ax, 0, None, None, None) == FHD_OK
     args = list(fake)
     args[2] = None                                                     # kz
-    assert lib.fhd_compute_grid(*args[:5], 8, 4, 4, 4, ax, *args[5:], None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_compute_grid(*args[:5], 8, 4, 4, 4, ax, 0, *args[5:], None) == FHD_ERR_INVALID_ARG
     assert "kz" in _last(lib)
     args = list(fake)
     args[6] = args[5] + 16                                             # rho_i overlaps rho_r
-    assert lib.fhd_compute_grid(*args[:5], 8, 4, 4, 4, ax, *args[5:], None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_compute_grid(*args[:5], 8, 4, 4, 4, ax, 0, *args[5:], None) == FHD_ERR_INVALID_ARG
     assert "overlaps" in _last(lib)
-    assert lib.fhd_grid_gather(fake[0] + 8, 8, 4, 4, 4, ax, fake[5], fake[6], None) == \
+    assert lib.fhd_grid_gather(fake[0] + 8, 8, 4, 4, 4, ax, 0, fake[5], fake[6], None) == \
         FHD_ERR_INVALID_ARG
     assert "16-byte" in _last(lib)
-    assert lib.fhd_grid_gather(fake[0], -8, 4, 4, 4, ax, fake[5], fake[6], None) == \
+    assert lib.fhd_grid_gather(fake[0], -8, 4, 4, 4, ax, 0, fake[5], fake[6], None) == \
         FHD_ERR_INVALID_ARG
+    for bad_precision in (-1, 2, 7):
+        assert lib.fhd_grid_gather(fake[0], 8, 4, 4, 4, ax, bad_precision, fake[5], fake[6],
+                                   None) == FHD_ERR_INVALID_ARG
+        assert "precision" in _last(lib)

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from non_cartesian_mri_fhd_amd import binding, build, inputs
+from non_cartesian_mri_fhd_amd import binding, build, inputs, metrics
 
 from pins import cartesian_fft_reference
 from test_gpu_parity import check
@@ -20,6 +20,7 @@ from test_gpu_parity import check
 pytestmark = pytest.mark.gpu
 
 ODD_AXIS = (0.3, 0.013, -0.2, 0.021, 0.11, -0.017)
+PRECISIONS = [binding.FHD_GRID_FP32, binding.FHD_GRID_BF16X3]
 
 
 @pytest.fixture(scope="module")
@@ -34,9 +35,9 @@ def t(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def gpu_grid(case, shape, axis, dev, out=None):
+def gpu_grid(case, shape, axis, dev, out=None, precision=binding.FHD_GRID_FP32):
     k = [t(case[a], dev) for a in ("kx", "ky", "kz", "Dr", "Di")]
-    rr, ri = binding.fhd_compute_grid(*k, shape, axis, *(out or (None, None)))
+    rr, ri = binding.fhd_compute_grid(*k, shape, axis, *(out or (None, None)), precision=precision)
     torch.cuda.synchronize(dev)
     return rr.cpu().numpy(), ri.cpu().numpy()
 
@@ -48,67 +49,75 @@ def oracle_on_grid(case, shape, axis, idx=None):
     return oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"], x, y, z)
 
 
+@pytest.mark.parametrize("prec", PRECISIONS)
 @pytest.mark.parametrize("name", ["random16", "spiral32"])
-def test_grid_workload_all_voxels(dev, name):
+def test_grid_workload_all_voxels(dev, name, prec):
     w = inputs.make_workload(name)
     L = inputs.WORKLOADS[name].L
-    rr, ri = gpu_grid(w, (L, L, L), inputs.grid_axis_of(L), dev)
+    rr, ri = gpu_grid(w, (L, L, L), inputs.grid_axis_of(L), dev, precision=prec)
     ref = oracle.fhd(w["kx"], w["ky"], w["kz"], w["Dr"], w["Di"], w["x"], w["y"], w["z"])
-    check("grid " + name, rr, ri, *ref)
+    check("grid %s precision %d" % (name, prec), rr, ri, *ref)
 
 
+@pytest.mark.parametrize("prec", PRECISIONS)
 @pytest.mark.parametrize("name,count", [("radial64", 8192), ("spiral128", 4096),
                                         ("vdrandom256", inputs.SUBSET_SIZE)])
-def test_grid_workload_sampled_voxels(dev, name, count):
+def test_grid_workload_sampled_voxels(dev, name, count, prec):
     """Full-size run in the benchmark's launch shape; the oracle computes a
     seeded voxel subset."""
     w = inputs.make_workload(name)
     L = inputs.WORKLOADS[name].L
-    rr, ri = gpu_grid(w, (L, L, L), inputs.grid_axis_of(L), dev)
+    rr, ri = gpu_grid(w, (L, L, L), inputs.grid_axis_of(L), dev, precision=prec)
     if name == "vdrandom256":
         idx = inputs.voxel_subset(w["N"])
     else:
         idx = inputs.voxel_subset(w["N"], count, seed=inputs.WORKLOADS[name].seed + 1000)
     ref_r, ref_i = oracle.fhd_subset(w, idx)
-    check("grid " + name, rr[idx], ri[idx], ref_r, ref_i)
+    check("grid %s precision %d" % (name, prec), rr[idx], ri[idx], ref_r, ref_i)
 
 
+@pytest.mark.parametrize("prec", PRECISIONS)
 @pytest.mark.parametrize("shape,M", [((1, 1, 1), 1), ((70, 5, 27), 1000), ((130, 3, 2), 7),
                                      ((64, 128, 1), 4097), ((33, 17, 9), 513),
-                                     ((7, 129, 2), 2049), ((1, 300, 1), 64)])
-def test_grid_ragged(dev, shape, M):
+                                     ((7, 129, 2), 2049), ((1, 300, 1), 64), ((40, 6, 5), 520),
+                                     ((40, 6, 5), 1016)])
+def test_grid_ragged(dev, shape, M, prec):
     """Grids whose edges cut the 64-column and 128-row tiles, sample counts
     off the 8-sample chunk and 512-sample stage, non-dyadic axis steps of
     either sign."""
     c = inputs.random_case(1, M, seed=M + shape[0])
-    rr, ri = gpu_grid(c, shape, ODD_AXIS, dev)
-    check("grid ragged %s M=%d" % (shape, M), rr, ri, *oracle_on_grid(c, shape, ODD_AXIS))
+    rr, ri = gpu_grid(c, shape, ODD_AXIS, dev, precision=prec)
+    check("grid ragged %s M=%d precision %d" % (shape, M, prec), rr, ri,
+          *oracle_on_grid(c, shape, ODD_AXIS))
 
 
-def test_grid_one_round_no_split(dev):
+@pytest.mark.parametrize("prec", PRECISIONS)
+def test_grid_one_round_no_split(dev, prec):
     """768 workgroups and 2 stages: the unsplit launch (one full round)."""
     shape, M = (64, 384, 256), 600
     c = inputs.random_case(1, M, seed=77)
-    rr, ri = gpu_grid(c, shape, ODD_AXIS, dev)
+    rr, ri = gpu_grid(c, shape, ODD_AXIS, dev, precision=prec)
     idx = inputs.voxel_subset(int(np.prod(shape)), 2048, seed=78)
     check("grid unsplit", rr[idx], ri[idx], *oracle_on_grid(c, shape, ODD_AXIS, idx))
 
 
+@pytest.mark.parametrize("prec", PRECISIONS)
 @pytest.mark.parametrize("L", [16, 32])
-def test_grid_cartesian_matches_fft(dev, L):
+def test_grid_cartesian_matches_fft(dev, L, prec):
     c = inputs.cartesian_case(L, seed=500 + L)
-    rr, ri = gpu_grid(c, (L, L, L), inputs.grid_axis_of(L), dev)
+    rr, ri = gpu_grid(c, (L, L, L), inputs.grid_axis_of(L), dev, precision=prec)
     ref = cartesian_fft_reference(c)
-    check("grid cartesian L=%d" % L, rr, ri, ref.real, ref.imag)
+    check("grid cartesian L=%d precision %d" % (L, prec), rr, ri, ref.real, ref.imag)
 
 
-def test_grid_no_samples_writes_zeros(dev):
+@pytest.mark.parametrize("prec", PRECISIONS)
+def test_grid_no_samples_writes_zeros(dev, prec):
     shape = (40, 9, 3)
     N = int(np.prod(shape))
     out = (torch.full((N,), 7.0, device=dev), torch.full((N,), -7.0, device=dev))
     e = np.zeros(0, np.float32)
     case = dict(kx=e, ky=e, kz=e, Dr=e, Di=e)
-    rr, ri = gpu_grid(case, shape, ODD_AXIS, dev, out)
+    rr, ri = gpu_grid(case, shape, ODD_AXIS, dev, out, precision=prec)
     assert not rr.any() and not ri.any()
 
 
@@ -119,17 +128,18 @@ def test_grid_empty_grid(dev):
         assert rr.shape == (0,) and ri.shape == (0,)
 
 
-def test_grid_repeatable_and_two_stage_equal(dev):
+@pytest.mark.parametrize("prec", PRECISIONS)
+def test_grid_repeatable_and_two_stage_equal(dev, prec):
     w = inputs.make_workload("spiral32")
     L = inputs.WORKLOADS["spiral32"].L
     axis = inputs.grid_axis_of(L)
-    a = gpu_grid(w, (L, L, L), axis, dev)
-    b = gpu_grid(w, (L, L, L), axis, dev)
+    a = gpu_grid(w, (L, L, L), axis, dev, precision=prec)
+    b = gpu_grid(w, (L, L, L), axis, dev, precision=prec)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     k = [t(w[n], dev) for n in ("kx", "ky", "kz", "Dr", "Di")]
     packed = binding.new_packed(w["M"], dev)
     binding.fhd_pack(*k, packed)
-    rr, ri = binding.fhd_grid_gather(packed, w["M"], (L, L, L), axis)
+    rr, ri = binding.fhd_grid_gather(packed, w["M"], (L, L, L), axis, precision=prec)
     torch.cuda.synchronize(dev)
     assert np.array_equal(rr.cpu().numpy(), a[0]) and np.array_equal(ri.cpu().numpy(), a[1])
 
@@ -144,3 +154,21 @@ def test_grid_agrees_with_direct_gather(dev):
     torch.cuda.synchronize(dev)
     check("grid vs direct", gr.cpu().numpy(), gi.cpu().numpy(),
           dr.cpu().numpy().astype(np.float64), di.cpu().numpy().astype(np.float64))
+
+
+def test_grid_bf16x3_close_to_fp32(dev):
+    """The split-bf16 products differ from the fp32 ones by about 1e-5 of the
+    result, well inside the gate; a wide dynamic range of |D| (1e-6 to 1e6)
+    stays accurate because bf16 keeps fp32's exponent range."""
+    rng = np.random.default_rng(33)
+    M = 5000
+    c = inputs.random_case(1, M, seed=34)
+    scale = (10.0 ** rng.uniform(-6, 6, M)).astype(np.float32)
+    c = dict(c, Dr=(c["Dr"] * scale).astype(np.float32), Di=(c["Di"] * scale).astype(np.float32))
+    shape = (48, 10, 7)
+    a = gpu_grid(c, shape, ODD_AXIS, dev, precision=binding.FHD_GRID_FP32)
+    b = gpu_grid(c, shape, ODD_AXIS, dev, precision=binding.FHD_GRID_BF16X3)
+    ref = oracle_on_grid(c, shape, ODD_AXIS)
+    check("grid wide range fp32", *a, *ref)
+    check("grid wide range bf16x3", *b, *ref)
+    assert metrics.rel_l2(*b, a[0].astype(np.float64), a[1].astype(np.float64)) < 1e-4
