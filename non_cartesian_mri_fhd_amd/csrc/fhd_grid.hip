@@ -41,6 +41,7 @@ namespace {
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int kTileYZ = 32;           // A rows per wave
@@ -154,36 +155,54 @@ __global__ __launch_bounds__(kBlock) void fhd_grid_kernel(
 
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both rounded to
 // nearest even: hi + lo carries 16 significant bits, x - (hi + lo) is
-// within 2^-17 |x|. Two values per v_cvt_pk_bf16_f32; the bf16 hi parts
-// widen back to fp32 by a shift (low half) or a mask (high half).
-__device__ __forceinline__ void split_bf16(const float (&x)[kChunk], bf16x8 &hi, bf16x8 &lo)
+// within 2^-17 |x|. Two values per v_cvt_pk_bf16_f32, packed as one dword
+// (element 2i in the low half); the bf16 hi parts widen back to fp32 by a
+// shift (low half) or a mask (high half).
+template <int E>
+__device__ __forceinline__ void split_bf16(const float (&x)[E], unsigned (&hi)[E / 2],
+                                           unsigned (&lo)[E / 2])
 {
 #pragma unroll
-    for (int i = 0; i < kChunk; i += 2) {
-        const bf16x2 h = __builtin_convertvector((float2v){x[i], x[i + 1]}, bf16x2);
-        const unsigned u = __builtin_bit_cast(unsigned, h);
-        const float h0 = __builtin_bit_cast(float, u << 16);
-        const float h1 = __builtin_bit_cast(float, u & 0xffff0000u);
-        const bf16x2 l = __builtin_convertvector((float2v){x[i] - h0, x[i + 1] - h1}, bf16x2);
-        hi[i] = h[0];
-        hi[i + 1] = h[1];
-        lo[i] = l[0];
-        lo[i + 1] = l[1];
+    for (int i = 0; i < E / 2; ++i) {
+        const unsigned h = __builtin_bit_cast(
+            unsigned, __builtin_convertvector((float2v){x[2 * i], x[2 * i + 1]}, bf16x2));
+        const float h0 = __builtin_bit_cast(float, h << 16);
+        const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+        hi[i] = h;
+        lo[i] = __builtin_bit_cast(
+            unsigned, __builtin_convertvector((float2v){x[2 * i] - h0, x[2 * i + 1] - h1}, bf16x2));
     }
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const unsigned (&w)[4])
+{
+    return __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
 }
 
 // The same product with bf16 matrix-core instructions in three passes:
 // a b = a_hi b_hi + a_hi b_lo + a_lo b_hi (a_lo b_lo, below 2^-17 |a b|,
 // dropped), accumulated in fp32 by v_mfma_f32_32x32x16_bf16. One such
-// instruction takes 16 samples; lane l supplies A[l % 32][8 (l / 32) + i]
-// and B[8 (l / 32) + i][l % 32], i < 8 (layout measured), so the two
-// half-waves take one chunk of 8 samples each, and the accumulator layout
-// is the fp32 instruction's. Same workgroup tiling as fhd_grid_kernel.
-__global__ __launch_bounds__(kBlock) void fhd_grid_bf16x3_kernel(
+// instruction takes 16 samples (two chunks); lane l supplies
+// A[l % 32][8 (l / 32) + i] and B[8 (l / 32) + i][l % 32], i < 8 (layout
+// measured), so half-wave h takes chunk h of the pair, and the accumulator
+// layout is the fp32 instruction's. A wave covers 32 (y, z) rows and TILES
+// 32-column tiles; the four waves of a workgroup are stacked along (y, z)
+// and share their 32 TILES columns, so B is made once per workgroup: each
+// lane computes 2 TILES of the 16 x 32 TILES elements, splits them and
+// writes them to LDS in operand order (double buffered, one barrier per 16
+// samples); each wave then reads its operands with ds_read_b128.
+template <int TILES>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TILES == 4 ? 2 : 3))) void fhd_grid_bf16x3_kernel(
     const float *__restrict__ packed, int nchunks, int splits, int nx, int ny, int64_t nyz,
     int tiles_x, GridAxis g, float *__restrict__ out_r, float *__restrict__ out_i)
 {
+    constexpr int kCols = 32 * TILES;          // columns per workgroup
+    constexpr int kPer = 16 * kCols / kBlock;  // B elements per lane and 16 samples
+    static_assert(kPer == 4 || kPer == 8, "a lane's B elements lie in one chunk");
     __shared__ float4 stage[2][kStageVec4];
+    // [buffer][part: b_r hi, b_r lo, b_i hi, b_i lo][tile][column][k half],
+    // 8 bf16 each: one lane's operand
+    __shared__ u32x4 bshare[2][4][TILES][32][2];
     const float4 *src = reinterpret_cast<const float4 *>(packed);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -193,24 +212,61 @@ __global__ __launch_bounds__(kBlock) void fhd_grid_bf16x3_kernel(
     const int64_t yz = yz0 + col;
     const float ry = grid_coord(g.y0, g.dy, yz % ny);
     const float rz = grid_coord(g.z0, g.dz, yz / ny);
-    float cx[kTilesX];
-#pragma unroll
-    for (int t = 0; t < kTilesX; ++t) cx[t] = grid_coord(g.x0, g.dx, bx * (32 * kTilesX) + 32 * t + col);
 
-    float16v acc_r[kTilesX], acc_i[kTilesX];
+    // B producer role: column pc of the workgroup's kCols, samples
+    // kPer pg .. kPer pg + kPer - 1 of each group of 16
+    const int pc = threadIdx.x % kCols, pg = threadIdx.x / kCols;
+    const float pxc = grid_coord(g.x0, g.dx, (int64_t)bx * kCols + pc);
+    const int p_tile = pc / 32, p_col = pc % 32, p_half = (kPer * pg) / kChunk;
+    const int p_vec = ((kPer * pg) % kChunk) / 4;   // first float4 of f0 in the chunk
+
+    float16v acc_r[TILES], acc_i[TILES];
 #pragma unroll
-    for (int t = 0; t < kTilesX; ++t)
+    for (int t = 0; t < TILES; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             acc_r[t][r] = 0.0f;
             acc_i[t][r] = 0.0f;
         }
 
-    int c0, c1;
+    int c0, c1, kb = 0;
     split_range(nchunks, splits, blockIdx.y, &c0, &c1);
     stream_chunk_groups<2>(src, c0, c1, stage, [&](const float4 *ch, int count) {
-        // half-wave h takes chunk h of the pair; a missing second chunk (odd
-        // stream end) is eight zero-amplitude samples
+        __builtin_amdgcn_s_setprio(1);
+        // B elements e^{i 2 pi kx x} of this lane's kPer samples and column;
+        // a missing second chunk (odd stream end) gives kx = 0 (its samples
+        // have zero amplitude in A)
+        {
+            float kxs[kPer];
+#pragma unroll
+            for (int v = 0; v < kPer / 4; ++v) {
+                float4 k4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (p_half < count) k4 = ch[p_half * kChunkVec4 + p_vec + v];
+                kxs[4 * v + 0] = k4.x;
+                kxs[4 * v + 1] = k4.y;
+                kxs[4 * v + 2] = k4.z;
+                kxs[4 * v + 3] = k4.w;
+            }
+            float br[kPer], bi[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const float p = kxs[i] * pxc;
+                br[i] = __builtin_amdgcn_cosf(p);
+                bi[i] = __builtin_amdgcn_sinf(p);
+            }
+            unsigned w[4][kPer / 2];
+            split_bf16<kPer>(br, w[0], w[1]);
+            split_bf16<kPer>(bi, w[2], w[3]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                unsigned *dst = reinterpret_cast<unsigned *>(&bshare[kb][q][p_tile][p_col][p_half]) +
+                                ((kPer * pg) % kChunk) / 2;
+#pragma unroll
+                for (int i = 0; i < kPer / 2; ++i) dst[i] = w[q][i];
+            }
+        }
+        // A elements of this lane's row, chunk `half` of the pair:
+        // a e^{i 2 pi (ky y + kz z + psi)}
         float f[kFields][kChunk];
         if (half < count) {
             load_chunk(ch + half * kChunkVec4, f);
@@ -220,8 +276,6 @@ __global__ __launch_bounds__(kBlock) void fhd_grid_bf16x3_kernel(
 #pragma unroll
                 for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
         }
-        __builtin_amdgcn_s_setprio(1);
-        // A elements of this lane's row: a e^{i 2 pi (ky y + kz z + psi)}
         float ar[kChunk], ai[kChunk];
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
@@ -229,25 +283,23 @@ __global__ __launch_bounds__(kBlock) void fhd_grid_bf16x3_kernel(
             ar[u] = f[4][u] * __builtin_amdgcn_cosf(q);
             ai[u] = f[4][u] * __builtin_amdgcn_sinf(q);
         }
-        bf16x8 arh, arl, aih, ail;
-        split_bf16(ar, arh, arl);
-        split_bf16(ai, aih, ail);
-        const bf16x8 naih = -aih, nail = -ail;
+        unsigned wa[4][4];
+        split_bf16<kChunk>(ar, wa[0], wa[1]);
+        split_bf16<kChunk>(ai, wa[2], wa[3]);
+        const bf16x8 arh = as_bf16x8(wa[0]), arl = as_bf16x8(wa[1]);
+        const bf16x8 aih = as_bf16x8(wa[2]), ail = as_bf16x8(wa[3]);
+        const u32x4 sign = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        const bf16x8 naih = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, aih) ^ sign);
+        const bf16x8 nail = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, ail) ^ sign);
+        __syncthreads();   // this group's B is in LDS
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-        for (int t = 0; t < kTilesX; ++t) {
-            // B elements of this lane's column: e^{i 2 pi kx x}
-            float br[kChunk], bi[kChunk];
-#pragma unroll
-            for (int u = 0; u < kChunk; ++u) {
-                const float p = f[0][u] * cx[t];
-                br[u] = __builtin_amdgcn_cosf(p);
-                bi[u] = __builtin_amdgcn_sinf(p);
-            }
-            bf16x8 brh, brl, bih, bil;
-            split_bf16(br, brh, brl);
-            split_bf16(bi, bih, bil);
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(0);
+        for (int t = 0; t < TILES; ++t) {
+            const bf16x8 brh = __builtin_bit_cast(bf16x8, bshare[kb][0][t][col][half]);
+            const bf16x8 brl = __builtin_bit_cast(bf16x8, bshare[kb][1][t][col][half]);
+            const bf16x8 bih = __builtin_bit_cast(bf16x8, bshare[kb][2][t][col][half]);
+            const bf16x8 bil = __builtin_bit_cast(bf16x8, bshare[kb][3][t][col][half]);
             // real part: a_r b_r - a_i b_i; imaginary part: a_r b_i + a_i b_r
             acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, brh, acc_r[t], 0, 0, 0);
             acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bih, acc_i[t], 0, 0, 0);
@@ -261,17 +313,17 @@ __global__ __launch_bounds__(kBlock) void fhd_grid_bf16x3_kernel(
             acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, brl, acc_i[t], 0, 0, 0);
             acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(nail, bih, acc_r[t], 0, 0, 0);
             acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ail, brh, acc_i[t], 0, 0, 0);
-            __builtin_amdgcn_s_setprio(1);
-            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        kb ^= 1;
     });
+    __builtin_amdgcn_s_setprio(0);
 
     const int64_t N = nyz * nx;
     float *dst_r = out_r + (int64_t)blockIdx.y * N, *dst_i = out_i + (int64_t)blockIdx.y * N;
 #pragma unroll
-    for (int t = 0; t < kTilesX; ++t) {
-        const int ix = bx * (32 * kTilesX) + 32 * t + col;
+    for (int t = 0; t < TILES; ++t) {
+        const int64_t ix = (int64_t)bx * kCols + 32 * t + col;
         if (ix >= nx) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -285,9 +337,9 @@ __global__ __launch_bounds__(kBlock) void fhd_grid_bf16x3_kernel(
 }
 
 // Workgroups of a grid kernel that fit on one CU at once (its register
-// budget), asked of the runtime once per device and kernel.
-template <int PRECISION>
-int grid_blocks_per_cu()
+// and LDS budget), asked of the runtime once per device and kernel.
+template <int KERNEL>
+int grid_blocks_per_cu(const void *kernel)
 {
     static int cached[64] = {0};
     int device = 0;
@@ -297,8 +349,6 @@ int grid_blocks_per_cu()
     }
     if (cached[device] == 0) {
         int n = 0;
-        const void *kernel = PRECISION == FHD_GRID_BF16X3 ? (const void *)fhd_grid_bf16x3_kernel
-                                                          : (const void *)fhd_grid_kernel;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n <= 0) {
             (void)hipGetLastError();
             n = 2;
@@ -315,23 +365,39 @@ int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const
 {
     const int64_t nyz = (int64_t)ny * nz, N = nyz * nx;
     if (N == 0) return FHD_OK;
-    const bool bf16x3 = precision == FHD_GRID_BF16X3;
+    // fp32: 2 tiles per wave; bf16x3: 4 tiles (2 when the grid is at most 64
+    // columns wide, where 4 would leave half of them idle)
+    const int kernel_id = precision == FHD_GRID_BF16X3 ? (nx > 64 ? 2 : 1) : 0;
+    const int tiles = kernel_id == 2 ? 4 : 2;
     const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
-    const int tiles_x = (nx + 32 * kTilesX - 1) / (32 * kTilesX);
+    const int tiles_x = (int)((nx + 32 * tiles - 1) / (32 * tiles));
     const int64_t slabs = (nyz + kTileYZ * kWaves - 1) / (kTileYZ * kWaves);
     const int64_t blocks = slabs * tiles_x;
     const GridAxis g{axis[0], axis[1], axis[2], axis[3], axis[4], axis[5]};
-    const int per_cu = bf16x3 ? grid_blocks_per_cu<FHD_GRID_BF16X3>() : grid_blocks_per_cu<FHD_GRID_FP32>();
+    int per_cu = 2;
+    const char *name = "fhd_grid_kernel launch";
+    if (kernel_id == 0) {
+        per_cu = grid_blocks_per_cu<0>((const void *)fhd_grid_kernel);
+    } else if (kernel_id == 1) {
+        per_cu = grid_blocks_per_cu<1>((const void *)fhd_grid_bf16x3_kernel<2>);
+        name = "fhd_grid_bf16x3_kernel<2> launch";
+    } else {
+        per_cu = grid_blocks_per_cu<2>((const void *)fhd_grid_bf16x3_kernel<4>);
+        name = "fhd_grid_bf16x3_kernel<4> launch";
+    }
     const int splits = split_count(blocks, nchunks, per_cu);
     auto launch = [&](int nsplit, float *out_r, float *out_i) {
         const dim3 grid((unsigned)blocks, (unsigned)nsplit);
-        if (bf16x3)
-            fhd_grid_bf16x3_kernel<<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, nsplit, nx, ny, nyz,
-                                                                     tiles_x, g, out_r, out_i);
-        else
+        if (kernel_id == 0)
             fhd_grid_kernel<<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, nsplit, nx, ny, nyz,
                                                               tiles_x, g, out_r, out_i);
-        return launch_status(bf16x3 ? "fhd_grid_bf16x3_kernel launch" : "fhd_grid_kernel launch");
+        else if (kernel_id == 1)
+            fhd_grid_bf16x3_kernel<2><<<grid, dim3(kBlock), 0, stream>>>(
+                packed, nchunks, nsplit, nx, ny, nyz, tiles_x, g, out_r, out_i);
+        else
+            fhd_grid_bf16x3_kernel<4><<<grid, dim3(kBlock), 0, stream>>>(
+                packed, nchunks, nsplit, nx, ny, nyz, tiles_x, g, out_r, out_i);
+        return launch_status(name);
     };
     if (splits == 1) return launch(1, rho_r, rho_i);
     float *part = nullptr;
