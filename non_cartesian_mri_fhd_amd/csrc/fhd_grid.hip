@@ -200,9 +200,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TILES ==
     constexpr int kPer = 16 * kCols / kBlock;  // B elements per lane and 16 samples
     static_assert(kPer == 4 || kPer == 8, "a lane's B elements lie in one chunk");
     __shared__ float4 stage[2][kStageVec4];
-    // [buffer][part: b_r hi, b_r lo, b_i hi, b_i lo][tile][column][k half],
-    // 8 bf16 each: one lane's operand
-    __shared__ u32x4 bshare[2][4][TILES][32][2];
+    // [buffer][part: b_r hi, b_r lo, b_i hi, b_i lo][tile][k half][column],
+    // 8 bf16 each: one lane's operand; a half-wave reads 32 consecutive
+    // entries (no bank conflicts)
+    __shared__ u32x4 bshare[2][4][TILES][2][32];
     const float4 *src = reinterpret_cast<const float4 *>(packed);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TILES ==
             split_bf16<kPer>(bi, w[2], w[3]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                unsigned *dst = reinterpret_cast<unsigned *>(&bshare[kb][q][p_tile][p_col][p_half]) +
+                unsigned *dst = reinterpret_cast<unsigned *>(&bshare[kb][q][p_tile][p_half][p_col]) +
                                 ((kPer * pg) % kChunk) / 2;
 #pragma unroll
                 for (int i = 0; i < kPer / 2; ++i) dst[i] = w[q][i];
@@ -296,10 +297,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TILES ==
         __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
-            const bf16x8 brh = __builtin_bit_cast(bf16x8, bshare[kb][0][t][col][half]);
-            const bf16x8 brl = __builtin_bit_cast(bf16x8, bshare[kb][1][t][col][half]);
-            const bf16x8 bih = __builtin_bit_cast(bf16x8, bshare[kb][2][t][col][half]);
-            const bf16x8 bil = __builtin_bit_cast(bf16x8, bshare[kb][3][t][col][half]);
+            const bf16x8 brh = __builtin_bit_cast(bf16x8, bshare[kb][0][t][half][col]);
+            const bf16x8 brl = __builtin_bit_cast(bf16x8, bshare[kb][1][t][half][col]);
+            const bf16x8 bih = __builtin_bit_cast(bf16x8, bshare[kb][2][t][half][col]);
+            const bf16x8 bil = __builtin_bit_cast(bf16x8, bshare[kb][3][t][half][col]);
             // real part: a_r b_r - a_i b_i; imaginary part: a_r b_i + a_i b_r
             acc_r[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, brh, acc_r[t], 0, 0, 0);
             acc_i[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bih, acc_i[t], 0, 0, 0);
