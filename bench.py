@@ -11,7 +11,7 @@ event timing on the launch stream), the sampled parity against the fp64
 oracle and the oracle's own CPU throughput on that sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--op fhd|forward|normal|cg|grid|grid_bf16x3]
+                    [--op fhd|forward|normal|cg|grid|grid_bf16x3|forward_grid]
 
 --op selects the operator timed (default fhd, the headline F^H D):
 forward = D = F rho; normal = F^H F rho (2 N M terms per step); cg = a
@@ -22,7 +22,9 @@ complex matrix product on the fp32 matrix cores (fhd_pack +
 fhd_grid_gather; N M terms per step, priced against the fp32 MFMA peak);
 grid_bf16x3 = the same product with each fp32 operand split into two bf16
 parts and three bf16 products per real product (priced as 24 FLOP per
-term against the 2.5 PFLOP/s dense bf16 peak).
+term against the 2.5 PFLOP/s dense bf16 peak); forward_grid = D = F rho
+with rho on the workload's grid, split-bf16 matrix products (same
+pricing).
 """
 from __future__ import annotations
 
@@ -153,7 +155,8 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="spiral128")
-    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid", "grid_bf16x3"])
+    ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid", "grid_bf16x3",
+                                                       "forward_grid"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -378,6 +381,19 @@ def bench_other(args) -> int:
         dominant = ("fhd_grid_bf16x3_kernel" if args.op == "grid_bf16x3" else "fhd_grid_kernel") + \
             " + reduce_splits_kernel"
         terms_per_step = float(N) * M
+    elif args.op == "forward_grid":
+        L = inputs.WORKLOADS[args.workload].L
+        axis = inputs.grid_axis_of(L)
+        Dr = torch.empty(M, device=dev)
+        Di = torch.empty(M, device=dev)
+
+        def pre():
+            pass
+
+        def main_kernel():
+            binding.fhd_forward_grid(t["kx"], t["ky"], t["kz"], (L, L, L), axis, img[0], img[1], Dr, Di)
+        dominant = "fhd_forward_grid_bf16x3_kernel + reduce_splits_kernel"
+        terms_per_step = float(N) * M
     elif args.op == "normal":
         qr = torch.empty(N, device=dev)
         qi = torch.empty(N, device=dev)
@@ -447,7 +463,7 @@ def bench_other(args) -> int:
                            "peak": P_MFMA_FP32 / 1e12, "unit": "TFLOP/s",
                            "frac": achieved / P_MFMA_FP32,
                            "traffic": measured_traffic("grid", args.workload)}
-    elif args.op == "grid_bf16x3":
+    elif args.op in ("grid_bf16x3", "forward_grid"):
         # three bf16 products per real product: 3 x 8 FLOP per term on the
         # bf16 matrix cores (2.5 PFLOP/s dense)
         achieved = 3 * MFMA_FLOP_PER_TERM * k_rate
@@ -459,7 +475,7 @@ def bench_other(args) -> int:
         if args.op in ("grid", "grid_bf16x3"):
             base, parity = cpu_baseline(w, args.workload, args.cpu_seconds,
                                         rr.cpu().numpy(), ri.cpu().numpy())
-        elif args.op == "forward":
+        elif args.op in ("forward", "forward_grid"):
             base, parity = oracle_forward_sample(w, args.workload, args.cpu_seconds,
                                                  Dr.cpu().numpy(), Di.cpu().numpy(), img_np)
         else:

@@ -210,6 +210,28 @@ int fhd_grid_gather(const void *packed, int M, int nx, int ny, int nz,
                     void *stream);
 
 /*
+ * D = F rho (page "Case study -- iterative MRI reconstruction", section 17.2:
+ * F maps the image to k-space, D_m = sum_n rho_n exp(-i 2 pi k_m . x_n))
+ * for rho on the Cartesian grid of fhd_compute_grid (same voxel order and
+ * coordinates), as a complex (ny*nz x nx) by (nx x M) matrix product on
+ * the matrix cores followed by the (y, z) phases and a sum over rows.
+ *   kx, ky, kz   : M fp32 values each (read only)
+ *   nx, ny, nz   : grid size, nx*ny*nz < 2^31
+ *   axis         : HOST array {x0, dx, y0, dy, z0, dz}, finite
+ *   precision    : FHD_GRID_BF16X3 (the only mode of this call)
+ *   rho_r, rho_i : nx*ny*nz fp32 values each (read only)
+ *   Dr, Di       : M fp32 values each (written), not overlapping any input
+ * Per-workgroup partial sums live in a stream-ordered workspace and are
+ * added in a fixed order: repeated calls are bitwise identical. M = 0 does
+ * nothing; an empty grid writes zeros.
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
+ */
+int fhd_forward_grid(const float *kx, const float *ky, const float *kz, int M,
+                     int nx, int ny, int nz, const float *axis, int precision,
+                     const float *rho_r, const float *rho_i, float *Dr, float *Di,
+                     void *stream);
+
+/*
  * Conjugate-gradient reconstruction (page "Case study -- iterative MRI
  * reconstruction", section 17.2 and its CG skeleton after section 17.3.6)
  * with the regulariser left out (the pages do not specify R or lambda):

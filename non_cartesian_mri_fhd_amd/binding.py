@@ -80,6 +80,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_compute_grid.restype = i32
     lib.fhd_grid_gather.argtypes = [vp] + [i32] * 4 + [fpp, i32, fp, fp, vp]
     lib.fhd_grid_gather.restype = i32
+    lib.fhd_forward_grid.argtypes = [fp] * 3 + [i32] * 4 + [fpp, i32, fp, fp, fp, fp, vp]
+    lib.fhd_forward_grid.restype = i32
     lib.fhd_gather_config.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
     lib.fhd_gather_config.restype = None
     lib.fhd_status_string.argtypes = [i32]
@@ -330,6 +332,27 @@ def fhd_grid_gather(packed, M: int, shape, axis, rho_r=None, rho_i=None, stream=
                                         int(precision), *outs, _stream(dev, stream)),
                "fhd_grid_gather")
     return rho_r, rho_i
+
+
+def fhd_forward_grid(kx, ky, kz, shape, axis, rho_r, rho_i, Dr=None, Di=None, stream=None,
+                     precision: int = FHD_GRID_BF16X3):
+    """D = F rho for rho on the grid shape = (nx, ny, nz) with axis
+    (x0, dx, y0, dy, z0, dz), voxel n = ix + nx*(iy + ny*iz). Returns (Dr, Di)."""
+    lib = load()
+    nx, ny, nz = (int(v) for v in shape)
+    M, N = kx.numel(), nx * ny * nz
+    dev = kx.device
+    if Dr is None:
+        Dr = torch.empty(M, dtype=torch.float32, device=dev)
+    if Di is None:
+        Di = torch.empty(M, dtype=torch.float32, device=dev)
+    ks = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"))]
+    img = [_vec(t, nm, N, dev) for t, nm in ((rho_r, "rho_r"), (rho_i, "rho_i"))]
+    outs = [_vec(t, nm, M, dev) for t, nm in ((Dr, "Dr"), (Di, "Di"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_forward_grid(*ks, M, nx, ny, nz, _axis(axis), int(precision), *img, *outs,
+                                         _stream(dev, stream)), "fhd_forward_grid")
+    return Dr, Di
 
 
 def new_packed(M: int, device) -> torch.Tensor:

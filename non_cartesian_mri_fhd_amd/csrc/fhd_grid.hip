@@ -29,6 +29,7 @@
 // therefore belong to the same sample, m0 + l / 32.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -359,6 +360,168 @@ int grid_blocks_per_cu(const void *kernel)
     return cached[device];
 }
 
+// ---------------------------------------------------------------------------
+// Forward F on a grid: D_m = sum_n rho_n e^{-i 2 pi k_m.x_n}, the other side
+// of the page's F^H D (section 17.2 defines F as the image-to-k-space map).
+// On the grid the exponential factors as before, but now the separable
+// side is the sum:
+//
+//     C[(iy, iz), m] = sum_ix rho[(iy, iz), ix] e^{-i 2 pi kx_m x_ix}
+//     D_m = sum_(iy, iz) e^{-i 2 pi (ky_m y + kz_m z)} C[(iy, iz), m]
+//
+// a complex (nyz x nx) by (nx x M) product followed by a phase and a sum
+// over its rows. Workgroup = 128 rows (4 waves of 32) x 64 of the nx
+// columns (4 groups of 16, the bf16 instruction's k); a wave keeps its
+// split rho operands in registers for the whole launch and walks the
+// samples 32 at a time. The e^{-i 2 pi kx x} operand (cos, and sin with
+// the sign folded into the accumulators) is made once per workgroup, 8
+// elements per lane, and shared through LDS. Per 32 samples a wave then
+// runs 48 MFMAs into three accumulators (Re: rho_r cos + rho_i sin; rho_r
+// sin; rho_i cos), applies the row phases, sums its 16 rows per lane, the
+// two half-waves and the four waves, and writes one partial D per sample.
+// The partials of all workgroups (rows x column groups) are added in a
+// fixed order afterwards.
+constexpr int kFwdK = 64;                 // x columns per workgroup
+constexpr int kFwdSteps = kFwdK / 16;     // bf16 MFMA k-groups per workgroup
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void fhd_forward_grid_bf16x3_kernel(
+    const float *__restrict__ rho_r, const float *__restrict__ rho_i, int nx, int ny, int64_t nyz,
+    const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz, int M,
+    int m_per_split, int kranges, GridAxis g, float *__restrict__ part_r, float *__restrict__ part_i)
+{
+    // [part: cos hi, cos lo, sin hi, sin lo][k-group][k half][sample]
+    __shared__ u32x4 bE[4][kFwdSteps][2][32];
+    __shared__ float red[kWaves][32][2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int64_t slab = blockIdx.x / kranges;
+    const int kr = blockIdx.x % kranges;
+    const int64_t row0 = slab * (kTileYZ * kWaves) + (int64_t)wave * kTileYZ;
+
+    // A operands: rho of row row0 + col, columns kr*64 + 16 s + 8 half + i,
+    // zero past the grid's edge
+    bf16x8 arh[kFwdSteps], arl[kFwdSteps], aih[kFwdSteps], ail[kFwdSteps];
+    {
+        const int64_t yz = row0 + col;
+#pragma unroll
+        for (int s = 0; s < kFwdSteps; ++s) {
+            float vr[kChunk], vi[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const int ix = kr * kFwdK + 16 * s + 8 * half + i;
+                const bool ok = yz < nyz && ix < nx;
+                vr[i] = ok ? rho_r[yz * nx + ix] : 0.0f;
+                vi[i] = ok ? rho_i[yz * nx + ix] : 0.0f;
+            }
+            unsigned w[4][4];
+            split_bf16<kChunk>(vr, w[0], w[1]);
+            split_bf16<kChunk>(vi, w[2], w[3]);
+            arh[s] = as_bf16x8(w[0]);
+            arl[s] = as_bf16x8(w[1]);
+            aih[s] = as_bf16x8(w[2]);
+            ail[s] = as_bf16x8(w[3]);
+        }
+    }
+    // producer role: sample pm of each group of 32, columns kr*64 + 8 pg + i
+    const int pm = threadIdx.x & 31, pg = threadIdx.x >> 5;
+    const int p_s = pg / 2, p_h = pg % 2;
+    float pxv[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) pxv[i] = grid_coord(g.x0, g.dx, (int64_t)kr * kFwdK + 8 * pg + i);
+    // epilogue rows of this lane (accumulator layout): their y and z
+    float ey[16], ez[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t yz = row0 + 8 * (r / 4) + 4 * half + (r % 4);
+        ey[r] = grid_coord(g.y0, g.dy, yz % ny);
+        ez[r] = grid_coord(g.z0, g.dz, yz / ny);
+    }
+
+    const int m_begin = blockIdx.y * m_per_split;
+    const int m_end = min(M, m_begin + m_per_split);
+    for (int mb = m_begin; mb < m_end; mb += 32) {
+        __builtin_amdgcn_s_setprio(1);
+        {
+            // e^{-i 2 pi kx x} = cos - i sin for this lane's sample and 8
+            // columns (samples past M: kx = 0, never stored)
+            const int m = mb + pm;
+            const float pk = m < M ? kx[m] : 0.0f;
+            float c[kChunk], sn[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const float p = pk * pxv[i];
+                c[i] = __builtin_amdgcn_cosf(p);
+                sn[i] = __builtin_amdgcn_sinf(p);
+            }
+            unsigned w[4][4];
+            split_bf16<kChunk>(c, w[0], w[1]);
+            split_bf16<kChunk>(sn, w[2], w[3]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bE[q][p_s][p_h][pm] = (u32x4){w[q][0], w[q][1], w[q][2], w[q][3]};
+        }
+        __syncthreads();   // B of these 32 samples is in LDS
+        __builtin_amdgcn_s_setprio(0);
+        float16v acc_r, acc_p, acc_q;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc_r[r] = 0.0f;
+            acc_p[r] = 0.0f;
+            acc_q[r] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < kFwdSteps; ++s) {
+            const bf16x8 ch = __builtin_bit_cast(bf16x8, bE[0][s][half][col]);
+            const bf16x8 cl = __builtin_bit_cast(bf16x8, bE[1][s][half][col]);
+            const bf16x8 sh = __builtin_bit_cast(bf16x8, bE[2][s][half][col]);
+            const bf16x8 sl = __builtin_bit_cast(bf16x8, bE[3][s][half][col]);
+            // Re C = rho_r cos + rho_i sin; Im C = rho_i cos - rho_r sin
+            acc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh[s], ch, acc_r, 0, 0, 0);
+            acc_p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh[s], sh, acc_p, 0, 0, 0);
+            acc_q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih[s], ch, acc_q, 0, 0, 0);
+            acc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh[s], cl, acc_r, 0, 0, 0);
+            acc_p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh[s], sl, acc_p, 0, 0, 0);
+            acc_q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih[s], cl, acc_q, 0, 0, 0);
+            acc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arl[s], ch, acc_r, 0, 0, 0);
+            acc_p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arl[s], sh, acc_p, 0, 0, 0);
+            acc_q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ail[s], ch, acc_q, 0, 0, 0);
+            acc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih[s], sh, acc_r, 0, 0, 0);
+            acc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih[s], sl, acc_r, 0, 0, 0);
+            acc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ail[s], sh, acc_r, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(1);
+        // D_m += e^{-i 2 pi (ky y + kz z)} C over this lane's 16 rows
+        const int m = mb + col;
+        const float eky = m < M ? ky[m] : 0.0f, ekz = m < M ? kz[m] : 0.0f;
+        float dr = 0.0f, di = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float ph = __builtin_fmaf(eky, ey[r], ekz * ez[r]);
+            const float cp = __builtin_amdgcn_cosf(ph), sp = __builtin_amdgcn_sinf(ph);
+            const float cr = acc_r[r], ci = acc_q[r] - acc_p[r];
+            dr = __builtin_fmaf(cp, cr, __builtin_fmaf(sp, ci, dr));
+            di = __builtin_fmaf(cp, ci, __builtin_fmaf(-sp, cr, di));
+        }
+        dr += __shfl_xor(dr, 32);
+        di += __shfl_xor(di, 32);
+        if (half == 0) {
+            red[wave][col][0] = dr;
+            red[wave][col][1] = di;
+        }
+        __syncthreads();   // all waves' sums are in LDS; B may be rewritten
+        if (threadIdx.x < 32 && mb + (int)threadIdx.x < m_end) {
+            float sr = 0.0f, si = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) {
+                sr += red[v][threadIdx.x][0];
+                si += red[v][threadIdx.x][1];
+            }
+            part_r[(int64_t)blockIdx.x * M + mb + threadIdx.x] = sr;
+            part_i[(int64_t)blockIdx.x * M + mb + threadIdx.x] = si;
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
 }  // namespace
 
 int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const float *axis,
@@ -411,6 +574,48 @@ int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const
     float *part_r = part, *part_i = part + (int64_t)splits * N;
     int rc = launch(splits, part_r, part_i);
     if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, N, rho_r, rho_i, stream);
+    const hipError_t f = hipFreeAsync(part, stream);
+    if (f != hipSuccess && rc == FHD_OK)
+        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
+    return rc;
+}
+
+int launch_forward_grid(const float *rho_r, const float *rho_i, int nx, int ny, int nz,
+                        const float *axis, int precision, const float *kx, const float *ky,
+                        const float *kz, int M, float *Dr, float *Di, hipStream_t stream)
+{
+    if (M == 0) return FHD_OK;
+    if (precision != FHD_GRID_BF16X3) return fail(FHD_ERR_INVALID_ARG, "precision");
+    const int64_t nyz = (int64_t)ny * nz;
+    const int kranges = (nx + kFwdK - 1) / kFwdK;
+    const int64_t slabs = (nyz + kTileYZ * kWaves - 1) / (kTileYZ * kWaves);
+    const int64_t blocks = slabs * kranges;
+    const GridAxis g{axis[0], axis[1], axis[2], axis[3], axis[4], axis[5]};
+    // cut the samples into parts of whole 32s so that the launch fills the
+    // chip (2 workgroups per CU at this kernel's register budget)
+    const int per_cu = grid_blocks_per_cu<3>((const void *)fhd_forward_grid_bf16x3_kernel);
+    int device = 0, cus = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    const int64_t groups = ((int64_t)M + 31) / 32;
+    int64_t msplits = ((int64_t)per_cu * cus + blocks - 1) / blocks;
+    msplits = std::max<int64_t>(1, std::min<int64_t>(msplits, groups));
+    const int m_per_split = (int)(((groups + msplits - 1) / msplits) * 32);
+    msplits = ((int64_t)M + m_per_split - 1) / m_per_split;
+    float *part = nullptr;
+    const hipError_t e = hipMallocAsync((void **)&part, (size_t)blocks * 2 * M * sizeof(float), stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (row partials): ") + hipGetErrorString(e));
+    }
+    float *part_r = part, *part_i = part + blocks * M;
+    fhd_forward_grid_bf16x3_kernel<<<dim3((unsigned)blocks, (unsigned)msplits), dim3(kBlock), 0, stream>>>(
+        rho_r, rho_i, nx, ny, nyz, kx, ky, kz, M, m_per_split, kranges, g, part_r, part_i);
+    int rc = launch_status("fhd_forward_grid_bf16x3_kernel launch");
+    if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, (int)blocks, M, Dr, Di, stream);
     const hipError_t f = hipFreeAsync(part, stream);
     if (f != hipSuccess && rc == FHD_OK)
         rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
@@ -488,4 +693,27 @@ extern "C" int fhd_compute_grid(const float *kx, const float *ky, const float *k
             rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
     }
     return rc;
+}
+
+extern "C" int fhd_forward_grid(const float *kx, const float *ky, const float *kz, int M, int nx, int ny,
+                                int nz, const float *axis, int precision, const float *rho_r,
+                                const float *rho_i, float *Dr, float *Di, void *stream)
+{
+    clear_error();
+    int64_t N = 0;
+    int rc = check_grid_args(M, nx, ny, nz, axis, precision, &N);
+    if (rc != FHD_OK || M == 0) return rc;
+    if (precision != FHD_GRID_BF16X3)
+        return fail(FHD_ERR_INVALID_ARG, "fhd_forward_grid supports FHD_GRID_BF16X3 only");
+    const int64_t mb = (int64_t)M * 4, nb = N * 4;
+    const Span all[] = {{kx, mb, "kx"},       {ky, mb, "ky"},       {kz, mb, "kz"},
+                        {rho_r, nb, "rho_r"}, {rho_i, nb, "rho_i"}, {Dr, mb, "Dr"},
+                        {Di, mb, "Di"}};
+    rc = check_host_side(all, 7);
+    if (rc == FHD_OK) rc = check_no_overlap(all, 7, 5);
+    if (rc == FHD_OK) rc = check_device_spans(all, 7);
+    if (rc != FHD_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (N == 0) return launch_reduce(nullptr, nullptr, 0, M, Dr, Di, s);   // empty image: D = 0
+    return launch_forward_grid(rho_r, rho_i, nx, ny, nz, axis, precision, kx, ky, kz, M, Dr, Di, s);
 }

@@ -196,5 +196,10 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
 // fhd_grid.hip: F^H D on a Cartesian grid (axis = x0, dx, y0, dy, z0, dz)
 int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const float *axis,
                        int precision, float *rho_r, float *rho_i, hipStream_t stream);
+// D = F rho for rho on an nx x ny x nz grid (at least one voxel), split-bf16
+// products only (precision FHD_GRID_BF16X3).
+int launch_forward_grid(const float *rho_r, const float *rho_i, int nx, int ny, int nz,
+                        const float *axis, int precision, const float *kx, const float *ky,
+                        const float *kz, int M, float *Dr, float *Di, hipStream_t stream);
 
 }  // namespace fhd

@@ -35,6 +35,7 @@ def lib():
     lib.fhd_normal.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
     lib.fhd_compute_grid.argtypes = [vp] * 5 + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 3
     lib.fhd_grid_gather.argtypes = [vp] + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 3
+    lib.fhd_forward_grid.argtypes = [vp] * 3 + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 5
     lib.fhd_last_error.restype = ctypes.c_char_p
     lib.fhd_status_string.restype = ctypes.c_char_p
     return lib
@@ -51,7 +52,7 @@ def test_header_declares_the_entry_points():
     for n in ("fhd_compute", "fhd_pack", "fhd_gather", "fhd_packed_bytes",
               "fhd_status_string", "fhd_last_error", "fhd_gather_config",
               "fhd_forward", "fhd_forward_pack", "fhd_forward_gather", "fhd_normal",
-              "fhd_cg", "fhd_cg_workspace_bytes", "fhd_compute_grid", "fhd_grid_gather"):
+              "fhd_cg", "fhd_cg_workspace_bytes", "fhd_compute_grid", "fhd_grid_gather", "fhd_forward_grid"):
         assert n in names
 
 
@@ -217,3 +218,24 @@ def test_grid_argument_checks(lib):
         assert lib.fhd_grid_gather(fake[0], 8, 4, 4, 4, ax, bad_precision, fake[5], fake[6],
                                    None) == FHD_ERR_INVALID_ARG
         assert "precision" in _last(lib)
+
+
+def test_forward_grid_argument_checks(lib):
+    axis = (ctypes.c_float * 6)(-0.5, 1 / 16, -0.5, 1 / 16, -0.5, 1 / 16)
+    ax = ctypes.addressof(axis)
+    fake = [0x100000 * (i + 1) for i in range(7)]
+    k, img, out = fake[:3], fake[3:5], fake[5:]
+    assert lib.fhd_forward_grid(*k, -1, 4, 4, 4, ax, 1, *img, *out, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_forward_grid(*k, 8, 4, -1, 4, ax, 1, *img, *out, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_forward_grid(*k, 8, 4, 4, 4, None, 1, *img, *out, None) == FHD_ERR_INVALID_ARG
+    # only the split-bf16 mode exists for F on a grid
+    assert lib.fhd_forward_grid(*k, 8, 4, 4, 4, ax, 0, *img, *out, None) == FHD_ERR_INVALID_ARG
+    assert "BF16X3" in _last(lib)
+    assert lib.fhd_forward_grid(*k, 8, 4, 4, 4, ax, 5, *img, *out, None) == FHD_ERR_INVALID_ARG
+    # no samples: nothing to do
+    assert lib.fhd_forward_grid(None, None, None, 0, 4, 4, 4, ax, 1, None, None, None, None,
+                                None) == FHD_OK
+    bad = list(out)
+    bad[1] = img[0]                                                    # Di aliases rho_r
+    assert lib.fhd_forward_grid(*k, 8, 4, 4, 4, ax, 1, *img, *bad, None) == FHD_ERR_INVALID_ARG
+    assert "overlaps" in _last(lib)

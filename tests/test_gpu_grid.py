@@ -172,3 +172,92 @@ def test_grid_bf16x3_close_to_fp32(dev):
     check("grid wide range fp32", *a, *ref)
     check("grid wide range bf16x3", *b, *ref)
     assert metrics.rel_l2(*b, a[0].astype(np.float64), a[1].astype(np.float64)) < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# forward F on a grid (fhd_forward_grid, split-bf16 products)
+# ---------------------------------------------------------------------------
+def gpu_forward_grid(case, img, shape, axis, dev):
+    k = [t(case[a], dev) for a in ("kx", "ky", "kz")]
+    Dr, Di = binding.fhd_forward_grid(*k, shape, axis, t(img[0], dev), t(img[1], dev))
+    torch.cuda.synchronize(dev)
+    return Dr.cpu().numpy(), Di.cpu().numpy()
+
+
+def oracle_forward_on_grid(case, img, shape, axis, idx=None):
+    x, y, z = inputs.coords_from_axis(*shape, axis)
+    kx, ky, kz = case["kx"], case["ky"], case["kz"]
+    if idx is not None:
+        kx, ky, kz = kx[idx], ky[idx], kz[idx]
+    return oracle.forward(kx, ky, kz, img[0], img[1], x, y, z)
+
+
+@pytest.mark.parametrize("name,samples", [("random16", None), ("spiral32", None),
+                                          ("radial64", 1024), ("spiral128", 384)])
+def test_forward_grid_workloads(dev, name, samples):
+    w = inputs.make_workload(name)
+    L = inputs.WORKLOADS[name].L
+    img = inputs.random_image(w["N"], seed=inputs.WORKLOADS[name].seed + 7)
+    Dr, Di = gpu_forward_grid(w, img, (L, L, L), inputs.grid_axis_of(L), dev)
+    idx = (np.arange(w["M"]) if samples is None else
+           inputs.voxel_subset(w["M"], samples, seed=inputs.WORKLOADS[name].seed + 3000))
+    ref = oracle_forward_on_grid(w, img, (L, L, L), inputs.grid_axis_of(L), idx)
+    check("forward grid " + name, Dr[idx], Di[idx], *ref)
+
+
+@pytest.mark.parametrize("shape,M", [((1, 1, 1), 1), ((70, 5, 27), 1000), ((130, 3, 2), 7),
+                                     ((64, 128, 1), 4097), ((33, 17, 9), 513),
+                                     ((7, 129, 2), 2049), ((200, 2, 3), 31)])
+def test_forward_grid_ragged(dev, shape, M):
+    """Grids whose edges cut the 128-row slabs and 64-column groups, sample
+    counts off the 32-sample step, non-dyadic axis steps of either sign."""
+    c = inputs.random_case(1, M, seed=2 * M + shape[0])
+    N = int(np.prod(shape))
+    img = inputs.random_image(N, seed=N + 3)
+    D = gpu_forward_grid(c, img, shape, ODD_AXIS, dev)
+    check("forward grid ragged %s M=%d" % (shape, M), *D,
+          *oracle_forward_on_grid(c, img, shape, ODD_AXIS))
+
+
+def test_forward_grid_adjoint_of_grid_gather(dev):
+    """<F^H D, rho> = <D, F rho> with both grid forms on the GPU."""
+    shape = (48, 20, 9)
+    N = int(np.prod(shape))
+    c = inputs.random_case(1, 3000, seed=61, kmax=20.0)
+    img = inputs.random_image(N, seed=62)
+    rr, ri = gpu_grid(c, shape, ODD_AXIS, dev, precision=binding.FHD_GRID_BF16X3)
+    Fr, Fi = gpu_forward_grid(c, img, shape, ODD_AXIS, dev)
+    rho = img[0].astype(np.float64) + 1j * img[1].astype(np.float64)
+    D = c["Dr"].astype(np.float64) + 1j * c["Di"].astype(np.float64)
+    lhs = np.vdot(rho, rr.astype(np.float64) + 1j * ri)
+    rhs = np.vdot(Fr.astype(np.float64) + 1j * Fi, D)
+    scale = np.linalg.norm(rho) * np.linalg.norm(D) * np.sqrt(3000)
+    assert abs(lhs - rhs) <= 1e-5 * scale, (lhs, rhs)
+
+
+def test_forward_grid_matches_direct_forward(dev):
+    w = inputs.make_workload("spiral32")
+    L = inputs.WORKLOADS["spiral32"].L
+    img = inputs.random_image(w["N"], seed=63)
+    g = gpu_forward_grid(w, img, (L, L, L), inputs.grid_axis_of(L), dev)
+    d = [t(w[a], dev) for a in ("kx", "ky", "kz", "x", "y", "z")]
+    Dr, Di = binding.fhd_forward(*d, t(img[0], dev), t(img[1], dev))
+    torch.cuda.synchronize(dev)
+    check("forward grid vs direct", *g, Dr.cpu().numpy().astype(np.float64),
+          Di.cpu().numpy().astype(np.float64))
+
+
+def test_forward_grid_repeatable_and_empty(dev):
+    c = inputs.random_case(1, 700, seed=64)
+    shape = (40, 9, 3)
+    img = inputs.random_image(int(np.prod(shape)), seed=65)
+    a = gpu_forward_grid(c, img, shape, ODD_AXIS, dev)
+    b = gpu_forward_grid(c, img, shape, ODD_AXIS, dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    e = np.zeros(0, np.float32)
+    k = [t(c[n], dev) for n in ("kx", "ky", "kz")]
+    Dr = torch.full((700,), 5.0, device=dev)
+    Di = torch.full((700,), 5.0, device=dev)
+    binding.fhd_forward_grid(*k, (0, 4, 4), ODD_AXIS, t(e, dev), t(e, dev), Dr, Di)
+    torch.cuda.synchronize(dev)
+    assert torch.count_nonzero(Dr).item() == 0 and torch.count_nonzero(Di).item() == 0
