@@ -11,7 +11,8 @@ event timing on the launch stream), the sampled parity against the fp64
 oracle and the oracle's own CPU throughput on that sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--op fhd|forward|normal|cg|grid|grid_bf16x3|forward_grid]
+                    [--op fhd|forward|normal|cg|grid|grid_bf16x3|forward_grid|
+                           normal_grid|cg_grid]
 
 --op selects the operator timed (default fhd, the headline F^H D):
 forward = D = F rho; normal = F^H F rho (2 N M terms per step); cg = a
@@ -24,7 +25,8 @@ grid_bf16x3 = the same product with each fp32 operand split into two bf16
 parts and three bf16 products per real product (priced as 24 FLOP per
 term against the 2.5 PFLOP/s dense bf16 peak); forward_grid = D = F rho
 with rho on the workload's grid, split-bf16 matrix products (same
-pricing).
+pricing); normal_grid, cg_grid = F^H F and the 3-iteration CG with both
+operators in that grid form.
 """
 from __future__ import annotations
 
@@ -156,7 +158,7 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="spiral128")
     ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid", "grid_bf16x3",
-                                                       "forward_grid"])
+                                                       "forward_grid", "normal_grid", "cg_grid"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -394,6 +396,31 @@ def bench_other(args) -> int:
             binding.fhd_forward_grid(t["kx"], t["ky"], t["kz"], (L, L, L), axis, img[0], img[1], Dr, Di)
         dominant = "fhd_forward_grid_bf16x3_kernel + reduce_splits_kernel"
         terms_per_step = float(N) * M
+    elif args.op == "normal_grid":
+        L = inputs.WORKLOADS[args.workload].L
+        axis = inputs.grid_axis_of(L)
+        qr = torch.empty(N, device=dev)
+        qi = torch.empty(N, device=dev)
+
+        def pre():
+            pass
+
+        def main_kernel():
+            binding.fhd_normal_grid(t["kx"], t["ky"], t["kz"], (L, L, L), axis, img[0], img[1], qr, qi)
+        terms_per_step = 2.0 * N * M
+    elif args.op == "cg_grid":
+        L = inputs.WORKLOADS[args.workload].L
+        axis = inputs.grid_axis_of(L)
+        rr = torch.empty(N, device=dev)
+        ri = torch.empty(N, device=dev)
+
+        def pre():
+            pass
+
+        def main_kernel():
+            binding.fhd_cg_grid(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], (L, L, L), axis, k_iters,
+                                0.0, rr, ri)
+        terms_per_step = float(N) * M * (1 + 2 * k_iters)
     elif args.op == "normal":
         qr = torch.empty(N, device=dev)
         qi = torch.empty(N, device=dev)
@@ -463,7 +490,7 @@ def bench_other(args) -> int:
                            "peak": P_MFMA_FP32 / 1e12, "unit": "TFLOP/s",
                            "frac": achieved / P_MFMA_FP32,
                            "traffic": measured_traffic("grid", args.workload)}
-    elif args.op in ("grid_bf16x3", "forward_grid"):
+    elif args.op in ("grid_bf16x3", "forward_grid", "normal_grid", "cg_grid"):
         # three bf16 products per real product: 3 x 8 FLOP per term on the
         # bf16 matrix cores (2.5 PFLOP/s dense)
         achieved = 3 * MFMA_FLOP_PER_TERM * k_rate

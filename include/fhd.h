@@ -266,6 +266,37 @@ int fhd_cg(const float *kx, const float *ky, const float *kz,
 int64_t fhd_cg_workspace_bytes(int M, int N, int max_iter);
 
 /*
+ * F^H F p on the Cartesian grid of fhd_compute_grid: fhd_forward_grid into a
+ * stream-ordered workspace, then the grid F^H (loop fission, as fhd_normal;
+ * section 17.3.2 names F^H F).
+ *   kx, ky, kz : M fp32 (read only); nx, ny, nz, axis: as fhd_compute_grid
+ *   precision  : FHD_GRID_BF16X3 (the only mode)
+ *   p_r, p_i   : nx*ny*nz fp32 (read only)
+ *   q_r, q_i   : nx*ny*nz fp32 (written), not overlapping any input
+ * M = 0 writes zeros; an empty grid does nothing.
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
+ */
+int fhd_normal_grid(const float *kx, const float *ky, const float *kz, int M,
+                    int nx, int ny, int nz, const float *axis, int precision,
+                    const float *p_r, const float *p_i, float *q_r, float *q_i,
+                    void *stream);
+
+/*
+ * fhd_cg with the voxels on the Cartesian grid of fhd_compute_grid and the
+ * matrix-core operators (F^H D and F^H F as fhd_compute_grid and
+ * fhd_normal_grid). Same iteration, scalars, stopping rule and outputs as
+ * fhd_cg; rho_r, rho_i hold nx*ny*nz values. precision: FHD_GRID_BF16X3.
+ * The workspace is fhd_cg_workspace_bytes(M, nx*ny*nz, max_iter) bytes,
+ * stream-ordered; the call synchronises `stream`.
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
+ */
+int fhd_cg_grid(const float *kx, const float *ky, const float *kz,
+                const float *Dr, const float *Di, int M,
+                int nx, int ny, int nz, const float *axis, int precision,
+                float *rho_r, float *rho_i, int max_iter, float tol,
+                int *iters_done, float *residuals, void *stream);
+
+/*
  * Launch shape of the gather kernel: voxels per lane, samples per packed
  * chunk and workgroup size (threads). Any pointer may be NULL.
  */

@@ -82,6 +82,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_grid_gather.restype = i32
     lib.fhd_forward_grid.argtypes = [fp] * 3 + [i32] * 4 + [fpp, i32, fp, fp, fp, fp, vp]
     lib.fhd_forward_grid.restype = i32
+    lib.fhd_normal_grid.argtypes = [fp] * 3 + [i32] * 4 + [fpp, i32, fp, fp, fp, fp, vp]
+    lib.fhd_normal_grid.restype = i32
+    lib.fhd_cg_grid.argtypes = ([fp] * 5 + [i32] * 4 + [fpp, i32, fp, fp, i32, ctypes.c_float,
+                                                      ctypes.POINTER(ctypes.c_int), fp, vp])
+    lib.fhd_cg_grid.restype = i32
     lib.fhd_gather_config.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
     lib.fhd_gather_config.restype = None
     lib.fhd_status_string.argtypes = [i32]
@@ -353,6 +358,49 @@ def fhd_forward_grid(kx, ky, kz, shape, axis, rho_r, rho_i, Dr=None, Di=None, st
         _check(lib, lib.fhd_forward_grid(*ks, M, nx, ny, nz, _axis(axis), int(precision), *img, *outs,
                                          _stream(dev, stream)), "fhd_forward_grid")
     return Dr, Di
+
+
+def fhd_normal_grid(kx, ky, kz, shape, axis, p_r, p_i, q_r=None, q_i=None, stream=None,
+                    precision: int = FHD_GRID_BF16X3):
+    """q = F^H F p for p on the grid shape = (nx, ny, nz). Returns (q_r, q_i)."""
+    lib = load()
+    nx, ny, nz = (int(v) for v in shape)
+    M, N = kx.numel(), nx * ny * nz
+    dev = kx.device
+    if q_r is None:
+        q_r = torch.empty(N, dtype=torch.float32, device=dev)
+    if q_i is None:
+        q_i = torch.empty(N, dtype=torch.float32, device=dev)
+    ks = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"))]
+    vs = [_vec(t, nm, N, dev) for t, nm in ((p_r, "p_r"), (p_i, "p_i"), (q_r, "q_r"), (q_i, "q_i"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_normal_grid(*ks, M, nx, ny, nz, _axis(axis), int(precision), *vs,
+                                        _stream(dev, stream)), "fhd_normal_grid")
+    return q_r, q_i
+
+
+def fhd_cg_grid(kx, ky, kz, Dr, Di, shape, axis, max_iter: int, tol: float = 0.0,
+                rho_r=None, rho_i=None, stream=None, precision: int = FHD_GRID_BF16X3):
+    """CG on F^H F rho = F^H D with rho on the grid shape = (nx, ny, nz)
+    (synchronises the stream). Returns (rho_r, rho_i, iterations, residuals)."""
+    import numpy as np
+    lib = load()
+    nx, ny, nz = (int(v) for v in shape)
+    M, N = kx.numel(), nx * ny * nz
+    dev = kx.device
+    if rho_r is None:
+        rho_r = torch.empty(N, dtype=torch.float32, device=dev)
+    if rho_i is None:
+        rho_i = torch.empty(N, dtype=torch.float32, device=dev)
+    ks = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"), (Dr, "Dr"), (Di, "Di"))]
+    outs = [_vec(t, nm, N, dev) for t, nm in ((rho_r, "rho_r"), (rho_i, "rho_i"))]
+    done = ctypes.c_int(0)
+    res = np.zeros(int(max_iter) + 1, dtype=np.float32)
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_cg_grid(*ks, M, nx, ny, nz, _axis(axis), int(precision), *outs,
+                                    int(max_iter), float(tol), ctypes.byref(done), res.ctypes.data,
+                                    _stream(dev, stream)), "fhd_cg_grid")
+    return rho_r, rho_i, done.value, res[:done.value + 1].copy()
 
 
 def new_packed(M: int, device) -> torch.Tensor:

@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -199,15 +200,15 @@ int read_back(void *dst, const void *src, size_t bytes, hipStream_t s)
     return FHD_OK;
 }
 
-int run_cg(const float *kx, const float *ky, const float *kz, const float *Dr, const float *Di,
-           const float *x, const float *y, const float *z, float *rho_r, float *rho_i, int M, int N,
-           int max_iter, float tol, int *iters_done, float *residuals, const CgWork &w,
-           hipStream_t s)
+// The CG loop over operator callbacks: rhs() writes b = F^H D into w.r,
+// normal() writes F^H F p (p in w.p) into w.ap; both enqueue on `s`.
+template <class Rhs, class Normal>
+int run_cg(Rhs &&rhs, Normal &&normal_op, float *rho_r, float *rho_i, int N, int max_iter, float tol,
+           int *iters_done, float *residuals, const CgWork &w, hipStream_t s)
 {
     const int64_t n = N;
     // b = F^H D into r; rho = 0; p = r; rs = <r, r>
-    int rc = launch_pack(kx, ky, kz, Dr, Di, M, w.smp, s);
-    if (rc == FHD_OK) rc = launch_gather(w.smp, M, x, y, z, w.r_r, w.r_i, N, s);
+    int rc = rhs();
     if (rc != FHD_OK) return rc;
     cg_start_kernel<<<vec_blocks(n), kVecBlock, 0, s>>>(rho_r, rho_i, w.p_r, w.p_i, w.r_r, w.r_i, n);
     if ((rc = launch_status("cg_start_kernel launch")) != FHD_OK) return rc;
@@ -219,7 +220,7 @@ int run_cg(const float *kx, const float *ky, const float *kz, const float *Dr, c
         if (!active) break;
         const int batch = std::min(kBatch, max_iter - launched);
         for (int b = 0; b < batch; ++b) {
-            if ((rc = normal(kx, ky, kz, x, y, z, M, N, w, s)) != FHD_OK) return rc;
+            if ((rc = normal_op()) != FHD_OK) return rc;
             rc = dot<DotUse::kAlpha>(w.p_r, w.p_i, w.ap_r, w.ap_i, n, w, max_iter, tol, s);
             if (rc != FHD_OK) return rc;
             cg_step_kernel<<<vec_blocks(n), kVecBlock, 0, s>>>(rho_r, rho_i, w.r_r, w.r_i, w.p_r,
@@ -244,6 +245,48 @@ int run_cg(const float *kx, const float *ky, const float *kz, const float *Dr, c
     return FHD_OK;
 }
 
+// Carves the workspace of fhd_cg_workspace_bytes(M, N, max_iter) bytes
+// (stream-ordered) into the CG vectors and scratch.
+int64_t work_bytes(int M, int N, int max_iter)
+{
+    const int64_t nb = (int64_t)N * 4, mb = (int64_t)M * 4;
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    return 6 * up(nb) + up(packed_bytes_for(N)) + up(packed_bytes_for(M)) + 2 * up(mb) +
+           up(kDotBlocks * 8) + up(sizeof(CgState)) + up(((int64_t)max_iter + 1) * 8);
+}
+
+int alloc_work(int M, int N, int max_iter, hipStream_t s, char **ws, CgWork *w)
+{
+    const int64_t mb = (int64_t)M * 4, nb = (int64_t)N * 4;
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    const int64_t bytes = work_bytes(M, N, max_iter);
+    const hipError_t e = hipMallocAsync((void **)ws, (size_t)bytes, s);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+    }
+    char *c = *ws;
+    auto take = [&](int64_t b) {
+        char *p = c;
+        c += up(b);
+        return p;
+    };
+    w->r_r = (float *)take(nb);
+    w->r_i = (float *)take(nb);
+    w->p_r = (float *)take(nb);
+    w->p_i = (float *)take(nb);
+    w->ap_r = (float *)take(nb);
+    w->ap_i = (float *)take(nb);
+    w->vox = (float *)take(packed_bytes_for(N));
+    w->smp = (float *)take(packed_bytes_for(M));
+    w->d_r = (float *)take(mb);
+    w->d_i = (float *)take(mb);
+    w->partial = (double *)take(kDotBlocks * 8);
+    w->state = (CgState *)take(sizeof(CgState));
+    w->history = (double *)take(((int64_t)max_iter + 1) * 8);
+    return FHD_OK;
+}
+
 }  // namespace
 }  // namespace fhd
 
@@ -252,10 +295,7 @@ using namespace fhd;
 extern "C" int64_t fhd_cg_workspace_bytes(int M, int N, int max_iter)
 {
     if (M < 0 || N < 0 || max_iter < 0) return -1;
-    const int64_t nb = (int64_t)N * 4, mb = (int64_t)M * 4;
-    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
-    return 6 * up(nb) + up(packed_bytes_for(N)) + up(packed_bytes_for(M)) + 2 * up(mb) +
-           up(kDotBlocks * 8) + up(sizeof(CgState)) + up(((int64_t)max_iter + 1) * 8);
+    return work_bytes(M, N, max_iter);
 }
 
 extern "C" int fhd_cg(const float *kx, const float *ky, const float *kz, const float *Dr,
@@ -282,36 +322,121 @@ extern "C" int fhd_cg(const float *kx, const float *ky, const float *kz, const f
 
     hipStream_t s = (hipStream_t)stream;
     char *ws = nullptr;
-    const int64_t bytes = fhd_cg_workspace_bytes(M, N, max_iter);
-    hipError_t e = hipMallocAsync((void **)&ws, (size_t)bytes, s);
+    CgWork w;
+    if ((rc = alloc_work(M, N, max_iter, s, &ws, &w)) != FHD_OK) return rc;
+    rc = run_cg(
+        [&] {
+            int r = launch_pack(kx, ky, kz, Dr, Di, M, w.smp, s);
+            return r == FHD_OK ? launch_gather(w.smp, M, x, y, z, w.r_r, w.r_i, N, s) : r;
+        },
+        [&] { return normal(kx, ky, kz, x, y, z, M, N, w, s); }, rho_r, rho_i, N, max_iter, tol,
+        iters_done, residuals, w, s);
+    const hipError_t e = hipFreeAsync(ws, s);
+    if (e != hipSuccess && rc == FHD_OK)
+        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
+    return rc;
+}
+
+// ---------------------------------------------------------------------------
+// The same on a Cartesian voxel grid with the matrix-core operators
+// (F by fhd_forward_grid's kernel, F^H by fhd_grid_gather's).
+// ---------------------------------------------------------------------------
+namespace {
+int check_grid_cg_args(int M, int nx, int ny, int nz, const float *axis, int precision, int64_t *N)
+{
+    if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
+    if (nx < 0 || ny < 0 || nz < 0) return fail(FHD_ERR_INVALID_ARG, "negative grid size");
+    const int64_t n = (int64_t)nx * ny * nz;
+    if (n > INT32_MAX) return fail(FHD_ERR_INVALID_ARG, "nx*ny*nz exceeds 2^31 - 1");
+    if (!axis) return fail(FHD_ERR_INVALID_ARG, "axis is NULL");
+    for (int i = 0; i < 6; ++i)
+        if (!std::isfinite(axis[i])) return fail(FHD_ERR_INVALID_ARG, "axis holds a non-finite value");
+    if (precision != FHD_GRID_BF16X3)
+        return fail(FHD_ERR_INVALID_ARG, "the grid operators F^H F and CG support FHD_GRID_BF16X3 only");
+    *N = n;
+    return FHD_OK;
+}
+}  // namespace
+
+extern "C" int fhd_normal_grid(const float *kx, const float *ky, const float *kz, int M, int nx, int ny,
+                               int nz, const float *axis, int precision, const float *p_r,
+                               const float *p_i, float *q_r, float *q_i, void *stream)
+{
+    clear_error();
+    int64_t N = 0;
+    int rc = check_grid_cg_args(M, nx, ny, nz, axis, precision, &N);
+    if (rc != FHD_OK || N == 0) return rc;
+    const int64_t mb = (int64_t)M * 4, nb = N * 4;
+    const Span all[] = {{kx, mb, "kx"}, {ky, mb, "ky"},   {kz, mb, "kz"},  {p_r, nb, "p_r"},
+                        {p_i, nb, "p_i"}, {q_r, nb, "q_r"}, {q_i, nb, "q_i"}};
+    rc = check_host_side(all, 7);
+    if (rc == FHD_OK) rc = check_no_overlap(all, 7, 5);
+    if (rc == FHD_OK) rc = check_device_spans(all, 7);
+    if (rc != FHD_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) return launch_reduce(nullptr, nullptr, 0, N, q_r, q_i, s);   // no samples: 0
+    // workspace: D (2 M floats) and the packed samples
+    const int64_t up_d = (2 * mb + 255) / 256 * 256;
+    char *ws = nullptr;
+    hipError_t e = hipMallocAsync((void **)&ws, (size_t)(up_d + packed_bytes_for(M)), s);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
     }
-    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
-    char *c = ws;
-    auto take = [&](int64_t b) {
-        char *p = c;
-        c += up(b);
-        return p;
-    };
-    CgWork w;
-    w.r_r = (float *)take(nb);
-    w.r_i = (float *)take(nb);
-    w.p_r = (float *)take(nb);
-    w.p_i = (float *)take(nb);
-    w.ap_r = (float *)take(nb);
-    w.ap_i = (float *)take(nb);
-    w.vox = (float *)take(packed_bytes_for(N));
-    w.smp = (float *)take(packed_bytes_for(M));
-    w.d_r = (float *)take(mb);
-    w.d_i = (float *)take(mb);
-    w.partial = (double *)take(kDotBlocks * 8);
-    w.state = (CgState *)take(sizeof(CgState));
-    w.history = (double *)take(((int64_t)max_iter + 1) * 8);
-    rc = run_cg(kx, ky, kz, Dr, Di, x, y, z, rho_r, rho_i, M, N, max_iter, tol, iters_done,
-                residuals, w, s);
+    float *d_r = (float *)ws, *d_i = d_r + M, *smp = (float *)(ws + up_d);
+    rc = launch_forward_grid(p_r, p_i, nx, ny, nz, axis, precision, kx, ky, kz, M, d_r, d_i, s);
+    if (rc == FHD_OK) rc = launch_pack(kx, ky, kz, d_r, d_i, M, smp, s);
+    if (rc == FHD_OK) rc = launch_grid_gather(smp, M, nx, ny, nz, axis, precision, q_r, q_i, s);
     e = hipFreeAsync(ws, s);
+    if (e != hipSuccess && rc == FHD_OK)
+        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
+    return rc;
+}
+
+extern "C" int fhd_cg_grid(const float *kx, const float *ky, const float *kz, const float *Dr,
+                           const float *Di, int M, int nx, int ny, int nz, const float *axis,
+                           int precision, float *rho_r, float *rho_i, int max_iter, float tol,
+                           int *iters_done, float *residuals, void *stream)
+{
+    clear_error();
+    int64_t N64 = 0;
+    int rc = check_grid_cg_args(M, nx, ny, nz, axis, precision, &N64);
+    if (rc != FHD_OK) return rc;
+    if (max_iter < 0) return fail(FHD_ERR_INVALID_ARG, "max_iter < 0");
+    if (!iters_done) return fail(FHD_ERR_INVALID_ARG, "iters_done is NULL");
+    if (!(tol >= 0.0f)) return fail(FHD_ERR_INVALID_ARG, "tol must be >= 0");
+    *iters_done = 0;
+    if (N64 == 0) return FHD_OK;
+    const int N = (int)N64;
+    const int64_t mb = (int64_t)M * 4, nb = N64 * 4;
+    const Span all[] = {{kx, mb, "kx"}, {ky, mb, "ky"}, {kz, mb, "kz"}, {Dr, mb, "Dr"},
+                        {Di, mb, "Di"}, {rho_r, nb, "rho_r"}, {rho_i, nb, "rho_i"}};
+    rc = check_host_side(all, 7);
+    if (rc == FHD_OK) rc = check_no_overlap(all, 7, 5);
+    if (rc == FHD_OK) rc = check_device_spans(all, 7);
+    if (rc != FHD_OK) return rc;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = nullptr;
+    CgWork w;
+    if ((rc = alloc_work(M, N, max_iter, s, &ws, &w)) != FHD_OK) return rc;
+    rc = run_cg(
+        [&] {
+            if (M == 0) return launch_reduce(nullptr, nullptr, 0, N, w.r_r, w.r_i, s);
+            int r = launch_pack(kx, ky, kz, Dr, Di, M, w.smp, s);
+            return r == FHD_OK ? launch_grid_gather(w.smp, M, nx, ny, nz, axis, precision, w.r_r, w.r_i, s)
+                               : r;
+        },
+        [&] {
+            if (M == 0) return launch_reduce(nullptr, nullptr, 0, N, w.ap_r, w.ap_i, s);
+            int r = launch_forward_grid(w.p_r, w.p_i, nx, ny, nz, axis, precision, kx, ky, kz, M, w.d_r,
+                                        w.d_i, s);
+            if (r == FHD_OK) r = launch_pack(kx, ky, kz, w.d_r, w.d_i, M, w.smp, s);
+            return r == FHD_OK ? launch_grid_gather(w.smp, M, nx, ny, nz, axis, precision, w.ap_r, w.ap_i, s)
+                               : r;
+        },
+        rho_r, rho_i, N, max_iter, tol, iters_done, residuals, w, s);
+    const hipError_t e = hipFreeAsync(ws, s);
     if (e != hipSuccess && rc == FHD_OK)
         rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
     return rc;

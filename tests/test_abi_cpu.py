@@ -36,6 +36,9 @@ def lib():
     lib.fhd_compute_grid.argtypes = [vp] * 5 + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 3
     lib.fhd_grid_gather.argtypes = [vp] + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 3
     lib.fhd_forward_grid.argtypes = [vp] * 3 + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 5
+    lib.fhd_normal_grid.argtypes = [vp] * 3 + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 5
+    lib.fhd_cg_grid.argtypes = ([vp] * 5 + [ctypes.c_int] * 4 + [vp, ctypes.c_int] + [vp] * 2 +
+                                [ctypes.c_int, ctypes.c_float, vp, vp, vp])
     lib.fhd_last_error.restype = ctypes.c_char_p
     lib.fhd_status_string.restype = ctypes.c_char_p
     return lib
@@ -52,7 +55,8 @@ def test_header_declares_the_entry_points():
     for n in ("fhd_compute", "fhd_pack", "fhd_gather", "fhd_packed_bytes",
               "fhd_status_string", "fhd_last_error", "fhd_gather_config",
               "fhd_forward", "fhd_forward_pack", "fhd_forward_gather", "fhd_normal",
-              "fhd_cg", "fhd_cg_workspace_bytes", "fhd_compute_grid", "fhd_grid_gather", "fhd_forward_grid"):
+              "fhd_cg", "fhd_cg_workspace_bytes", "fhd_compute_grid", "fhd_grid_gather", "fhd_forward_grid",
+              "fhd_normal_grid", "fhd_cg_grid"):
         assert n in names
 
 
@@ -239,3 +243,30 @@ def test_forward_grid_argument_checks(lib):
     bad[1] = img[0]                                                    # Di aliases rho_r
     assert lib.fhd_forward_grid(*k, 8, 4, 4, 4, ax, 1, *img, *bad, None) == FHD_ERR_INVALID_ARG
     assert "overlaps" in _last(lib)
+
+
+def test_normal_and_cg_grid_argument_checks(lib):
+    axis = (ctypes.c_float * 6)(-0.5, 1 / 16, -0.5, 1 / 16, -0.5, 1 / 16)
+    ax = ctypes.addressof(axis)
+    done = ctypes.c_int(9)
+    d = ctypes.addressof(done)
+    fake = [0x100000 * (i + 1) for i in range(7)]
+    assert lib.fhd_normal_grid(*fake[:3], 8, 4, 4, 4, ax, 0, *fake[3:], None) == FHD_ERR_INVALID_ARG
+    assert "BF16X3" in _last(lib)
+    assert lib.fhd_normal_grid(*fake[:3], -1, 4, 4, 4, ax, 1, *fake[3:], None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_normal_grid(*fake[:3], 8, 0, 4, 4, ax, 1, *fake[3:], None) == FHD_OK
+    bad = list(fake)
+    bad[5] = bad[3]                                                    # q_r aliases p_r
+    assert lib.fhd_normal_grid(*bad[:3], 8, 4, 4, 4, ax, 1, *bad[3:], None) == FHD_ERR_INVALID_ARG
+    args = fake[:5]
+    assert lib.fhd_cg_grid(*args, 8, 4, 4, 4, ax, 1, fake[5], fake[6], 3, 0.0, None, None,
+                           None) == FHD_ERR_INVALID_ARG
+    assert "iters_done" in _last(lib)
+    assert lib.fhd_cg_grid(*args, 8, 4, 4, 4, ax, 1, fake[5], fake[6], -1, 0.0, d, None,
+                           None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_cg_grid(*args, 8, 4, 4, 4, ax, 1, fake[5], fake[6], 3, float("nan"), d, None,
+                           None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_cg_grid(*args, 8, 4, 4, 4, ax, 0, fake[5], fake[6], 3, 0.0, d, None,
+                           None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_cg_grid(*args, 8, 4, 0, 4, ax, 1, None, None, 3, 0.0, d, None, None) == FHD_OK
+    assert done.value == 0

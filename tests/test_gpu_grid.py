@@ -261,3 +261,71 @@ def test_forward_grid_repeatable_and_empty(dev):
     binding.fhd_forward_grid(*k, (0, 4, 4), ODD_AXIS, t(e, dev), t(e, dev), Dr, Di)
     torch.cuda.synchronize(dev)
     assert torch.count_nonzero(Dr).item() == 0 and torch.count_nonzero(Di).item() == 0
+
+
+# ---------------------------------------------------------------------------
+# F^H F and CG on a grid (fhd_normal_grid, fhd_cg_grid)
+# ---------------------------------------------------------------------------
+def test_normal_grid_is_N_identity_on_full_cartesian_grid(dev):
+    L = 16
+    kx, ky, kz = inputs.cartesian_kgrid(L)
+    N = L ** 3
+    pr, pi = inputs.random_image(N, seed=81)
+    qr, qi = binding.fhd_normal_grid(t(kx, dev), t(ky, dev), t(kz, dev), (L, L, L),
+                                     inputs.grid_axis_of(L), t(pr, dev), t(pi, dev))
+    torch.cuda.synchronize(dev)
+    check("grid F^H F = N I", qr.cpu().numpy(), qi.cpu().numpy(), N * pr.astype(np.float64),
+          N * pi.astype(np.float64))
+
+
+def test_normal_grid_matches_oracle_composition(dev):
+    shape = (40, 9, 7)
+    N = int(np.prod(shape))
+    c = inputs.random_case(1, 2000, seed=82, kmax=12.0)
+    pr, pi = inputs.random_image(N, seed=83)
+    k = [t(c[a], dev) for a in ("kx", "ky", "kz")]
+    qr, qi = binding.fhd_normal_grid(*k, shape, ODD_AXIS, t(pr, dev), t(pi, dev))
+    torch.cuda.synchronize(dev)
+    x, y, z = inputs.coords_from_axis(*shape, ODD_AXIS)
+    Dr, Di = oracle.forward(c["kx"], c["ky"], c["kz"], pr, pi, x, y, z)
+    ref = oracle.fhd(c["kx"], c["ky"], c["kz"], Dr, Di, x, y, z)
+    check("grid F^H F p", qr.cpu().numpy(), qi.cpu().numpy(), *ref)
+
+
+def _cg_grid_case():
+    L = 8
+    rng = np.random.default_rng(72)
+    M = 3000
+    k = rng.uniform(-3.5, 3.5, (3, M)).astype(np.float32)
+    D = rng.standard_normal((2, M)).astype(np.float32)
+    x, y, z = inputs.grid_coords(L)
+    return L, dict(kx=k[0], ky=k[1], kz=k[2], Dr=D[0], Di=D[1], x=x, y=y, z=z)
+
+
+@pytest.mark.parametrize("iters", [6, 9])
+def test_cg_grid_matches_oracle_cg(dev, iters):
+    L, c = _cg_grid_case()
+    d = [t(c[a], dev) for a in ("kx", "ky", "kz", "Dr", "Di")]
+    rr, ri, done, res = binding.fhd_cg_grid(*d, (L, L, L), inputs.grid_axis_of(L), iters)
+    torch.cuda.synchronize(dev)
+    ref, ref_res = oracle.cg(c["kx"], c["ky"], c["kz"], c["Dr"], c["Di"], c["x"], c["y"], c["z"],
+                             iters=iters)
+    assert done == iters == len(ref_res) - 1
+    check("grid cg %d iterations" % iters, rr.cpu().numpy(), ri.cpu().numpy(), ref.real, ref.imag)
+    assert np.allclose(res, ref_res, rtol=1e-3, atol=0), (res, ref_res)
+
+
+def test_cg_grid_one_step_on_full_grid(dev):
+    L = 16
+    kx, ky, kz = inputs.cartesian_kgrid(L)
+    x, y, z = inputs.grid_coords(L)
+    tr, ti = inputs.random_image(L ** 3, seed=84)
+    Dr, Di = oracle.forward(kx, ky, kz, tr, ti, x, y, z)
+    rs0 = float(L ** 6 * np.sum(tr.astype(np.float64) ** 2 + ti.astype(np.float64) ** 2))
+    d = [t(a, dev) for a in (kx, ky, kz, Dr.astype(np.float32), Di.astype(np.float32))]
+    rr, ri, done, res = binding.fhd_cg_grid(*d, (L, L, L), inputs.grid_axis_of(L), 5,
+                                            tol=1e-8 * rs0)
+    torch.cuda.synchronize(dev)
+    assert done == 1, res
+    check("grid cg full grid", rr.cpu().numpy(), ri.cpu().numpy(), tr.astype(np.float64),
+          ti.astype(np.float64))
