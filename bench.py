@@ -52,7 +52,9 @@ METRIC = "F^H D voxel-sample terms/s at 128^3 x 100k; % of FP32 VALU/trans roofl
 # 13 FLOP (the fixed convention); the transcendentals a term needs depend
 # on the gather's path: 2 where each term's sin and cos are evaluated
 # (ROOF_TERMS = min(P_fp32 / 13, P_trans / 2), transcendental-bound), 4
-# per 8 terms on the ramp path, whose ceiling is then the FP32 one.
+# per sample and lane of 16 voxels on the F^H ramp path (4 per sample and
+# chunk of 8 voxels for F's ramp chunks), whose ceiling is then the FP32
+# one.
 CUS, SIMDS_PER_CU, TRANS_LANES_PER_CYCLE, CLOCK_HZ = 256, 4, 8, 2.4e9
 P_FP32 = 157.3e12
 P_TRANS = CUS * SIMDS_PER_CU * TRANS_LANES_PER_CYCLE * CLOCK_HZ
@@ -63,7 +65,8 @@ MFMA_FLOP_PER_TERM = 8
 P_MFMA_FP32 = 157.3e12
 P_MFMA_BF16 = 2.5e15
 TRANS_PER_TERM_DIRECT = 2.0
-TRANS_PER_TERM_RAMP = 4.0 / 8
+TRANS_PER_TERM_RAMP = 4.0 / 16   # F^H D: 4 per sample and lane of 16 voxels
+TRANS_PER_TERM_RAMP_F = 4.0 / 8  # F: 4 per sample and chunk of 8 voxels
 ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / TRANS_PER_TERM_DIRECT)
 
 
@@ -462,13 +465,14 @@ def bench_other(args) -> int:
     k_rate = terms_per_step / (float(np.mean(kms)) * 1e-3)
     # ceiling: F^H terms at the adjoint gather's path mix, F terms direct
     NM = float(N) * M
-    ramp = ramp_voxel_fraction(w["x"], w["y"], w["z"])
+    gcfg = binding.gather_config()
+    ramp = ramp_voxel_fraction(w["x"], w["y"], w["z"], gcfg["block_threads"], gcfg["voxels_per_lane"])
     ramp_f = ramp_chunk_fraction(w["x"], w["y"], w["z"])
     adjoint = {"normal": 1, "cg": 1 + k_iters}.get(args.op, 0)
     forward_terms = {"forward": 1, "normal": 1, "cg": k_iters}.get(args.op, 0)
     roof = roof_terms([(adjoint * NM * ramp, TRANS_PER_TERM_RAMP),
                        (adjoint * NM * (1 - ramp), TRANS_PER_TERM_DIRECT),
-                       (forward_terms * NM * ramp_f, TRANS_PER_TERM_RAMP),
+                       (forward_terms * NM * ramp_f, TRANS_PER_TERM_RAMP_F),
                        (forward_terms * NM * (1 - ramp_f), TRANS_PER_TERM_DIRECT)])
     out = {
         "metric": "%s voxel-sample terms/s (%s)" % (args.op, args.workload),
