@@ -43,18 +43,26 @@ sys.path.insert(0, ROOT)
 
 METRIC = "F^H D voxel-sample terms/s at 128^3 x 100k; % of FP32 VALU/trans roofline"
 
-# gfx950 ALU ceiling of the gathers, from unit counts and clock:
-# 256 CUs x 4 SIMDs at 2.4 GHz. FP32 vector peak 157.3 TFLOP/s (AMD's
-# figure). v_sin_f32 / v_cos_f32 issue one wave64 instruction per 8 SIMD
-# cycles, i.e. 8 lanes per cycle per SIMD (measured by the issue-rate
-# micro-benchmarks; a quarter of the FP32 FMA rate), so the
+# gfx950 ALU ceilings of the gathers, from unit counts and clock: 256 CUs
+# x 4 SIMDs at 2.4 GHz. FP32 vector peak 157.3 TFLOP/s (AMD's figure:
+# two FP32 FMA instructions per SIMD issue quad-cycle). v_sin_f32 /
+# v_cos_f32 issue one wave64 instruction per 8 SIMD cycles, i.e. 8 lanes
+# per cycle per SIMD (measured by the issue-rate micro-benchmarks), so the
 # transcendental peak is 256 * 4 * 8 * 2.4e9 = 1.97e13 /s. A term counts
-# 13 FLOP (the fixed convention); the transcendentals a term needs depend
-# on the gather's path: 2 where each term's sin and cos are evaluated
-# (ROOF_TERMS = min(P_fp32 / 13, P_trans / 2), transcendental-bound), 4
-# per sample and lane of 16 voxels on the F^H ramp path (4 per sample and
-# chunk of 8 voxels for F's ramp chunks), whose ceiling is then the FP32
-# one.
+# 13 FLOP (the fixed convention) and every ceiling is quoted as 13 x
+# terms/s.
+#   direct evaluation (sin and cos of every term): R = min(P_fp32 / 13,
+#     P_trans / 2) = 9.83e12 terms/s, transcendental-bound;
+#   ramp evaluation (F^H D, 16 voxels per lane): per sample and lane 4
+#     transcendentals and 71 other VALU instructions (phase 3, step 1,
+#     amplitude 2, rotation 4, 2 cos 1, 2 x 2 adds for the two seeds, 14
+#     x (2 FMA + 2 adds)) for 16 terms; the 13-FLOP convention no longer
+#     bounds it, the issue port does: at best two VALU instructions per
+#     quad-cycle and two quad-cycles per transcendental, i.e.
+#     4 (71/2 + 2 x 4) / 16 = 10.9 clk per wave-term, 1.45e13 terms/s;
+#   F's ramp chunks (Horner): per sample and chunk of 8 voxels 4
+#     transcendentals and 36 VALU (phase 3, step 1, Horner 28, finish 4):
+#     13 clk per wave-term, 1.21e13 terms/s.
 CUS, SIMDS_PER_CU, TRANS_LANES_PER_CYCLE, CLOCK_HZ = 256, 4, 8, 2.4e9
 P_FP32 = 157.3e12
 P_TRANS = CUS * SIMDS_PER_CU * TRANS_LANES_PER_CYCLE * CLOCK_HZ
@@ -65,17 +73,26 @@ MFMA_FLOP_PER_TERM = 8
 P_MFMA_FP32 = 157.3e12
 P_MFMA_BF16 = 2.5e15
 TRANS_PER_TERM_DIRECT = 2.0
-TRANS_PER_TERM_RAMP = 4.0 / 16   # F^H D: 4 per sample and lane of 16 voxels
-TRANS_PER_TERM_RAMP_F = 4.0 / 8  # F: 4 per sample and chunk of 8 voxels
 ROOF_TERMS = min(P_FP32 / FLOP_PER_TERM, P_TRANS / TRANS_PER_TERM_DIRECT)
 
 
+def issue_terms(valu: float, trans: float) -> float:
+    """Terms/s when each wave64 term needs `valu` VALU instructions (two per
+    quad-cycle at best) and `trans` transcendentals (two quad-cycles each)
+    on every SIMD of the chip."""
+    clk_per_wave_term = 4.0 * (valu / 2.0 + 2.0 * trans)
+    return CUS * SIMDS_PER_CU * CLOCK_HZ * 64 / clk_per_wave_term
+
+
+ROOF_TERMS_RAMP = issue_terms(71.0 / 16, 4.0 / 16)
+ROOF_TERMS_RAMP_F = issue_terms(36.0 / 8, 4.0 / 8)
+
+
 def roof_terms(parts) -> float:
-    """Terms/s ceiling of work made of (terms, transcendentals per term)
-    parts run one after another: total terms over the sum of each part's
-    time at min(P_fp32 / 13, P_trans / t)."""
+    """Terms/s ceiling of work made of (terms, ceiling terms/s) parts run
+    one after another: total terms over the sum of each part's time."""
     total = sum(n for n, _ in parts)
-    t_min = sum(n / min(P_FP32 / FLOP_PER_TERM, P_TRANS / t) for n, t in parts if n > 0)
+    t_min = sum(n / r for n, r in parts if n > 0)
     return total / t_min if t_min > 0 else ROOF_TERMS
 
 
@@ -264,7 +281,7 @@ def main(argv=None) -> int:
     # the ceiling for the paths this voxel layout takes (the x-fastest
     # grids of the workloads: the ramp path throughout)
     ramp = ramp_voxel_fraction(w["x"], w["y"], w["z"], cfg["block_threads"], cfg["voxels_per_lane"])
-    roof = roof_terms([(terms * ramp, TRANS_PER_TERM_RAMP), (terms * (1 - ramp), TRANS_PER_TERM_DIRECT)])
+    roof = roof_terms([(terms * ramp, ROOF_TERMS_RAMP), (terms * (1 - ramp), ROOF_TERMS)])
     achieved = FLOP_PER_TERM * terms / (gather_ms * 1e-3) / 1e12
     peak = FLOP_PER_TERM * roof / 1e12
     out = {
@@ -470,10 +487,10 @@ def bench_other(args) -> int:
     ramp_f = ramp_chunk_fraction(w["x"], w["y"], w["z"])
     adjoint = {"normal": 1, "cg": 1 + k_iters}.get(args.op, 0)
     forward_terms = {"forward": 1, "normal": 1, "cg": k_iters}.get(args.op, 0)
-    roof = roof_terms([(adjoint * NM * ramp, TRANS_PER_TERM_RAMP),
-                       (adjoint * NM * (1 - ramp), TRANS_PER_TERM_DIRECT),
-                       (forward_terms * NM * ramp_f, TRANS_PER_TERM_RAMP_F),
-                       (forward_terms * NM * (1 - ramp_f), TRANS_PER_TERM_DIRECT)])
+    roof = roof_terms([(adjoint * NM * ramp, ROOF_TERMS_RAMP),
+                       (adjoint * NM * (1 - ramp), ROOF_TERMS),
+                       (forward_terms * NM * ramp_f, ROOF_TERMS_RAMP_F),
+                       (forward_terms * NM * (1 - ramp_f), ROOF_TERMS)])
     out = {
         "metric": "%s voxel-sample terms/s (%s)" % (args.op, args.workload),
         "value": value, "unit": "terms/s", "n_gpus": 1, "steps": args.steps,

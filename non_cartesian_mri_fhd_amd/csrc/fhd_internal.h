@@ -14,8 +14,9 @@
 //
 //  * stream_chunks() walks a packed stream through LDS in stages of
 //    kStageChunks chunks, double buffered: while a workgroup works on one
-//    stage, each lane holds three float4 of the next stage in registers and
-//    writes them to the other buffer before the stage barrier. Every lane
+//    stage, the next one is copied straight from memory into the other
+//    buffer (global_load_lds, no registers held), completed before the
+//    stage barrier. Every lane
 //    then reads each chunk with same-address ds_read_b128, which the LDS
 //    broadcasts, so the stream's values reach the FMAs in VGPRs (on gfx950
 //    an FP32 FMA with an SGPR operand issues at half rate and never pairs).
@@ -41,7 +42,7 @@ constexpr int kPackBlock = 256;
 
 static_assert(kBlock % 64 == 0, "workgroup must be whole wave64s");
 static_assert(kChunk * kFields % 4 == 0, "chunks must be whole float4s");
-static_assert(kStageLoads == 3, "stream_chunks holds three float4 per lane");
+static_assert(kStageLoads * kBlock >= kStageVec4, "a stage is at most kStageLoads float4 per lane");
 
 inline int64_t packed_bytes_for(int64_t count)
 {
@@ -92,32 +93,34 @@ __device__ __forceinline__ void stream_chunk_groups(const float4 *__restrict__ s
     src += (int64_t)c_begin * kChunkVec4;
     const int64_t total_vec4 = (int64_t)nchunks * kChunkVec4;
     const int nstages = (nchunks + kStageChunks - 1) / kStageChunks;
-    for (int i = threadIdx.x; i < kStageVec4 && i < total_vec4; i += kBlock) stage[0][i] = src[i];
+    // Stage st's float4 i goes to stage[st & 1][i] by global_load_lds: each
+    // wave's 64 lanes copy 64 consecutive float4 straight into LDS at the
+    // wave's base (lane l at base + l), with no registers in between.
+    const int wave_base = threadIdx.x & ~63;
+    auto load_stage = [&](int st) {
+        float4 *dst = stage[st & 1];
+        const int64_t first = (int64_t)st * kStageVec4;
+#pragma unroll
+        for (int k = 0; k < kStageLoads; ++k) {
+            const int i = k * kBlock + threadIdx.x;
+            if (i < kStageVec4 && first + i < total_vec4)
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(src + first + i),
+                    (__attribute__((address_space(3))) void *)(dst + k * kBlock + wave_base), 16, 0, 0);
+        }
+    };
+    if (nstages > 0) load_stage(0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int st = 0; st < nstages; ++st) {
-        // prefetch the next stage into registers (indices clamped in bounds;
-        // the clamped copies are never written to LDS)
-        const bool more = st + 1 < nstages;
-        const int64_t next = (int64_t)(st + 1) * kStageVec4 + threadIdx.x;
-        float4 r0, r1, r2;
-        if (more) {
-            r0 = src[min(next, total_vec4 - 1)];
-            r1 = src[min(next + kBlock, total_vec4 - 1)];
-            r2 = src[min(next + 2 * kBlock, total_vec4 - 1)];
-        }
+        // the next stage streams into the other buffer (last read before the
+        // previous barrier) while this one is worked on
+        if (st + 1 < nstages) load_stage(st + 1);
         const int chunks_here = min(kStageChunks, nchunks - st * kStageChunks);
         const float4 *buf = stage[st & 1];
         for (int c = 0; c < chunks_here; c += STEP) body(buf + c * kChunkVec4, min(STEP, chunks_here - c));
-        if (more) {
-            // the other buffer was last read before the previous barrier
-            float4 *dst = stage[(st + 1) & 1];
-            const int i0 = threadIdx.x;
-            if (next < total_vec4) dst[i0] = r0;
-            if (i0 + kBlock < kStageVec4 && next + kBlock < total_vec4) dst[i0 + kBlock] = r1;
-            if (i0 + 2 * kBlock < kStageVec4 && next + 2 * kBlock < total_vec4)
-                dst[i0 + 2 * kBlock] = r2;
-        }
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 }

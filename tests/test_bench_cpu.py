@@ -50,12 +50,20 @@ def test_ramp_fraction_mirrors_the_kernel_test():
 
 
 def test_roof_terms_mixes_paths():
-    r_direct = bench.roof_terms([(1.0, bench.TRANS_PER_TERM_DIRECT)])
-    r_ramp = bench.roof_terms([(1.0, bench.TRANS_PER_TERM_RAMP)])
-    assert r_direct == bench.ROOF_TERMS
-    assert r_ramp == bench.P_FP32 / bench.FLOP_PER_TERM
-    mixed = bench.roof_terms([(1.0, bench.TRANS_PER_TERM_RAMP), (1.0, bench.TRANS_PER_TERM_DIRECT)])
+    r_direct, r_ramp = bench.ROOF_TERMS, bench.ROOF_TERMS_RAMP
+    assert bench.roof_terms([(1.0, r_direct)]) == r_direct
+    mixed = bench.roof_terms([(1.0, r_ramp), (1.0, r_direct)])
     assert abs(mixed - 2 / (1 / r_ramp + 1 / r_direct)) < 1e-6 * mixed
+
+
+def test_issue_ceilings():
+    # pure FMA pairs at two per quad-cycle: the FP32 vector peak at 2 FLOP each
+    assert abs(bench.issue_terms(1.0, 0.0) * 2 - bench.P_FP32) / bench.P_FP32 < 2e-3
+    # transcendentals only: the measured transcendental issue rate
+    assert abs(bench.issue_terms(0.0, 1.0) - bench.P_TRANS) / bench.P_TRANS < 1e-12
+    # the ramp paths' ceilings lie above the direct-form R
+    assert bench.ROOF_TERMS_RAMP > bench.ROOF_TERMS_RAMP_F > bench.ROOF_TERMS
+
 
 
 def test_ramp_chunk_fraction():
