@@ -144,18 +144,19 @@ def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 8) -> float:
 # readings (factors 2.0 and 1.0). Valid only for the sources they were taken
 # on (SHA-256 over the listed files, in order); any later edit reports null
 # until the counters are taken again.
-#   fhd  (fhd_gather_kernel): 39.4 MiB read (x, y, z and the packed samples
-#        once per XCD L2) + 16.0 MiB written (rho)
+#   fhd  (fhd_gather_kernel): 59.4 MiB read (x, y, z by each of the 2
+#        sample splits, the packed samples once per XCD L2) + 47.0 MiB
+#        written (2 split partial sums of rho, register spills)
 #   grid (fhd_grid_kernel):   15.4 MiB read (packed samples once per XCD L2)
 #        + 48.0 MiB written (3 split partial sums of rho)
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
     "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
-            "sha256": "5ef3acb66f15cb4557181db1f1a7fcb778c31b9ef15173e79aa71ab81bbbf874",
-            "bytes_per_launch": (20164.0 * 2.0 + 16384 * 1.0) * 1024},
+            "sha256": "85f059516c247b3ccb1226b0ea0af3ebf7ab6475775f3761b374346bf3f4c6a8",
+            "bytes_per_launch": (30399.5 * 2.0 + 48128 * 1.0) * 1024},
     "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
-             "sha256": "52123b52ce807d2bcff36893bc7a982590104eada543d42e2961b7d7621770d0",
-             "bytes_per_launch": (7876.0 * 2.0 + 49152 * 1.0) * 1024},
+             "sha256": "ac3393f12420e92aabc5ef9ed72d6fbe3b3f19558e764a1c3d67733a2c57d476",
+             "bytes_per_launch": (7892.0 * 2.0 + 49152 * 1.0) * 1024},
 }
 
 
