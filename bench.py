@@ -53,13 +53,18 @@ METRIC = "F^H D voxel-sample terms/s at 128^3 x 100k; % of FP32 VALU/trans roofl
 # terms/s.
 #   direct evaluation (sin and cos of every term): R = min(P_fp32 / 13,
 #     P_trans / 2) = 9.83e12 terms/s, transcendental-bound;
-#   ramp evaluation (F^H D, 16 voxels per lane): per sample and lane 4
-#     transcendentals and 71 other VALU instructions (phase 3, step 1,
-#     amplitude 2, rotation 4, 2 cos 1, 2 x 2 adds for the two seeds, 14
-#     x (2 FMA + 2 adds)) for 16 terms; the 13-FLOP convention no longer
-#     bounds it, the issue port does: at best two VALU instructions per
-#     quad-cycle and two quad-cycles per transcendental, i.e.
-#     4 (71/2 + 2 x 4) / 16 = 10.9 clk per wave-term, 1.45e13 terms/s;
+#   ramp evaluation (F^H D, 16 voxels per lane in 8 symmetric pairs, one
+#     x step for the whole workgroup, as on any grid): one lane per sample
+#     writes an LDS record of the pairs' sample-only factors, and every
+#     lane spends per sample 2 transcendentals and 35 other VALU
+#     instructions (centre phase 3, 8 x 4 accumulating FMAs) on 16 terms;
+#     the records cost about 40 VALU and 2 transcendentals per sample and
+#     workgroup of 4096 voxels, which is left out. The 13-FLOP convention
+#     no longer bounds it, the issue port does: at best two VALU
+#     instructions per quad-cycle and two quad-cycles per transcendental,
+#     i.e. 4 (35/2 + 2 x 2) / 16 = 5.4 clk per wave-term, 2.93e13 terms/s
+#     (a workgroup whose lanes step differently forms everything per lane:
+#     55 VALU and 4 transcendentals, 1.77e13);
 #   F's ramp chunks (Horner): per sample and chunk of 8 voxels 4
 #     transcendentals and 36 VALU (phase 3, step 1, Horner 28, finish 4):
 #     13 clk per wave-term, 1.21e13 terms/s.
@@ -84,7 +89,7 @@ def issue_terms(valu: float, trans: float) -> float:
     return CUS * SIMDS_PER_CU * CLOCK_HZ * 64 / clk_per_wave_term
 
 
-ROOF_TERMS_RAMP = issue_terms(71.0 / 16, 4.0 / 16)
+ROOF_TERMS_RAMP = issue_terms(35.0 / 16, 2.0 / 16)
 ROOF_TERMS_RAMP_F = issue_terms(36.0 / 8, 4.0 / 8)
 
 

@@ -32,18 +32,24 @@
 //
 //    When, in addition, each lane's voxels are equally spaced along x
 //    (x_v = x_0 + v dx to fp32 rounding, checked exactly), the phase is a
-//    ramp p_v = p_0 + v d with d = kx dx, and the phasors follow from two
-//    seeds: a e^{i 2 pi p_0} by v_cos/v_sin, its rotation by e^{i 2 pi d}
-//    (also v_cos/v_sin), then the three-term recurrence
-//    w_{v+1} = 2 cos(2 pi d) w_v - w_{v-1}, which holds for any sinusoid of
-//    step d and is linear, so the amplitude rides along. Four
-//    transcendentals per sample and lane instead of 2 kVox. Rounding in the
-//    recurrence grows at most like v^2 ulp (v < kVox); the seeds carry the
-//    same phase rounding as the direct evaluation.
+//    ramp with step d = kx dx. The voxels pair up symmetrically about the
+//    lane's centre, where one phasor u = a e^{i 2 pi p_c} is evaluated; a
+//    pair at +-(j + 1/2) dx from it gets u (C_j +- i S_j) with real
+//    C_j = cos(2 pi (j + 1/2) d), S_j = sin(2 pi (j + 1/2) d), which follow
+//    from cos and sin of half a step by the three-term recurrence of any
+//    sinusoid. The lane accumulates u C_j and i u S_j per pair and unfolds
+//    them into the two voxels at the end: four FMAs per voxel pair. When
+//    all lanes of the workgroup share the step (any grid), C_j and S_j are
+//    the same for every lane, so one lane per sample forms them into an LDS
+//    record and the others read it back: per sample and lane, 3 FMAs of
+//    phase, 2 transcendentals and 32 FMAs for 16 terms. Otherwise each lane
+//    forms them itself (4 transcendentals and 55 VALU operations). Rounding
+//    in the recurrence grows at most like j^2 ulp (j < kVox / 2); the centre
+//    phase carries one more rounding than a direct evaluation.
 //
 // Per voxel-sample term: direct paths, phase 1 + 2/kVox FMA (3 FMA on the
-// general path), v_cos_f32, v_sin_f32, 2 FMA accumulate; ramp path, 4/kVox
-// transcendentals and about 5 VALU operations.
+// general path), v_cos_f32, v_sin_f32, 2 FMA accumulate; ramp path, 2/kVox
+// transcendentals and 35/kVox VALU operations (shared step).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -60,6 +66,7 @@ constexpr int kDirectGroup = 8; // voxels per transcendental group on the direct
 static_assert(kVox % kDirectGroup == 0, "direct groups tile a lane's voxels");
 constexpr int kRampGroup = 4;   // samples per transcendental group on the ramp path
 static_assert(kChunk % kRampGroup == 0, "ramp groups tile a chunk");
+static_assert(kVox % 2 == 0, "the ramp path pairs a lane's voxels");
 
 __global__ __launch_bounds__(kPackBlock) void fhd_pack_kernel(
     const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
@@ -134,11 +141,31 @@ __device__ __forceinline__ void accumulate_chunk(const float4 *ch, const float (
     }
 }
 
-// Ramp path: a lane's V voxels share y and z and sit at x0 + v dx.
+// 2 cos(2 pi d) of the ramp path's recurrence from s = sin(2 pi d / 2),
+// as 2 - 4 s^2, which stays accurate for small steps d.
+__device__ __forceinline__ float ramp_k2(float s) { return __builtin_fmaf(-4.0f * s, s, 2.0f); }
+
+// Ramp path: a lane's V voxels share y and z and sit at x0 + v dx. They
+// pair up around the lane's centre x_c = x0 + (V-1)/2 dx: voxel V/2 + j and
+// voxel V/2 - 1 - j sit at x_c +- (j + 1/2) dx. With h = d/2 = kx dx / 2,
+// p_c = p_0 + (V-1) h and u = a e^{i 2 pi p_c}, their phasors are
+// u (C_j +- i S_j), C_j = cos(2 pi (2j+1) h), S_j = sin(2 pi (2j+1) h), both
+// real. So the lane accumulates, per pair,
+//   sum_j = sum over samples of u C_j      (acc[j])
+//   dif_j = sum over samples of i u S_j    (acc[V/2 + j])
+// at four FMAs per pair, and ramp_unfold() turns them into the two voxels'
+// sums (sum_j + dif_j and sum_j - dif_j). C_j and S_j follow from
+// (cos 2 pi h, sin 2 pi h) by the three-term recurrence
+// c_{j+1} = 2 cos(2 pi d) c_j - c_{j-1} (started at c_{-1} = C_0,
+// s_{-1} = -S_0). Per sample and lane: 4 transcendentals and 55 other VALU
+// instructions for V = 16 terms. (Workgroups whose lanes all share one step
+// take ramp_one_step() instead, which forms the sample-only part once per
+// workgroup.)
 template <int V>
-__device__ __forceinline__ void accumulate_chunk_ramp(const float4 *ch, float x0, float dx, float y,
+__device__ __forceinline__ void accumulate_chunk_ramp(const float4 *ch, float x0, float hdx, float y,
                                                       float z, float (&acc_r)[V], float (&acc_i)[V])
 {
+    constexpr int P = V / 2;   // voxel pairs per lane
     float f[kFields][kChunk];
     load_chunk(ch, f);
     const float(&skx)[kChunk] = f[0];
@@ -148,53 +175,229 @@ __device__ __forceinline__ void accumulate_chunk_ramp(const float4 *ch, float x0
     const float(&amp)[kChunk] = f[4];
     // the transcendentals of kRampGroup samples issue as one group at raised
     // wave priority (longer groups let more of the other waves' VALU work
-    // pair up; 4 measured best)
+    // pair up)
 #pragma unroll
     for (int u0 = 0; u0 < kChunk; u0 += kRampGroup) {
-        float p0[kRampGroup], d[kRampGroup], c0[kRampGroup], s0[kRampGroup], cd[kRampGroup],
-            sd[kRampGroup];
+        float pc[kRampGroup], h[kRampGroup], cc[kRampGroup], sc[kRampGroup], ch1[kRampGroup],
+            sh1[kRampGroup];
 #pragma unroll
         for (int t = 0; t < kRampGroup; ++t) {
             const int u = u0 + t;
-            p0[t] = __builtin_fmaf(skx[u], x0, __builtin_fmaf(sky[u], y, __builtin_fmaf(skz[u], z, psi[u])));
-            d[t] = skx[u] * dx;
+            const float p0 = __builtin_fmaf(skx[u], x0, __builtin_fmaf(sky[u], y, __builtin_fmaf(skz[u], z, psi[u])));
+            h[t] = skx[u] * hdx;
+            pc[t] = __builtin_fmaf((float)(V - 1), h[t], p0);
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < kRampGroup; ++t) {
-            c0[t] = __builtin_amdgcn_cosf(p0[t]);
-            s0[t] = __builtin_amdgcn_sinf(p0[t]);
-            cd[t] = __builtin_amdgcn_cosf(d[t]);
-            sd[t] = __builtin_amdgcn_sinf(d[t]);
+            cc[t] = __builtin_amdgcn_cosf(pc[t]);
+            sc[t] = __builtin_amdgcn_sinf(pc[t]);
+            ch1[t] = __builtin_amdgcn_cosf(h[t]);
+            sh1[t] = __builtin_amdgcn_sinf(h[t]);
         }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < kRampGroup; ++t) {
             const int u = u0 + t;
-            // w_0 = a e^{i 2 pi p0}; w_1 = w_0 e^{i 2 pi d}
-            float wr0 = amp[u] * c0[t], wi0 = amp[u] * s0[t];
-            float wr1 = __builtin_fmaf(wr0, cd[t], -wi0 * sd[t]);
-            float wi1 = __builtin_fmaf(wi0, cd[t], wr0 * sd[t]);
-            const float two_cd = cd[t] + cd[t];
-            acc_r[0] += wr0;
-            acc_i[0] += wi0;
-            acc_r[1] += wr1;
-            acc_i[1] += wi1;
+            const float ur = amp[u] * cc[t], ui = amp[u] * sc[t];
+            const float k2 = ramp_k2(sh1[t]);
+            float cp = ch1[t], sp = -sh1[t];   // index -1
+            float c = ch1[t], s = sh1[t];      // index 0
 #pragma unroll
-            for (int v = 2; v < V; ++v) {
-                const float wr2 = __builtin_fmaf(two_cd, wr1, -wr0);
-                const float wi2 = __builtin_fmaf(two_cd, wi1, -wi0);
-                acc_r[v] += wr2;
-                acc_i[v] += wi2;
-                wr0 = wr1;
-                wi0 = wi1;
-                wr1 = wr2;
-                wi1 = wi2;
+            for (int j = 0; j < P; ++j) {
+                if (j > 0) {
+                    const float cn = __builtin_fmaf(k2, c, -cp), sn = __builtin_fmaf(k2, s, -sp);
+                    cp = c;
+                    sp = s;
+                    c = cn;
+                    s = sn;
+                }
+                acc_r[j] = __builtin_fmaf(ur, c, acc_r[j]);
+                acc_i[j] = __builtin_fmaf(ui, c, acc_i[j]);
+                acc_r[P + j] = __builtin_fmaf(-ui, s, acc_r[P + j]);
+                acc_i[P + j] = __builtin_fmaf(ur, s, acc_i[P + j]);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Ramp path for a workgroup whose lanes all step by the same dx. Then C_j,
+// S_j and the centre offset (V-1) h are sample-only: one lane per sample
+// forms them (with the amplitude folded in) into an LDS record
+//   [a C_0 .. a C_{P-1}][a S_0 .. a S_{P-1}][kx ky kz psi + (V-1) h]
+// (kRampRecord float4), and every lane reads the records back as LDS
+// broadcasts. Per sample and lane: 3 FMAs for the centre phase p_c, cos and
+// sin of it (u / a), and the 4 P accumulating FMAs -- 35 VALU and 2
+// transcendentals for V = 16 terms.
+constexpr int kRampRecord = kVox / 4 + 1;      // float4 per sample record
+constexpr int kSideSamples = 128;               // records per LDS round
+static_assert(kVox % 8 == 0, "a record holds whole float4s of C and S");
+static_assert((kStageChunks * kChunk) % kSideSamples == 0, "rounds tile a stage");
+static_assert(kSideSamples % kRampGroup == 0 && kSideSamples <= kBlock, "one record per lane");
+
+// Lane i < n writes the record of the stage's sample r0 + i.
+template <int V>
+__device__ __forceinline__ void ramp_records(const float4 *buf, int r0, int n, float hdx,
+                                             float4 *side)
+{
+    constexpr int P = V / 2;
+    const int i = threadIdx.x;
+    if (i >= n) return;
+    const int s = r0 + i;
+    const float *b = reinterpret_cast<const float *>(buf) + (s / kChunk) * (kFields * kChunk) + s % kChunk;
+    const float kx = b[0], ky = b[kChunk], kz = b[2 * kChunk], psi = b[3 * kChunk], amp = b[4 * kChunk];
+    const float h = kx * hdx;
+    const float c1 = __builtin_amdgcn_cosf(h), s1 = __builtin_amdgcn_sinf(h), k2 = ramp_k2(s1);
+    float C[P], S[P];
+    float cp = c1, sp = -s1, c = c1, sn = s1;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        if (j > 0) {
+            const float cn = __builtin_fmaf(k2, c, -cp), snn = __builtin_fmaf(k2, sn, -sp);
+            cp = c;
+            sp = sn;
+            c = cn;
+            sn = snn;
+        }
+        C[j] = amp * c;
+        S[j] = amp * sn;
+    }
+    float4 *rec = side + i * kRampRecord;
+#pragma unroll
+    for (int q = 0; q < P / 4; ++q) {
+        rec[q] = make_float4(C[4 * q], C[4 * q + 1], C[4 * q + 2], C[4 * q + 3]);
+        rec[P / 4 + q] = make_float4(S[4 * q], S[4 * q + 1], S[4 * q + 2], S[4 * q + 3]);
+    }
+    rec[P / 2] = make_float4(kx, ky, kz, __builtin_fmaf((float)(V - 1), h, psi));
+}
+
+// Accumulates records [0, n) of `side` (n a multiple of kRampGroup) into
+// the pair sums (acc[j] = sum_j, acc[V/2 + j] = dif_j). The LDS reads run
+// ahead of their use: a group's phase inputs during the previous group's
+// FMAs, a sample's C and S during the previous sample's FMAs (the first
+// sample's during the transcendentals).
+template <int V>
+__device__ __forceinline__ void ramp_accumulate_records(const float4 *side, int n, float x0, float y,
+                                                        float z, float (&acc_r)[V], float (&acc_i)[V])
+{
+    constexpr int P = V / 2;
+    constexpr int Q = P / 2;   // float4 of C and S per record
+    float4 q[kRampGroup];
+#pragma unroll
+    for (int t = 0; t < kRampGroup; ++t) q[t] = side[t * kRampRecord + Q];
+    for (int i = 0; i < n; i += kRampGroup) {
+        const float4 *rec = side + i * kRampRecord;
+        float cc[kRampGroup], sc[kRampGroup];
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t)
+            cc[t] = __builtin_fmaf(q[t].x, x0, __builtin_fmaf(q[t].y, y, __builtin_fmaf(q[t].z, z, q[t].w)));
+        float4 cs[Q];
+#pragma unroll
+        for (int e = 0; e < Q; ++e) cs[e] = rec[e];
+        // the next group's phase inputs (this group's again after the last)
+        const float4 *nxt = i + kRampGroup < n ? rec + kRampGroup * kRampRecord : rec;
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) q[t] = nxt[t * kRampRecord + Q];
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) {
+            sc[t] = __builtin_amdgcn_sinf(cc[t]);
+            cc[t] = __builtin_amdgcn_cosf(cc[t]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) {
+            float4 cn[Q];
+            if (t + 1 < kRampGroup) {
+#pragma unroll
+                for (int e = 0; e < Q; ++e) cn[e] = rec[(t + 1) * kRampRecord + e];
+            }
+            float C[P], S[P];
+#pragma unroll
+            for (int e = 0; e < Q / 2; ++e) {
+                C[4 * e] = cs[e].x;
+                C[4 * e + 1] = cs[e].y;
+                C[4 * e + 2] = cs[e].z;
+                C[4 * e + 3] = cs[e].w;
+                S[4 * e] = cs[Q / 2 + e].x;
+                S[4 * e + 1] = cs[Q / 2 + e].y;
+                S[4 * e + 2] = cs[Q / 2 + e].z;
+                S[4 * e + 3] = cs[Q / 2 + e].w;
+            }
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                acc_r[j] = __builtin_fmaf(cc[t], C[j], acc_r[j]);
+                acc_i[j] = __builtin_fmaf(sc[t], C[j], acc_i[j]);
+                acc_r[P + j] = __builtin_fmaf(-sc[t], S[j], acc_r[P + j]);
+                acc_i[P + j] = __builtin_fmaf(cc[t], S[j], acc_i[P + j]);
+            }
+            if (t + 1 < kRampGroup) {
+#pragma unroll
+                for (int e = 0; e < Q; ++e) cs[e] = cn[e];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Streams chunks [c_begin, c_end) like stream_chunks(), and turns each stage
+// into sample records kSideSamples at a time: records written, LDS barrier,
+// accumulated by every lane, LDS barrier. The next stage's copy is issued
+// after the first round's records are written, so no barrier waits for it
+// before the stage's end.
+template <int V>
+__device__ __forceinline__ void ramp_one_step(const float4 *__restrict__ src, int c_begin, int c_end,
+                                              float4 (*stage)[kStageVec4], float4 *side, float x0,
+                                              float hdx, float y, float z, float (&acc_r)[V],
+                                              float (&acc_i)[V])
+{
+    const int nchunks = c_end > c_begin ? c_end - c_begin : 0;
+    src += (int64_t)c_begin * kChunkVec4;
+    const int64_t total_vec4 = (int64_t)nchunks * kChunkVec4;
+    const int nstages = (nchunks + kStageChunks - 1) / kStageChunks;
+    if (nstages > 0) issue_stage_load(src, total_vec4, 0, stage[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int st = 0; st < nstages; ++st) {
+        const int samples = min(kStageChunks, nchunks - st * kStageChunks) * kChunk;
+        const float4 *buf = stage[st & 1];
+        for (int r0 = 0; r0 < samples; r0 += kSideSamples) {
+            const int n = min(kSideSamples, samples - r0);
+            ramp_records<V>(buf, r0, n, hdx, side);
+            lds_barrier();
+            if (r0 == 0 && st + 1 < nstages) issue_stage_load(src, total_vec4, st + 1, stage[(st + 1) & 1]);
+            ramp_accumulate_records<V>(side, n, x0, y, z, acc_r, acc_i);
+            lds_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+}
+
+// Pair sums of the ramp path (acc[j] = sum_j, acc[V/2 + j] = dif_j) to the
+// voxels' sums: voxel V/2 + j gets sum_j + dif_j, voxel V/2 - 1 - j gets
+// sum_j - dif_j.
+template <int V>
+__device__ __forceinline__ void ramp_unfold(float (&acc_r)[V], float (&acc_i)[V])
+{
+    constexpr int P = V / 2;
+    float out_r[V], out_i[V];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        out_r[P + j] = acc_r[j] + acc_r[P + j];
+        out_i[P + j] = acc_i[j] + acc_i[P + j];
+        out_r[P - 1 - j] = acc_r[j] - acc_r[P + j];
+        out_i[P - 1 - j] = acc_i[j] - acc_i[P + j];
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        acc_r[v] = out_r[v];
+        acc_i[v] = out_i[v];
     }
 }
 
@@ -209,6 +412,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     float *__restrict__ out_r, float *__restrict__ out_i, int N)
 {
     __shared__ float4 stage[2][kStageVec4];
+    __shared__ float4 side[kSideSamples * kRampRecord];   // ramp path with one step per workgroup
+    __shared__ float wg_dx;
     const float4 *src = reinterpret_cast<const float4 *>(packed);
 
     // lane l of workgroup b owns voxels (b*kBlock + l)*V + v, v < V
@@ -247,16 +452,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         ramp = ramp && __builtin_fmaf((float)v, dx, px[0]) == px[v];
     // one decision per workgroup, so every branch's stage barriers are
     // reached by every wave of the workgroup
+    if (threadIdx.x == 0) wg_dx = dx;
     const bool all_ramp = __syncthreads_and(ramp);
     const bool shared = __syncthreads_and(same_yz);
+    // ...and whether all of its lanes step by the same dx (bitwise)
+    const bool one_step = all_ramp && __syncthreads_and(__float_as_uint(dx) == __float_as_uint(wg_dx));
 
     int c0, c1;
     split_range(nchunks, splits, blockIdx.y, &c0, &c1);
-    if (all_ramp)
-        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
-            accumulate_chunk_ramp<V>(ch, px[0], dx, py[0], pz[0], acc_r, acc_i);
-        });
-    else if (shared)
+    if (all_ramp) {
+        const float hdx = 0.5f * dx;
+        if (one_step) {
+            ramp_one_step<V>(src, c0, c1, stage, side, px[0], hdx, py[0], pz[0], acc_r, acc_i);
+        } else {
+            stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
+                accumulate_chunk_ramp<V>(ch, px[0], hdx, py[0], pz[0], acc_r, acc_i);
+            });
+        }
+        ramp_unfold<V>(acc_r, acc_i);
+    } else if (shared)
         stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
             accumulate_chunk<V, true>(ch, px, py, pz, acc_r, acc_i);
         });

@@ -76,6 +76,34 @@ __device__ __forceinline__ void load_chunk(const float4 *ch, float (&f)[kFields]
     }
 }
 
+// Issues stage `st` of a packed stream of `total_vec4` float4 (starting at
+// src) into `dst` with global_load_lds: each wave's 64 lanes copy 64
+// consecutive float4 straight into LDS at the wave's base (lane l at
+// base + l), with no registers in between. Complete once vmcnt reaches 0.
+__device__ __forceinline__ void issue_stage_load(const float4 *__restrict__ src, int64_t total_vec4,
+                                                 int st, float4 *dst)
+{
+    const int wave_base = threadIdx.x & ~63;
+    const int64_t first = (int64_t)st * kStageVec4;
+#pragma unroll
+    for (int k = 0; k < kStageLoads; ++k) {
+        const int i = k * kBlock + threadIdx.x;
+        if (i < kStageVec4 && first + i < total_vec4)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(src + first + i),
+                (__attribute__((address_space(3))) void *)(dst + k * kBlock + wave_base), 16, 0, 0);
+    }
+}
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads()
+// it does not wait for outstanding global loads (a stage copy in flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Streams chunks [c_begin, c_end) of `src` through the workgroup's LDS
 // stage buffers and calls body(chunks, count) for every STEP consecutive
 // chunks of a stage, in order, in every lane: `chunks` points at the first
@@ -93,30 +121,15 @@ __device__ __forceinline__ void stream_chunk_groups(const float4 *__restrict__ s
     src += (int64_t)c_begin * kChunkVec4;
     const int64_t total_vec4 = (int64_t)nchunks * kChunkVec4;
     const int nstages = (nchunks + kStageChunks - 1) / kStageChunks;
-    // Stage st's float4 i goes to stage[st & 1][i] by global_load_lds: each
-    // wave's 64 lanes copy 64 consecutive float4 straight into LDS at the
-    // wave's base (lane l at base + l), with no registers in between.
-    const int wave_base = threadIdx.x & ~63;
-    auto load_stage = [&](int st) {
-        float4 *dst = stage[st & 1];
-        const int64_t first = (int64_t)st * kStageVec4;
-#pragma unroll
-        for (int k = 0; k < kStageLoads; ++k) {
-            const int i = k * kBlock + threadIdx.x;
-            if (i < kStageVec4 && first + i < total_vec4)
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(src + first + i),
-                    (__attribute__((address_space(3))) void *)(dst + k * kBlock + wave_base), 16, 0, 0);
-        }
-    };
-    if (nstages > 0) load_stage(0);
+    // stage st goes to stage[st & 1]
+    if (nstages > 0) issue_stage_load(src, total_vec4, 0, stage[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int st = 0; st < nstages; ++st) {
         // the next stage streams into the other buffer (last read before the
         // previous barrier) while this one is worked on
-        if (st + 1 < nstages) load_stage(st + 1);
+        if (st + 1 < nstages) issue_stage_load(src, total_vec4, st + 1, stage[(st + 1) & 1]);
         const int chunks_here = min(kStageChunks, nchunks - st * kStageChunks);
         const float4 *buf = stage[st & 1];
         for (int c = 0; c < chunks_here; c += STEP) body(buf + c * kChunkVec4, min(STEP, chunks_here - c));

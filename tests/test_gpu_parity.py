@@ -218,7 +218,7 @@ def test_large_exact_phases_closed_form(dev):
 
 
 def test_ramp_shared_and_general_paths(dev):
-    """One grid, three voxel orders. x fastest: each lane's 8 voxels share y
+    """One grid, three voxel orders. x fastest: each lane's 16 voxels share y
     and z and are equally spaced in x (the ramp path). The same with voxels
     1 and 2 of every 8 swapped: y, z still shared, x no longer a ramp (the
     shared-phase path). z fastest: nothing shared (the general path). The
@@ -271,6 +271,46 @@ def test_ramp_path_nyquist_and_zero_steps(dev):
     rr, ri = gpu_fhd(w, dev)
     ref = oracle.fhd(kx, ky, kz, Dr, Di, x, y, z)
     check("ramp degenerate steps", rr, ri, *ref)
+
+
+def test_ramp_path_per_lane_steps(dev):
+    """Lanes whose 16 voxels are exact ramps, in two layouts of two
+    workgroups each. A: every lane steps by 1/128 (the ramp path with one
+    step per workgroup, half-step values formed once per sample in LDS).
+    B: the same voxels, except that one lane of the second workgroup steps
+    by 3/256, so that workgroup forms the half-step values per lane. Both
+    meet the oracle gate, and the second workgroup's other voxels agree
+    between A and B to rounding (the shared-step form folds the amplitude
+    and the centre offset into its sample records, one rounding each)."""
+    V, lanes = 16, 256
+    groups = 2 * lanes
+    rng = np.random.default_rng(31)
+    k = inputs.make_kspace("spiral32")
+    x0 = (rng.integers(-64, 44, groups) / 128.0).astype(np.float32)
+    yz = [np.repeat(rng.uniform(-0.5, 0.5, groups).astype(np.float32), V) for _ in range(2)]
+    steps = np.full(groups, 1.0 / 128, np.float32)
+    odd = lanes + 5
+    out = []
+    for layout in ("A", "B"):
+        st = steps.copy()
+        if layout == "B":
+            st[odd] = np.float32(3.0 / 256)
+        x = (x0[:, None] + np.arange(V, dtype=np.float32)[None, :] * st[:, None]).reshape(-1)
+        x = x.astype(np.float32)
+        # exact ramps: x0 + v step is a multiple of 1/256 below 1 in magnitude
+        assert np.array_equal(x, (x0[:, None].astype(np.float64) + np.arange(V)[None, :] * st[:, None].astype(np.float64)).reshape(-1))
+        rr, ri = gpu_fhd(dict(k, x=x, y=yz[0], z=yz[1]), dev)
+        ref = oracle.fhd(k["kx"], k["ky"], k["kz"], k["Dr"], k["Di"], x, yz[0], yz[1])
+        check("ramp steps, layout " + layout, rr, ri, *ref)
+        out.append((rr, ri))
+    keep = np.ones(groups * V, bool)
+    keep[:lanes * V] = False                      # first workgroup: one step in both
+    keep[odd * V:(odd + 1) * V] = False           # the lane that differs
+    a, b = out
+    diff = metrics.rel_l2(a[0][keep], a[1][keep], b[0][keep].astype(np.float64),
+                          b[1][keep].astype(np.float64))
+    print("shared-step vs per-lane form: rel diff %.2e" % diff)
+    assert 0 < diff < 2e-6
 
 
 def test_mixed_waves(dev):
