@@ -118,22 +118,22 @@ int split_count(int64_t blocks, int nchunks, int per_cu)
     const int64_t resident = (int64_t)per_cu * cus_cached[device];
     const int64_t stages = (nchunks + kStageChunks - 1) / kStageChunks;
     if (blocks <= 0 || stages <= 1) return 1;
-    if (blocks < resident) {
-        int64_t splits = resident / blocks;
-        if (splits > stages) splits = stages;
-        return splits < 1 ? 1 : (int)splits;
-    }
-    // Enough workgroups for one round: split only where it evens out the
-    // last, partly filled round (up to 4 ways, and only for a gain of more
-    // than a tenth).
-    auto fill = [&](int64_t s) {
-        const int64_t n = blocks * s, rounds = (n + resident - 1) / resident;
-        return (double)n / (double)(rounds * resident);
+    // Cutting the stream s ways makes every workgroup's work 1/s as long and
+    // the launch ceil(s blocks / resident) rounds of them: time ~ rounds / s,
+    // bounded below by blocks / resident. Take the fewest ways (at most one
+    // per stage, and at most 16 or two rounds' worth) that come within 3 %
+    // of the best.
+    auto cost = [&](int64_t s) {
+        return (double)((blocks * s + resident - 1) / resident) / (double)s;
     };
-    int best = 1;
-    for (int64_t s = 2; s <= 4 && s <= stages; ++s)
-        if (fill(s) > 1.1 * fill(best)) best = (int)s;
-    return best;
+    int64_t most = 2 * resident / blocks;
+    if (most < 16) most = 16;
+    if (most > stages) most = stages;
+    double lowest = cost(1);
+    for (int64_t s = 2; s <= most; ++s) lowest = cost(s) < lowest ? cost(s) : lowest;
+    for (int64_t s = 1; s <= most; ++s)
+        if (cost(s) <= 1.03 * lowest) return (int)s;
+    return 1;
 }
 
 namespace {

@@ -339,6 +339,12 @@ __device__ __forceinline__ void ramp_accumulate_records(const float4 *side, int 
             if (t + 1 < kRampGroup) {
 #pragma unroll
                 for (int e = 0; e < Q; ++e) cs[e] = cn[e];
+                // the next sample's reads go out after this sample's first
+                // FMAs (whose operands are then in), so waiting for them
+                // never waits for the reads just issued
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, Q, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4 * P - 2, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -401,12 +407,15 @@ __device__ __forceinline__ void ramp_unfold(float (&acc_r)[V], float (&acc_i)[V]
     }
 }
 
-// At least 4 waves per SIMD (<= 128 VGPRs): a 128^3 grid at 8 voxels per
-// lane is exactly 4 waves per SIMD, so all of them are resident at once.
-// Split s = blockIdx.y of `splits` takes its share of the sample stream and
-// writes rho (splits == 1) or its partial sums at out + s*N.
-template <int V>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void fhd_gather_kernel(
+// Two instances share the grid: ONE_STEP = true takes the workgroups whose
+// lanes are ramps with one common step (the ramp path with sample records,
+// at 5 waves per SIMD, <= 96 VGPRs) and ONE_STEP = false all others (at 4
+// waves per SIMD, <= 128 VGPRs); each instance's workgroups of the other
+// kind return after the test. Split s = blockIdx.y of `splits` takes its
+// share of the sample stream and writes rho (splits == 1) or its partial
+// sums at out + s*N.
+template <int V, bool ONE_STEP>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP ? 5 : 4))) void fhd_gather_kernel(
     const float *__restrict__ packed, int nchunks, int splits,
     const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
     float *__restrict__ out_r, float *__restrict__ out_i, int N)
@@ -458,17 +467,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     // ...and whether all of its lanes step by the same dx (bitwise)
     const bool one_step = all_ramp && __syncthreads_and(__float_as_uint(dx) == __float_as_uint(wg_dx));
 
+    if (one_step != ONE_STEP) return;   // the other instance's workgroup
+
     int c0, c1;
     split_range(nchunks, splits, blockIdx.y, &c0, &c1);
-    if (all_ramp) {
+    if constexpr (ONE_STEP) {
+        ramp_one_step<V>(src, c0, c1, stage, side, px[0], 0.5f * dx, py[0], pz[0], acc_r, acc_i);
+        ramp_unfold<V>(acc_r, acc_i);
+    } else if (all_ramp) {
         const float hdx = 0.5f * dx;
-        if (one_step) {
-            ramp_one_step<V>(src, c0, c1, stage, side, px[0], hdx, py[0], pz[0], acc_r, acc_i);
-        } else {
-            stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
-                accumulate_chunk_ramp<V>(ch, px[0], hdx, py[0], pz[0], acc_r, acc_i);
-            });
-        }
+        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
+            accumulate_chunk_ramp<V>(ch, px[0], hdx, py[0], pz[0], acc_r, acc_i);
+        });
         ramp_unfold<V>(acc_r, acc_i);
     } else if (shared)
         stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
@@ -504,6 +514,24 @@ int launch_pack(const float *kx, const float *ky, const float *kz, const float *
     return launch_status("fhd_pack_kernel launch");
 }
 
+// Workgroups of fhd_gather_kernel<kVox, true> that fit on one CU at once
+// (register and LDS budget), asked of the runtime once per device.
+int one_step_blocks_per_cu()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 4;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, reinterpret_cast<const void *>(fhd_gather_kernel<kVox, true>), kBlock, 0) != hipSuccess ||
+            n < 1)
+            n = 4;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
                   float *rho_r, float *rho_i, int N, hipStream_t stream)
 {
@@ -511,27 +539,34 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
     const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
     const int64_t per_block = (int64_t)kBlock * kVox;
     const int64_t blocks = ((int64_t)N + per_block - 1) / per_block;
-    const int splits = split_count(blocks, nchunks);
-    if (splits == 1) {
-        fhd_gather_kernel<kVox><<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
-            packed, nchunks, 1, x, y, z, rho_r, rho_i, N);
-        return launch_status("fhd_gather_kernel launch");
+    // sized for the one-step instance, the one that runs at length on grids
+    const int splits = split_count(blocks, nchunks, one_step_blocks_per_cu());
+    float *part = nullptr, *part_r = rho_r, *part_i = rho_i;
+    if (splits > 1) {
+        const hipError_t e = hipMallocAsync((void **)&part, (size_t)splits * 2 * N * sizeof(float), stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (split partials): ") +
+                                           hipGetErrorString(e));
+        }
+        part_r = part;
+        part_i = part + (int64_t)splits * N;
     }
-    float *part = nullptr;
-    const hipError_t e = hipMallocAsync((void **)&part, (size_t)splits * 2 * N * sizeof(float), stream);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (split partials): ") +
-                                       hipGetErrorString(e));
+    const dim3 grid((unsigned)blocks, (unsigned)splits);
+    fhd_gather_kernel<kVox, true><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, x, y, z,
+                                                                      part_r, part_i, N);
+    int rc = launch_status("fhd_gather_kernel<one step> launch");
+    if (rc == FHD_OK) {
+        fhd_gather_kernel<kVox, false><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, x, y,
+                                                                           z, part_r, part_i, N);
+        rc = launch_status("fhd_gather_kernel launch");
     }
-    float *part_r = part, *part_i = part + (int64_t)splits * N;
-    fhd_gather_kernel<kVox><<<dim3((unsigned)blocks, (unsigned)splits), dim3(kBlock), 0, stream>>>(
-        packed, nchunks, splits, x, y, z, part_r, part_i, N);
-    int rc = launch_status("fhd_gather_kernel launch");
-    if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, N, rho_r, rho_i, stream);
-    const hipError_t f = hipFreeAsync(part, stream);
-    if (f != hipSuccess && rc == FHD_OK)
-        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
+    if (splits > 1) {
+        if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, N, rho_r, rho_i, stream);
+        const hipError_t f = hipFreeAsync(part, stream);
+        if (f != hipSuccess && rc == FHD_OK)
+            rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
+    }
     return rc;
 }
 

@@ -163,6 +163,14 @@ __global__ __launch_bounds__(kBlock) void form_kernel(float *__restrict__ out,
                 asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a2) : "v"(y), "v"(x));
                 asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a3) : "v"(y), "v"(x));
                 asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a4) : "v"(y), "v"(x));
+            } else if constexpr (F == 10) {   // v_fmac_f32 with a DPP row broadcast of src0
+#define FHDMB_I(i) asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:5 row_mask:0xf bank_mask:0xf" : "+v"(a##i) : "v"(y), "v"(x));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 11) {   // v_mov_b32 with a DPP row broadcast
+#define FHDMB_I(i) asm volatile("v_mov_b32_dpp %0, %1 row_newbcast:5 row_mask:0xf bank_mask:0xf" : "=v"(t##i) : "v"(a##i));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
             } else if constexpr (F == 9) {   // gather mix with SGPR operands
                 asm volatile("v_sin_f32_e32 %0, %1" : "+v"(t0) : "v"(x));
                 asm volatile("v_cos_f32_e32 %0, %1" : "+v"(t1) : "v"(x));
@@ -198,6 +206,7 @@ const FormEntry kForms[] = {
     {"fma_vop3_sgpr", 8, form_kernel<4>}, {"fmamk_literal", 8, form_kernel<5>},
     {"fract", 8, form_kernel<6>}, {"sin", 8, form_kernel<7>},
     {"mix_2trans_5fma_vgpr", 7, form_kernel<8>}, {"mix_2trans_5fma_sgpr", 7, form_kernel<9>},
+    {"fmac_vop2_dpp_row_bcast", 8, form_kernel<10>}, {"mov_dpp_row_bcast", 8, form_kernel<11>},
 };
 
 }  // namespace
