@@ -277,14 +277,15 @@ __device__ __forceinline__ void ramp_records(const float4 *buf, int r0, int n, f
 // Accumulates records [0, n) of `side` (n a multiple of kRampGroup) into
 // the pair sums (acc[j] = sum_j, acc[V/2 + j] = dif_j). The LDS reads run
 // ahead of their use: a group's phase inputs during the previous group's
-// FMAs, a sample's C and S during the previous sample's FMAs (the first
-// sample's during the transcendentals).
+// last sample's FMAs, a sample's C and S during the previous sample's FMAs
+// (the first sample's during the transcendentals).
 template <int V>
 __device__ __forceinline__ void ramp_accumulate_records(const float4 *side, int n, float x0, float y,
                                                         float z, float (&acc_r)[V], float (&acc_i)[V])
 {
     constexpr int P = V / 2;
     constexpr int Q = P / 2;   // float4 of C and S per record
+    static_assert(Q == kRampGroup, "a sample's C and S and a group's phase inputs are equally many reads");
     float4 q[kRampGroup];
 #pragma unroll
     for (int t = 0; t < kRampGroup; ++t) q[t] = side[t * kRampRecord + Q];
@@ -299,8 +300,6 @@ __device__ __forceinline__ void ramp_accumulate_records(const float4 *side, int 
         for (int e = 0; e < Q; ++e) cs[e] = rec[e];
         // the next group's phase inputs (this group's again after the last)
         const float4 *nxt = i + kRampGroup < n ? rec + kRampGroup * kRampRecord : rec;
-#pragma unroll
-        for (int t = 0; t < kRampGroup; ++t) q[t] = nxt[t * kRampRecord + Q];
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -312,10 +311,16 @@ __device__ __forceinline__ void ramp_accumulate_records(const float4 *side, int 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < kRampGroup; ++t) {
+            // the next sample's C and S, or during the group's last sample
+            // (in the registers C and S would take) the next group's phase
+            // inputs
             float4 cn[Q];
             if (t + 1 < kRampGroup) {
 #pragma unroll
                 for (int e = 0; e < Q; ++e) cn[e] = rec[(t + 1) * kRampRecord + e];
+            } else {
+#pragma unroll
+                for (int u = 0; u < kRampGroup; ++u) q[u] = nxt[u * kRampRecord + Q];
             }
             float C[P], S[P];
 #pragma unroll
@@ -339,13 +344,13 @@ __device__ __forceinline__ void ramp_accumulate_records(const float4 *side, int 
             if (t + 1 < kRampGroup) {
 #pragma unroll
                 for (int e = 0; e < Q; ++e) cs[e] = cn[e];
-                // the next sample's reads go out after this sample's first
-                // FMAs (whose operands are then in), so waiting for them
-                // never waits for the reads just issued
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, Q, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4 * P - 2, 0);
             }
+            // the reads go out after this sample's first FMAs (whose
+            // operands are then in), so waiting for them never waits for
+            // the reads just issued
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, Q, 0);   // Q == kRampGroup reads either way
+            __builtin_amdgcn_sched_group_barrier(0x002, 4 * P - 2, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }

@@ -77,26 +77,35 @@ __device__ __forceinline__ void load_chunk(const float4 *ch, float (&f)[kFields]
 }
 
 // Issues stage `st` of a packed stream of `total_vec4` float4 (starting at
-// src) into `dst` with global_load_lds: each wave's 64 lanes copy 64
+// src) into `dst` with buffer_load ... lds: each wave's 64 lanes copy 64
 // consecutive float4 straight into LDS at the wave's base (lane l at
-// base + l), with no registers in between. Complete once vmcnt reaches 0.
+// base + l), with no registers in between. The buffer descriptor (SGPRs)
+// starts at the stage and ends at the stream's end or the stage's, so a
+// lane's offset is the same 32-bit value at every stage and reads past the
+// end return zeros. Complete once vmcnt reaches 0.
 __device__ __forceinline__ void issue_stage_load(const float4 *__restrict__ src, int64_t total_vec4,
                                                  int st, float4 *dst)
 {
     const int wave_base = threadIdx.x & ~63;
     const int64_t first = (int64_t)st * kStageVec4;
+    const int64_t left = total_vec4 - first;
+    const int bytes = (int)(left < kStageVec4 ? left : kStageVec4) * 16;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(src + first), (short)0, bytes, 0x00020000);
 #pragma unroll
     for (int k = 0; k < kStageLoads; ++k) {
         const int i = k * kBlock + threadIdx.x;
-        if (i < kStageVec4 && first + i < total_vec4)
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(src + first + i),
-                (__attribute__((address_space(3))) void *)(dst + k * kBlock + wave_base), 16, 0, 0);
+        if (i < kStageVec4)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void *)(dst + k * kBlock + wave_base), 16,
+                (unsigned)i * 16u, 0, 0, 0);
     }
 }
 
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads()
-// it does not wait for outstanding global loads (a stage copy in flight).
+// it does not wait for outstanding global loads into registers. (A stage
+// copy by global_load_lds writes LDS, so the compiler still waits for it
+// here: issue one where that wait costs little.)
 __device__ __forceinline__ void lds_barrier()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
