@@ -90,6 +90,7 @@ def issue_terms(valu: float, trans: float) -> float:
 
 
 ROOF_TERMS_RAMP = issue_terms(35.0 / 16, 2.0 / 16)
+ROOF_TERMS_RAMP_LANE = issue_terms(55.0 / 16, 4.0 / 16)
 ROOF_TERMS_RAMP_F = issue_terms(36.0 / 8, 4.0 / 8)
 
 
@@ -104,64 +105,76 @@ def roof_terms(parts) -> float:
 def _lane_ramps(x, y, z, vox: int = 8):
     """Per group of `vox` consecutive voxels (the last partial group
     dropped): do they share y and z bitwise and sit at x_0 + v (x_1 - x_0)
-    rounded once to fp32 -- the gathers' ramp test."""
+    rounded once to fp32 -- the gathers' ramp test -- and that step."""
     x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
     full = x.size // vox * vox
     lanes = full // vox
     if lanes == 0:
-        return np.zeros(0, bool)
+        return np.zeros(0, bool), np.zeros(0, np.float32)
     X, Y, Z = (a[:full].reshape(lanes, vox) for a in (x, y, z))
     same = (np.all(Y.view(np.uint32) == Y[:, :1].view(np.uint32), axis=1)
             & np.all(Z.view(np.uint32) == Z[:, :1].view(np.uint32), axis=1))
     dx = (X[:, 1] - X[:, 0]).astype(np.float32)
     v = np.arange(vox, dtype=np.float64)
     ramp_x = (X[:, :1].astype(np.float64) + v * dx[:, None].astype(np.float64)).astype(np.float32)
-    return same & np.isfinite(dx) & np.all(ramp_x == X, axis=1)
+    return same & np.isfinite(dx) & np.all(ramp_x == X, axis=1), dx
 
 
 def ramp_chunk_fraction(x, y, z, vox: int = 8) -> float:
     """Fraction of voxels that F's pre-pass writes as ramp chunks."""
     n = np.asarray(x).size
-    return float(np.sum(_lane_ramps(x, y, z, vox)) * vox / n) if n else 0.0
+    return float(np.sum(_lane_ramps(x, y, z, vox)[0]) * vox / n) if n else 0.0
 
 
-def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 8) -> float:
-    """Fraction of voxels whose F^H D gather workgroup takes the ramp path,
+def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 8) -> tuple[float, float]:
+    """Fractions of voxels whose F^H D gather workgroup takes the ramp path,
     by the kernel's own test: every lane's `vox` voxels form a ramp (see
-    _lane_ramps) and the workgroup's lanes all exist."""
+    _lane_ramps) and the workgroup's lanes all exist. Returned as (one
+    step: every lane of the workgroup has the same x step bitwise, per-lane
+    steps: the other ramp workgroups)."""
     N = np.asarray(x).size
-    lane_ok = _lane_ramps(x, y, z, vox)
+    lane_ok, dx = _lane_ramps(x, y, z, vox)
     lanes = lane_ok.size
     if lanes == 0:
-        return 0.0
+        return 0.0, 0.0
     per_block = block
     blocks = (lanes + per_block - 1) // per_block
     ok = np.zeros(blocks * per_block, bool)
     ok[:lanes] = lane_ok
+    steps = np.zeros(blocks * per_block, np.float32)
+    steps[:lanes] = dx
     # lanes past N (a partial last workgroup) stay False: such a
     # workgroup never qualifies
     block_ok = ok.reshape(blocks, per_block).all(axis=1)
+    S = steps.view(np.uint32).reshape(blocks, per_block)
+    one = block_ok & np.all(S == S[:, :1], axis=1)
     voxels = np.minimum(block * vox, N - np.arange(blocks) * block * vox)
-    return float(np.sum(voxels[block_ok]) / N)
+    return float(np.sum(voxels[one]) / N), float(np.sum(voxels[block_ok & ~one]) / N)
+
+
+def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 8) -> float:
+    """Fraction of voxels on the ramp path, either form."""
+    return sum(ramp_voxel_fractions(x, y, z, block, vox))
+
 
 # HBM bytes per launch of each operator's dominant kernel at 128^3 x 100k,
 # from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by a 1 GiB copy's
 # readings (factors 2.0 and 1.0). Valid only for the sources they were taken
 # on (SHA-256 over the listed files, in order); any later edit reports null
 # until the counters are taken again.
-#   fhd  (fhd_gather_kernel): 59.4 MiB read (x, y, z by each of the 2
-#        sample splits, the packed samples once per XCD L2) + 47.0 MiB
-#        written (2 split partial sums of rho, register spills)
+#   fhd  (fhd_gather_kernel<16, true>): 108.2 MiB read (x, y, z by each of
+#        the 5 sample splits, the packed samples once per XCD L2, a few
+#        spilled registers) + 92.5 MiB written (5 split partial sums of rho)
 #   grid (fhd_grid_kernel):   15.4 MiB read (packed samples once per XCD L2)
 #        + 48.0 MiB written (3 split partial sums of rho)
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
     "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
-            "sha256": "85f059516c247b3ccb1226b0ea0af3ebf7ab6475775f3761b374346bf3f4c6a8",
-            "bytes_per_launch": (30399.5 * 2.0 + 48128 * 1.0) * 1024},
+            "sha256": "c3544d9a046c2646323e6a51543a1578e517cf0cfb0dee608f419bf8dfb91c43",
+            "bytes_per_launch": (55374.0 * 2.0 + 94720 * 1.0) * 1024},
     "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
-             "sha256": "ac3393f12420e92aabc5ef9ed72d6fbe3b3f19558e764a1c3d67733a2c57d476",
-             "bytes_per_launch": (7892.0 * 2.0 + 49152 * 1.0) * 1024},
+             "sha256": "3cb2fe5084067543b1ff691ab4411b30773a609f83b0dbb3710a77f0fa69fa14",
+             "bytes_per_launch": (7876.0 * 2.0 + 49152 * 1.0) * 1024},
 }
 
 
@@ -286,8 +299,9 @@ def main(argv=None) -> int:
 
     # the ceiling for the paths this voxel layout takes (the x-fastest
     # grids of the workloads: the ramp path throughout)
-    ramp = ramp_voxel_fraction(w["x"], w["y"], w["z"], cfg["block_threads"], cfg["voxels_per_lane"])
-    roof = roof_terms([(terms * ramp, ROOF_TERMS_RAMP), (terms * (1 - ramp), ROOF_TERMS)])
+    one, lane = ramp_voxel_fractions(w["x"], w["y"], w["z"], cfg["block_threads"], cfg["voxels_per_lane"])
+    roof = roof_terms([(terms * one, ROOF_TERMS_RAMP), (terms * lane, ROOF_TERMS_RAMP_LANE),
+                       (terms * (1 - one - lane), ROOF_TERMS)])
     achieved = FLOP_PER_TERM * terms / (gather_ms * 1e-3) / 1e12
     peak = FLOP_PER_TERM * roof / 1e12
     out = {
@@ -306,7 +320,7 @@ def main(argv=None) -> int:
         "config": {
             "workload": "%s: F^H D over %d^3 voxels x %d samples (%s)"
                         % (args.workload, w["L"], M, inputs.WORKLOADS[args.workload].trajectory),
-            "N": N, "M": M, "terms": terms, "ramp_path_voxel_fraction": ramp, **cfg,
+            "N": N, "M": M, "terms": terms, "ramp_path_voxel_fraction": one + lane, "one_step_voxel_fraction": one, **cfg,
         },
         "roofline": {
             "bound": "alu",
@@ -489,12 +503,13 @@ def bench_other(args) -> int:
     # ceiling: F^H terms at the adjoint gather's path mix, F terms direct
     NM = float(N) * M
     gcfg = binding.gather_config()
-    ramp = ramp_voxel_fraction(w["x"], w["y"], w["z"], gcfg["block_threads"], gcfg["voxels_per_lane"])
+    one, lane = ramp_voxel_fractions(w["x"], w["y"], w["z"], gcfg["block_threads"], gcfg["voxels_per_lane"])
     ramp_f = ramp_chunk_fraction(w["x"], w["y"], w["z"])
     adjoint = {"normal": 1, "cg": 1 + k_iters}.get(args.op, 0)
     forward_terms = {"forward": 1, "normal": 1, "cg": k_iters}.get(args.op, 0)
-    roof = roof_terms([(adjoint * NM * ramp, ROOF_TERMS_RAMP),
-                       (adjoint * NM * (1 - ramp), ROOF_TERMS),
+    roof = roof_terms([(adjoint * NM * one, ROOF_TERMS_RAMP),
+                       (adjoint * NM * lane, ROOF_TERMS_RAMP_LANE),
+                       (adjoint * NM * (1 - one - lane), ROOF_TERMS),
                        (forward_terms * NM * ramp_f, ROOF_TERMS_RAMP_F),
                        (forward_terms * NM * (1 - ramp_f), ROOF_TERMS)])
     out = {

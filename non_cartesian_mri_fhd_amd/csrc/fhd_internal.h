@@ -15,7 +15,7 @@
 //  * stream_chunks() walks a packed stream through LDS in stages of
 //    kStageChunks chunks, double buffered: while a workgroup works on one
 //    stage, the next one is copied straight from memory into the other
-//    buffer (global_load_lds, no registers held), completed before the
+//    buffer (buffer_load ... lds, no registers held), completed before the
 //    stage barrier. Every lane
 //    then reads each chunk with same-address ds_read_b128, which the LDS
 //    broadcasts, so the stream's values reach the FMAs in VGPRs (on gfx950
@@ -104,7 +104,7 @@ __device__ __forceinline__ void issue_stage_load(const float4 *__restrict__ src,
 
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads()
 // it does not wait for outstanding global loads into registers. (A stage
-// copy by global_load_lds writes LDS, so the compiler still waits for it
+// copy into LDS counts as an LDS write, so the compiler still waits for it
 // here: issue one where that wait costs little.)
 __device__ __forceinline__ void lds_barrier()
 {

@@ -49,6 +49,24 @@ def test_ramp_fraction_mirrors_the_kernel_test():
     assert bench.ramp_voxel_fraction(x[:m], y[:m], z[:m]) == (L ** 3 - 2048) / m
 
 
+def test_ramp_fractions_split_by_step():
+    """A workgroup whose lanes are ramps with different x steps counts as
+    per-lane steps; workgroups sharing one step count as one step."""
+    vox, block = 16, 256
+    lanes = 2 * block
+    rng = np.random.default_rng(3)
+    x0 = (rng.integers(-64, 44, lanes) / 128.0).astype(np.float32)
+    steps = np.full(lanes, 1.0 / 128, np.float32)
+    steps[block + 7] = np.float32(3.0 / 256)
+    x = (x0[:, None] + np.arange(vox, dtype=np.float32)[None, :] * steps[:, None]).reshape(-1)
+    y, z = (np.repeat(rng.uniform(-0.5, 0.5, lanes).astype(np.float32), vox) for _ in range(2))
+    assert bench.ramp_voxel_fractions(x, y, z, block, vox) == (0.5, 0.5)
+    assert bench.ramp_voxel_fraction(x, y, z, block, vox) == 1.0
+    steps[block + 7] = np.float32(1.0 / 128)
+    x = (x0[:, None] + np.arange(vox, dtype=np.float32)[None, :] * steps[:, None]).reshape(-1)
+    assert bench.ramp_voxel_fractions(x, y, z, block, vox) == (1.0, 0.0)
+
+
 def test_roof_terms_mixes_paths():
     r_direct, r_ramp = bench.ROOF_TERMS, bench.ROOF_TERMS_RAMP
     assert bench.roof_terms([(1.0, r_direct)]) == r_direct
@@ -62,7 +80,7 @@ def test_issue_ceilings():
     # transcendentals only: the measured transcendental issue rate
     assert abs(bench.issue_terms(0.0, 1.0) - bench.P_TRANS) / bench.P_TRANS < 1e-12
     # the ramp paths' ceilings lie above the direct-form R
-    assert bench.ROOF_TERMS_RAMP > bench.ROOF_TERMS_RAMP_F > bench.ROOF_TERMS
+    assert bench.ROOF_TERMS_RAMP > bench.ROOF_TERMS_RAMP_LANE > bench.ROOF_TERMS_RAMP_F > bench.ROOF_TERMS
 
 
 
