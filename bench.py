@@ -67,7 +67,10 @@ METRIC = "F^H D voxel-sample terms/s at 128^3 x 100k; % of FP32 VALU/trans roofl
 #     55 VALU and 4 transcendentals, 1.77e13);
 #   F's ramp chunks (Horner): per sample and chunk of 8 voxels 4
 #     transcendentals and 36 VALU (phase 3, step 1, Horner 28, finish 4):
-#     13 clk per wave-term, 1.21e13 terms/s.
+#     13 clk per wave-term, 1.21e13 terms/s; F's 16-voxel ramps (voxel
+#     pairs about the centre, a chunk pair): per sample 4 transcendentals
+#     and 57 VALU (phase 5, 2 cos(2 pi d) 2, recurrence 14, pair sums 32,
+#     finish 4) for 16 terms: 9.1 clk per wave-term, 1.73e13 terms/s.
 CUS, SIMDS_PER_CU, TRANS_LANES_PER_CYCLE, CLOCK_HZ = 256, 4, 8, 2.4e9
 P_FP32 = 157.3e12
 P_TRANS = CUS * SIMDS_PER_CU * TRANS_LANES_PER_CYCLE * CLOCK_HZ
@@ -92,6 +95,7 @@ def issue_terms(valu: float, trans: float) -> float:
 ROOF_TERMS_RAMP = issue_terms(35.0 / 16, 2.0 / 16)
 ROOF_TERMS_RAMP_LANE = issue_terms(55.0 / 16, 4.0 / 16)
 ROOF_TERMS_RAMP_F = issue_terms(36.0 / 8, 4.0 / 8)
+ROOF_TERMS_RAMP_F16 = issue_terms(57.0 / 16, 4.0 / 16)
 
 
 def roof_terms(parts) -> float:
@@ -121,9 +125,23 @@ def _lane_ramps(x, y, z, vox: int = 8):
 
 
 def ramp_chunk_fraction(x, y, z, vox: int = 8) -> float:
-    """Fraction of voxels that F's pre-pass writes as ramp chunks."""
+    """Fraction of voxels that F's pre-pass writes as ramp chunks of `vox`."""
     n = np.asarray(x).size
     return float(np.sum(_lane_ramps(x, y, z, vox)[0]) * vox / n) if n else 0.0
+
+
+def ramp_chunk_fractions(x, y, z) -> tuple[float, float]:
+    """Fractions of voxels that F's pre-pass writes as 16-voxel ramps (chunk
+    pairs) and as 8-voxel ramp chunks (the other chunks)."""
+    n = np.asarray(x).size
+    if n == 0:
+        return 0.0, 0.0
+    ok16 = _lane_ramps(x, y, z, 16)[0]
+    ok8 = _lane_ramps(x, y, z, 8)[0]
+    both8 = ok8[:2 * ok16.size].reshape(-1, 2)
+    # chunks of a 16-voxel ramp are 8-voxel ramps too: count them once
+    single = int(np.sum(ok8)) - 2 * int(np.sum(ok16 & both8.all(axis=1)))
+    return float(np.sum(ok16) * 16 / n), float(single * 8 / n)
 
 
 def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 8) -> tuple[float, float]:
@@ -504,14 +522,15 @@ def bench_other(args) -> int:
     NM = float(N) * M
     gcfg = binding.gather_config()
     one, lane = ramp_voxel_fractions(w["x"], w["y"], w["z"], gcfg["block_threads"], gcfg["voxels_per_lane"])
-    ramp_f = ramp_chunk_fraction(w["x"], w["y"], w["z"])
+    ramp_f16, ramp_f = ramp_chunk_fractions(w["x"], w["y"], w["z"])
     adjoint = {"normal": 1, "cg": 1 + k_iters}.get(args.op, 0)
     forward_terms = {"forward": 1, "normal": 1, "cg": k_iters}.get(args.op, 0)
     roof = roof_terms([(adjoint * NM * one, ROOF_TERMS_RAMP),
                        (adjoint * NM * lane, ROOF_TERMS_RAMP_LANE),
                        (adjoint * NM * (1 - one - lane), ROOF_TERMS),
+                       (forward_terms * NM * ramp_f16, ROOF_TERMS_RAMP_F16),
                        (forward_terms * NM * ramp_f, ROOF_TERMS_RAMP_F),
-                       (forward_terms * NM * (1 - ramp_f), ROOF_TERMS)])
+                       (forward_terms * NM * (1 - ramp_f16 - ramp_f), ROOF_TERMS)])
     out = {
         "metric": "%s voxel-sample terms/s (%s)" % (args.op, args.workload),
         "value": value, "unit": "terms/s", "n_gpus": 1, "steps": args.steps,

@@ -10,22 +10,30 @@
 //
 //  * fhd_forward_pack_kernel -- per-voxel pre-pass. Writes each voxel as the
 //    record (x, y, z, s, a) with a = |rho| and s = -arg(rho) / (2 pi), so
-//    that rho e^{-i 2 pi k.x} = a e^{-i 2 pi (k.x + s)}. A chunk of 8
-//    voxels that share y and z and sit at x0 + u dx (checked exactly; every
-//    chunk of an x-fastest grid) is written as a ramp chunk instead:
-//    Re rho_u, -Im rho_u, then (x0, dx, y, z), marked by -1 in the last
-//    slot of the amplitude field (amplitudes are never negative).
+//    that rho e^{-i 2 pi k.x} = a e^{-i 2 pi (k.x + s)}. Voxels on a line
+//    in x at equal steps (checked exactly; every x-fastest grid) are
+//    written instead as
+//      - a 16-voxel ramp, when both chunks of an aligned chunk pair are one
+//        ramp: the first chunk holds, for the voxel pairs 8 + j and 7 - j
+//        about the centre, A_j = c_{8+j} + c_{7-j} and B_j = c_{8+j} - c_{7-j}
+//        (c = conj(rho)) and (x0, dx/2, y, z), marked by -2 in the last
+//        slot of the amplitude field; the second chunk holds zeros and -3;
+//      - else an 8-voxel ramp chunk: Re rho_u, -Im rho_u, then
+//        (x0, dx, y, z), marked by -1 (amplitudes are never negative).
 //
 //  * fhd_forward_gather_kernel -- one lane per kSamp consecutive samples,
-//    no atomics; every lane walks the same voxel stream through LDS
-//    (stream_chunks) and accumulates conj(D). Per term of a general chunk:
-//    p = kx x + ky y + kz z + s (3 FMA; 2 + 1/kSamp when all of a lane's
-//    samples share kz, as within a plane of a stack of spirals -- bitwise
-//    identical), v_cos_f32, v_sin_f32, 2 FMA. A ramp chunk is a polynomial
-//    in z = e^{i 2 pi kx dx}: sum_u conj(rho_u) e^{i 2 pi k.x_u} =
-//    e^{i 2 pi k.x_0} sum_u conj(rho_u) z^u, evaluated by Horner's rule
-//    (4 FMA per voxel) after 4 transcendentals per sample and chunk. The
-//    accumulated imaginary part is negated once at the end (exact).
+//    no atomics; every lane walks the same voxel stream through LDS, a
+//    chunk pair at a time, and accumulates conj(D). Per term of a general
+//    chunk: p = kx x + ky y + kz z + s (3 FMA; 2 + 1/kSamp when all of a
+//    lane's samples share kz, as within a plane of a stack of spirals --
+//    bitwise identical), v_cos_f32, v_sin_f32, 2 FMA. A 16-voxel ramp is
+//    e^{i 2 pi k.x_c} sum_j (A_j C_j + i B_j S_j) with the real factors
+//    C_j, S_j = cos, sin(2 pi (j + 1/2) kx dx) from a three-term recurrence:
+//    4 transcendentals and 57 other VALU instructions per sample for 16
+//    terms. An 8-voxel ramp chunk is a polynomial in z = e^{i 2 pi kx dx},
+//    e^{i 2 pi k.x_0} sum_u conj(rho_u) z^u, by Horner's rule (4 FMA per
+//    voxel) after 4 transcendentals per sample. The accumulated imaginary
+//    part is negated once at the end (exact).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -58,17 +66,43 @@ __global__ __launch_bounds__(kPackBlock) void fhd_forward_pack_kernel(
         re = rho_r[n];
         im = rho_i[n];
     }
-    const int lane = threadIdx.x & 63, base = lane & ~(kChunk - 1), u = lane & (kChunk - 1);
-    const float x0 = __shfl(fx, base), x1 = __shfl(fx, base + 1);
-    const float y0 = __shfl(fy, base), z0 = __shfl(fz, base);
+    const int lane = threadIdx.x & 63;
+    // 16-voxel ramps: chunk pairs (2c, 2c + 1), 16 lanes of one wave
+    const int base16 = lane & ~(2 * kChunk - 1), w = lane & (2 * kChunk - 1);
+    const float x0 = __shfl(fx, base16), x1 = __shfl(fx, base16 + 1);
+    const float y0 = __shfl(fy, base16), z0 = __shfl(fz, base16);
     const float dx = x1 - x0;
-    const bool mine = live && __float_as_uint(fy) == __float_as_uint(y0) &&
-                      __float_as_uint(fz) == __float_as_uint(z0) && __builtin_isfinite(dx) &&
-                      __builtin_fmaf((float)u, dx, x0) == fx;
+    const bool same = live && __float_as_uint(fy) == __float_as_uint(y0) &&
+                      __float_as_uint(fz) == __float_as_uint(z0) && __builtin_isfinite(dx);
+    const bool mine16 = same && __builtin_fmaf((float)w, dx, x0) == fx;
+    const bool ramp16 = ((__ballot(mine16) >> base16) & 0xffffull) == 0xffffull;
+    // 8-voxel ramps: single chunks
+    const int base = lane & ~(kChunk - 1), u = lane & (kChunk - 1);
+    const float x0c = __shfl(fx, base), x1c = __shfl(fx, base + 1);
+    const float y0c = __shfl(fy, base), z0c = __shfl(fz, base);
+    const float dxc = x1c - x0c;
+    const bool mine = live && __float_as_uint(fy) == __float_as_uint(y0c) &&
+                      __float_as_uint(fz) == __float_as_uint(z0c) && __builtin_isfinite(dxc) &&
+                      __builtin_fmaf((float)u, dxc, x0c) == fx;
     const bool ramp = ((__ballot(mine) >> base) & 0xffull) == 0xffull;
+    // pair sums of conj(rho) about the 16-voxel centre: slot j < 8 of the
+    // pair's first chunk gets A_j = c_{8+j} + c_{7-j}, B_j = c_{8+j} - c_{7-j}
+    const float hr = __shfl(re, base16 + kChunk + (w & (kChunk - 1)));
+    const float hi = -__shfl(im, base16 + kChunk + (w & (kChunk - 1)));
+    const float lr = __shfl(re, base16 + kChunk - 1 - (w & (kChunk - 1)));
+    const float li = -__shfl(im, base16 + kChunk - 1 - (w & (kChunk - 1)));
     if (n >= N_pad) return;
-    if (ramp) {
-        const float geo = u == 0 ? x0 : u == 1 ? dx : u == 2 ? y0 : u == 3 ? z0 : 0.0f;
+    if (ramp16) {
+        if (w < kChunk) {
+            const float geo = w == 0 ? x0 : w == 1 ? 0.5f * dx : w == 2 ? y0 : w == 3 ? z0 : 0.0f;
+            store_record(packed, n, hr + lr, hi + li, hr - lr, hi - li, w == kChunk - 1 ? -2.0f : geo);
+        } else {
+            // the pair's second chunk carries nothing: zero amplitudes and a
+            // marker, so that it adds 0 however it is read
+            store_record(packed, n, 0.0f, 0.0f, 0.0f, 0.0f, w == 2 * kChunk - 1 ? -3.0f : 0.0f);
+        }
+    } else if (ramp) {
+        const float geo = u == 0 ? x0c : u == 1 ? dxc : u == 2 ? y0c : u == 3 ? z0c : 0.0f;
         store_record(packed, n, re, -im, geo, 0.0f, u == kChunk - 1 ? -1.0f : 0.0f);
     } else {
         float s = 0.0f, amp = 0.0f;
@@ -125,6 +159,75 @@ __device__ __forceinline__ void accumulate_ramp_chunk(const float (&f)[kFields][
             }
             acc_r[j] = __builtin_fmaf(er[t], hr, __builtin_fmaf(-ei[t], hi, acc_r[j]));
             acc_i[j] = __builtin_fmaf(er[t], hi, __builtin_fmaf(ei[t], hr, acc_i[j]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// A 16-voxel ramp (a chunk pair): with c_u = conj(rho_u), centre
+// x_c = x_0 + 7.5 dx, h = kx dx / 2 and theta_j = 2 pi (2j + 1) h,
+//   sum_u c_u e^{i 2 pi k.x_u} = e^{i 2 pi k.x_c} sum_j (A_j C_j + i B_j S_j)
+// with A_j = c_{8+j} + c_{7-j}, B_j = c_{8+j} - c_{7-j} (written by the
+// pre-pass), C_j = cos theta_j and S_j = sin theta_j by the three-term
+// recurrence from cos and sin of 2 pi h. Per sample: 4 transcendentals and
+// 57 other VALU instructions for 16 terms (Horner over the two chunks: 8
+// and 72).
+template <int S>
+__device__ __forceinline__ void accumulate_ramp_pair(const float4 *ch, const float (&kx)[S],
+                                                     const float (&ky)[S], const float (&kz)[S],
+                                                     float (&acc_r)[S], float (&acc_i)[S])
+{
+    constexpr int P = kChunk;   // voxel pairs
+    float f[kFields][kChunk];
+    load_chunk(ch, f);
+    const float(&ar)[P] = f[0];
+    const float(&ai)[P] = f[1];
+    const float(&br)[P] = f[2];
+    const float(&bi)[P] = f[3];
+    const float x0 = f[4][0], hdx = f[4][1], y = f[4][2], z = f[4][3];
+#pragma unroll
+    for (int j0 = 0; j0 < S; j0 += kRampGroup) {
+        float pc[kRampGroup], h[kRampGroup], er[kRampGroup], ei[kRampGroup], c1[kRampGroup],
+            s1[kRampGroup];
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) {
+            const int j = j0 + t;
+            h[t] = kx[j] * hdx;
+            pc[t] = __builtin_fmaf(2.0f * kChunk - 1.0f, h[t],
+                                   __builtin_fmaf(kx[j], x0, __builtin_fmaf(ky[j], y, kz[j] * z)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) {
+            er[t] = __builtin_amdgcn_cosf(pc[t]);
+            ei[t] = __builtin_amdgcn_sinf(pc[t]);
+            c1[t] = __builtin_amdgcn_cosf(h[t]);
+            s1[t] = __builtin_amdgcn_sinf(h[t]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < kRampGroup; ++t) {
+            const int j = j0 + t;
+            const float k2 = __builtin_fmaf(-4.0f * s1[t], s1[t], 2.0f);   // 2 cos(4 pi h)
+            float cp = c1[t], sp = -s1[t], c = c1[t], sn = s1[t];
+            float pr = 0.0f, pi = 0.0f;
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                if (q > 0) {
+                    const float cn = __builtin_fmaf(k2, c, -cp), snn = __builtin_fmaf(k2, sn, -sp);
+                    cp = c;
+                    sp = sn;
+                    c = cn;
+                    sn = snn;
+                }
+                // P += A_q C_q + i B_q S_q
+                pr = __builtin_fmaf(ar[q], c, __builtin_fmaf(-bi[q], sn, pr));
+                pi = __builtin_fmaf(ai[q], c, __builtin_fmaf(br[q], sn, pi));
+            }
+            acc_r[j] = __builtin_fmaf(er[t], pr, __builtin_fmaf(-ei[t], pi, acc_r[j]));
+            acc_i[j] = __builtin_fmaf(er[t], pi, __builtin_fmaf(ei[t], pr, acc_i[j]));
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -221,13 +324,26 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 
     int c0, c1;
     split_range(nchunks, splits, blockIdx.y, &c0, &c1);
+    // chunk pairs (2c, 2c + 1): stages and splits start at even chunks, so a
+    // 16-voxel ramp's two chunks always arrive together
+    auto pair = [&](const float4 *ch, int count, auto shared_kz) {
+        // every lane reads the same chunk: a scalar branch
+        const float mark = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                                                          int, reinterpret_cast<const float *>(ch)[kFields * kChunk - 1])));
+        if (count == 2 && mark == -2.0f) {
+            accumulate_ramp_pair<S>(ch, sx, sy, sz, acc_r, acc_i);
+            return;
+        }
+        for (int c = 0; c < count; ++c)
+            accumulate_voxels<S, decltype(shared_kz)::value>(ch + c * kChunkVec4, sx, sy, sz, acc_r, acc_i);
+    };
     if (shared)
-        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
-            accumulate_voxels<S, true>(ch, sx, sy, sz, acc_r, acc_i);
+        stream_chunk_groups<2>(src, c0, c1, stage, [&](const float4 *ch, int count) {
+            pair(ch, count, std::true_type());
         });
     else
-        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
-            accumulate_voxels<S, false>(ch, sx, sy, sz, acc_r, acc_i);
+        stream_chunk_groups<2>(src, c0, c1, stage, [&](const float4 *ch, int count) {
+            pair(ch, count, std::false_type());
         });
 
     float *dst_r = out_r + (int64_t)blockIdx.y * M, *dst_i = out_i + (int64_t)blockIdx.y * M;

@@ -84,6 +84,19 @@ def test_issue_ceilings():
 
 
 
+def test_ramp_chunk_fractions_pairs_and_chunks():
+    """16-voxel ramps count once; a disturbed voxel demotes its pair to two
+    chunks of which the untouched one is still an 8-voxel ramp."""
+    from non_cartesian_mri_fhd_amd import inputs
+    L = 16
+    x, y, z = inputs.grid_coords(L)
+    assert bench.ramp_chunk_fractions(x, y, z) == (1.0, 0.0)
+    x2 = x.copy()
+    x2[21] += np.float32(1e-3)   # voxel 5 of the pair (16..31): its chunk 16..23 fails
+    f16, f8 = bench.ramp_chunk_fractions(x2, y, z)
+    assert f16 == 1.0 - 16 / L ** 3 and f8 == 8 / L ** 3
+
+
 def test_ramp_chunk_fraction():
     from non_cartesian_mri_fhd_amd import inputs
     L = 16

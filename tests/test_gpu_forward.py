@@ -28,6 +28,13 @@ def t(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
+def bench_fractions(x, y, z):
+    """(16-voxel ramp, 8-voxel ramp chunk) voxel fractions the pre-pass
+    should find, by the benchmark's host-side replica of its test."""
+    import bench
+    return bench.ramp_chunk_fractions(x, y, z)
+
+
 def gpu_forward(case, img, dev):
     c = to_dev(case, dev)
     Dr, Di = binding.fhd_forward(c["kx"], c["ky"], c["kz"], c["x"], c["y"], c["z"],
@@ -176,6 +183,25 @@ def test_forward_ramp_and_direct_chunks_agree(dev):
     check("forward ramp chunks", *ramp, *ref)
     check("forward direct chunks", *direct, *ref)
     assert metrics.rel_l2(*ramp, direct[0].astype(np.float64), direct[1].astype(np.float64)) < 5e-5
+
+
+def test_forward_ramp_pairs_and_single_chunks_agree(dev):
+    """The same voxels as 16-voxel ramps (x-fastest grid order: every chunk
+    pair is one ramp) and as 8-voxel ramp chunks only (the two chunks of
+    every pair swapped, so no pair is a ramp but every chunk still is):
+    both match the oracle and each other to rounding."""
+    w = inputs.make_workload("spiral32")
+    img = inputs.random_image(w["N"], seed=24)
+    n = np.arange(w["N"]).reshape(-1, 2, 8)[:, ::-1, :].reshape(-1)
+    assert bench_fractions(w["x"], w["y"], w["z"]) == (1.0, 0.0)
+    assert bench_fractions(w["x"][n], w["y"][n], w["z"][n]) == (0.0, 1.0)
+    pairs = gpu_forward(w, img, dev)
+    single = gpu_forward(dict(w, x=w["x"][n], y=w["y"][n], z=w["z"][n]),
+                         (img[0][n], img[1][n]), dev)
+    ref = oracle.forward(w["kx"], w["ky"], w["kz"], img[0], img[1], w["x"], w["y"], w["z"])
+    check("forward 16-voxel ramps", *pairs, *ref)
+    check("forward 8-voxel ramp chunks", *single, *ref)
+    assert metrics.rel_l2(*pairs, single[0].astype(np.float64), single[1].astype(np.float64)) < 5e-5
 
 
 def test_forward_ramp_degenerate_steps_and_partial_chunk(dev):
