@@ -68,9 +68,10 @@ METRIC = "F^H D voxel-sample terms/s at 128^3 x 100k; % of FP32 VALU/trans roofl
 #   F's ramp chunks (Horner): per sample and chunk of 8 voxels 4
 #     transcendentals and 36 VALU (phase 3, step 1, Horner 28, finish 4):
 #     13 clk per wave-term, 1.21e13 terms/s; F's 16-voxel ramps (voxel
-#     pairs about the centre, a chunk pair): per sample 4 transcendentals
-#     and 57 VALU (phase 5, 2 cos(2 pi d) 2, recurrence 14, pair sums 32,
-#     finish 4) for 16 terms: 9.1 clk per wave-term, 1.73e13 terms/s.
+#     pairs about the centre, a chunk pair, the pairs' real factors kept
+#     per lane while the step repeats): per sample 2 transcendentals and 40
+#     VALU (centre phase 4, pair sums 32, finish 4) for 16 terms: 6.0 clk
+#     per wave-term, 2.62e13 terms/s.
 CUS, SIMDS_PER_CU, TRANS_LANES_PER_CYCLE, CLOCK_HZ = 256, 4, 8, 2.4e9
 P_FP32 = 157.3e12
 P_TRANS = CUS * SIMDS_PER_CU * TRANS_LANES_PER_CYCLE * CLOCK_HZ
@@ -95,7 +96,7 @@ def issue_terms(valu: float, trans: float) -> float:
 ROOF_TERMS_RAMP = issue_terms(35.0 / 16, 2.0 / 16)
 ROOF_TERMS_RAMP_LANE = issue_terms(55.0 / 16, 4.0 / 16)
 ROOF_TERMS_RAMP_F = issue_terms(36.0 / 8, 4.0 / 8)
-ROOF_TERMS_RAMP_F16 = issue_terms(57.0 / 16, 4.0 / 16)
+ROOF_TERMS_RAMP_F16 = issue_terms(40.0 / 16, 2.0 / 16)
 
 
 def roof_terms(parts) -> float:

@@ -28,9 +28,11 @@
 //    lane's samples share kz, as within a plane of a stack of spirals --
 //    bitwise identical), v_cos_f32, v_sin_f32, 2 FMA. A 16-voxel ramp is
 //    e^{i 2 pi k.x_c} sum_j (A_j C_j + i B_j S_j) with the real factors
-//    C_j, S_j = cos, sin(2 pi (j + 1/2) kx dx) from a three-term recurrence:
-//    4 transcendentals and 57 other VALU instructions per sample for 16
-//    terms. An 8-voxel ramp chunk is a polynomial in z = e^{i 2 pi kx dx},
+//    C_j, S_j = cos, sin(2 pi (j + 1/2) kx dx) from a three-term recurrence,
+//    which the lane keeps for its samples while the step repeats (on a
+//    grid they are formed once): 2 transcendentals and 40 other VALU
+//    instructions per sample for 16 terms. Two samples per lane leave the
+//    registers for those factors. An 8-voxel ramp chunk is a polynomial in z = e^{i 2 pi kx dx},
 //    e^{i 2 pi k.x_0} sum_u conj(rho_u) z^u, by Horner's rule (4 FMA per
 //    voxel) after 4 transcendentals per sample. The accumulated imaginary
 //    part is negated once at the end (exact).
@@ -45,7 +47,7 @@
 namespace fhd {
 namespace {
 
-constexpr int kSamp = 8;        // consecutive samples per lane
+constexpr int kSamp = 2;        // consecutive samples per lane (2, 1, 4, 8 measured: 2 best)
 constexpr int kRampGroup = 2;   // samples per transcendental group on ramp chunks
 static_assert(kSamp % kRampGroup == 0, "ramp groups tile a lane's samples");
 
@@ -169,13 +171,48 @@ __device__ __forceinline__ void accumulate_ramp_chunk(const float (&f)[kFields][
 //   sum_u c_u e^{i 2 pi k.x_u} = e^{i 2 pi k.x_c} sum_j (A_j C_j + i B_j S_j)
 // with A_j = c_{8+j} + c_{7-j}, B_j = c_{8+j} - c_{7-j} (written by the
 // pre-pass), C_j = cos theta_j and S_j = sin theta_j by the three-term
-// recurrence from cos and sin of 2 pi h. Per sample: 4 transcendentals and
-// 57 other VALU instructions for 16 terms (Horner over the two chunks: 8
-// and 72).
+// recurrence from cos and sin of 2 pi h. C_j, S_j and h depend on the
+// sample and the step alone, so the lane keeps them for its samples
+// (RampFactors) and forms them again only when a ramp's step differs from
+// the last one (on a grid: once). Per sample and ramp then: 2
+// transcendentals and 40 other VALU instructions for 16 terms.
+template <int S>
+struct RampFactors {
+    float hdx;                       // the step they were formed for (NaN: none yet)
+    float h[S], c[S][kChunk], s[S][kChunk];
+};
+
+template <int S>
+__device__ __forceinline__ void ramp_factors(float hdx, const float (&kx)[S], RampFactors<S> &rf)
+{
+    rf.hdx = hdx;
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const float h = kx[j] * hdx;
+        const float c1 = __builtin_amdgcn_cosf(h), s1 = __builtin_amdgcn_sinf(h);
+        const float k2 = __builtin_fmaf(-4.0f * s1, s1, 2.0f);   // 2 cos(4 pi h)
+        float cp = c1, sp = -s1, c = c1, sn = s1;
+        rf.h[j] = h;
+#pragma unroll
+        for (int q = 0; q < kChunk; ++q) {
+            if (q > 0) {
+                const float cn = __builtin_fmaf(k2, c, -cp), snn = __builtin_fmaf(k2, sn, -sp);
+                cp = c;
+                sp = sn;
+                c = cn;
+                sn = snn;
+            }
+            rf.c[j][q] = c;
+            rf.s[j][q] = sn;
+        }
+    }
+}
+
 template <int S>
 __device__ __forceinline__ void accumulate_ramp_pair(const float4 *ch, const float (&kx)[S],
                                                      const float (&ky)[S], const float (&kz)[S],
-                                                     float (&acc_r)[S], float (&acc_i)[S])
+                                                     RampFactors<S> &rf, float (&acc_r)[S],
+                                                     float (&acc_i)[S])
 {
     constexpr int P = kChunk;   // voxel pairs
     float f[kFields][kChunk];
@@ -185,15 +222,16 @@ __device__ __forceinline__ void accumulate_ramp_pair(const float4 *ch, const flo
     const float(&br)[P] = f[2];
     const float(&bi)[P] = f[3];
     const float x0 = f[4][0], hdx = f[4][1], y = f[4][2], z = f[4][3];
+    // every lane reads the same pair: a scalar branch
+    if (__builtin_bit_cast(unsigned, hdx) != __builtin_bit_cast(unsigned, rf.hdx))
+        ramp_factors<S>(hdx, kx, rf);
 #pragma unroll
     for (int j0 = 0; j0 < S; j0 += kRampGroup) {
-        float pc[kRampGroup], h[kRampGroup], er[kRampGroup], ei[kRampGroup], c1[kRampGroup],
-            s1[kRampGroup];
+        float pc[kRampGroup], er[kRampGroup], ei[kRampGroup];
 #pragma unroll
         for (int t = 0; t < kRampGroup; ++t) {
             const int j = j0 + t;
-            h[t] = kx[j] * hdx;
-            pc[t] = __builtin_fmaf(2.0f * kChunk - 1.0f, h[t],
+            pc[t] = __builtin_fmaf(2.0f * kChunk - 1.0f, rf.h[j],
                                    __builtin_fmaf(kx[j], x0, __builtin_fmaf(ky[j], y, kz[j] * z)));
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -202,29 +240,18 @@ __device__ __forceinline__ void accumulate_ramp_pair(const float4 *ch, const flo
         for (int t = 0; t < kRampGroup; ++t) {
             er[t] = __builtin_amdgcn_cosf(pc[t]);
             ei[t] = __builtin_amdgcn_sinf(pc[t]);
-            c1[t] = __builtin_amdgcn_cosf(h[t]);
-            s1[t] = __builtin_amdgcn_sinf(h[t]);
         }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < kRampGroup; ++t) {
             const int j = j0 + t;
-            const float k2 = __builtin_fmaf(-4.0f * s1[t], s1[t], 2.0f);   // 2 cos(4 pi h)
-            float cp = c1[t], sp = -s1[t], c = c1[t], sn = s1[t];
             float pr = 0.0f, pi = 0.0f;
 #pragma unroll
             for (int q = 0; q < P; ++q) {
-                if (q > 0) {
-                    const float cn = __builtin_fmaf(k2, c, -cp), snn = __builtin_fmaf(k2, sn, -sp);
-                    cp = c;
-                    sp = sn;
-                    c = cn;
-                    sn = snn;
-                }
                 // P += A_q C_q + i B_q S_q
-                pr = __builtin_fmaf(ar[q], c, __builtin_fmaf(-bi[q], sn, pr));
-                pi = __builtin_fmaf(ai[q], c, __builtin_fmaf(br[q], sn, pi));
+                pr = __builtin_fmaf(ar[q], rf.c[j][q], __builtin_fmaf(-bi[q], rf.s[j][q], pr));
+                pi = __builtin_fmaf(ai[q], rf.c[j][q], __builtin_fmaf(br[q], rf.s[j][q], pi));
             }
             acc_r[j] = __builtin_fmaf(er[t], pr, __builtin_fmaf(-ei[t], pi, acc_r[j]));
             acc_i[j] = __builtin_fmaf(er[t], pi, __builtin_fmaf(ei[t], pr, acc_i[j]));
@@ -322,6 +349,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     for (int j = 1; j < S; ++j) same_kz = same_kz && __float_as_uint(sz[j]) == __float_as_uint(sz[0]);
     const bool shared = __syncthreads_and(same_kz);
 
+    RampFactors<S> rf;
+    rf.hdx = __builtin_nanf("");
     int c0, c1;
     split_range(nchunks, splits, blockIdx.y, &c0, &c1);
     // chunk pairs (2c, 2c + 1): stages and splits start at even chunks, so a
@@ -331,7 +360,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         const float mark = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                                                           int, reinterpret_cast<const float *>(ch)[kFields * kChunk - 1])));
         if (count == 2 && mark == -2.0f) {
-            accumulate_ramp_pair<S>(ch, sx, sy, sz, acc_r, acc_i);
+            accumulate_ramp_pair<S>(ch, sx, sy, sz, rf, acc_r, acc_i);
             return;
         }
         for (int c = 0; c < count; ++c)
