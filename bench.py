@@ -97,6 +97,14 @@ ROOF_TERMS_RAMP = issue_terms(35.0 / 16, 2.0 / 16)
 ROOF_TERMS_RAMP_LANE = issue_terms(55.0 / 16, 4.0 / 16)
 ROOF_TERMS_RAMP_F = issue_terms(36.0 / 8, 4.0 / 8)
 ROOF_TERMS_RAMP_F16 = issue_terms(40.0 / 16, 2.0 / 16)
+# F^H D on lines of 64 voxels along x with one step per unit of 4096 (any
+# x-fastest grid with rows of a multiple of 64 voxels): the voxels pair up
+# about each line's centre and the sum becomes four real matrix products
+# (lines x samples by samples x pairs), each as three bf16 products of
+# split fp32 operands on the matrix cores: 6 bf16 multiply-adds = 12 FLOP
+# per term against the 2.5 PFLOP/s dense bf16 peak
+LINES_FLOP_PER_TERM = 12
+ROOF_TERMS_LINES = P_MFMA_BF16 / LINES_FLOP_PER_TERM
 
 
 def roof_terms(parts) -> float:
@@ -145,34 +153,55 @@ def ramp_chunk_fractions(x, y, z) -> tuple[float, float]:
     return float(np.sum(ok16) * 16 / n), float(single * 8 / n)
 
 
-def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 8) -> tuple[float, float]:
-    """Fractions of voxels whose F^H D gather workgroup takes the ramp path,
-    by the kernel's own test: every lane's `vox` voxels form a ramp (see
-    _lane_ramps) and the workgroup's lanes all exist. Returned as (one
-    step: every lane of the workgroup has the same x step bitwise, per-lane
-    steps: the other ramp workgroups)."""
+def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64):
+    """Per unit of block*vox consecutive voxels (one workgroup of each F^H D
+    gather instance), the class the gather's classify kernel gives it, by
+    the same tests: 2 when the unit is whole and every aligned run of `line`
+    voxels is a line along x (see _lane_ramps) with one step for the unit
+    (the matrix-core instance); else 1 when every lane's `vox` voxels are
+    such a ramp, all with one step (the ramp path with sample records);
+    else 0. Returned with, per unit, whether all its lanes are ramps (the
+    per-lane ramp path when the class is 0) and its voxel count."""
+    x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
+    N = x.size
+    unit = block * vox
+    units = (N + unit - 1) // unit
+    counts = np.minimum(unit, N - np.arange(units) * unit)
+
+    def per_unit(per):
+        # groups of `per` voxels past N (a partial last unit) stay False
+        ok, dx = _lane_ramps(x, y, z, per)
+        n = units * (unit // per)
+        o = np.zeros(n, bool)
+        o[:ok.size] = ok
+        st = np.zeros(n, np.float32)
+        st[:dx.size] = dx
+        o = o.reshape(units, -1)
+        S = st.view(np.uint32).reshape(units, -1)
+        every = o.all(axis=1)
+        return every, every & np.all(S == S[:, :1], axis=1)
+
+    all_ramp, one = per_unit(vox)
+    _, lines = per_unit(line)
+    lines &= counts == unit
+    cls = np.where(lines, 2, np.where(one, 1, 0))
+    return cls, all_ramp, counts
+
+
+def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16) -> tuple[float, float, float]:
+    """Fractions of voxels by the F^H D gather path their unit takes (see
+    gather_unit_classes): (lines on the matrix cores, ramps with one step
+    for the workgroup, ramps with per-lane steps); the rest is direct."""
     N = np.asarray(x).size
-    lane_ok, dx = _lane_ramps(x, y, z, vox)
-    lanes = lane_ok.size
-    if lanes == 0:
-        return 0.0, 0.0
-    per_block = block
-    blocks = (lanes + per_block - 1) // per_block
-    ok = np.zeros(blocks * per_block, bool)
-    ok[:lanes] = lane_ok
-    steps = np.zeros(blocks * per_block, np.float32)
-    steps[:lanes] = dx
-    # lanes past N (a partial last workgroup) stay False: such a
-    # workgroup never qualifies
-    block_ok = ok.reshape(blocks, per_block).all(axis=1)
-    S = steps.view(np.uint32).reshape(blocks, per_block)
-    one = block_ok & np.all(S == S[:, :1], axis=1)
-    voxels = np.minimum(block * vox, N - np.arange(blocks) * block * vox)
-    return float(np.sum(voxels[one]) / N), float(np.sum(voxels[block_ok & ~one]) / N)
+    if N == 0:
+        return 0.0, 0.0, 0.0
+    cls, all_ramp, counts = gather_unit_classes(x, y, z, block, vox)
+    return (float(np.sum(counts[cls == 2]) / N), float(np.sum(counts[cls == 1]) / N),
+            float(np.sum(counts[(cls == 0) & all_ramp]) / N))
 
 
-def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 8) -> float:
-    """Fraction of voxels on the ramp path, either form."""
+def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 16) -> float:
+    """Fraction of voxels on a ramp path, any form (lines included)."""
     return sum(ramp_voxel_fractions(x, y, z, block, vox))
 
 
@@ -310,6 +339,21 @@ def main(argv=None) -> int:
 
     ms_step = wall * 1e3 / args.steps
     gather_all = np.array([e[1].elapsed_time(e[2]) for e in ev])
+
+    # the same gather held to the vector-ALU fp32 paths (fhd_gather_paths,
+    # FHD_GATHER_VECTOR), timed beside it: the evidence that the
+    # matrix-core form of lines beats the VALU form on this workload
+    vec_r = torch.empty_like(rho_r)
+    vec_i = torch.empty_like(rho_i)
+    binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], vec_r, vec_i, paths=binding.FHD_GATHER_VECTOR)
+    vev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)]
+    for e in vev:
+        e[0].record(stream)
+        binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], vec_r, vec_i,
+                           paths=binding.FHD_GATHER_VECTOR)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    vec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in vev]))
     gather_ms = float(np.mean(gather_all))
     pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     terms = float(N) * float(M)
@@ -318,11 +362,20 @@ def main(argv=None) -> int:
 
     # the ceiling for the paths this voxel layout takes (the x-fastest
     # grids of the workloads: the ramp path throughout)
-    one, lane = ramp_voxel_fractions(w["x"], w["y"], w["z"], cfg["block_threads"], cfg["voxels_per_lane"])
-    roof = roof_terms([(terms * one, ROOF_TERMS_RAMP), (terms * lane, ROOF_TERMS_RAMP_LANE),
-                       (terms * (1 - one - lane), ROOF_TERMS)])
-    achieved = FLOP_PER_TERM * terms / (gather_ms * 1e-3) / 1e12
-    peak = FLOP_PER_TERM * roof / 1e12
+    lines, one, lane = ramp_voxel_fractions(w["x"], w["y"], w["z"], cfg["block_threads"],
+                                            cfg["voxels_per_lane"])
+    roof = roof_terms([(terms * lines, ROOF_TERMS_LINES), (terms * one, ROOF_TERMS_RAMP),
+                       (terms * lane, ROOF_TERMS_RAMP_LANE),
+                       (terms * (1 - lines - one - lane), ROOF_TERMS)])
+    rate = terms / (gather_ms * 1e-3)
+    if lines == 1.0:
+        # every unit on the matrix cores: bf16 FLOP against the bf16 peak
+        roofline = {"bound": "mfma", "achieved": LINES_FLOP_PER_TERM * rate / 1e12,
+                    "peak": P_MFMA_BF16 / 1e12}
+    else:
+        roofline = {"bound": "alu", "achieved": FLOP_PER_TERM * rate / 1e12,
+                    "peak": FLOP_PER_TERM * roof / 1e12}
+    roofline.update(unit="TFLOP/s", frac=rate / roof, traffic=measured_traffic("fhd", args.workload))
     out = {
         "metric": METRIC,
         "value": value,
@@ -339,16 +392,10 @@ def main(argv=None) -> int:
         "config": {
             "workload": "%s: F^H D over %d^3 voxels x %d samples (%s)"
                         % (args.workload, w["L"], M, inputs.WORKLOADS[args.workload].trajectory),
-            "N": N, "M": M, "terms": terms, "ramp_path_voxel_fraction": one + lane, "one_step_voxel_fraction": one, **cfg,
+            "N": N, "M": M, "terms": terms, "lines_voxel_fraction": lines,
+            "one_step_voxel_fraction": one, "per_lane_ramp_voxel_fraction": lane, **cfg,
         },
-        "roofline": {
-            "bound": "alu",
-            "achieved": achieved,
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": achieved / peak,
-            "traffic": measured_traffic("fhd", args.workload),
-        },
+        "roofline": roofline,
         "roofline_direct_form": {
             "note": "R for 2 transcendentals per term, the pages' direct evaluation",
             "peak": FLOP_PER_TERM * ROOF_TERMS / 1e12, "unit": "TFLOP/s",
@@ -357,6 +404,13 @@ def main(argv=None) -> int:
                       "fhd_gather_kernel_median": float(np.median(gather_all)),
                       "fhd_gather_kernel_min": float(np.min(gather_all))},
         "gflops_13_per_term": FLOP_PER_TERM * value / 1e9,
+        "vector_paths_only": {
+            "note": "fhd_gather_paths(FHD_GATHER_VECTOR): every unit on the fp32 VALU paths",
+            "gather_ms": vec_ms, "terms_per_s": terms / (vec_ms * 1e-3),
+            "matrix_core_speedup": vec_ms / gather_ms,
+            "frac_of_valu_ceiling": terms / (vec_ms * 1e-3) / roof_terms(
+                [(terms * (lines + one), ROOF_TERMS_RAMP), (terms * lane, ROOF_TERMS_RAMP_LANE),
+                 (terms * (1 - lines - one - lane), ROOF_TERMS)])},
     }
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, args.workload, args.cpu_seconds,
@@ -522,13 +576,15 @@ def bench_other(args) -> int:
     # ceiling: F^H terms at the adjoint gather's path mix, F terms direct
     NM = float(N) * M
     gcfg = binding.gather_config()
-    one, lane = ramp_voxel_fractions(w["x"], w["y"], w["z"], gcfg["block_threads"], gcfg["voxels_per_lane"])
+    lines, one, lane = ramp_voxel_fractions(w["x"], w["y"], w["z"], gcfg["block_threads"],
+                                            gcfg["voxels_per_lane"])
     ramp_f16, ramp_f = ramp_chunk_fractions(w["x"], w["y"], w["z"])
     adjoint = {"normal": 1, "cg": 1 + k_iters}.get(args.op, 0)
     forward_terms = {"forward": 1, "normal": 1, "cg": k_iters}.get(args.op, 0)
-    roof = roof_terms([(adjoint * NM * one, ROOF_TERMS_RAMP),
+    roof = roof_terms([(adjoint * NM * lines, ROOF_TERMS_LINES),
+                       (adjoint * NM * one, ROOF_TERMS_RAMP),
                        (adjoint * NM * lane, ROOF_TERMS_RAMP_LANE),
-                       (adjoint * NM * (1 - one - lane), ROOF_TERMS),
+                       (adjoint * NM * (1 - lines - one - lane), ROOF_TERMS),
                        (forward_terms * NM * ramp_f16, ROOF_TERMS_RAMP_F16),
                        (forward_terms * NM * ramp_f, ROOF_TERMS_RAMP_F),
                        (forward_terms * NM * (1 - ramp_f16 - ramp_f), ROOF_TERMS)])

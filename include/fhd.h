@@ -101,13 +101,36 @@ int fhd_pack(const float *kx, const float *ky, const float *kz,
  *                  16-byte aligned
  *   x, y, z      : N fp32 values each (read only)
  *   rho_r, rho_i : N fp32 values each (written), not overlapping any input
- * M = 0 writes zeros; N = 0 does nothing. The per-voxel summation order is
- * fixed, so repeated calls give bitwise identical results.
- * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_HIP.
+ * M = 0 writes zeros; N = 0 does nothing. The voxels are taken in units of
+ * 4096 consecutive ones. A whole unit whose aligned runs of 64 voxels are
+ * lines along x with one common step (same y and z bitwise, x_v = x_0 +
+ * v dx rounded once; any x-fastest grid whose rows are a multiple of 64
+ * voxels) is summed on the matrix cores in split bf16 (about 1e-5
+ * relative); every other unit in fp32 on the vector ALUs. The per-voxel
+ * summation order is fixed, so repeated calls give bitwise identical
+ * results. The library allocates and frees a small stream-ordered
+ * workspace on `stream` (unit classes; partial sums when the voxels are too
+ * few to fill the GPU).
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
  */
 int fhd_gather(const void *packed, int M,
                const float *x, const float *y, const float *z,
                float *rho_r, float *rho_i, int N, void *stream);
+
+/* Paths fhd_gather_paths may take. */
+#define FHD_GATHER_ALL 0    /* as fhd_gather: lines on the matrix cores */
+#define FHD_GATHER_VECTOR 1 /* vector-ALU fp32 paths only, for every unit */
+
+/*
+ * fhd_gather with a choice of paths: `paths` is FHD_GATHER_ALL (identical
+ * to fhd_gather) or FHD_GATHER_VECTOR (units of lines take the fp32 ramp
+ * paths of the vector ALUs instead of the split-bf16 matrix cores: fp32
+ * arithmetic throughout, about 1e-6 relative). Other arguments and errors
+ * as fhd_gather; any other `paths` is FHD_ERR_INVALID_ARG.
+ */
+int fhd_gather_paths(const void *packed, int M,
+                     const float *x, const float *y, const float *z,
+                     float *rho_r, float *rho_i, int N, int paths, void *stream);
 
 /*
  * Forward operator F (image to k-space; page "Case study -- iterative MRI

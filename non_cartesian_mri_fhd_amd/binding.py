@@ -21,6 +21,8 @@ FHD_ERR_HIP = -2
 FHD_ERR_ALLOC = -3
 FHD_GRID_FP32 = 0
 FHD_GRID_BF16X3 = 1
+FHD_GATHER_ALL = 0
+FHD_GATHER_VECTOR = 1
 
 LIBRARY = lib_path("libfhd.so")
 
@@ -62,6 +64,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_pack.restype = i32
     lib.fhd_gather.argtypes = [vp, i32] + [fp] * 5 + [i32, vp]
     lib.fhd_gather.restype = i32
+    lib.fhd_gather_paths.argtypes = [vp, i32] + [fp] * 5 + [i32, i32, vp]
+    lib.fhd_gather_paths.restype = i32
     lib.fhd_forward.argtypes = [fp] * 10 + [i32, i32, vp]
     lib.fhd_forward.restype = i32
     lib.fhd_forward_pack.argtypes = [fp] * 5 + [i32, vp, i64, vp]
@@ -168,8 +172,11 @@ def fhd_pack(kx, ky, kz, Dr, Di, packed: torch.Tensor, stream=None) -> torch.Ten
     return packed
 
 
-def fhd_gather(packed: torch.Tensor, M: int, x, y, z, rho_r=None, rho_i=None, stream=None):
-    """Gather over a packed k-space of M samples; returns (rho_r, rho_i)."""
+def fhd_gather(packed: torch.Tensor, M: int, x, y, z, rho_r=None, rho_i=None, stream=None,
+               paths: int | None = None):
+    """Gather over a packed k-space of M samples; returns (rho_r, rho_i).
+    paths=None calls fhd_gather; FHD_GATHER_ALL or FHD_GATHER_VECTOR calls
+    fhd_gather_paths with it."""
     lib = load()
     N = x.numel()
     dev = x.device
@@ -184,8 +191,12 @@ def fhd_gather(packed: torch.Tensor, M: int, x, y, z, rho_r=None, rho_i=None, st
     ptrs = [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"),
                                                (rho_r, "rho_r"), (rho_i, "rho_i"))]
     with torch.cuda.device(dev):
-        _check(lib, lib.fhd_gather(packed.data_ptr(), int(M), *ptrs, N, _stream(dev, stream)),
-               "fhd_gather")
+        if paths is None:
+            _check(lib, lib.fhd_gather(packed.data_ptr(), int(M), *ptrs, N, _stream(dev, stream)),
+                   "fhd_gather")
+        else:
+            _check(lib, lib.fhd_gather_paths(packed.data_ptr(), int(M), *ptrs, N, int(paths),
+                                             _stream(dev, stream)), "fhd_gather_paths")
     return rho_r, rho_i
 
 

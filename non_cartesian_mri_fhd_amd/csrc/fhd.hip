@@ -55,6 +55,7 @@
 #include <cmath>
 #include <cstdint>
 #include <string>
+#include <type_traits>
 
 #include "fhd_internal.h"
 
@@ -412,27 +413,35 @@ __device__ __forceinline__ void ramp_unfold(float (&acc_r)[V], float (&acc_i)[V]
     }
 }
 
-// Two instances share the grid: ONE_STEP = true takes the workgroups whose
-// lanes are ramps with one common step (the ramp path with sample records,
-// at 5 waves per SIMD, <= 96 VGPRs) and ONE_STEP = false all others (at 4
-// waves per SIMD, <= 128 VGPRs); each instance's workgroups of the other
-// kind return after the test. Split s = blockIdx.y of `splits` takes its
-// share of the sample stream and writes rho (splits == 1) or its partial
-// sums at out + s*N.
-template <int V, bool ONE_STEP>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP ? 5 : 4))) void fhd_gather_kernel(
-    const float *__restrict__ packed, int nchunks, int splits,
-    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
-    float *__restrict__ out_r, float *__restrict__ out_i, int N)
-{
-    __shared__ float4 stage[2][kStageVec4];
-    __shared__ float4 side[kSideSamples * kRampRecord];   // ramp path with one step per workgroup
-    __shared__ float wg_dx;
-    const float4 *src = reinterpret_cast<const float4 *>(packed);
+// ---------------------------------------------------------------------------
+// Units and their classes
+// ---------------------------------------------------------------------------
+// Every gather instance takes voxels in units of kUnitVox consecutive
+// voxels (one workgroup each, the same grid for all). fhd_classify_kernel
+// tests each unit once and records which instance takes it:
+//   kClassLines   -- every aligned run of kLineVox voxels is one line along
+//                    x (same y and z bitwise, x_v = x_0 + v dx rounded once)
+//                    and all lines share dx bitwise (any x-fastest grid
+//                    whose rows are multiples of kLineVox voxels long): the
+//                    matrix-core instance;
+//   kClassOneStep -- otherwise, every lane's kVox voxels are such a ramp and
+//                    all lanes share the step: the ramp path with sample
+//                    records;
+//   kClassGeneral -- everything else (per-lane ramps, shared (y, z), direct).
+constexpr int kUnitVox = kBlock * kVox;   // 4096 voxels
+constexpr int kLineVox = 64;              // voxels per line of the matrix-core instance
+enum : int { kClassGeneral = 0, kClassOneStep = 1, kClassLines = 2 };
+static_assert(kLineVox % kVox == 0 && 64 % (kLineVox / kVox) == 0,
+              "a line is whole lanes of one wave");
 
-    // lane l of workgroup b owns voxels (b*kBlock + l)*V + v, v < V
-    const int64_t n0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * V;
-    float px[V], py[V], pz[V], acc_r[V], acc_i[V];
+// Lane l of workgroup b owns voxels (b kBlock + l) V + v, v < V. Voxels past
+// N copy the lane's first voxel, so they never spoil the shared-(y, z) test
+// (their results are not stored).
+template <int V>
+__device__ __forceinline__ void load_lane_voxels(const float *__restrict__ x, const float *__restrict__ y,
+                                                 const float *__restrict__ z, int N, int64_t n0,
+                                                 float (&px)[V], float (&py)[V], float (&pz)[V])
+{
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int64_t n = n0 + v;
@@ -440,11 +449,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP
         px[v] = live ? x[n] : 0.0f;
         py[v] = live ? y[n] : 0.0f;
         pz[v] = live ? z[n] : 0.0f;
-        acc_r[v] = 0.0f;
-        acc_i[v] = 0.0f;
     }
-    // voxels past N copy the lane's first voxel, so they never spoil the
-    // shared-(y, z) test (their results are not stored)
 #pragma unroll
     for (int v = 1; v < V; ++v)
         if (n0 + v >= N) {
@@ -452,47 +457,139 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP
             py[v] = py[0];
             pz[v] = pz[0];
         }
-    bool same_yz = true;
-#pragma unroll
-    for (int v = 1; v < V; ++v)
-        same_yz = same_yz && __float_as_uint(py[v]) == __float_as_uint(py[0]) &&
-                  __float_as_uint(pz[v]) == __float_as_uint(pz[0]);
-    // equal spacing along x: every x_v is x0 + v dx rounded once (lanes with
-    // voxels past N never qualify)
-    const float dx = px[1] - px[0];
-    bool ramp = same_yz && n0 + V <= N && __builtin_isfinite(dx);
-#pragma unroll
-    for (int v = 1; v < V; ++v)
-        ramp = ramp && __builtin_fmaf((float)v, dx, px[0]) == px[v];
-    // one decision per workgroup, so every branch's stage barriers are
-    // reached by every wave of the workgroup
-    if (threadIdx.x == 0) wg_dx = dx;
-    const bool all_ramp = __syncthreads_and(ramp);
-    const bool shared = __syncthreads_and(same_yz);
-    // ...and whether all of its lanes step by the same dx (bitwise)
-    const bool one_step = all_ramp && __syncthreads_and(__float_as_uint(dx) == __float_as_uint(wg_dx));
+}
 
-    if (one_step != ONE_STEP) return;   // the other instance's workgroup
+// Whether the lane's voxels share y and z bitwise (*same_yz) and, in
+// addition, sit at x_0 + v dx rounded once with dx = x_1 - x_0 (returned;
+// lanes with voxels past N never qualify); *dx gets that step.
+template <int V>
+__device__ __forceinline__ bool lane_ramp(const float (&px)[V], const float (&py)[V],
+                                          const float (&pz)[V], int64_t n0, int N, bool *same_yz,
+                                          float *dx)
+{
+    bool same = true;
+#pragma unroll
+    for (int v = 1; v < V; ++v)
+        same = same && __float_as_uint(py[v]) == __float_as_uint(py[0]) &&
+               __float_as_uint(pz[v]) == __float_as_uint(pz[0]);
+    const float d = px[1] - px[0];
+    bool ramp = same && n0 + V <= N && __builtin_isfinite(d);
+#pragma unroll
+    for (int v = 1; v < V; ++v) ramp = ramp && __builtin_fmaf((float)v, d, px[0]) == px[v];
+    *same_yz = same;
+    *dx = d;
+    return ramp;
+}
+
+// Whether the lane's voxels lie on the line of kLineVox voxels that its
+// group of kLineVox / V lanes forms: y and z equal to the line's first
+// voxel's bitwise and x_v = x_0 + v dx rounded once, dx = x_1 - x_0 of the
+// line; *dx gets the line's step.
+template <int V>
+__device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (&py)[V],
+                                             const float (&pz)[V], float *dx)
+{
+    constexpr int kLanes = kLineVox / V;
+    const int lane = threadIdx.x & 63;
+    const int lead = lane & ~(kLanes - 1);
+    const float x0 = __shfl(px[0], lead), x1 = __shfl(px[1], lead);
+    const float y0 = __shfl(py[0], lead), z0 = __shfl(pz[0], lead);
+    const float d = x1 - x0;
+    const int first = V * (lane & (kLanes - 1));
+    bool ok = __builtin_isfinite(d);
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+        ok = ok && __builtin_fmaf((float)(first + v), d, x0) == px[v] &&
+             __float_as_uint(py[v]) == __float_as_uint(y0) && __float_as_uint(pz[v]) == __float_as_uint(z0);
+    *dx = d;
+    return ok;
+}
+
+// One workgroup per unit: cls[b] = the class of unit b (never kClassLines
+// unless allow_lines).
+__global__ __launch_bounds__(kBlock) void fhd_classify_kernel(const float *__restrict__ x,
+                                                              const float *__restrict__ y,
+                                                              const float *__restrict__ z, int N,
+                                                              int allow_lines, int *__restrict__ cls)
+{
+    __shared__ float wg_dx, wg_ldx;
+    const int64_t unit = (int64_t)blockIdx.x * kUnitVox;
+    const int64_t n0 = unit + (int64_t)threadIdx.x * kVox;
+    float px[kVox], py[kVox], pz[kVox];
+    load_lane_voxels<kVox>(x, y, z, N, n0, px, py, pz);
+    bool same_yz;
+    float dx, ldx;
+    const bool ramp = lane_ramp<kVox>(px, py, pz, n0, N, &same_yz, &dx);
+    const bool on_line = allow_lines && lane_on_line<kVox>(px, py, pz, &ldx) && unit + kUnitVox <= N;
+    if (threadIdx.x == 0) {
+        wg_dx = dx;
+        wg_ldx = ldx;
+    }
+    // every branch below is uniform over the workgroup, so each barrier is
+    // reached by every wave
+    const bool all_ramp = __syncthreads_and(ramp);
+    const bool all_line = __syncthreads_and(on_line);
+    const bool lines = all_line && __syncthreads_and(__float_as_uint(ldx) == __float_as_uint(wg_ldx));
+    const bool one_step = !lines && all_ramp && __syncthreads_and(__float_as_uint(dx) == __float_as_uint(wg_dx));
+    if (threadIdx.x == 0) cls[blockIdx.x] = lines ? kClassLines : one_step ? kClassOneStep : kClassGeneral;
+}
+
+// Two VALU instances share the grid: ONE_STEP = true takes the units of
+// class kClassOneStep (the ramp path with sample records, at 5 waves per
+// SIMD, <= 96 VGPRs) and ONE_STEP = false those of class kClassGeneral (at
+// 4 waves per SIMD, <= 128 VGPRs); each returns at once for the others.
+// Split s = blockIdx.y of `splits` takes its share of the sample stream and
+// writes rho (splits == 1) or its partial sums at out + s*N.
+template <int V, bool ONE_STEP>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP ? 5 : 4))) void fhd_gather_kernel(
+    const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
+    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
+    float *__restrict__ out_r, float *__restrict__ out_i, int N)
+{
+    static_assert(V * kBlock == kUnitVox, "a workgroup is one unit");
+    if (cls[blockIdx.x] != (ONE_STEP ? kClassOneStep : kClassGeneral)) return;
+    __shared__ float4 stage[2][kStageVec4];
+    __shared__ float4 side[kSideSamples * kRampRecord];   // ramp path with one step per workgroup
+    const float4 *src = reinterpret_cast<const float4 *>(packed);
+
+    const int64_t n0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * V;
+    float px[V], py[V], pz[V], acc_r[V], acc_i[V];
+    load_lane_voxels<V>(x, y, z, N, n0, px, py, pz);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        acc_r[v] = 0.0f;
+        acc_i[v] = 0.0f;
+    }
+    bool same_yz;
+    float dx;
+    const bool ramp = lane_ramp<V>(px, py, pz, n0, N, &same_yz, &dx);
 
     int c0, c1;
     split_range(nchunks, splits, blockIdx.y, &c0, &c1);
     if constexpr (ONE_STEP) {
+        // every lane is a ramp of the unit's common step
         ramp_one_step<V>(src, c0, c1, stage, side, px[0], 0.5f * dx, py[0], pz[0], acc_r, acc_i);
         ramp_unfold<V>(acc_r, acc_i);
-    } else if (all_ramp) {
-        const float hdx = 0.5f * dx;
-        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
-            accumulate_chunk_ramp<V>(ch, px[0], hdx, py[0], pz[0], acc_r, acc_i);
-        });
-        ramp_unfold<V>(acc_r, acc_i);
-    } else if (shared)
-        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
-            accumulate_chunk<V, true>(ch, px, py, pz, acc_r, acc_i);
-        });
-    else
-        stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
-            accumulate_chunk<V, false>(ch, px, py, pz, acc_r, acc_i);
-        });
+    } else {
+        // one decision per workgroup, so every branch's stage barriers are
+        // reached by every wave of the workgroup
+        const bool all_ramp = __syncthreads_and(ramp);
+        const bool shared = __syncthreads_and(same_yz);
+        if (all_ramp) {
+            const float hdx = 0.5f * dx;
+            stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
+                accumulate_chunk_ramp<V>(ch, px[0], hdx, py[0], pz[0], acc_r, acc_i);
+            });
+            ramp_unfold<V>(acc_r, acc_i);
+        } else if (shared)
+            stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
+                accumulate_chunk<V, true>(ch, px, py, pz, acc_r, acc_i);
+            });
+        else
+            stream_chunks(src, c0, c1, stage, [&](const float4 *ch) {
+                accumulate_chunk<V, false>(ch, px, py, pz, acc_r, acc_i);
+            });
+    }
 
     float *dst_r = out_r + (int64_t)blockIdx.y * N, *dst_i = out_i + (int64_t)blockIdx.y * N;
 #pragma unroll
@@ -502,6 +599,173 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP
             dst_r[n] = acc_r[v];
             dst_i[n] = acc_i[v];
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Lines on the matrix cores
+// ---------------------------------------------------------------------------
+// In a unit of class kClassLines the voxels of a line pair up about its
+// centre x_c = x_0 + (kLineVox - 1) dx / 2, and pair j, at x_c +- (j + 1/2)
+// dx, gets
+//
+//   sum_m U[l, m] (B_C[m, j] +- i B_S[m, j])
+//   U[l, m]   = exp(i 2 pi (k_m . x_c(l) + psi_m))     (line l's centre)
+//   B_C[m, j] = a_m cos(2 pi (2j + 1) kx_m dx / 2)      (real, the same for
+//   B_S[m, j] = a_m sin(2 pi (2j + 1) kx_m dx / 2)       every line)
+//
+// i.e. four real matrix products (lines x samples) by (samples x pairs):
+// P_rc = U_r B_C, P_ic = U_i B_C, P_is = U_i B_S, P_rs = U_r B_S, and voxel
+// kLineVox/2 + j gets (P_rc - P_is, P_ic + P_rs), voxel kLineVox/2 - 1 - j
+// (P_rc + P_is, P_ic - P_rs). They run on the bf16 matrix cores with every
+// fp32 operand split into a bf16 high part and a bf16 remainder, three
+// products per real product (the remainders' product, below 2^-17 of it,
+// dropped), accumulated in fp32: 12 v_mfma_f32_32x32x16_bf16 per 32 lines
+// x 32 pairs x 16 samples, 6 bf16 multiply-adds per term in place of two
+// transcendentals per 16 terms and 2 FMAs per term on the vector ALUs.
+//
+// Operand layout of v_mfma_f32_32x32x16_bf16 (measured): lane l supplies
+// A[l % 32][8 (l / 32) + i] and B[8 (l / 32) + i][l % 32], i < 8, and
+// accumulator register r of lane l holds C[8 (r / 4) + 4 (l / 32) + r % 4]
+// [l % 32]. A wave takes 32 lines (rows) and all 32 pairs (columns); per 16
+// samples (a chunk pair, chunk l / 32 for lane l) a lane forms U of its
+// line for its 8 samples (3 FMA, 2 transcendentals each) and, shared by the
+// workgroup through LDS, 8 elements of B_C (wave 0) or B_S (wave 1) for its
+// pair (1 multiply, 1 transcendental, 1 multiply each), split, published
+// with one LDS barrier (double buffered).
+constexpr int kLinesBlock = 128;                    // 2 waves
+constexpr int kLinePairs = kLineVox / 2;
+static_assert(kLinePairs == 32, "the pairs fill one 32-column tile");
+static_assert(kUnitVox == 32 * kLineVox * (kLinesBlock / 64), "a wave takes 32 lines of the unit");
+static_assert(kLinesBlock / 64 == 2, "wave 0 forms B_C, wave 1 B_S");
+
+__global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_lines_kernel(
+    const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
+    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
+    float *__restrict__ out_r, float *__restrict__ out_i, int N)
+{
+    if (cls[blockIdx.x] != kClassLines) return;
+    __shared__ float4 stage[2][kStageVec4];
+    // [buffer][B_C hi, B_C lo, B_S hi, B_S lo][k half][pair]: one lane's
+    // 8-sample operand each; a half-wave reads 32 consecutive entries
+    __shared__ u32x4 bshare[2][4][2][kLinePairs];
+    const float4 *src = reinterpret_cast<const float4 *>(packed);
+    const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // line 32 wave + col of the unit (the whole unit lies below N)
+    const int64_t unit = (int64_t)blockIdx.x * kUnitVox;
+    const int64_t first = unit + (int64_t)(32 * wave + col) * kLineVox;
+    const float x0 = x[first], dx = x[first + 1] - x0, ly = y[first], lz = z[first];
+    const float xc = __builtin_fmaf(0.5f * (float)(kLineVox - 1), dx, x0);
+    // pair `col`'s angle per unit kx: (2 col + 1) dx / 2 (dx is the unit's)
+    const float tj = (float)(2 * col + 1) * (0.5f * dx);
+
+    float16v prc, pic, pis, prs;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        prc[r] = 0.0f;
+        pic[r] = 0.0f;
+        pis[r] = 0.0f;
+        prs[r] = 0.0f;
+    }
+
+    int c0, c1, kb = 0;
+    split_range(nchunks, splits, blockIdx.y, &c0, &c1);
+    const int nch = c1 > c0 ? c1 - c0 : 0;
+    src += (int64_t)c0 * kChunkVec4;
+    const int64_t total_vec4 = (int64_t)nch * kChunkVec4;
+    const int nstages = (nch + kStageChunks - 1) / kStageChunks;
+    if (nstages > 0) issue_stage_load<kLinesBlock>(src, total_vec4, 0, stage[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // one group of 16 samples: chunks ch and ch + 1 of the stage (the
+    // second replaced by zeros, i.e. amplitude 0 in B, when ONE)
+    auto group = [&](const float4 *ch, auto one) {
+        float f[kFields][kChunk];
+        if constexpr (decltype(one)::value) {
+            if (half == 0) {
+                load_chunk(ch, f);
+            } else {
+#pragma unroll
+                for (int q = 0; q < kFields; ++q)
+#pragma unroll
+                    for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
+            }
+        } else {
+            load_chunk(ch + half * kChunkVec4, f);
+        }
+        __builtin_amdgcn_s_setprio(1);
+        float b[kChunk];
+        if (wave == 0) {
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) b[i] = f[4][i] * __builtin_amdgcn_cosf(f[0][i] * tj);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) b[i] = f[4][i] * __builtin_amdgcn_sinf(f[0][i] * tj);
+        }
+        unsigned bh[4], bl[4];
+        split_bf16<kChunk>(b, bh, bl);
+        bshare[kb][2 * wave + 0][half][col] = (u32x4){bh[0], bh[1], bh[2], bh[3]};
+        bshare[kb][2 * wave + 1][half][col] = (u32x4){bl[0], bl[1], bl[2], bl[3]};
+        float ur[kChunk], ui[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const float p = __builtin_fmaf(f[0][i], xc, __builtin_fmaf(f[1][i], ly, __builtin_fmaf(f[2][i], lz, f[3][i])));
+            ur[i] = __builtin_amdgcn_cosf(p);
+            ui[i] = __builtin_amdgcn_sinf(p);
+        }
+        unsigned wa[4][4];
+        split_bf16<kChunk>(ur, wa[0], wa[1]);
+        split_bf16<kChunk>(ui, wa[2], wa[3]);
+        const bf16x8 arh = as_bf16x8(wa[0]), arl = as_bf16x8(wa[1]);
+        const bf16x8 aih = as_bf16x8(wa[2]), ail = as_bf16x8(wa[3]);
+        __builtin_amdgcn_s_setprio(0);
+        lds_barrier();   // this group's B is in LDS
+        const bf16x8 bch = __builtin_bit_cast(bf16x8, bshare[kb][0][half][col]);
+        const bf16x8 bcl = __builtin_bit_cast(bf16x8, bshare[kb][1][half][col]);
+        const bf16x8 bsh = __builtin_bit_cast(bf16x8, bshare[kb][2][half][col]);
+        const bf16x8 bsl = __builtin_bit_cast(bf16x8, bshare[kb][3][half][col]);
+        prc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bch, prc, 0, 0, 0);
+        pic = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, bch, pic, 0, 0, 0);
+        pis = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, bsh, pis, 0, 0, 0);
+        prs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bsh, prs, 0, 0, 0);
+        prc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bcl, prc, 0, 0, 0);
+        pic = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, bcl, pic, 0, 0, 0);
+        pis = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, bsl, pis, 0, 0, 0);
+        prs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bsl, prs, 0, 0, 0);
+        prc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arl, bch, prc, 0, 0, 0);
+        pic = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ail, bch, pic, 0, 0, 0);
+        pis = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ail, bsh, pis, 0, 0, 0);
+        prs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arl, bsh, prs, 0, 0, 0);
+        kb ^= 1;
+    };
+    for (int st = 0; st < nstages; ++st) {
+        const int chunks_here = min(kStageChunks, nch - st * kStageChunks);
+        const float4 *buf = stage[st & 1];
+        for (int c = 0; c + 1 < chunks_here; c += 2) {
+            group(buf + c * kChunkVec4, std::false_type{});
+            // the next stage's copy goes out once the stage's first group
+            // has passed its barrier, so no later barrier waits long for it
+            if (c == 0 && st + 1 < nstages)
+                issue_stage_load<kLinesBlock>(src, total_vec4, st + 1, stage[(st + 1) & 1]);
+        }
+        // an odd chunk at the stream's end (the last stage only)
+        if (chunks_here & 1) group(buf + (chunks_here - 1) * kChunkVec4, std::true_type{});
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // unfold the pair sums into the line's voxels: row 8 (r / 4) + 4 half +
+    // r % 4 of the wave's 32 lines, pair col
+    float *dst_r = out_r + (int64_t)blockIdx.y * N, *dst_i = out_i + (int64_t)blockIdx.y * N;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t line = unit + (int64_t)(32 * wave + 8 * (r / 4) + 4 * half + (r % 4)) * kLineVox;
+        dst_r[line + kLinePairs + col] = prc[r] - pis[r];
+        dst_i[line + kLinePairs + col] = pic[r] + prs[r];
+        dst_r[line + kLinePairs - 1 - col] = prc[r] + pis[r];
+        dst_i[line + kLinePairs - 1 - col] = pic[r] - prs[r];
     }
 }
 
@@ -519,59 +783,71 @@ int launch_pack(const float *kx, const float *ky, const float *kz, const float *
     return launch_status("fhd_pack_kernel launch");
 }
 
-// Workgroups of fhd_gather_kernel<kVox, true> that fit on one CU at once
-// (register and LDS budget), asked of the runtime once per device.
-int one_step_blocks_per_cu()
+// Workgroups of a gather instance that fit on one CU at once (register
+// and LDS budget), asked of the runtime once per device and instance.
+template <int KERNEL>
+int blocks_per_cu(const void *kernel, int block)
 {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 4;
     if (cached[dev] == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void *>(fhd_gather_kernel<kVox, true>), kBlock, 0) != hipSuccess ||
-            n < 1)
-            n = 4;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, 0) != hipSuccess || n < 1) n = 4;
         cached[dev] = n;
     }
     return cached[dev];
 }
 
 int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
-                  float *rho_r, float *rho_i, int N, hipStream_t stream)
+                  float *rho_r, float *rho_i, int N, hipStream_t stream, bool matrix_cores)
 {
     if (N == 0) return FHD_OK;
     const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
-    const int64_t per_block = (int64_t)kBlock * kVox;
-    const int64_t blocks = ((int64_t)N + per_block - 1) / per_block;
-    // sized for the one-step instance, the one that runs at length on grids
-    const int splits = split_count(blocks, nchunks, one_step_blocks_per_cu());
-    float *part = nullptr, *part_r = rho_r, *part_i = rho_i;
-    if (splits > 1) {
-        const hipError_t e = hipMallocAsync((void **)&part, (size_t)splits * 2 * N * sizeof(float), stream);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (split partials): ") +
-                                           hipGetErrorString(e));
-        }
-        part_r = part;
-        part_i = part + (int64_t)splits * N;
+    const int64_t blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
+    // sized for the matrix-core instance, the one that runs at length on
+    // grids
+    const int splits = split_count(
+        blocks, nchunks,
+        blocks_per_cu<0>(reinterpret_cast<const void *>(fhd_gather_lines_kernel), kLinesBlock));
+    // one workspace: the unit classes, then (splits > 1) the partial sums
+    const size_t cls_bytes = ((size_t)blocks * sizeof(int) + 255) / 256 * 256;
+    const size_t part_bytes = splits > 1 ? (size_t)splits * 2 * N * sizeof(float) : 0;
+    char *work = nullptr;
+    const hipError_t e = hipMallocAsync((void **)&work, cls_bytes + part_bytes, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (gather workspace): ") + hipGetErrorString(e));
     }
+    int *cls = reinterpret_cast<int *>(work);
+    float *part_r = rho_r, *part_i = rho_i;
+    if (splits > 1) {
+        part_r = reinterpret_cast<float *>(work + cls_bytes);
+        part_i = part_r + (int64_t)splits * N;
+    }
+    fhd_classify_kernel<<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(x, y, z, N, matrix_cores ? 1 : 0,
+                                                                              cls);
+    int rc = launch_status("fhd_classify_kernel launch");
     const dim3 grid((unsigned)blocks, (unsigned)splits);
-    fhd_gather_kernel<kVox, true><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, x, y, z,
-                                                                      part_r, part_i, N);
-    int rc = launch_status("fhd_gather_kernel<one step> launch");
+    if (rc == FHD_OK && matrix_cores) {
+        fhd_gather_lines_kernel<<<grid, dim3(kLinesBlock), 0, stream>>>(packed, nchunks, splits, cls, x, y,
+                                                                        z, part_r, part_i, N);
+        rc = launch_status("fhd_gather_lines_kernel launch");
+    }
     if (rc == FHD_OK) {
-        fhd_gather_kernel<kVox, false><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, x, y,
-                                                                           z, part_r, part_i, N);
+        fhd_gather_kernel<kVox, true><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, cls, x, y,
+                                                                          z, part_r, part_i, N);
+        rc = launch_status("fhd_gather_kernel<one step> launch");
+    }
+    if (rc == FHD_OK) {
+        fhd_gather_kernel<kVox, false><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, cls, x,
+                                                                           y, z, part_r, part_i, N);
         rc = launch_status("fhd_gather_kernel launch");
     }
-    if (splits > 1) {
-        if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, N, rho_r, rho_i, stream);
-        const hipError_t f = hipFreeAsync(part, stream);
-        if (f != hipSuccess && rc == FHD_OK)
-            rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
-    }
+    if (splits > 1 && rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, N, rho_r, rho_i, stream);
+    const hipError_t f = hipFreeAsync(work, stream);
+    if (f != hipSuccess && rc == FHD_OK)
+        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
     return rc;
 }
 
@@ -616,12 +892,15 @@ extern "C" int fhd_pack(const float *kx, const float *ky, const float *kz, const
     return launch_pack(kx, ky, kz, Dr, Di, M, (float *)packed, (hipStream_t)stream);
 }
 
-extern "C" int fhd_gather(const void *packed, int M, const float *x, const float *y, const float *z,
-                          float *rho_r, float *rho_i, int N, void *stream)
+extern "C" int fhd_gather_paths(const void *packed, int M, const float *x, const float *y,
+                                const float *z, float *rho_r, float *rho_i, int N, int paths,
+                                void *stream)
 {
     clear_error();
     if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
     if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
+    if (paths != FHD_GATHER_ALL && paths != FHD_GATHER_VECTOR)
+        return fail(FHD_ERR_INVALID_ARG, "paths must be FHD_GATHER_ALL or FHD_GATHER_VECTOR");
     if (N == 0) return FHD_OK;
     const int64_t nb = (int64_t)N * 4;
     const Span all[] = {{packed, M > 0 ? packed_bytes_for(M) : 0, "packed", 16},
@@ -631,7 +910,14 @@ extern "C" int fhd_gather(const void *packed, int M, const float *x, const float
     if (rc == FHD_OK) rc = check_no_overlap(all, 6, 4);
     if (rc == FHD_OK) rc = check_device_spans(all, 6);
     if (rc != FHD_OK) return rc;
-    return launch_gather((const float *)packed, M, x, y, z, rho_r, rho_i, N, (hipStream_t)stream);
+    return launch_gather((const float *)packed, M, x, y, z, rho_r, rho_i, N, (hipStream_t)stream,
+                         paths == FHD_GATHER_ALL);
+}
+
+extern "C" int fhd_gather(const void *packed, int M, const float *x, const float *y, const float *z,
+                          float *rho_r, float *rho_i, int N, void *stream)
+{
+    return fhd_gather_paths(packed, M, x, y, z, rho_r, rho_i, N, FHD_GATHER_ALL, stream);
 }
 
 extern "C" int fhd_compute(const float *kx, const float *ky, const float *kz, const float *Dr,

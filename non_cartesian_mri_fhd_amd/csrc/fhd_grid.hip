@@ -39,12 +39,6 @@
 namespace fhd {
 namespace {
 
-typedef float float16v __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef float float2v __attribute__((ext_vector_type(2)));
-
 constexpr int kTileYZ = 32;           // A rows per wave
 constexpr int kTilesX = 2;            // 32-column B tiles per wave
 constexpr int kWaves = kBlock / 64;   // 4 waves per workgroup, stacked along yz
@@ -152,32 +146,6 @@ __global__ __launch_bounds__(kBlock) void fhd_grid_kernel(
             }
         }
     }
-}
-
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both rounded to
-// nearest even: hi + lo carries 16 significant bits, x - (hi + lo) is
-// within 2^-17 |x|. Two values per v_cvt_pk_bf16_f32, packed as one dword
-// (element 2i in the low half); the bf16 hi parts widen back to fp32 by a
-// shift (low half) or a mask (high half).
-template <int E>
-__device__ __forceinline__ void split_bf16(const float (&x)[E], unsigned (&hi)[E / 2],
-                                           unsigned (&lo)[E / 2])
-{
-#pragma unroll
-    for (int i = 0; i < E / 2; ++i) {
-        const unsigned h = __builtin_bit_cast(
-            unsigned, __builtin_convertvector((float2v){x[2 * i], x[2 * i + 1]}, bf16x2));
-        const float h0 = __builtin_bit_cast(float, h << 16);
-        const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
-        hi[i] = h;
-        lo[i] = __builtin_bit_cast(
-            unsigned, __builtin_convertvector((float2v){x[2 * i] - h0, x[2 * i + 1] - h1}, bf16x2));
-    }
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const unsigned (&w)[4])
-{
-    return __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
 }
 
 // The same product with bf16 matrix-core instructions in three passes:

@@ -37,12 +37,10 @@ constexpr int kFields = 5;         // three coordinates, phase offset, amplitude
 constexpr int kChunkVec4 = kChunk * kFields / 4;        // 10 float4 per chunk
 constexpr int kStageChunks = 64;   // chunks per LDS stage (512 records, 10 KB)
 constexpr int kStageVec4 = kStageChunks * kChunkVec4;   // 640 float4
-constexpr int kStageLoads = (kStageVec4 + kBlock - 1) / kBlock;   // 3 per lane
 constexpr int kPackBlock = 256;
 
 static_assert(kBlock % 64 == 0, "workgroup must be whole wave64s");
 static_assert(kChunk * kFields % 4 == 0, "chunks must be whole float4s");
-static_assert(kStageLoads * kBlock >= kStageVec4, "a stage is at most kStageLoads float4 per lane");
 
 inline int64_t packed_bytes_for(int64_t count)
 {
@@ -77,15 +75,18 @@ __device__ __forceinline__ void load_chunk(const float4 *ch, float (&f)[kFields]
 }
 
 // Issues stage `st` of a packed stream of `total_vec4` float4 (starting at
-// src) into `dst` with buffer_load ... lds: each wave's 64 lanes copy 64
-// consecutive float4 straight into LDS at the wave's base (lane l at
-// base + l), with no registers in between. The buffer descriptor (SGPRs)
-// starts at the stage and ends at the stream's end or the stage's, so a
-// lane's offset is the same 32-bit value at every stage and reads past the
-// end return zeros. Complete once vmcnt reaches 0.
+// src) into `dst` with buffer_load ... lds, for a workgroup of BLOCK lanes:
+// each wave's 64 lanes copy 64 consecutive float4 straight into LDS at the
+// wave's base (lane l at base + l), with no registers in between. The
+// buffer descriptor (SGPRs) starts at the stage and ends at the stream's
+// end or the stage's, so a lane's offset is the same 32-bit value at every
+// stage and reads past the end return zeros. Complete once vmcnt reaches 0.
+template <int BLOCK = kBlock>
 __device__ __forceinline__ void issue_stage_load(const float4 *__restrict__ src, int64_t total_vec4,
                                                  int st, float4 *dst)
 {
+    static_assert(BLOCK % 64 == 0, "workgroup must be whole wave64s");
+    constexpr int loads = (kStageVec4 + BLOCK - 1) / BLOCK;
     const int wave_base = threadIdx.x & ~63;
     const int64_t first = (int64_t)st * kStageVec4;
     const int64_t left = total_vec4 - first;
@@ -93,11 +94,11 @@ __device__ __forceinline__ void issue_stage_load(const float4 *__restrict__ src,
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)(src + first), (short)0, bytes, 0x00020000);
 #pragma unroll
-    for (int k = 0; k < kStageLoads; ++k) {
-        const int i = k * kBlock + threadIdx.x;
+    for (int k = 0; k < loads; ++k) {
+        const int i = k * BLOCK + threadIdx.x;
         if (i < kStageVec4)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void *)(dst + k * kBlock + wave_base), 16,
+                rsrc, (__attribute__((address_space(3))) void *)(dst + k * BLOCK + wave_base), 16,
                 (unsigned)i * 16u, 0, 0, 0);
     }
 }
@@ -118,9 +119,9 @@ __device__ __forceinline__ void lds_barrier()
 // chunks of a stage, in order, in every lane: `chunks` points at the first
 // of them in LDS and `count` (1..STEP) says how many are valid (fewer only
 // at the end of the stream; the LDS beyond them holds stale data and must
-// not be read). Every lane of the workgroup must call it (it holds
-// workgroup barriers). Chunks past the end of `src` are never read.
-template <int STEP, typename Body>
+// not be read). Every lane of the workgroup (BLOCK lanes) must call it (it
+// holds workgroup barriers). Chunks past the end of `src` are never read.
+template <int STEP, int BLOCK = kBlock, typename Body>
 __device__ __forceinline__ void stream_chunk_groups(const float4 *__restrict__ src, int c_begin,
                                                     int c_end, float4 (*stage)[kStageVec4],
                                                     Body &&body)
@@ -131,14 +132,14 @@ __device__ __forceinline__ void stream_chunk_groups(const float4 *__restrict__ s
     const int64_t total_vec4 = (int64_t)nchunks * kChunkVec4;
     const int nstages = (nchunks + kStageChunks - 1) / kStageChunks;
     // stage st goes to stage[st & 1]
-    if (nstages > 0) issue_stage_load(src, total_vec4, 0, stage[0]);
+    if (nstages > 0) issue_stage_load<BLOCK>(src, total_vec4, 0, stage[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int st = 0; st < nstages; ++st) {
         // the next stage streams into the other buffer (last read before the
         // previous barrier) while this one is worked on
-        if (st + 1 < nstages) issue_stage_load(src, total_vec4, st + 1, stage[(st + 1) & 1]);
+        if (st + 1 < nstages) issue_stage_load<BLOCK>(src, total_vec4, st + 1, stage[(st + 1) & 1]);
         const int chunks_here = min(kStageChunks, nchunks - st * kStageChunks);
         const float4 *buf = stage[st & 1];
         for (int c = 0; c < chunks_here; c += STEP) body(buf + c * kChunkVec4, min(STEP, chunks_here - c));
@@ -166,6 +167,48 @@ __device__ __forceinline__ void split_range(int nchunks, int splits, int s, int 
     const int b = s * per * kStageChunks;
     *c_begin = min(b, nchunks);
     *c_end = min(b + per * kStageChunks, nchunks);
+}
+
+// ---------------------------------------------------------------------------
+// split-bf16 operands of the matrix cores
+// ---------------------------------------------------------------------------
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both rounded to
+// nearest even: hi + lo carries 16 significant bits, x - (hi + lo) is
+// within 2^-17 |x|. Two values per v_cvt_pk_bf16_f32, packed as one dword
+// (element 2i in the low half). x - hi comes from v_dot2c_f32_bf16 as
+// x + (-1) hi_0 + 0 hi_1 (or 0 hi_0 + (-1) hi_1): the products are exact
+// and so is the sum, x - hi being an fp32 value, so this equals the
+// subtraction of hi widened to fp32 in one instruction instead of two. The
+// constant pairs stay in VGPRs: as an inline constant, -1.0 is not read by
+// v_dot2c_f32_bf16 as the pair (-1, 0) the compiler encodes it for
+// (measured: every low result wrong; register operands exact).
+template <int E>
+__device__ __forceinline__ void split_bf16(const float (&x)[E], unsigned (&hi)[E / 2],
+                                           unsigned (&lo)[E / 2])
+{
+    unsigned c0 = 0x0000bf80u, c1 = 0xbf800000u;   // bf16 pairs (-1, 0) and (0, -1)
+    asm("" : "+v"(c0));
+    asm("" : "+v"(c1));
+    const bf16x2 first = __builtin_bit_cast(bf16x2, c0), second = __builtin_bit_cast(bf16x2, c1);
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+        const bf16x2 h = __builtin_convertvector((float2v){x[2 * i], x[2 * i + 1]}, bf16x2);
+        hi[i] = __builtin_bit_cast(unsigned, h);
+        const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, first, x[2 * i], false);
+        const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, second, x[2 * i + 1], false);
+        lo[i] = __builtin_bit_cast(unsigned, __builtin_convertvector((float2v){l0, l1}, bf16x2));
+    }
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const unsigned (&w)[4])
+{
+    return __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
 }
 
 // ---------------------------------------------------------------------------
@@ -211,8 +254,9 @@ int launch_reduce(const float *part_r, const float *part_i, int splits, int64_t 
 // fhd.hip: adjoint F^H D
 int launch_pack(const float *kx, const float *ky, const float *kz, const float *Dr, const float *Di,
                 int M, float *packed, hipStream_t stream);
+// matrix_cores = false keeps every unit on the vector-ALU paths.
 int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
-                  float *rho_r, float *rho_i, int N, hipStream_t stream);
+                  float *rho_r, float *rho_i, int N, hipStream_t stream, bool matrix_cores = true);
 // fhd_forward.hip: forward F
 int launch_forward_pack(const float *x, const float *y, const float *z, const float *rho_r,
                         const float *rho_i, int N, float *packed, hipStream_t stream);

@@ -40,13 +40,13 @@ def test_ramp_fraction_mirrors_the_kernel_test():
     swap = n.copy()
     swap[1::8], swap[2::8] = n[2::8], n[1::8]
     assert bench.ramp_voxel_fraction(x[swap], y[swap], z[swap]) == 0.0
-    # one voxel off the grid spoils its workgroup only (2048 voxels of 32768)
+    # one voxel off the grid spoils its unit only (4096 voxels of 32768)
     x2 = x.copy()
     x2[5000] += np.float32(1e-3)
-    assert bench.ramp_voxel_fraction(x2, y, z) == 1.0 - 2048 / L ** 3
-    # a partial last workgroup takes a direct path
+    assert bench.ramp_voxel_fraction(x2, y, z) == 1.0 - 4096 / L ** 3
+    # a partial last unit takes a direct path
     m = L ** 3 - 8
-    assert bench.ramp_voxel_fraction(x[:m], y[:m], z[:m]) == (L ** 3 - 2048) / m
+    assert bench.ramp_voxel_fraction(x[:m], y[:m], z[:m]) == (L ** 3 - 4096) / m
 
 
 def test_ramp_fractions_split_by_step():
@@ -60,11 +60,49 @@ def test_ramp_fractions_split_by_step():
     steps[block + 7] = np.float32(3.0 / 256)
     x = (x0[:, None] + np.arange(vox, dtype=np.float32)[None, :] * steps[:, None]).reshape(-1)
     y, z = (np.repeat(rng.uniform(-0.5, 0.5, lanes).astype(np.float32), vox) for _ in range(2))
-    assert bench.ramp_voxel_fractions(x, y, z, block, vox) == (0.5, 0.5)
+    assert bench.ramp_voxel_fractions(x, y, z, block, vox) == (0.0, 0.5, 0.5)
     assert bench.ramp_voxel_fraction(x, y, z, block, vox) == 1.0
     steps[block + 7] = np.float32(1.0 / 128)
     x = (x0[:, None] + np.arange(vox, dtype=np.float32)[None, :] * steps[:, None]).reshape(-1)
-    assert bench.ramp_voxel_fractions(x, y, z, block, vox) == (1.0, 0.0)
+    assert bench.ramp_voxel_fractions(x, y, z, block, vox) == (0.0, 1.0, 0.0)
+
+
+def test_gather_unit_classes_lines():
+    """Units of 4096 voxels whose aligned 64-voxel runs are lines along x
+    with one step take the matrix-core class (2); the same voxels with each
+    64-run made of 16-voxel pieces of four rows are one-step ramps (1); a
+    unit with one line of another step, a partial last unit and a z-fastest
+    order are class 0 (the first still all per-lane ramps)."""
+    from non_cartesian_mri_fhd_amd import inputs
+    ax = (-0.5, 1.0 / 64, -0.5, 1.0 / 16, -0.25, 1.0 / 32)
+    x, y, z = inputs.coords_from_axis(64, 16, 8, ax)
+    cls, all_ramp, counts = bench.gather_unit_classes(x, y, z)
+    assert cls.tolist() == [2, 2] and counts.tolist() == [4096, 4096]
+    # rows of 128: lines are half rows
+    x2, y2, z2 = inputs.coords_from_axis(128, 16, 4, (-0.5, 1.0 / 128, -0.5, 1.0 / 16, 0.0, 0.25))
+    assert bench.gather_unit_classes(x2, y2, z2)[0].tolist() == [2, 2]
+    # 64-runs of four rows' 16-voxel pieces
+    perm = np.arange(x.size).reshape(-1, 4, 4, 16).transpose(0, 2, 1, 3).reshape(-1)
+    assert bench.gather_unit_classes(x[perm], y[perm], z[perm])[0].tolist() == [1, 1]
+    assert bench.ramp_voxel_fractions(x[perm], y[perm], z[perm]) == (0.0, 1.0, 0.0)
+    # one line of the second unit at twice the step
+    xs = x.copy()
+    first = 4096 + 64 * 5
+    xs[first:first + 64] = (xs[first] + np.arange(64) * (2.0 / 64)).astype(np.float32)
+    cls, all_ramp, _ = bench.gather_unit_classes(xs, y, z)
+    assert cls.tolist() == [2, 0] and all_ramp.tolist() == [True, True]
+    assert bench.ramp_voxel_fractions(xs, y, z) == (0.5, 0.0, 0.5)
+    # a step of zero is a line too
+    x0 = np.full_like(x, np.float32(0.125))
+    assert bench.gather_unit_classes(x0, y, z)[0].tolist() == [2, 2]
+    # partial last unit
+    x3, y3, z3 = inputs.coords_from_axis(64, 16, 9, ax)
+    cls, all_ramp, counts = bench.gather_unit_classes(x3, y3, z3)
+    assert cls.tolist() == [2, 2, 0] and counts.tolist() == [4096, 4096, 1024]
+    assert not all_ramp[2]
+    # z fastest
+    n = np.arange(x.size).reshape(8, 16, 64).transpose(2, 1, 0).reshape(-1)
+    assert bench.gather_unit_classes(x[n], y[n], z[n])[0].tolist() == [0, 0]
 
 
 def test_roof_terms_mixes_paths():
