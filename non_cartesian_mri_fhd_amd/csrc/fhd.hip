@@ -635,6 +635,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP
 // with one LDS barrier (double buffered).
 constexpr int kLinesBlock = 128;                    // 2 waves
 constexpr int kLinePairs = kLineVox / 2;
+// stages of 32 chunks (5 KB, double buffered): with B's 8 KB the LDS holds
+// as many workgroups as the registers allow (3 waves per SIMD)
+constexpr int kLinesStageChunks = 32;
+constexpr int kLinesStageVec4 = kLinesStageChunks * kChunkVec4;
 static_assert(kLinePairs == 32, "the pairs fill one 32-column tile");
 static_assert(kUnitVox == 32 * kLineVox * (kLinesBlock / 64), "a wave takes 32 lines of the unit");
 static_assert(kLinesBlock / 64 == 2, "wave 0 forms B_C, wave 1 B_S");
@@ -645,7 +649,7 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
     float *__restrict__ out_r, float *__restrict__ out_i, int N)
 {
     if (cls[blockIdx.x] != kClassLines) return;
-    __shared__ float4 stage[2][kStageVec4];
+    __shared__ float4 stage[2][kLinesStageVec4];
     // [buffer][B_C hi, B_C lo, B_S hi, B_S lo][k half][pair]: one lane's
     // 8-sample operand each; a half-wave reads 32 consecutive entries
     __shared__ u32x4 bshare[2][4][2][kLinePairs];
@@ -671,12 +675,12 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
     }
 
     int c0, c1, kb = 0;
-    split_range(nchunks, splits, blockIdx.y, &c0, &c1);
+    split_range<kLinesStageChunks>(nchunks, splits, blockIdx.y, &c0, &c1);
     const int nch = c1 > c0 ? c1 - c0 : 0;
     src += (int64_t)c0 * kChunkVec4;
     const int64_t total_vec4 = (int64_t)nch * kChunkVec4;
-    const int nstages = (nch + kStageChunks - 1) / kStageChunks;
-    if (nstages > 0) issue_stage_load<kLinesBlock>(src, total_vec4, 0, stage[0]);
+    const int nstages = (nch + kLinesStageChunks - 1) / kLinesStageChunks;
+    if (nstages > 0) issue_stage_load<kLinesBlock, kLinesStageVec4>(src, total_vec4, 0, stage[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // one group of 16 samples: chunks ch and ch + 1 of the stage (the
@@ -741,14 +745,14 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
         kb ^= 1;
     };
     for (int st = 0; st < nstages; ++st) {
-        const int chunks_here = min(kStageChunks, nch - st * kStageChunks);
+        const int chunks_here = min(kLinesStageChunks, nch - st * kLinesStageChunks);
         const float4 *buf = stage[st & 1];
         for (int c = 0; c + 1 < chunks_here; c += 2) {
             group(buf + c * kChunkVec4, std::false_type{});
             // the next stage's copy goes out once the stage's first group
             // has passed its barrier, so no later barrier waits long for it
             if (c == 0 && st + 1 < nstages)
-                issue_stage_load<kLinesBlock>(src, total_vec4, st + 1, stage[(st + 1) & 1]);
+                issue_stage_load<kLinesBlock, kLinesStageVec4>(src, total_vec4, st + 1, stage[(st + 1) & 1]);
         }
         // an odd chunk at the stream's end (the last stage only)
         if (chunks_here & 1) group(buf + (chunks_here - 1) * kChunkVec4, std::true_type{});

@@ -75,28 +75,29 @@ __device__ __forceinline__ void load_chunk(const float4 *ch, float (&f)[kFields]
 }
 
 // Issues stage `st` of a packed stream of `total_vec4` float4 (starting at
-// src) into `dst` with buffer_load ... lds, for a workgroup of BLOCK lanes:
+// src; stages of STAGE_VEC4 float4) into `dst` with buffer_load ... lds, for
+// a workgroup of BLOCK lanes:
 // each wave's 64 lanes copy 64 consecutive float4 straight into LDS at the
 // wave's base (lane l at base + l), with no registers in between. The
 // buffer descriptor (SGPRs) starts at the stage and ends at the stream's
 // end or the stage's, so a lane's offset is the same 32-bit value at every
 // stage and reads past the end return zeros. Complete once vmcnt reaches 0.
-template <int BLOCK = kBlock>
+template <int BLOCK = kBlock, int STAGE_VEC4 = kStageVec4>
 __device__ __forceinline__ void issue_stage_load(const float4 *__restrict__ src, int64_t total_vec4,
                                                  int st, float4 *dst)
 {
     static_assert(BLOCK % 64 == 0, "workgroup must be whole wave64s");
-    constexpr int loads = (kStageVec4 + BLOCK - 1) / BLOCK;
+    constexpr int loads = (STAGE_VEC4 + BLOCK - 1) / BLOCK;
     const int wave_base = threadIdx.x & ~63;
-    const int64_t first = (int64_t)st * kStageVec4;
+    const int64_t first = (int64_t)st * STAGE_VEC4;
     const int64_t left = total_vec4 - first;
-    const int bytes = (int)(left < kStageVec4 ? left : kStageVec4) * 16;
+    const int bytes = (int)(left < STAGE_VEC4 ? left : STAGE_VEC4) * 16;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)(src + first), (short)0, bytes, 0x00020000);
 #pragma unroll
     for (int k = 0; k < loads; ++k) {
         const int i = k * BLOCK + threadIdx.x;
-        if (i < kStageVec4)
+        if (i < STAGE_VEC4)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc, (__attribute__((address_space(3))) void *)(dst + k * BLOCK + wave_base), 16,
                 (unsigned)i * 16u, 0, 0, 0);
@@ -158,15 +159,16 @@ __device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, in
 }
 
 // Chunk range of split `s` when nchunks chunks are cut into `splits` parts
-// of whole stages.
+// of whole stages of STAGE_CHUNKS chunks.
+template <int STAGE_CHUNKS = kStageChunks>
 __device__ __forceinline__ void split_range(int nchunks, int splits, int s, int *c_begin,
                                             int *c_end)
 {
-    const int stages = (nchunks + kStageChunks - 1) / kStageChunks;
+    const int stages = (nchunks + STAGE_CHUNKS - 1) / STAGE_CHUNKS;
     const int per = (stages + splits - 1) / splits;   // stages per split
-    const int b = s * per * kStageChunks;
+    const int b = s * per * STAGE_CHUNKS;
     *c_begin = min(b, nchunks);
-    *c_end = min(b + per * kStageChunks, nchunks);
+    *c_end = min(b + per * STAGE_CHUNKS, nchunks);
 }
 
 // ---------------------------------------------------------------------------
