@@ -153,15 +153,19 @@ def ramp_chunk_fractions(x, y, z) -> tuple[float, float]:
     return float(np.sum(ok16) * 16 / n), float(single * 8 / n)
 
 
-def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64):
-    """Per unit of block*vox consecutive voxels (one workgroup of each F^H D
-    gather instance), the class the gather's classify kernel gives it, by
-    the same tests: 2 when the unit is whole and every aligned run of `line`
-    voxels is a line along x (see _lane_ramps) with one step for the unit
-    (the matrix-core instance); else 1 when every lane's `vox` voxels are
-    such a ramp, all with one step (the ramp path with sample records);
-    else 0. Returned with, per unit, whether all its lanes are ramps (the
-    per-lane ramp path when the class is 0) and its voxel count."""
+def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64,
+                        long_line: int = 128):
+    """Per unit of block*vox consecutive voxels (one workgroup of the F^H D
+    gather's single-unit instances), the class its classify kernel gives
+    it, by the same tests (a line: see _lane_ramps): 3 when the unit and
+    the other unit of its aligned pair are whole and all their aligned runs
+    of `long_line` voxels are lines with one step for the pair (the
+    long-line matrix-core instance); else 2 when the unit is whole and its
+    aligned runs of `line` voxels are lines with one step (the matrix-core
+    instance); else 1 when every lane's `vox` voxels are such a ramp, all
+    with one step (the ramp path with sample records); else 0. Returned
+    with, per unit, whether all its lanes are ramps (the per-lane ramp path
+    when the class is 0) and its voxel count."""
     x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
     N = x.size
     unit = block * vox
@@ -169,7 +173,8 @@ def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64
     counts = np.minimum(unit, N - np.arange(units) * unit)
 
     def per_unit(per):
-        # groups of `per` voxels past N (a partial last unit) stay False
+        # groups of `per` voxels past N (a partial last unit) stay False;
+        # returns (all groups qualify, ... with one step, that step)
         ok, dx = _lane_ramps(x, y, z, per)
         n = units * (unit // per)
         o = np.zeros(n, bool)
@@ -179,24 +184,34 @@ def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64
         o = o.reshape(units, -1)
         S = st.view(np.uint32).reshape(units, -1)
         every = o.all(axis=1)
-        return every, every & np.all(S == S[:, :1], axis=1)
+        return every, every & np.all(S == S[:, :1], axis=1), S[:, 0]
 
-    all_ramp, one = per_unit(vox)
-    _, lines = per_unit(line)
-    lines &= counts == unit
-    cls = np.where(lines, 2, np.where(one, 1, 0))
+    whole = counts == unit
+    all_ramp, one, _ = per_unit(vox)
+    _, lines, _ = per_unit(line)
+    _, longl, step = per_unit(long_line)
+    lines &= whole
+    longl &= whole
+    pair = np.zeros(units, bool)
+    both = units // 2 * 2
+    if both:
+        ok = (longl[0:both:2] & longl[1:both:2] & (step[0:both:2] == step[1:both:2]))
+        pair[0:both:2] = ok
+        pair[1:both:2] = ok
+    cls = np.where(pair, 3, np.where(lines, 2, np.where(one, 1, 0)))
     return cls, all_ramp, counts
 
 
 def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16) -> tuple[float, float, float]:
     """Fractions of voxels by the F^H D gather path their unit takes (see
-    gather_unit_classes): (lines on the matrix cores, ramps with one step
-    for the workgroup, ramps with per-lane steps); the rest is direct."""
+    gather_unit_classes): (lines on the matrix cores, either instance; ramps
+    with one step for the workgroup; ramps with per-lane steps); the rest
+    is direct."""
     N = np.asarray(x).size
     if N == 0:
         return 0.0, 0.0, 0.0
     cls, all_ramp, counts = gather_unit_classes(x, y, z, block, vox)
-    return (float(np.sum(counts[cls == 2]) / N), float(np.sum(counts[cls == 1]) / N),
+    return (float(np.sum(counts[cls >= 2]) / N), float(np.sum(counts[cls == 1]) / N),
             float(np.sum(counts[(cls == 0) & all_ramp]) / N))
 
 

@@ -417,22 +417,28 @@ __device__ __forceinline__ void ramp_unfold(float (&acc_r)[V], float (&acc_i)[V]
 // Units and their classes
 // ---------------------------------------------------------------------------
 // Every gather instance takes voxels in units of kUnitVox consecutive
-// voxels (one workgroup each, the same grid for all). fhd_classify_kernel
-// tests each unit once and records which instance takes it:
-//   kClassLines   -- every aligned run of kLineVox voxels is one line along
-//                    x (same y and z bitwise, x_v = x_0 + v dx rounded once)
-//                    and all lines share dx bitwise (any x-fastest grid
-//                    whose rows are multiples of kLineVox voxels long): the
-//                    matrix-core instance;
-//   kClassOneStep -- otherwise, every lane's kVox voxels are such a ramp and
-//                    all lanes share the step: the ramp path with sample
-//                    records;
-//   kClassGeneral -- everything else (per-lane ramps, shared (y, z), direct).
+// voxels (a workgroup takes one unit, or an aligned pair of units). The
+// classify kernel tests each unit once and records which instance takes
+// it; a "line" is a run of voxels along x at a common step (same y and z
+// bitwise, x_v = x_0 + v dx rounded once), and the classes are
+//   kClassLongPair -- both units of an aligned pair are whole and their
+//                     aligned runs of kLongLineVox voxels are lines of one
+//                     step for the pair (any x-fastest grid whose rows are a
+//                     multiple of 128 voxels): the long-line matrix-core
+//                     instance, two units per workgroup;
+//   kClassLines    -- otherwise, the unit is whole and its aligned runs of
+//                     kLineVox voxels are lines of one step for the unit
+//                     (rows a multiple of 64): the matrix-core instance;
+//   kClassOneStep  -- otherwise, every lane's kVox voxels are such a ramp
+//                     and all lanes share the step: the ramp path with
+//                     sample records;
+//   kClassGeneral  -- everything else (per-lane ramps, shared (y, z), direct).
 constexpr int kUnitVox = kBlock * kVox;   // 4096 voxels
 constexpr int kLineVox = 64;              // voxels per line of the matrix-core instance
-enum : int { kClassGeneral = 0, kClassOneStep = 1, kClassLines = 2 };
-static_assert(kLineVox % kVox == 0 && 64 % (kLineVox / kVox) == 0,
-              "a line is whole lanes of one wave");
+constexpr int kLongLineVox = 128;         // and of the long-line instance
+enum : int { kClassGeneral = 0, kClassOneStep = 1, kClassLines = 2, kClassLongPair = 3 };
+static_assert(kLineVox % kVox == 0 && 64 % (kLineVox / kVox) == 0, "a line is whole lanes of one wave");
+static_assert(kLongLineVox % kVox == 0 && 64 % (kLongLineVox / kVox) == 0, "a line is whole lanes of one wave");
 
 // Lane l of workgroup b owns voxels (b kBlock + l) V + v, v < V. Voxels past
 // N copy the lane's first voxel, so they never spoil the shared-(y, z) test
@@ -481,15 +487,15 @@ __device__ __forceinline__ bool lane_ramp(const float (&px)[V], const float (&py
     return ramp;
 }
 
-// Whether the lane's voxels lie on the line of kLineVox voxels that its
-// group of kLineVox / V lanes forms: y and z equal to the line's first
-// voxel's bitwise and x_v = x_0 + v dx rounded once, dx = x_1 - x_0 of the
-// line; *dx gets the line's step.
-template <int V>
+// Whether the lane's voxels lie on the line of LINE voxels that its group
+// of LINE / V lanes forms: y and z equal to the line's first voxel's
+// bitwise and x_v = x_0 + v dx rounded once, dx = x_1 - x_0 of the line;
+// *dx gets the line's step.
+template <int LINE, int V>
 __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (&py)[V],
                                              const float (&pz)[V], float *dx)
 {
-    constexpr int kLanes = kLineVox / V;
+    constexpr int kLanes = LINE / V;
     const int lane = threadIdx.x & 63;
     const int lead = lane & ~(kLanes - 1);
     const float x0 = __shfl(px[0], lead), x1 = __shfl(px[1], lead);
@@ -505,33 +511,56 @@ __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (
     return ok;
 }
 
-// One workgroup per unit: cls[b] = the class of unit b (never kClassLines
-// unless allow_lines).
+// One workgroup per aligned pair of units (units 2b and 2b + 1 < units):
+// cls[u] = the class of unit u (never a matrix-core class unless
+// allow_lines).
 __global__ __launch_bounds__(kBlock) void fhd_classify_kernel(const float *__restrict__ x,
                                                               const float *__restrict__ y,
                                                               const float *__restrict__ z, int N,
-                                                              int allow_lines, int *__restrict__ cls)
+                                                              int64_t units, int allow_lines,
+                                                              int *__restrict__ cls)
 {
-    __shared__ float wg_dx, wg_ldx;
-    const int64_t unit = (int64_t)blockIdx.x * kUnitVox;
-    const int64_t n0 = unit + (int64_t)threadIdx.x * kVox;
-    float px[kVox], py[kVox], pz[kVox];
-    load_lane_voxels<kVox>(x, y, z, N, n0, px, py, pz);
-    bool same_yz;
-    float dx, ldx;
-    const bool ramp = lane_ramp<kVox>(px, py, pz, n0, N, &same_yz, &dx);
-    const bool on_line = allow_lines && lane_on_line<kVox>(px, py, pz, &ldx) && unit + kUnitVox <= N;
-    if (threadIdx.x == 0) {
-        wg_dx = dx;
-        wg_ldx = ldx;
+    __shared__ float wg_step[3];   // the unit's first lane's ramp step and line steps
+    int c[2] = {kClassGeneral, kClassGeneral};
+    bool long_lines[2] = {false, false};
+    float long_step[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int64_t u = 2 * (int64_t)blockIdx.x + k;
+        if (u >= units) break;   // uniform: the grid's last pair may hold one unit
+        const int64_t unit = u * kUnitVox;
+        const int64_t n0 = unit + (int64_t)threadIdx.x * kVox;
+        float px[kVox], py[kVox], pz[kVox];
+        load_lane_voxels<kVox>(x, y, z, N, n0, px, py, pz);
+        bool same_yz;
+        float dx, d64, d128;
+        const bool ramp = lane_ramp<kVox>(px, py, pz, n0, N, &same_yz, &dx);
+        const bool whole = unit + kUnitVox <= N;
+        const bool on64 = whole && lane_on_line<kLineVox, kVox>(px, py, pz, &d64);
+        const bool on128 = whole && lane_on_line<kLongLineVox, kVox>(px, py, pz, &d128);
+        if (threadIdx.x == 0) {
+            wg_step[0] = dx;
+            wg_step[1] = d64;
+            wg_step[2] = d128;
+        }
+        // every branch below is uniform over the workgroup, so each barrier
+        // is reached by every wave
+        const bool all_ramp = __syncthreads_and(ramp);
+        const bool all64 = __syncthreads_and(on64);
+        const bool all128 = __syncthreads_and(on128);
+        const bool one_step = all_ramp && __syncthreads_and(__float_as_uint(dx) == __float_as_uint(wg_step[0]));
+        const bool lines64 = all64 && __syncthreads_and(__float_as_uint(d64) == __float_as_uint(wg_step[1]));
+        long_lines[k] = all128 && __syncthreads_and(__float_as_uint(d128) == __float_as_uint(wg_step[2]));
+        long_step[k] = wg_step[2];
+        c[k] = allow_lines && lines64 ? kClassLines : one_step ? kClassOneStep : kClassGeneral;
+        __syncthreads();   // wg_step is read before the next unit writes it
     }
-    // every branch below is uniform over the workgroup, so each barrier is
-    // reached by every wave
-    const bool all_ramp = __syncthreads_and(ramp);
-    const bool all_line = __syncthreads_and(on_line);
-    const bool lines = all_line && __syncthreads_and(__float_as_uint(ldx) == __float_as_uint(wg_ldx));
-    const bool one_step = !lines && all_ramp && __syncthreads_and(__float_as_uint(dx) == __float_as_uint(wg_dx));
-    if (threadIdx.x == 0) cls[blockIdx.x] = lines ? kClassLines : one_step ? kClassOneStep : kClassGeneral;
+    const bool pair = allow_lines && long_lines[0] && long_lines[1] &&
+                      __float_as_uint(long_step[0]) == __float_as_uint(long_step[1]);
+    if (threadIdx.x < 2) {
+        const int64_t u = 2 * (int64_t)blockIdx.x + threadIdx.x;
+        if (u < units) cls[u] = pair ? kClassLongPair : threadIdx.x == 0 ? c[0] : c[1];
+    }
 }
 
 // Two VALU instances share the grid: ONE_STEP = true takes the units of
@@ -773,6 +802,184 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
     }
 }
 
+// ---------------------------------------------------------------------------
+// Long lines on the matrix cores
+// ---------------------------------------------------------------------------
+// An aligned pair of units of class kClassLongPair is 64 lines of
+// kLongLineVox voxels with one step: the same four real products as the
+// matrix-core instance above, with 64 pairs per line about the centre
+// x_0 + (kLongLineVox - 1) dx / 2 and the B factors of a sample shared by all
+// 64 lines of the workgroup. Per sample, the workgroup forms 64 U elements
+// and 128 B values for 8192 voxels (the single-unit form: 64 and 64 for
+// 4096), so the vector work per term is 36 % lower and matches the matrix
+// cores' 6 bf16 multiply-adds per term.
+//
+// Four waves of 16 lines each, on v_mfma_f32_16x16x32_bf16 (operand layout
+// measured: lane l supplies A[l % 16][8 (l / 16) + i] and B[8 (l / 16) +
+// i][l % 16], i < 8; accumulator register r of lane l holds C[4 (l / 16) +
+// r][l % 16]): per 32 samples (four chunks, chunk l / 16 for lane l) a lane
+// forms U of its line for its 8 samples and 16 B values -- wave w the
+// B_C (w < 2) or B_S (w >= 2, as a cosine a quarter turn later) elements of
+// pair tiles 2 (w % 2) and 2 (w % 2) + 1 for its pair l % 16 -- published
+// through LDS (double buffered, one barrier per 32 samples); each wave then
+// takes 4 pair tiles of 16: 48 products of 16 x 16 x 32.
+constexpr int kLongPairs = kLongLineVox / 2;       // 64
+constexpr int kLongTiles = kLongPairs / 16;        // 16-pair tiles
+constexpr int kPairVox = 2 * kUnitVox;             // voxels per workgroup
+constexpr int kLongBlock = 256;                    // 4 waves of 16 lines
+constexpr int kLongGroup = 4;                      // chunks per product step (32 samples)
+static_assert(kPairVox == kLongLineVox * 16 * (kLongBlock / 64), "a wave takes 16 lines of the pair");
+static_assert(kLongTiles == 4 && kLongBlock / 64 == 4, "each wave forms 2 tiles of B_C or B_S");
+static_assert(kLinesStageChunks % kLongGroup == 0, "product steps tile a stage");
+
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_long_lines_kernel(
+    const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
+    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
+    float *__restrict__ out_r, float *__restrict__ out_i, int N)
+{
+    if (cls[2 * (int64_t)blockIdx.x] != kClassLongPair) return;
+    __shared__ float4 stage[2][kLinesStageVec4];
+    // [buffer][B_C hi, B_C lo, B_S hi, B_S lo][tile][k quarter][pair in
+    // tile]: one lane's 8-sample operand each; a wave reads 64 consecutive
+    // entries (no bank conflicts)
+    __shared__ u32x4 bshare[2][4][kLongTiles][4][16];
+    const float4 *src = reinterpret_cast<const float4 *>(packed);
+    const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // line 16 wave + col of the pair (both units lie below N)
+    const int64_t base = (int64_t)blockIdx.x * kPairVox;
+    const int64_t first = base + (int64_t)(16 * wave + col) * kLongLineVox;
+    const float x0 = x[first], dx = x[first + 1] - x0, ly = y[first], lz = z[first];
+    const float xc = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x0);
+    // B role: B_C or B_S (a cosine a quarter turn later) for tiles t0, t0 + 1
+    const int part = wave >> 1, t0 = 2 * (wave & 1);
+    const float turn = part == 0 ? 0.0f : -0.25f;
+    const float tj0 = (float)(2 * (16 * t0 + col) + 1) * (0.5f * dx);
+    const float tj1 = (float)(2 * (16 * (t0 + 1) + col) + 1) * (0.5f * dx);
+
+    float4v prc[kLongTiles], pic[kLongTiles], pis[kLongTiles], prs[kLongTiles];
+#pragma unroll
+    for (int t = 0; t < kLongTiles; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            prc[t][r] = 0.0f;
+            pic[t][r] = 0.0f;
+            pis[t][r] = 0.0f;
+            prs[t][r] = 0.0f;
+        }
+
+    int c0, c1, kb = 0;
+    split_range<kLinesStageChunks>(nchunks, splits, blockIdx.y, &c0, &c1);
+    const int nch = c1 > c0 ? c1 - c0 : 0;
+    src += (int64_t)c0 * kChunkVec4;
+    const int64_t total_vec4 = (int64_t)nch * kChunkVec4;
+    const int nstages = (nch + kLinesStageChunks - 1) / kLinesStageChunks;
+
+    // one step of 32 samples: chunks ch .. ch + 3 of the stage, of which
+    // the first `count` hold samples (the others read as zeros, amplitude 0
+    // in B, when PARTIAL)
+    auto step = [&](const float4 *ch, int count, auto partial) {
+        float f[kFields][kChunk];
+        if constexpr (decltype(partial)::value) {
+            if (quarter_k < count) {
+                load_chunk(ch + quarter_k * kChunkVec4, f);
+            } else {
+#pragma unroll
+                for (int q = 0; q < kFields; ++q)
+#pragma unroll
+                    for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
+            }
+        } else {
+            load_chunk(ch + quarter_k * kChunkVec4, f);
+        }
+        __builtin_amdgcn_s_setprio(1);
+        float b0[kChunk], b1[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            b0[i] = f[4][i] * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj0, turn));
+            b1[i] = f[4][i] * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj1, turn));
+        }
+        unsigned h0[4], l0[4], h1[4], l1[4];
+        split_bf16<kChunk>(b0, h0, l0);
+        split_bf16<kChunk>(b1, h1, l1);
+        bshare[kb][2 * part + 0][t0][quarter_k][col] = (u32x4){h0[0], h0[1], h0[2], h0[3]};
+        bshare[kb][2 * part + 1][t0][quarter_k][col] = (u32x4){l0[0], l0[1], l0[2], l0[3]};
+        bshare[kb][2 * part + 0][t0 + 1][quarter_k][col] = (u32x4){h1[0], h1[1], h1[2], h1[3]};
+        bshare[kb][2 * part + 1][t0 + 1][quarter_k][col] = (u32x4){l1[0], l1[1], l1[2], l1[3]};
+        float ur[kChunk], ui[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const float p = __builtin_fmaf(f[0][i], xc, __builtin_fmaf(f[1][i], ly, __builtin_fmaf(f[2][i], lz, f[3][i])));
+            ur[i] = __builtin_amdgcn_cosf(p);
+            ui[i] = __builtin_amdgcn_sinf(p);
+        }
+        unsigned wa[4][4];
+        split_bf16<kChunk>(ur, wa[0], wa[1]);
+        split_bf16<kChunk>(ui, wa[2], wa[3]);
+        const bf16x8 arh = as_bf16x8(wa[0]), arl = as_bf16x8(wa[1]);
+        const bf16x8 aih = as_bf16x8(wa[2]), ail = as_bf16x8(wa[3]);
+        __builtin_amdgcn_s_setprio(0);
+        lds_barrier();   // this step's B is in LDS
+#pragma unroll
+        for (int t = 0; t < kLongTiles; ++t) {
+            const bf16x8 bch = __builtin_bit_cast(bf16x8, bshare[kb][0][t][quarter_k][col]);
+            const bf16x8 bcl = __builtin_bit_cast(bf16x8, bshare[kb][1][t][quarter_k][col]);
+            const bf16x8 bsh = __builtin_bit_cast(bf16x8, bshare[kb][2][t][quarter_k][col]);
+            const bf16x8 bsl = __builtin_bit_cast(bf16x8, bshare[kb][3][t][quarter_k][col]);
+            prc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bch, prc[t], 0, 0, 0);
+            pic[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bch, pic[t], 0, 0, 0);
+            pis[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bsh, pis[t], 0, 0, 0);
+            prs[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bsh, prs[t], 0, 0, 0);
+            prc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bcl, prc[t], 0, 0, 0);
+            pic[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bcl, pic[t], 0, 0, 0);
+            pis[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bsl, pis[t], 0, 0, 0);
+            prs[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bsl, prs[t], 0, 0, 0);
+            prc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arl, bch, prc[t], 0, 0, 0);
+            pic[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ail, bch, pic[t], 0, 0, 0);
+            pis[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ail, bsh, pis[t], 0, 0, 0);
+            prs[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arl, bsh, prs[t], 0, 0, 0);
+        }
+        kb ^= 1;
+    };
+
+    if (nstages > 0) issue_stage_load<kLongBlock, kLinesStageVec4>(src, total_vec4, 0, stage[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int st = 0; st < nstages; ++st) {
+        const int chunks_here = min(kLinesStageChunks, nch - st * kLinesStageChunks);
+        const float4 *buf = stage[st & 1];
+        int c = 0;
+        for (; c + kLongGroup <= chunks_here; c += kLongGroup) {
+            step(buf + c * kChunkVec4, kLongGroup, std::false_type{});
+            // the next stage's copy goes out once the stage's first step has
+            // passed its barrier, so no later barrier waits long for it
+            if (c == 0 && st + 1 < nstages)
+                issue_stage_load<kLongBlock, kLinesStageVec4>(src, total_vec4, st + 1, stage[(st + 1) & 1]);
+        }
+        // 1 to 3 chunks at the stream's end (the last stage only)
+        if (c < chunks_here) step(buf + c * kChunkVec4, chunks_here - c, std::true_type{});
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // unfold: row 4 (l / 16) + r of the wave's 16 lines, pair 16 t + l % 16
+    float *dst_r = out_r + (int64_t)blockIdx.y * N, *dst_i = out_i + (int64_t)blockIdx.y * N;
+#pragma unroll
+    for (int t = 0; t < kLongTiles; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t line = base + (int64_t)(16 * wave + 4 * quarter_k + r) * kLongLineVox;
+            const int j = 16 * t + col;
+            dst_r[line + kLongPairs + j] = prc[t][r] - pis[t][r];
+            dst_i[line + kLongPairs + j] = pic[t][r] + prs[t][r];
+            dst_r[line + kLongPairs - 1 - j] = prc[t][r] + pis[t][r];
+            dst_i[line + kLongPairs - 1 - j] = pic[t][r] - prs[t][r];
+        }
+}
+
 }  // namespace
 
 // Launches without argument checks; callers have checked.
@@ -809,11 +1016,12 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
     if (N == 0) return FHD_OK;
     const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
     const int64_t blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
-    // sized for the matrix-core instance, the one that runs at length on
-    // grids
+    const int64_t pairs = (blocks + 1) / 2;
+    // sized for the long-line instance, the one that runs at length on
+    // grids with rows of 128 voxels or more
     const int splits = split_count(
-        blocks, nchunks,
-        blocks_per_cu<0>(reinterpret_cast<const void *>(fhd_gather_lines_kernel), kLinesBlock));
+        pairs, nchunks,
+        blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel), kLongBlock));
     // one workspace: the unit classes, then (splits > 1) the partial sums
     const size_t cls_bytes = ((size_t)blocks * sizeof(int) + 255) / 256 * 256;
     const size_t part_bytes = splits > 1 ? (size_t)splits * 2 * N * sizeof(float) : 0;
@@ -829,10 +1037,15 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
         part_r = reinterpret_cast<float *>(work + cls_bytes);
         part_i = part_r + (int64_t)splits * N;
     }
-    fhd_classify_kernel<<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(x, y, z, N, matrix_cores ? 1 : 0,
-                                                                              cls);
+    fhd_classify_kernel<<<dim3((unsigned)pairs), dim3(kBlock), 0, stream>>>(x, y, z, N, blocks,
+                                                                             matrix_cores ? 1 : 0, cls);
     int rc = launch_status("fhd_classify_kernel launch");
     const dim3 grid((unsigned)blocks, (unsigned)splits);
+    if (rc == FHD_OK && matrix_cores) {
+        fhd_gather_long_lines_kernel<<<dim3((unsigned)pairs, (unsigned)splits), dim3(kLongBlock), 0, stream>>>(
+            packed, nchunks, splits, cls, x, y, z, part_r, part_i, N);
+        rc = launch_status("fhd_gather_long_lines_kernel launch");
+    }
     if (rc == FHD_OK && matrix_cores) {
         fhd_gather_lines_kernel<<<grid, dim3(kLinesBlock), 0, stream>>>(packed, nchunks, splits, cls, x, y,
                                                                         z, part_r, part_i, N);

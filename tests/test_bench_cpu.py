@@ -78,9 +78,16 @@ def test_gather_unit_classes_lines():
     x, y, z = inputs.coords_from_axis(64, 16, 8, ax)
     cls, all_ramp, counts = bench.gather_unit_classes(x, y, z)
     assert cls.tolist() == [2, 2] and counts.tolist() == [4096, 4096]
-    # rows of 128: lines are half rows
+    # rows of 128: pairs of units of 128-voxel lines
     x2, y2, z2 = inputs.coords_from_axis(128, 16, 4, (-0.5, 1.0 / 128, -0.5, 1.0 / 16, 0.0, 0.25))
-    assert bench.gather_unit_classes(x2, y2, z2)[0].tolist() == [2, 2]
+    assert bench.gather_unit_classes(x2, y2, z2)[0].tolist() == [3, 3]
+    # ... but not a pair whose units step differently, nor a lone last unit
+    x3, y3, z3 = inputs.coords_from_axis(128, 8, 4, (-0.5, 1.0 / 64, -0.5, 1.0 / 8, 0.0, 0.25))
+    xx, yy, zz = (np.concatenate(t) for t in ((x2[:4096], x3, x2), (y2[:4096], y3, y2), (z2[:4096], z3, z2)))
+    assert bench.gather_unit_classes(xx, yy, zz)[0].tolist() == [2, 2, 3, 3]
+    x4, y4, z4 = inputs.coords_from_axis(128, 32, 3, (-0.5, 1.0 / 128, -0.5, 1.0 / 32, 0.0, 0.25))
+    assert bench.gather_unit_classes(x4, y4, z4)[0].tolist() == [3, 3, 2]
+    assert bench.ramp_voxel_fractions(xx, yy, zz) == (1.0, 0.0, 0.0)
     # 64-runs of four rows' 16-voxel pieces
     perm = np.arange(x.size).reshape(-1, 4, 4, 16).transpose(0, 2, 1, 3).reshape(-1)
     assert bench.gather_unit_classes(x[perm], y[perm], z[perm])[0].tolist() == [1, 1]

@@ -56,18 +56,42 @@ def classes(case):
     return bench.gather_unit_classes(case["x"], case["y"], case["z"])[0].tolist()
 
 
-@pytest.mark.parametrize("shape,axis,M", [
-    ((64, 16, 8), AX64, 3000),                                        # lines = rows
-    ((128, 16, 4), (-0.5, 1.0 / 128, -0.5, 1.0 / 16, 0.0, 0.25), 1009),   # half rows, odd chunk count
-    ((64, 32, 6), (0.25, -1.0 / 64, -0.5, 1.0 / 32, -0.5, 1.0 / 8), 5),    # negative step, one chunk
-    ((256, 8, 4), (-0.5, 1.0 / 256, -0.5, 1.0 / 8, -0.5, 0.25), 1537),     # quarter rows, 3 stages + 1
+@pytest.mark.parametrize("shape,axis,M,cls", [
+    ((64, 16, 8), AX64, 3000, [2, 2]),                                     # lines = rows
+    ((128, 16, 4), (-0.5, 1.0 / 128, -0.5, 1.0 / 16, 0.0, 0.25), 1009, [3, 3]),   # tail of 3 chunks
+    ((64, 32, 6), (0.25, -1.0 / 64, -0.5, 1.0 / 32, -0.5, 1.0 / 8), 5, [2, 2, 2]),  # negative step, one chunk
+    ((256, 8, 4), (-0.5, 1.0 / 256, -0.5, 1.0 / 8, -0.5, 0.25), 1537, [3, 3]),    # half rows, 3 stages + 1
+    ((128, 32, 3), (-0.5, 1.0 / 128, -0.5, 1.0 / 32, 0.0, 0.25), 272, [3, 3, 2]),  # lone last unit, tail of 2
+    ((384, 8, 4), (-0.75, 1.0 / 256, -0.5, 1.0 / 8, -0.5, 0.25), 2000, [3, 3, 2]),
 ])
-def test_lines_grids(dev, shape, axis, M):
+def test_lines_grids(dev, shape, axis, M, cls):
     x, y, z = inputs.coords_from_axis(*shape, axis)
-    c = dict(inputs.random_case(1, M, seed=sum(shape) + M, kmax=shape[0] / 2.0), x=x, y=y, z=z)
-    assert set(classes(c)) == {2}
+    c = dict(inputs.random_case(1, M, seed=sum(shape) + M, kmax=min(shape[0], 256) / 2.0), x=x, y=y, z=z)
+    assert classes(c) == cls
     rr, ri = gpu_fhd(c, dev)
     check("lines %s M=%d" % (shape, M), c, rr, ri)
+
+
+def test_long_lines_against_lines(dev):
+    """Rows of 128 (the long-line instance, unit pairs) and the same voxels
+    with the two halves of every row swapped (64-voxel lines only: the
+    single-unit matrix-core instance) meet the oracle gate and agree to
+    rounding, not bitwise."""
+    k = inputs.make_kspace("spiral32")
+    x, y, z = inputs.coords_from_axis(128, 16, 4, (-0.5, 1.0 / 128, -0.5, 1.0 / 16, 0.0, 0.25))
+    perm = np.arange(x.size).reshape(-1, 2, 64)[:, ::-1, :].reshape(-1)
+    a = dict(k, x=x, y=y, z=z)
+    b = dict(k, x=x[perm], y=y[perm], z=z[perm])
+    assert classes(a) == [3, 3] and classes(b) == [2, 2]
+    ra = gpu_fhd(a, dev)
+    rb = gpu_fhd(b, dev)
+    check("long lines", a, *ra)
+    check("64-voxel lines", b, *rb)
+    back = (np.empty_like(rb[0]), np.empty_like(rb[1]))
+    back[0][perm], back[1][perm] = rb
+    diff = metrics.rel_l2(ra[0], ra[1], back[0].astype(np.float64), back[1].astype(np.float64))
+    print("long lines vs 64-voxel lines: rel diff %.2e" % diff)
+    assert 0 < diff < 1e-4
 
 
 def test_lines_spiral_kspace_and_ragged_tail(dev):
