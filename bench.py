@@ -285,7 +285,7 @@ def cpu_baseline(w: dict, name: str, target_s: float, rho_r, rho_i) -> tuple[dic
     from non_cartesian_mri_fhd_amd import inputs, metrics
     threads = oracle.default_threads()
     N, M = w["N"], w["M"]
-    probe = inputs.voxel_subset(N, 64, seed=4242)
+    probe = inputs.voxel_subset(N, 1024, seed=4242)
     t0 = time.perf_counter()
     oracle.fhd_subset(w, probe, threads=threads)
     rate = probe.size * M / (time.perf_counter() - t0)
@@ -443,7 +443,7 @@ def oracle_forward_sample(w: dict, name: str, target_s: float, Dr, Di, img):
     from non_cartesian_mri_fhd_amd import inputs, metrics
     threads = oracle.default_threads()
     N, M = w["N"], w["M"]
-    probe = inputs.voxel_subset(M, 16, seed=4243)
+    probe = inputs.voxel_subset(M, 128, seed=4243)
     t0 = time.perf_counter()
     oracle.forward(w["kx"][probe], w["ky"][probe], w["kz"][probe], img[0], img[1],
                    w["x"], w["y"], w["z"], threads=threads)

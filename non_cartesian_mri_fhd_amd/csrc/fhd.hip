@@ -513,12 +513,14 @@ __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (
 
 // One workgroup per aligned pair of units (units 2b and 2b + 1 < units):
 // cls[u] = the class of unit u (never a matrix-core class unless
-// allow_lines).
+// allow_lines); the first pair's workgroup also records whether that pair
+// is of class kClassLongPair (info[0]) and its lines' step (info[1], bits).
 __global__ __launch_bounds__(kBlock) void fhd_classify_kernel(const float *__restrict__ x,
                                                               const float *__restrict__ y,
                                                               const float *__restrict__ z, int N,
                                                               int64_t units, int allow_lines,
-                                                              int *__restrict__ cls)
+                                                              int *__restrict__ cls,
+                                                              int *__restrict__ info)
 {
     __shared__ float wg_step[3];   // the unit's first lane's ramp step and line steps
     int c[2] = {kClassGeneral, kClassGeneral};
@@ -560,6 +562,10 @@ __global__ __launch_bounds__(kBlock) void fhd_classify_kernel(const float *__res
     if (threadIdx.x < 2) {
         const int64_t u = 2 * (int64_t)blockIdx.x + threadIdx.x;
         if (u < units) cls[u] = pair ? kClassLongPair : threadIdx.x == 0 ? c[0] : c[1];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        info[0] = pair ? 1 : 0;
+        info[1] = (int)__float_as_uint(long_step[0]);
     }
 }
 
@@ -834,17 +840,86 @@ static_assert(kLinesStageChunks % kLongGroup == 0, "product steps tile a stage")
 
 typedef float float4v __attribute__((ext_vector_type(4)));
 
+// B operands of one product step (32 samples), laid out as the operands are
+// read: [B_C hi, B_C lo, B_S hi, B_S lo][tile][k quarter][pair in tile],
+// 8 bf16 (one lane's operand) each; a wave reads 64 consecutive entries
+// (no bank conflicts). 16 KB.
+constexpr int kLongStepVec4 = 4 * kLongTiles * 4 * 16;
+typedef u32x4 LongStepB[4][kLongTiles][4][16];
+
+// Lane (wave w, lane l) of a step's B: B_C (w < 2) or B_S (w >= 2, as a
+// cosine a quarter turn later) of pair tiles 2 (w % 2) and 2 (w % 2) + 1,
+// pair l % 16 of each, samples 8 (l / 16) .. + 7 (f: their chunk; dx: the
+// step of the lines), split and stored at their place in `dst`.
+__device__ __forceinline__ void long_step_b(const float (&f)[kFields][kChunk], float dx, int wave,
+                                            int quarter_k, int col, LongStepB &dst)
+{
+    const int part = wave >> 1, t0 = 2 * (wave & 1);
+    const float turn = part == 0 ? 0.0f : -0.25f;
+    const float tj0 = (float)(2 * (16 * t0 + col) + 1) * (0.5f * dx);
+    const float tj1 = (float)(2 * (16 * (t0 + 1) + col) + 1) * (0.5f * dx);
+    float b0[kChunk], b1[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        b0[i] = f[4][i] * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj0, turn));
+        b1[i] = f[4][i] * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj1, turn));
+    }
+    unsigned h0[4], l0[4], h1[4], l1[4];
+    split_bf16<kChunk>(b0, h0, l0);
+    split_bf16<kChunk>(b1, h1, l1);
+    dst[2 * part + 0][t0][quarter_k][col] = (u32x4){h0[0], h0[1], h0[2], h0[3]};
+    dst[2 * part + 1][t0][quarter_k][col] = (u32x4){l0[0], l0[1], l0[2], l0[3]};
+    dst[2 * part + 0][t0 + 1][quarter_k][col] = (u32x4){h1[0], h1[1], h1[2], h1[3]};
+    dst[2 * part + 1][t0 + 1][quarter_k][col] = (u32x4){l1[0], l1[1], l1[2], l1[3]};
+}
+
+// The B operands of every product step of the sample stream, formed once per
+// call for the step of the first pair of units when that pair is of class
+// kClassLongPair (info[0] = 1, info[1] = its step's bits, as the classify
+// kernel records them): step g at table + g kLongStepVec4, chunks past the
+// stream's end as zeros. The long-line workgroups whose lines have that
+// step copy them into LDS instead of forming them (same arithmetic, same
+// bits).
+__global__ __launch_bounds__(kLongBlock) void fhd_long_table_kernel(const float *__restrict__ packed, int nchunks,
+                                                                    const int *__restrict__ info,
+                                                                    float4 *__restrict__ table)
+{
+    if (info[0] == 0) return;
+    const float dx = __int_as_float(info[1]);
+    const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t chunk = (int64_t)blockIdx.x * kLongGroup + quarter_k;
+    float f[kFields][kChunk];
+    if (chunk < nchunks) {
+        const float4 *c = reinterpret_cast<const float4 *>(packed) + chunk * kChunkVec4;
+#pragma unroll
+        for (int q = 0; q < kChunkVec4; ++q) {
+            const float4 t = c[q];
+            const int field = (4 * q) / kChunk, at = (4 * q) % kChunk;
+            f[field][at + 0] = t.x;
+            f[field][at + 1] = t.y;
+            f[field][at + 2] = t.z;
+            f[field][at + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kFields; ++q)
+#pragma unroll
+            for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
+    }
+    long_step_b(f, dx, wave, quarter_k, col,
+                *reinterpret_cast<LongStepB *>(table + (int64_t)blockIdx.x * kLongStepVec4));
+}
+
 __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_long_lines_kernel(
     const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
+    const int *__restrict__ info, const float4 *__restrict__ table,
     const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
     float *__restrict__ out_r, float *__restrict__ out_i, int N)
 {
     if (cls[2 * (int64_t)blockIdx.x] != kClassLongPair) return;
     __shared__ float4 stage[2][kLinesStageVec4];
-    // [buffer][B_C hi, B_C lo, B_S hi, B_S lo][tile][k quarter][pair in
-    // tile]: one lane's 8-sample operand each; a wave reads 64 consecutive
-    // entries (no bank conflicts)
-    __shared__ u32x4 bshare[2][4][kLongTiles][4][16];
+    __shared__ LongStepB bshare[2];
     const float4 *src = reinterpret_cast<const float4 *>(packed);
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -854,11 +929,8 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
     const int64_t first = base + (int64_t)(16 * wave + col) * kLongLineVox;
     const float x0 = x[first], dx = x[first + 1] - x0, ly = y[first], lz = z[first];
     const float xc = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x0);
-    // B role: B_C or B_S (a cosine a quarter turn later) for tiles t0, t0 + 1
-    const int part = wave >> 1, t0 = 2 * (wave & 1);
-    const float turn = part == 0 ? 0.0f : -0.25f;
-    const float tj0 = (float)(2 * (16 * t0 + col) + 1) * (0.5f * dx);
-    const float tj1 = (float)(2 * (16 * (t0 + 1) + col) + 1) * (0.5f * dx);
+    // every line of the pair has the step dx (bitwise), so this is uniform
+    const bool use_table = info[0] != 0 && __float_as_uint(dx) == (unsigned)info[1];
 
     float4v prc[kLongTiles], pic[kLongTiles], pis[kLongTiles], prs[kLongTiles];
 #pragma unroll
@@ -877,11 +949,16 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
     src += (int64_t)c0 * kChunkVec4;
     const int64_t total_vec4 = (int64_t)nch * kChunkVec4;
     const int nstages = (nch + kLinesStageChunks - 1) / kLinesStageChunks;
+    const int64_t table_vec4 = (((int64_t)nchunks + kLongGroup - 1) / kLongGroup) * kLongStepVec4;
+    const int g0 = c0 / kLongGroup;   // the split's first product step (splits are whole stages)
 
-    // one step of 32 samples: chunks ch .. ch + 3 of the stage, of which
-    // the first `count` hold samples (the others read as zeros, amplitude 0
-    // in B, when PARTIAL)
-    auto step = [&](const float4 *ch, int count, auto partial) {
+    // One step of 32 samples: chunks ch .. ch + 3 of the stage, of which the
+    // first `count` hold samples (the others read as zeros, amplitude 0 in
+    // B, when PARTIAL). TABLE: this step's B was copied into bshare[kb]
+    // during the previous step; the next step's (step g + 1) goes out once
+    // this one's barrier is passed.
+    auto step = [&](const float4 *ch, int count, int g, auto partial, auto from_table) {
+        constexpr bool kTable = decltype(from_table)::value;
         float f[kFields][kChunk];
         if constexpr (decltype(partial)::value) {
             if (quarter_k < count) {
@@ -896,19 +973,7 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
             load_chunk(ch + quarter_k * kChunkVec4, f);
         }
         __builtin_amdgcn_s_setprio(1);
-        float b0[kChunk], b1[kChunk];
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            b0[i] = f[4][i] * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj0, turn));
-            b1[i] = f[4][i] * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj1, turn));
-        }
-        unsigned h0[4], l0[4], h1[4], l1[4];
-        split_bf16<kChunk>(b0, h0, l0);
-        split_bf16<kChunk>(b1, h1, l1);
-        bshare[kb][2 * part + 0][t0][quarter_k][col] = (u32x4){h0[0], h0[1], h0[2], h0[3]};
-        bshare[kb][2 * part + 1][t0][quarter_k][col] = (u32x4){l0[0], l0[1], l0[2], l0[3]};
-        bshare[kb][2 * part + 0][t0 + 1][quarter_k][col] = (u32x4){h1[0], h1[1], h1[2], h1[3]};
-        bshare[kb][2 * part + 1][t0 + 1][quarter_k][col] = (u32x4){l1[0], l1[1], l1[2], l1[3]};
+        if constexpr (!kTable) long_step_b(f, dx, wave, quarter_k, col, bshare[kb]);
         float ur[kChunk], ui[kChunk];
 #pragma unroll
         for (int i = 0; i < kChunk; ++i) {
@@ -923,6 +988,11 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
         const bf16x8 aih = as_bf16x8(wa[2]), ail = as_bf16x8(wa[3]);
         __builtin_amdgcn_s_setprio(0);
         lds_barrier();   // this step's B is in LDS
+        // bshare[kb ^ 1] was last read before the barrier just passed
+        if constexpr (kTable)
+            if ((int64_t)(g + 1) * kLongStepVec4 < table_vec4)
+                issue_stage_load<kLongBlock, kLongStepVec4>(table, table_vec4, g + 1,
+                                                             reinterpret_cast<float4 *>(&bshare[kb ^ 1]));
 #pragma unroll
         for (int t = 0; t < kLongTiles; ++t) {
             const bf16x8 bch = __builtin_bit_cast(bf16x8, bshare[kb][0][t][quarter_k][col]);
@@ -945,25 +1015,38 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
         kb ^= 1;
     };
 
-    if (nstages > 0) issue_stage_load<kLongBlock, kLinesStageVec4>(src, total_vec4, 0, stage[0]);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int st = 0; st < nstages; ++st) {
-        const int chunks_here = min(kLinesStageChunks, nch - st * kLinesStageChunks);
-        const float4 *buf = stage[st & 1];
-        int c = 0;
-        for (; c + kLongGroup <= chunks_here; c += kLongGroup) {
-            step(buf + c * kChunkVec4, kLongGroup, std::false_type{});
-            // the next stage's copy goes out once the stage's first step has
-            // passed its barrier, so no later barrier waits long for it
-            if (c == 0 && st + 1 < nstages)
-                issue_stage_load<kLongBlock, kLinesStageVec4>(src, total_vec4, st + 1, stage[(st + 1) & 1]);
+    auto walk = [&](auto from_table) {
+        if (nstages > 0) {
+            issue_stage_load<kLongBlock, kLinesStageVec4>(src, total_vec4, 0, stage[0]);
+            if constexpr (decltype(from_table)::value)
+                issue_stage_load<kLongBlock, kLongStepVec4>(table, table_vec4, g0,
+                                                             reinterpret_cast<float4 *>(&bshare[0]));
         }
-        // 1 to 3 chunks at the stream's end (the last stage only)
-        if (c < chunks_here) step(buf + c * kChunkVec4, chunks_here - c, std::true_type{});
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-    }
+        for (int st = 0; st < nstages; ++st) {
+            const int chunks_here = min(kLinesStageChunks, nch - st * kLinesStageChunks);
+            const float4 *buf = stage[st & 1];
+            const int gs = g0 + st * (kLinesStageChunks / kLongGroup);
+            int c = 0;
+            for (; c + kLongGroup <= chunks_here; c += kLongGroup) {
+                step(buf + c * kChunkVec4, kLongGroup, gs + c / kLongGroup, std::false_type{}, from_table);
+                // the next stage's copy goes out once the stage's first step
+                // has passed its barrier, so no later barrier waits long for it
+                if (c == 0 && st + 1 < nstages)
+                    issue_stage_load<kLongBlock, kLinesStageVec4>(src, total_vec4, st + 1, stage[(st + 1) & 1]);
+            }
+            // 1 to 3 chunks at the stream's end (the last stage only)
+            if (c < chunks_here)
+                step(buf + c * kChunkVec4, chunks_here - c, gs + c / kLongGroup, std::true_type{}, from_table);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    };
+    if (use_table)
+        walk(std::true_type{});
+    else
+        walk(std::false_type{});
 
     // unfold: row 4 (l / 16) + r of the wave's 16 lines, pair 16 t + l % 16
     float *dst_r = out_r + (int64_t)blockIdx.y * N, *dst_i = out_i + (int64_t)blockIdx.y * N;
@@ -1022,28 +1105,39 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
     const int splits = split_count(
         pairs, nchunks,
         blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel), kLongBlock));
-    // one workspace: the unit classes, then (splits > 1) the partial sums
-    const size_t cls_bytes = ((size_t)blocks * sizeof(int) + 255) / 256 * 256;
+    // one workspace: the unit classes and the B-table record, the B table
+    // of the long-line instance (16 KB per 32 samples), then (splits > 1)
+    // the partial sums
+    const size_t cls_bytes = ((size_t)blocks * sizeof(int) + 2 * sizeof(int) + 255) / 256 * 256;
+    const int64_t steps = ((int64_t)nchunks + kLongGroup - 1) / kLongGroup;
+    const size_t table_bytes = matrix_cores ? (size_t)steps * kLongStepVec4 * sizeof(float4) : 0;
     const size_t part_bytes = splits > 1 ? (size_t)splits * 2 * N * sizeof(float) : 0;
     char *work = nullptr;
-    const hipError_t e = hipMallocAsync((void **)&work, cls_bytes + part_bytes, stream);
+    const hipError_t e = hipMallocAsync((void **)&work, cls_bytes + table_bytes + part_bytes, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (gather workspace): ") + hipGetErrorString(e));
     }
     int *cls = reinterpret_cast<int *>(work);
+    int *info = cls + blocks;
+    float4 *table = reinterpret_cast<float4 *>(work + cls_bytes);
     float *part_r = rho_r, *part_i = rho_i;
     if (splits > 1) {
-        part_r = reinterpret_cast<float *>(work + cls_bytes);
+        part_r = reinterpret_cast<float *>(work + cls_bytes + table_bytes);
         part_i = part_r + (int64_t)splits * N;
     }
     fhd_classify_kernel<<<dim3((unsigned)pairs), dim3(kBlock), 0, stream>>>(x, y, z, N, blocks,
-                                                                             matrix_cores ? 1 : 0, cls);
+                                                                             matrix_cores ? 1 : 0, cls, info);
     int rc = launch_status("fhd_classify_kernel launch");
     const dim3 grid((unsigned)blocks, (unsigned)splits);
+    if (rc == FHD_OK && matrix_cores && steps > 0) {
+        fhd_long_table_kernel<<<dim3((unsigned)steps), dim3(kLongBlock), 0, stream>>>(packed, nchunks, info,
+                                                                                      table);
+        rc = launch_status("fhd_long_table_kernel launch");
+    }
     if (rc == FHD_OK && matrix_cores) {
         fhd_gather_long_lines_kernel<<<dim3((unsigned)pairs, (unsigned)splits), dim3(kLongBlock), 0, stream>>>(
-            packed, nchunks, splits, cls, x, y, z, part_r, part_i, N);
+            packed, nchunks, splits, cls, info, table, x, y, z, part_r, part_i, N);
         rc = launch_status("fhd_gather_long_lines_kernel launch");
     }
     if (rc == FHD_OK && matrix_cores) {

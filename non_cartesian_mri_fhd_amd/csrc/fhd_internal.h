@@ -90,8 +90,8 @@ __device__ __forceinline__ void issue_stage_load(const float4 *__restrict__ src,
     constexpr int loads = (STAGE_VEC4 + BLOCK - 1) / BLOCK;
     const int wave_base = threadIdx.x & ~63;
     const int64_t first = (int64_t)st * STAGE_VEC4;
-    const int64_t left = total_vec4 - first;
-    const int bytes = (int)(left < STAGE_VEC4 ? left : STAGE_VEC4) * 16;
+    const int64_t left = total_vec4 - first;   // callers pass st with left > 0
+    const int bytes = (int)(left <= 0 ? 0 : left < STAGE_VEC4 ? left : STAGE_VEC4) * 16;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)(src + first), (short)0, bytes, 0x00020000);
 #pragma unroll

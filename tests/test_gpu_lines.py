@@ -220,3 +220,23 @@ def test_gather_paths_rejects_unknown_mode(dev):
                               out[0].data_ptr(), out[1].data_ptr(), x.numel(), 2, None)
     assert rc == binding.FHD_ERR_INVALID_ARG
     assert b"paths" in ctypes.string_at(lib.fhd_last_error())
+
+
+def test_long_lines_table_and_in_kernel_factors_agree_bitwise(dev):
+    """The long-line instance takes its B factors from a table formed once
+    per call for the first pair's step, and forms them itself in pairs of
+    another step: the same arithmetic either way. Two pairs of units (steps
+    1/128 and 1/256) in both orders: each pair's result is bitwise the same
+    whichever way its factors were formed."""
+    ga = inputs.coords_from_axis(128, 16, 4, (-0.5, 1.0 / 128, -0.5, 1.0 / 16, 0.0, 0.25))
+    gb = inputs.coords_from_axis(128, 16, 4, (-0.25, 1.0 / 256, -0.5, 1.0 / 16, 0.125, 0.25))
+    k = inputs.make_kspace("spiral32")
+    one = dict(k, **{n: np.concatenate((a, b)) for n, a, b in zip("xyz", ga, gb)})
+    two = dict(k, **{n: np.concatenate((b, a)) for n, a, b in zip("xyz", ga, gb)})
+    assert classes(one) == [3, 3, 3, 3] and classes(two) == [3, 3, 3, 3]
+    r1 = gpu_fhd(one, dev)
+    r2 = gpu_fhd(two, dev)
+    check("two steps", one, *r1)
+    h = ga[0].size
+    for p in range(2):
+        assert np.array_equal(r1[p][:h], r2[p][h:]) and np.array_equal(r1[p][h:], r2[p][:h])
