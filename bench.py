@@ -154,7 +154,7 @@ def ramp_chunk_fractions(x, y, z) -> tuple[float, float]:
 
 
 def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64,
-                        long_line: int = 128):
+                        long_line: int = 128, allow_lines: bool = True):
     """Per unit of block*vox consecutive voxels (one workgroup of the F^H D
     gather's single-unit instances), the class its classify kernel gives
     it, by the same tests (a line: see _lane_ramps): 3 when the unit and
@@ -165,7 +165,8 @@ def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64
     instance); else 1 when every lane's `vox` voxels are such a ramp, all
     with one step (the ramp path with sample records); else 0. Returned
     with, per unit, whether all its lanes are ramps (the per-lane ramp path
-    when the class is 0) and its voxel count."""
+    when the class is 0) and its voxel count. allow_lines=False mirrors
+    FHD_GATHER_VECTOR (no unit takes a matrix-core class)."""
     x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
     N = x.size
     unit = block * vox
@@ -190,8 +191,8 @@ def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64
     all_ramp, one, _ = per_unit(vox)
     _, lines, _ = per_unit(line)
     _, longl, step = per_unit(long_line)
-    lines &= whole
-    longl &= whole
+    lines &= whole & allow_lines
+    longl &= whole & allow_lines
     pair = np.zeros(units, bool)
     both = units // 2 * 2
     if both:
@@ -202,7 +203,8 @@ def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64
     return cls, all_ramp, counts
 
 
-def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16) -> tuple[float, float, float]:
+def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16,
+                         allow_lines: bool = True) -> tuple[float, float, float]:
     """Fractions of voxels by the F^H D gather path their unit takes (see
     gather_unit_classes): (lines on the matrix cores, either instance; ramps
     with one step for the workgroup; ramps with per-lane steps); the rest
@@ -210,7 +212,7 @@ def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16) -> tuple[floa
     N = np.asarray(x).size
     if N == 0:
         return 0.0, 0.0, 0.0
-    cls, all_ramp, counts = gather_unit_classes(x, y, z, block, vox)
+    cls, all_ramp, counts = gather_unit_classes(x, y, z, block, vox, allow_lines=allow_lines)
     return (float(np.sum(counts[cls >= 2]) / N), float(np.sum(counts[cls == 1]) / N),
             float(np.sum(counts[(cls == 0) & all_ramp]) / N))
 
@@ -225,19 +227,19 @@ def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 16) -> float:
 # readings (factors 2.0 and 1.0). Valid only for the sources they were taken
 # on (SHA-256 over the listed files, in order); any later edit reports null
 # until the counters are taken again.
-#   fhd  (fhd_gather_kernel<16, true>): 108.2 MiB read (x, y, z by each of
-#        the 5 sample splits, the packed samples once per XCD L2, a few
-#        spilled registers) + 92.5 MiB written (5 split partial sums of rho)
-#   grid (fhd_grid_kernel):   15.4 MiB read (packed samples once per XCD L2)
+#   fhd  (fhd_gather_long_lines_kernel): 414.3 MiB read (the 48.8 MiB B
+#        table about once per XCD L2, the packed samples, x, y, z) + 48.1
+#        MiB written (3 split partial sums of rho)
+#   grid (fhd_grid_kernel):   15.6 MiB read (packed samples once per XCD L2)
 #        + 48.0 MiB written (3 split partial sums of rho)
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
     "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
-            "sha256": "c3544d9a046c2646323e6a51543a1578e517cf0cfb0dee608f419bf8dfb91c43",
-            "bytes_per_launch": (55374.0 * 2.0 + 94720 * 1.0) * 1024},
+            "sha256": "65c51340ff0ca67f909b105e264121042c39a026e7bd9e91c3aa85c67b8a9a90",
+            "bytes_per_launch": (212134.0 * 2.0 + 49246 * 1.0) * 1024},
     "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
-             "sha256": "3cb2fe5084067543b1ff691ab4411b30773a609f83b0dbb3710a77f0fa69fa14",
-             "bytes_per_launch": (7876.0 * 2.0 + 49152 * 1.0) * 1024},
+             "sha256": "9888524503e259259b3d4de5019911087d974ceb47876f8b21ad17f945d0d7f8",
+             "bytes_per_launch": (7965.4 * 2.0 + 49152 * 1.0) * 1024},
 }
 
 
@@ -261,6 +263,9 @@ def parse(argv=None):
     ap.add_argument("--workload", default="spiral128")
     ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid", "grid_bf16x3",
                                                        "forward_grid", "normal_grid", "cg_grid"])
+    ap.add_argument("--paths", default="all", choices=["all", "vector"],
+                    help="F^H D gather paths (--op fhd): all (fhd_gather: lines on the matrix cores) "
+                         "or vector (fhd_gather_paths with FHD_GATHER_VECTOR: the fp32 VALU paths only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -331,9 +336,12 @@ def main(argv=None) -> int:
     rho_r = torch.empty(N, dtype=torch.float32, device=dev)
     rho_i = torch.empty(N, dtype=torch.float32, device=dev)
 
+    paths = None if args.paths == "all" else binding.FHD_GATHER_VECTOR
+    other = binding.FHD_GATHER_VECTOR if args.paths == "all" else binding.FHD_GATHER_ALL
+
     def step():
         binding.fhd_pack(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], packed)
-        binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], rho_r, rho_i)
+        binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], rho_r, rho_i, paths=paths)
 
     for _ in range(args.warmup):
         step()
@@ -347,7 +355,7 @@ def main(argv=None) -> int:
         e[0].record(stream)
         binding.fhd_pack(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], packed)
         e[1].record(stream)
-        binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], rho_r, rho_i)
+        binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], rho_r, rho_i, paths=paths)
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -355,20 +363,19 @@ def main(argv=None) -> int:
     ms_step = wall * 1e3 / args.steps
     gather_all = np.array([e[1].elapsed_time(e[2]) for e in ev])
 
-    # the same gather held to the vector-ALU fp32 paths (fhd_gather_paths,
-    # FHD_GATHER_VECTOR), timed beside it: the evidence that the
-    # matrix-core form of lines beats the VALU form on this workload
-    vec_r = torch.empty_like(rho_r)
-    vec_i = torch.empty_like(rho_i)
-    binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], vec_r, vec_i, paths=binding.FHD_GATHER_VECTOR)
+    # the same gather with the other choice of paths, timed beside it: by
+    # default the vector-ALU fp32 paths (FHD_GATHER_VECTOR), the evidence
+    # that the matrix-core form of lines beats the VALU form here
+    alt_r = torch.empty_like(rho_r)
+    alt_i = torch.empty_like(rho_i)
+    binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], alt_r, alt_i, paths=other)
     vev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)]
     for e in vev:
         e[0].record(stream)
-        binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], vec_r, vec_i,
-                           paths=binding.FHD_GATHER_VECTOR)
+        binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], alt_r, alt_i, paths=other)
         e[1].record(stream)
     torch.cuda.synchronize()
-    vec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in vev]))
+    alt_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in vev]))
     gather_ms = float(np.mean(gather_all))
     pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     terms = float(N) * float(M)
@@ -377,11 +384,16 @@ def main(argv=None) -> int:
 
     # the ceiling for the paths this voxel layout takes (the x-fastest
     # grids of the workloads: the ramp path throughout)
-    lines, one, lane = ramp_voxel_fractions(w["x"], w["y"], w["z"], cfg["block_threads"],
-                                            cfg["voxels_per_lane"])
-    roof = roof_terms([(terms * lines, ROOF_TERMS_LINES), (terms * one, ROOF_TERMS_RAMP),
-                       (terms * lane, ROOF_TERMS_RAMP_LANE),
-                       (terms * (1 - lines - one - lane), ROOF_TERMS)])
+    def ceiling(allow_lines):
+        fr = ramp_voxel_fractions(w["x"], w["y"], w["z"], cfg["block_threads"], cfg["voxels_per_lane"],
+                                  allow_lines=allow_lines)
+        ln, on, la = fr
+        return fr, roof_terms([(terms * ln, ROOF_TERMS_LINES), (terms * on, ROOF_TERMS_RAMP),
+                               (terms * la, ROOF_TERMS_RAMP_LANE),
+                               (terms * (1 - ln - on - la), ROOF_TERMS)])
+
+    (lines, one, lane), roof = ceiling(args.paths == "all")
+    _, alt_roof = ceiling(args.paths != "all")
     rate = terms / (gather_ms * 1e-3)
     if lines == 1.0:
         # every unit on the matrix cores: bf16 FLOP against the bf16 peak
@@ -419,14 +431,14 @@ def main(argv=None) -> int:
                       "fhd_gather_kernel_median": float(np.median(gather_all)),
                       "fhd_gather_kernel_min": float(np.min(gather_all))},
         "gflops_13_per_term": FLOP_PER_TERM * value / 1e9,
-        "vector_paths_only": {
-            "note": "fhd_gather_paths(FHD_GATHER_VECTOR): every unit on the fp32 VALU paths",
-            "gather_ms": vec_ms, "terms_per_s": terms / (vec_ms * 1e-3),
-            "matrix_core_speedup": vec_ms / gather_ms,
-            "frac_of_valu_ceiling": terms / (vec_ms * 1e-3) / roof_terms(
-                [(terms * (lines + one), ROOF_TERMS_RAMP), (terms * lane, ROOF_TERMS_RAMP_LANE),
-                 (terms * (1 - lines - one - lane), ROOF_TERMS)])},
+        ("vector_paths_only" if args.paths == "all" else "all_paths"): {
+            "note": ("fhd_gather_paths(FHD_GATHER_VECTOR): every unit on the fp32 VALU paths"
+                     if args.paths == "all" else "fhd_gather: lines on the matrix cores"),
+            "gather_ms": alt_ms, "terms_per_s": terms / (alt_ms * 1e-3),
+            "speedup_of_the_timed_paths": alt_ms / gather_ms,
+            "frac_of_its_ceiling": terms / (alt_ms * 1e-3) / alt_roof},
     }
+    out["config"]["paths"] = args.paths
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, args.workload, args.cpu_seconds,
                                     rho_r.cpu().numpy(), rho_i.cpu().numpy())

@@ -50,6 +50,15 @@
 // Per voxel-sample term: direct paths, phase 1 + 2/kVox FMA (3 FMA on the
 // general path), v_cos_f32, v_sin_f32, 2 FMA accumulate; ramp path, 2/kVox
 // transcendentals and 35/kVox VALU operations (shared step).
+//
+//  * fhd_classify_kernel -- tests every unit of 4096 voxels once per call and
+//    records which instance takes it. Units whose voxels form lines along x
+//    at one step (every x-fastest grid with rows of a multiple of 64) go to
+//    the matrix-core instances, fhd_gather_long_lines_kernel (lines of 128,
+//    two units per workgroup) and fhd_gather_lines_kernel (lines of 64):
+//    the voxels pair up about each line's centre and the sum becomes real
+//    matrix products (lines x samples)(samples x pairs) in split bf16 (see
+//    "Lines on the matrix cores" below); the rest go to fhd_gather_kernel.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -1100,11 +1109,15 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
     const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
     const int64_t blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
     const int64_t pairs = (blocks + 1) / 2;
-    // sized for the long-line instance, the one that runs at length on
-    // grids with rows of 128 voxels or more
-    const int splits = split_count(
-        pairs, nchunks,
-        blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel), kLongBlock));
+    // sized for the instance that runs at length on grids: the long-line one
+    // (rows of 128 voxels or more), or with the vector paths only the
+    // one-step ramp path
+    const int splits =
+        matrix_cores
+            ? split_count(pairs, nchunks,
+                          blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel), kLongBlock))
+            : split_count(blocks, nchunks,
+                          blocks_per_cu<2>(reinterpret_cast<const void *>(fhd_gather_kernel<kVox, true>), kBlock));
     // one workspace: the unit classes and the B-table record, the B table
     // of the long-line instance (16 KB per 32 samples), then (splits > 1)
     // the partial sums
