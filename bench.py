@@ -217,6 +217,18 @@ def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16,
             float(np.sum(counts[(cls == 0) & all_ramp]) / N))
 
 
+def forward_lines_form(x, y, z, block: int = 256, vox: int = 16, long_line: int = 128) -> bool:
+    """Whether fhd_forward takes its matrix-core line form, by the same
+    rule: a whole number of unit pairs, every unit of class 3, and one step
+    for every line of `long_line` voxels."""
+    N = np.asarray(x).size
+    if N == 0 or N % (2 * block * vox) != 0:
+        return False
+    cls = gather_unit_classes(x, y, z, block, vox)[0]
+    ok, dx = _lane_ramps(x, y, z, long_line)
+    return bool(np.all(cls == 3) and dx.size and np.all(dx.view(np.uint32) == dx.view(np.uint32)[0]))
+
+
 def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 16) -> float:
     """Fraction of voxels on a ramp path, any form (lines included)."""
     return sum(ramp_voxel_fractions(x, y, z, block, vox))
@@ -264,8 +276,10 @@ def parse(argv=None):
     ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid", "grid_bf16x3",
                                                        "forward_grid", "normal_grid", "cg_grid"])
     ap.add_argument("--paths", default="all", choices=["all", "vector"],
-                    help="F^H D gather paths (--op fhd): all (fhd_gather: lines on the matrix cores) "
-                         "or vector (fhd_gather_paths with FHD_GATHER_VECTOR: the fp32 VALU paths only)")
+                    help="paths (--op fhd): all (fhd_gather: lines on the matrix cores) or vector "
+                         "(fhd_gather_paths with FHD_GATHER_VECTOR: the fp32 VALU paths only); "
+                         "--op forward --paths vector times fhd_forward_pack + fhd_forward_gather, "
+                         "the vector form of F")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -495,7 +509,8 @@ def bench_other(args) -> int:
     # launch stream around its dominant kernel (None where one call covers it)
     dominant = None
     k_iters = 3
-    if args.op == "forward":
+    if args.op == "forward" and args.paths == "vector":
+        # the two-stage entry points, which are always the vector form
         Dr = torch.empty(M, device=dev)
         Di = torch.empty(M, device=dev)
         vox = binding.new_packed(N, dev)
@@ -506,6 +521,16 @@ def bench_other(args) -> int:
         def main_kernel():
             binding.fhd_forward_gather(vox, N, t["kx"], t["ky"], t["kz"], Dr, Di)
         dominant = "fhd_forward_gather_kernel"
+        terms_per_step = float(N) * M
+    elif args.op == "forward":
+        Dr = torch.empty(M, device=dev)
+        Di = torch.empty(M, device=dev)
+
+        def pre():
+            pass
+
+        def main_kernel():
+            binding.fhd_forward(t["kx"], t["ky"], t["kz"], t["x"], t["y"], t["z"], img[0], img[1], Dr, Di)
         terms_per_step = float(N) * M
     elif args.op in ("grid", "grid_bf16x3"):
         precision = binding.FHD_GRID_BF16X3 if args.op == "grid_bf16x3" else binding.FHD_GRID_FP32
@@ -608,13 +633,15 @@ def bench_other(args) -> int:
     ramp_f16, ramp_f = ramp_chunk_fractions(w["x"], w["y"], w["z"])
     adjoint = {"normal": 1, "cg": 1 + k_iters}.get(args.op, 0)
     forward_terms = {"forward": 1, "normal": 1, "cg": k_iters}.get(args.op, 0)
+    f_lines = 1.0 if args.paths == "all" and forward_lines_form(w["x"], w["y"], w["z"]) else 0.0
     roof = roof_terms([(adjoint * NM * lines, ROOF_TERMS_LINES),
                        (adjoint * NM * one, ROOF_TERMS_RAMP),
                        (adjoint * NM * lane, ROOF_TERMS_RAMP_LANE),
                        (adjoint * NM * (1 - lines - one - lane), ROOF_TERMS),
-                       (forward_terms * NM * ramp_f16, ROOF_TERMS_RAMP_F16),
-                       (forward_terms * NM * ramp_f, ROOF_TERMS_RAMP_F),
-                       (forward_terms * NM * (1 - ramp_f16 - ramp_f), ROOF_TERMS)])
+                       (forward_terms * NM * f_lines, ROOF_TERMS_LINES),
+                       (forward_terms * NM * (1 - f_lines) * ramp_f16, ROOF_TERMS_RAMP_F16),
+                       (forward_terms * NM * (1 - f_lines) * ramp_f, ROOF_TERMS_RAMP_F),
+                       (forward_terms * NM * (1 - f_lines) * (1 - ramp_f16 - ramp_f), ROOF_TERMS)])
     out = {
         "metric": "%s voxel-sample terms/s (%s)" % (args.op, args.workload),
         "value": value, "unit": "terms/s", "n_gpus": 1, "steps": args.steps,
@@ -628,6 +655,13 @@ def bench_other(args) -> int:
         "kernel_ms": {"timed": dominant or "whole call", "mean": float(np.mean(kms)),
                       "median": float(np.median(kms)), "min": float(np.min(kms))},
     }
+    if args.op in ("forward", "normal", "cg") and (adjoint == 0 or lines == 1.0) and \
+            (forward_terms == 0 or f_lines == 1.0):
+        # every term on the bf16 matrix cores (both operators in line form)
+        out["roofline"] = {"bound": "mfma", "achieved": LINES_FLOP_PER_TERM * k_rate / 1e12,
+                           "peak": P_MFMA_BF16 / 1e12, "unit": "TFLOP/s",
+                           "frac": k_rate / roof, "traffic": None}
+        out["dtype"] = "bf16x3 (fp32 accumulation)"
     if args.op == "grid":
         # one complex multiply-add per term on the fp32 matrix cores
         achieved = MFMA_FLOP_PER_TERM * k_rate

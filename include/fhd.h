@@ -146,6 +146,14 @@ int fhd_gather_paths(const void *packed, int M,
  *   Dr, Di             : M fp32 values each (written), not overlapping any
  *                        input
  *   M = 0 does nothing; N = 0 writes zeros (an empty sum).
+ * When every aligned pair of 4096-voxel units consists of lines of 128
+ * voxels along x with one common step (same y and z bitwise, x_v = x_0 +
+ * v dx rounded once; any x-fastest grid whose rows are a multiple of 128
+ * voxels and whose voxel count is a multiple of 8192), F runs on the
+ * matrix cores in split bf16 (about 1e-5 relative); otherwise on the
+ * vector ALUs in fp32 (the form fhd_forward_pack / fhd_forward_gather
+ * always take). The choice is made on the device; the library allocates
+ * its stream-ordered workspaces on `stream`.
  * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
  */
 int fhd_forward(const float *kx, const float *ky, const float *kz,
@@ -184,7 +192,9 @@ int fhd_forward_gather(const void *packed, int N,
  * iteration (section 17.2; split by loop fission into F and F^H, section
  * 17.3.2). Runs F into a k-space temporary and F^H back, all in one
  * stream-ordered workspace of fhd_packed_bytes(N) + fhd_packed_bytes(M) +
- * 8*M bytes.
+ * 8*M bytes (plus the smaller ones fhd_forward and fhd_gather take). F and
+ * F^H each take their matrix-core form where fhd_forward and fhd_gather
+ * would.
  *   kx, ky, kz       : M fp32 values each (read only)
  *   x, y, z, p_r/_i  : N fp32 values each (read only)
  *   q_r, q_i         : N fp32 values each (written), not overlapping any

@@ -141,8 +141,10 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float *__restr
                                                             const float *__restrict__ part_i,
                                                             int splits, int64_t n,
                                                             float *__restrict__ out_r,
-                                                            float *__restrict__ out_i)
+                                                            float *__restrict__ out_i,
+                                                            const int *__restrict__ gate, int gate_want)
 {
+    if (gate != nullptr && lines_form_ran(gate) != (gate_want != 0)) return;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     float sr = 0.0f, si = 0.0f;
@@ -157,11 +159,11 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float *__restr
 }  // namespace
 
 int launch_reduce(const float *part_r, const float *part_i, int splits, int64_t n, float *out_r,
-                  float *out_i, hipStream_t stream)
+                  float *out_i, hipStream_t stream, const int *gate, bool gate_want)
 {
     if (n == 0) return FHD_OK;
     reduce_splits_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(
-        part_r, part_i, splits, n, out_r, out_i);
+        part_r, part_i, splits, n, out_r, out_i, gate, gate_want ? 1 : 0);
     return launch_status("reduce_splits_kernel launch");
 }
 

@@ -442,10 +442,7 @@ __device__ __forceinline__ void ramp_unfold(float (&acc_r)[V], float (&acc_i)[V]
 //                     and all lanes share the step: the ramp path with
 //                     sample records;
 //   kClassGeneral  -- everything else (per-lane ramps, shared (y, z), direct).
-constexpr int kUnitVox = kBlock * kVox;   // 4096 voxels
-constexpr int kLineVox = 64;              // voxels per line of the matrix-core instance
-constexpr int kLongLineVox = 128;         // and of the long-line instance
-enum : int { kClassGeneral = 0, kClassOneStep = 1, kClassLines = 2, kClassLongPair = 3 };
+static_assert(kUnitVox == kBlock * kVox, "a unit is one workgroup of the vector instances");
 static_assert(kLineVox % kVox == 0 && 64 % (kLineVox / kVox) == 0, "a line is whole lanes of one wave");
 static_assert(kLongLineVox % kVox == 0 && 64 % (kLongLineVox / kVox) == 0, "a line is whole lanes of one wave");
 
@@ -523,7 +520,8 @@ __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (
 // One workgroup per aligned pair of units (units 2b and 2b + 1 < units):
 // cls[u] = the class of unit u (never a matrix-core class unless
 // allow_lines); the first pair's workgroup also records whether that pair
-// is of class kClassLongPair (info[0]) and its lines' step (info[1], bits).
+// is of class kClassLongPair (info[0]) and its lines' step (info[1], bits),
+// and clears info[2] (a flag the forward operator's line pre-pass sets).
 __global__ __launch_bounds__(kBlock) void fhd_classify_kernel(const float *__restrict__ x,
                                                               const float *__restrict__ y,
                                                               const float *__restrict__ z, int N,
@@ -575,6 +573,7 @@ __global__ __launch_bounds__(kBlock) void fhd_classify_kernel(const float *__res
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         info[0] = pair ? 1 : 0;
         info[1] = (int)__float_as_uint(long_step[0]);
+        info[2] = 0;
     }
 }
 
@@ -1102,6 +1101,16 @@ int blocks_per_cu(const void *kernel, int block)
     return cached[dev];
 }
 
+int launch_classify(const float *x, const float *y, const float *z, int N, bool allow_lines, int *cls,
+                    int *info, hipStream_t stream)
+{
+    const int64_t blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
+    const int64_t pairs = (blocks + 1) / 2;
+    fhd_classify_kernel<<<dim3((unsigned)pairs), dim3(kBlock), 0, stream>>>(x, y, z, N, blocks,
+                                                                             allow_lines ? 1 : 0, cls, info);
+    return launch_status("fhd_classify_kernel launch");
+}
+
 int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
                   float *rho_r, float *rho_i, int N, hipStream_t stream, bool matrix_cores)
 {
@@ -1139,9 +1148,7 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
         part_r = reinterpret_cast<float *>(work + cls_bytes + table_bytes);
         part_i = part_r + (int64_t)splits * N;
     }
-    fhd_classify_kernel<<<dim3((unsigned)pairs), dim3(kBlock), 0, stream>>>(x, y, z, N, blocks,
-                                                                             matrix_cores ? 1 : 0, cls, info);
-    int rc = launch_status("fhd_classify_kernel launch");
+    int rc = launch_classify(x, y, z, N, matrix_cores, cls, info, stream);
     const dim3 grid((unsigned)blocks, (unsigned)splits);
     if (rc == FHD_OK && matrix_cores && steps > 0) {
         fhd_long_table_kernel<<<dim3((unsigned)steps), dim3(kLongBlock), 0, stream>>>(packed, nchunks, info,

@@ -185,8 +185,7 @@ int dot(const float *ur, const float *ui, const float *vr, const float *vi, int6
 int normal(const float *kx, const float *ky, const float *kz, const float *x, const float *y,
            const float *z, int M, int N, const CgWork &w, hipStream_t s)
 {
-    int rc = launch_forward_pack(x, y, z, w.p_r, w.p_i, N, w.vox, s);
-    if (rc == FHD_OK) rc = launch_forward_gather(w.vox, N, kx, ky, kz, w.d_r, w.d_i, M, s);
+    int rc = launch_forward(x, y, z, w.p_r, w.p_i, N, kx, ky, kz, w.d_r, w.d_i, M, w.vox, s);
     if (rc == FHD_OK) rc = launch_pack(kx, ky, kz, w.d_r, w.d_i, M, w.smp, s);
     if (rc == FHD_OK) rc = launch_gather(w.smp, M, x, y, z, w.ap_r, w.ap_i, N, s);
     return rc;

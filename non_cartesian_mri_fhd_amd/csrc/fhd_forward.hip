@@ -54,8 +54,9 @@ static_assert(kSamp % kRampGroup == 0, "ramp groups tile a lane's samples");
 __global__ __launch_bounds__(kPackBlock) void fhd_forward_pack_kernel(
     const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
     const float *__restrict__ rho_r, const float *__restrict__ rho_i,
-    float *__restrict__ packed, int N, int64_t N_pad)
+    float *__restrict__ packed, int N, int64_t N_pad, const int *__restrict__ gate)
 {
+    if (gate != nullptr && lines_form_ran(gate)) return;   // the line form took F
     // every lane stays to the end: the ramp test exchanges values between
     // the 8 lanes of a chunk (a chunk never straddles N_pad or a wave)
     const int64_t n = (int64_t)blockIdx.x * kPackBlock + threadIdx.x;
@@ -319,8 +320,9 @@ template <int S>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void fhd_forward_gather_kernel(
     const float *__restrict__ packed, int nchunks, int splits,
     const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
-    float *__restrict__ out_r, float *__restrict__ out_i, int M)
+    float *__restrict__ out_r, float *__restrict__ out_i, int M, const int *__restrict__ gate)
 {
+    if (gate != nullptr && lines_form_ran(gate)) return;   // the line form took F
     __shared__ float4 stage[2][kStageVec4];
     const float4 *src = reinterpret_cast<const float4 *>(packed);
 
@@ -386,21 +388,248 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     }
 }
 
+// ---------------------------------------------------------------------------
+// F on lines of voxels, on the matrix cores
+// ---------------------------------------------------------------------------
+// When the voxels are lines of kLongLineVox along x with one step dx (every
+// aligned pair of units of class kClassLongPair, one step throughout), the
+// voxels of a line pair up about its centre x_c = x_0 + (kLongLineVox - 1)
+// dx / 2, and with rho+_j, rho-_j the voxels at x_c +- (j + 1/2) dx,
+//
+//   D_m = sum_l conj(V[l, m]) T[l, m],   V = exp(i 2 pi k_m . x_c(l))
+//   T[l, m] = sum_j (P_j C_j(m) - i Q_j S_j(m)),
+//   P_j = rho+_j + rho-_j, Q_j = rho+_j - rho-_j,
+//   C_j, S_j = cos, sin(2 pi (2j + 1) kx_m dx / 2),
+//
+// i.e. T_re = sum_K A_re[l, K] B[K, m], T_im = sum_K A_im[l, K] B[K, m]
+// over K = (j, cos part) then (j, sin part), with A_re = [P_r | Q_i],
+// A_im = [P_i | -Q_r], B = [C | S]: two real products with K = 2 x 64, in
+// split bf16 (three bf16 products per fp32 product, fp32 accumulation), 6
+// bf16 multiply-adds per term; then per line and sample one phasor (2
+// transcendentals for 128 terms) and a complex multiply-add.
+//
+// fhd_forward_lines_pack_kernel forms A once per call, in operand order,
+// in tiles of 16 lines; fhd_forward_lines_kernel gives each wave 32
+// samples (two 16-sample columns of v_mfma_f32_16x16x32_bf16, layout:
+// lane l supplies A[l % 16][8 (l / 16) + i] and B[8 (l / 16) + i][l % 16],
+// accumulator register r holds C[4 (l / 16) + r][l % 16]), keeps their B
+// operands in registers, and walks the tiles of its split through LDS.
+constexpr int kFwdBlock = 256;                          // 4 waves
+constexpr int kFwdTileLines = 16;
+constexpr int kFwdPairs = kLongLineVox / 2;             // 64
+constexpr int kFwdKSteps = 2 * kFwdPairs / 32;          // 4 products of K = 32
+constexpr int kFwdOpsVec4 = kFwdKSteps * 4 * 64;        // [k step][re hi, re lo, im hi, im lo][lane]
+constexpr int kFwdTileVec4 = kFwdOpsVec4 + kFwdTileLines;   // then (x_c, y, z, 0) per line
+constexpr int kFwdTileVox = kFwdTileLines * kLongLineVox;
+constexpr int kFwdColumns = 2;                          // 16-sample columns per wave
+constexpr int kFwdBlockSamples = (kFwdBlock / 64) * 16 * kFwdColumns;
+constexpr int kFwdStageRegs = (kFwdTileVec4 + kFwdBlock - 1) / kFwdBlock;
+static_assert(kFwdBlock / 64 == kFwdKSteps, "one pre-pass wave per k step");
+static_assert((2 * kUnitVox) % kFwdTileVox == 0, "tiles tile a pair of units");
+
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// One workgroup per tile of 16 lines: wave s forms k step s of the A
+// operands (lane l: line l % 16, K = 32 s + 8 (l / 16) + i), the first 16
+// lanes of wave 0 the lines' centres; a line that breaks the rule (its unit
+// pair not of class kClassLongPair, or a step other than the first pair's)
+// sets info[2], and the vector form then takes F.
+__global__ __launch_bounds__(kFwdBlock) void fhd_forward_lines_pack_kernel(
+    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
+    const float *__restrict__ rho_r, const float *__restrict__ rho_i, const int *__restrict__ cls,
+    int *__restrict__ info, u32x4 *__restrict__ tiles)
+{
+    const int s = threadIdx.x >> 6, lane = threadIdx.x & 63, row = lane & 15, quarter_k = lane >> 4;
+    const int64_t base = ((int64_t)blockIdx.x * kFwdTileLines + row) * kLongLineVox;
+    const bool sine = s >= kFwdKSteps / 2;   // K >= 64: the S part
+    float re[kChunk], im[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        const int j = (32 * s + 8 * quarter_k + i) % kFwdPairs;
+        const int64_t up = base + kFwdPairs + j, dn = base + kFwdPairs - 1 - j;
+        const float ur = rho_r[up], ui = rho_i[up], dr = rho_r[dn], di = rho_i[dn];
+        re[i] = sine ? ui - di : ur + dr;      // Q_i | P_r
+        im[i] = sine ? dr - ur : ui + di;      // -Q_r | P_i
+    }
+    unsigned rh[4], rl[4], ih[4], il[4];
+    split_bf16<kChunk>(re, rh, rl);
+    split_bf16<kChunk>(im, ih, il);
+    u32x4 *t = tiles + (int64_t)blockIdx.x * kFwdTileVec4 + s * 4 * 64 + lane;
+    t[0 * 64] = (u32x4){rh[0], rh[1], rh[2], rh[3]};
+    t[1 * 64] = (u32x4){rl[0], rl[1], rl[2], rl[3]};
+    t[2 * 64] = (u32x4){ih[0], ih[1], ih[2], ih[3]};
+    t[3 * 64] = (u32x4){il[0], il[1], il[2], il[3]};
+    if (s == 0 && quarter_k == 0) {
+        const float x0 = x[base], dx = x[base + 1] - x0;
+        const float xc = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x0);
+        tiles[(int64_t)blockIdx.x * kFwdTileVec4 + kFwdOpsVec4 + row] =
+            (u32x4){__float_as_uint(xc), __float_as_uint(y[base]), __float_as_uint(z[base]), 0u};
+        const bool ok = info[0] != 0 && cls[base / kUnitVox] == kClassLongPair &&
+                        __float_as_uint(dx) == (unsigned)info[1];
+        if (!ok) atomicOr(&info[2], 1);
+    }
+}
+
+// Workgroup b, split s: samples b kFwdBlockSamples .. + 127 (wave w the 32
+// from 32 w; lane l the sample l % 16 of each of its two columns, rows 4
+// (l / 16) .. + 3 of each tile), tiles of split s of the line stream; writes
+// D (splits == 1) or its partial sums at out + s M.
+__global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_forward_lines_kernel(
+    const u32x4 *__restrict__ tiles, int ntiles, int splits, const int *__restrict__ info,
+    const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
+    float *__restrict__ out_r, float *__restrict__ out_i, int M)
+{
+    if (!lines_form_ran(info)) return;   // the vector form takes F
+    __shared__ u32x4 stage[2][kFwdTileVec4];
+    const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float hdx = 0.5f * __int_as_float(info[1]);
+
+    int64_t m[kFwdColumns];
+    float skx[kFwdColumns], sky[kFwdColumns], skz[kFwdColumns];
+#pragma unroll
+    for (int t = 0; t < kFwdColumns; ++t) {
+        m[t] = (int64_t)blockIdx.x * kFwdBlockSamples + wave * 16 * kFwdColumns + t * 16 + col;
+        const bool live = m[t] < M;   // samples past M compute with k = 0 and are not stored
+        skx[t] = live ? kx[m[t]] : 0.0f;
+        sky[t] = live ? ky[m[t]] : 0.0f;
+        skz[t] = live ? kz[m[t]] : 0.0f;
+    }
+    // B operands, held for the whole walk: K = 32 s + 8 (l / 16) + i, pair
+    // j = K % 64, cos (K < 64) or sin
+    bf16x8 bh[kFwdColumns][kFwdKSteps], bl[kFwdColumns][kFwdKSteps];
+#pragma unroll
+    for (int t = 0; t < kFwdColumns; ++t)
+#pragma unroll
+        for (int s = 0; s < kFwdKSteps; ++s) {
+            float v[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const int j = (32 * s + 8 * quarter_k + i) % kFwdPairs;
+                const float a = skx[t] * ((float)(2 * j + 1) * hdx);
+                v[i] = s < kFwdKSteps / 2 ? __builtin_amdgcn_cosf(a) : __builtin_amdgcn_sinf(a);
+            }
+            unsigned h[4], l[4];
+            split_bf16<kChunk>(v, h, l);
+            bh[t][s] = as_bf16x8(h);
+            bl[t][s] = as_bf16x8(l);
+        }
+
+    float dr[kFwdColumns], di[kFwdColumns];
+#pragma unroll
+    for (int t = 0; t < kFwdColumns; ++t) {
+        dr[t] = 0.0f;
+        di[t] = 0.0f;
+    }
+    const int per = (ntiles + splits - 1) / splits;
+    const int t0 = min(ntiles, (int)blockIdx.y * per), t1 = min(ntiles, t0 + per);
+
+    // tiles reach LDS through registers: loaded at the start of the
+    // previous tile, stored at its end
+    u32x4 sreg[kFwdStageRegs];
+    auto load_tile = [&](int tau) {
+#pragma unroll
+        for (int k = 0; k < kFwdStageRegs; ++k) {
+            const int i = k * kFwdBlock + threadIdx.x;
+            if (i < kFwdTileVec4) sreg[k] = tiles[(int64_t)tau * kFwdTileVec4 + i];
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < kFwdStageRegs; ++k) {
+            const int i = k * kFwdBlock + threadIdx.x;
+            if (i < kFwdTileVec4) stage[buf][i] = sreg[k];
+        }
+    };
+    if (t0 < t1) {
+        load_tile(t0);
+        store_tile(0);
+    }
+    lds_barrier();
+    int b = 0;
+    for (int tau = t0; tau < t1; ++tau) {
+        const bool more = tau + 1 < t1;   // uniform
+        if (more) load_tile(tau + 1);
+        float4v tre[kFwdColumns], tim[kFwdColumns];
+#pragma unroll
+        for (int t = 0; t < kFwdColumns; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                tre[t][r] = 0.0f;
+                tim[t][r] = 0.0f;
+            }
+#pragma unroll
+        for (int s = 0; s < kFwdKSteps; ++s) {
+            const u32x4 *op = &stage[b][s * 4 * 64 + lane];
+            const bf16x8 arh = __builtin_bit_cast(bf16x8, op[0 * 64]);
+            const bf16x8 arl = __builtin_bit_cast(bf16x8, op[1 * 64]);
+            const bf16x8 aih = __builtin_bit_cast(bf16x8, op[2 * 64]);
+            const bf16x8 ail = __builtin_bit_cast(bf16x8, op[3 * 64]);
+#pragma unroll
+            for (int t = 0; t < kFwdColumns; ++t) {
+                tre[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bh[t][s], tre[t], 0, 0, 0);
+                tim[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bh[t][s], tim[t], 0, 0, 0);
+                tre[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bl[t][s], tre[t], 0, 0, 0);
+                tim[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bl[t][s], tim[t], 0, 0, 0);
+                tre[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arl, bh[t][s], tre[t], 0, 0, 0);
+                tim[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ail, bh[t][s], tim[t], 0, 0, 0);
+            }
+        }
+        // D += conj(V) T for rows 4 (l / 16) + r, with V of the row's centre
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const u32x4 c = stage[b][kFwdOpsVec4 + 4 * quarter_k + r];
+            const float xc = __uint_as_float(c.x), ly = __uint_as_float(c.y), lz = __uint_as_float(c.z);
+#pragma unroll
+            for (int t = 0; t < kFwdColumns; ++t) {
+                const float p = __builtin_fmaf(skx[t], xc, __builtin_fmaf(sky[t], ly, skz[t] * lz));
+                const float vc = __builtin_amdgcn_cosf(p), vs = __builtin_amdgcn_sinf(p);
+                dr[t] = __builtin_fmaf(vc, tre[t][r], __builtin_fmaf(vs, tim[t][r], dr[t]));
+                di[t] = __builtin_fmaf(vc, tim[t][r], __builtin_fmaf(-vs, tre[t][r], di[t]));
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        // the other buffer was last read before the previous barrier
+        if (more) store_tile(b ^ 1);
+        lds_barrier();
+        b ^= 1;
+    }
+
+    // each column's four row groups (lanes col + 16 q) add up
+#pragma unroll
+    for (int t = 0; t < kFwdColumns; ++t) {
+        dr[t] += __shfl_xor(dr[t], 16);
+        di[t] += __shfl_xor(di[t], 16);
+        dr[t] += __shfl_xor(dr[t], 32);
+        di[t] += __shfl_xor(di[t], 32);
+    }
+    if (quarter_k == 0) {
+        float *dst_r = out_r + (int64_t)blockIdx.y * M, *dst_i = out_i + (int64_t)blockIdx.y * M;
+#pragma unroll
+        for (int t = 0; t < kFwdColumns; ++t)
+            if (m[t] < M) {
+                dst_r[m[t]] = dr[t];
+                dst_i[m[t]] = di[t];
+            }
+    }
+}
+
 }  // namespace
 
 int launch_forward_pack(const float *x, const float *y, const float *z, const float *rho_r,
-                        const float *rho_i, int N, float *packed, hipStream_t stream)
+                        const float *rho_i, int N, float *packed, hipStream_t stream, const int *gate)
 {
     if (N == 0) return FHD_OK;
     const int64_t N_pad = (int64_t)((N + kChunk - 1) / kChunk) * kChunk;
     const int64_t blocks = (N_pad + kPackBlock - 1) / kPackBlock;
     fhd_forward_pack_kernel<<<dim3((unsigned)blocks), dim3(kPackBlock), 0, stream>>>(
-        x, y, z, rho_r, rho_i, packed, N, N_pad);
+        x, y, z, rho_r, rho_i, packed, N, N_pad, gate);
     return launch_status("fhd_forward_pack_kernel launch");
 }
 
 int launch_forward_gather(const float *packed, int N, const float *kx, const float *ky,
-                          const float *kz, float *Dr, float *Di, int M, hipStream_t stream)
+                          const float *kz, float *Dr, float *Di, int M, hipStream_t stream, const int *gate)
 {
     if (M == 0) return FHD_OK;
     const int nchunks = (int)(((int64_t)N + kChunk - 1) / kChunk);
@@ -409,7 +638,7 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
     const int splits = split_count(blocks, nchunks);
     if (splits == 1) {
         fhd_forward_gather_kernel<kSamp><<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
-            packed, nchunks, 1, kx, ky, kz, Dr, Di, M);
+            packed, nchunks, 1, kx, ky, kz, Dr, Di, M, gate);
         return launch_status("fhd_forward_gather_kernel launch");
     }
     float *part = nullptr;
@@ -422,10 +651,77 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
     float *part_r = part, *part_i = part + (int64_t)splits * M;
     fhd_forward_gather_kernel<kSamp>
         <<<dim3((unsigned)blocks, (unsigned)splits), dim3(kBlock), 0, stream>>>(
-            packed, nchunks, splits, kx, ky, kz, part_r, part_i, M);
+            packed, nchunks, splits, kx, ky, kz, part_r, part_i, M, gate);
     int rc = launch_status("fhd_forward_gather_kernel launch");
-    if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, M, Dr, Di, stream);
+    if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, M, Dr, Di, stream, gate, false);
     const hipError_t f = hipFreeAsync(part, stream);
+    if (f != hipSuccess && rc == FHD_OK)
+        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
+    return rc;
+}
+
+
+int launch_forward(const float *x, const float *y, const float *z, const float *rho_r,
+                   const float *rho_i, int N, const float *kx, const float *ky, const float *kz,
+                   float *Dr, float *Di, int M, float *vox, hipStream_t stream)
+{
+    if (M == 0) return FHD_OK;
+    if (N == 0 || N % (2 * kUnitVox) != 0) {
+        // not whole pairs of units: the vector form
+        int rc = launch_forward_pack(x, y, z, rho_r, rho_i, N, vox, stream);
+        return rc == FHD_OK ? launch_forward_gather(vox, N, kx, ky, kz, Dr, Di, M, stream) : rc;
+    }
+    const int64_t units = N / kUnitVox, ntiles = N / kFwdTileVox;
+    const int64_t blocks = ((int64_t)M + kFwdBlockSamples - 1) / kFwdBlockSamples;
+    static int per_cu_cache[64] = {0};
+    int dev = 0, per_cu = 3;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        if (per_cu_cache[dev] == 0) {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &n, reinterpret_cast<const void *>(fhd_forward_lines_kernel), kFwdBlock, 0) != hipSuccess ||
+                n < 1)
+                n = 3;
+            per_cu_cache[dev] = n;
+        }
+        per_cu = per_cu_cache[dev];
+    }
+    // cut the line stream so the sample blocks fill whole rounds (each part
+    // at least one tile)
+    const int splits = split_count(blocks, (int)(ntiles * kStageChunks), per_cu);
+    // one workspace: unit classes and the flag words | line tiles | partials
+    const size_t cls_bytes = ((size_t)units * sizeof(int) + 4 * sizeof(int) + 255) / 256 * 256;
+    const size_t tile_bytes = (size_t)ntiles * kFwdTileVec4 * sizeof(u32x4);
+    const size_t part_bytes = splits > 1 ? (size_t)splits * 2 * M * sizeof(float) : 0;
+    char *work = nullptr;
+    const hipError_t e = hipMallocAsync((void **)&work, cls_bytes + tile_bytes + part_bytes, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (forward workspace): ") + hipGetErrorString(e));
+    }
+    int *cls = reinterpret_cast<int *>(work), *info = cls + units;
+    u32x4 *tiles = reinterpret_cast<u32x4 *>(work + cls_bytes);
+    float *part_r = Dr, *part_i = Di;
+    if (splits > 1) {
+        part_r = reinterpret_cast<float *>(work + cls_bytes + tile_bytes);
+        part_i = part_r + (int64_t)splits * M;
+    }
+    int rc = launch_classify(x, y, z, N, true, cls, info, stream);
+    if (rc == FHD_OK) {
+        fhd_forward_lines_pack_kernel<<<dim3((unsigned)ntiles), dim3(kFwdBlock), 0, stream>>>(
+            x, y, z, rho_r, rho_i, cls, info, tiles);
+        rc = launch_status("fhd_forward_lines_pack_kernel launch");
+    }
+    if (rc == FHD_OK) {
+        fhd_forward_lines_kernel<<<dim3((unsigned)blocks, (unsigned)splits), dim3(kFwdBlock), 0, stream>>>(
+            tiles, (int)ntiles, splits, info, kx, ky, kz, part_r, part_i, M);
+        rc = launch_status("fhd_forward_lines_kernel launch");
+    }
+    if (rc == FHD_OK && splits > 1) rc = launch_reduce(part_r, part_i, splits, M, Dr, Di, stream, info, true);
+    // the vector form, which stands aside when the line form ran
+    if (rc == FHD_OK) rc = launch_forward_pack(x, y, z, rho_r, rho_i, N, vox, stream, info);
+    if (rc == FHD_OK) rc = launch_forward_gather(vox, N, kx, ky, kz, Dr, Di, M, stream, info);
+    const hipError_t f = hipFreeAsync(work, stream);
     if (f != hipSuccess && rc == FHD_OK)
         rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
     return rc;
@@ -503,9 +799,8 @@ extern "C" int fhd_forward(const float *kx, const float *ky, const float *kz, co
             (void)hipGetLastError();
             return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
         }
-        rc = launch_forward_pack(x, y, z, rho_r, rho_i, N, packed, s);
     }
-    if (rc == FHD_OK) rc = launch_forward_gather(packed, N, kx, ky, kz, Dr, Di, M, s);
+    if (rc == FHD_OK) rc = launch_forward(x, y, z, rho_r, rho_i, N, kx, ky, kz, Dr, Di, M, packed, s);
     if (packed) {
         const hipError_t e = hipFreeAsync(packed, s);
         if (e != hipSuccess && rc == FHD_OK)
@@ -548,8 +843,7 @@ extern "C" int fhd_normal(const float *kx, const float *ky, const float *kz, con
     }
     float *vox = (float *)ws, *smp = (float *)(ws + vox_bytes);
     float *d_r = (float *)(ws + vox_bytes + smp_bytes), *d_i = d_r + M;
-    rc = launch_forward_pack(x, y, z, p_r, p_i, N, vox, s);
-    if (rc == FHD_OK) rc = launch_forward_gather(vox, N, kx, ky, kz, d_r, d_i, M, s);
+    rc = launch_forward(x, y, z, p_r, p_i, N, kx, ky, kz, d_r, d_i, M, vox, s);
     if (rc == FHD_OK) rc = launch_pack(kx, ky, kz, d_r, d_i, M, smp, s);
     if (rc == FHD_OK) rc = launch_gather(smp, M, x, y, z, q_r, q_i, N, s);
     const hipError_t f = hipFreeAsync(ws, s);

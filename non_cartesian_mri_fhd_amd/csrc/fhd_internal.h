@@ -39,6 +39,15 @@ constexpr int kStageChunks = 64;   // chunks per LDS stage (512 records, 10 KB)
 constexpr int kStageVec4 = kStageChunks * kChunkVec4;   // 640 float4
 constexpr int kPackBlock = 256;
 
+// Voxel units of the F^H D classification (fhd.hip, fhd_classify_kernel):
+// 4096 consecutive voxels; class kClassLongPair marks both units of an
+// aligned pair whose aligned runs of kLongLineVox voxels are lines along x
+// of one step (same y and z bitwise, x_v = x_0 + v dx rounded once).
+constexpr int kUnitVox = 4096;
+constexpr int kLineVox = 64;
+constexpr int kLongLineVox = 128;
+enum : int { kClassGeneral = 0, kClassOneStep = 1, kClassLines = 2, kClassLongPair = 3 };
+
 static_assert(kBlock % 64 == 0, "workgroup must be whole wave64s");
 static_assert(kChunk * kFields % 4 == 0, "chunks must be whole float4s");
 
@@ -246,9 +255,10 @@ int launch_status(const char *what);
 int split_count(int64_t blocks, int nchunks, int per_cu = 4);
 
 // out[i] = sum_{s < splits} part[s*n + i] in increasing s, for the real
-// and the imaginary parts (stream-ordered launch, no checks).
+// and the imaginary parts (stream-ordered launch, no checks). With a gate,
+// only when lines_form_ran(gate) == gate_want.
 int launch_reduce(const float *part_r, const float *part_i, int splits, int64_t n, float *out_r,
-                  float *out_i, hipStream_t stream);
+                  float *out_i, hipStream_t stream, const int *gate = nullptr, bool gate_want = true);
 
 // Kernel launches without argument checks (callers have checked). A gather
 // whose output is too small to fill the chip splits the stream, with a
@@ -256,14 +266,33 @@ int launch_reduce(const float *part_r, const float *part_i, int splits, int64_t 
 // fhd.hip: adjoint F^H D
 int launch_pack(const float *kx, const float *ky, const float *kz, const float *Dr, const float *Di,
                 int M, float *packed, hipStream_t stream);
+// Whether the forward operator's line form ran (and the vector form is to
+// stand aside): info as launch_classify leaves it, with info[2] set by the
+// line pre-pass when some line breaks the rule.
+__device__ __forceinline__ bool lines_form_ran(const int *info) { return info[0] != 0 && info[2] == 0; }
+
+// Classes of the ceil(N / kUnitVox) units into cls; info[0] = 1 if the
+// first pair is of class kClassLongPair, info[1] its step's bits, info[2]
+// = 0 (stream-ordered; allow_lines = false gives no matrix-core class).
+int launch_classify(const float *x, const float *y, const float *z, int N, bool allow_lines, int *cls,
+                    int *info, hipStream_t stream);
 // matrix_cores = false keeps every unit on the vector-ALU paths.
 int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
                   float *rho_r, float *rho_i, int N, hipStream_t stream, bool matrix_cores = true);
 // fhd_forward.hip: forward F
+// (with a gate: nothing when lines_form_ran(gate))
 int launch_forward_pack(const float *x, const float *y, const float *z, const float *rho_r,
-                        const float *rho_i, int N, float *packed, hipStream_t stream);
+                        const float *rho_i, int N, float *packed, hipStream_t stream,
+                        const int *gate = nullptr);
 int launch_forward_gather(const float *packed, int N, const float *kx, const float *ky,
-                          const float *kz, float *Dr, float *Di, int M, hipStream_t stream);
+                          const float *kz, float *Dr, float *Di, int M, hipStream_t stream,
+                          const int *gate = nullptr);
+// D = F rho: on the matrix cores when every aligned pair of voxel units is
+// lines of 128 voxels along x of one common step (decided on the device),
+// else packed into vox (packed_bytes_for(N) bytes) for the vector gather.
+int launch_forward(const float *x, const float *y, const float *z, const float *rho_r,
+                   const float *rho_i, int N, const float *kx, const float *ky, const float *kz,
+                   float *Dr, float *Di, int M, float *vox, hipStream_t stream);
 // fhd_grid.hip: F^H D on a Cartesian grid (axis = x0, dx, y0, dy, z0, dz)
 int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const float *axis,
                        int precision, float *rho_r, float *rho_i, hipStream_t stream);

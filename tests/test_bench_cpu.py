@@ -152,3 +152,18 @@ def test_ramp_chunk_fraction():
     assert bench.ramp_chunk_fraction(x2, y, z) == 1.0 - 16 / L ** 3
     m = L ** 3 - 3                            # partial last chunk
     assert bench.ramp_chunk_fraction(x[:m], y[:m], z[:m]) == (L ** 3 - 8) / m
+
+
+def test_forward_lines_form_mirror():
+    """fhd_forward's line form: whole unit pairs of 128-voxel lines with one
+    step throughout; rows of 64, a second step or a partial pair fall back."""
+    from non_cartesian_mri_fhd_amd import inputs
+    ax = (-0.5, 1.0 / 128, -0.5, 1.0 / 16, 0.0, 0.25)
+    x, y, z = inputs.coords_from_axis(128, 16, 4, ax)
+    assert bench.forward_lines_form(x, y, z)
+    x2, y2, z2 = inputs.coords_from_axis(64, 16, 8, (-0.5, 1.0 / 64, -0.5, 1.0 / 16, 0.0, 0.25))
+    assert not bench.forward_lines_form(x2, y2, z2)
+    gb = inputs.coords_from_axis(128, 16, 4, (-0.25, 1.0 / 256, -0.5, 1.0 / 16, 0.125, 0.25))
+    xx, yy, zz = (np.concatenate((a, b)) for a, b in zip((x, y, z), gb))
+    assert not bench.forward_lines_form(xx, yy, zz)
+    assert not bench.forward_lines_form(x[:4096], y[:4096], z[:4096])

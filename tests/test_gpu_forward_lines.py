@@ -1,0 +1,146 @@
+"""GPU parity of the forward operator F in its matrix-core line form (every
+aligned pair of 4096-voxel units is lines of 128 voxels along x with one
+step) against the fp64 oracle, against the vector form on the same voxels,
+and through adjointness with F^H D.
+
+Gate as in test_gpu_parity: relative L2 <= 5e-4 and every element within
+10x that bound times the reference's rms. The line form computes in split
+bf16 (three bf16 products per fp32 product, fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle
+from non_cartesian_mri_fhd_amd import binding, build, inputs, metrics
+
+pytestmark = pytest.mark.gpu
+
+REL_L2_TOL = 5e-4
+ELEM_TOL = 10 * REL_L2_TOL
+AX128 = (-0.5, 1.0 / 128, -0.5, 1.0 / 16, 0.0, 0.25)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    build.ensure_built()
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def t(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def gpu_forward(k, x, y, z, img, dev):
+    Dr, Di = binding.fhd_forward(t(k["kx"], dev), t(k["ky"], dev), t(k["kz"], dev), t(x, dev), t(y, dev),
+                                 t(z, dev), t(img[0], dev), t(img[1], dev))
+    torch.cuda.synchronize(dev)
+    return Dr.cpu().numpy(), Di.cpu().numpy()
+
+
+def check(tag, k, x, y, z, img, Dr, Di):
+    ref_r, ref_i = oracle.forward(k["kx"], k["ky"], k["kz"], img[0], img[1], x, y, z)
+    e = metrics.rel_l2(Dr, Di, ref_r, ref_i)
+    worst = metrics.max_abs_err(Dr, Di, ref_r, ref_i)
+    scale = metrics.rms(ref_r, ref_i)
+    print("%s: rel_l2=%.3e max_err/rms=%.3e" % (tag, e, worst / scale), flush=True)
+    assert np.all(np.isfinite(Dr)) and np.all(np.isfinite(Di))
+    assert e <= REL_L2_TOL, (tag, e)
+    assert worst <= ELEM_TOL * scale, (tag, worst, scale)
+    return e
+
+
+def all_long_pairs(x, y, z):
+    cls = bench.gather_unit_classes(x, y, z)[0]
+    return cls.size > 0 and bool(np.all(cls == 3))
+
+
+@pytest.mark.parametrize("shape,axis,M", [
+    ((128, 16, 4), AX128, 3000),                                           # one pair of units
+    ((256, 16, 6), (-0.5, 1.0 / 256, -0.5, 1.0 / 16, -0.5, 1.0 / 6), 1000),   # 3 pairs, half rows
+    ((128, 32, 2), (0.25, -1.0 / 128, -0.5, 1.0 / 32, 0.0, 0.5), 129),      # negative step, ragged M
+    ((128, 16, 4), AX128, 1),
+])
+def test_forward_lines_grids(dev, shape, axis, M):
+    x, y, z = inputs.coords_from_axis(*shape, axis)
+    assert all_long_pairs(x, y, z)
+    k = inputs.random_case(1, M, seed=sum(shape) + M, kmax=shape[0] / 2.0)
+    img = inputs.random_image(x.size, seed=M + 5)
+    check("forward lines %s M=%d" % (shape, M), k, x, y, z, img, *gpu_forward(k, x, y, z, img, dev))
+
+
+def test_forward_lines_against_vector_form(dev):
+    """Rows of 128 (the line form) and the same voxels with the two halves
+    of every row swapped (64-voxel lines only: the vector form) meet the
+    oracle gate and agree to rounding, not bitwise."""
+    k = inputs.make_kspace("spiral32")
+    x, y, z = inputs.coords_from_axis(128, 16, 4, AX128)
+    perm = np.arange(x.size).reshape(-1, 2, 64)[:, ::-1, :].reshape(-1)
+    img = inputs.random_image(x.size, seed=31)
+    pimg = (img[0][perm], img[1][perm])
+    assert all_long_pairs(x, y, z) and not all_long_pairs(x[perm], y[perm], z[perm])
+    a = gpu_forward(k, x, y, z, img, dev)
+    b = gpu_forward(k, x[perm], y[perm], z[perm], pimg, dev)
+    check("line form", k, x, y, z, img, *a)
+    check("vector form", k, x[perm], y[perm], z[perm], pimg, *b)
+    diff = metrics.rel_l2(a[0], a[1], b[0].astype(np.float64), b[1].astype(np.float64))
+    print("line vs vector form: rel diff %.2e" % diff)
+    assert 0 < diff < 1e-4
+
+
+def test_forward_lines_fall_back_on_a_second_step(dev):
+    """Two pairs of units of different steps: not one step throughout, so
+    the vector form takes F (bitwise the two-stage vector entry points)."""
+    ga = inputs.coords_from_axis(128, 16, 4, AX128)
+    gb = inputs.coords_from_axis(128, 16, 4, (-0.25, 1.0 / 256, -0.5, 1.0 / 16, 0.125, 0.25))
+    x, y, z = (np.concatenate((a, b)) for a, b in zip(ga, gb))
+    assert all_long_pairs(x, y, z)
+    k = inputs.make_kspace("random16")
+    img = inputs.random_image(x.size, seed=8)
+    a = gpu_forward(k, x, y, z, img, dev)
+    check("two steps", k, x, y, z, img, *a)
+    packed = binding.new_packed(x.size, dev)
+    binding.fhd_forward_pack(t(x, dev), t(y, dev), t(z, dev), t(img[0], dev), t(img[1], dev), packed)
+    g = binding.fhd_forward_gather(packed, x.size, t(k["kx"], dev), t(k["ky"], dev), t(k["kz"], dev))
+    torch.cuda.synchronize(dev)
+    assert np.array_equal(a[0], g[0].cpu().numpy()) and np.array_equal(a[1], g[1].cpu().numpy())
+
+
+def test_forward_lines_adjointness_and_normal(dev):
+    """<F^H D, rho> = <D, F rho> with both operators in their line forms,
+    and F^H F p against the oracle's composition."""
+    x, y, z = inputs.coords_from_axis(128, 16, 4, AX128)
+    c = inputs.random_case(1, 2000, seed=41, kmax=32.0)
+    img = inputs.random_image(x.size, seed=42)
+    d = {n: t(c[n], dev) for n in ("kx", "ky", "kz", "Dr", "Di")}
+    X, Y, Z = t(x, dev), t(y, dev), t(z, dev)
+    rr, ri = binding.fhd_compute(d["kx"], d["ky"], d["kz"], d["Dr"], d["Di"], X, Y, Z)
+    Fr, Fi = binding.fhd_forward(d["kx"], d["ky"], d["kz"], X, Y, Z, t(img[0], dev), t(img[1], dev))
+    qr, qi = binding.fhd_normal(d["kx"], d["ky"], d["kz"], X, Y, Z, t(img[0], dev), t(img[1], dev))
+    torch.cuda.synchronize(dev)
+    rho = img[0].astype(np.float64) + 1j * img[1].astype(np.float64)
+    D = c["Dr"].astype(np.float64) + 1j * c["Di"].astype(np.float64)
+    lhs = np.vdot(rho, rr.cpu().numpy().astype(np.float64) + 1j * ri.cpu().numpy())
+    rhs = np.vdot(Fr.cpu().numpy().astype(np.float64) + 1j * Fi.cpu().numpy(), D)
+    scale = np.linalg.norm(rho) * np.linalg.norm(D) * np.sqrt(2000)
+    assert abs(lhs - rhs) <= 1e-4 * scale, (lhs, rhs)
+    Dr_ref, Di_ref = oracle.forward(c["kx"], c["ky"], c["kz"], img[0], img[1], x, y, z)
+    q_ref = oracle.fhd(c["kx"], c["ky"], c["kz"], Dr_ref.astype(np.float32), Di_ref.astype(np.float32), x, y, z)
+    e = metrics.rel_l2(qr.cpu().numpy(), qi.cpu().numpy(), *q_ref)
+    print("normal, line forms: rel_l2=%.3e" % e)
+    assert e <= REL_L2_TOL
+
+
+def test_forward_lines_zero_image_and_repeatable(dev):
+    x, y, z = inputs.coords_from_axis(128, 16, 4, AX128)
+    k = inputs.make_kspace("spiral32")
+    zero = (np.zeros(x.size, np.float32), np.zeros(x.size, np.float32))
+    Dr, Di = gpu_forward(k, x, y, z, zero, dev)
+    assert not np.any(Dr) and not np.any(Di)
+    img = inputs.random_image(x.size, seed=3)
+    a = gpu_forward(k, x, y, z, img, dev)
+    b = gpu_forward(k, x, y, z, img, dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
