@@ -239,19 +239,25 @@ def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 16) -> float:
 # readings (factors 2.0 and 1.0). Valid only for the sources they were taken
 # on (SHA-256 over the listed files, in order); any later edit reports null
 # until the counters are taken again.
-#   fhd  (fhd_gather_long_lines_kernel): 414.3 MiB read (the 48.8 MiB B
+#   fhd  (fhd_gather_long_lines_kernel): 414.4 MiB read (the 48.8 MiB B
 #        table about once per XCD L2, the packed samples, x, y, z) + 48.1
 #        MiB written (3 split partial sums of rho)
-#   grid (fhd_grid_kernel):   15.6 MiB read (packed samples once per XCD L2)
+#   grid (fhd_grid_kernel):   15.4 MiB read (packed samples once per XCD L2)
 #        + 48.0 MiB written (3 split partial sums of rho)
+#   forward (fhd_forward_lines_kernel): 146.6 MiB read (the 17 MB of line
+#        operand tiles about once per XCD L2, k) + 8.4 MiB written (the
+#        split partial sums of D)
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
     "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
-            "sha256": "65c51340ff0ca67f909b105e264121042c39a026e7bd9e91c3aa85c67b8a9a90",
-            "bytes_per_launch": (212134.0 * 2.0 + 49246 * 1.0) * 1024},
+            "sha256": "2742cfcc1f402b8272f7e7e481d7d301752f5bf1a17889fdfa5beb6c77d42336",
+            "bytes_per_launch": (212191.0 * 2.0 + 49281.0 * 1.0) * 1024},
     "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
-             "sha256": "9888524503e259259b3d4de5019911087d974ceb47876f8b21ad17f945d0d7f8",
-             "bytes_per_launch": (7965.4 * 2.0 + 49152 * 1.0) * 1024},
+             "sha256": "b1b1479f1a3565e78aa09c4f94013be3f4790b1f2dfc96d2775dd1407cc3389f",
+             "bytes_per_launch": (7881.0 * 2.0 + 49152.0 * 1.0) * 1024},
+    "forward": {"workload": "spiral128", "sources": ["fhd_forward.hip", "fhd_internal.h"],
+                "sha256": "0cb29af5c5f7694c4c83cde1b24d4410e4943e133d3d23502514d0919befbf4b",
+                "bytes_per_launch": (75084.0 * 2.0 + 8594.0 * 1.0) * 1024},
 }
 
 
@@ -407,6 +413,7 @@ def main(argv=None) -> int:
                                (terms * (1 - ln - on - la), ROOF_TERMS)])
 
     (lines, one, lane), roof = ceiling(args.paths == "all")
+    dominant_kernel = "fhd_gather_long_lines_kernel" if lines == 1.0 else "fhd_gather_kernel"
     _, alt_roof = ceiling(args.paths != "all")
     rate = terms / (gather_ms * 1e-3)
     if lines == 1.0:
@@ -441,9 +448,11 @@ def main(argv=None) -> int:
             "note": "R for 2 transcendentals per term, the pages' direct evaluation",
             "peak": FLOP_PER_TERM * ROOF_TERMS / 1e12, "unit": "TFLOP/s",
             "frac": FLOP_PER_TERM * terms / (gather_ms * 1e-3) / (FLOP_PER_TERM * ROOF_TERMS)},
-        "kernel_ms": {"fhd_gather_kernel": gather_ms, "fhd_pack_kernel": pack_ms,
-                      "fhd_gather_kernel_median": float(np.median(gather_all)),
-                      "fhd_gather_kernel_min": float(np.min(gather_all))},
+        # HIP events around each fhd_gather call: its classify, B-table,
+        # gather and reduce kernels, of which the dominant one takes ~97 %
+        "kernel_ms": {"timed": "fhd_gather call", "dominant": dominant_kernel, "mean": gather_ms,
+                      "median": float(np.median(gather_all)), "min": float(np.min(gather_all)),
+                      "fhd_pack_call": pack_ms},
         "gflops_13_per_term": FLOP_PER_TERM * value / 1e9,
         ("vector_paths_only" if args.paths == "all" else "all_paths"): {
             "note": ("fhd_gather_paths(FHD_GATHER_VECTOR): every unit on the fp32 VALU paths"
@@ -660,7 +669,8 @@ def bench_other(args) -> int:
         # every term on the bf16 matrix cores (both operators in line form)
         out["roofline"] = {"bound": "mfma", "achieved": LINES_FLOP_PER_TERM * k_rate / 1e12,
                            "peak": P_MFMA_BF16 / 1e12, "unit": "TFLOP/s",
-                           "frac": k_rate / roof, "traffic": None}
+                           "frac": k_rate / roof,
+                           "traffic": measured_traffic("forward", args.workload) if args.op == "forward" else None}
         out["dtype"] = "bf16x3 (fp32 accumulation)"
     if args.op == "grid":
         # one complex multiply-add per term on the fp32 matrix cores

@@ -18,9 +18,9 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_only_for_the_profiled_workload():
-    for op in ("fhd", "grid"):
+    for op in ("fhd", "grid", "forward"):
         assert bench.measured_traffic(op, "radial64") is None
-    assert bench.measured_traffic("forward", "spiral128") is None
+    assert bench.measured_traffic("normal", "spiral128") is None
 
 
 def test_roofline_constants():
