@@ -280,7 +280,9 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="spiral128")
     ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid", "grid_bf16x3",
-                                                       "forward_grid", "normal_grid", "cg_grid"])
+                                                       "forward_grid", "normal_grid", "cg_grid", "scatter"],
+                    help="scatter: fhd_scatter (a lane per sample, atomic adds), timed beside "
+                         "fhd_compute on the same workload; use a small workload (spiral32)")
     ap.add_argument("--paths", default="all", choices=["all", "vector"],
                     help="paths (--op fhd): all (fhd_gather: lines on the matrix cores) or vector "
                          "(fhd_gather_paths with FHD_GATHER_VECTOR: the fp32 VALU paths only); "
@@ -595,6 +597,17 @@ def bench_other(args) -> int:
             binding.fhd_cg_grid(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], (L, L, L), axis, k_iters,
                                 0.0, rr, ri)
         terms_per_step = float(N) * M * (1 + 2 * k_iters)
+    elif args.op == "scatter":
+        rr = torch.empty(N, device=dev)
+        ri = torch.empty(N, device=dev)
+
+        def pre():
+            pass
+
+        def main_kernel():
+            binding.fhd_scatter(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], t["x"], t["y"], t["z"],
+                                rr, ri)
+        terms_per_step = float(N) * M
     elif args.op == "normal":
         qr = torch.empty(N, device=dev)
         qi = torch.empty(N, device=dev)
@@ -687,8 +700,30 @@ def bench_other(args) -> int:
         out["roofline"] = {"bound": "mfma", "achieved": achieved / 1e12,
                            "peak": P_MFMA_BF16 / 1e12, "unit": "TFLOP/s",
                            "frac": achieved / P_MFMA_BF16, "traffic": None}
+    if args.op == "scatter":
+        # the gather form on the same workload, timed the same way
+        gr = torch.empty(N, device=dev)
+        gi = torch.empty(N, device=dev)
+        args_g = [t[n] for n in ("kx", "ky", "kz", "Dr", "Di", "x", "y", "z")]
+        binding.fhd_compute(*args_g, gr, gi)
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)]
+        for e in gev:
+            e[0].record(stream)
+            binding.fhd_compute(*args_g, gr, gi)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        g_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in gev]))
+        out["roofline"] = {"bound": "alu", "achieved": FLOP_PER_TERM * k_rate / 1e12,
+                           "peak": FLOP_PER_TERM * ROOF_TERMS / 1e12, "unit": "TFLOP/s",
+                           "frac": k_rate / ROOF_TERMS, "traffic": None,
+                           "note": "direct-form ceiling R (2 transcendentals per term)"}
+        out["gather_form"] = {"call": "fhd_compute", "ms": g_ms, "terms_per_s": terms_per_step / (g_ms * 1e-3),
+                              "scatter_over_gather_time": float(np.mean(kms)) / g_ms,
+                              "rel_l2_scatter_vs_gather": float(
+                                  np.linalg.norm((rr - gr).double().cpu().numpy() + 1j * (ri - gi).double().cpu().numpy())
+                                  / np.linalg.norm(gr.double().cpu().numpy() + 1j * gi.double().cpu().numpy()))}
     if not args.no_cpu_baseline:
-        if args.op in ("grid", "grid_bf16x3"):
+        if args.op in ("grid", "grid_bf16x3", "scatter"):
             base, parity = cpu_baseline(w, args.workload, args.cpu_seconds,
                                         rr.cpu().numpy(), ri.cpu().numpy())
         elif args.op in ("forward", "forward_grid"):

@@ -71,6 +71,23 @@ int fhd_compute(const float *kx, const float *ky, const float *kz,
                 float *rho_r, float *rho_i, int M, int N, void *stream);
 
 /*
+ * rho = F^H D in the scatter form that section 17.3.1 compares with the
+ * gather form: one lane per sample m adds D_m e^{+i 2 pi k_m . x_n} into
+ * every rho_n with fp32 atomic adds (the compiler merges a wave's 64 adds to
+ * one address into one). Kept as the measured evidence for fhd_compute's
+ * gather form; slow by design at large N x M (every term ends in an atomic
+ * path). The summation order varies from run to run, so results match
+ * fhd_compute's to rounding only. No workspace.
+ *   arguments : as for fhd_compute (same layout, ownership, overlap rules)
+ * M = 0 writes zeros; N = 0 does nothing.
+ * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_HIP.
+ */
+int fhd_scatter(const float *kx, const float *ky, const float *kz,
+                const float *Dr, const float *Di,
+                const float *x, const float *y, const float *z,
+                float *rho_r, float *rho_i, int M, int N, void *stream);
+
+/*
  * Size in bytes of the packed k-space that fhd_pack writes for M samples,
  * or -1 if M < 0. M is padded up to a whole chunk of samples.
  */

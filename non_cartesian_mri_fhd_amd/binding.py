@@ -58,6 +58,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     fp, vp, i32, i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.fhd_compute.argtypes = [fp] * 10 + [i32, i32, vp]
     lib.fhd_compute.restype = i32
+    lib.fhd_scatter.argtypes = [fp] * 10 + [i32, i32, vp]
+    lib.fhd_scatter.restype = i32
     lib.fhd_packed_bytes.argtypes = [i32]
     lib.fhd_packed_bytes.restype = i64
     lib.fhd_pack.argtypes = [fp] * 5 + [i32, vp, i64, vp]
@@ -153,6 +155,25 @@ def fhd_compute(kx, ky, kz, Dr, Di, x, y, z, rho_r=None, rho_i=None, stream=None
                                                (rho_r, "rho_r"), (rho_i, "rho_i"))]
     with torch.cuda.device(dev):
         _check(lib, lib.fhd_compute(*ptrs, M, N, _stream(dev, stream)), "fhd_compute")
+    return rho_r, rho_i
+
+
+def fhd_scatter(kx, ky, kz, Dr, Di, x, y, z, rho_r=None, rho_i=None, stream=None):
+    """rho = F^H D in the scatter form (a lane per sample, atomic adds into
+    rho); the same contract as fhd_compute. Returns (rho_r, rho_i)."""
+    lib = load()
+    M, N = kx.numel(), x.numel()
+    dev = x.device
+    if rho_r is None:
+        rho_r = torch.empty(N, dtype=torch.float32, device=dev)
+    if rho_i is None:
+        rho_i = torch.empty(N, dtype=torch.float32, device=dev)
+    ptrs = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"),
+                                               (Dr, "Dr"), (Di, "Di"))]
+    ptrs += [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"),
+                                               (rho_r, "rho_r"), (rho_i, "rho_i"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_scatter(*ptrs, M, N, _stream(dev, stream)), "fhd_scatter")
     return rho_r, rho_i
 
 

@@ -27,7 +27,8 @@ HIP_FLAGS = [
 
 # library name -> source files
 LIBRARIES = {
-    "libfhd.so": ["fhd.hip", "fhd_forward.hip", "fhd_cg.hip", "fhd_grid.hip", "abi_checks.hip"],
+    "libfhd.so": ["fhd.hip", "fhd_forward.hip", "fhd_cg.hip", "fhd_grid.hip", "fhd_scatter.hip",
+                  "abi_checks.hip"],
     "libfhd_microbench.so": ["microbench.hip"],
 }
 
