@@ -517,63 +517,77 @@ __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (
     return ok;
 }
 
-// One workgroup per aligned pair of units (units 2b and 2b + 1 < units):
-// cls[u] = the class of unit u (never a matrix-core class unless
-// allow_lines); the first pair's workgroup also records whether that pair
-// is of class kClassLongPair (info[0]) and its lines' step (info[1], bits),
-// and clears info[2] (a flag the forward operator's line pre-pass sets).
-__global__ __launch_bounds__(kBlock) void fhd_classify_kernel(const float *__restrict__ x,
-                                                              const float *__restrict__ y,
-                                                              const float *__restrict__ z, int N,
-                                                              int64_t units, int allow_lines,
-                                                              int *__restrict__ cls,
-                                                              int *__restrict__ info)
+// One workgroup per aligned pair of units (units 2b and 2b + 1 < units),
+// one half of the workgroup (kBlock lanes, the lane-to-voxel map of the
+// gather instances) per unit, both tested at once: cls[u] = the class of
+// unit u (never a matrix-core class unless allow_lines); the first pair's
+// workgroup also records whether that pair is of class kClassLongPair
+// (info[0]) and its lines' step (info[1], bits), and clears info[2] (a flag
+// the forward operator's line pre-pass sets). Two barriers: one to publish
+// each unit's first-lane steps, one to combine the waves' votes.
+constexpr int kClassifyBlock = 2 * kBlock;
+__global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const float *__restrict__ x,
+                                                                      const float *__restrict__ y,
+                                                                      const float *__restrict__ z, int N,
+                                                                      int64_t units, int allow_lines,
+                                                                      int *__restrict__ cls,
+                                                                      int *__restrict__ info)
 {
-    __shared__ float wg_step[3];   // the unit's first lane's ramp step and line steps
-    int c[2] = {kClassGeneral, kClassGeneral};
-    bool long_lines[2] = {false, false};
-    float long_step[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int64_t u = 2 * (int64_t)blockIdx.x + k;
-        if (u >= units) break;   // uniform: the grid's last pair may hold one unit
-        const int64_t unit = u * kUnitVox;
-        const int64_t n0 = unit + (int64_t)threadIdx.x * kVox;
+    constexpr int kWavesPerUnit = kBlock / 64;
+    __shared__ float wg_step[2][3];                // each unit's first lane's ramp and line steps
+    __shared__ int votes[2 * kWavesPerUnit][3];    // per wave: one step, 64-lines, 128-lines
+    const int half = threadIdx.x / kBlock, t = threadIdx.x % kBlock;
+    const int64_t u = 2 * (int64_t)blockIdx.x + half;
+    const bool present = u < units;   // the grid's last pair may hold one unit
+    const int64_t unit = u * kUnitVox;
+    const int64_t n0 = unit + (int64_t)t * kVox;
+    bool ramp = false, on64 = false, on128 = false;
+    float dx = 0.0f, d64 = 0.0f, d128 = 0.0f;
+    if (present) {   // uniform over each wave
         float px[kVox], py[kVox], pz[kVox];
         load_lane_voxels<kVox>(x, y, z, N, n0, px, py, pz);
         bool same_yz;
-        float dx, d64, d128;
-        const bool ramp = lane_ramp<kVox>(px, py, pz, n0, N, &same_yz, &dx);
+        ramp = lane_ramp<kVox>(px, py, pz, n0, N, &same_yz, &dx);
         const bool whole = unit + kUnitVox <= N;
-        const bool on64 = whole && lane_on_line<kLineVox, kVox>(px, py, pz, &d64);
-        const bool on128 = whole && lane_on_line<kLongLineVox, kVox>(px, py, pz, &d128);
-        if (threadIdx.x == 0) {
-            wg_step[0] = dx;
-            wg_step[1] = d64;
-            wg_step[2] = d128;
+        on64 = whole && lane_on_line<kLineVox, kVox>(px, py, pz, &d64);
+        on128 = whole && lane_on_line<kLongLineVox, kVox>(px, py, pz, &d128);
+        if (t == 0) {
+            wg_step[half][0] = dx;
+            wg_step[half][1] = d64;
+            wg_step[half][2] = d128;
         }
-        // every branch below is uniform over the workgroup, so each barrier
-        // is reached by every wave
-        const bool all_ramp = __syncthreads_and(ramp);
-        const bool all64 = __syncthreads_and(on64);
-        const bool all128 = __syncthreads_and(on128);
-        const bool one_step = all_ramp && __syncthreads_and(__float_as_uint(dx) == __float_as_uint(wg_step[0]));
-        const bool lines64 = all64 && __syncthreads_and(__float_as_uint(d64) == __float_as_uint(wg_step[1]));
-        long_lines[k] = all128 && __syncthreads_and(__float_as_uint(d128) == __float_as_uint(wg_step[2]));
-        long_step[k] = wg_step[2];
-        c[k] = allow_lines && lines64 ? kClassLines : one_step ? kClassOneStep : kClassGeneral;
-        __syncthreads();   // wg_step is read before the next unit writes it
     }
-    const bool pair = allow_lines && long_lines[0] && long_lines[1] &&
-                      __float_as_uint(long_step[0]) == __float_as_uint(long_step[1]);
-    if (threadIdx.x < 2) {
-        const int64_t u = 2 * (int64_t)blockIdx.x + threadIdx.x;
-        if (u < units) cls[u] = pair ? kClassLongPair : threadIdx.x == 0 ? c[0] : c[1];
+    __syncthreads();
+    const bool one = ramp && __float_as_uint(dx) == __float_as_uint(wg_step[half][0]);
+    const bool l64 = on64 && __float_as_uint(d64) == __float_as_uint(wg_step[half][1]);
+    const bool l128 = on128 && __float_as_uint(d128) == __float_as_uint(wg_step[half][2]);
+    const int wave = threadIdx.x / 64;
+    const bool all_one = __all(one), all64 = __all(l64), all128 = __all(l128);
+    if ((threadIdx.x & 63) == 0) {
+        votes[wave][0] = all_one;
+        votes[wave][1] = all64;
+        votes[wave][2] = all128;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        info[0] = pair ? 1 : 0;
-        info[1] = (int)__float_as_uint(long_step[0]);
-        info[2] = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int c[2], lng[2];
+        for (int k = 0; k < 2; ++k) {
+            int v[3] = {1, 1, 1};
+            for (int w = 0; w < kWavesPerUnit; ++w)
+                for (int q = 0; q < 3; ++q) v[q] &= votes[k * kWavesPerUnit + w][q];
+            c[k] = allow_lines && v[1] ? kClassLines : v[0] ? kClassOneStep : kClassGeneral;
+            lng[k] = v[2];
+        }
+        const bool has_second = 2 * (int64_t)blockIdx.x + 1 < units;
+        const bool pair = allow_lines && has_second && lng[0] && lng[1] &&
+                          __float_as_uint(wg_step[0][2]) == __float_as_uint(wg_step[1][2]);
+        cls[2 * (int64_t)blockIdx.x] = pair ? kClassLongPair : c[0];
+        if (has_second) cls[2 * (int64_t)blockIdx.x + 1] = pair ? kClassLongPair : c[1];
+        if (blockIdx.x == 0) {
+            info[0] = pair ? 1 : 0;
+            info[1] = (int)__float_as_uint(wg_step[0][2]);
+            info[2] = 0;
+        }
     }
 }
 
@@ -1106,8 +1120,8 @@ int launch_classify(const float *x, const float *y, const float *z, int N, bool 
 {
     const int64_t blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
     const int64_t pairs = (blocks + 1) / 2;
-    fhd_classify_kernel<<<dim3((unsigned)pairs), dim3(kBlock), 0, stream>>>(x, y, z, N, blocks,
-                                                                             allow_lines ? 1 : 0, cls, info);
+    fhd_classify_kernel<<<dim3((unsigned)pairs), dim3(kClassifyBlock), 0, stream>>>(x, y, z, N, blocks,
+                                                                                     allow_lines ? 1 : 0, cls, info);
     return launch_status("fhd_classify_kernel launch");
 }
 
