@@ -250,8 +250,8 @@ def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 16) -> float:
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
     "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
-            "sha256": "2742cfcc1f402b8272f7e7e481d7d301752f5bf1a17889fdfa5beb6c77d42336",
-            "bytes_per_launch": (212191.0 * 2.0 + 49281.0 * 1.0) * 1024},
+            "sha256": "06682e06fa3978508c2a95b7fe2bbf787202fa20fad9475ffb59727405e29ea5",
+            "bytes_per_launch": (212442.3 * 2.0 + 49262.0 * 1.0) * 1024},
     "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
              "sha256": "b1b1479f1a3565e78aa09c4f94013be3f4790b1f2dfc96d2775dd1407cc3389f",
              "bytes_per_launch": (7881.0 * 2.0 + 49152.0 * 1.0) * 1024},
