@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kVecBlock) void dot_partial_kernel(
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int w = kVecBlock / 2; w > 0; w >>= 1) {
-        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
     if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kVecBlock) void dot_final_kernel(const double *__re
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int w = kVecBlock / 2; w > 0; w >>= 1) {
-        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
     if (threadIdx.x != 0) return;
