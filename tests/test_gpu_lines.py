@@ -240,3 +240,16 @@ def test_long_lines_table_and_in_kernel_factors_agree_bitwise(dev):
     h = ga[0].size
     for p in range(2):
         assert np.array_equal(r1[p][:h], r2[p][h:]) and np.array_equal(r1[p][h:], r2[p][:h])
+
+
+def test_long_pairs_then_a_ragged_partial_unit(dev):
+    """Two long-line pairs followed by 100 random voxels (a partial third
+    pair's first unit): the partial unit takes a vector path, the pairs the
+    long-line form; the whole result meets the oracle gate."""
+    g = inputs.coords_from_axis(128, 32, 4, (-0.5, 1.0 / 128, -0.5, 1.0 / 32, 0.0, 0.25))
+    r = inputs.random_case(100, 1, seed=77)
+    x, y, z = (np.concatenate((a, r[n])) for a, n in zip(g, ("x", "y", "z")))
+    c = dict(inputs.random_case(1, 700, seed=78, kmax=64.0), x=x, y=y, z=z)
+    assert classes(c)[:4] == [3, 3, 3, 3] and classes(c)[4] != 3
+    rr, ri = gpu_fhd(c, dev)
+    check("long pairs + ragged unit", c, rr, ri)
