@@ -250,14 +250,14 @@ def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 16) -> float:
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 TRAFFIC = {
     "fhd": {"workload": "spiral128", "sources": ["fhd.hip", "fhd_internal.h"],
-            "sha256": "06682e06fa3978508c2a95b7fe2bbf787202fa20fad9475ffb59727405e29ea5",
-            "bytes_per_launch": (212442.3 * 2.0 + 49262.0 * 1.0) * 1024},
+            "sha256": "700209e517e5110bf56990065da5d5492a2c683198a4c0d50e0f2352043cd72e",
+            "bytes_per_launch": (213337.7 * 2.0 + 49224.3 * 1.0) * 1024},
     "grid": {"workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
              "sha256": "b1b1479f1a3565e78aa09c4f94013be3f4790b1f2dfc96d2775dd1407cc3389f",
              "bytes_per_launch": (7881.0 * 2.0 + 49152.0 * 1.0) * 1024},
     "forward": {"workload": "spiral128", "sources": ["fhd_forward.hip", "fhd_internal.h"],
-                "sha256": "0cb29af5c5f7694c4c83cde1b24d4410e4943e133d3d23502514d0919befbf4b",
-                "bytes_per_launch": (75084.0 * 2.0 + 8594.0 * 1.0) * 1024},
+                "sha256": "9d2169da1eeef71dd5922037a019fdccd37625bf2540d492141f3ceaed2a8aa1",
+                "bytes_per_launch": (75065.7 * 2.0 + 8594.0 * 1.0) * 1024},
 }
 
 
