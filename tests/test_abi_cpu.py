@@ -23,6 +23,7 @@ def lib():
     lib = ctypes.CDLL(build.lib_path("libfhd.so"))
     vp = ctypes.c_void_p
     lib.fhd_compute.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
+    lib.fhd_scatter.argtypes = [vp] * 10 + [ctypes.c_int, ctypes.c_int, vp]
     lib.fhd_pack.argtypes = [vp] * 5 + [ctypes.c_int, vp, ctypes.c_int64, vp]
     lib.fhd_gather.argtypes = [vp, ctypes.c_int] + [vp] * 5 + [ctypes.c_int, vp]
     lib.fhd_packed_bytes.argtypes = [ctypes.c_int]
@@ -270,3 +271,26 @@ def test_normal_and_cg_grid_argument_checks(lib):
                            None) == FHD_ERR_INVALID_ARG
     assert lib.fhd_cg_grid(*args, 8, 4, 0, 4, ax, 1, None, None, 3, 0.0, d, None, None) == FHD_OK
     assert done.value == 0
+
+
+def test_scatter_argument_checks(lib):
+    """fhd_scatter shares fhd_compute's contract: sizes, NULLs, alignment and
+    overlap are rejected on the host before any HIP call."""
+    assert lib.fhd_scatter(*[None] * 10, -1, 4, None) == FHD_ERR_INVALID_ARG
+    assert "M < 0" in _last(lib)
+    assert lib.fhd_scatter(*[None] * 10, 4, -1, None) == FHD_ERR_INVALID_ARG
+    assert "N < 0" in _last(lib)
+    assert lib.fhd_scatter(*[None] * 10, 5, 0, None) == FHD_OK
+    fake = [0x100000 * (i + 1) for i in range(10)]
+    args = list(fake)
+    args[3] = None
+    assert lib.fhd_scatter(*args, 16, 16, None) == FHD_ERR_INVALID_ARG
+    assert "Dr" in _last(lib)
+    args = list(fake)
+    args[7] += 2
+    assert lib.fhd_scatter(*args, 16, 16, None) == FHD_ERR_INVALID_ARG
+    assert "aligned" in _last(lib)
+    args = list(fake)
+    args[9] = args[8] + 8
+    assert lib.fhd_scatter(*args, 16, 16, None) == FHD_ERR_INVALID_ARG
+    assert "overlaps" in _last(lib)
