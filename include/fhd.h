@@ -43,6 +43,37 @@ extern "C" {
 #define FHD_ERR_HIP (-2)         /* a HIP runtime or launch error */
 #define FHD_ERR_ALLOC (-3)       /* the library could not get its workspace */
 
+/*
+ * Paths (the `paths` argument of the *_paths entry points). Voxels are
+ * taken in units of 4096 consecutive ones. A unit whose aligned runs of 64
+ * (or, for a pair of units, 128) voxels are lines along x with one common
+ * step -- same y and z bitwise, x_v = x_0 + v dx rounded once to fp32; the
+ * rows of any x-fastest grid whose rows are a multiple of 64 voxels -- can
+ * be summed on the matrix cores: the voxels pair up about each line's
+ * centre and F^H D (or F) becomes real matrix products of per-line centre
+ * phasors and per-sample cos / sin factors (the same sum, evaluated in a
+ * different order). Every other unit is summed on the vector ALUs in fp32.
+ *
+ *   FHD_GATHER_ALL    (the default of fhd_compute, fhd_gather, fhd_forward,
+ *                     fhd_normal, fhd_cg) lines on the matrix cores with
+ *                     fp32-class products: each fp32 operand is split into
+ *                     an fp16 part and an fp16 remainder (22 significant
+ *                     bits together; amplitudes scaled by a power of two
+ *                     into fp16's range first, and the sums scaled back),
+ *                     three fp16 products per fp32 product with fp32
+ *                     accumulation: per product within about 3 x 2^-24
+ *                     relative of the fp32 product, the same order as fp32
+ *                     rounding and below the hardware sine's error.
+ *   FHD_GATHER_VECTOR every unit on the vector ALUs in fp32.
+ *   FHD_GATHER_BF16X3 lines on the matrix cores as above but with bf16 parts
+ *                     (16 significant bits together): per product within
+ *                     about 3 x 2^-17 relative, roughly 1e-5 relative on a
+ *                     sum. Faster on some shapes; an explicit opt-in.
+ */
+#define FHD_GATHER_ALL 0
+#define FHD_GATHER_VECTOR 1
+#define FHD_GATHER_BF16X3 2
+
 /* Arithmetic of the grid form's matrix products (fhd_compute_grid). */
 #define FHD_GRID_FP32 0   /* fp32 matrix-core products, fp32 accumulation */
 #define FHD_GRID_BF16X3 1 /* each fp32 operand split into two bf16 parts,
@@ -54,8 +85,11 @@ extern "C" {
  * rho = F^H D over N voxels and M samples (section 17.3, F^H D equation).
  * Runs the loop-fission pre-pass (fhd_pack, section 17.3.2) into a
  * stream-ordered workspace of fhd_packed_bytes(M) bytes that the library
- * allocates and frees on `stream`, then the gather kernel (fhd_gather,
- * one lane per voxel with no atomics, section 17.3.1).
+ * allocates and frees on `stream`, then the gather (fhd_gather, one lane
+ * per voxel with no atomics, section 17.3.1) with the default paths,
+ * FHD_GATHER_ALL: units of lines along x on the matrix cores with
+ * fp32-class split-fp16 products, the rest on the vector ALUs in fp32 (see
+ * the paths above).
  *   kx, ky, kz, Dr, Di : M fp32 values each (read only)
  *   x, y, z            : N fp32 values each (read only)
  *   rho_r, rho_i       : N fp32 values each (written); they must not
@@ -63,12 +97,24 @@ extern "C" {
  *   M >= 0, N >= 0     : M = 0 writes zeros (an empty sum); N = 0 does
  *                        nothing. Pointers may be NULL only when the
  *                        matching size is 0.
+ * Non-finite inputs give non-finite outputs where they enter the sum.
  * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
  */
 int fhd_compute(const float *kx, const float *ky, const float *kz,
                 const float *Dr, const float *Di,
                 const float *x, const float *y, const float *z,
                 float *rho_r, float *rho_i, int M, int N, void *stream);
+
+/*
+ * fhd_compute with a choice of paths (FHD_GATHER_ALL, FHD_GATHER_VECTOR or
+ * FHD_GATHER_BF16X3; anything else is FHD_ERR_INVALID_ARG). Same arguments,
+ * workspace and errors otherwise.
+ */
+int fhd_compute_paths(const float *kx, const float *ky, const float *kz,
+                      const float *Dr, const float *Di,
+                      const float *x, const float *y, const float *z,
+                      float *rho_r, float *rho_i, int M, int N, int paths,
+                      void *stream);
 
 /*
  * rho = F^H D in the scatter form that section 17.3.1 compares with the
@@ -113,37 +159,32 @@ int fhd_pack(const float *kx, const float *ky, const float *kz,
  * Gather kernel over packed k-space (section 17.3.1, gather form; 17.3.3,
  * accumulators in registers; 17.3.4, every lane reads the same sample at
  * once; 17.3.5, hardware sin/cos). rho = F^H D for the M samples that
- * fhd_pack wrote into `packed` (same M).
+ * fhd_pack wrote into `packed` (same M), with the default paths
+ * (FHD_GATHER_ALL: lines on the matrix cores in fp32-class split fp16, the
+ * rest on the vector ALUs in fp32).
  *   packed       : fhd_packed_bytes(M) bytes written by fhd_pack (read only),
  *                  16-byte aligned
  *   x, y, z      : N fp32 values each (read only)
  *   rho_r, rho_i : N fp32 values each (written), not overlapping any input
- * M = 0 writes zeros; N = 0 does nothing. The voxels are taken in units of
- * 4096 consecutive ones. A whole unit whose aligned runs of 64 voxels are
- * lines along x with one common step (same y and z bitwise, x_v = x_0 +
- * v dx rounded once; any x-fastest grid whose rows are a multiple of 64
- * voxels) is summed on the matrix cores in split bf16 (about 1e-5
- * relative); every other unit in fp32 on the vector ALUs. The per-voxel
- * summation order is fixed, so repeated calls give bitwise identical
- * results. The library allocates and frees a small stream-ordered
- * workspace on `stream` (unit classes; partial sums when the voxels are too
- * few to fill the GPU).
+ * M = 0 writes zeros; N = 0 does nothing. The per-voxel summation order is
+ * fixed, so repeated calls give bitwise identical results. The library
+ * allocates and frees a stream-ordered workspace on `stream`: the unit
+ * classes, on the matrix-core paths the samples' cos / sin factor table
+ * (16 KB per 32 samples: 49 MB at M = 100,000), and the partial sums
+ * (2 x 4 bytes per voxel and part) when the voxels are too few to fill
+ * the GPU in one pass over the samples.
  * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
  */
 int fhd_gather(const void *packed, int M,
                const float *x, const float *y, const float *z,
                float *rho_r, float *rho_i, int N, void *stream);
 
-/* Paths fhd_gather_paths may take. */
-#define FHD_GATHER_ALL 0    /* as fhd_gather: lines on the matrix cores */
-#define FHD_GATHER_VECTOR 1 /* vector-ALU fp32 paths only, for every unit */
-
 /*
- * fhd_gather with a choice of paths: `paths` is FHD_GATHER_ALL (identical
- * to fhd_gather) or FHD_GATHER_VECTOR (units of lines take the fp32 ramp
- * paths of the vector ALUs instead of the split-bf16 matrix cores: fp32
- * arithmetic throughout, about 1e-6 relative). Other arguments and errors
- * as fhd_gather; any other `paths` is FHD_ERR_INVALID_ARG.
+ * fhd_gather with a choice of paths: FHD_GATHER_ALL (identical to
+ * fhd_gather), FHD_GATHER_VECTOR (every unit on the vector ALUs in fp32)
+ * or FHD_GATHER_BF16X3 (lines on the matrix cores in split bf16). Other
+ * arguments and errors as fhd_gather; any other `paths` is
+ * FHD_ERR_INVALID_ARG.
  */
 int fhd_gather_paths(const void *packed, int M,
                      const float *x, const float *y, const float *z,
@@ -167,7 +208,8 @@ int fhd_gather_paths(const void *packed, int M,
  * voxels along x with one common step (same y and z bitwise, x_v = x_0 +
  * v dx rounded once; any x-fastest grid whose rows are a multiple of 128
  * voxels and whose voxel count is a multiple of 8192), F runs on the
- * matrix cores in split bf16 (about 1e-5 relative); otherwise on the
+ * matrix cores with fp32-class split-fp16 products (FHD_GATHER_ALL; each
+ * line's operands scaled by its own power of two); otherwise on the
  * vector ALUs in fp32 (the form fhd_forward_pack / fhd_forward_gather
  * always take). The choice is made on the device; the library allocates
  * its stream-ordered workspaces on `stream`.
@@ -177,6 +219,17 @@ int fhd_forward(const float *kx, const float *ky, const float *kz,
                 const float *x, const float *y, const float *z,
                 const float *rho_r, const float *rho_i,
                 float *Dr, float *Di, int M, int N, void *stream);
+
+/*
+ * fhd_forward with a choice of paths: FHD_GATHER_ALL (identical to
+ * fhd_forward), FHD_GATHER_VECTOR (the vector form always) or
+ * FHD_GATHER_BF16X3 (the line form in split bf16 where it applies). Any
+ * other value is FHD_ERR_INVALID_ARG; otherwise as fhd_forward.
+ */
+int fhd_forward_paths(const float *kx, const float *ky, const float *kz,
+                      const float *x, const float *y, const float *z,
+                      const float *rho_r, const float *rho_i,
+                      float *Dr, float *Di, int M, int N, int paths, void *stream);
 
 /*
  * Pre-pass of F: packs the voxels and the image into `packed` in the record
@@ -210,8 +263,8 @@ int fhd_forward_gather(const void *packed, int N,
  * 17.3.2). Runs F into a k-space temporary and F^H back, all in one
  * stream-ordered workspace of fhd_packed_bytes(N) + fhd_packed_bytes(M) +
  * 8*M bytes (plus the smaller ones fhd_forward and fhd_gather take). F and
- * F^H each take their matrix-core form where fhd_forward and fhd_gather
- * would.
+ * F^H each take their matrix-core form (fp32-class split fp16) where
+ * fhd_forward and fhd_gather would.
  *   kx, ky, kz       : M fp32 values each (read only)
  *   x, y, z, p_r/_i  : N fp32 values each (read only)
  *   q_r, q_i         : N fp32 values each (written), not overlapping any
@@ -223,6 +276,13 @@ int fhd_normal(const float *kx, const float *ky, const float *kz,
                const float *x, const float *y, const float *z,
                const float *p_r, const float *p_i,
                float *q_r, float *q_i, int M, int N, void *stream);
+
+/* fhd_normal with a choice of paths for both F and F^H (as
+ * fhd_forward_paths and fhd_gather_paths). */
+int fhd_normal_paths(const float *kx, const float *ky, const float *kz,
+                     const float *x, const float *y, const float *z,
+                     const float *p_r, const float *p_i,
+                     float *q_r, float *q_i, int M, int N, int paths, void *stream);
 
 /*
  * F^H D for voxels on a Cartesian grid, as a complex matrix product on the
@@ -311,6 +371,15 @@ int fhd_cg(const float *kx, const float *ky, const float *kz,
            float *rho_r, float *rho_i, int M, int N, int max_iter, float tol,
            int *iters_done, float *residuals, void *stream);
 
+/* fhd_cg with a choice of paths for every F and F^H it applies
+ * (FHD_GATHER_ALL, the default, FHD_GATHER_VECTOR or FHD_GATHER_BF16X3;
+ * anything else is FHD_ERR_INVALID_ARG). */
+int fhd_cg_paths(const float *kx, const float *ky, const float *kz,
+                 const float *Dr, const float *Di,
+                 const float *x, const float *y, const float *z,
+                 float *rho_r, float *rho_i, int M, int N, int max_iter, float tol,
+                 int *iters_done, float *residuals, int paths, void *stream);
+
 /* Workspace bytes fhd_cg allocates for M samples, N voxels and max_iter
  * iterations (-1 if any is negative). */
 int64_t fhd_cg_workspace_bytes(int M, int N, int max_iter);
@@ -351,6 +420,32 @@ int fhd_cg_grid(const float *kx, const float *ky, const float *kz,
  * chunk and workgroup size (threads). Any pointer may be NULL.
  */
 void fhd_gather_config(int *voxels_per_lane, int *samples_per_chunk, int *block_threads);
+
+/*
+ * Measurement hook, not part of any computation. After this call, the
+ * calling thread's next `count` launches of the library kernel named
+ * `kernel` record events[2*i] on their stream just before launch i and
+ * events[2*i + 1] just after it, so hipEventElapsedTime(events[2*i],
+ * events[2*i + 1]) is that launch's duration on the GPU. Names are the
+ * kernels' as a profiler lists them, with template arguments:
+ * "fhd_gather_long_lines_kernel<true>" (split fp16) or "<false>" (split
+ * bf16), "fhd_gather_lines_kernel<true>"/"<false>",
+ * "fhd_gather_kernel<16, true>" (one-step ramps) or "<16, false>",
+ * "fhd_forward_lines_kernel<true>"/"<false>",
+ * "fhd_forward_gather_kernel<2>", "fhd_grid_kernel",
+ * "fhd_grid_bf16x3_kernel<4>"/"<2>", "fhd_forward_grid_bf16x3_kernel".
+ *   kernel : NUL-terminated name (copied), or NULL to disarm
+ *   events : 2*count hipEvent_t created by the caller (the handles are
+ *            copied; the events must live until they have been recorded)
+ *   count  : launches to record, >= 0 (0 disarms)
+ * Launches past `count`, of other kernels or on other threads record
+ * nothing. Errors: FHD_ERR_INVALID_ARG (count < 0, NULL events or a NULL
+ * handle among them; the hook is then disarmed).
+ */
+int fhd_time_kernel(const char *kernel, void *const *events, int count);
+
+/* Launches recorded on the calling thread since its last fhd_time_kernel. */
+int fhd_timed_launches(void);
 
 /* Static description of a status code. Never NULL. */
 const char *fhd_status_string(int status);

@@ -23,6 +23,7 @@ FHD_GRID_FP32 = 0
 FHD_GRID_BF16X3 = 1
 FHD_GATHER_ALL = 0
 FHD_GATHER_VECTOR = 1
+FHD_GATHER_BF16X3 = 2
 
 LIBRARY = lib_path("libfhd.so")
 
@@ -58,6 +59,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     fp, vp, i32, i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.fhd_compute.argtypes = [fp] * 10 + [i32, i32, vp]
     lib.fhd_compute.restype = i32
+    lib.fhd_compute_paths.argtypes = [fp] * 10 + [i32, i32, i32, vp]
+    lib.fhd_compute_paths.restype = i32
     lib.fhd_scatter.argtypes = [fp] * 10 + [i32, i32, vp]
     lib.fhd_scatter.restype = i32
     lib.fhd_packed_bytes.argtypes = [i32]
@@ -70,15 +73,22 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_gather_paths.restype = i32
     lib.fhd_forward.argtypes = [fp] * 10 + [i32, i32, vp]
     lib.fhd_forward.restype = i32
+    lib.fhd_forward_paths.argtypes = [fp] * 10 + [i32, i32, i32, vp]
+    lib.fhd_forward_paths.restype = i32
     lib.fhd_forward_pack.argtypes = [fp] * 5 + [i32, vp, i64, vp]
     lib.fhd_forward_pack.restype = i32
     lib.fhd_forward_gather.argtypes = [vp, i32] + [fp] * 5 + [i32, vp]
     lib.fhd_forward_gather.restype = i32
     lib.fhd_normal.argtypes = [fp] * 10 + [i32, i32, vp]
     lib.fhd_normal.restype = i32
+    lib.fhd_normal_paths.argtypes = [fp] * 10 + [i32, i32, i32, vp]
+    lib.fhd_normal_paths.restype = i32
     lib.fhd_cg.argtypes = [fp] * 10 + [i32, i32, i32, ctypes.c_float,
                                        ctypes.POINTER(ctypes.c_int), ctypes.c_void_p, vp]
     lib.fhd_cg.restype = i32
+    lib.fhd_cg_paths.argtypes = [fp] * 10 + [i32, i32, i32, ctypes.c_float,
+                                             ctypes.POINTER(ctypes.c_int), ctypes.c_void_p, i32, vp]
+    lib.fhd_cg_paths.restype = i32
     lib.fhd_cg_workspace_bytes.argtypes = [i32, i32, i32]
     lib.fhd_cg_workspace_bytes.restype = i64
     fpp = ctypes.POINTER(ctypes.c_float)
@@ -93,6 +103,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_cg_grid.argtypes = ([fp] * 5 + [i32] * 4 + [fpp, i32, fp, fp, i32, ctypes.c_float,
                                                       ctypes.POINTER(ctypes.c_int), fp, vp])
     lib.fhd_cg_grid.restype = i32
+    lib.fhd_time_kernel.argtypes = [ctypes.c_char_p, ctypes.c_void_p, i32]
+    lib.fhd_time_kernel.restype = i32
+    lib.fhd_timed_launches.argtypes = []
+    lib.fhd_timed_launches.restype = i32
     lib.fhd_gather_config.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
     lib.fhd_gather_config.restype = None
     lib.fhd_status_string.argtypes = [i32]
@@ -140,8 +154,10 @@ def fhd_packed_bytes(M: int) -> int:
     return int(n)
 
 
-def fhd_compute(kx, ky, kz, Dr, Di, x, y, z, rho_r=None, rho_i=None, stream=None):
-    """rho = F^H D; returns (rho_r, rho_i), float32 tensors on x's device."""
+def fhd_compute(kx, ky, kz, Dr, Di, x, y, z, rho_r=None, rho_i=None, stream=None,
+                paths: int | None = None):
+    """rho = F^H D; returns (rho_r, rho_i), float32 tensors on x's device.
+    paths=None calls fhd_compute; otherwise fhd_compute_paths with it."""
     lib = load()
     M, N = kx.numel(), x.numel()
     dev = x.device
@@ -154,7 +170,11 @@ def fhd_compute(kx, ky, kz, Dr, Di, x, y, z, rho_r=None, rho_i=None, stream=None
     ptrs += [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"),
                                                (rho_r, "rho_r"), (rho_i, "rho_i"))]
     with torch.cuda.device(dev):
-        _check(lib, lib.fhd_compute(*ptrs, M, N, _stream(dev, stream)), "fhd_compute")
+        if paths is None:
+            _check(lib, lib.fhd_compute(*ptrs, M, N, _stream(dev, stream)), "fhd_compute")
+        else:
+            _check(lib, lib.fhd_compute_paths(*ptrs, M, N, int(paths), _stream(dev, stream)),
+                   "fhd_compute_paths")
     return rho_r, rho_i
 
 
@@ -196,8 +216,8 @@ def fhd_pack(kx, ky, kz, Dr, Di, packed: torch.Tensor, stream=None) -> torch.Ten
 def fhd_gather(packed: torch.Tensor, M: int, x, y, z, rho_r=None, rho_i=None, stream=None,
                paths: int | None = None):
     """Gather over a packed k-space of M samples; returns (rho_r, rho_i).
-    paths=None calls fhd_gather; FHD_GATHER_ALL or FHD_GATHER_VECTOR calls
-    fhd_gather_paths with it."""
+    paths=None calls fhd_gather; FHD_GATHER_ALL, FHD_GATHER_VECTOR or
+    FHD_GATHER_BF16X3 calls fhd_gather_paths with it."""
     lib = load()
     N = x.numel()
     dev = x.device
@@ -221,8 +241,10 @@ def fhd_gather(packed: torch.Tensor, M: int, x, y, z, rho_r=None, rho_i=None, st
     return rho_r, rho_i
 
 
-def fhd_forward(kx, ky, kz, x, y, z, rho_r, rho_i, Dr=None, Di=None, stream=None):
-    """D = F rho; returns (Dr, Di), float32 tensors on kx's device."""
+def fhd_forward(kx, ky, kz, x, y, z, rho_r, rho_i, Dr=None, Di=None, stream=None,
+                paths: int | None = None):
+    """D = F rho; returns (Dr, Di), float32 tensors on kx's device.
+    paths=None calls fhd_forward; otherwise fhd_forward_paths with it."""
     lib = load()
     M, N = kx.numel(), x.numel()
     dev = kx.device
@@ -235,7 +257,11 @@ def fhd_forward(kx, ky, kz, x, y, z, rho_r, rho_i, Dr=None, Di=None, stream=None
                                                (rho_r, "rho_r"), (rho_i, "rho_i"))]
     ptrs += [_vec(t, nm, M, dev) for t, nm in ((Dr, "Dr"), (Di, "Di"))]
     with torch.cuda.device(dev):
-        _check(lib, lib.fhd_forward(*ptrs, M, N, _stream(dev, stream)), "fhd_forward")
+        if paths is None:
+            _check(lib, lib.fhd_forward(*ptrs, M, N, _stream(dev, stream)), "fhd_forward")
+        else:
+            _check(lib, lib.fhd_forward_paths(*ptrs, M, N, int(paths), _stream(dev, stream)),
+                   "fhd_forward_paths")
     return Dr, Di
 
 
@@ -276,8 +302,10 @@ def fhd_forward_gather(packed: torch.Tensor, N: int, kx, ky, kz, Dr=None, Di=Non
     return Dr, Di
 
 
-def fhd_normal(kx, ky, kz, x, y, z, p_r, p_i, q_r=None, q_i=None, stream=None):
-    """q = F^H F p; returns (q_r, q_i), float32 tensors on x's device."""
+def fhd_normal(kx, ky, kz, x, y, z, p_r, p_i, q_r=None, q_i=None, stream=None,
+               paths: int | None = None):
+    """q = F^H F p; returns (q_r, q_i), float32 tensors on x's device.
+    paths=None calls fhd_normal; otherwise fhd_normal_paths with it."""
     lib = load()
     M, N = kx.numel(), x.numel()
     dev = x.device
@@ -289,16 +317,21 @@ def fhd_normal(kx, ky, kz, x, y, z, p_r, p_i, q_r=None, q_i=None, stream=None):
     ptrs += [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"), (p_r, "p_r"),
                                                (p_i, "p_i"), (q_r, "q_r"), (q_i, "q_i"))]
     with torch.cuda.device(dev):
-        _check(lib, lib.fhd_normal(*ptrs, M, N, _stream(dev, stream)), "fhd_normal")
+        if paths is None:
+            _check(lib, lib.fhd_normal(*ptrs, M, N, _stream(dev, stream)), "fhd_normal")
+        else:
+            _check(lib, lib.fhd_normal_paths(*ptrs, M, N, int(paths), _stream(dev, stream)),
+                   "fhd_normal_paths")
     return q_r, q_i
 
 
 def fhd_cg(kx, ky, kz, Dr, Di, x, y, z, max_iter: int, tol: float = 0.0,
-           rho_r=None, rho_i=None, stream=None):
+           rho_r=None, rho_i=None, stream=None, paths: int | None = None):
     """CG on F^H F rho = F^H D from rho = 0 (synchronises the stream).
 
     Returns (rho_r, rho_i, iterations, residuals) with residuals the numpy
     array of squared residual norms ||r_k||^2, k = 0..iterations.
+    paths=None calls fhd_cg; otherwise fhd_cg_paths with it.
     """
     import numpy as np
     lib = load()
@@ -315,8 +348,13 @@ def fhd_cg(kx, ky, kz, Dr, Di, x, y, z, max_iter: int, tol: float = 0.0,
     res = np.zeros(int(max_iter) + 1, dtype=np.float32)
     done = ctypes.c_int(0)
     with torch.cuda.device(dev):
-        _check(lib, lib.fhd_cg(*ptrs, M, N, int(max_iter), float(tol), ctypes.byref(done),
-                               res.ctypes.data, _stream(dev, stream)), "fhd_cg")
+        if paths is None:
+            _check(lib, lib.fhd_cg(*ptrs, M, N, int(max_iter), float(tol), ctypes.byref(done),
+                                   res.ctypes.data, _stream(dev, stream)), "fhd_cg")
+        else:
+            _check(lib, lib.fhd_cg_paths(*ptrs, M, N, int(max_iter), float(tol), ctypes.byref(done),
+                                         res.ctypes.data, int(paths), _stream(dev, stream)),
+                   "fhd_cg_paths")
     return rho_r, rho_i, done.value, res[:done.value + 1].copy()
 
 
@@ -438,3 +476,31 @@ def fhd_cg_grid(kx, ky, kz, Dr, Di, shape, axis, max_iter: int, tol: float = 0.0
 def new_packed(M: int, device) -> torch.Tensor:
     """Device buffer of fhd_packed_bytes(M) bytes for fhd_pack / fhd_gather."""
     return torch.empty(max(fhd_packed_bytes(M), 4), dtype=torch.uint8, device=device)
+
+
+class KernelTimer:
+    """Durations of the next `count` launches of one library kernel, from
+    HIP events the library records on the kernel's own stream just before
+    and after each launch (fhd_time_kernel). Arm, run the calls, synchronise,
+    then read durations_ms(); the hook is thread-local."""
+
+    def __init__(self, kernel: str, count: int, device):
+        lib = load()
+        self.kernel = kernel
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * count)]
+        # torch creates its events lazily: record each once so the handles exist
+        s = torch.cuda.current_stream(device)
+        for e in self.events:
+            e.record(s)
+        torch.cuda.synchronize(device)
+        handles = (ctypes.c_void_p * max(1, 2 * count))(*[e.cuda_event for e in self.events])
+        _check(lib, lib.fhd_time_kernel(kernel.encode(), handles, int(count)), "fhd_time_kernel")
+
+    def durations_ms(self) -> list:
+        n = load().fhd_timed_launches()
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(n)]
+
+    @staticmethod
+    def disarm() -> None:
+        load().fhd_time_kernel(None, None, 0)
+

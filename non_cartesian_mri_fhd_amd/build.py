@@ -55,10 +55,28 @@ def build_all(verbose: bool = False) -> list[str]:
     return [build_library(n, verbose) for n in LIBRARIES]
 
 
+def sources_of(name: str) -> list[str]:
+    """Every file a library is built from: its sources, the package's
+    private headers and the public headers."""
+    files = [os.path.join(CSRC, s) for s in LIBRARIES[name]]
+    files += [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".h")]
+    files += [os.path.join(INCLUDE, f) for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h")]
+    return files
+
+
+def is_stale(name: str) -> bool:
+    """Whether the library is missing or older than any file it is built from."""
+    out = lib_path(name)
+    if not os.path.exists(out):
+        return True
+    built = os.path.getmtime(out)
+    return any(os.path.getmtime(f) > built for f in sources_of(name))
+
+
 def ensure_built() -> None:
-    """Build only the libraries that are missing (never rebuilds)."""
+    """Build the libraries that are missing or older than their sources."""
     for n in LIBRARIES:
-        if not os.path.exists(lib_path(n)):
+        if is_stale(n):
             build_library(n)
 
 

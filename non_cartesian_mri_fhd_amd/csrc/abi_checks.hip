@@ -2,6 +2,7 @@
 // every entry point of libfhd.so.
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "fhd_internal.h"
 
@@ -62,6 +63,35 @@ int fail(int status, const std::string &msg)
 }
 
 void clear_error() { g_last_error.clear(); }
+
+namespace {
+// The calling thread's armed kernel events (fhd_time_kernel).
+struct KernelEvents {
+    std::string name;
+    std::vector<hipEvent_t> events;   // start, stop per launch
+    int used = 0;
+};
+thread_local KernelEvents g_kernel_events;
+}  // namespace
+
+int timed_begin(const char *kernel, hipStream_t stream)
+{
+    KernelEvents &k = g_kernel_events;
+    if (k.events.empty() || 2 * k.used >= (int)k.events.size() || k.name != kernel) return -1;
+    const int slot = k.used++;
+    (void)hipEventRecord(k.events[2 * slot], stream);
+    return slot;
+}
+
+void timed_end(int slot, hipStream_t stream)
+{
+    if (slot >= 0) (void)hipEventRecord(g_kernel_events.events[2 * slot + 1], stream);
+}
+
+int fail_paths()
+{
+    return fail(FHD_ERR_INVALID_ARG, "paths must be FHD_GATHER_ALL, FHD_GATHER_VECTOR or FHD_GATHER_BF16X3");
+}
 
 int check_host_side(const Span *spans, int count)
 {
@@ -188,3 +218,22 @@ extern "C" const char *fhd_status_string(int status)
 }
 
 extern "C" const char *fhd_last_error(void) { return fhd::g_last_error.c_str(); }
+
+extern "C" int fhd_time_kernel(const char *kernel, void *const *events, int count)
+{
+    fhd::clear_error();
+    fhd::KernelEvents &k = fhd::g_kernel_events;
+    k.events.clear();
+    k.used = 0;
+    k.name.clear();
+    if (count < 0) return fhd::fail(FHD_ERR_INVALID_ARG, "count < 0");
+    if (count == 0 || !kernel) return FHD_OK;
+    if (!events) return fhd::fail(FHD_ERR_INVALID_ARG, "events is NULL");
+    for (int i = 0; i < 2 * count; ++i)
+        if (!events[i]) return fhd::fail(FHD_ERR_INVALID_ARG, "events holds a NULL event");
+    k.name = kernel;
+    for (int i = 0; i < 2 * count; ++i) k.events.push_back((hipEvent_t)events[i]);
+    return FHD_OK;
+}
+
+extern "C" int fhd_timed_launches(void) { return fhd::g_kernel_events.used; }

@@ -525,15 +525,51 @@ __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (
 // (info[0]) and its lines' step (info[1], bits), and clears info[2] (a flag
 // the forward operator's line pre-pass sets). Two barriers: one to publish
 // each unit's first-lane steps, one to combine the waves' votes.
+//
+// When the grid holds kAmpSlots more workgroups than pairs, workgroup
+// pairs + s instead writes slot s (info[4 + s]) with the largest amplitude
+// (bits) of the chunks c = s kClassifyBlock + t, s kClassifyBlock + t +
+// kAmpSlots kClassifyBlock, ... of `packed` (nchunks chunks): the
+// matrix-core products in fp16 scale the amplitudes by it (amp_shift).
 constexpr int kClassifyBlock = 2 * kBlock;
 __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const float *__restrict__ x,
                                                                       const float *__restrict__ y,
                                                                       const float *__restrict__ z, int N,
                                                                       int64_t units, int allow_lines,
                                                                       int *__restrict__ cls,
-                                                                      int *__restrict__ info)
+                                                                      int *__restrict__ info,
+                                                                      const float4 *__restrict__ packed,
+                                                                      int nchunks)
 {
     constexpr int kWavesPerUnit = kBlock / 64;
+    const int64_t pairs = (units + 1) / 2;
+    if ((int64_t)blockIdx.x >= pairs) {   // an amplitude slot (uniform over the workgroup)
+        __shared__ unsigned wave_max[kClassifyBlock / 64];
+        const int slot = (int)((int64_t)blockIdx.x - pairs);
+        unsigned m = 0u;
+        for (int64_t c = (int64_t)slot * kClassifyBlock + threadIdx.x; c < nchunks;
+             c += (int64_t)kAmpSlots * kClassifyBlock) {
+            // the amplitude field: the chunk's float4s 8 and 9
+            const float4 a = packed[c * kChunkVec4 + 8], b = packed[c * kChunkVec4 + 9];
+            const unsigned v[8] = {__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
+                                   __float_as_uint(a.w), __float_as_uint(b.x), __float_as_uint(b.y),
+                                   __float_as_uint(b.z), __float_as_uint(b.w)};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = v[i] > m ? v[i] : m;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const unsigned t = (unsigned)__shfl_xor((int)m, o);
+            m = t > m ? t : m;
+        }
+        if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x / 64] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 1; w < kClassifyBlock / 64; ++w) m = wave_max[w] > m ? wave_max[w] : m;
+            info[4 + slot] = (int)m;
+        }
+        return;
+    }
     __shared__ float wg_step[2][3];                // each unit's first lane's ramp and line steps
     __shared__ int votes[2 * kWavesPerUnit][3];    // per wave: one step, 64-lines, 128-lines
     const int half = threadIdx.x / kBlock, t = threadIdx.x % kBlock;
@@ -700,10 +736,11 @@ static_assert(kLinePairs == 32, "the pairs fill one 32-column tile");
 static_assert(kUnitVox == 32 * kLineVox * (kLinesBlock / 64), "a wave takes 32 lines of the unit");
 static_assert(kLinesBlock / 64 == 2, "wave 0 forms B_C, wave 1 B_S");
 
+template <bool F16>
 __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_lines_kernel(
     const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
-    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
-    float *__restrict__ out_r, float *__restrict__ out_i, int N)
+    const int *__restrict__ info, const float *__restrict__ x, const float *__restrict__ y,
+    const float *__restrict__ z, float *__restrict__ out_r, float *__restrict__ out_i, int N)
 {
     if (cls[blockIdx.x] != kClassLines) return;
     __shared__ float4 stage[2][kLinesStageVec4];
@@ -713,6 +750,9 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
     const float4 *src = reinterpret_cast<const float4 *>(packed);
     const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // fp16 products: amplitudes scaled by 2^sh into fp16's range, the sums
+    // scaled back at the end (powers of two: exact)
+    const int sh = F16 ? read_amp_shift(info) : 0;
 
     // line 32 wave + col of the unit (the whole unit lies below N)
     const int64_t unit = (int64_t)blockIdx.x * kUnitVox;
@@ -757,16 +797,18 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
             load_chunk(ch + half * kChunkVec4, f);
         }
         __builtin_amdgcn_s_setprio(1);
-        float b[kChunk];
+        float b[kChunk], amp[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) amp[i] = scale_amp<F16>(f[4][i], sh);
         if (wave == 0) {
 #pragma unroll
-            for (int i = 0; i < kChunk; ++i) b[i] = f[4][i] * __builtin_amdgcn_cosf(f[0][i] * tj);
+            for (int i = 0; i < kChunk; ++i) b[i] = amp[i] * __builtin_amdgcn_cosf(f[0][i] * tj);
         } else {
 #pragma unroll
-            for (int i = 0; i < kChunk; ++i) b[i] = f[4][i] * __builtin_amdgcn_sinf(f[0][i] * tj);
+            for (int i = 0; i < kChunk; ++i) b[i] = amp[i] * __builtin_amdgcn_sinf(f[0][i] * tj);
         }
         unsigned bh[4], bl[4];
-        split_bf16<kChunk>(b, bh, bl);
+        split_parts<F16, kChunk>(b, bh, bl);
         bshare[kb][2 * wave + 0][half][col] = (u32x4){bh[0], bh[1], bh[2], bh[3]};
         bshare[kb][2 * wave + 1][half][col] = (u32x4){bl[0], bl[1], bl[2], bl[3]};
         float ur[kChunk], ui[kChunk];
@@ -777,28 +819,26 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
             ui[i] = __builtin_amdgcn_sinf(p);
         }
         unsigned wa[4][4];
-        split_bf16<kChunk>(ur, wa[0], wa[1]);
-        split_bf16<kChunk>(ui, wa[2], wa[3]);
-        const bf16x8 arh = as_bf16x8(wa[0]), arl = as_bf16x8(wa[1]);
-        const bf16x8 aih = as_bf16x8(wa[2]), ail = as_bf16x8(wa[3]);
+        split_parts<F16, kChunk>(ur, wa[0], wa[1]);
+        split_parts<F16, kChunk>(ui, wa[2], wa[3]);
+        const u32x4 arh = {wa[0][0], wa[0][1], wa[0][2], wa[0][3]}, arl = {wa[1][0], wa[1][1], wa[1][2], wa[1][3]};
+        const u32x4 aih = {wa[2][0], wa[2][1], wa[2][2], wa[2][3]}, ail = {wa[3][0], wa[3][1], wa[3][2], wa[3][3]};
         __builtin_amdgcn_s_setprio(0);
         lds_barrier();   // this group's B is in LDS
-        const bf16x8 bch = __builtin_bit_cast(bf16x8, bshare[kb][0][half][col]);
-        const bf16x8 bcl = __builtin_bit_cast(bf16x8, bshare[kb][1][half][col]);
-        const bf16x8 bsh = __builtin_bit_cast(bf16x8, bshare[kb][2][half][col]);
-        const bf16x8 bsl = __builtin_bit_cast(bf16x8, bshare[kb][3][half][col]);
-        prc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bch, prc, 0, 0, 0);
-        pic = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, bch, pic, 0, 0, 0);
-        pis = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, bsh, pis, 0, 0, 0);
-        prs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bsh, prs, 0, 0, 0);
-        prc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bcl, prc, 0, 0, 0);
-        pic = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, bcl, pic, 0, 0, 0);
-        pis = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aih, bsl, pis, 0, 0, 0);
-        prs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arh, bsl, prs, 0, 0, 0);
-        prc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arl, bch, prc, 0, 0, 0);
-        pic = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ail, bch, pic, 0, 0, 0);
-        pis = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ail, bsh, pis, 0, 0, 0);
-        prs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(arl, bsh, prs, 0, 0, 0);
+        const u32x4 bch = bshare[kb][0][half][col], bcl = bshare[kb][1][half][col];
+        const u32x4 bsh = bshare[kb][2][half][col], bsl = bshare[kb][3][half][col];
+        prc = mfma32<F16>(arh, bch, prc);
+        pic = mfma32<F16>(aih, bch, pic);
+        pis = mfma32<F16>(aih, bsh, pis);
+        prs = mfma32<F16>(arh, bsh, prs);
+        prc = mfma32<F16>(arh, bcl, prc);
+        pic = mfma32<F16>(aih, bcl, pic);
+        pis = mfma32<F16>(aih, bsl, pis);
+        prs = mfma32<F16>(arh, bsl, prs);
+        prc = mfma32<F16>(arl, bch, prc);
+        pic = mfma32<F16>(ail, bch, pic);
+        pis = mfma32<F16>(ail, bsh, pis);
+        prs = mfma32<F16>(arl, bsh, prs);
         kb ^= 1;
     };
     for (int st = 0; st < nstages; ++st) {
@@ -823,10 +863,10 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int64_t line = unit + (int64_t)(32 * wave + 8 * (r / 4) + 4 * half + (r % 4)) * kLineVox;
-        dst_r[line + kLinePairs + col] = prc[r] - pis[r];
-        dst_i[line + kLinePairs + col] = pic[r] + prs[r];
-        dst_r[line + kLinePairs - 1 - col] = prc[r] + pis[r];
-        dst_i[line + kLinePairs - 1 - col] = pic[r] - prs[r];
+        dst_r[line + kLinePairs + col] = unscale<F16>(prc[r] - pis[r], sh);
+        dst_i[line + kLinePairs + col] = unscale<F16>(pic[r] + prs[r], sh);
+        dst_r[line + kLinePairs - 1 - col] = unscale<F16>(prc[r] + pis[r], sh);
+        dst_i[line + kLinePairs - 1 - col] = unscale<F16>(pic[r] - prs[r], sh);
     }
 }
 
@@ -860,8 +900,6 @@ static_assert(kPairVox == kLongLineVox * 16 * (kLongBlock / 64), "a wave takes 1
 static_assert(kLongTiles == 4 && kLongBlock / 64 == 4, "each wave forms 2 tiles of B_C or B_S");
 static_assert(kLinesStageChunks % kLongGroup == 0, "product steps tile a stage");
 
-typedef float float4v __attribute__((ext_vector_type(4)));
-
 // B operands of one product step (32 samples), laid out as the operands are
 // read: [B_C hi, B_C lo, B_S hi, B_S lo][tile][k quarter][pair in tile],
 // 8 bf16 (one lane's operand) each; a wave reads 64 consecutive entries
@@ -872,9 +910,11 @@ typedef u32x4 LongStepB[4][kLongTiles][4][16];
 // Lane (wave w, lane l) of a step's B: B_C (w < 2) or B_S (w >= 2, as a
 // cosine a quarter turn later) of pair tiles 2 (w % 2) and 2 (w % 2) + 1,
 // pair l % 16 of each, samples 8 (l / 16) .. + 7 (f: their chunk; dx: the
-// step of the lines), split and stored at their place in `dst`.
+// step of the lines; sh: the amplitudes' scaling in the fp16 form), split
+// and stored at their place in `dst`.
+template <bool F16>
 __device__ __forceinline__ void long_step_b(const float (&f)[kFields][kChunk], float dx, int wave,
-                                            int quarter_k, int col, LongStepB &dst)
+                                            int quarter_k, int col, int sh, LongStepB &dst)
 {
     const int part = wave >> 1, t0 = 2 * (wave & 1);
     const float turn = part == 0 ? 0.0f : -0.25f;
@@ -883,12 +923,13 @@ __device__ __forceinline__ void long_step_b(const float (&f)[kFields][kChunk], f
     float b0[kChunk], b1[kChunk];
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-        b0[i] = f[4][i] * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj0, turn));
-        b1[i] = f[4][i] * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj1, turn));
+        const float amp = scale_amp<F16>(f[4][i], sh);
+        b0[i] = amp * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj0, turn));
+        b1[i] = amp * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj1, turn));
     }
     unsigned h0[4], l0[4], h1[4], l1[4];
-    split_bf16<kChunk>(b0, h0, l0);
-    split_bf16<kChunk>(b1, h1, l1);
+    split_parts<F16, kChunk>(b0, h0, l0);
+    split_parts<F16, kChunk>(b1, h1, l1);
     dst[2 * part + 0][t0][quarter_k][col] = (u32x4){h0[0], h0[1], h0[2], h0[3]};
     dst[2 * part + 1][t0][quarter_k][col] = (u32x4){l0[0], l0[1], l0[2], l0[3]};
     dst[2 * part + 0][t0 + 1][quarter_k][col] = (u32x4){h1[0], h1[1], h1[2], h1[3]};
@@ -902,12 +943,14 @@ __device__ __forceinline__ void long_step_b(const float (&f)[kFields][kChunk], f
 // stream's end as zeros. The long-line workgroups whose lines have that
 // step copy them into LDS instead of forming them (same arithmetic, same
 // bits).
+template <bool F16>
 __global__ __launch_bounds__(kLongBlock) void fhd_long_table_kernel(const float *__restrict__ packed, int nchunks,
                                                                     const int *__restrict__ info,
                                                                     float4 *__restrict__ table)
 {
     if (info[0] == 0) return;
     const float dx = __int_as_float(info[1]);
+    const int sh = F16 ? read_amp_shift(info) : 0;
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t chunk = (int64_t)blockIdx.x * kLongGroup + quarter_k;
@@ -929,10 +972,11 @@ __global__ __launch_bounds__(kLongBlock) void fhd_long_table_kernel(const float 
 #pragma unroll
             for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
     }
-    long_step_b(f, dx, wave, quarter_k, col,
-                *reinterpret_cast<LongStepB *>(table + (int64_t)blockIdx.x * kLongStepVec4));
+    long_step_b<F16>(f, dx, wave, quarter_k, col, sh,
+                     *reinterpret_cast<LongStepB *>(table + (int64_t)blockIdx.x * kLongStepVec4));
 }
 
+template <bool F16>
 __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_long_lines_kernel(
     const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
     const int *__restrict__ info, const float4 *__restrict__ table,
@@ -945,6 +989,7 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
     const float4 *src = reinterpret_cast<const float4 *>(packed);
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sh = F16 ? read_amp_shift(info) : 0;
 
     // line 16 wave + col of the pair (both units lie below N)
     const int64_t base = (int64_t)blockIdx.x * kPairVox;
@@ -994,7 +1039,7 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
         } else {
             load_chunk(ch + quarter_k * kChunkVec4, f);
         }
-        if constexpr (!kTable) long_step_b(f, dx, wave, quarter_k, col, bshare[kb]);
+        if constexpr (!kTable) long_step_b<F16>(f, dx, wave, quarter_k, col, sh, bshare[kb]);
         float ur[kChunk], ui[kChunk];
 #pragma unroll
         for (int i = 0; i < kChunk; ++i) {
@@ -1003,10 +1048,10 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
             ui[i] = __builtin_amdgcn_sinf(p);
         }
         unsigned wa[4][4];
-        split_bf16<kChunk>(ur, wa[0], wa[1]);
-        split_bf16<kChunk>(ui, wa[2], wa[3]);
-        const bf16x8 arh = as_bf16x8(wa[0]), arl = as_bf16x8(wa[1]);
-        const bf16x8 aih = as_bf16x8(wa[2]), ail = as_bf16x8(wa[3]);
+        split_parts<F16, kChunk>(ur, wa[0], wa[1]);
+        split_parts<F16, kChunk>(ui, wa[2], wa[3]);
+        const u32x4 arh = {wa[0][0], wa[0][1], wa[0][2], wa[0][3]}, arl = {wa[1][0], wa[1][1], wa[1][2], wa[1][3]};
+        const u32x4 aih = {wa[2][0], wa[2][1], wa[2][2], wa[2][3]}, ail = {wa[3][0], wa[3][1], wa[3][2], wa[3][3]};
         lds_barrier();   // this step's B is in LDS
         // bshare[kb ^ 1] was last read before the barrier just passed
         if constexpr (kTable)
@@ -1020,22 +1065,20 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < kLongTiles; ++t) {
-            const bf16x8 bch = __builtin_bit_cast(bf16x8, bshare[kb][0][t][quarter_k][col]);
-            const bf16x8 bcl = __builtin_bit_cast(bf16x8, bshare[kb][1][t][quarter_k][col]);
-            const bf16x8 bsh = __builtin_bit_cast(bf16x8, bshare[kb][2][t][quarter_k][col]);
-            const bf16x8 bsl = __builtin_bit_cast(bf16x8, bshare[kb][3][t][quarter_k][col]);
-            prc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bch, prc[t], 0, 0, 0);
-            pic[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bch, pic[t], 0, 0, 0);
-            pis[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bsh, pis[t], 0, 0, 0);
-            prs[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bsh, prs[t], 0, 0, 0);
-            prc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bcl, prc[t], 0, 0, 0);
-            pic[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bcl, pic[t], 0, 0, 0);
-            pis[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bsl, pis[t], 0, 0, 0);
-            prs[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bsl, prs[t], 0, 0, 0);
-            prc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arl, bch, prc[t], 0, 0, 0);
-            pic[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ail, bch, pic[t], 0, 0, 0);
-            pis[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ail, bsh, pis[t], 0, 0, 0);
-            prs[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arl, bsh, prs[t], 0, 0, 0);
+            const u32x4 bch = bshare[kb][0][t][quarter_k][col], bcl = bshare[kb][1][t][quarter_k][col];
+            const u32x4 bsh = bshare[kb][2][t][quarter_k][col], bsl = bshare[kb][3][t][quarter_k][col];
+            prc[t] = mfma16<F16>(arh, bch, prc[t]);
+            pic[t] = mfma16<F16>(aih, bch, pic[t]);
+            pis[t] = mfma16<F16>(aih, bsh, pis[t]);
+            prs[t] = mfma16<F16>(arh, bsh, prs[t]);
+            prc[t] = mfma16<F16>(arh, bcl, prc[t]);
+            pic[t] = mfma16<F16>(aih, bcl, pic[t]);
+            pis[t] = mfma16<F16>(aih, bsl, pis[t]);
+            prs[t] = mfma16<F16>(arh, bsl, prs[t]);
+            prc[t] = mfma16<F16>(arl, bch, prc[t]);
+            pic[t] = mfma16<F16>(ail, bch, pic[t]);
+            pis[t] = mfma16<F16>(ail, bsh, pis[t]);
+            prs[t] = mfma16<F16>(arl, bsh, prs[t]);
         }
         __builtin_amdgcn_s_setprio(0);
         kb ^= 1;
@@ -1082,10 +1125,10 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
         for (int r = 0; r < 4; ++r) {
             const int64_t line = base + (int64_t)(16 * wave + 4 * quarter_k + r) * kLongLineVox;
             const int j = 16 * t + col;
-            dst_r[line + kLongPairs + j] = prc[t][r] - pis[t][r];
-            dst_i[line + kLongPairs + j] = pic[t][r] + prs[t][r];
-            dst_r[line + kLongPairs - 1 - j] = prc[t][r] + pis[t][r];
-            dst_i[line + kLongPairs - 1 - j] = pic[t][r] - prs[t][r];
+            dst_r[line + kLongPairs + j] = unscale<F16>(prc[t][r] - pis[t][r], sh);
+            dst_i[line + kLongPairs + j] = unscale<F16>(pic[t][r] + prs[t][r], sh);
+            dst_r[line + kLongPairs - 1 - j] = unscale<F16>(prc[t][r] + pis[t][r], sh);
+            dst_i[line + kLongPairs - 1 - j] = unscale<F16>(pic[t][r] - prs[t][r], sh);
         }
 }
 
@@ -1120,19 +1163,51 @@ int blocks_per_cu(const void *kernel, int block)
 }
 
 int launch_classify(const float *x, const float *y, const float *z, int N, bool allow_lines, int *cls,
-                    int *info, hipStream_t stream)
+                    int *info, hipStream_t stream, bool amp_slots, const float *packed, int M)
 {
     const int64_t blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
     const int64_t pairs = (blocks + 1) / 2;
-    fhd_classify_kernel<<<dim3((unsigned)pairs), dim3(kClassifyBlock), 0, stream>>>(x, y, z, N, blocks,
-                                                                                     allow_lines ? 1 : 0, cls, info);
+    const int nchunks = amp_slots && M > 0 ? (int)(((int64_t)M + kChunk - 1) / kChunk) : 0;
+    const int64_t grid = pairs + (amp_slots ? kAmpSlots : 0);
+    fhd_classify_kernel<<<dim3((unsigned)grid), dim3(kClassifyBlock), 0, stream>>>(
+        x, y, z, N, blocks, allow_lines ? 1 : 0, cls, info, reinterpret_cast<const float4 *>(packed), nchunks);
     return launch_status("fhd_classify_kernel launch");
 }
 
+// The matrix-core instances of one split type (F16: fp16 parts, the
+// default; else bf16 parts).
+template <bool F16>
+int launch_line_instances(const float *packed, int nchunks, int splits, int64_t blocks, int64_t pairs,
+                          int64_t steps, const int *cls, const int *info, float4 *table, const float *x,
+                          const float *y, const float *z, float *part_r, float *part_i, int N,
+                          hipStream_t stream)
+{
+    int rc = FHD_OK;
+    if (steps > 0) {
+        fhd_long_table_kernel<F16><<<dim3((unsigned)steps), dim3(kLongBlock), 0, stream>>>(packed, nchunks, info,
+                                                                                           table);
+        rc = launch_status("fhd_long_table_kernel launch");
+    }
+    if (rc == FHD_OK) {
+        TimedLaunch timed(F16 ? "fhd_gather_long_lines_kernel<true>" : "fhd_gather_long_lines_kernel<false>", stream);
+        fhd_gather_long_lines_kernel<F16><<<dim3((unsigned)pairs, (unsigned)splits), dim3(kLongBlock), 0, stream>>>(
+            packed, nchunks, splits, cls, info, table, x, y, z, part_r, part_i, N);
+        rc = launch_status("fhd_gather_long_lines_kernel launch");
+    }
+    if (rc == FHD_OK) {
+        TimedLaunch timed(F16 ? "fhd_gather_lines_kernel<true>" : "fhd_gather_lines_kernel<false>", stream);
+        fhd_gather_lines_kernel<F16><<<dim3((unsigned)blocks, (unsigned)splits), dim3(kLinesBlock), 0, stream>>>(
+            packed, nchunks, splits, cls, info, x, y, z, part_r, part_i, N);
+        rc = launch_status("fhd_gather_lines_kernel launch");
+    }
+    return rc;
+}
+
 int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
-                  float *rho_r, float *rho_i, int N, hipStream_t stream, bool matrix_cores)
+                  float *rho_r, float *rho_i, int N, hipStream_t stream, int paths)
 {
     if (N == 0) return FHD_OK;
+    const bool matrix_cores = paths != FHD_GATHER_VECTOR;
     const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
     const int64_t blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
     const int64_t pairs = (blocks + 1) / 2;
@@ -1142,14 +1217,14 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
     const int splits =
         matrix_cores
             ? split_count(pairs, nchunks,
-                          blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel), kLongBlock))
+                          blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel<true>), kLongBlock))
             : split_count(blocks, nchunks,
                           blocks_per_cu<2>(reinterpret_cast<const void *>(fhd_gather_kernel<kVox, true>), kBlock));
-    // one workspace: the unit classes and the B-table record, the B table
-    // of the long-line instance (16 KB per 32 samples), then (splits > 1)
-    // the partial sums
-    const size_t cls_bytes = ((size_t)blocks * sizeof(int) + 2 * sizeof(int) + 255) / 256 * 256;
-    const int64_t steps = ((int64_t)nchunks + kLongGroup - 1) / kLongGroup;
+    // one workspace: the unit classes and the info words, the B table of
+    // the long-line instance (16 KB per 32 samples), then (splits > 1) the
+    // partial sums
+    const size_t cls_bytes = ((size_t)blocks * sizeof(int) + kInfoWords * sizeof(int) + 255) / 256 * 256;
+    const int64_t steps = M > 0 ? ((int64_t)nchunks + kLongGroup - 1) / kLongGroup : 0;
     const size_t table_bytes = matrix_cores ? (size_t)steps * kLongStepVec4 * sizeof(float4) : 0;
     const size_t part_bytes = splits > 1 ? (size_t)splits * 2 * N * sizeof(float) : 0;
     char *work = nullptr;
@@ -1166,29 +1241,24 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
         part_r = reinterpret_cast<float *>(work + cls_bytes + table_bytes);
         part_i = part_r + (int64_t)splits * N;
     }
-    int rc = launch_classify(x, y, z, N, matrix_cores, cls, info, stream);
+    // the fp16 products need the largest amplitude: the classification's
+    // extra workgroups reduce it
+    const bool f16 = paths == FHD_GATHER_ALL;
+    int rc = launch_classify(x, y, z, N, matrix_cores, cls, info, stream, f16, packed, M);
     const dim3 grid((unsigned)blocks, (unsigned)splits);
-    if (rc == FHD_OK && matrix_cores && steps > 0) {
-        fhd_long_table_kernel<<<dim3((unsigned)steps), dim3(kLongBlock), 0, stream>>>(packed, nchunks, info,
-                                                                                      table);
-        rc = launch_status("fhd_long_table_kernel launch");
-    }
-    if (rc == FHD_OK && matrix_cores) {
-        fhd_gather_long_lines_kernel<<<dim3((unsigned)pairs, (unsigned)splits), dim3(kLongBlock), 0, stream>>>(
-            packed, nchunks, splits, cls, info, table, x, y, z, part_r, part_i, N);
-        rc = launch_status("fhd_gather_long_lines_kernel launch");
-    }
-    if (rc == FHD_OK && matrix_cores) {
-        fhd_gather_lines_kernel<<<grid, dim3(kLinesBlock), 0, stream>>>(packed, nchunks, splits, cls, x, y,
-                                                                        z, part_r, part_i, N);
-        rc = launch_status("fhd_gather_lines_kernel launch");
-    }
+    if (rc == FHD_OK && matrix_cores)
+        rc = f16 ? launch_line_instances<true>(packed, nchunks, splits, blocks, pairs, steps, cls, info, table, x, y,
+                                               z, part_r, part_i, N, stream)
+                 : launch_line_instances<false>(packed, nchunks, splits, blocks, pairs, steps, cls, info, table, x,
+                                                y, z, part_r, part_i, N, stream);
     if (rc == FHD_OK) {
+        TimedLaunch timed("fhd_gather_kernel<16, true>", stream);
         fhd_gather_kernel<kVox, true><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, cls, x, y,
                                                                           z, part_r, part_i, N);
         rc = launch_status("fhd_gather_kernel<one step> launch");
     }
     if (rc == FHD_OK) {
+        TimedLaunch timed("fhd_gather_kernel<16, false>", stream);
         fhd_gather_kernel<kVox, false><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, cls, x,
                                                                            y, z, part_r, part_i, N);
         rc = launch_status("fhd_gather_kernel launch");
@@ -1248,8 +1318,7 @@ extern "C" int fhd_gather_paths(const void *packed, int M, const float *x, const
     clear_error();
     if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
     if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
-    if (paths != FHD_GATHER_ALL && paths != FHD_GATHER_VECTOR)
-        return fail(FHD_ERR_INVALID_ARG, "paths must be FHD_GATHER_ALL or FHD_GATHER_VECTOR");
+    if (!valid_paths(paths)) return fail_paths();
     if (N == 0) return FHD_OK;
     const int64_t nb = (int64_t)N * 4;
     const Span all[] = {{packed, M > 0 ? packed_bytes_for(M) : 0, "packed", 16},
@@ -1259,8 +1328,7 @@ extern "C" int fhd_gather_paths(const void *packed, int M, const float *x, const
     if (rc == FHD_OK) rc = check_no_overlap(all, 6, 4);
     if (rc == FHD_OK) rc = check_device_spans(all, 6);
     if (rc != FHD_OK) return rc;
-    return launch_gather((const float *)packed, M, x, y, z, rho_r, rho_i, N, (hipStream_t)stream,
-                         paths == FHD_GATHER_ALL);
+    return launch_gather((const float *)packed, M, x, y, z, rho_r, rho_i, N, (hipStream_t)stream, paths);
 }
 
 extern "C" int fhd_gather(const void *packed, int M, const float *x, const float *y, const float *z,
@@ -1269,13 +1337,14 @@ extern "C" int fhd_gather(const void *packed, int M, const float *x, const float
     return fhd_gather_paths(packed, M, x, y, z, rho_r, rho_i, N, FHD_GATHER_ALL, stream);
 }
 
-extern "C" int fhd_compute(const float *kx, const float *ky, const float *kz, const float *Dr,
-                           const float *Di, const float *x, const float *y, const float *z,
-                           float *rho_r, float *rho_i, int M, int N, void *stream)
+extern "C" int fhd_compute_paths(const float *kx, const float *ky, const float *kz, const float *Dr,
+                                 const float *Di, const float *x, const float *y, const float *z,
+                                 float *rho_r, float *rho_i, int M, int N, int paths, void *stream)
 {
     clear_error();
     if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
     if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
+    if (!valid_paths(paths)) return fail_paths();
     if (N == 0) return FHD_OK;
     const int64_t mb = (int64_t)M * 4, nb = (int64_t)N * 4;
     const Span all[] = {{kx, mb, "kx"}, {ky, mb, "ky"}, {kz, mb, "kz"}, {Dr, mb, "Dr"},
@@ -1296,11 +1365,18 @@ extern "C" int fhd_compute(const float *kx, const float *ky, const float *kz, co
         }
         rc = launch_pack(kx, ky, kz, Dr, Di, M, packed, s);
     }
-    if (rc == FHD_OK) rc = launch_gather(packed, M, x, y, z, rho_r, rho_i, N, s);
+    if (rc == FHD_OK) rc = launch_gather(packed, M, x, y, z, rho_r, rho_i, N, s, paths);
     if (packed) {
         const hipError_t e = hipFreeAsync(packed, s);
         if (e != hipSuccess && rc == FHD_OK)
             rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
     }
     return rc;
+}
+
+extern "C" int fhd_compute(const float *kx, const float *ky, const float *kz, const float *Dr,
+                           const float *Di, const float *x, const float *y, const float *z,
+                           float *rho_r, float *rho_i, int M, int N, void *stream)
+{
+    return fhd_compute_paths(kx, ky, kz, Dr, Di, x, y, z, rho_r, rho_i, M, N, FHD_GATHER_ALL, stream);
 }

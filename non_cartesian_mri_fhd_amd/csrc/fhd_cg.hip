@@ -183,11 +183,11 @@ int dot(const float *ur, const float *ui, const float *vr, const float *vi, int6
 
 // Ap = F^H F p
 int normal(const float *kx, const float *ky, const float *kz, const float *x, const float *y,
-           const float *z, int M, int N, const CgWork &w, hipStream_t s)
+           const float *z, int M, int N, const CgWork &w, hipStream_t s, int paths)
 {
-    int rc = launch_forward(x, y, z, w.p_r, w.p_i, N, kx, ky, kz, w.d_r, w.d_i, M, w.vox, s);
+    int rc = launch_forward(x, y, z, w.p_r, w.p_i, N, kx, ky, kz, w.d_r, w.d_i, M, w.vox, s, paths);
     if (rc == FHD_OK) rc = launch_pack(kx, ky, kz, w.d_r, w.d_i, M, w.smp, s);
-    if (rc == FHD_OK) rc = launch_gather(w.smp, M, x, y, z, w.ap_r, w.ap_i, N, s);
+    if (rc == FHD_OK) rc = launch_gather(w.smp, M, x, y, z, w.ap_r, w.ap_i, N, s, paths);
     return rc;
 }
 
@@ -297,15 +297,16 @@ extern "C" int64_t fhd_cg_workspace_bytes(int M, int N, int max_iter)
     return work_bytes(M, N, max_iter);
 }
 
-extern "C" int fhd_cg(const float *kx, const float *ky, const float *kz, const float *Dr,
-                      const float *Di, const float *x, const float *y, const float *z,
-                      float *rho_r, float *rho_i, int M, int N, int max_iter, float tol,
-                      int *iters_done, float *residuals, void *stream)
+extern "C" int fhd_cg_paths(const float *kx, const float *ky, const float *kz, const float *Dr,
+                            const float *Di, const float *x, const float *y, const float *z,
+                            float *rho_r, float *rho_i, int M, int N, int max_iter, float tol,
+                            int *iters_done, float *residuals, int paths, void *stream)
 {
     clear_error();
     if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
     if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
     if (max_iter < 0) return fail(FHD_ERR_INVALID_ARG, "max_iter < 0");
+    if (!valid_paths(paths)) return fail_paths();
     if (!iters_done) return fail(FHD_ERR_INVALID_ARG, "iters_done is NULL");
     if (!(tol >= 0.0f)) return fail(FHD_ERR_INVALID_ARG, "tol must be >= 0");
     *iters_done = 0;
@@ -326,14 +327,23 @@ extern "C" int fhd_cg(const float *kx, const float *ky, const float *kz, const f
     rc = run_cg(
         [&] {
             int r = launch_pack(kx, ky, kz, Dr, Di, M, w.smp, s);
-            return r == FHD_OK ? launch_gather(w.smp, M, x, y, z, w.r_r, w.r_i, N, s) : r;
+            return r == FHD_OK ? launch_gather(w.smp, M, x, y, z, w.r_r, w.r_i, N, s, paths) : r;
         },
-        [&] { return normal(kx, ky, kz, x, y, z, M, N, w, s); }, rho_r, rho_i, N, max_iter, tol,
+        [&] { return normal(kx, ky, kz, x, y, z, M, N, w, s, paths); }, rho_r, rho_i, N, max_iter, tol,
         iters_done, residuals, w, s);
     const hipError_t e = hipFreeAsync(ws, s);
     if (e != hipSuccess && rc == FHD_OK)
         rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
     return rc;
+}
+
+extern "C" int fhd_cg(const float *kx, const float *ky, const float *kz, const float *Dr,
+                      const float *Di, const float *x, const float *y, const float *z,
+                      float *rho_r, float *rho_i, int M, int N, int max_iter, float tol,
+                      int *iters_done, float *residuals, void *stream)
+{
+    return fhd_cg_paths(kx, ky, kz, Dr, Di, x, y, z, rho_r, rho_i, M, N, max_iter, tol, iters_done,
+                        residuals, FHD_GATHER_ALL, stream);
 }
 
 // ---------------------------------------------------------------------------

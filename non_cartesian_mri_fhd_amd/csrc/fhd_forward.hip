@@ -427,13 +427,15 @@ constexpr int kFwdStageRegs = (kFwdTileVec4 + kFwdBlock - 1) / kFwdBlock;
 static_assert(kFwdBlock / 64 == kFwdKSteps, "one pre-pass wave per k step");
 static_assert((2 * kUnitVox) % kFwdTileVox == 0, "tiles tile a pair of units");
 
-typedef float float4v __attribute__((ext_vector_type(4)));
-
 // One workgroup per tile of 16 lines: wave s forms k step s of the A
 // operands (lane l: line l % 16, K = 32 s + 8 (l / 16) + i), the first 16
 // lanes of wave 0 the lines' centres; a line that breaks the rule (its unit
 // pair not of class kClassLongPair, or a step other than the first pair's)
-// sets info[2], and the vector form then takes F.
+// sets info[2], and the vector form then takes F. F16: the operands are
+// split into fp16 parts, each line's scaled by a power of two 2^sh (with
+// the line's largest |value| times 2^sh in [2^14, 2^15): amp_shift), and
+// sh is stored in the line's centre record for the gather to undo.
+template <bool F16>
 __global__ __launch_bounds__(kFwdBlock) void fhd_forward_lines_pack_kernel(
     const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
     const float *__restrict__ rho_r, const float *__restrict__ rho_i, const int *__restrict__ cls,
@@ -451,9 +453,37 @@ __global__ __launch_bounds__(kFwdBlock) void fhd_forward_lines_pack_kernel(
         re[i] = sine ? ui - di : ur + dr;      // Q_i | P_r
         im[i] = sine ? dr - ur : ui + di;      // -Q_r | P_i
     }
+    int sh = 0;
+    if constexpr (F16) {
+        // the line's largest magnitude: over the lane's values, the wave's
+        // four lanes of the row, then the four waves (LDS)
+        __shared__ unsigned row_max[kFwdKSteps][kFwdTileLines];
+        unsigned m = 0u;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const unsigned a = __float_as_uint(re[i]) & 0x7fffffffu, b = __float_as_uint(im[i]) & 0x7fffffffu;
+            m = a > m ? a : m;
+            m = b > m ? b : m;
+        }
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) {
+            const unsigned t = (unsigned)__shfl_xor((int)m, o);
+            m = t > m ? t : m;
+        }
+        if (quarter_k == 0) row_max[s][row] = m;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kFwdKSteps; ++w) m = row_max[w][row] > m ? row_max[w][row] : m;
+        sh = amp_shift(m);
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            re[i] = __builtin_ldexpf(re[i], sh);
+            im[i] = __builtin_ldexpf(im[i], sh);
+        }
+    }
     unsigned rh[4], rl[4], ih[4], il[4];
-    split_bf16<kChunk>(re, rh, rl);
-    split_bf16<kChunk>(im, ih, il);
+    split_parts<F16, kChunk>(re, rh, rl);
+    split_parts<F16, kChunk>(im, ih, il);
     u32x4 *t = tiles + (int64_t)blockIdx.x * kFwdTileVec4 + s * 4 * 64 + lane;
     t[0 * 64] = (u32x4){rh[0], rh[1], rh[2], rh[3]};
     t[1 * 64] = (u32x4){rl[0], rl[1], rl[2], rl[3]};
@@ -463,7 +493,7 @@ __global__ __launch_bounds__(kFwdBlock) void fhd_forward_lines_pack_kernel(
         const float x0 = x[base], dx = x[base + 1] - x0;
         const float xc = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x0);
         tiles[(int64_t)blockIdx.x * kFwdTileVec4 + kFwdOpsVec4 + row] =
-            (u32x4){__float_as_uint(xc), __float_as_uint(y[base]), __float_as_uint(z[base]), 0u};
+            (u32x4){__float_as_uint(xc), __float_as_uint(y[base]), __float_as_uint(z[base]), (unsigned)sh};
         const bool ok = info[0] != 0 && cls[base / kUnitVox] == kClassLongPair &&
                         __float_as_uint(dx) == (unsigned)info[1];
         if (!ok) atomicOr(&info[2], 1);
@@ -474,6 +504,7 @@ __global__ __launch_bounds__(kFwdBlock) void fhd_forward_lines_pack_kernel(
 // from 32 w; lane l the sample l % 16 of each of its two columns, rows 4
 // (l / 16) .. + 3 of each tile), tiles of split s of the line stream; writes
 // D (splits == 1) or its partial sums at out + s M.
+template <bool F16>
 __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_forward_lines_kernel(
     const u32x4 *__restrict__ tiles, int ntiles, int splits, const int *__restrict__ info,
     const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
@@ -495,9 +526,9 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) 
         sky[t] = live ? ky[m[t]] : 0.0f;
         skz[t] = live ? kz[m[t]] : 0.0f;
     }
-    // B operands, held for the whole walk: K = 32 s + 8 (l / 16) + i, pair
-    // j = K % 64, cos (K < 64) or sin
-    bf16x8 bh[kFwdColumns][kFwdKSteps], bl[kFwdColumns][kFwdKSteps];
+    // B operands (cos and sin, |B| <= 1: no scaling), held for the whole
+    // walk: K = 32 s + 8 (l / 16) + i, pair j = K % 64, cos (K < 64) or sin
+    u32x4 bh[kFwdColumns][kFwdKSteps], bl[kFwdColumns][kFwdKSteps];
 #pragma unroll
     for (int t = 0; t < kFwdColumns; ++t)
 #pragma unroll
@@ -510,9 +541,9 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) 
                 v[i] = s < kFwdKSteps / 2 ? __builtin_amdgcn_cosf(a) : __builtin_amdgcn_sinf(a);
             }
             unsigned h[4], l[4];
-            split_bf16<kChunk>(v, h, l);
-            bh[t][s] = as_bf16x8(h);
-            bl[t][s] = as_bf16x8(l);
+            split_parts<F16, kChunk>(v, h, l);
+            bh[t][s] = (u32x4){h[0], h[1], h[2], h[3]};
+            bl[t][s] = (u32x4){l[0], l[1], l[2], l[3]};
         }
 
     float dr[kFwdColumns], di[kFwdColumns];
@@ -565,22 +596,20 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) 
 #pragma unroll
         for (int s = 0; s < kFwdKSteps; ++s) {
             const u32x4 *op = &stage[b][s * 4 * 64 + lane];
-            const bf16x8 arh = __builtin_bit_cast(bf16x8, op[0 * 64]);
-            const bf16x8 arl = __builtin_bit_cast(bf16x8, op[1 * 64]);
-            const bf16x8 aih = __builtin_bit_cast(bf16x8, op[2 * 64]);
-            const bf16x8 ail = __builtin_bit_cast(bf16x8, op[3 * 64]);
+            const u32x4 arh = op[0 * 64], arl = op[1 * 64], aih = op[2 * 64], ail = op[3 * 64];
 #pragma unroll
             for (int t = 0; t < kFwdColumns; ++t) {
-                tre[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bh[t][s], tre[t], 0, 0, 0);
-                tim[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bh[t][s], tim[t], 0, 0, 0);
-                tre[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arh, bl[t][s], tre[t], 0, 0, 0);
-                tim[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aih, bl[t][s], tim[t], 0, 0, 0);
-                tre[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arl, bh[t][s], tre[t], 0, 0, 0);
-                tim[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ail, bh[t][s], tim[t], 0, 0, 0);
+                tre[t] = mfma16<F16>(arh, bh[t][s], tre[t]);
+                tim[t] = mfma16<F16>(aih, bh[t][s], tim[t]);
+                tre[t] = mfma16<F16>(arh, bl[t][s], tre[t]);
+                tim[t] = mfma16<F16>(aih, bl[t][s], tim[t]);
+                tre[t] = mfma16<F16>(arl, bh[t][s], tre[t]);
+                tim[t] = mfma16<F16>(ail, bh[t][s], tim[t]);
             }
         }
         __builtin_amdgcn_s_setprio(0);
         // D += conj(V) T for rows 4 (l / 16) + r, with V of the row's centre
+        // (scaled by the row's 2^-sh in the fp16 form)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const u32x4 c = stage[b][kFwdOpsVec4 + 4 * quarter_k + r];
@@ -588,7 +617,8 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) 
 #pragma unroll
             for (int t = 0; t < kFwdColumns; ++t) {
                 const float p = __builtin_fmaf(skx[t], xc, __builtin_fmaf(sky[t], ly, skz[t] * lz));
-                const float vc = __builtin_amdgcn_cosf(p), vs = __builtin_amdgcn_sinf(p);
+                const float vc = unscale<F16>(__builtin_amdgcn_cosf(p), (int)c.w);
+                const float vs = unscale<F16>(__builtin_amdgcn_sinf(p), (int)c.w);
                 dr[t] = __builtin_fmaf(vc, tre[t][r], __builtin_fmaf(vs, tim[t][r], dr[t]));
                 di[t] = __builtin_fmaf(vc, tim[t][r], __builtin_fmaf(-vs, tre[t][r], di[t]));
             }
@@ -640,8 +670,11 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
     const int64_t blocks = ((int64_t)M + per_block - 1) / per_block;
     const int splits = split_count(blocks, nchunks);
     if (splits == 1) {
-        fhd_forward_gather_kernel<kSamp><<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
-            packed, nchunks, 1, kx, ky, kz, Dr, Di, M, gate);
+        {
+            TimedLaunch timed("fhd_forward_gather_kernel<2>", stream);
+            fhd_forward_gather_kernel<kSamp><<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(
+                packed, nchunks, 1, kx, ky, kz, Dr, Di, M, gate);
+        }
         return launch_status("fhd_forward_gather_kernel launch");
     }
     float *part = nullptr;
@@ -652,9 +685,12 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
                                        hipGetErrorString(e));
     }
     float *part_r = part, *part_i = part + (int64_t)splits * M;
-    fhd_forward_gather_kernel<kSamp>
-        <<<dim3((unsigned)blocks, (unsigned)splits), dim3(kBlock), 0, stream>>>(
-            packed, nchunks, splits, kx, ky, kz, part_r, part_i, M, gate);
+    {
+        TimedLaunch timed("fhd_forward_gather_kernel<2>", stream);
+        fhd_forward_gather_kernel<kSamp>
+            <<<dim3((unsigned)blocks, (unsigned)splits), dim3(kBlock), 0, stream>>>(
+                packed, nchunks, splits, kx, ky, kz, part_r, part_i, M, gate);
+    }
     int rc = launch_status("fhd_forward_gather_kernel launch");
     if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, M, Dr, Di, stream, gate, false);
     const hipError_t f = hipFreeAsync(part, stream);
@@ -664,13 +700,32 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
 }
 
 
+// The line form's pre-pass and gather of one split type (F16: fp16 parts).
+template <bool F16>
+int launch_forward_lines(const float *x, const float *y, const float *z, const float *rho_r,
+                         const float *rho_i, const int *cls, int *info, u32x4 *tiles, int64_t ntiles,
+                         int64_t blocks, int splits, const float *kx, const float *ky, const float *kz,
+                         float *part_r, float *part_i, int M, hipStream_t stream)
+{
+    fhd_forward_lines_pack_kernel<F16><<<dim3((unsigned)ntiles), dim3(kFwdBlock), 0, stream>>>(
+        x, y, z, rho_r, rho_i, cls, info, tiles);
+    int rc = launch_status("fhd_forward_lines_pack_kernel launch");
+    if (rc == FHD_OK) {
+        TimedLaunch timed(F16 ? "fhd_forward_lines_kernel<true>" : "fhd_forward_lines_kernel<false>", stream);
+        fhd_forward_lines_kernel<F16><<<dim3((unsigned)blocks, (unsigned)splits), dim3(kFwdBlock), 0, stream>>>(
+            tiles, (int)ntiles, splits, info, kx, ky, kz, part_r, part_i, M);
+        rc = launch_status("fhd_forward_lines_kernel launch");
+    }
+    return rc;
+}
+
 int launch_forward(const float *x, const float *y, const float *z, const float *rho_r,
                    const float *rho_i, int N, const float *kx, const float *ky, const float *kz,
-                   float *Dr, float *Di, int M, float *vox, hipStream_t stream)
+                   float *Dr, float *Di, int M, float *vox, hipStream_t stream, int paths)
 {
     if (M == 0) return FHD_OK;
-    if (N == 0 || N % (2 * kUnitVox) != 0) {
-        // not whole pairs of units: the vector form
+    if (N == 0 || N % (2 * kUnitVox) != 0 || paths == FHD_GATHER_VECTOR) {
+        // not whole pairs of units (or the vector form asked for)
         int rc = launch_forward_pack(x, y, z, rho_r, rho_i, N, vox, stream);
         return rc == FHD_OK ? launch_forward_gather(vox, N, kx, ky, kz, Dr, Di, M, stream) : rc;
     }
@@ -682,7 +737,7 @@ int launch_forward(const float *x, const float *y, const float *z, const float *
         if (per_cu_cache[dev] == 0) {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, reinterpret_cast<const void *>(fhd_forward_lines_kernel), kFwdBlock, 0) != hipSuccess ||
+                    &n, reinterpret_cast<const void *>(fhd_forward_lines_kernel<true>), kFwdBlock, 0) != hipSuccess ||
                 n < 1)
                 n = 3;
             per_cu_cache[dev] = n;
@@ -693,7 +748,7 @@ int launch_forward(const float *x, const float *y, const float *z, const float *
     // at least one tile)
     const int splits = split_count(blocks, (int)(ntiles * kStageChunks), per_cu);
     // one workspace: unit classes and the flag words | line tiles | partials
-    const size_t cls_bytes = ((size_t)units * sizeof(int) + 4 * sizeof(int) + 255) / 256 * 256;
+    const size_t cls_bytes = ((size_t)units * sizeof(int) + kInfoWords * sizeof(int) + 255) / 256 * 256;
     const size_t tile_bytes = (size_t)ntiles * kFwdTileVec4 * sizeof(u32x4);
     const size_t part_bytes = splits > 1 ? (size_t)splits * 2 * M * sizeof(float) : 0;
     char *work = nullptr;
@@ -710,16 +765,12 @@ int launch_forward(const float *x, const float *y, const float *z, const float *
         part_i = part_r + (int64_t)splits * M;
     }
     int rc = launch_classify(x, y, z, N, true, cls, info, stream);
-    if (rc == FHD_OK) {
-        fhd_forward_lines_pack_kernel<<<dim3((unsigned)ntiles), dim3(kFwdBlock), 0, stream>>>(
-            x, y, z, rho_r, rho_i, cls, info, tiles);
-        rc = launch_status("fhd_forward_lines_pack_kernel launch");
-    }
-    if (rc == FHD_OK) {
-        fhd_forward_lines_kernel<<<dim3((unsigned)blocks, (unsigned)splits), dim3(kFwdBlock), 0, stream>>>(
-            tiles, (int)ntiles, splits, info, kx, ky, kz, part_r, part_i, M);
-        rc = launch_status("fhd_forward_lines_kernel launch");
-    }
+    if (rc == FHD_OK)
+        rc = paths == FHD_GATHER_BF16X3
+                 ? launch_forward_lines<false>(x, y, z, rho_r, rho_i, cls, info, tiles, ntiles, blocks, splits, kx,
+                                               ky, kz, part_r, part_i, M, stream)
+                 : launch_forward_lines<true>(x, y, z, rho_r, rho_i, cls, info, tiles, ntiles, blocks, splits, kx,
+                                              ky, kz, part_r, part_i, M, stream);
     if (rc == FHD_OK && splits > 1) rc = launch_reduce(part_r, part_i, splits, M, Dr, Di, stream, info, true);
     // the vector form, which stands aside when the line form ran
     if (rc == FHD_OK) rc = launch_forward_pack(x, y, z, rho_r, rho_i, N, vox, stream, info);
@@ -776,13 +827,14 @@ extern "C" int fhd_forward_gather(const void *packed, int N, const float *kx, co
                                  (hipStream_t)stream);
 }
 
-extern "C" int fhd_forward(const float *kx, const float *ky, const float *kz, const float *x,
-                           const float *y, const float *z, const float *rho_r, const float *rho_i,
-                           float *Dr, float *Di, int M, int N, void *stream)
+extern "C" int fhd_forward_paths(const float *kx, const float *ky, const float *kz, const float *x,
+                                 const float *y, const float *z, const float *rho_r, const float *rho_i,
+                                 float *Dr, float *Di, int M, int N, int paths, void *stream)
 {
     clear_error();
     if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
     if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
+    if (!valid_paths(paths)) return fail_paths();
     if (M == 0) return FHD_OK;
     const int64_t mb = (int64_t)M * 4, nb = (int64_t)N * 4;
     const Span all[] = {{kx, mb, "kx"}, {ky, mb, "ky"}, {kz, mb, "kz"},
@@ -803,7 +855,7 @@ extern "C" int fhd_forward(const float *kx, const float *ky, const float *kz, co
             return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
         }
     }
-    if (rc == FHD_OK) rc = launch_forward(x, y, z, rho_r, rho_i, N, kx, ky, kz, Dr, Di, M, packed, s);
+    if (rc == FHD_OK) rc = launch_forward(x, y, z, rho_r, rho_i, N, kx, ky, kz, Dr, Di, M, packed, s, paths);
     if (packed) {
         const hipError_t e = hipFreeAsync(packed, s);
         if (e != hipSuccess && rc == FHD_OK)
@@ -812,16 +864,24 @@ extern "C" int fhd_forward(const float *kx, const float *ky, const float *kz, co
     return rc;
 }
 
+extern "C" int fhd_forward(const float *kx, const float *ky, const float *kz, const float *x,
+                           const float *y, const float *z, const float *rho_r, const float *rho_i,
+                           float *Dr, float *Di, int M, int N, void *stream)
+{
+    return fhd_forward_paths(kx, ky, kz, x, y, z, rho_r, rho_i, Dr, Di, M, N, FHD_GATHER_ALL, stream);
+}
+
 // q = F^H F p: F into a k-space temporary, then F^H (loop fission of the
 // normal operator into its two halves, page "Case study -- iterative MRI
 // reconstruction", section 17.3.2).
-extern "C" int fhd_normal(const float *kx, const float *ky, const float *kz, const float *x,
-                          const float *y, const float *z, const float *p_r, const float *p_i,
-                          float *q_r, float *q_i, int M, int N, void *stream)
+extern "C" int fhd_normal_paths(const float *kx, const float *ky, const float *kz, const float *x,
+                                const float *y, const float *z, const float *p_r, const float *p_i,
+                                float *q_r, float *q_i, int M, int N, int paths, void *stream)
 {
     clear_error();
     if (M < 0) return fail(FHD_ERR_INVALID_ARG, "M < 0");
     if (N < 0) return fail(FHD_ERR_INVALID_ARG, "N < 0");
+    if (!valid_paths(paths)) return fail_paths();
     if (N == 0) return FHD_OK;
     const int64_t mb = (int64_t)M * 4, nb = (int64_t)N * 4;
     const Span all[] = {{kx, mb, "kx"}, {ky, mb, "ky"}, {kz, mb, "kz"},
@@ -834,7 +894,7 @@ extern "C" int fhd_normal(const float *kx, const float *ky, const float *kz, con
     if (rc != FHD_OK) return rc;
 
     hipStream_t s = (hipStream_t)stream;
-    if (M == 0) return launch_gather(nullptr, 0, x, y, z, q_r, q_i, N, s);   // empty sum
+    if (M == 0) return launch_gather(nullptr, 0, x, y, z, q_r, q_i, N, s, paths);   // empty sum
     // one workspace: packed voxels | packed samples | D (real, imaginary)
     const int64_t vox_bytes = packed_bytes_for(N), smp_bytes = packed_bytes_for(M);
     const int64_t d_bytes = 2 * mb;
@@ -846,11 +906,18 @@ extern "C" int fhd_normal(const float *kx, const float *ky, const float *kz, con
     }
     float *vox = (float *)ws, *smp = (float *)(ws + vox_bytes);
     float *d_r = (float *)(ws + vox_bytes + smp_bytes), *d_i = d_r + M;
-    rc = launch_forward(x, y, z, p_r, p_i, N, kx, ky, kz, d_r, d_i, M, vox, s);
+    rc = launch_forward(x, y, z, p_r, p_i, N, kx, ky, kz, d_r, d_i, M, vox, s, paths);
     if (rc == FHD_OK) rc = launch_pack(kx, ky, kz, d_r, d_i, M, smp, s);
-    if (rc == FHD_OK) rc = launch_gather(smp, M, x, y, z, q_r, q_i, N, s);
+    if (rc == FHD_OK) rc = launch_gather(smp, M, x, y, z, q_r, q_i, N, s, paths);
     const hipError_t f = hipFreeAsync(ws, s);
     if (f != hipSuccess && rc == FHD_OK)
         rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
     return rc;
+}
+
+extern "C" int fhd_normal(const float *kx, const float *ky, const float *kz, const float *x,
+                          const float *y, const float *z, const float *p_r, const float *p_i,
+                          float *q_r, float *q_i, int M, int N, void *stream)
+{
+    return fhd_normal_paths(kx, ky, kz, x, y, z, p_r, p_i, q_r, q_i, M, N, FHD_GATHER_ALL, stream);
 }

@@ -520,15 +520,19 @@ int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const
     const int splits = split_count(blocks, nchunks, per_cu);
     auto launch = [&](int nsplit, float *out_r, float *out_i) {
         const dim3 grid((unsigned)blocks, (unsigned)nsplit);
-        if (kernel_id == 0)
+        if (kernel_id == 0) {
+            TimedLaunch timed("fhd_grid_kernel", stream);
             fhd_grid_kernel<<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, nsplit, nx, ny, nyz,
                                                               tiles_x, g, out_r, out_i);
-        else if (kernel_id == 1)
+        } else if (kernel_id == 1) {
+            TimedLaunch timed("fhd_grid_bf16x3_kernel<2>", stream);
             fhd_grid_bf16x3_kernel<2><<<grid, dim3(kBlock), 0, stream>>>(
                 packed, nchunks, nsplit, nx, ny, nyz, tiles_x, g, out_r, out_i);
-        else
+        } else {
+            TimedLaunch timed("fhd_grid_bf16x3_kernel<4>", stream);
             fhd_grid_bf16x3_kernel<4><<<grid, dim3(kBlock), 0, stream>>>(
                 packed, nchunks, nsplit, nx, ny, nyz, tiles_x, g, out_r, out_i);
+        }
         return launch_status(name);
     };
     if (splits == 1) return launch(1, rho_r, rho_i);
@@ -580,8 +584,11 @@ int launch_forward_grid(const float *rho_r, const float *rho_i, int nx, int ny, 
         return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (row partials): ") + hipGetErrorString(e));
     }
     float *part_r = part, *part_i = part + blocks * M;
-    fhd_forward_grid_bf16x3_kernel<<<dim3((unsigned)blocks, (unsigned)msplits), dim3(kBlock), 0, stream>>>(
-        rho_r, rho_i, nx, ny, nyz, kx, ky, kz, M, m_per_split, kranges, g, part_r, part_i);
+    {
+        TimedLaunch timed("fhd_forward_grid_bf16x3_kernel", stream);
+        fhd_forward_grid_bf16x3_kernel<<<dim3((unsigned)blocks, (unsigned)msplits), dim3(kBlock), 0, stream>>>(
+            rho_r, rho_i, nx, ny, nyz, kx, ky, kz, M, m_per_split, kranges, g, part_r, part_i);
+    }
     int rc = launch_status("fhd_forward_grid_bf16x3_kernel launch");
     if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, (int)blocks, M, Dr, Di, stream);
     const hipError_t f = hipFreeAsync(part, stream);

@@ -48,6 +48,15 @@ constexpr int kLineVox = 64;
 constexpr int kLongLineVox = 128;
 enum : int { kClassGeneral = 0, kClassOneStep = 1, kClassLines = 2, kClassLongPair = 3 };
 
+// Words the classification leaves after the unit classes ("info"): [0] 1
+// if the first pair of units is of class kClassLongPair, [1] its lines'
+// step (bits), [2] a flag the forward operator's line pre-pass sets, [3]
+// unused, then kAmpSlots partial maxima of the packed sample amplitudes
+// (bits), one per reduction workgroup (the largest amplitude is their
+// maximum; see read_amp_shift).
+constexpr int kAmpSlots = 64;
+constexpr int kInfoWords = 4 + kAmpSlots;
+
 static_assert(kBlock % 64 == 0, "workgroup must be whole wave64s");
 static_assert(kChunk * kFields % 4 == 0, "chunks must be whole float4s");
 
@@ -223,6 +232,128 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const unsigned (&w)[4])
 }
 
 // ---------------------------------------------------------------------------
+// split-fp16 operands (the fp32-class form of the matrix-core products)
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// x = hi + lo with hi = f16(x) and lo = f16(x - hi), both rounded to
+// nearest even. For |x| in [2^-2, 2^15] both parts are normal fp16 numbers
+// and x - (hi + lo) is within 2^-23 |x| (11 + 11 significant bits plus the
+// sign of the remainder); below, lo is an fp16 subnormal and the error is
+// at most 2^-25 in absolute terms (gfx950 keeps fp16 subnormals in
+// v_cvt_pk_f16_f32 and in the f16 matrix products: measured). Callers keep
+// |x| below 2^15 (fp16 overflows at 65520). x - hi comes from
+// v_dot2c_f32_f16 exactly as in split_bf16 (the products with -1 and 0 are
+// exact, and so is the sum).
+template <int E>
+__device__ __forceinline__ void split_f16(const float (&x)[E], unsigned (&hi)[E / 2],
+                                          unsigned (&lo)[E / 2])
+{
+    unsigned c0 = 0x0000bc00u, c1 = 0xbc000000u;   // fp16 pairs (-1, 0) and (0, -1)
+    asm("" : "+v"(c0));
+    asm("" : "+v"(c1));
+    const f16x2 first = __builtin_bit_cast(f16x2, c0), second = __builtin_bit_cast(f16x2, c1);
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+        const f16x2 h = __builtin_convertvector((float2v){x[2 * i], x[2 * i + 1]}, f16x2);
+        hi[i] = __builtin_bit_cast(unsigned, h);
+        const float l0 = __builtin_amdgcn_fdot2(h, first, x[2 * i], false);
+        const float l1 = __builtin_amdgcn_fdot2(h, second, x[2 * i + 1], false);
+        lo[i] = __builtin_bit_cast(unsigned, __builtin_convertvector((float2v){l0, l1}, f16x2));
+    }
+}
+
+// The two-part split of the matrix-core line forms: fp16 (the default,
+// fp32-class products) or bf16 (the opt-in three-product form with 16
+// significant bits per operand).
+template <bool F16, int E>
+__device__ __forceinline__ void split_parts(const float (&x)[E], unsigned (&hi)[E / 2],
+                                            unsigned (&lo)[E / 2])
+{
+    if constexpr (F16)
+        split_f16<E>(x, hi, lo);
+    else
+        split_bf16<E>(x, hi, lo);
+}
+
+// One 16 x 16 x 32 product of split operands held as 4 dwords each (8
+// two-byte elements), fp32 accumulation.
+typedef float float4v __attribute__((ext_vector_type(4)));
+template <bool F16>
+__device__ __forceinline__ float4v mfma16(u32x4 a, u32x4 b, float4v c)
+{
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One 32 x 32 x 16 product, as mfma16.
+template <bool F16>
+__device__ __forceinline__ float16v mfma32(u32x4 a, u32x4 b, float16v c)
+{
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Power-of-two scaling of the amplitudes that enter the fp16 products: for
+// a largest amplitude amax (bits as stored by the amplitude reduction),
+// the shift s with amax 2^s in [2^14, 2^15), so that every scaled value
+// stays below fp16's range limit and values down to 2^-16 amax keep the
+// full 22-bit split. 0 for amax = 0 or not finite (the result is then 0,
+// or not finite as the fp32 sum would be); a subnormal amax counts as
+// 2^-126.
+__device__ __forceinline__ int amp_shift(unsigned amax_bits)
+{
+    const int ex = (int)((amax_bits >> 23) & 0xffu);
+    if (amax_bits == 0u || ex == 0xff) return 0;
+    const int e = ex == 0 ? -126 : ex - 127;   // amax in [2^e, 2^(e+1))
+    return 14 - e;
+}
+
+// An amplitude as it enters the products (scaled by 2^sh in the fp16
+// form), and a product's sum as it leaves them (scaled back). Powers of two:
+// exact unless the value leaves fp32's range.
+template <bool F16>
+__device__ __forceinline__ float scale_amp(float a, int sh)
+{
+    if constexpr (F16)
+        return __builtin_ldexpf(a, sh);
+    else
+        return a;
+}
+template <bool F16>
+__device__ __forceinline__ float unscale(float v, int sh)
+{
+    if constexpr (F16)
+        return __builtin_ldexpf(v, -sh);
+    else
+        return v;
+}
+
+// The shift amp_shift() gives for the largest amplitude of the slots the
+// classification filled (info + 4): every lane of the wave reads one slot
+// and the wave takes the maximum. Uniform over the wave.
+__device__ __forceinline__ int read_amp_shift(const int *__restrict__ info)
+{
+    static_assert(kAmpSlots == 64, "one slot per lane of a wave");
+    unsigned m = (unsigned)info[4 + (threadIdx.x & 63)];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned t = (unsigned)__shfl_xor((int)m, o);
+        m = t > m ? t : m;
+    }
+    return __builtin_amdgcn_readfirstlane(amp_shift(m));
+}
+
+// ---------------------------------------------------------------------------
 // host side (abi_checks.hip)
 // ---------------------------------------------------------------------------
 struct Span {
@@ -236,6 +367,14 @@ struct Span {
 int fail(int status, const std::string &msg);
 void clear_error();
 
+// Whether `paths` is one of FHD_GATHER_ALL, FHD_GATHER_VECTOR,
+// FHD_GATHER_BF16X3; fail_paths() records the error for one that is not.
+inline bool valid_paths(int paths)
+{
+    return paths == FHD_GATHER_ALL || paths == FHD_GATHER_VECTOR || paths == FHD_GATHER_BF16X3;
+}
+int fail_paths();
+
 // NULL and alignment of every span with bytes > 0; no HIP call.
 int check_host_side(const Span *spans, int count);
 // Spans [first_out, count) are outputs: none may overlap any other span.
@@ -246,6 +385,21 @@ int check_no_overlap(const Span *spans, int count, int first_out);
 int check_device_spans(const Span *spans, int count);
 // FHD_ERR_HIP with `what` if the last launch failed.
 int launch_status(const char *what);
+
+// Measurement hook (fhd_time_kernel): when the calling thread has armed it
+// for `kernel`, timed_begin records the next start event on `stream` and
+// returns its slot (else -1); timed_end records the matching stop event.
+int timed_begin(const char *kernel, hipStream_t stream);
+void timed_end(int slot, hipStream_t stream);
+// Brackets one kernel launch in a scope: { TimedLaunch t(name, s); k<<<>>>(); }
+struct TimedLaunch {
+    int slot;
+    hipStream_t stream;
+    TimedLaunch(const char *kernel, hipStream_t s) : slot(timed_begin(kernel, s)), stream(s) {}
+    ~TimedLaunch() { timed_end(slot, stream); }
+    TimedLaunch(const TimedLaunch &) = delete;
+    TimedLaunch &operator=(const TimedLaunch &) = delete;
+};
 
 // How many parts to cut a stream of `nchunks` chunks into, for a gather
 // whose output needs `blocks` workgroups of which `per_cu` fit on a CU at
@@ -274,11 +428,17 @@ __device__ __forceinline__ bool lines_form_ran(const int *info) { return info[0]
 // Classes of the ceil(N / kUnitVox) units into cls; info[0] = 1 if the
 // first pair is of class kClassLongPair, info[1] its step's bits, info[2]
 // = 0 (stream-ordered; allow_lines = false gives no matrix-core class).
+// With amp_slots, also the amplitude slots info[4 .. 4 + kAmpSlots) of
+// the packed k-space of M samples (zeros when M = 0; info holds kInfoWords
+// words).
 int launch_classify(const float *x, const float *y, const float *z, int N, bool allow_lines, int *cls,
-                    int *info, hipStream_t stream);
-// matrix_cores = false keeps every unit on the vector-ALU paths.
+                    int *info, hipStream_t stream, bool amp_slots = false, const float *packed = nullptr,
+                    int M = 0);
+// paths: FHD_GATHER_ALL (lines on the matrix cores in split fp16, the
+// rest on the vector ALUs), FHD_GATHER_BF16X3 (the same in split bf16) or
+// FHD_GATHER_VECTOR (every unit on the vector-ALU paths).
 int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
-                  float *rho_r, float *rho_i, int N, hipStream_t stream, bool matrix_cores = true);
+                  float *rho_r, float *rho_i, int N, hipStream_t stream, int paths = FHD_GATHER_ALL);
 // fhd_forward.hip: forward F
 // (with a gate: nothing when lines_form_ran(gate))
 int launch_forward_pack(const float *x, const float *y, const float *z, const float *rho_r,
@@ -290,9 +450,10 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
 // D = F rho: on the matrix cores when every aligned pair of voxel units is
 // lines of 128 voxels along x of one common step (decided on the device),
 // else packed into vox (packed_bytes_for(N) bytes) for the vector gather.
+// paths as for launch_gather (FHD_GATHER_VECTOR: the vector form always).
 int launch_forward(const float *x, const float *y, const float *z, const float *rho_r,
                    const float *rho_i, int N, const float *kx, const float *ky, const float *kz,
-                   float *Dr, float *Di, int M, float *vox, hipStream_t stream);
+                   float *Dr, float *Di, int M, float *vox, hipStream_t stream, int paths = FHD_GATHER_ALL);
 // fhd_grid.hip: F^H D on a Cartesian grid (axis = x0, dx, y0, dy, z0, dz)
 int launch_grid_gather(const float *packed, int M, int nx, int ny, int nz, const float *axis,
                        int precision, float *rho_r, float *rho_i, hipStream_t stream);

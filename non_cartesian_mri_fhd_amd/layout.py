@@ -1,0 +1,131 @@
+"""Host-side mirror of the voxel-layout tests the F^H D and F kernels run on
+the device: which path each unit of voxels takes.
+
+The gathers classify their voxels on the GPU (fhd.hip: fhd_classify_kernel;
+fhd_forward.hip: the forward pre-pass's ramp test). The functions below
+repeat those tests in numpy, bit for bit on the same fp32 coordinates, so a
+benchmark can price each voxel at its path's ceiling and a test can assert
+which path it exercised. No F^H D arithmetic happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _lane_ramps(x, y, z, vox: int = 8):
+    """Per group of `vox` consecutive voxels (the last partial group
+    dropped): do they share y and z bitwise and sit at x_0 + v (x_1 - x_0)
+    rounded once to fp32 -- the gathers' ramp test -- and that step."""
+    x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
+    full = x.size // vox * vox
+    lanes = full // vox
+    if lanes == 0:
+        return np.zeros(0, bool), np.zeros(0, np.float32)
+    X, Y, Z = (a[:full].reshape(lanes, vox) for a in (x, y, z))
+    same = (np.all(Y.view(np.uint32) == Y[:, :1].view(np.uint32), axis=1)
+            & np.all(Z.view(np.uint32) == Z[:, :1].view(np.uint32), axis=1))
+    dx = (X[:, 1] - X[:, 0]).astype(np.float32)
+    v = np.arange(vox, dtype=np.float64)
+    ramp_x = (X[:, :1].astype(np.float64) + v * dx[:, None].astype(np.float64)).astype(np.float32)
+    return same & np.isfinite(dx) & np.all(ramp_x == X, axis=1), dx
+
+
+def ramp_chunk_fraction(x, y, z, vox: int = 8) -> float:
+    """Fraction of voxels that F's pre-pass writes as ramp chunks of `vox`."""
+    n = np.asarray(x).size
+    return float(np.sum(_lane_ramps(x, y, z, vox)[0]) * vox / n) if n else 0.0
+
+
+def ramp_chunk_fractions(x, y, z) -> tuple[float, float]:
+    """Fractions of voxels that F's pre-pass writes as 16-voxel ramps (chunk
+    pairs) and as 8-voxel ramp chunks (the other chunks)."""
+    n = np.asarray(x).size
+    if n == 0:
+        return 0.0, 0.0
+    ok16 = _lane_ramps(x, y, z, 16)[0]
+    ok8 = _lane_ramps(x, y, z, 8)[0]
+    both8 = ok8[:2 * ok16.size].reshape(-1, 2)
+    # chunks of a 16-voxel ramp are 8-voxel ramps too: count them once
+    single = int(np.sum(ok8)) - 2 * int(np.sum(ok16 & both8.all(axis=1)))
+    return float(np.sum(ok16) * 16 / n), float(single * 8 / n)
+
+
+def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64,
+                        long_line: int = 128, allow_lines: bool = True):
+    """Per unit of block*vox consecutive voxels (one workgroup of the F^H D
+    gather's single-unit instances), the class its classify kernel gives
+    it, by the same tests (a line: see _lane_ramps): 3 when the unit and
+    the other unit of its aligned pair are whole and all their aligned runs
+    of `long_line` voxels are lines with one step for the pair (the
+    long-line matrix-core instance); else 2 when the unit is whole and its
+    aligned runs of `line` voxels are lines with one step (the matrix-core
+    instance); else 1 when every lane's `vox` voxels are such a ramp, all
+    with one step (the ramp path with sample records); else 0. Returned
+    with, per unit, whether all its lanes are ramps (the per-lane ramp path
+    when the class is 0) and its voxel count. allow_lines=False mirrors
+    FHD_GATHER_VECTOR (no unit takes a matrix-core class)."""
+    x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
+    N = x.size
+    unit = block * vox
+    units = (N + unit - 1) // unit
+    counts = np.minimum(unit, N - np.arange(units) * unit)
+
+    def per_unit(per):
+        # groups of `per` voxels past N (a partial last unit) stay False;
+        # returns (all groups qualify, ... with one step, that step)
+        ok, dx = _lane_ramps(x, y, z, per)
+        n = units * (unit // per)
+        o = np.zeros(n, bool)
+        o[:ok.size] = ok
+        st = np.zeros(n, np.float32)
+        st[:dx.size] = dx
+        o = o.reshape(units, -1)
+        S = st.view(np.uint32).reshape(units, -1)
+        every = o.all(axis=1)
+        return every, every & np.all(S == S[:, :1], axis=1), S[:, 0]
+
+    whole = counts == unit
+    all_ramp, one, _ = per_unit(vox)
+    _, lines, _ = per_unit(line)
+    _, longl, step = per_unit(long_line)
+    lines &= whole & allow_lines
+    longl &= whole & allow_lines
+    pair = np.zeros(units, bool)
+    both = units // 2 * 2
+    if both:
+        ok = (longl[0:both:2] & longl[1:both:2] & (step[0:both:2] == step[1:both:2]))
+        pair[0:both:2] = ok
+        pair[1:both:2] = ok
+    cls = np.where(pair, 3, np.where(lines, 2, np.where(one, 1, 0)))
+    return cls, all_ramp, counts
+
+
+def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16,
+                         allow_lines: bool = True) -> tuple[float, float, float]:
+    """Fractions of voxels by the F^H D gather path their unit takes (see
+    gather_unit_classes): (lines on the matrix cores, either instance; ramps
+    with one step for the workgroup; ramps with per-lane steps); the rest
+    is direct."""
+    N = np.asarray(x).size
+    if N == 0:
+        return 0.0, 0.0, 0.0
+    cls, all_ramp, counts = gather_unit_classes(x, y, z, block, vox, allow_lines=allow_lines)
+    return (float(np.sum(counts[cls >= 2]) / N), float(np.sum(counts[cls == 1]) / N),
+            float(np.sum(counts[(cls == 0) & all_ramp]) / N))
+
+
+def forward_lines_form(x, y, z, block: int = 256, vox: int = 16, long_line: int = 128) -> bool:
+    """Whether fhd_forward takes its matrix-core line form, by the same
+    rule: a whole number of unit pairs, every unit of class 3, and one step
+    for every line of `long_line` voxels."""
+    N = np.asarray(x).size
+    if N == 0 or N % (2 * block * vox) != 0:
+        return False
+    cls = gather_unit_classes(x, y, z, block, vox)[0]
+    ok, dx = _lane_ramps(x, y, z, long_line)
+    return bool(np.all(cls == 3) and dx.size and np.all(dx.view(np.uint32) == dx.view(np.uint32)[0]))
+
+
+def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 16) -> float:
+    """Fraction of voxels on a ramp path, any form (lines included)."""
+    return sum(ramp_voxel_fractions(x, y, z, block, vox))

@@ -57,7 +57,9 @@ def test_header_declares_the_entry_points():
               "fhd_status_string", "fhd_last_error", "fhd_gather_config",
               "fhd_forward", "fhd_forward_pack", "fhd_forward_gather", "fhd_normal",
               "fhd_cg", "fhd_cg_workspace_bytes", "fhd_compute_grid", "fhd_grid_gather", "fhd_forward_grid",
-              "fhd_normal_grid", "fhd_cg_grid"):
+              "fhd_normal_grid", "fhd_cg_grid", "fhd_compute_paths", "fhd_gather_paths",
+              "fhd_forward_paths", "fhd_normal_paths", "fhd_cg_paths", "fhd_time_kernel",
+              "fhd_timed_launches"):
         assert n in names
 
 
@@ -294,3 +296,64 @@ def test_scatter_argument_checks(lib):
     args[9] = args[8] + 8
     assert lib.fhd_scatter(*args, 16, 16, None) == FHD_ERR_INVALID_ARG
     assert "overlaps" in _last(lib)
+
+
+def test_unknown_paths_rejected_before_any_device_call(lib):
+    """Every *_paths entry point refuses a paths value other than
+    FHD_GATHER_ALL (0), FHD_GATHER_VECTOR (1) and FHD_GATHER_BF16X3 (2),
+    with sizes that would otherwise do nothing."""
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.fhd_compute_paths.argtypes = [vp] * 10 + [i32, i32, i32, vp]
+    lib.fhd_gather_paths.argtypes = [vp, i32] + [vp] * 5 + [i32, i32, vp]
+    lib.fhd_forward_paths.argtypes = [vp] * 10 + [i32, i32, i32, vp]
+    lib.fhd_normal_paths.argtypes = [vp] * 10 + [i32, i32, i32, vp]
+    lib.fhd_cg_paths.argtypes = [vp] * 10 + [i32, i32, i32, ctypes.c_float, vp, vp, i32, vp]
+    done = ctypes.c_int(0)
+    for bad in (-1, 3, 7):
+        assert lib.fhd_compute_paths(*[None] * 10, 0, 0, bad, None) == FHD_ERR_INVALID_ARG
+        assert b"paths" in lib.fhd_last_error()
+        assert lib.fhd_gather_paths(None, 0, *[None] * 5, 0, bad, None) == FHD_ERR_INVALID_ARG
+        assert lib.fhd_forward_paths(*[None] * 10, 0, 0, bad, None) == FHD_ERR_INVALID_ARG
+        assert lib.fhd_normal_paths(*[None] * 10, 0, 0, bad, None) == FHD_ERR_INVALID_ARG
+        assert lib.fhd_cg_paths(*[None] * 10, 0, 0, 3, 0.0, ctypes.byref(done), None, bad,
+                                None) == FHD_ERR_INVALID_ARG
+    for good in (0, 1, 2):
+        assert lib.fhd_compute_paths(*[None] * 10, 0, 0, good, None) == FHD_OK
+        assert lib.fhd_gather_paths(None, 0, *[None] * 5, 0, good, None) == FHD_OK
+        assert lib.fhd_forward_paths(*[None] * 10, 0, 0, good, None) == FHD_OK
+        assert lib.fhd_normal_paths(*[None] * 10, 0, 0, good, None) == FHD_OK
+        assert lib.fhd_cg_paths(*[None] * 10, 0, 0, 3, 0.0, ctypes.byref(done), None, good,
+                                None) == FHD_OK
+
+
+def test_kernel_timing_hook_arguments(lib):
+    """fhd_time_kernel needs no device: it only copies the names and
+    handles; bad arguments are refused and leave the hook disarmed."""
+    lib.fhd_time_kernel.argtypes = [ctypes.c_char_p, ctypes.c_void_p, ctypes.c_int]
+    lib.fhd_timed_launches.restype = ctypes.c_int
+    two = (ctypes.c_void_p * 2)(1, 2)     # opaque handles, never used here
+    assert lib.fhd_time_kernel(b"fhd_gather_kernel<16, true>", two, -1) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_time_kernel(b"fhd_gather_kernel<16, true>", None, 1) == FHD_ERR_INVALID_ARG
+    holes = (ctypes.c_void_p * 2)(1, None)
+    assert lib.fhd_time_kernel(b"fhd_gather_kernel<16, true>", holes, 1) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_time_kernel(b"fhd_gather_kernel<16, true>", two, 1) == FHD_OK
+    assert lib.fhd_timed_launches() == 0
+    assert lib.fhd_time_kernel(None, None, 0) == FHD_OK
+    assert lib.fhd_timed_launches() == 0
+
+
+
+def test_stale_library_is_rebuilt_when_a_source_is_newer(tmp_path):
+    """ensure_built() rebuilds a library older than any of its sources or
+    headers (here: a header's time set an hour ahead, then restored)."""
+    build.ensure_built()
+    assert not build.is_stale("libfhd.so")
+    header = os.path.join(ROOT, "include", "fhd.h")
+    st = os.stat(header)
+    try:
+        os.utime(header, (st.st_atime, os.path.getmtime(build.lib_path("libfhd.so")) + 3600))
+        assert build.is_stale("libfhd.so")
+    finally:
+        os.utime(header, (st.st_atime, st.st_mtime))
+    assert not build.is_stale("libfhd.so")
+    assert header in build.sources_of("libfhd.so")

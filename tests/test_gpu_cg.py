@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import oracle
-from non_cartesian_mri_fhd_amd import binding, build, inputs, metrics
+from non_cartesian_mri_fhd_amd import binding, build, inputs, layout, metrics
 
 from test_gpu_parity import check, to_dev
 
@@ -20,10 +20,10 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run(case, dev, iters, tol=0.0):
+def run(case, dev, iters, tol=0.0, paths=None):
     d = to_dev(case, dev)
     rr, ri, done, res = binding.fhd_cg(d["kx"], d["ky"], d["kz"], d["Dr"], d["Di"],
-                                       d["x"], d["y"], d["z"], iters, tol)
+                                       d["x"], d["y"], d["z"], iters, tol, paths=paths)
     torch.cuda.synchronize(dev)
     return rr.cpu().numpy(), ri.cpu().numpy(), done, res
 
@@ -120,3 +120,30 @@ def test_cg_tolerance_stop_inside_a_batch(dev, stop):
     assert done == stop == len(ref_stop) - 1 and len(res) == stop + 1
     assert res[stop] < tol <= res[stop - 1]
     check("cg stop at %d" % stop, rr, ri, ref.real, ref.imag)
+
+
+@pytest.mark.parametrize("paths", ["all", "bf16x3", "vector"])
+def test_cg_line_form_matches_oracle_cg(dev, paths):
+    """CG with both operators in their matrix-core line form: 128 x 16 x 4
+    voxels (an aligned pair of units of 128-voxel lines, so F^H takes the
+    long-line instance and F its line form), 12,000 random samples in the
+    grid's Nyquist box, 20 iterations, against the oracle's fp64 CG; the
+    vector paths and the split-bf16 form on the same case."""
+    shape, axis = (128, 16, 4), (-0.5, 1.0 / 128, -0.5, 1.0 / 16, -0.5, 0.25)
+    x, y, z = inputs.coords_from_axis(*shape, axis)
+    assert layout.gather_unit_classes(x, y, z)[0].tolist() == [3, 3]
+    assert layout.forward_lines_form(x, y, z)
+    rng = np.random.default_rng(75)
+    M = 12000
+    k = np.stack([rng.uniform(-n / 2, n / 2, M) for n in shape]).astype(np.float32)
+    D = rng.standard_normal((2, M)).astype(np.float32)
+    case = dict(kx=k[0], ky=k[1], kz=k[2], Dr=D[0], Di=D[1], x=x, y=y, z=z)
+    iters = 20
+    code = {"all": binding.FHD_GATHER_ALL, "bf16x3": binding.FHD_GATHER_BF16X3,
+            "vector": binding.FHD_GATHER_VECTOR}[paths]
+    rr, ri, done, res = run(case, dev, iters, paths=code)
+    ref, ref_res = oracle.cg(k[0], k[1], k[2], D[0], D[1], x, y, z, iters=iters)
+    assert done == iters == len(ref_res) - 1
+    check("cg line form (%s), %d iterations" % (paths, iters), rr, ri, ref.real, ref.imag)
+    assert np.allclose(res, ref_res, rtol=2e-3, atol=0), (res, ref_res)
+

@@ -28,11 +28,11 @@ def t(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def bench_fractions(x, y, z):
-    """(16-voxel ramp, 8-voxel ramp chunk) voxel fractions the pre-pass
-    should find, by the benchmark's host-side replica of its test."""
-    import bench
-    return bench.ramp_chunk_fractions(x, y, z)
+def chunk_fractions(x, y, z):
+    """Fractions of voxels in 16-voxel ramps and 8-voxel ramp chunks that the
+    pre-pass should find, by the package's host-side replica of its test."""
+    from non_cartesian_mri_fhd_amd import layout
+    return layout.ramp_chunk_fractions(x, y, z)
 
 
 def gpu_forward(case, img, dev):
@@ -193,8 +193,8 @@ def test_forward_ramp_pairs_and_single_chunks_agree(dev):
     w = inputs.make_workload("spiral32")
     img = inputs.random_image(w["N"], seed=24)
     n = np.arange(w["N"]).reshape(-1, 2, 8)[:, ::-1, :].reshape(-1)
-    assert bench_fractions(w["x"], w["y"], w["z"]) == (1.0, 0.0)
-    assert bench_fractions(w["x"][n], w["y"][n], w["z"][n]) == (0.0, 1.0)
+    assert chunk_fractions(w["x"], w["y"], w["z"]) == (1.0, 0.0)
+    assert chunk_fractions(w["x"][n], w["y"][n], w["z"][n]) == (0.0, 1.0)
     pairs = gpu_forward(w, img, dev)
     single = gpu_forward(dict(w, x=w["x"][n], y=w["y"][n], z=w["z"][n]),
                          (img[0][n], img[1][n]), dev)

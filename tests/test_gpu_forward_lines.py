@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-import bench
+from non_cartesian_mri_fhd_amd import layout
 import oracle
 from non_cartesian_mri_fhd_amd import binding, build, inputs, metrics
 
@@ -54,7 +54,7 @@ def check(tag, k, x, y, z, img, Dr, Di):
 
 
 def all_long_pairs(x, y, z):
-    cls = bench.gather_unit_classes(x, y, z)[0]
+    cls = layout.gather_unit_classes(x, y, z)[0]
     return cls.size > 0 and bool(np.all(cls == 3))
 
 

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-import bench
+from non_cartesian_mri_fhd_amd import layout
 import oracle
 from non_cartesian_mri_fhd_amd import binding, build, inputs, metrics
 
@@ -53,7 +53,7 @@ def check(tag, case, rr, ri):
 
 
 def classes(case):
-    return bench.gather_unit_classes(case["x"], case["y"], case["z"])[0].tolist()
+    return layout.gather_unit_classes(case["x"], case["y"], case["z"])[0].tolist()
 
 
 @pytest.mark.parametrize("shape,axis,M,cls", [
@@ -217,7 +217,7 @@ def test_gather_paths_rejects_unknown_mode(dev):
     out = [torch.empty(x.numel(), device=dev) for _ in range(2)]
     packed = binding.new_packed(8, dev)
     rc = lib.fhd_gather_paths(packed.data_ptr(), 8, x.data_ptr(), y.data_ptr(), z.data_ptr(),
-                              out[0].data_ptr(), out[1].data_ptr(), x.numel(), 2, None)
+                              out[0].data_ptr(), out[1].data_ptr(), x.numel(), 3, None)
     assert rc == binding.FHD_ERR_INVALID_ARG
     assert b"paths" in ctypes.string_at(lib.fhd_last_error())
 

@@ -78,6 +78,28 @@ def test_workload_sampled_voxels(dev, name, count):
     check(name, rr[idx], ri[idx], ref_r, ref_i)
 
 
+@pytest.mark.parametrize("name,count", [("radial64", 4096), ("spiral128", 4096),
+                                        ("vdrandom256", inputs.SUBSET_SIZE)])
+@pytest.mark.parametrize("paths", ["vector", "bf16x3"])
+def test_workload_sampled_voxels_other_paths(dev, name, count, paths):
+    """The fp32 vector paths (FHD_GATHER_VECTOR) and the opt-in split-bf16
+    line form (FHD_GATHER_BF16X3) at full size, in the launch shape the
+    benchmark times them in, on seeded voxel subsets."""
+    w = inputs.make_workload(name)
+    t = to_dev(w, dev)
+    code = binding.FHD_GATHER_VECTOR if paths == "vector" else binding.FHD_GATHER_BF16X3
+    rr, ri = binding.fhd_compute(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], t["x"], t["y"], t["z"],
+                                 paths=code)
+    torch.cuda.synchronize(dev)
+    rr, ri = rr.cpu().numpy(), ri.cpu().numpy()
+    if name == "vdrandom256":
+        idx = inputs.voxel_subset(w["N"])
+    else:
+        idx = inputs.voxel_subset(w["N"], count, seed=inputs.WORKLOADS[name].seed + 1000)
+    ref_r, ref_i = oracle.fhd_subset(w, idx)
+    check("%s %s" % (name, paths), rr[idx], ri[idx], ref_r, ref_i)
+
+
 @pytest.mark.parametrize("L", [16, 32, 64])
 def test_cartesian_grid_matches_numpy_ifft(dev, L):
     """Full integer k-grid over an L^3 voxel grid reduces to N * ifftn."""
