@@ -906,6 +906,12 @@ static_assert(kLinesStageChunks % kLongGroup == 0, "product steps tile a stage")
 // (no bank conflicts). 16 KB.
 constexpr int kLongStepVec4 = 4 * kLongTiles * 4 * 16;
 typedef u32x4 LongStepB[4][kLongTiles][4][16];
+// A product step's LDS buffer: its B operands and its four sample chunks.
+constexpr int kLongStepChunkVec4 = kLongGroup * kChunkVec4;   // 40 float4
+struct LongStep {
+    LongStepB b;
+    float4 chunks[kLongStepChunkVec4];
+};
 
 // Lane (wave w, lane l) of a step's B: B_C (w < 2) or B_S (w >= 2, as a
 // cosine a quarter turn later) of pair tiles 2 (w % 2) and 2 (w % 2) + 1,
@@ -978,26 +984,35 @@ __global__ __launch_bounds__(kLongBlock) void fhd_long_table_kernel(const float 
 
 template <bool F16>
 __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_long_lines_kernel(
-    const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
+    const float *__restrict__ packed, int nchunks, int splits, int pairs, const int *__restrict__ cls,
     const int *__restrict__ info, const float4 *__restrict__ table,
     const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
     float *__restrict__ out_r, float *__restrict__ out_i, int N)
 {
-    if (cls[2 * (int64_t)blockIdx.x] != kClassLongPair) return;
-    __shared__ float4 stage[2][kLinesStageVec4];
-    __shared__ LongStepB bshare[2];
+    // workgroup -> (pair, split), split-major over the XCDs (see xcd_unit)
+    const int64_t unit = xcd_unit(blockIdx.x, (int64_t)pairs * splits);
+    const int64_t pair = unit % pairs;
+    const int split = (int)(unit / pairs);
+    if (cls[2 * pair] != kClassLongPair) return;
+    // Two step buffers, each a step's B operands and its four sample
+    // chunks, used alternately: while the workgroup works on one step, the
+    // next step's data is copied straight into the other buffer (buffer_load
+    // ... lds). They are two variables, not one array, so the copy in flight
+    // into one is known not to alias reads of the other, and no read waits
+    // for a copy it does not need.
+    __shared__ LongStep buf0, buf1;
     const float4 *src = reinterpret_cast<const float4 *>(packed);
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sh = F16 ? read_amp_shift(info) : 0;
 
     // line 16 wave + col of the pair (both units lie below N)
-    const int64_t base = (int64_t)blockIdx.x * kPairVox;
+    const int64_t base = pair * kPairVox;
     const int64_t first = base + (int64_t)(16 * wave + col) * kLongLineVox;
     const float x0 = x[first], dx = x[first + 1] - x0, ly = y[first], lz = z[first];
     const float xc = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x0);
     // every line of the pair has the step dx (bitwise), so this is uniform
-    const bool use_table = info[0] != 0 && __float_as_uint(dx) == (unsigned)info[1];
+    const bool use_table = table != nullptr && info[0] != 0 && __float_as_uint(dx) == (unsigned)info[1];
 
     float4v prc[kLongTiles], pic[kLongTiles], pis[kLongTiles], prs[kLongTiles];
 #pragma unroll
@@ -1010,54 +1025,60 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
             prs[t][r] = 0.0f;
         }
 
-    int c0, c1, kb = 0;
-    split_range<kLinesStageChunks>(nchunks, splits, blockIdx.y, &c0, &c1);
+    // this split's chunks [c0, c1): steps g0 .. g0 + nsteps - 1 of the
+    // sample stream (splits are whole stages of 32 chunks, so whole steps;
+    // only the stream's last step may hold fewer than four chunks)
+    int c0, c1;
+    split_range<kLinesStageChunks>(nchunks, splits, split, &c0, &c1);
     const int nch = c1 > c0 ? c1 - c0 : 0;
     src += (int64_t)c0 * kChunkVec4;
     const int64_t total_vec4 = (int64_t)nch * kChunkVec4;
-    const int nstages = (nch + kLinesStageChunks - 1) / kLinesStageChunks;
+    const int nsteps = (nch + kLongGroup - 1) / kLongGroup;
     const int64_t table_vec4 = (((int64_t)nchunks + kLongGroup - 1) / kLongGroup) * kLongStepVec4;
-    const int g0 = c0 / kLongGroup;   // the split's first product step (splits are whole stages)
+    const int g0 = c0 / kLongGroup;
 
-    // One step of 32 samples: chunks ch .. ch + 3 of the stage, of which the
-    // first `count` hold samples (the others read as zeros, amplitude 0 in
-    // B, when PARTIAL). TABLE: this step's B was copied into bshare[kb]
-    // during the previous step; the next step's (step g + 1) goes out once
-    // this one's barrier is passed.
-    auto step = [&](const float4 *ch, int count, int g, auto partial, auto from_table) {
+    // Copies step i of the split (its chunks and, from the table, its B
+    // operands) into `dst`. Chunks past the split's end read as zeros
+    // (amplitude 0: they add nothing), as do the table's past the stream's.
+    auto copy_step = [&](int i, LongStep &dst, auto from_table) {
+        issue_stage_load<kLongBlock, kLongStepChunkVec4>(src, total_vec4, i, dst.chunks);
+        if constexpr (decltype(from_table)::value)
+            issue_stage_load<kLongBlock, kLongStepVec4>(table, table_vec4, g0 + i,
+                                                         reinterpret_cast<float4 *>(&dst.b));
+    };
+
+    // Step i of the split, in `cur`, whose copy was issued during the
+    // previous step. The copies are shared work (lanes of every wave copy
+    // parts of the buffer, and wave 0 alone the chunks), and a wave's own
+    // wait covers only its own copies, so the step opens with every wave
+    // waiting for its copies and a barrier: after it `cur` is whole in LDS,
+    // and every wave has finished reading `next` (the previous step's
+    // buffer), into which the copy of step i + 1 then goes. Without the
+    // table, the workgroup forms the step's B operands into `cur` itself,
+    // behind a second barrier.
+    auto step = [&](int i, LongStep &cur, LongStep &next, auto from_table) {
         constexpr bool kTable = decltype(from_table)::value;
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        if (i + 1 < nsteps) copy_step(i + 1, next, from_table);
         float f[kFields][kChunk];
-        if constexpr (decltype(partial)::value) {
-            if (quarter_k < count) {
-                load_chunk(ch + quarter_k * kChunkVec4, f);
-            } else {
-#pragma unroll
-                for (int q = 0; q < kFields; ++q)
-#pragma unroll
-                    for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
-            }
-        } else {
-            load_chunk(ch + quarter_k * kChunkVec4, f);
+        load_chunk(cur.chunks + quarter_k * kChunkVec4, f);
+        if constexpr (!kTable) {
+            long_step_b<F16>(f, dx, wave, quarter_k, col, sh, cur.b);
+            lds_barrier();
         }
-        if constexpr (!kTable) long_step_b<F16>(f, dx, wave, quarter_k, col, sh, bshare[kb]);
         float ur[kChunk], ui[kChunk];
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            const float p = __builtin_fmaf(f[0][i], xc, __builtin_fmaf(f[1][i], ly, __builtin_fmaf(f[2][i], lz, f[3][i])));
-            ur[i] = __builtin_amdgcn_cosf(p);
-            ui[i] = __builtin_amdgcn_sinf(p);
+        for (int k = 0; k < kChunk; ++k) {
+            const float p = __builtin_fmaf(f[0][k], xc, __builtin_fmaf(f[1][k], ly, __builtin_fmaf(f[2][k], lz, f[3][k])));
+            ur[k] = __builtin_amdgcn_cosf(p);
+            ui[k] = __builtin_amdgcn_sinf(p);
         }
         unsigned wa[4][4];
         split_parts<F16, kChunk>(ur, wa[0], wa[1]);
         split_parts<F16, kChunk>(ui, wa[2], wa[3]);
         const u32x4 arh = {wa[0][0], wa[0][1], wa[0][2], wa[0][3]}, arl = {wa[1][0], wa[1][1], wa[1][2], wa[1][3]};
         const u32x4 aih = {wa[2][0], wa[2][1], wa[2][2], wa[2][3]}, ail = {wa[3][0], wa[3][1], wa[3][2], wa[3][3]};
-        lds_barrier();   // this step's B is in LDS
-        // bshare[kb ^ 1] was last read before the barrier just passed
-        if constexpr (kTable)
-            if ((int64_t)(g + 1) * kLongStepVec4 < table_vec4)
-                issue_stage_load<kLongBlock, kLongStepVec4>(table, table_vec4, g + 1,
-                                                             reinterpret_cast<float4 *>(&bshare[kb ^ 1]));
         // the products run at raised wave priority: a wave with MFMAs to
         // issue goes before the other waves' operand work, which keeps the
         // matrix core fed (measured 3 % faster than raising the operand
@@ -1065,8 +1086,8 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < kLongTiles; ++t) {
-            const u32x4 bch = bshare[kb][0][t][quarter_k][col], bcl = bshare[kb][1][t][quarter_k][col];
-            const u32x4 bsh = bshare[kb][2][t][quarter_k][col], bsl = bshare[kb][3][t][quarter_k][col];
+            const u32x4 bch = cur.b[0][t][quarter_k][col], bcl = cur.b[1][t][quarter_k][col];
+            const u32x4 bsh = cur.b[2][t][quarter_k][col], bsl = cur.b[3][t][quarter_k][col];
             prc[t] = mfma16<F16>(arh, bch, prc[t]);
             pic[t] = mfma16<F16>(aih, bch, pic[t]);
             pis[t] = mfma16<F16>(aih, bsh, pis[t]);
@@ -1081,36 +1102,17 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
             prs[t] = mfma16<F16>(arl, bsh, prs[t]);
         }
         __builtin_amdgcn_s_setprio(0);
-        kb ^= 1;
     };
 
+    // steps in pairs, so each buffer is named statically
     auto walk = [&](auto from_table) {
-        if (nstages > 0) {
-            issue_stage_load<kLongBlock, kLinesStageVec4>(src, total_vec4, 0, stage[0]);
-            if constexpr (decltype(from_table)::value)
-                issue_stage_load<kLongBlock, kLongStepVec4>(table, table_vec4, g0,
-                                                             reinterpret_cast<float4 *>(&bshare[0]));
+        if (nsteps > 0) copy_step(0, buf0, from_table);
+        int i = 0;
+        for (; i + 1 < nsteps; i += 2) {
+            step(i, buf0, buf1, from_table);
+            step(i + 1, buf1, buf0, from_table);
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        for (int st = 0; st < nstages; ++st) {
-            const int chunks_here = min(kLinesStageChunks, nch - st * kLinesStageChunks);
-            const float4 *buf = stage[st & 1];
-            const int gs = g0 + st * (kLinesStageChunks / kLongGroup);
-            int c = 0;
-            for (; c + kLongGroup <= chunks_here; c += kLongGroup) {
-                step(buf + c * kChunkVec4, kLongGroup, gs + c / kLongGroup, std::false_type{}, from_table);
-                // the next stage's copy goes out once the stage's first step
-                // has passed its barrier, so no later barrier waits long for it
-                if (c == 0 && st + 1 < nstages)
-                    issue_stage_load<kLongBlock, kLinesStageVec4>(src, total_vec4, st + 1, stage[(st + 1) & 1]);
-            }
-            // 1 to 3 chunks at the stream's end (the last stage only)
-            if (c < chunks_here)
-                step(buf + c * kChunkVec4, chunks_here - c, gs + c / kLongGroup, std::true_type{}, from_table);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
+        if (i < nsteps) step(i, buf0, buf1, from_table);
     };
     if (use_table)
         walk(std::true_type{});
@@ -1118,7 +1120,7 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
         walk(std::false_type{});
 
     // unfold: row 4 (l / 16) + r of the wave's 16 lines, pair 16 t + l % 16
-    float *dst_r = out_r + (int64_t)blockIdx.y * N, *dst_i = out_i + (int64_t)blockIdx.y * N;
+    float *dst_r = out_r + (int64_t)split * N, *dst_i = out_i + (int64_t)split * N;
 #pragma unroll
     for (int t = 0; t < kLongTiles; ++t)
 #pragma unroll
@@ -1183,18 +1185,21 @@ int launch_line_instances(const float *packed, int nchunks, int splits, int64_t 
                           hipStream_t stream)
 {
     int rc = FHD_OK;
-    if (steps > 0) {
+    // a class needs whole units: with fewer than two (one) whole units no
+    // unit can take the long-line (line) instance, which is not launched
+    const bool long_pairs = (int64_t)N >= 2 * (int64_t)kUnitVox, whole_unit = N >= kUnitVox;
+    if (long_pairs && steps > 0) {
         fhd_long_table_kernel<F16><<<dim3((unsigned)steps), dim3(kLongBlock), 0, stream>>>(packed, nchunks, info,
                                                                                            table);
         rc = launch_status("fhd_long_table_kernel launch");
     }
-    if (rc == FHD_OK) {
+    if (rc == FHD_OK && long_pairs) {
         TimedLaunch timed(F16 ? "fhd_gather_long_lines_kernel<true>" : "fhd_gather_long_lines_kernel<false>", stream);
-        fhd_gather_long_lines_kernel<F16><<<dim3((unsigned)pairs, (unsigned)splits), dim3(kLongBlock), 0, stream>>>(
-            packed, nchunks, splits, cls, info, table, x, y, z, part_r, part_i, N);
+        fhd_gather_long_lines_kernel<F16><<<dim3((unsigned)(pairs * splits)), dim3(kLongBlock), 0, stream>>>(
+            packed, nchunks, splits, (int)pairs, cls, info, table, x, y, z, part_r, part_i, N);
         rc = launch_status("fhd_gather_long_lines_kernel launch");
     }
-    if (rc == FHD_OK) {
+    if (rc == FHD_OK && whole_unit) {
         TimedLaunch timed(F16 ? "fhd_gather_lines_kernel<true>" : "fhd_gather_lines_kernel<false>", stream);
         fhd_gather_lines_kernel<F16><<<dim3((unsigned)blocks, (unsigned)splits), dim3(kLinesBlock), 0, stream>>>(
             packed, nchunks, splits, cls, info, x, y, z, part_r, part_i, N);
@@ -1203,67 +1208,84 @@ int launch_line_instances(const float *packed, int nchunks, int splits, int64_t 
     return rc;
 }
 
-int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
-                  float *rho_r, float *rho_i, int N, hipStream_t stream, int paths)
+GatherPlan plan_gather(int M, int N, int paths, bool with_table)
 {
-    if (N == 0) return FHD_OK;
+    GatherPlan g;
+    g.paths = paths;
+    g.nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
+    g.blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
+    g.pairs = (g.blocks + 1) / 2;
     const bool matrix_cores = paths != FHD_GATHER_VECTOR;
-    const int nchunks = (int)(((int64_t)M + kChunk - 1) / kChunk);
-    const int64_t blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
-    const int64_t pairs = (blocks + 1) / 2;
     // sized for the instance that runs at length on grids: the long-line one
     // (rows of 128 voxels or more), or with the vector paths only the
     // one-step ramp path
-    const int splits =
-        matrix_cores
-            ? split_count(pairs, nchunks,
-                          blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel<true>), kLongBlock))
-            : split_count(blocks, nchunks,
-                          blocks_per_cu<2>(reinterpret_cast<const void *>(fhd_gather_kernel<kVox, true>), kBlock));
-    // one workspace: the unit classes and the info words, the B table of
+    g.splits = matrix_cores
+                   ? split_count(g.pairs, g.nchunks,
+                                 blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel<true>),
+                                                  kLongBlock))
+                   : split_count(g.blocks, g.nchunks,
+                                 blocks_per_cu<2>(reinterpret_cast<const void *>(fhd_gather_kernel<kVox, true>), kBlock));
+    // the workspace: the unit classes and the info words, the B table of
     // the long-line instance (16 KB per 32 samples), then (splits > 1) the
     // partial sums
-    const size_t cls_bytes = ((size_t)blocks * sizeof(int) + kInfoWords * sizeof(int) + 255) / 256 * 256;
-    const int64_t steps = M > 0 ? ((int64_t)nchunks + kLongGroup - 1) / kLongGroup : 0;
-    const size_t table_bytes = matrix_cores ? (size_t)steps * kLongStepVec4 * sizeof(float4) : 0;
-    const size_t part_bytes = splits > 1 ? (size_t)splits * 2 * N * sizeof(float) : 0;
-    char *work = nullptr;
-    const hipError_t e = hipMallocAsync((void **)&work, cls_bytes + table_bytes + part_bytes, stream);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (gather workspace): ") + hipGetErrorString(e));
-    }
+    g.cls_bytes = ((size_t)g.blocks * sizeof(int) + kInfoWords * sizeof(int) + 255) / 256 * 256;
+    g.steps = M > 0 && matrix_cores && with_table ? ((int64_t)g.nchunks + kLongGroup - 1) / kLongGroup : 0;
+    g.table_bytes = (size_t)g.steps * kLongStepVec4 * sizeof(float4);
+    g.part_bytes = g.splits > 1 ? (size_t)g.splits * 2 * N * sizeof(float) : 0;
+    return g;
+}
+
+int run_gather(const GatherPlan &g, char *work, const float *packed, int M, const float *x, const float *y,
+               const float *z, float *rho_r, float *rho_i, int N, hipStream_t stream)
+{
+    const bool matrix_cores = g.paths != FHD_GATHER_VECTOR;
     int *cls = reinterpret_cast<int *>(work);
-    int *info = cls + blocks;
-    float4 *table = reinterpret_cast<float4 *>(work + cls_bytes);
+    int *info = cls + g.blocks;
+    float4 *table = g.steps > 0 ? reinterpret_cast<float4 *>(work + g.cls_bytes) : nullptr;
     float *part_r = rho_r, *part_i = rho_i;
-    if (splits > 1) {
-        part_r = reinterpret_cast<float *>(work + cls_bytes + table_bytes);
-        part_i = part_r + (int64_t)splits * N;
+    if (g.splits > 1) {
+        part_r = reinterpret_cast<float *>(work + g.cls_bytes + g.table_bytes);
+        part_i = part_r + (int64_t)g.splits * N;
     }
     // the fp16 products need the largest amplitude: the classification's
     // extra workgroups reduce it
-    const bool f16 = paths == FHD_GATHER_ALL;
+    const bool f16 = g.paths == FHD_GATHER_ALL;
     int rc = launch_classify(x, y, z, N, matrix_cores, cls, info, stream, f16, packed, M);
-    const dim3 grid((unsigned)blocks, (unsigned)splits);
+    const dim3 grid((unsigned)g.blocks, (unsigned)g.splits);
     if (rc == FHD_OK && matrix_cores)
-        rc = f16 ? launch_line_instances<true>(packed, nchunks, splits, blocks, pairs, steps, cls, info, table, x, y,
-                                               z, part_r, part_i, N, stream)
-                 : launch_line_instances<false>(packed, nchunks, splits, blocks, pairs, steps, cls, info, table, x,
-                                                y, z, part_r, part_i, N, stream);
-    if (rc == FHD_OK) {
+        rc = f16 ? launch_line_instances<true>(packed, g.nchunks, g.splits, g.blocks, g.pairs, g.steps, cls, info,
+                                               table, x, y, z, part_r, part_i, N, stream)
+                 : launch_line_instances<false>(packed, g.nchunks, g.splits, g.blocks, g.pairs, g.steps, cls, info,
+                                                table, x, y, z, part_r, part_i, N, stream);
+    // the one-step ramp class also needs a whole unit
+    if (rc == FHD_OK && N >= kUnitVox) {
         TimedLaunch timed("fhd_gather_kernel<16, true>", stream);
-        fhd_gather_kernel<kVox, true><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, cls, x, y,
+        fhd_gather_kernel<kVox, true><<<grid, dim3(kBlock), 0, stream>>>(packed, g.nchunks, g.splits, cls, x, y,
                                                                           z, part_r, part_i, N);
         rc = launch_status("fhd_gather_kernel<one step> launch");
     }
     if (rc == FHD_OK) {
         TimedLaunch timed("fhd_gather_kernel<16, false>", stream);
-        fhd_gather_kernel<kVox, false><<<grid, dim3(kBlock), 0, stream>>>(packed, nchunks, splits, cls, x,
+        fhd_gather_kernel<kVox, false><<<grid, dim3(kBlock), 0, stream>>>(packed, g.nchunks, g.splits, cls, x,
                                                                            y, z, part_r, part_i, N);
         rc = launch_status("fhd_gather_kernel launch");
     }
-    if (splits > 1 && rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, N, rho_r, rho_i, stream);
+    if (g.splits > 1 && rc == FHD_OK) rc = launch_reduce(part_r, part_i, g.splits, N, rho_r, rho_i, stream);
+    return rc;
+}
+
+int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
+                  float *rho_r, float *rho_i, int N, hipStream_t stream, int paths)
+{
+    if (N == 0) return FHD_OK;
+    const GatherPlan g = plan_gather(M, N, paths, true);
+    char *work = nullptr;
+    const hipError_t e = hipMallocAsync((void **)&work, g.work_bytes(), stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (gather workspace): ") + hipGetErrorString(e));
+    }
+    int rc = run_gather(g, work, packed, M, x, y, z, rho_r, rho_i, N, stream);
     const hipError_t f = hipFreeAsync(work, stream);
     if (f != hipSuccess && rc == FHD_OK)
         rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));

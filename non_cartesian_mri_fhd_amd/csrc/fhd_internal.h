@@ -176,6 +176,19 @@ __device__ __forceinline__ void stream_chunks(const float4 *__restrict__ src, in
                            [&](const float4 *ch, int) { body(ch); });
 }
 
+// The hardware hands workgroup b of a launch to XCD b % kXcds (each XCD
+// has its own L2). For a grid of `total` work units numbered split-major,
+// xcd_unit gives workgroup b the unit that makes each XCD's workgroups a
+// contiguous run of units -- so each XCD walks one split's part of the
+// sample stream (two at a boundary) instead of all of them. A bijection of
+// [0, total).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_unit(int64_t b, int64_t total)
+{
+    const int64_t per = total / kXcds, rem = total % kXcds, k = b % kXcds;
+    return k * per + (k < rem ? k : rem) + b / kXcds;
+}
+
 // Chunk range of split `s` when nchunks chunks are cut into `splits` parts
 // of whole stages of STAGE_CHUNKS chunks.
 template <int STAGE_CHUNKS = kStageChunks>
@@ -436,9 +449,27 @@ int launch_classify(const float *x, const float *y, const float *z, int N, bool 
                     int M = 0);
 // paths: FHD_GATHER_ALL (lines on the matrix cores in split fp16, the
 // rest on the vector ALUs), FHD_GATHER_BF16X3 (the same in split bf16) or
-// FHD_GATHER_VECTOR (every unit on the vector-ALU paths).
+// FHD_GATHER_VECTOR (every unit on the vector-ALU paths). Takes its
+// workspace stream-ordered from hipMallocAsync.
 int launch_gather(const float *packed, int M, const float *x, const float *y, const float *z,
                   float *rho_r, float *rho_i, int N, hipStream_t stream, int paths = FHD_GATHER_ALL);
+
+// The gather's launch shape and workspace for M samples and N > 0 voxels:
+// the unit classes and info words, the long-line instance's B table (left
+// out when with_table is false: its workgroups then form B themselves, with
+// bitwise the same results), and the split partial sums. run_gather
+// launches the gather into a caller's workspace of work_bytes() bytes,
+// 256-byte aligned; nothing in it needs clearing first.
+struct GatherPlan {
+    int paths = FHD_GATHER_ALL;
+    int nchunks = 0, splits = 1;
+    int64_t blocks = 0, pairs = 0, steps = 0;
+    size_t cls_bytes = 0, table_bytes = 0, part_bytes = 0;
+    size_t work_bytes() const { return cls_bytes + table_bytes + part_bytes; }
+};
+GatherPlan plan_gather(int M, int N, int paths, bool with_table);
+int run_gather(const GatherPlan &g, char *work, const float *packed, int M, const float *x, const float *y,
+               const float *z, float *rho_r, float *rho_i, int N, hipStream_t stream);
 // fhd_forward.hip: forward F
 // (with a gate: nothing when lines_form_ran(gate))
 int launch_forward_pack(const float *x, const float *y, const float *z, const float *rho_r,

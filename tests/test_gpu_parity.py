@@ -177,6 +177,23 @@ def test_bitwise_repeatable_and_two_stage_equal(dev):
         assert torch.equal(u[0], v[0]) and torch.equal(u[1], v[1])
 
 
+@pytest.mark.parametrize("paths", ["all", "bf16x3"])
+def test_full_size_line_form_repeatable(dev, paths):
+    """At 128^3 x 100,000, in the launch shape the benchmark times (the
+    long-line instance with its B table, three sample splits), four calls
+    in a row give bitwise identical results. The workgroups' waves share
+    each step's copies into LDS, so a missing wait between them would show
+    up as differences from run to run."""
+    w = inputs.make_workload("spiral128")
+    t = to_dev(w, dev)
+    code = binding.FHD_GATHER_ALL if paths == "all" else binding.FHD_GATHER_BF16X3
+    runs = [binding.fhd_compute(t["kx"], t["ky"], t["kz"], t["Dr"], t["Di"], t["x"], t["y"], t["z"],
+                                paths=code) for _ in range(4)]
+    torch.cuda.synchronize(dev)
+    for r in runs[1:]:
+        assert torch.equal(r[0], runs[0][0]) and torch.equal(r[1], runs[0][1])
+
+
 def test_side_stream(dev):
     """Work is enqueued on the caller's stream."""
     c = inputs.random_case(3000, 500, seed=8)
