@@ -422,6 +422,37 @@ int fhd_cg_grid(const float *kx, const float *ky, const float *kz,
 void fhd_gather_config(int *voxels_per_lane, int *samples_per_chunk, int *block_threads);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fhd_compute_paths (same arguments, same results bit for bit) with every
+ * temporary -- the packed k-space, the unit classes and the split partial
+ * sums -- in one device array of FHD_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held from the library's first use of that GPU
+ * until the process ends. The call allocates and frees nothing.
+ *   - The workspace needed is about 20 bytes per sample (rounded up to 8
+ *     samples), 4 bytes per 4096 voxels plus 272, and, when the voxels are
+ *     too few to fill the GPU in one pass over the samples, 8 bytes per
+ *     voxel for each of up to 16 partial sums (3 at 128^3 voxels); the
+ *     call computes it exactly and returns FHD_ERR_INVALID_ARG, saying how
+ *     many bytes it needed, when it exceeds the array. 128^3 voxels x
+ *     100,000 samples needs about 50 MiB; 256^3 x 100,000 about 2 MiB.
+ *   - Every call on one GPU uses that GPU's array: calls that overlap on
+ *     one GPU (on different streams, or from different threads without
+ *     ordering) race and give wrong results. Calls on one stream are
+ *     ordered and safe. Nothing in the array needs clearing between calls.
+ *   - The long-line form builds its cos / sin factor operands inside each
+ *     workgroup instead of from a per-call table (slightly slower).
+ * Errors: FHD_ERR_INVALID_ARG (also for a workspace beyond the array),
+ * FHD_ERR_HIP.
+ */
+#define FHD_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+int fhd_compute_noalloc(const float *kx, const float *ky, const float *kz,
+                        const float *Dr, const float *Di,
+                        const float *x, const float *y, const float *z,
+                        float *rho_r, float *rho_i, int M, int N, int paths,
+                        void *stream);
+
+/*
  * Measurement hook, not part of any computation. After this call, the
  * calling thread's next `count` launches of the library kernel named
  * `kernel` record events[2*i] on their stream just before launch i and

@@ -61,6 +61,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_compute.restype = i32
     lib.fhd_compute_paths.argtypes = [fp] * 10 + [i32, i32, i32, vp]
     lib.fhd_compute_paths.restype = i32
+    lib.fhd_compute_noalloc.argtypes = [fp] * 10 + [i32, i32, i32, vp]
+    lib.fhd_compute_noalloc.restype = i32
     lib.fhd_scatter.argtypes = [fp] * 10 + [i32, i32, vp]
     lib.fhd_scatter.restype = i32
     lib.fhd_packed_bytes.argtypes = [i32]
@@ -175,6 +177,24 @@ def fhd_compute(kx, ky, kz, Dr, Di, x, y, z, rho_r=None, rho_i=None, stream=None
         else:
             _check(lib, lib.fhd_compute_paths(*ptrs, M, N, int(paths), _stream(dev, stream)),
                    "fhd_compute_paths")
+    return rho_r, rho_i
+
+
+def fhd_compute_noalloc(kx, ky, kz, Dr, Di, x, y, z, rho_r, rho_i, stream=None,
+                        paths: int = FHD_GATHER_ALL):
+    """rho = F^H D with no allocation in the library (its static per-GPU
+    scratch array holds every temporary); rho_r and rho_i are the caller's
+    float32 tensors. Calls that overlap on one GPU race."""
+    lib = load()
+    M, N = kx.numel(), x.numel()
+    dev = x.device
+    ptrs = [_vec(t, nm, M, dev) for t, nm in ((kx, "kx"), (ky, "ky"), (kz, "kz"),
+                                               (Dr, "Dr"), (Di, "Di"))]
+    ptrs += [_vec(t, nm, N, dev) for t, nm in ((x, "x"), (y, "y"), (z, "z"),
+                                               (rho_r, "rho_r"), (rho_i, "rho_i"))]
+    with torch.cuda.device(dev):
+        _check(lib, lib.fhd_compute_noalloc(*ptrs, M, N, int(paths), _stream(dev, stream)),
+               "fhd_compute_noalloc")
     return rho_r, rho_i
 
 

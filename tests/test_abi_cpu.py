@@ -357,3 +357,21 @@ def test_stale_library_is_rebuilt_when_a_source_is_newer(tmp_path):
         os.utime(header, (st.st_atime, st.st_mtime))
     assert not build.is_stale("libfhd.so")
     assert header in build.sources_of("libfhd.so")
+
+
+def test_noalloc_argument_checks(lib):
+    """fhd_compute_noalloc refuses bad arguments, and a workspace beyond its
+    scratch array, before touching any device memory: four million samples
+    need 80 MB of packed k-space alone, above FHD_NOALLOC_SCRATCH_BYTES
+    (64 MiB). The pointers of that case are never dereferenced."""
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.fhd_compute_noalloc.argtypes = [vp] * 10 + [i32, i32, i32, vp]
+    assert lib.fhd_compute_noalloc(*[None] * 10, -1, 5, 0, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_compute_noalloc(*[None] * 10, 5, -1, 0, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_compute_noalloc(*[None] * 10, 0, 0, 3, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_compute_noalloc(*[None] * 10, 0, 0, 0, None) == FHD_OK
+    assert lib.fhd_compute_noalloc(*[None] * 10, 0, 5, 0, None) == FHD_ERR_INVALID_ARG
+    fake = [0x10000000 * (i + 1) for i in range(10)]
+    assert lib.fhd_compute_noalloc(*fake, 4_000_000, 4096, 0, None) == FHD_ERR_INVALID_ARG
+    msg = lib.fhd_last_error()
+    assert b"needs" in msg and str(64 * 1024 * 1024).encode() in msg
