@@ -177,12 +177,31 @@ def path_dtype(paths: str, lines_fraction: float) -> str:
     return "mixed: %.3f of voxels %s; the rest f32" % (lines_fraction, PATH_DTYPE[paths])
 
 
-def roofline_for(kernel: str, terms: float, kernel_ms: float, traffic) -> dict:
+def alu_ceiling(kernel: str, fractions=None) -> float:
+    """Terms/s issue ceiling of a vector-ALU kernel: the one-step ramp
+    instance at ROOF_TERMS_RAMP, the general instance at its mix of per-lane
+    ramps and direct evaluation (fractions = the layout's voxel fractions
+    (lines, one-step, per-lane ramps)), F's vector gather at its ramp-chunk
+    ceiling on ramp layouts, else direct evaluation R."""
+    if kernel == "fhd_gather_kernel<16, true>":
+        return ROOF_TERMS_RAMP
+    if kernel == "fhd_gather_kernel<16, false>" and fractions is not None:
+        ln, on, la = fractions
+        return roof_terms([(la, ROOF_TERMS_RAMP_LANE), (max(0.0, 1.0 - ln - on - la), ROOF_TERMS)])
+    if kernel.startswith("fhd_forward_gather_kernel") and fractions is not None and sum(fractions[1:]) > 0.5:
+        return ROOF_TERMS_RAMP_F
+    return ROOF_TERMS
+
+
+def roofline_for(kernel: str, terms: float, kernel_ms: float, traffic, fractions=None) -> dict:
     """Roofline figures of one launch of `kernel` over `terms` voxel-sample
     terms taking kernel_ms: achieved = 13 FLOP per term over the launch's
-    duration, against the peak of the arithmetic the kernel runs on (dense
-    fp16/bf16 matrix cores for the line forms, the FP32 vector peak for the
-    vector paths), with the matrix cores' executed-FLOP utilisation beside."""
+    duration. The line forms are held against the dense fp16/bf16
+    matrix-core peak (with their executed-FLOP utilisation beside); the
+    vector-ALU kernels against their own issue ceiling (alu_ceiling, from
+    the instruction counts per term and the chip's SIMD count and clock),
+    expressed at 13 FLOP per term, since their ramp recurrences reach a
+    13-FLOP term with fewer operations than 13."""
     rate = terms / (kernel_ms * 1e-3)
     out = {"kernel": kernel, "achieved": FLOP_PER_TERM * rate / 1e12, "unit": "TFLOP/s",
            "traffic": traffic, "flop_per_term": FLOP_PER_TERM}
@@ -192,9 +211,11 @@ def roofline_for(kernel: str, terms: float, kernel_ms: float, traffic) -> dict:
                              "tflops": LINES_EXEC_FLOP_PER_TERM * rate / 1e12,
                              "frac": LINES_EXEC_FLOP_PER_TERM * rate / P_MFMA_F16})
     else:
-        out.update(bound="alu", peak=P_FP32 / 1e12,
-                   note="the ramp paths evaluate fewer operations per term than 13 FLOP; "
-                        "path_ceiling gives the fraction of their issue ceiling")
+        ceiling = alu_ceiling(kernel, fractions)
+        out.update(bound="alu", peak=FLOP_PER_TERM * ceiling / 1e12, ceiling_terms_per_s=ceiling,
+                   fp32_vector_peak=P_FP32 / 1e12,
+                   note="peak: this kernel's VALU + transcendental issue ceiling in terms/s "
+                        "(256 CUs x 4 SIMDs x 2.4 GHz) at 13 FLOP per term")
     out["frac"] = out["achieved"] / out["peak"]
     return out
 
@@ -392,7 +413,8 @@ def main(argv=None) -> int:
             "one_step_voxel_fraction": one, "per_lane_ramp_voxel_fraction": lane,
             **binding.gather_config(),
         },
-        "roofline": roofline_for(kernel, terms * kernel_share, k_ms, measured_traffic(kernel, args.workload)),
+        "roofline": roofline_for(kernel, terms * kernel_share, k_ms, measured_traffic(kernel, args.workload),
+                                 (lines, one, lane)),
         "roofline_direct_form": {
             "note": "R = 9.83e12 terms/s: the pages' direct evaluation, 2 transcendentals per term "
                     "on the vector ALUs; fraction of the whole fhd_gather call",
@@ -417,11 +439,12 @@ def main(argv=None) -> int:
         c2, _, n2 = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=p != "vector")
         k2, share2 = adjoint_kernel(c2, n2, p)
         call_ms, kms = timed_calls(lambda: gather(p), 3, stream, k2, 1, dev)
-        (l2, _, _), _ = adjoint_ceiling(w, p != "vector")
-        others[p] = {"dtype": path_dtype(p, l2), "fhd_gather_call": summary(call_ms),
+        fr2, _ = adjoint_ceiling(w, p != "vector")
+        others[p] = {"dtype": path_dtype(p, fr2[0]), "fhd_gather_call": summary(call_ms),
                      "kernel_ms": {"kernel": k2, **summary(kms)},
                      "terms_per_s": terms / (np.mean(call_ms) * 1e-3),
-                     "roofline": roofline_for(k2, terms * share2, summary(kms)["mean"], None),
+                     "roofline": roofline_for(k2, terms * share2, summary(kms)["mean"],
+                                              measured_traffic(k2, args.workload), fr2),
                      "time_over_timed_path": float(np.mean(call_ms) / np.mean(gather_ms))}
     out["other_paths"] = others
 
@@ -558,7 +581,10 @@ def bench_other(args) -> int:
                                "frac": exec_flop * rate / peak, "flop_per_term": exec_flop,
                                "traffic": measured_traffic(kernel, args.workload)}
         else:
-            out["roofline"] = roofline_for(kernel, per_launch, km["mean"], measured_traffic(kernel, args.workload))
+            # F's vector gather sees the voxels' ramps whatever the paths
+            fr, _ = adjoint_ceiling(w, args.paths != "vector" and not kernel.startswith("fhd_forward_gather"))
+            out["roofline"] = roofline_for(kernel, per_launch, km["mean"], measured_traffic(kernel, args.workload),
+                                           fr)
         out["kernel_ms"] = {"kernel": kernel, "launches_per_call": launches, **km}
     if args.op == "scatter":
         gr = torch.empty(N, device=dev)
