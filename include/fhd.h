@@ -22,6 +22,13 @@
  *     stream) and the call returns without synchronising. Calls on one
  *     stream run in order.
  *   - Outputs are overwritten, never accumulated into.
+ *   - Temporaries (packed k-space, unit classes, factor tables, split
+ *     partial sums) live in device buffers the library keeps per (device,
+ *     stream) between calls, grown when a call needs more, until
+ *     fhd_release_workspaces(). While `stream` is being captured into a
+ *     graph, a call takes stream-ordered allocations (hipMallocAsync) and
+ *     frees them (hipFreeAsync) instead. Calls on one stream from several
+ *     host threads are serialised by the library.
  *   - Return value: FHD_OK (0) or a negative FHD_ERR_* status. Argument
  *     checks that need no device (null pointers, negative sizes, overlaps,
  *     alignment) run before any HIP call; then pointers are checked to be
@@ -84,8 +91,8 @@ extern "C" {
 /*
  * rho = F^H D over N voxels and M samples (section 17.3, F^H D equation).
  * Runs the loop-fission pre-pass (fhd_pack, section 17.3.2) into a
- * stream-ordered workspace of fhd_packed_bytes(M) bytes that the library
- * allocates and frees on `stream`, then the gather (fhd_gather, one lane
+ * workspace of fhd_packed_bytes(M) bytes that the library keeps for
+ * `stream`, then the gather (fhd_gather, one lane
  * per voxel with no atomics, section 17.3.1) with the default paths,
  * FHD_GATHER_ALL: units of lines along x on the matrix cores with
  * fp32-class split-fp16 products, the rest on the vector ALUs in fp32 (see
@@ -432,9 +439,11 @@ void fhd_gather_config(int *voxels_per_lane, int *samples_per_chunk, int *block_
  *   - The workspace needed is about 20 bytes per sample (rounded up to 8
  *     samples), 4 bytes per 4096 voxels plus 272, and, when the voxels are
  *     too few to fill the GPU in one pass over the samples, 8 bytes per
- *     voxel for each of up to 16 partial sums (3 at 128^3 voxels); the
- *     call computes it exactly and returns FHD_ERR_INVALID_ARG, saying how
- *     many bytes it needed, when it exceeds the array. 128^3 voxels x
+ *     voxel for each partial sum: as many as the instance that takes most
+ *     of an x-fastest grid needs to fill the GPU (3 at 128^3 voxels, 24 at
+ *     64^3), the other instances' within the larger of that and 48 MiB;
+ *     the call computes it exactly and returns FHD_ERR_INVALID_ARG, saying
+ *     how many bytes it needed, when it exceeds the array. 128^3 voxels x
  *     100,000 samples needs about 50 MiB; 256^3 x 100,000 about 2 MiB.
  *   - Every call on one GPU uses that GPU's array: calls that overlap on
  *     one GPU (on different streams, or from different threads without
@@ -477,6 +486,14 @@ int fhd_time_kernel(const char *kernel, void *const *events, int count);
 
 /* Launches recorded on the calling thread since its last fhd_time_kernel. */
 int fhd_timed_launches(void);
+
+/*
+ * Frees every workspace the library keeps (see the conventions above),
+ * after waiting for all work on each device that holds one. The next call
+ * on a stream allocates again. Not to be called while another thread is
+ * inside a library call. Errors: FHD_ERR_HIP.
+ */
+int fhd_release_workspaces(void);
 
 /* Static description of a status code. Never NULL. */
 const char *fhd_status_string(int status);

@@ -111,6 +111,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fhd_timed_launches.restype = i32
     lib.fhd_gather_config.argtypes = [ctypes.POINTER(ctypes.c_int)] * 3
     lib.fhd_gather_config.restype = None
+    lib.fhd_release_workspaces.argtypes = []
+    lib.fhd_release_workspaces.restype = i32
     lib.fhd_status_string.argtypes = [i32]
     lib.fhd_status_string.restype = ctypes.c_char_p
     lib.fhd_last_error.argtypes = []
@@ -178,6 +180,12 @@ def fhd_compute(kx, ky, kz, Dr, Di, x, y, z, rho_r=None, rho_i=None, stream=None
             _check(lib, lib.fhd_compute_paths(*ptrs, M, N, int(paths), _stream(dev, stream)),
                    "fhd_compute_paths")
     return rho_r, rho_i
+
+
+def fhd_release_workspaces() -> None:
+    """Free the device buffers the library keeps per stream between calls."""
+    lib = load()
+    _check(lib, lib.fhd_release_workspaces(), "fhd_release_workspaces")
 
 
 def fhd_compute_noalloc(kx, ky, kz, Dr, Di, x, y, z, rho_r, rho_i, stream=None,

@@ -28,7 +28,7 @@ HIP_FLAGS = [
 # library name -> source files
 LIBRARIES = {
     "libfhd.so": ["fhd.hip", "fhd_forward.hip", "fhd_cg.hip", "fhd_grid.hip", "fhd_scatter.hip",
-                  "fhd_noalloc.hip", "abi_checks.hip"],
+                  "fhd_noalloc.hip", "fhd_workspace.hip", "abi_checks.hip"],
     "libfhd_microbench.so": ["microbench.hip"],
 }
 

@@ -127,34 +127,49 @@ int check_device_spans(const Span *spans, int count)
     return FHD_OK;
 }
 
-int split_count(int64_t blocks, int nchunks, int per_cu)
+int device_cus()
 {
     static int cus_cached[64] = {0};
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= 64) {
         (void)hipGetLastError();
-        return 1;
+        return 0;
     }
     if (cus_cached[device] == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
             cus <= 0) {
             (void)hipGetLastError();
-            return 1;
+            return 0;
         }
         cus_cached[device] = cus;
     }
+    return cus_cached[device];
+}
+
+int split_count(int64_t blocks, int nchunks, int per_cu, int granule)
+{
+    const int cus = device_cus();
+    if (cus <= 0) return 1;
     if (per_cu < 1) per_cu = 1;
-    const int64_t resident = (int64_t)per_cu * cus_cached[device];
-    const int64_t stages = (nchunks + kStageChunks - 1) / kStageChunks;
+    const int64_t resident = (int64_t)per_cu * cus;
+    if (granule < 1) granule = 1;
+    const int64_t stages = (nchunks + granule - 1) / granule;
     if (blocks <= 0 || stages <= 1) return 1;
     // Cutting the stream s ways makes every workgroup's work 1/s as long and
     // the launch ceil(s blocks / resident) rounds of them: time ~ rounds / s,
     // bounded below by blocks / resident. Take the fewest ways (at most one
-    // per stage, and at most 16 or two rounds' worth) that come within 3 %
+    // per granule, and at most 16 or two rounds' worth) that come within 3 %
     // of the best.
+    // s ways give every split ceil(stages / s) granules, so only
+    // ceil(stages / that) of them have any: count those
+    auto ways = [&](int64_t s) {
+        const int64_t per = (stages + s - 1) / s;
+        return (stages + per - 1) / per;
+    };
     auto cost = [&](int64_t s) {
-        return (double)((blocks * s + resident - 1) / resident) / (double)s;
+        const int64_t w = ways(s);
+        return (double)((blocks * w + resident - 1) / resident) / (double)w;
     };
     int64_t most = 2 * resident / blocks;
     if (most < 16) most = 16;
@@ -162,7 +177,7 @@ int split_count(int64_t blocks, int nchunks, int per_cu)
     double lowest = cost(1);
     for (int64_t s = 2; s <= most; ++s) lowest = cost(s) < lowest ? cost(s) : lowest;
     for (int64_t s = 1; s <= most; ++s)
-        if (cost(s) <= 1.03 * lowest) return (int)s;
+        if (cost(s) <= 1.03 * lowest) return (int)ways(s);
     return 1;
 }
 
@@ -177,8 +192,24 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float *__restr
     if (gate != nullptr && lines_form_ran(gate) != (gate_want != 0)) return;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
+    // eight rows' loads in flight at a time, added in row order
+    constexpr int kBatch = 8;
     float sr = 0.0f, si = 0.0f;
-    for (int s = 0; s < splits; ++s) {
+    int s = 0;
+    for (; s + kBatch <= splits; s += kBatch) {
+        float a[kBatch], b[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            a[k] = part_r[(int64_t)(s + k) * n + i];
+            b[k] = part_i[(int64_t)(s + k) * n + i];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            sr += a[k];
+            si += b[k];
+        }
+    }
+    for (; s < splits; ++s) {
         sr += part_r[(int64_t)s * n + i];
         si += part_i[(int64_t)s * n + i];
     }

@@ -72,6 +72,7 @@ namespace fhd {
 namespace {
 
 constexpr int kVox = 16;        // consecutive voxels per lane
+constexpr int kVecGranuleChunks = 8;   // the vector instances' split granule (64 samples)
 constexpr int kDirectGroup = 8; // voxels per transcendental group on the direct paths
 static_assert(kVox % kDirectGroup == 0, "direct groups tile a lane's voxels");
 constexpr int kRampGroup = 4;   // samples per transcendental group on the ramp path
@@ -448,12 +449,32 @@ static_assert(kLongLineVox % kVox == 0 && 64 % (kLongLineVox / kVox) == 0, "a li
 
 // Lane l of workgroup b owns voxels (b kBlock + l) V + v, v < V. Voxels past
 // N copy the lane's first voxel, so they never spoil the shared-(y, z) test
-// (their results are not stored).
-template <int V>
+// (their results are not stored). With VEC4, a lane with all V voxels in
+// range reads them as float4s when the coordinate arrays are 16-byte
+// aligned (the classification; the gather instances keep scalar loads,
+// which leave their register allocation as it is).
+template <int V, bool VEC4 = false>
 __device__ __forceinline__ void load_lane_voxels(const float *__restrict__ x, const float *__restrict__ y,
                                                  const float *__restrict__ z, int N, int64_t n0,
                                                  float (&px)[V], float (&py)[V], float (&pz)[V])
 {
+    if constexpr (VEC4 && V % 4 == 0) {
+        const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) |
+                               reinterpret_cast<uintptr_t>(z)) & 15) == 0;
+        if (aligned && n0 + V <= N) {
+            const float4 *x4 = reinterpret_cast<const float4 *>(x + n0);
+            const float4 *y4 = reinterpret_cast<const float4 *>(y + n0);
+            const float4 *z4 = reinterpret_cast<const float4 *>(z + n0);
+#pragma unroll
+            for (int q = 0; q < V / 4; ++q) {
+                const float4 a = x4[q], b = y4[q], c = z4[q];
+                px[4 * q] = a.x, px[4 * q + 1] = a.y, px[4 * q + 2] = a.z, px[4 * q + 3] = a.w;
+                py[4 * q] = b.x, py[4 * q + 1] = b.y, py[4 * q + 2] = b.z, py[4 * q + 3] = b.w;
+                pz[4 * q] = c.x, pz[4 * q + 1] = c.y, pz[4 * q + 2] = c.z, pz[4 * q + 3] = c.w;
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         const int64_t n = n0 + v;
@@ -581,7 +602,7 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
     float dx = 0.0f, d64 = 0.0f, d128 = 0.0f;
     if (present) {   // uniform over each wave
         float px[kVox], py[kVox], pz[kVox];
-        load_lane_voxels<kVox>(x, y, z, N, n0, px, py, pz);
+        load_lane_voxels<kVox, true>(x, y, z, N, n0, px, py, pz);
         bool same_yz;
         ramp = lane_ramp<kVox>(px, py, pz, n0, N, &same_yz, &dx);
         const bool whole = unit + kUnitVox <= N;
@@ -631,8 +652,10 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
 // class kClassOneStep (the ramp path with sample records, at 5 waves per
 // SIMD, <= 96 VGPRs) and ONE_STEP = false those of class kClassGeneral (at
 // 4 waves per SIMD, <= 128 VGPRs); each returns at once for the others.
-// Split s = blockIdx.y of `splits` takes its share of the sample stream and
-// writes rho (splits == 1) or its partial sums at out + s*N.
+// Split s = blockIdx.y of `splits` takes its share of the sample stream, in
+// whole granules of kVecGranuleChunks chunks (so that a grid of few units
+// can still fill the chip), and writes rho (splits == 1) or its partial
+// sums at out + s*N.
 template <int V, bool ONE_STEP>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP ? 5 : 4))) void fhd_gather_kernel(
     const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
@@ -658,7 +681,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP
     const bool ramp = lane_ramp<V>(px, py, pz, n0, N, &same_yz, &dx);
 
     int c0, c1;
-    split_range(nchunks, splits, blockIdx.y, &c0, &c1);
+    split_range<kVecGranuleChunks>(nchunks, splits, blockIdx.y, &c0, &c1);
     if constexpr (ONE_STEP) {
         // every lane is a ramp of the unit's common step
         ramp_one_step<V>(src, c0, c1, stage, side, px[0], 0.5f * dx, py[0], pz[0], acc_r, acc_i);
@@ -1177,36 +1200,89 @@ int launch_classify(const float *x, const float *y, const float *z, int N, bool 
 }
 
 // The matrix-core instances of one split type (F16: fp16 parts, the
-// default; else bf16 parts).
+// default; else bf16 parts). Each writes rho itself when its split count
+// is 1, else its partial sums.
 template <bool F16>
-int launch_line_instances(const float *packed, int nchunks, int splits, int64_t blocks, int64_t pairs,
-                          int64_t steps, const int *cls, const int *info, float4 *table, const float *x,
-                          const float *y, const float *z, float *part_r, float *part_i, int N,
-                          hipStream_t stream)
+int launch_line_instances(const GatherPlan &g, const int *cls, const int *info, float4 *table, const float *x,
+                          const float *y, const float *z, float *rho_r, float *rho_i, float *part_r,
+                          float *part_i, int N, const float *packed, hipStream_t stream)
 {
     int rc = FHD_OK;
     // a class needs whole units: with fewer than two (one) whole units no
     // unit can take the long-line (line) instance, which is not launched
     const bool long_pairs = (int64_t)N >= 2 * (int64_t)kUnitVox, whole_unit = N >= kUnitVox;
-    if (long_pairs && steps > 0) {
-        fhd_long_table_kernel<F16><<<dim3((unsigned)steps), dim3(kLongBlock), 0, stream>>>(packed, nchunks, info,
-                                                                                           table);
+    if (long_pairs && g.steps > 0) {
+        fhd_long_table_kernel<F16><<<dim3((unsigned)g.steps), dim3(kLongBlock), 0, stream>>>(packed, g.nchunks,
+                                                                                             info, table);
         rc = launch_status("fhd_long_table_kernel launch");
     }
     if (rc == FHD_OK && long_pairs) {
+        const bool direct = g.s_long == 1;
         TimedLaunch timed(F16 ? "fhd_gather_long_lines_kernel<true>" : "fhd_gather_long_lines_kernel<false>", stream);
-        fhd_gather_long_lines_kernel<F16><<<dim3((unsigned)(pairs * splits)), dim3(kLongBlock), 0, stream>>>(
-            packed, nchunks, splits, (int)pairs, cls, info, table, x, y, z, part_r, part_i, N);
+        fhd_gather_long_lines_kernel<F16><<<dim3((unsigned)(g.pairs * g.s_long)), dim3(kLongBlock), 0, stream>>>(
+            packed, g.nchunks, g.s_long, (int)g.pairs, cls, info, table, x, y, z, direct ? rho_r : part_r,
+            direct ? rho_i : part_i, N);
         rc = launch_status("fhd_gather_long_lines_kernel launch");
     }
     if (rc == FHD_OK && whole_unit) {
+        const bool direct = g.s_lines == 1;
         TimedLaunch timed(F16 ? "fhd_gather_lines_kernel<true>" : "fhd_gather_lines_kernel<false>", stream);
-        fhd_gather_lines_kernel<F16><<<dim3((unsigned)blocks, (unsigned)splits), dim3(kLinesBlock), 0, stream>>>(
-            packed, nchunks, splits, cls, info, x, y, z, part_r, part_i, N);
+        fhd_gather_lines_kernel<F16><<<dim3((unsigned)g.blocks, (unsigned)g.s_lines), dim3(kLinesBlock), 0,
+                                        stream>>>(packed, g.nchunks, g.s_lines, cls, info, x, y, z,
+                                                  direct ? rho_r : part_r, direct ? rho_i : part_i, N);
         rc = launch_status("fhd_gather_lines_kernel launch");
     }
     return rc;
 }
+
+// rho_n = the sum over s < S of part[s N + n] in increasing s, where S is
+// the split count of the instance that took voxel n's unit; nothing where
+// S = 1 (that instance wrote rho itself).
+__global__ __launch_bounds__(256) void fhd_reduce_units_kernel(const float *__restrict__ part_r,
+                                                               const float *__restrict__ part_i,
+                                                               const int *__restrict__ cls, int s_vec,
+                                                               int s_lines, int s_long, int N,
+                                                               float *__restrict__ out_r,
+                                                               float *__restrict__ out_i)
+{
+    static_assert(kUnitVox % 256 == 0, "a workgroup lies in one unit");
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= N) return;
+    const int c = cls[i / kUnitVox];
+    const int splits = c == kClassLongPair ? s_long : c == kClassLines ? s_lines : s_vec;
+    if (splits <= 1) return;
+    // eight rows' loads in flight at a time, added in row order
+    constexpr int kBatch = 8;
+    float sr = 0.0f, si = 0.0f;
+    int s = 0;
+    for (; s + kBatch <= splits; s += kBatch) {
+        float a[kBatch], b[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            a[k] = part_r[(int64_t)(s + k) * N + i];
+            b[k] = part_i[(int64_t)(s + k) * N + i];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            sr += a[k];
+            si += b[k];
+        }
+    }
+    for (; s < splits; ++s) {
+        sr += part_r[(int64_t)s * N + i];
+        si += part_i[(int64_t)s * N + i];
+    }
+    out_r[i] = sr;
+    out_i[i] = si;
+}
+
+// Partial sums beyond the first instance's own rows: at most this many
+// bytes. The first instance in the plan -- the long-line one where it can
+// run, else the 64-voxel line one, else the vector ones -- takes the split
+// count that balances it; the instances behind it (which take what the
+// first one leaves: rows of other lengths, voxels off a grid) at most as
+// many rows as the first one's or this budget allows.
+constexpr size_t kPartBudget = (size_t)48 << 20;
 
 GatherPlan plan_gather(int M, int N, int paths, bool with_table)
 {
@@ -1216,15 +1292,36 @@ GatherPlan plan_gather(int M, int N, int paths, bool with_table)
     g.blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
     g.pairs = (g.blocks + 1) / 2;
     const bool matrix_cores = paths != FHD_GATHER_VECTOR;
-    // sized for the instance that runs at length on grids: the long-line one
-    // (rows of 128 voxels or more), or with the vector paths only the
-    // one-step ramp path
-    g.splits = matrix_cores
-                   ? split_count(g.pairs, g.nchunks,
-                                 blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel<true>),
-                                                  kLongBlock))
-                   : split_count(g.blocks, g.nchunks,
-                                 blocks_per_cu<2>(reinterpret_cast<const void *>(fhd_gather_kernel<kVox, true>), kBlock));
+    const bool long_pairs = matrix_cores && (int64_t)N >= 2 * (int64_t)kUnitVox;
+    const bool whole_unit = matrix_cores && N >= kUnitVox;
+    if (long_pairs)
+        g.s_long = split_count(g.pairs, g.nchunks,
+                               blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel<true>),
+                                                kLongBlock),
+                               kLinesStageChunks);
+    if (whole_unit)
+        g.s_lines = split_count(g.blocks, g.nchunks,
+                                blocks_per_cu<3>(reinterpret_cast<const void *>(fhd_gather_lines_kernel<true>),
+                                                 kLinesBlock),
+                                kLinesStageChunks);
+    // the vector instances split as the one-step ramp instance needs: at
+    // its full occupancy when the units alone fill the CUs (the splits then
+    // even out the last round), else to two workgroups per CU (measured:
+    // more, each with fewer samples, take longer on grids of a few units)
+    const int vec_occupancy =
+        blocks_per_cu<2>(reinterpret_cast<const void *>(fhd_gather_kernel<kVox, true>), kBlock);
+    const int vec_per_cu = g.blocks >= device_cus() || vec_occupancy < 2 ? vec_occupancy : 2;
+    g.s_vec = split_count(g.blocks, g.nchunks, vec_per_cu, kVecGranuleChunks);
+    if (matrix_cores) {
+        const int first = long_pairs ? g.s_long : whole_unit ? g.s_lines : g.s_vec;
+        const int64_t budget_rows = N > 0 ? (int64_t)(kPartBudget / (2 * sizeof(float) * (size_t)N)) : 1;
+        const int cap = (int)(budget_rows > first ? (budget_rows < (1 << 20) ? budget_rows : (1 << 20)) : first);
+        if (long_pairs && g.s_lines > cap) g.s_lines = cap;
+        if (g.s_vec > cap) g.s_vec = cap;
+    }
+    g.splits = g.s_vec;
+    if (g.s_long > g.splits) g.splits = g.s_long;
+    if (g.s_lines > g.splits) g.splits = g.s_lines;
     // the workspace: the unit classes and the info words, the B table of
     // the long-line instance (16 KB per 32 samples), then (splits > 1) the
     // partial sums
@@ -1242,7 +1339,7 @@ int run_gather(const GatherPlan &g, char *work, const float *packed, int M, cons
     int *cls = reinterpret_cast<int *>(work);
     int *info = cls + g.blocks;
     float4 *table = g.steps > 0 ? reinterpret_cast<float4 *>(work + g.cls_bytes) : nullptr;
-    float *part_r = rho_r, *part_i = rho_i;
+    float *part_r = nullptr, *part_i = nullptr;
     if (g.splits > 1) {
         part_r = reinterpret_cast<float *>(work + g.cls_bytes + g.table_bytes);
         part_i = part_r + (int64_t)g.splits * N;
@@ -1251,26 +1348,36 @@ int run_gather(const GatherPlan &g, char *work, const float *packed, int M, cons
     // extra workgroups reduce it
     const bool f16 = g.paths == FHD_GATHER_ALL;
     int rc = launch_classify(x, y, z, N, matrix_cores, cls, info, stream, f16, packed, M);
-    const dim3 grid((unsigned)g.blocks, (unsigned)g.splits);
-    if (rc == FHD_OK && matrix_cores)
-        rc = f16 ? launch_line_instances<true>(packed, g.nchunks, g.splits, g.blocks, g.pairs, g.steps, cls, info,
-                                               table, x, y, z, part_r, part_i, N, stream)
-                 : launch_line_instances<false>(packed, g.nchunks, g.splits, g.blocks, g.pairs, g.steps, cls, info,
-                                                table, x, y, z, part_r, part_i, N, stream);
+    // which launched instance splits (the others write rho themselves)
+    bool any_split = false;
+    if (rc == FHD_OK && matrix_cores) {
+        rc = f16 ? launch_line_instances<true>(g, cls, info, table, x, y, z, rho_r, rho_i, part_r, part_i, N,
+                                               packed, stream)
+                 : launch_line_instances<false>(g, cls, info, table, x, y, z, rho_r, rho_i, part_r, part_i, N,
+                                                packed, stream);
+        any_split = ((int64_t)N >= 2 * (int64_t)kUnitVox && g.s_long > 1) || (N >= kUnitVox && g.s_lines > 1);
+    }
+    const dim3 grid((unsigned)g.blocks, (unsigned)g.s_vec);
+    float *vec_r = g.s_vec > 1 ? part_r : rho_r, *vec_i = g.s_vec > 1 ? part_i : rho_i;
+    any_split = any_split || g.s_vec > 1;
     // the one-step ramp class also needs a whole unit
     if (rc == FHD_OK && N >= kUnitVox) {
         TimedLaunch timed("fhd_gather_kernel<16, true>", stream);
-        fhd_gather_kernel<kVox, true><<<grid, dim3(kBlock), 0, stream>>>(packed, g.nchunks, g.splits, cls, x, y,
-                                                                          z, part_r, part_i, N);
+        fhd_gather_kernel<kVox, true><<<grid, dim3(kBlock), 0, stream>>>(packed, g.nchunks, g.s_vec, cls, x, y, z,
+                                                                          vec_r, vec_i, N);
         rc = launch_status("fhd_gather_kernel<one step> launch");
     }
     if (rc == FHD_OK) {
         TimedLaunch timed("fhd_gather_kernel<16, false>", stream);
-        fhd_gather_kernel<kVox, false><<<grid, dim3(kBlock), 0, stream>>>(packed, g.nchunks, g.splits, cls, x,
-                                                                           y, z, part_r, part_i, N);
+        fhd_gather_kernel<kVox, false><<<grid, dim3(kBlock), 0, stream>>>(packed, g.nchunks, g.s_vec, cls, x, y,
+                                                                           z, vec_r, vec_i, N);
         rc = launch_status("fhd_gather_kernel launch");
     }
-    if (g.splits > 1 && rc == FHD_OK) rc = launch_reduce(part_r, part_i, g.splits, N, rho_r, rho_i, stream);
+    if (rc == FHD_OK && any_split) {
+        fhd_reduce_units_kernel<<<dim3((unsigned)(((int64_t)N + 255) / 256)), dim3(256), 0, stream>>>(
+            part_r, part_i, cls, g.s_vec, g.s_lines, g.s_long, N, rho_r, rho_i);
+        rc = launch_status("fhd_reduce_units_kernel launch");
+    }
     return rc;
 }
 
@@ -1279,17 +1386,12 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
 {
     if (N == 0) return FHD_OK;
     const GatherPlan g = plan_gather(M, N, paths, true);
+    StreamBuffer buf(stream, kSlotGather);
     char *work = nullptr;
-    const hipError_t e = hipMallocAsync((void **)&work, g.work_bytes(), stream);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (gather workspace): ") + hipGetErrorString(e));
-    }
-    int rc = run_gather(g, work, packed, M, x, y, z, rho_r, rho_i, N, stream);
-    const hipError_t f = hipFreeAsync(work, stream);
-    if (f != hipSuccess && rc == FHD_OK)
-        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
-    return rc;
+    int rc = buf.get(g.work_bytes(), &work);
+    if (rc == FHD_OK) rc = run_gather(g, work, packed, M, x, y, z, rho_r, rho_i, N, stream);
+    const int f = buf.finish();
+    return rc != FHD_OK ? rc : f;
 }
 
 int adjoint_gather_vox_per_lane() { return kVox; }
@@ -1378,22 +1480,14 @@ extern "C" int fhd_compute_paths(const float *kx, const float *ky, const float *
     if (rc != FHD_OK) return rc;
 
     hipStream_t s = (hipStream_t)stream;
-    float *packed = nullptr;
-    if (M > 0) {
-        const hipError_t e = hipMallocAsync((void **)&packed, (size_t)packed_bytes_for(M), s);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
-        }
-        rc = launch_pack(kx, ky, kz, Dr, Di, M, packed, s);
-    }
+    StreamBuffer buf(s, kSlotPacked);
+    char *mem = nullptr;
+    rc = buf.get(M > 0 ? (size_t)packed_bytes_for(M) : 0, &mem);
+    float *packed = reinterpret_cast<float *>(mem);
+    if (rc == FHD_OK && M > 0) rc = launch_pack(kx, ky, kz, Dr, Di, M, packed, s);
     if (rc == FHD_OK) rc = launch_gather(packed, M, x, y, z, rho_r, rho_i, N, s, paths);
-    if (packed) {
-        const hipError_t e = hipFreeAsync(packed, s);
-        if (e != hipSuccess && rc == FHD_OK)
-            rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
-    }
-    return rc;
+    const int f = buf.finish();
+    return rc != FHD_OK ? rc : f;
 }
 
 extern "C" int fhd_compute(const float *kx, const float *ky, const float *kz, const float *Dr,

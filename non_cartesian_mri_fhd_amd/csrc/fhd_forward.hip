@@ -677,26 +677,21 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
         }
         return launch_status("fhd_forward_gather_kernel launch");
     }
-    float *part = nullptr;
-    const hipError_t e = hipMallocAsync((void **)&part, (size_t)splits * 2 * M * sizeof(float), stream);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (split partials): ") +
-                                       hipGetErrorString(e));
-    }
-    float *part_r = part, *part_i = part + (int64_t)splits * M;
+    StreamBuffer buf(stream, kSlotForwardPart);
+    char *mem = nullptr;
+    int rc = buf.get((size_t)splits * 2 * M * sizeof(float), &mem);
+    if (rc != FHD_OK) return rc;
+    float *part_r = reinterpret_cast<float *>(mem), *part_i = part_r + (int64_t)splits * M;
     {
         TimedLaunch timed("fhd_forward_gather_kernel<2>", stream);
         fhd_forward_gather_kernel<kSamp>
             <<<dim3((unsigned)blocks, (unsigned)splits), dim3(kBlock), 0, stream>>>(
                 packed, nchunks, splits, kx, ky, kz, part_r, part_i, M, gate);
     }
-    int rc = launch_status("fhd_forward_gather_kernel launch");
+    rc = launch_status("fhd_forward_gather_kernel launch");
     if (rc == FHD_OK) rc = launch_reduce(part_r, part_i, splits, M, Dr, Di, stream, gate, false);
-    const hipError_t f = hipFreeAsync(part, stream);
-    if (f != hipSuccess && rc == FHD_OK)
-        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
-    return rc;
+    const int f = buf.finish();
+    return rc != FHD_OK ? rc : f;
 }
 
 
@@ -751,12 +746,10 @@ int launch_forward(const float *x, const float *y, const float *z, const float *
     const size_t cls_bytes = ((size_t)units * sizeof(int) + kInfoWords * sizeof(int) + 255) / 256 * 256;
     const size_t tile_bytes = (size_t)ntiles * kFwdTileVec4 * sizeof(u32x4);
     const size_t part_bytes = splits > 1 ? (size_t)splits * 2 * M * sizeof(float) : 0;
+    StreamBuffer buf(stream, kSlotForward);
     char *work = nullptr;
-    const hipError_t e = hipMallocAsync((void **)&work, cls_bytes + tile_bytes + part_bytes, stream);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync (forward workspace): ") + hipGetErrorString(e));
-    }
+    int rc = buf.get(cls_bytes + tile_bytes + part_bytes, &work);
+    if (rc != FHD_OK) return rc;
     int *cls = reinterpret_cast<int *>(work), *info = cls + units;
     u32x4 *tiles = reinterpret_cast<u32x4 *>(work + cls_bytes);
     float *part_r = Dr, *part_i = Di;
@@ -764,7 +757,7 @@ int launch_forward(const float *x, const float *y, const float *z, const float *
         part_r = reinterpret_cast<float *>(work + cls_bytes + tile_bytes);
         part_i = part_r + (int64_t)splits * M;
     }
-    int rc = launch_classify(x, y, z, N, true, cls, info, stream);
+    rc = launch_classify(x, y, z, N, true, cls, info, stream);
     if (rc == FHD_OK)
         rc = paths == FHD_GATHER_BF16X3
                  ? launch_forward_lines<false>(x, y, z, rho_r, rho_i, cls, info, tiles, ntiles, blocks, splits, kx,
@@ -775,10 +768,8 @@ int launch_forward(const float *x, const float *y, const float *z, const float *
     // the vector form, which stands aside when the line form ran
     if (rc == FHD_OK) rc = launch_forward_pack(x, y, z, rho_r, rho_i, N, vox, stream, info);
     if (rc == FHD_OK) rc = launch_forward_gather(vox, N, kx, ky, kz, Dr, Di, M, stream, info);
-    const hipError_t f = hipFreeAsync(work, stream);
-    if (f != hipSuccess && rc == FHD_OK)
-        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
-    return rc;
+    const int f = buf.finish();
+    return rc != FHD_OK ? rc : f;
 }
 
 }  // namespace fhd
@@ -847,21 +838,14 @@ extern "C" int fhd_forward_paths(const float *kx, const float *ky, const float *
     if (rc != FHD_OK) return rc;
 
     hipStream_t s = (hipStream_t)stream;
-    float *packed = nullptr;
-    if (N > 0) {
-        const hipError_t e = hipMallocAsync((void **)&packed, (size_t)packed_bytes_for(N), s);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
-        }
-    }
-    if (rc == FHD_OK) rc = launch_forward(x, y, z, rho_r, rho_i, N, kx, ky, kz, Dr, Di, M, packed, s, paths);
-    if (packed) {
-        const hipError_t e = hipFreeAsync(packed, s);
-        if (e != hipSuccess && rc == FHD_OK)
-            rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
-    }
-    return rc;
+    StreamBuffer buf(s, kSlotForwardPacked);
+    char *mem = nullptr;
+    rc = buf.get(N > 0 ? (size_t)packed_bytes_for(N) : 0, &mem);
+    if (rc == FHD_OK)
+        rc = launch_forward(x, y, z, rho_r, rho_i, N, kx, ky, kz, Dr, Di, M, reinterpret_cast<float *>(mem), s,
+                            paths);
+    const int f = buf.finish();
+    return rc != FHD_OK ? rc : f;
 }
 
 extern "C" int fhd_forward(const float *kx, const float *ky, const float *kz, const float *x,
@@ -898,21 +882,17 @@ extern "C" int fhd_normal_paths(const float *kx, const float *ky, const float *k
     // one workspace: packed voxels | packed samples | D (real, imaginary)
     const int64_t vox_bytes = packed_bytes_for(N), smp_bytes = packed_bytes_for(M);
     const int64_t d_bytes = 2 * mb;
+    StreamBuffer buf(s, kSlotNormal);
     char *ws = nullptr;
-    const hipError_t e = hipMallocAsync((void **)&ws, (size_t)(vox_bytes + smp_bytes + d_bytes), s);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(FHD_ERR_ALLOC, std::string("hipMallocAsync: ") + hipGetErrorString(e));
-    }
+    rc = buf.get((size_t)(vox_bytes + smp_bytes + d_bytes), &ws);
+    if (rc != FHD_OK) return rc;
     float *vox = (float *)ws, *smp = (float *)(ws + vox_bytes);
     float *d_r = (float *)(ws + vox_bytes + smp_bytes), *d_i = d_r + M;
     rc = launch_forward(x, y, z, p_r, p_i, N, kx, ky, kz, d_r, d_i, M, vox, s, paths);
     if (rc == FHD_OK) rc = launch_pack(kx, ky, kz, d_r, d_i, M, smp, s);
     if (rc == FHD_OK) rc = launch_gather(smp, M, x, y, z, q_r, q_i, N, s, paths);
-    const hipError_t f = hipFreeAsync(ws, s);
-    if (f != hipSuccess && rc == FHD_OK)
-        rc = fail(FHD_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(f));
-    return rc;
+    const int f = buf.finish();
+    return rc != FHD_OK ? rc : f;
 }
 
 extern "C" int fhd_normal(const float *kx, const float *ky, const float *kz, const float *x,

@@ -416,10 +416,12 @@ struct TimedLaunch {
 
 // How many parts to cut a stream of `nchunks` chunks into, for a gather
 // whose output needs `blocks` workgroups of which `per_cu` fit on a CU at
-// once: below one round, enough parts to fill it (at least one stage per
-// part); above, up to 4 parts where that evens out a partly filled last
-// round.
-int split_count(int64_t blocks, int nchunks, int per_cu = 4);
+// once: below one round, enough parts to fill it (at least `granule`
+// chunks per part); above, a few parts where that evens out a partly
+// filled last round.
+int split_count(int64_t blocks, int nchunks, int per_cu = 4, int granule = kStageChunks);
+// Compute units of the current device (cached per device); 0 on error.
+int device_cus();
 
 // out[i] = sum_{s < splits} part[s*n + i] in increasing s, for the real
 // and the imaginary parts (stream-ordered launch, no checks). With a gate,
@@ -460,9 +462,44 @@ int launch_gather(const float *packed, int M, const float *x, const float *y, co
 // bitwise the same results), and the split partial sums. run_gather
 // launches the gather into a caller's workspace of work_bytes() bytes,
 // 256-byte aligned; nothing in it needs clearing first.
+// A device buffer for one call's stream-ordered use on `stream`: the
+// stream's kept buffer for `slot` (grown when too small), or, while the
+// stream is being captured into a graph, a stream-ordered allocation that
+// finish() (or the destructor) frees. From get() to finish() the call holds
+// its stream's lock, so calls on one stream from several threads do not
+// interleave their launches.
+enum : int {
+    kSlotGather = 0,      // classes, long-line table, partial sums of F^H D
+    kSlotPacked,          // packed k-space of fhd_compute
+    kSlotForward,         // classes, line tiles, partial sums of F
+    kSlotForwardPacked,   // packed voxels of F's vector form
+    kSlotForwardPart,     // partial sums of F's vector form
+    kSlotNormal,          // packed voxels, packed samples and F p of F^H F
+    kSlots
+};
+struct WorkspaceEntry;
+class StreamBuffer {
+public:
+    StreamBuffer(hipStream_t stream, int slot);
+    ~StreamBuffer();
+    int get(size_t bytes, char **out);   // at most once per object
+    int finish();
+    StreamBuffer(const StreamBuffer &) = delete;
+    StreamBuffer &operator=(const StreamBuffer &) = delete;
+
+private:
+    hipStream_t stream_;
+    int slot_;
+    char *async_ = nullptr;
+    WorkspaceEntry *entry_ = nullptr;
+};
+
+// Each instance cuts the sample stream into its own number of splits (1:
+// it writes rho itself); `splits` partial-sum rows of N serve them all.
 struct GatherPlan {
     int paths = FHD_GATHER_ALL;
     int nchunks = 0, splits = 1;
+    int s_long = 1, s_lines = 1, s_vec = 1;
     int64_t blocks = 0, pairs = 0, steps = 0;
     size_t cls_bytes = 0, table_bytes = 0, part_bytes = 0;
     size_t work_bytes() const { return cls_bytes + table_bytes + part_bytes; }

@@ -47,6 +47,7 @@ int main(void)
     expect(fhd_compute_grid(c[0], c[1], c[2], c[3], c[4], 3, 2, 2, -1, axis, FHD_GRID_FP32, fake[8], fake[9], NULL) == FHD_ERR_INVALID_ARG, "grid size < 0");
     expect(fhd_time_kernel("fhd_gather_kernel<16, true>", NULL, 1) == FHD_ERR_INVALID_ARG, "timing hook NULL events");
     expect(fhd_time_kernel(NULL, NULL, 0) == FHD_OK && fhd_timed_launches() == 0, "timing hook disarm");
+    expect(fhd_release_workspaces() == FHD_OK, "release with nothing kept");
     for (int s = 0; s >= -4; --s) expect(strlen(fhd_status_string(s)) > 0, "status string");
     if (failures) return 1;
     printf("ABI argument checks passed under the sanitizers\n");

@@ -375,3 +375,11 @@ def test_noalloc_argument_checks(lib):
     assert lib.fhd_compute_noalloc(*fake, 4_000_000, 4096, 0, None) == FHD_ERR_INVALID_ARG
     msg = lib.fhd_last_error()
     assert b"needs" in msg and str(64 * 1024 * 1024).encode() in msg
+
+
+def test_release_workspaces_with_nothing_kept(lib):
+    """With no call made on any stream there is nothing to free: FHD_OK,
+    and no device is needed for it."""
+    lib.fhd_release_workspaces.argtypes = []
+    lib.fhd_release_workspaces.restype = ctypes.c_int
+    assert lib.fhd_release_workspaces() == FHD_OK
