@@ -146,12 +146,19 @@ def measured_traffic(kernel: str, workload: str):
     return entry["bytes_per_launch"] if h.hexdigest() == entry["sha256"] else None
 
 
-def adjoint_kernel(cls: np.ndarray, counts: np.ndarray, paths: str) -> tuple[str, float]:
+def adjoint_kernel(cls: np.ndarray, counts: np.ndarray, paths: str, quads=None) -> tuple[str, float]:
     """The F^H D kernel that takes most voxels, for unit classes as the
-    layout mirror gives them, and the fraction of voxels it takes."""
+    layout mirror gives them (and the quads the line-pair instance takes),
+    and the fraction of voxels it takes."""
     split = "false" if paths == "bf16x3" else "true"
-    names = {3: "fhd_gather_long_lines_kernel<%s>" % split, 2: "fhd_gather_lines_kernel<%s>" % split,
-             1: "fhd_gather_kernel<16, true>", 0: "fhd_gather_kernel<16, false>"}
+    names = {4: "fhd_gather_patch_kernel<%s, true>" % split, 3: "fhd_gather_long_lines_kernel<%s>" % split,
+             2: "fhd_gather_lines_kernel<%s>" % split, 1: "fhd_gather_kernel<16, true>",
+             0: "fhd_gather_kernel<16, false>"}
+    cls = np.array(cls)
+    if quads is not None and quads.size:
+        taken = np.zeros(cls.size, bool)
+        taken[:4 * quads.size] = np.repeat(quads, 4)
+        cls[taken] = 4
     total = float(np.sum(counts)) or 1.0
     share = {c: float(np.sum(counts[cls == c])) / total for c in names}
     best = max(share, key=share.get)
@@ -205,7 +212,7 @@ def roofline_for(kernel: str, terms: float, kernel_ms: float, traffic, fractions
     rate = terms / (kernel_ms * 1e-3)
     out = {"kernel": kernel, "achieved": FLOP_PER_TERM * rate / 1e12, "unit": "TFLOP/s",
            "traffic": traffic, "flop_per_term": FLOP_PER_TERM}
-    if "lines" in kernel:
+    if "lines" in kernel or "patch" in kernel:
         out.update(bound="mfma", peak=P_MFMA_F16 / 1e12,
                    executed={"flop_per_term": LINES_EXEC_FLOP_PER_TERM,
                              "tflops": LINES_EXEC_FLOP_PER_TERM * rate / 1e12,
@@ -371,7 +378,8 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
-    kernel, kernel_share = adjoint_kernel(cls, counts, args.paths)
+    lp = layout.line_pair_quads(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
+    kernel, kernel_share = adjoint_kernel(cls, counts, args.paths, lp)
     timer = binding.KernelTimer(kernel, args.steps, dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -437,7 +445,8 @@ def main(argv=None) -> int:
             continue
         gather(p)
         c2, _, n2 = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=p != "vector")
-        k2, share2 = adjoint_kernel(c2, n2, p)
+        lp2 = layout.line_pair_quads(w["x"], w["y"], w["z"], c2) if p != "vector" else None
+        k2, share2 = adjoint_kernel(c2, n2, p, lp2)
         call_ms, kms = timed_calls(lambda: gather(p), 3, stream, k2, 1, dev)
         fr2, _ = adjoint_ceiling(w, p != "vector")
         others[p] = {"dtype": path_dtype(p, fr2[0]), "fhd_gather_call": summary(call_ms),
@@ -485,7 +494,8 @@ def bench_other(args) -> int:
     split = "false" if args.paths == "bf16x3" else "true"
     f_lines = args.paths != "vector" and layout.forward_lines_form(w["x"], w["y"], w["z"])
     cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
-    adj_kernel, adj_share = adjoint_kernel(cls, counts, args.paths)
+    lp = layout.line_pair_quads(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
+    adj_kernel, adj_share = adjoint_kernel(cls, counts, args.paths, lp)
     fwd_kernel = "fhd_forward_lines_kernel<%s>" % split if f_lines else "fhd_forward_gather_kernel<2>"
     out_r = torch.empty(max(N, M), device=dev)
     out_i = torch.empty(max(N, M), device=dev)

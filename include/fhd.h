@@ -59,7 +59,11 @@ extern "C" {
  * be summed on the matrix cores: the voxels pair up about each line's
  * centre and F^H D (or F) becomes real matrix products of per-line centre
  * phasors and per-sample cos / sin factors (the same sum, evaluated in a
- * different order). Every other unit is summed on the vector ALUs in fp32.
+ * different order). Where, in four units, the lines of 128 also come two
+ * by two as one line and that line moved by one offset (the rows of a
+ * grid), F^H D pairs the voxels of each two lines about their common
+ * centre instead, with half the per-line work. Every other unit is summed
+ * on the vector ALUs in fp32.
  *
  *   FHD_GATHER_ALL    (the default of fhd_compute, fhd_gather, fhd_forward,
  *                     fhd_normal, fhd_cg) lines on the matrix cores with
@@ -437,24 +441,29 @@ void fhd_gather_config(int *voxels_per_lane, int *samples_per_chunk, int *block_
  * library, one per GPU, held from the library's first use of that GPU
  * until the process ends. The call allocates and frees nothing.
  *   - The workspace needed is about 20 bytes per sample (rounded up to 8
- *     samples), 4 bytes per 4096 voxels plus 272, and, when the voxels are
+ *     samples), 8 bytes per 4096 voxels plus 272, and, when the voxels are
  *     too few to fill the GPU in one pass over the samples, 8 bytes per
  *     voxel for each partial sum: as many as the instance that takes most
- *     of an x-fastest grid needs to fill the GPU (3 at 128^3 voxels, 24 at
+ *     of an x-fastest grid needs to fill the GPU (4 at 128^3 voxels, 32 at
  *     64^3), the other instances' within the larger of that and 48 MiB;
  *     the call computes it exactly and returns FHD_ERR_INVALID_ARG, saying
  *     how many bytes it needed, when it exceeds the array. 128^3 voxels x
- *     100,000 samples needs about 50 MiB; 256^3 x 100,000 about 2 MiB.
+ *     100,000 samples needs about 66 MiB; 256^3 x 100,000 about 3 MiB.
  *   - Every call on one GPU uses that GPU's array: calls that overlap on
  *     one GPU (on different streams, or from different threads without
  *     ordering) race and give wrong results. Calls on one stream are
  *     ordered and safe. Nothing in the array needs clearing between calls.
- *   - The long-line form builds its cos / sin factor operands inside each
- *     workgroup instead of from a per-call table (slightly slower).
+ *   - The long-line and line-pair forms build their cos / sin factor
+ *     operands inside each workgroup instead of from a per-call table
+ *     (slower), with the same arithmetic: the results equal
+ *     fhd_compute_paths' bit for bit except on grids where some quads of
+ *     line pairs differ from the first quad's step or offset, which
+ *     fhd_compute_paths sums as long lines and this entry point as line
+ *     pairs (both within the same bound).
  * Errors: FHD_ERR_INVALID_ARG (also for a workspace beyond the array),
  * FHD_ERR_HIP.
  */
-#define FHD_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+#define FHD_NOALLOC_SCRATCH_BYTES (128 * 1024 * 1024)
 int fhd_compute_noalloc(const float *kx, const float *ky, const float *kz,
                         const float *Dr, const float *Di,
                         const float *x, const float *y, const float *z,
@@ -468,8 +477,10 @@ int fhd_compute_noalloc(const float *kx, const float *ky, const float *kz,
  * events[2*i + 1] just after it, so hipEventElapsedTime(events[2*i],
  * events[2*i + 1]) is that launch's duration on the GPU. Names are the
  * kernels' as a profiler lists them, with template arguments:
- * "fhd_gather_long_lines_kernel<true>" (split fp16) or "<false>" (split
- * bf16), "fhd_gather_lines_kernel<true>"/"<false>",
+ * "fhd_gather_patch_kernel<true, true>" (line pairs, split fp16, B table)
+ * or "<false, true>" (split bf16), "<true, false>"/"<false, false>" (B
+ * formed in the workgroups), "fhd_gather_long_lines_kernel<true>" (split
+ * fp16) or "<false>" (split bf16), "fhd_gather_lines_kernel<true>"/"<false>",
  * "fhd_gather_kernel<16, true>" (one-step ramps) or "<16, false>",
  * "fhd_forward_lines_kernel<true>"/"<false>",
  * "fhd_forward_gather_kernel<2>", "fhd_grid_kernel",

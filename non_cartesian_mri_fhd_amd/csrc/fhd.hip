@@ -547,6 +547,13 @@ __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (
 // the forward operator's line pre-pass sets). Two barriers: one to publish
 // each unit's first-lane steps, one to combine the waves' votes.
 //
+// With `patches` set, the workgroup also records in patches[2 b] and
+// patches[2 b + 1] whether the pair's 64 lines, taken two by two (lines
+// 2i and 2i + 1), are all one line and that line moved by one common
+// offset d (bitwise the same difference of their first voxels' x, y and z;
+// a long pair only), with its lines' step dx and d (bits): {flag, dx, 0,
+// 0} and {d.x, d.y, d.z, 0}.
+//
 // When the grid holds kAmpSlots more workgroups than pairs, workgroup
 // pairs + s instead writes slot s (info[4 + s]) with the largest amplitude
 // (bits) of the chunks c = s kClassifyBlock + t, s kClassifyBlock + t +
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
                                                                       int *__restrict__ cls,
                                                                       int *__restrict__ info,
                                                                       const float4 *__restrict__ packed,
-                                                                      int nchunks)
+                                                                      int nchunks, int4 *__restrict__ patches)
 {
     constexpr int kWavesPerUnit = kBlock / 64;
     const int64_t pairs = (units + 1) / 2;
@@ -592,7 +599,8 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
         return;
     }
     __shared__ float wg_step[2][3];                // each unit's first lane's ramp and line steps
-    __shared__ int votes[2 * kWavesPerUnit][3];    // per wave: one step, 64-lines, 128-lines
+    __shared__ float wg_shift[3];                  // the pair's first two lines' offset
+    __shared__ int votes[2 * kWavesPerUnit][4];    // per wave: one step, 64-lines, 128-lines, shifts
     const int half = threadIdx.x / kBlock, t = threadIdx.x % kBlock;
     const int64_t u = 2 * (int64_t)blockIdx.x + half;
     const bool present = u < units;   // the grid's last pair may hold one unit
@@ -600,6 +608,12 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
     const int64_t n0 = unit + (int64_t)t * kVox;
     bool ramp = false, on64 = false, on128 = false;
     float dx = 0.0f, d64 = 0.0f, d128 = 0.0f;
+    // this lane's line pair (lines 2i and 2i + 1 of kLongLineVox voxels:
+    // the lanes from a_lead and from a_lead + 8 of the wave): the offset of
+    // the second's first voxel from the first's
+    constexpr int kLineLanes = kLongLineVox / kVox;
+    static_assert(kLineLanes == 8 && 64 % (2 * kLineLanes) == 0, "a wave holds whole line pairs");
+    float sx = 0.0f, sy = 0.0f, sz = 0.0f;
     if (present) {   // uniform over each wave
         float px[kVox], py[kVox], pz[kVox];
         load_lane_voxels<kVox, true>(x, y, z, N, n0, px, py, pz);
@@ -608,32 +622,47 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
         const bool whole = unit + kUnitVox <= N;
         on64 = whole && lane_on_line<kLineVox, kVox>(px, py, pz, &d64);
         on128 = whole && lane_on_line<kLongLineVox, kVox>(px, py, pz, &d128);
+        const int a_lead = (threadIdx.x & 63) & ~(2 * kLineLanes - 1);
+        sx = __shfl(px[0], a_lead + kLineLanes) - __shfl(px[0], a_lead);
+        sy = __shfl(py[0], a_lead + kLineLanes) - __shfl(py[0], a_lead);
+        sz = __shfl(pz[0], a_lead + kLineLanes) - __shfl(pz[0], a_lead);
         if (t == 0) {
             wg_step[half][0] = dx;
             wg_step[half][1] = d64;
             wg_step[half][2] = d128;
+            if (half == 0) {
+                wg_shift[0] = sx;
+                wg_shift[1] = sy;
+                wg_shift[2] = sz;
+            }
         }
     }
     __syncthreads();
     const bool one = ramp && __float_as_uint(dx) == __float_as_uint(wg_step[half][0]);
     const bool l64 = on64 && __float_as_uint(d64) == __float_as_uint(wg_step[half][1]);
     const bool l128 = on128 && __float_as_uint(d128) == __float_as_uint(wg_step[half][2]);
+    const bool shifted = l128 && __builtin_isfinite(sx) && __builtin_isfinite(sy) && __builtin_isfinite(sz) &&
+                         __float_as_uint(sx) == __float_as_uint(wg_shift[0]) &&
+                         __float_as_uint(sy) == __float_as_uint(wg_shift[1]) &&
+                         __float_as_uint(sz) == __float_as_uint(wg_shift[2]);
     const int wave = threadIdx.x / 64;
-    const bool all_one = __all(one), all64 = __all(l64), all128 = __all(l128);
+    const bool all_one = __all(one), all64 = __all(l64), all128 = __all(l128), all_shift = __all(shifted);
     if ((threadIdx.x & 63) == 0) {
         votes[wave][0] = all_one;
         votes[wave][1] = all64;
         votes[wave][2] = all128;
+        votes[wave][3] = all_shift;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int c[2], lng[2];
+        int c[2], lng[2], shf = 1;
         for (int k = 0; k < 2; ++k) {
-            int v[3] = {1, 1, 1};
+            int v[4] = {1, 1, 1, 1};
             for (int w = 0; w < kWavesPerUnit; ++w)
-                for (int q = 0; q < 3; ++q) v[q] &= votes[k * kWavesPerUnit + w][q];
+                for (int q = 0; q < 4; ++q) v[q] &= votes[k * kWavesPerUnit + w][q];
             c[k] = allow_lines && v[1] ? kClassLines : v[0] ? kClassOneStep : kClassGeneral;
             lng[k] = v[2];
+            shf &= v[3];
         }
         const bool has_second = 2 * (int64_t)blockIdx.x + 1 < units;
         const bool pair = allow_lines && has_second && lng[0] && lng[1] &&
@@ -644,6 +673,13 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
             info[0] = pair ? 1 : 0;
             info[1] = (int)__float_as_uint(wg_step[0][2]);
             info[2] = 0;
+        }
+        if (patches) {
+            const bool patch = pair && shf;
+            patches[2 * (int64_t)blockIdx.x] = make_int4(patch ? 1 : 0, (int)__float_as_uint(wg_step[0][2]), 0, 0);
+            patches[2 * (int64_t)blockIdx.x + 1] =
+                make_int4((int)__float_as_uint(wg_shift[0]), (int)__float_as_uint(wg_shift[1]),
+                          (int)__float_as_uint(wg_shift[2]), 0);
         }
     }
 }
@@ -893,6 +929,37 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
     }
 }
 
+// Whether quad q (units 4q .. 4q + 3) is taken by the line-pair instance:
+// both of its unit pairs are long pairs with the line-pair structure, the
+// same step and the same offset (records from the classification, two
+// int4 per unit pair).
+__device__ __forceinline__ bool patch_quad(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                           int64_t units, int64_t q)
+{
+    if (patches == nullptr || 4 * q + 3 >= units) return false;
+    if (cls[4 * q] != kClassLongPair || cls[4 * q + 2] != kClassLongPair) return false;
+    const int4 a0 = patches[4 * q], a1 = patches[4 * q + 1], b0 = patches[4 * q + 2], b1 = patches[4 * q + 3];
+    return a0.x != 0 && b0.x != 0 && a0.y == b0.y && a1.x == b1.x && a1.y == b1.y && a1.z == b1.z;
+}
+
+// How the line-pair instance runs in a call: not at all, with a B table
+// formed for quad 0's step and offset (it then takes the quads that share
+// them; the long-line instance takes the other long pairs), or forming
+// each step's B operands itself (it takes every quad).
+enum : int { kPatchNone = 0, kPatchTable = 1, kPatchFormed = 2 };
+
+// Whether quad q is taken by the line-pair instance in `mode`.
+__device__ __forceinline__ bool patch_taken(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                            int64_t units, int64_t q, int mode)
+{
+    if (mode == kPatchNone || !patch_quad(cls, patches, units, q)) return false;
+    if (mode == kPatchFormed) return true;
+    if (q == 0) return true;
+    if (!patch_quad(cls, patches, units, 0)) return false;
+    const int4 r0 = patches[0], r1 = patches[1], a0 = patches[4 * q], a1 = patches[4 * q + 1];
+    return r0.y == a0.y && r1.x == a1.x && r1.y == a1.y && r1.z == a1.z;
+}
+
 // ---------------------------------------------------------------------------
 // Long lines on the matrix cores
 // ---------------------------------------------------------------------------
@@ -968,16 +1035,20 @@ __device__ __forceinline__ void long_step_b(const float (&f)[kFields][kChunk], f
 // The B operands of every product step of the sample stream, formed once per
 // call for the step of the first pair of units when that pair is of class
 // kClassLongPair (info[0] = 1, info[1] = its step's bits, as the classify
-// kernel records them): step g at table + g kLongStepVec4, chunks past the
+// kernel records them) and not taken by the line-pair instance (which then
+// most likely takes every long pair): step g at table + g kLongStepVec4,
+// chunks past the
 // stream's end as zeros. The long-line workgroups whose lines have that
 // step copy them into LDS instead of forming them (same arithmetic, same
 // bits).
 template <bool F16>
 __global__ __launch_bounds__(kLongBlock) void fhd_long_table_kernel(const float *__restrict__ packed, int nchunks,
-                                                                    const int *__restrict__ info,
+                                                                    const int *__restrict__ cls,
+                                                                    const int4 *__restrict__ patches, int64_t units,
+                                                                    int patch_mode, const int *__restrict__ info,
                                                                     float4 *__restrict__ table)
 {
-    if (info[0] == 0) return;
+    if (info[0] == 0 || patch_taken(cls, patches, units, 0, patch_mode)) return;
     const float dx = __int_as_float(info[1]);
     const int sh = F16 ? read_amp_shift(info) : 0;
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
@@ -1008,15 +1079,15 @@ __global__ __launch_bounds__(kLongBlock) void fhd_long_table_kernel(const float 
 template <bool F16>
 __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_long_lines_kernel(
     const float *__restrict__ packed, int nchunks, int splits, int pairs, const int *__restrict__ cls,
-    const int *__restrict__ info, const float4 *__restrict__ table,
-    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
-    float *__restrict__ out_r, float *__restrict__ out_i, int N)
+    const int4 *__restrict__ patches, int64_t units, int patch_mode, const int *__restrict__ info,
+    const float4 *__restrict__ table, const float *__restrict__ x, const float *__restrict__ y,
+    const float *__restrict__ z, float *__restrict__ out_r, float *__restrict__ out_i, int N)
 {
     // workgroup -> (pair, split), split-major over the XCDs (see xcd_unit)
     const int64_t unit = xcd_unit(blockIdx.x, (int64_t)pairs * splits);
     const int64_t pair = unit % pairs;
     const int split = (int)(unit / pairs);
-    if (cls[2 * pair] != kClassLongPair) return;
+    if (cls[2 * pair] != kClassLongPair || patch_taken(cls, patches, units, pair / 2, patch_mode)) return;
     // Two step buffers, each a step's B operands and its four sample
     // chunks, used alternately: while the workgroup works on one step, the
     // next step's data is copied straight into the other buffer (buffer_load
@@ -1034,8 +1105,11 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
     const int64_t first = base + (int64_t)(16 * wave + col) * kLongLineVox;
     const float x0 = x[first], dx = x[first + 1] - x0, ly = y[first], lz = z[first];
     const float xc = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x0);
-    // every line of the pair has the step dx (bitwise), so this is uniform
-    const bool use_table = table != nullptr && info[0] != 0 && __float_as_uint(dx) == (unsigned)info[1];
+    // every line of the pair has the step dx (bitwise), so this is uniform;
+    // the table exists when the first pair is a long pair outside the
+    // line-pair instance's quads
+    const bool use_table = table != nullptr && info[0] != 0 && !patch_taken(cls, patches, units, 0, patch_mode) &&
+                           __float_as_uint(dx) == (unsigned)info[1];
 
     float4v prc[kLongTiles], pic[kLongTiles], pis[kLongTiles], prs[kLongTiles];
 #pragma unroll
@@ -1157,6 +1231,253 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
         }
 }
 
+// ---------------------------------------------------------------------------
+// Line pairs on the matrix cores
+// ---------------------------------------------------------------------------
+// A quad -- two aligned long pairs of units, 16384 voxels, 128 lines of
+// kLongLineVox -- whose lines, two by two, are one line and the same line
+// moved by an offset d (lines 2i and 2i + 1; every pair of the quad with the
+// same step dx and the same d, as the classification's records say: the
+// rows of an x-fastest grid, with d one row along y, or, for rows of 256
+// voxels, the second half of the row along x). The 256 voxels of a line
+// pair sit symmetrically about
+//
+//   c = x_c(line 2i) + d / 2
+//
+// as 128 symmetric pairs: for j < 64,
+//   pair j      (tiles 0-3)  c +- o, o = (j + 1/2) dx e_x + d / 2
+//               (+: line 2i + 1's voxel 64 + j; -: line 2i's voxel 63 - j)
+//   pair 64 + j (tiles 4-7)  c +- o, o = (j + 1/2) dx e_x - d / 2
+//               (+: line 2i's voxel 64 + j; -: line 2i + 1's voxel 63 - j)
+// so the sum is the long-line form's four real products with one U element
+// per line pair instead of per line and 128 pair columns,
+//
+//   B_C[m, p] = a_m cos(2 pi k_m . o_p),  B_S[m, p] = a_m sin(2 pi k_m . o_p),
+//   k_m . o_p = kx_m (2j + 1) dx / 2 +- k_m . d / 2,
+//
+// twice the matrix-core work per U element: the vector work per term (the
+// U elements' phases, transcendentals and splits) is half the long-line
+// form's, while the matrix cores run the same 12 FLOP per term.
+//
+// Four waves of 16 line pairs (waves 0 and 1 the quad's first unit pair,
+// waves 2 and 3 its second), each with all 8 tiles of 16 pair columns: 96
+// products of 16 x 16 x 32 per 32 samples. The B operands of a step are
+// 32 KB (formed once per call into a table, or by the workgroup itself),
+// double buffered with the step's four sample chunks: 66.8 KB of LDS, two
+// workgroups (8 waves) per CU.
+constexpr int kQuadVox = 2 * kPairVox;              // voxels per workgroup
+constexpr int kPatchPairs = 2 * kLongPairs;         // 128 pair columns
+constexpr int kPatchTiles = kPatchPairs / 16;       // 8
+constexpr int kPatchBlock = 256;                    // 4 waves of 16 line pairs
+static_assert(kQuadVox == 2 * kLongLineVox * 16 * (kPatchBlock / 64), "a wave takes 16 line pairs");
+static_assert(kPatchTiles == 8 && kPatchBlock / 64 == 4, "each wave forms 4 tiles of B_C or B_S");
+
+// B operands of one step: [B_C hi, B_C lo, B_S hi, B_S lo][tile][k
+// quarter][column in tile], one lane's 8 fp16 or bf16 each. 32 KB.
+constexpr int kPatchStepVec4 = 4 * kPatchTiles * 4 * 16;
+typedef u32x4 PatchStepB[4][kPatchTiles][4][16];
+struct PatchStep {
+    PatchStepB b;
+    float4 chunks[kLongStepChunkVec4];
+};
+
+// Lane (wave w, lane l) of a step's B: B_C (w < 2) or B_S (w >= 2, as a
+// cosine a quarter turn later) of pair tiles 4 (w % 2) .. 4 (w % 2) + 3,
+// column l % 16 of each, samples 8 (l / 16) .. + 7 (f: their chunk; dx and
+// d: the quad's step and offset; sh: the amplitudes' scaling in the fp16
+// form), split and stored at their place in `dst`.
+template <bool F16>
+__device__ __forceinline__ void patch_step_b(const float (&f)[kFields][kChunk], float dx, float ddx, float ddy,
+                                             float ddz, int wave, int quarter_k, int col, int sh, PatchStepB &dst)
+{
+    const int part = wave >> 1, side = wave & 1, t0 = 4 * side;
+    const float turn = part == 0 ? 0.0f : -0.25f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int j = 16 * tt + col;
+        const float tj = (float)(2 * j + 1) * (0.5f * dx);
+        float b[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const float hd = 0.5f * __builtin_fmaf(f[0][i], ddx, __builtin_fmaf(f[1][i], ddy, f[2][i] * ddz));
+            const float amp = scale_amp<F16>(f[4][i], sh);
+            b[i] = amp * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj, (side == 0 ? hd : -hd) + turn));
+        }
+        unsigned h[4], l[4];
+        split_parts<F16, kChunk>(b, h, l);
+        dst[2 * part + 0][t0 + tt][quarter_k][col] = (u32x4){h[0], h[1], h[2], h[3]};
+        dst[2 * part + 1][t0 + tt][quarter_k][col] = (u32x4){l[0], l[1], l[2], l[3]};
+    }
+}
+
+// The B operands of every step of the sample stream for quad 0's step and
+// offset, formed once per call when quad 0 is taken by the line-pair
+// instance: step g at table + g kPatchStepVec4, chunks past the stream's end
+// as zeros. Quads with that step and offset copy them into LDS instead of
+// forming them (same arithmetic, same bits).
+template <bool F16>
+__global__ __launch_bounds__(kPatchBlock) void fhd_patch_table_kernel(const float *__restrict__ packed, int nchunks,
+                                                                      const int *__restrict__ cls,
+                                                                      const int4 *__restrict__ patches,
+                                                                      int64_t units, const int *__restrict__ info,
+                                                                      float4 *__restrict__ table)
+{
+    if (!patch_quad(cls, patches, units, 0)) return;
+    const float dx = __int_as_float(patches[0].y);
+    const int4 d = patches[1];
+    const int sh = F16 ? read_amp_shift(info) : 0;
+    const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t chunk = (int64_t)blockIdx.x * kLongGroup + quarter_k;
+    float f[kFields][kChunk];
+    if (chunk < nchunks) {
+        load_chunk(reinterpret_cast<const float4 *>(packed) + chunk * kChunkVec4, f);
+    } else {
+#pragma unroll
+        for (int q = 0; q < kFields; ++q)
+#pragma unroll
+            for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
+    }
+    patch_step_b<F16>(f, dx, __int_as_float(d.x), __int_as_float(d.y), __int_as_float(d.z), wave, quarter_k, col, sh,
+                      *reinterpret_cast<PatchStepB *>(table + (int64_t)blockIdx.x * kPatchStepVec4));
+}
+
+// TABLE: the B operands come from the table (mode kPatchTable, the quads
+// that share quad 0's step and offset); else the workgroup forms them
+// (mode kPatchFormed, every quad; two separate instances, so the table
+// form's register allocation does not carry the forming code's).
+template <bool F16, bool TABLE>
+__global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(2))) void fhd_gather_patch_kernel(
+    const float *__restrict__ packed, int nchunks, int splits, int64_t quads, int64_t units,
+    const int *__restrict__ cls, const int4 *__restrict__ patches, const int *__restrict__ info,
+    const float4 *__restrict__ table, const float *__restrict__ x, const float *__restrict__ y,
+    const float *__restrict__ z, float *__restrict__ out_r, float *__restrict__ out_i, int N)
+{
+    // workgroup -> (quad, split), split-major over the XCDs (see xcd_unit)
+    const int64_t unit = xcd_unit(blockIdx.x, quads * splits);
+    const int64_t quad = unit % quads;
+    const int split = (int)(unit / quads);
+    if (!patch_taken(cls, patches, units, quad, TABLE ? kPatchTable : kPatchFormed)) return;
+    // two step buffers used alternately, as in the long-line instance
+    __shared__ PatchStep buf0, buf1;
+    const float4 *src = reinterpret_cast<const float4 *>(packed);
+    const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sh = F16 ? read_amp_shift(info) : 0;
+    const float dx = __int_as_float(patches[4 * quad].y);
+    const int4 dbits = patches[4 * quad + 1];
+    const float ddx = __int_as_float(dbits.x), ddy = __int_as_float(dbits.y), ddz = __int_as_float(dbits.z);
+
+    // line pair 16 wave + col of the quad: lines 2 lp and 2 lp + 1
+    const int64_t base = quad * kQuadVox;
+    const int64_t first = base + (int64_t)(2 * (16 * wave + col)) * kLongLineVox;
+    const float x0 = x[first], ly = y[first], lz = z[first];
+    const float cx = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x0) + 0.5f * ddx;
+    const float cy = ly + 0.5f * ddy, cz = lz + 0.5f * ddz;
+
+    float4v prc[kPatchTiles], pic[kPatchTiles], pis[kPatchTiles], prs[kPatchTiles];
+#pragma unroll
+    for (int t = 0; t < kPatchTiles; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            prc[t][r] = 0.0f;
+            pic[t][r] = 0.0f;
+            pis[t][r] = 0.0f;
+            prs[t][r] = 0.0f;
+        }
+
+    int c0, c1;
+    split_range<kLinesStageChunks>(nchunks, splits, split, &c0, &c1);
+    const int nch = c1 > c0 ? c1 - c0 : 0;
+    src += (int64_t)c0 * kChunkVec4;
+    const int64_t total_vec4 = (int64_t)nch * kChunkVec4;
+    const int nsteps = (nch + kLongGroup - 1) / kLongGroup;
+    const int64_t table_vec4 = (((int64_t)nchunks + kLongGroup - 1) / kLongGroup) * kPatchStepVec4;
+    const int g0 = c0 / kLongGroup;
+
+    auto copy_step = [&](int i, PatchStep &dst, auto from_table) __attribute__((always_inline)) {
+        issue_stage_load<kPatchBlock, kLongStepChunkVec4>(src, total_vec4, i, dst.chunks);
+        if constexpr (decltype(from_table)::value)
+            issue_stage_load<kPatchBlock, kPatchStepVec4>(table, table_vec4, g0 + i,
+                                                           reinterpret_cast<float4 *>(&dst.b));
+    };
+
+    // step i in `cur` (see the long-line instance's step for the order of
+    // waits, barriers and copies)
+    auto step = [&](int i, PatchStep &cur, PatchStep &next, auto from_table) __attribute__((always_inline)) {
+        constexpr bool kTable = decltype(from_table)::value;
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        if (i + 1 < nsteps) copy_step(i + 1, next, from_table);
+        float f[kFields][kChunk];
+        load_chunk(cur.chunks + quarter_k * kChunkVec4, f);
+        if constexpr (!kTable) {
+            patch_step_b<F16>(f, dx, ddx, ddy, ddz, wave, quarter_k, col, sh, cur.b);
+            lds_barrier();
+        }
+        float ur[kChunk], ui[kChunk];
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k) {
+            const float p = __builtin_fmaf(f[0][k], cx, __builtin_fmaf(f[1][k], cy, __builtin_fmaf(f[2][k], cz, f[3][k])));
+            ur[k] = __builtin_amdgcn_cosf(p);
+            ui[k] = __builtin_amdgcn_sinf(p);
+        }
+        unsigned wa[4][4];
+        split_parts<F16, kChunk>(ur, wa[0], wa[1]);
+        split_parts<F16, kChunk>(ui, wa[2], wa[3]);
+        const u32x4 arh = {wa[0][0], wa[0][1], wa[0][2], wa[0][3]}, arl = {wa[1][0], wa[1][1], wa[1][2], wa[1][3]};
+        const u32x4 aih = {wa[2][0], wa[2][1], wa[2][2], wa[2][3]}, ail = {wa[3][0], wa[3][1], wa[3][2], wa[3][3]};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t = 0; t < kPatchTiles; ++t) {
+            const u32x4 bch = cur.b[0][t][quarter_k][col], bcl = cur.b[1][t][quarter_k][col];
+            const u32x4 bsh = cur.b[2][t][quarter_k][col], bsl = cur.b[3][t][quarter_k][col];
+            prc[t] = mfma16<F16>(arh, bch, prc[t]);
+            pic[t] = mfma16<F16>(aih, bch, pic[t]);
+            pis[t] = mfma16<F16>(aih, bsh, pis[t]);
+            prs[t] = mfma16<F16>(arh, bsh, prs[t]);
+            prc[t] = mfma16<F16>(arh, bcl, prc[t]);
+            pic[t] = mfma16<F16>(aih, bcl, pic[t]);
+            pis[t] = mfma16<F16>(aih, bsl, pis[t]);
+            prs[t] = mfma16<F16>(arh, bsl, prs[t]);
+            prc[t] = mfma16<F16>(arl, bch, prc[t]);
+            pic[t] = mfma16<F16>(ail, bch, pic[t]);
+            pis[t] = mfma16<F16>(ail, bsh, pis[t]);
+            prs[t] = mfma16<F16>(arl, bsh, prs[t]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    auto walk = [&](auto from_table) __attribute__((always_inline)) {
+        if (nsteps > 0) copy_step(0, buf0, from_table);
+        int i = 0;
+        for (; i + 1 < nsteps; i += 2) {
+            step(i, buf0, buf1, from_table);
+            step(i + 1, buf1, buf0, from_table);
+        }
+        if (i < nsteps) step(i, buf0, buf1, from_table);
+    };
+    walk(std::integral_constant<bool, TABLE>{});
+
+    // unfold: row 4 (l / 16) + r of the wave's 16 line pairs, pair column
+    // 16 t + l % 16 (side t / 4, j = 16 (t % 4) + l % 16)
+    float *dst_r = out_r + (int64_t)split * N, *dst_i = out_i + (int64_t)split * N;
+#pragma unroll
+    for (int t = 0; t < kPatchTiles; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t line_a = base + (int64_t)(2 * (16 * wave + 4 * quarter_k + r)) * kLongLineVox;
+            const int64_t line_b = line_a + kLongLineVox;
+            const int j = 16 * (t % 4) + col;
+            const int64_t plus = (t < 4 ? line_b : line_a) + kLongPairs + j;
+            const int64_t minus = (t < 4 ? line_a : line_b) + kLongPairs - 1 - j;
+            dst_r[plus] = unscale<F16>(prc[t][r] - pis[t][r], sh);
+            dst_i[plus] = unscale<F16>(pic[t][r] + prs[t][r], sh);
+            dst_r[minus] = unscale<F16>(prc[t][r] + pis[t][r], sh);
+            dst_i[minus] = unscale<F16>(pic[t][r] - prs[t][r], sh);
+        }
+}
+
 }  // namespace
 
 // Launches without argument checks; callers have checked.
@@ -1188,40 +1509,68 @@ int blocks_per_cu(const void *kernel, int block)
 }
 
 int launch_classify(const float *x, const float *y, const float *z, int N, bool allow_lines, int *cls,
-                    int *info, hipStream_t stream, bool amp_slots, const float *packed, int M)
+                    int *info, hipStream_t stream, bool amp_slots, const float *packed, int M, int4 *patches)
 {
     const int64_t blocks = ((int64_t)N + kUnitVox - 1) / kUnitVox;
     const int64_t pairs = (blocks + 1) / 2;
     const int nchunks = amp_slots && M > 0 ? (int)(((int64_t)M + kChunk - 1) / kChunk) : 0;
     const int64_t grid = pairs + (amp_slots ? kAmpSlots : 0);
     fhd_classify_kernel<<<dim3((unsigned)grid), dim3(kClassifyBlock), 0, stream>>>(
-        x, y, z, N, blocks, allow_lines ? 1 : 0, cls, info, reinterpret_cast<const float4 *>(packed), nchunks);
+        x, y, z, N, blocks, allow_lines ? 1 : 0, cls, info, reinterpret_cast<const float4 *>(packed), nchunks,
+        patches);
     return launch_status("fhd_classify_kernel launch");
 }
 
 // The matrix-core instances of one split type (F16: fp16 parts, the
 // default; else bf16 parts). Each writes rho itself when its split count
-// is 1, else its partial sums.
+// is 1, else its partial sums. The line-pair and long-line instances share
+// one split count (both take units of class kClassLongPair).
 template <bool F16>
-int launch_line_instances(const GatherPlan &g, const int *cls, const int *info, float4 *table, const float *x,
-                          const float *y, const float *z, float *rho_r, float *rho_i, float *part_r,
-                          float *part_i, int N, const float *packed, hipStream_t stream)
+int launch_line_instances(const GatherPlan &g, const int *cls, const int4 *patches, const int *info,
+                          float4 *long_table, float4 *patch_table, const float *x, const float *y, const float *z,
+                          float *rho_r, float *rho_i, float *part_r, float *part_i, int N, const float *packed,
+                          hipStream_t stream)
 {
     int rc = FHD_OK;
-    // a class needs whole units: with fewer than two (one) whole units no
-    // unit can take the long-line (line) instance, which is not launched
-    const bool long_pairs = (int64_t)N >= 2 * (int64_t)kUnitVox, whole_unit = N >= kUnitVox;
-    if (long_pairs && g.steps > 0) {
-        fhd_long_table_kernel<F16><<<dim3((unsigned)g.steps), dim3(kLongBlock), 0, stream>>>(packed, g.nchunks,
-                                                                                             info, table);
+    // a class needs whole units: with fewer than four (two, one) whole
+    // units no unit can take the line-pair (long-line, line) instance,
+    // which is not launched
+    const bool quads = g.quads > 0, long_pairs = (int64_t)N >= 2 * (int64_t)kUnitVox, whole_unit = N >= kUnitVox;
+    const bool direct_long = g.s_long == 1;
+    if (quads && patch_table) {
+        fhd_patch_table_kernel<F16><<<dim3((unsigned)g.steps), dim3(kPatchBlock), 0, stream>>>(
+            packed, g.nchunks, cls, patches, g.blocks, info, patch_table);
+        rc = launch_status("fhd_patch_table_kernel launch");
+    }
+    const int mode = !quads ? kPatchNone : patch_table ? kPatchTable : kPatchFormed;
+    if (rc == FHD_OK && quads) {
+        const dim3 grid((unsigned)(g.quads * g.s_long));
+        float *out_r = direct_long ? rho_r : part_r, *out_i = direct_long ? rho_i : part_i;
+        if (mode == kPatchTable) {
+            TimedLaunch timed(F16 ? "fhd_gather_patch_kernel<true, true>" : "fhd_gather_patch_kernel<false, true>",
+                              stream);
+            fhd_gather_patch_kernel<F16, true><<<grid, dim3(kPatchBlock), 0, stream>>>(
+                packed, g.nchunks, g.s_long, g.quads, g.blocks, cls, patches, info, patch_table, x, y, z, out_r,
+                out_i, N);
+        } else {
+            TimedLaunch timed(F16 ? "fhd_gather_patch_kernel<true, false>" : "fhd_gather_patch_kernel<false, false>",
+                              stream);
+            fhd_gather_patch_kernel<F16, false><<<grid, dim3(kPatchBlock), 0, stream>>>(
+                packed, g.nchunks, g.s_long, g.quads, g.blocks, cls, patches, info, nullptr, x, y, z, out_r, out_i,
+                N);
+        }
+        rc = launch_status("fhd_gather_patch_kernel launch");
+    }
+    if (rc == FHD_OK && long_pairs && long_table) {
+        fhd_long_table_kernel<F16><<<dim3((unsigned)g.steps), dim3(kLongBlock), 0, stream>>>(
+            packed, g.nchunks, cls, patches, g.blocks, mode, info, long_table);
         rc = launch_status("fhd_long_table_kernel launch");
     }
     if (rc == FHD_OK && long_pairs) {
-        const bool direct = g.s_long == 1;
         TimedLaunch timed(F16 ? "fhd_gather_long_lines_kernel<true>" : "fhd_gather_long_lines_kernel<false>", stream);
         fhd_gather_long_lines_kernel<F16><<<dim3((unsigned)(g.pairs * g.s_long)), dim3(kLongBlock), 0, stream>>>(
-            packed, g.nchunks, g.s_long, (int)g.pairs, cls, info, table, x, y, z, direct ? rho_r : part_r,
-            direct ? rho_i : part_i, N);
+            packed, g.nchunks, g.s_long, (int)g.pairs, cls, patches, g.blocks, mode, info, long_table, x, y, z,
+            direct_long ? rho_r : part_r, direct_long ? rho_i : part_i, N);
         rc = launch_status("fhd_gather_long_lines_kernel launch");
     }
     if (rc == FHD_OK && whole_unit) {
@@ -1294,7 +1643,16 @@ GatherPlan plan_gather(int M, int N, int paths, bool with_table)
     const bool matrix_cores = paths != FHD_GATHER_VECTOR;
     const bool long_pairs = matrix_cores && (int64_t)N >= 2 * (int64_t)kUnitVox;
     const bool whole_unit = matrix_cores && N >= kUnitVox;
-    if (long_pairs)
+    g.quads = matrix_cores ? (int64_t)N / kQuadVox : 0;   // whole quads only
+    // the long pairs' split count: sized for the line-pair instance where
+    // quads can exist (on grids it takes every long pair), else for the
+    // long-line one
+    if (g.quads > 0)
+        g.s_long = split_count(g.quads, g.nchunks,
+                               blocks_per_cu<4>(reinterpret_cast<const void *>(fhd_gather_patch_kernel<true, true>),
+                                                kPatchBlock),
+                               kLinesStageChunks);
+    else if (long_pairs)
         g.s_long = split_count(g.pairs, g.nchunks,
                                blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel<true>),
                                                 kLongBlock),
@@ -1322,12 +1680,15 @@ GatherPlan plan_gather(int M, int N, int paths, bool with_table)
     g.splits = g.s_vec;
     if (g.s_long > g.splits) g.splits = g.s_long;
     if (g.s_lines > g.splits) g.splits = g.s_lines;
-    // the workspace: the unit classes and the info words, the B table of
-    // the long-line instance (16 KB per 32 samples), then (splits > 1) the
-    // partial sums
-    g.cls_bytes = ((size_t)g.blocks * sizeof(int) + kInfoWords * sizeof(int) + 255) / 256 * 256;
-    g.steps = M > 0 && matrix_cores && with_table ? ((int64_t)g.nchunks + kLongGroup - 1) / kLongGroup : 0;
+    // the workspace: the unit classes and the info words, the unit pairs'
+    // line-pair records (two int4 each), the B tables of the long-line
+    // (16 KB per 32 samples) and line-pair (32 KB) instances, then (splits
+    // > 1) the partial sums
+    g.patch_offset = ((size_t)g.blocks * sizeof(int) + kInfoWords * sizeof(int) + 15) / 16 * 16;
+    g.cls_bytes = (g.patch_offset + (matrix_cores ? (size_t)g.pairs * 2 * sizeof(int4) : 0) + 255) / 256 * 256;
+    g.steps = M > 0 && long_pairs && with_table ? ((int64_t)g.nchunks + kLongGroup - 1) / kLongGroup : 0;
     g.table_bytes = (size_t)g.steps * kLongStepVec4 * sizeof(float4);
+    g.patch_table_bytes = g.quads > 0 ? (size_t)g.steps * kPatchStepVec4 * sizeof(float4) : 0;
     g.part_bytes = g.splits > 1 ? (size_t)g.splits * 2 * N * sizeof(float) : 0;
     return g;
 }
@@ -1338,23 +1699,26 @@ int run_gather(const GatherPlan &g, char *work, const float *packed, int M, cons
     const bool matrix_cores = g.paths != FHD_GATHER_VECTOR;
     int *cls = reinterpret_cast<int *>(work);
     int *info = cls + g.blocks;
-    float4 *table = g.steps > 0 ? reinterpret_cast<float4 *>(work + g.cls_bytes) : nullptr;
+    int4 *patches = matrix_cores ? reinterpret_cast<int4 *>(work + g.patch_offset) : nullptr;
+    float4 *long_table = g.table_bytes > 0 ? reinterpret_cast<float4 *>(work + g.cls_bytes) : nullptr;
+    float4 *patch_table =
+        g.patch_table_bytes > 0 ? reinterpret_cast<float4 *>(work + g.cls_bytes + g.table_bytes) : nullptr;
     float *part_r = nullptr, *part_i = nullptr;
     if (g.splits > 1) {
-        part_r = reinterpret_cast<float *>(work + g.cls_bytes + g.table_bytes);
+        part_r = reinterpret_cast<float *>(work + g.cls_bytes + g.table_bytes + g.patch_table_bytes);
         part_i = part_r + (int64_t)g.splits * N;
     }
     // the fp16 products need the largest amplitude: the classification's
     // extra workgroups reduce it
     const bool f16 = g.paths == FHD_GATHER_ALL;
-    int rc = launch_classify(x, y, z, N, matrix_cores, cls, info, stream, f16, packed, M);
+    int rc = launch_classify(x, y, z, N, matrix_cores, cls, info, stream, f16, packed, M, patches);
     // which launched instance splits (the others write rho themselves)
     bool any_split = false;
     if (rc == FHD_OK && matrix_cores) {
-        rc = f16 ? launch_line_instances<true>(g, cls, info, table, x, y, z, rho_r, rho_i, part_r, part_i, N,
-                                               packed, stream)
-                 : launch_line_instances<false>(g, cls, info, table, x, y, z, rho_r, rho_i, part_r, part_i, N,
-                                                packed, stream);
+        rc = f16 ? launch_line_instances<true>(g, cls, patches, info, long_table, patch_table, x, y, z, rho_r,
+                                               rho_i, part_r, part_i, N, packed, stream)
+                 : launch_line_instances<false>(g, cls, patches, info, long_table, patch_table, x, y, z, rho_r,
+                                                rho_i, part_r, part_i, N, packed, stream);
         any_split = ((int64_t)N >= 2 * (int64_t)kUnitVox && g.s_long > 1) || (N >= kUnitVox && g.s_lines > 1);
     }
     const dim3 grid((unsigned)g.blocks, (unsigned)g.s_vec);

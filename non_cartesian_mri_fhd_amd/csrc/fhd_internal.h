@@ -445,10 +445,11 @@ __device__ __forceinline__ bool lines_form_ran(const int *info) { return info[0]
 // = 0 (stream-ordered; allow_lines = false gives no matrix-core class).
 // With amp_slots, also the amplitude slots info[4 .. 4 + kAmpSlots) of
 // the packed k-space of M samples (zeros when M = 0; info holds kInfoWords
-// words).
+// words). With patches (two int4 per unit pair), also each pair's
+// line-pair record (the line-pair instance's classification).
 int launch_classify(const float *x, const float *y, const float *z, int N, bool allow_lines, int *cls,
                     int *info, hipStream_t stream, bool amp_slots = false, const float *packed = nullptr,
-                    int M = 0);
+                    int M = 0, int4 *patches = nullptr);
 // paths: FHD_GATHER_ALL (lines on the matrix cores in split fp16, the
 // rest on the vector ALUs), FHD_GATHER_BF16X3 (the same in split bf16) or
 // FHD_GATHER_VECTOR (every unit on the vector-ALU paths). Takes its
@@ -500,9 +501,9 @@ struct GatherPlan {
     int paths = FHD_GATHER_ALL;
     int nchunks = 0, splits = 1;
     int s_long = 1, s_lines = 1, s_vec = 1;
-    int64_t blocks = 0, pairs = 0, steps = 0;
-    size_t cls_bytes = 0, table_bytes = 0, part_bytes = 0;
-    size_t work_bytes() const { return cls_bytes + table_bytes + part_bytes; }
+    int64_t blocks = 0, pairs = 0, quads = 0, steps = 0;
+    size_t patch_offset = 0, cls_bytes = 0, table_bytes = 0, patch_table_bytes = 0, part_bytes = 0;
+    size_t work_bytes() const { return cls_bytes + table_bytes + patch_table_bytes + part_bytes; }
 };
 GatherPlan plan_gather(int M, int N, int paths, bool with_table);
 int run_gather(const GatherPlan &g, char *work, const float *packed, int M, const float *x, const float *y,

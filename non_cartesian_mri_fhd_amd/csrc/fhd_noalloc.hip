@@ -2,14 +2,15 @@
 // callers that cannot allocate device memory (code under HIP graph
 // capture, tight serving loops, harnesses that forbid hipMalloc).
 //
-// Its workspace -- the packed k-space, the unit classes and info words and
-// the split partial sums -- lives in one file-scope device array, `scratch`,
-// of kScratchBytes per GPU, held from the library's first use of a GPU
-// until the process ends. The long-line instance forms its cos / sin factor
-// operands in each workgroup instead of reading a per-call table (bitwise
-// the same results), which keeps the workspace at 20 bytes per sample, 4
-// bytes per 4096 voxels and, when the voxels are too few to fill the GPU
-// in one pass, 8 bytes per voxel and partial sum.
+// Its workspace -- the packed k-space, the unit classes, info words and
+// line-pair records and the split partial sums -- lives in one file-scope
+// device array, `scratch`, of kScratchBytes per GPU, held from the
+// library's first use of a GPU until the process ends. The long-line and
+// line-pair instances form their cos / sin factor operands in each
+// workgroup instead of reading a per-call table (the same arithmetic),
+// which keeps the workspace at 20 bytes per sample, 8 bytes per 4096
+// voxels and, when the voxels are too few to fill the GPU in one pass, 8
+// bytes per voxel and partial sum.
 //
 // In host code `scratch` names a host-side stand-in, not the array's device
 // address: the address comes from hipGetSymbolAddress, once per device

@@ -100,6 +100,52 @@ def gather_unit_classes(x, y, z, block: int = 256, vox: int = 16, line: int = 64
     return cls, all_ramp, counts
 
 
+def line_pair_quads(x, y, z, cls=None, block: int = 256, vox: int = 16, long_line: int = 128,
+                    formed: bool = False):
+    """Per quad of four units (units 4q .. 4q + 3, all present), whether
+    the F^H D line-pair instance takes it, by the classify kernel's
+    line-pair record: both unit pairs of the quad of class 3, in each the
+    lines 2i + 1 the lines 2i moved by one common offset d (bitwise equal
+    fp32 differences of their first voxels' x, y, z, all finite; d from
+    the pair's lines 0 and 1), the same step and d in both pairs; and,
+    unless `formed` (the instance forming its own B operands, as in
+    fhd_compute_noalloc), quad 0 so too with the quad's step and d."""
+    x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
+    unit = block * vox
+    if cls is None:
+        cls = gather_unit_classes(x, y, z, block, vox)[0]
+    quads = x.size // (4 * unit)
+    if quads == 0:
+        return np.zeros(0, bool)
+    nl = 4 * unit // long_line                     # lines per quad
+    first = np.arange(quads * nl) * long_line      # every line's first voxel
+    fx, fy, fz = x[first], y[first], z[first]
+    step = (x[first + 1] - fx).astype(np.float32)
+    sx = (fx[1::2] - fx[0::2]).astype(np.float32)  # per line pair
+    sy = (fy[1::2] - fy[0::2]).astype(np.float32)
+    sz = (fz[1::2] - fz[0::2]).astype(np.float32)
+    lp_per_pair = nl // 4                          # line pairs per unit pair
+    P = quads * 2
+
+    def bits(a):
+        return a.view(np.uint32).reshape(P, lp_per_pair)
+
+    SX, SY, SZ = bits(sx), bits(sy), bits(sz)
+    fin = (np.isfinite(sx) & np.isfinite(sy) & np.isfinite(sz)).reshape(P, lp_per_pair)
+    shifted = (fin.all(axis=1) & np.all(SX == SX[:, :1], axis=1) & np.all(SY == SY[:, :1], axis=1)
+               & np.all(SZ == SZ[:, :1], axis=1))
+    long_pair = cls[0:4 * quads:2] == 3
+    rec_ok = long_pair & shifted
+    pstep = step.view(np.uint32).reshape(P, 2 * lp_per_pair)[:, 0]
+    key = np.stack([pstep, SX[:, 0], SY[:, 0], SZ[:, 0]], axis=1)
+    quad = rec_ok[0::2] & rec_ok[1::2] & np.all(key[0::2] == key[1::2], axis=1)
+    if formed:
+        return quad
+    if not quad[0]:
+        return np.zeros(quads, bool)
+    return quad & np.all(key[0::2] == key[0], axis=1)
+
+
 def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16,
                          allow_lines: bool = True) -> tuple[float, float, float]:
     """Fractions of voxels by the F^H D gather path their unit takes (see

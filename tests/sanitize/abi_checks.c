@@ -41,7 +41,7 @@ int main(void)
     expect(fhd_pack(c[0], c[1], c[2], c[3], c[4], 10, fake[5], 8, NULL) == FHD_ERR_INVALID_ARG, "short pack buffer");
     expect(strstr(fhd_last_error(), "packed_bytes") != NULL, "pack message");
     expect(fhd_packed_bytes(-1) == -1 && fhd_packed_bytes(9) == 2 * 160, "packed bytes");
-    expect(fhd_compute_noalloc(c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], fake[8], fake[9], 4000000, 4096, 0, NULL) == FHD_ERR_INVALID_ARG, "noalloc beyond scratch");
+    expect(fhd_compute_noalloc(c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], fake[8], fake[9], 8000000, 4096, 0, NULL) == FHD_ERR_INVALID_ARG, "noalloc beyond scratch");
     expect(strstr(fhd_last_error(), "needs") != NULL, "noalloc message");
     float axis[6] = {0.0f, 1.0f, 0.0f, 1.0f, 0.0f, 1.0f};
     expect(fhd_compute_grid(c[0], c[1], c[2], c[3], c[4], 3, 2, 2, -1, axis, FHD_GRID_FP32, fake[8], fake[9], NULL) == FHD_ERR_INVALID_ARG, "grid size < 0");

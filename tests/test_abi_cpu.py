@@ -361,9 +361,9 @@ def test_stale_library_is_rebuilt_when_a_source_is_newer(tmp_path):
 
 def test_noalloc_argument_checks(lib):
     """fhd_compute_noalloc refuses bad arguments, and a workspace beyond its
-    scratch array, before touching any device memory: four million samples
-    need 80 MB of packed k-space alone, above FHD_NOALLOC_SCRATCH_BYTES
-    (64 MiB). The pointers of that case are never dereferenced."""
+    scratch array, before touching any device memory: eight million samples
+    need 160 MB of packed k-space alone, above FHD_NOALLOC_SCRATCH_BYTES
+    (128 MiB). The pointers of that case are never dereferenced."""
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.fhd_compute_noalloc.argtypes = [vp] * 10 + [i32, i32, i32, vp]
     assert lib.fhd_compute_noalloc(*[None] * 10, -1, 5, 0, None) == FHD_ERR_INVALID_ARG
@@ -372,9 +372,9 @@ def test_noalloc_argument_checks(lib):
     assert lib.fhd_compute_noalloc(*[None] * 10, 0, 0, 0, None) == FHD_OK
     assert lib.fhd_compute_noalloc(*[None] * 10, 0, 5, 0, None) == FHD_ERR_INVALID_ARG
     fake = [0x10000000 * (i + 1) for i in range(10)]
-    assert lib.fhd_compute_noalloc(*fake, 4_000_000, 4096, 0, None) == FHD_ERR_INVALID_ARG
+    assert lib.fhd_compute_noalloc(*fake, 8_000_000, 4096, 0, None) == FHD_ERR_INVALID_ARG
     msg = lib.fhd_last_error()
-    assert b"needs" in msg and str(64 * 1024 * 1024).encode() in msg
+    assert b"needs" in msg and str(128 * 1024 * 1024).encode() in msg
 
 
 def test_release_workspaces_with_nothing_kept(lib):

@@ -1,0 +1,109 @@
+"""The line-pair matrix-core instance of F^H D, through the C ABI.
+
+Quads of four units whose lines of 128 voxels, two by two, are one line and
+the same line moved by a common offset d (rows of a grid along y, or the
+two halves of rows of 256 along x) are summed about each line pair's
+centre. Each case states which quads the instance takes (the host mirror
+of the classification, layout.line_pair_quads) and checks every voxel
+against the oracle; quads that break the structure fall back to the
+long-line instance. fhd_compute_noalloc forms the B operands itself and
+takes every quad with the structure: where both forms take the same quads
+its output is bitwise fhd_compute's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from non_cartesian_mri_fhd_amd import binding, build, inputs, layout, metrics
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    build.ensure_built()
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def grid_case(shape, M, seed, kmax=None):
+    nx, ny, nz = shape
+    x, y, z = inputs.coords_from_axis(nx, ny, nz, (-0.5, 1.0 / nx, -0.5, 1.0 / ny, -0.5, 1.0 / nz))
+    rng = np.random.default_rng(seed)
+    km = kmax if kmax is not None else min(shape) / 2.0
+    kx, ky, kz = (rng.uniform(-km, km, M).astype(np.float32) for _ in range(3))
+    Dr, Di = (rng.standard_normal(M).astype(np.float32) for _ in range(2))
+    return dict(kx=kx, ky=ky, kz=kz, Dr=Dr, Di=Di, x=x, y=y, z=z)
+
+
+def run(case, dev, paths=binding.FHD_GATHER_ALL, noalloc=False):
+    t = [torch.from_numpy(np.ascontiguousarray(case[k])).to(dev)
+         for k in ("kx", "ky", "kz", "Dr", "Di", "x", "y", "z")]
+    N = t[5].numel()
+    if noalloc:
+        rr, ri = torch.empty(N, device=dev), torch.empty(N, device=dev)
+        binding.fhd_compute_noalloc(*t, rr, ri, paths=paths)
+    else:
+        rr, ri = binding.fhd_compute(*t, paths=paths)
+    torch.cuda.synchronize(dev)
+    return rr.cpu().numpy(), ri.cpu().numpy()
+
+
+def bend_rows(case, first_line, count, amount):
+    """Moves lines first_line .. first_line + count - 1 (of 128 voxels) by
+    `amount` along y, breaking the common line-pair offset there."""
+    y = case["y"].copy()
+    for ln in range(first_line, first_line + count):
+        y[ln * 128:(ln + 1) * 128] += np.float32(amount)
+    case["y"] = y
+    return case
+
+
+def cases():
+    # one quad of rows along y; one quad of 256-voxel rows (d along x); two
+    # quads; two quads, the second bent (long lines there); the first bent
+    # (no quad in the table form, the second in the formed one)
+    yield "128x32x4", grid_case((128, 32, 4), 3001, 960), [True], [True]
+    yield "256x16x4", grid_case((256, 16, 4), 2999, 961), [True], [True]
+    yield "128x64x4", grid_case((128, 64, 4), 2048, 962), [True, True], [True, True]
+    c = bend_rows(grid_case((128, 64, 4), 2048, 963), 128 + 1, 1, 1.0 / 512)
+    yield "second quad bent", c, [True, False], [True, False]
+    c = bend_rows(grid_case((128, 64, 4), 2048, 964), 3, 1, 1.0 / 512)
+    yield "first quad bent", c, [False, False], [False, True]
+
+
+@pytest.mark.parametrize("name,case,taken,formed", list(cases()), ids=[c[0] for c in cases()])
+def test_line_pairs_match_the_oracle(dev, name, case, taken, formed):
+    cls = layout.gather_unit_classes(case["x"], case["y"], case["z"])[0]
+    assert np.all(cls == 3), (name, cls)
+    assert layout.line_pair_quads(case["x"], case["y"], case["z"], cls).tolist() == taken, name
+    assert layout.line_pair_quads(case["x"], case["y"], case["z"], cls, formed=True).tolist() == formed, name
+    ref = oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"], case["x"], case["y"], case["z"])
+    print("line pairs: %s" % name, flush=True)
+    got = run(case, dev)
+    e = metrics.rel_l2(*got, *ref)
+    vec = metrics.rel_l2(*run(case, dev, binding.FHD_GATHER_VECTOR), *ref)
+    na = run(case, dev, noalloc=True)
+    e_na = metrics.rel_l2(*na, *ref)
+    print("  rel-L2 default %.3g, vector %.3g, noalloc %.3g" % (e, vec, e_na), flush=True)
+    assert e <= TOL and e_na <= TOL and vec <= TOL
+    if taken == formed:
+        assert np.array_equal(got[0], na[0]) and np.array_equal(got[1], na[1]), name
+
+
+def test_line_pairs_split_sums_repeatable(dev):
+    """The same call twice on a grid large enough for several sample
+    splits per quad gives the same bits (fixed-order sums, no races)."""
+    case = grid_case((128, 128, 8), 20000, 965, kmax=32.0)
+    assert layout.line_pair_quads(case["x"], case["y"], case["z"]).all()
+    a = run(case, dev)
+    b = run(case, dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    idx = inputs.voxel_subset(case["x"].size, 600, seed=966)
+    ref = oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"],
+                     case["x"][idx], case["y"][idx], case["z"][idx])
+    assert metrics.rel_l2(a[0][idx], a[1][idx], *ref) <= TOL

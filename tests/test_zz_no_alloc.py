@@ -49,11 +49,11 @@ def noalloc(lib, t, paths, dev):
 
 @pytest.mark.parametrize("paths", ["all", "vector", "bf16x3"])
 def test_noalloc_matches_compute_on_calls_of_shrinking_size(lib, paths):
-    """128^3 x 100,000 (the line forms; about 50 MiB of workspace) or, on the
-    vector paths, whose five partial sums at 128^3 need more than the
-    scratch holds, 64^3 x 65,536; then smaller calls on the same scratch."""
+    """128^3 x 100,000 (about 70 MiB of workspace on the line forms, whose
+    line-pair workgroups form their B operands themselves here; 86 MB on
+    the vector paths), then smaller calls on the same scratch."""
     dev = torch.device("cuda:0")
-    first = "radial64" if paths == "vector" else "spiral128"
+    first = "spiral128"
     cases = [(first, inputs.make_workload(first)),
              ("spiral32", inputs.make_workload("spiral32")),
              ("ragged 5000 x 123", inputs.random_case(5000, 123, seed=931))]
@@ -72,16 +72,10 @@ def test_noalloc_matches_compute_on_calls_of_shrinking_size(lib, paths):
 
 
 def test_noalloc_refuses_a_workspace_beyond_its_scratch(lib):
-    """Four million samples need 80 MB of packed k-space alone, more than
-    the 64 MiB scratch: FHD_ERR_INVALID_ARG, saying what was needed. So do
-    the vector paths' five partial sums at 128^3 voxels (80 MB)."""
+    """Eight million samples need 160 MB of packed k-space alone, more than
+    the 128 MiB scratch: FHD_ERR_INVALID_ARG, saying what was needed."""
     dev = torch.device("cuda:0")
-    t = device_case(inputs.make_workload("spiral128"), dev)
-    rr, ri = (torch.empty(t[5].numel(), device=dev) for _ in range(2))
-    rc = lib.fhd_compute_noalloc(*[a.data_ptr() for a in t], rr.data_ptr(), ri.data_ptr(), t[0].numel(),
-                                 t[5].numel(), binding.FHD_GATHER_VECTOR, None)
-    assert rc == binding.FHD_ERR_INVALID_ARG and b"needs" in lib.fhd_last_error()
-    M, N = 4_000_000, 4096
+    M, N = 8_000_000, 4096
     k = torch.zeros(M, device=dev)
     v = torch.zeros(N, device=dev)
     out = [torch.empty(N, device=dev) for _ in range(2)]
@@ -89,7 +83,7 @@ def test_noalloc_refuses_a_workspace_beyond_its_scratch(lib):
                                  v.data_ptr(), v.data_ptr(), v.data_ptr(), out[0].data_ptr(), out[1].data_ptr(),
                                  M, N, binding.FHD_GATHER_ALL, None)
     assert rc == binding.FHD_ERR_INVALID_ARG
-    assert b"needs" in lib.fhd_last_error()
+    assert b"needs" in lib.fhd_last_error() and str(128 * 1024 * 1024).encode() in lib.fhd_last_error()
 
 
 def test_noalloc_empty_sizes(lib):
