@@ -119,17 +119,29 @@ PATH_DTYPE = {
     "vector": "f32",
 }
 
-# HBM bytes per launch of a kernel on spiral128, from rocprofv3 FETCH_SIZE
-# and WRITE_SIZE passes (KiB per dispatch) scaled by a 1 GiB copy's readings
-# (factors 2.0 and 1.0; copycal.py). Valid only for the sources they were
-# taken on (SHA-256 over the listed files, in order): any later edit
-# reports null until the counters are taken again.
+# HBM bytes per launch of a kernel on one workload, from rocprofv3
+# FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch, the mean of the
+# call's full launches) scaled by a 1 GiB copy's readings (factors 2.0 and
+# 1.0; copycal.py). Valid only for the sources they were taken on
+# (SHA-256 over the listed files, in order): any later edit reports null
+# until the counters are taken again.
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
+_GATHER_SRC = ["fhd.hip", "fhd_internal.h"]
+_GATHER_SHA = "b05bd53763c9b3bac95677f067709916b560d937b1fee421cd5c70fffa13cede"
 TRAFFIC = {
-    "fhd_grid_kernel": {
-        "workload": "spiral128", "sources": ["fhd_grid.hip", "fhd_internal.h"],
-        "sha256": "b1b1479f1a3565e78aa09c4f94013be3f4790b1f2dfc96d2775dd1407cc3389f",
-        "bytes_per_launch": (7881.0 * 2.0 + 49152.0 * 1.0) * 1024},
+    "fhd_gather_patch_kernel<true, true>": {
+        "workload": "spiral128", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
+        "bytes_per_launch": (108286.0 * 2.0 + 65771.0 * 1.0) * 1024},
+    "fhd_gather_kernel<16, true>": {
+        "workload": "spiral128", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
+        "bytes_per_launch": (54788.0 * 2.0 + 92160.0 * 1.0) * 1024},
+    "fhd_gather_lines_kernel<true>": {
+        "workload": "radial64", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
+        "bytes_per_launch": (5979.0 * 2.0 + 49152.0 * 1.0) * 1024},
+    "fhd_forward_lines_kernel<true>": {
+        "workload": "spiral128", "sources": ["fhd_forward.hip", "fhd_internal.h"],
+        "sha256": "180b23387c0e9b8650ba365c5376dbed83a7ab2e6d12011a9aa858a9d9722062",
+        "bytes_per_launch": (74996.0 * 2.0 + 8594.0 * 1.0) * 1024},
 }
 
 

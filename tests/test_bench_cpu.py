@@ -18,9 +18,32 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_only_for_the_profiled_workload():
-    for op in ("fhd", "grid", "forward"):
-        assert bench.measured_traffic(op, "radial64") is None
-    assert bench.measured_traffic("normal", "spiral128") is None
+    for kernel, entry in bench.TRAFFIC.items():
+        other = "vdrandom256" if entry["workload"] != "vdrandom256" else "spiral128"
+        assert bench.measured_traffic(kernel, other) is None
+    assert bench.measured_traffic("fhd_grid_kernel", "spiral128") is None
+
+
+def test_traffic_follows_the_sources(tmp_path, monkeypatch):
+    """A recorded figure holds only for the sources it was taken on."""
+    kernel, entry = next(iter(bench.TRAFFIC.items()))
+    src = tmp_path / "csrc"
+    src.mkdir()
+    for name in entry["sources"]:
+        (src / name).write_bytes(open(os.path.join(bench.CSRC, name), "rb").read())
+    monkeypatch.setattr(bench, "CSRC", str(src))
+    same = bench.measured_traffic(kernel, entry["workload"])
+    (src / entry["sources"][0]).write_bytes(b"// edited\n" + (src / entry["sources"][0]).read_bytes())
+    assert bench.measured_traffic(kernel, entry["workload"]) is None
+    if same is not None:
+        assert same == entry["bytes_per_launch"]
+
+
+def test_alu_kernels_priced_at_their_issue_ceiling():
+    r = bench.roofline_for("fhd_gather_kernel<16, true>", 1e12, 50.0, None, (0.0, 1.0, 0.0))
+    assert r["bound"] == "alu" and abs(r["frac"] - 1e12 / 0.05 / bench.ROOF_TERMS_RAMP) < 1e-12
+    m = bench.roofline_for("fhd_gather_patch_kernel<true, true>", 1e12, 50.0, None)
+    assert m["bound"] == "mfma" and m["peak"] == bench.P_MFMA_F16 / 1e12
 
 
 def test_roofline_constants():
