@@ -135,9 +135,10 @@ TRAFFIC = {
     "fhd_gather_kernel<16, true>": {
         "workload": "spiral128", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
         "bytes_per_launch": (54788.0 * 2.0 + 92160.0 * 1.0) * 1024},
-    "fhd_gather_lines_kernel<true>": {
-        "workload": "radial64", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
-        "bytes_per_launch": (5979.0 * 2.0 + 49152.0 * 1.0) * 1024},
+    "fhd_gather_patch64_kernel<true, true>": {
+        "workload": "radial64", "sources": _GATHER_SRC,
+        "sha256": "e1ee16a4e91cc4340cb87c2fdf1a00d467c7495ce78841ff9fff32ced098aca5",
+        "bytes_per_launch": (20186.5 * 2.0 + 65536.0 * 1.0) * 1024},
     "fhd_forward_lines_kernel<true>": {
         "workload": "spiral128", "sources": ["fhd_forward.hip", "fhd_internal.h"],
         "sha256": "180b23387c0e9b8650ba365c5376dbed83a7ab2e6d12011a9aa858a9d9722062",
@@ -158,19 +159,24 @@ def measured_traffic(kernel: str, workload: str):
     return entry["bytes_per_launch"] if h.hexdigest() == entry["sha256"] else None
 
 
-def adjoint_kernel(cls: np.ndarray, counts: np.ndarray, paths: str, quads=None) -> tuple[str, float]:
+def adjoint_kernel(cls: np.ndarray, counts: np.ndarray, paths: str, quads=None,
+                   pairs64=None) -> tuple[str, float]:
     """The F^H D kernel that takes most voxels, for unit classes as the
-    layout mirror gives them (and the quads the line-pair instance takes),
-    and the fraction of voxels it takes."""
+    layout mirror gives them (and the quads and unit pairs the line-pair
+    instances take), and the fraction of voxels it takes."""
     split = "false" if paths == "bf16x3" else "true"
-    names = {4: "fhd_gather_patch_kernel<%s, true>" % split, 3: "fhd_gather_long_lines_kernel<%s>" % split,
-             2: "fhd_gather_lines_kernel<%s>" % split, 1: "fhd_gather_kernel<16, true>",
-             0: "fhd_gather_kernel<16, false>"}
+    names = {5: "fhd_gather_patch64_kernel<%s, true>" % split, 4: "fhd_gather_patch_kernel<%s, true>" % split,
+             3: "fhd_gather_long_lines_kernel<%s>" % split, 2: "fhd_gather_lines_kernel<%s>" % split,
+             1: "fhd_gather_kernel<16, true>", 0: "fhd_gather_kernel<16, false>"}
     cls = np.array(cls)
     if quads is not None and quads.size:
         taken = np.zeros(cls.size, bool)
         taken[:4 * quads.size] = np.repeat(quads, 4)
         cls[taken] = 4
+    if pairs64 is not None and pairs64.size:
+        taken = np.zeros(cls.size, bool)
+        taken[:2 * pairs64.size] = np.repeat(pairs64, 2)
+        cls[taken & (cls == 2)] = 5
     total = float(np.sum(counts)) or 1.0
     share = {c: float(np.sum(counts[cls == c])) / total for c in names}
     best = max(share, key=share.get)
@@ -391,7 +397,8 @@ def main(argv=None) -> int:
 
     cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
     lp = layout.line_pair_quads(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
-    kernel, kernel_share = adjoint_kernel(cls, counts, args.paths, lp)
+    lp64 = layout.line_pair64_pairs(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
+    kernel, kernel_share = adjoint_kernel(cls, counts, args.paths, lp, lp64)
     timer = binding.KernelTimer(kernel, args.steps, dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -458,7 +465,8 @@ def main(argv=None) -> int:
         gather(p)
         c2, _, n2 = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=p != "vector")
         lp2 = layout.line_pair_quads(w["x"], w["y"], w["z"], c2) if p != "vector" else None
-        k2, share2 = adjoint_kernel(c2, n2, p, lp2)
+        lq2 = layout.line_pair64_pairs(w["x"], w["y"], w["z"], c2) if p != "vector" else None
+        k2, share2 = adjoint_kernel(c2, n2, p, lp2, lq2)
         call_ms, kms = timed_calls(lambda: gather(p), 3, stream, k2, 1, dev)
         fr2, _ = adjoint_ceiling(w, p != "vector")
         others[p] = {"dtype": path_dtype(p, fr2[0]), "fhd_gather_call": summary(call_ms),
@@ -507,7 +515,8 @@ def bench_other(args) -> int:
     f_lines = args.paths != "vector" and layout.forward_lines_form(w["x"], w["y"], w["z"])
     cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
     lp = layout.line_pair_quads(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
-    adj_kernel, adj_share = adjoint_kernel(cls, counts, args.paths, lp)
+    lp64 = layout.line_pair64_pairs(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
+    adj_kernel, adj_share = adjoint_kernel(cls, counts, args.paths, lp, lp64)
     fwd_kernel = "fhd_forward_lines_kernel<%s>" % split if f_lines else "fhd_forward_gather_kernel<2>"
     out_r = torch.empty(max(N, M), device=dev)
     out_i = torch.empty(max(N, M), device=dev)

@@ -59,11 +59,11 @@ extern "C" {
  * be summed on the matrix cores: the voxels pair up about each line's
  * centre and F^H D (or F) becomes real matrix products of per-line centre
  * phasors and per-sample cos / sin factors (the same sum, evaluated in a
- * different order). Where, in four units, the lines of 128 also come two
- * by two as one line and that line moved by one offset (the rows of a
- * grid), F^H D pairs the voxels of each two lines about their common
- * centre instead, with half the per-line work. Every other unit is summed
- * on the vector ALUs in fp32.
+ * different order). Where, in four units (lines of 128) or two units
+ * (lines of 64), the lines also come two by two as one line and that line
+ * moved by one offset (the rows of a grid), F^H D pairs the voxels of each
+ * two lines about their common centre instead, with half the per-line
+ * work. Every other unit is summed on the vector ALUs in fp32.
  *
  *   FHD_GATHER_ALL    (the default of fhd_compute, fhd_gather, fhd_forward,
  *                     fhd_normal, fhd_cg) lines on the matrix cores with
@@ -479,7 +479,8 @@ int fhd_compute_noalloc(const float *kx, const float *ky, const float *kz,
  * kernels' as a profiler lists them, with template arguments:
  * "fhd_gather_patch_kernel<true, true>" (line pairs, split fp16, B table)
  * or "<false, true>" (split bf16), "<true, false>"/"<false, false>" (B
- * formed in the workgroups), "fhd_gather_long_lines_kernel<true>" (split
+ * formed in the workgroups), "fhd_gather_patch64_kernel<...>" (the same
+ * for 64-voxel line pairs), "fhd_gather_long_lines_kernel<true>" (split
  * fp16) or "<false>" (split bf16), "fhd_gather_lines_kernel<true>"/"<false>",
  * "fhd_gather_kernel<16, true>" (one-step ramps) or "<16, false>",
  * "fhd_forward_lines_kernel<true>"/"<false>",

@@ -548,11 +548,12 @@ __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (
 // each unit's first-lane steps, one to combine the waves' votes.
 //
 // With `patches` set, the workgroup also records in patches[2 b] and
-// patches[2 b + 1] whether the pair's 64 lines, taken two by two (lines
-// 2i and 2i + 1), are all one line and that line moved by one common
-// offset d (bitwise the same difference of their first voxels' x, y and z;
-// a long pair only), with its lines' step dx and d (bits): {flag, dx, 0,
-// 0} and {d.x, d.y, d.z, 0}.
+// patches[2 b + 1] whether the pair's lines, taken two by two (lines 2i
+// and 2i + 1), are all one line and that line moved by one common offset d
+// (bitwise the same difference of their first voxels' x, y and z), with
+// the lines' step dx and d (bits): {flag, dx, 0, 0} and {d.x, d.y, d.z,
+// 0}; flag 1 for the 64 lines of 128 voxels of a long pair, 2 for the 128
+// lines of 64 voxels of two units of class kClassLines with one step.
 //
 // When the grid holds kAmpSlots more workgroups than pairs, workgroup
 // pairs + s instead writes slot s (info[4 + s]) with the largest amplitude
@@ -599,8 +600,8 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
         return;
     }
     __shared__ float wg_step[2][3];                // each unit's first lane's ramp and line steps
-    __shared__ float wg_shift[3];                  // the pair's first two lines' offset
-    __shared__ int votes[2 * kWavesPerUnit][4];    // per wave: one step, 64-lines, 128-lines, shifts
+    __shared__ float wg_shift[2][3];               // the pair's first two lines' offset (128, 64)
+    __shared__ int votes[2 * kWavesPerUnit][5];    // per wave: one step, 64-lines, 128-lines, shifts
     const int half = threadIdx.x / kBlock, t = threadIdx.x % kBlock;
     const int64_t u = 2 * (int64_t)blockIdx.x + half;
     const bool present = u < units;   // the grid's last pair may hold one unit
@@ -611,9 +612,10 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
     // this lane's line pair (lines 2i and 2i + 1 of kLongLineVox voxels:
     // the lanes from a_lead and from a_lead + 8 of the wave): the offset of
     // the second's first voxel from the first's
-    constexpr int kLineLanes = kLongLineVox / kVox;
+    constexpr int kLineLanes = kLongLineVox / kVox, kLine64Lanes = kLineVox / kVox;
     static_assert(kLineLanes == 8 && 64 % (2 * kLineLanes) == 0, "a wave holds whole line pairs");
-    float sx = 0.0f, sy = 0.0f, sz = 0.0f;
+    static_assert(kLine64Lanes == 4, "a 64-voxel line pair is 8 lanes");
+    float sx = 0.0f, sy = 0.0f, sz = 0.0f, sx64 = 0.0f, sy64 = 0.0f, sz64 = 0.0f;
     if (present) {   // uniform over each wave
         float px[kVox], py[kVox], pz[kVox];
         load_lane_voxels<kVox, true>(x, y, z, N, n0, px, py, pz);
@@ -626,14 +628,21 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
         sx = __shfl(px[0], a_lead + kLineLanes) - __shfl(px[0], a_lead);
         sy = __shfl(py[0], a_lead + kLineLanes) - __shfl(py[0], a_lead);
         sz = __shfl(pz[0], a_lead + kLineLanes) - __shfl(pz[0], a_lead);
+        const int a64 = (threadIdx.x & 63) & ~(2 * kLine64Lanes - 1);
+        sx64 = __shfl(px[0], a64 + kLine64Lanes) - __shfl(px[0], a64);
+        sy64 = __shfl(py[0], a64 + kLine64Lanes) - __shfl(py[0], a64);
+        sz64 = __shfl(pz[0], a64 + kLine64Lanes) - __shfl(pz[0], a64);
         if (t == 0) {
             wg_step[half][0] = dx;
             wg_step[half][1] = d64;
             wg_step[half][2] = d128;
             if (half == 0) {
-                wg_shift[0] = sx;
-                wg_shift[1] = sy;
-                wg_shift[2] = sz;
+                wg_shift[0][0] = sx;
+                wg_shift[0][1] = sy;
+                wg_shift[0][2] = sz;
+                wg_shift[1][0] = sx64;
+                wg_shift[1][1] = sy64;
+                wg_shift[1][2] = sz64;
             }
         }
     }
@@ -642,27 +651,34 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
     const bool l64 = on64 && __float_as_uint(d64) == __float_as_uint(wg_step[half][1]);
     const bool l128 = on128 && __float_as_uint(d128) == __float_as_uint(wg_step[half][2]);
     const bool shifted = l128 && __builtin_isfinite(sx) && __builtin_isfinite(sy) && __builtin_isfinite(sz) &&
-                         __float_as_uint(sx) == __float_as_uint(wg_shift[0]) &&
-                         __float_as_uint(sy) == __float_as_uint(wg_shift[1]) &&
-                         __float_as_uint(sz) == __float_as_uint(wg_shift[2]);
+                         __float_as_uint(sx) == __float_as_uint(wg_shift[0][0]) &&
+                         __float_as_uint(sy) == __float_as_uint(wg_shift[0][1]) &&
+                         __float_as_uint(sz) == __float_as_uint(wg_shift[0][2]);
+    const bool shifted64 = l64 && __builtin_isfinite(sx64) && __builtin_isfinite(sy64) &&
+                           __builtin_isfinite(sz64) && __float_as_uint(sx64) == __float_as_uint(wg_shift[1][0]) &&
+                           __float_as_uint(sy64) == __float_as_uint(wg_shift[1][1]) &&
+                           __float_as_uint(sz64) == __float_as_uint(wg_shift[1][2]);
     const int wave = threadIdx.x / 64;
     const bool all_one = __all(one), all64 = __all(l64), all128 = __all(l128), all_shift = __all(shifted);
+    const bool all_shift64 = __all(shifted64);
     if ((threadIdx.x & 63) == 0) {
         votes[wave][0] = all_one;
         votes[wave][1] = all64;
         votes[wave][2] = all128;
         votes[wave][3] = all_shift;
+        votes[wave][4] = all_shift64;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int c[2], lng[2], shf = 1;
+        int c[2], lng[2], shf = 1, shf64 = 1;
         for (int k = 0; k < 2; ++k) {
-            int v[4] = {1, 1, 1, 1};
+            int v[5] = {1, 1, 1, 1, 1};
             for (int w = 0; w < kWavesPerUnit; ++w)
-                for (int q = 0; q < 4; ++q) v[q] &= votes[k * kWavesPerUnit + w][q];
+                for (int q = 0; q < 5; ++q) v[q] &= votes[k * kWavesPerUnit + w][q];
             c[k] = allow_lines && v[1] ? kClassLines : v[0] ? kClassOneStep : kClassGeneral;
             lng[k] = v[2];
             shf &= v[3];
+            shf64 &= v[4];
         }
         const bool has_second = 2 * (int64_t)blockIdx.x + 1 < units;
         const bool pair = allow_lines && has_second && lng[0] && lng[1] &&
@@ -675,11 +691,17 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
             info[2] = 0;
         }
         if (patches) {
-            const bool patch = pair && shf;
-            patches[2 * (int64_t)blockIdx.x] = make_int4(patch ? 1 : 0, (int)__float_as_uint(wg_step[0][2]), 0, 0);
+            // 1: 128-voxel line pairs (a long pair); 2: 64-voxel line pairs
+            // (both units of class kClassLines with one step for the pair)
+            const bool pair64 = !pair && has_second && c[0] == kClassLines && c[1] == kClassLines &&
+                                __float_as_uint(wg_step[0][1]) == __float_as_uint(wg_step[1][1]) && shf64;
+            const int flag = pair && shf ? 1 : pair64 ? 2 : 0;
+            const int sel = flag == 2 ? 1 : 0;
+            patches[2 * (int64_t)blockIdx.x] =
+                make_int4(flag, (int)__float_as_uint(wg_step[0][flag == 2 ? 1 : 2]), 0, 0);
             patches[2 * (int64_t)blockIdx.x + 1] =
-                make_int4((int)__float_as_uint(wg_shift[0]), (int)__float_as_uint(wg_shift[1]),
-                          (int)__float_as_uint(wg_shift[2]), 0);
+                make_int4((int)__float_as_uint(wg_shift[sel][0]), (int)__float_as_uint(wg_shift[sel][1]),
+                          (int)__float_as_uint(wg_shift[sel][2]), 0);
         }
     }
 }
@@ -755,6 +777,55 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ONE_STEP
 }
 
 // ---------------------------------------------------------------------------
+// Which line-pair workgroups take a group of units
+// ---------------------------------------------------------------------------
+// Whether quad q (units 4q .. 4q + 3) is taken by the line-pair instance:
+// both of its unit pairs are long pairs with the line-pair structure, the
+// same step and the same offset (records from the classification, two
+// int4 per unit pair).
+__device__ __forceinline__ bool patch_quad(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                           int64_t units, int64_t q)
+{
+    if (patches == nullptr || 4 * q + 3 >= units) return false;
+    if (cls[4 * q] != kClassLongPair || cls[4 * q + 2] != kClassLongPair) return false;
+    const int4 a0 = patches[4 * q], a1 = patches[4 * q + 1], b0 = patches[4 * q + 2], b1 = patches[4 * q + 3];
+    return a0.x == 1 && b0.x == 1 && a0.y == b0.y && a1.x == b1.x && a1.y == b1.y && a1.z == b1.z;
+}
+
+// How the line-pair instance runs in a call: not at all, with a B table
+// formed for quad 0's step and offset (it then takes the quads that share
+// them; the long-line instance takes the other long pairs), or forming
+// each step's B operands itself (it takes every quad).
+enum : int { kPatchNone = 0, kPatchTable = 1, kPatchFormed = 2 };
+
+// Whether unit pair p (units 2p, 2p + 1) is taken by the 64-voxel
+// line-pair instance in `mode`: both units of class kClassLines and the
+// pair's record says its 64-voxel lines pair up (flag 2); in the table
+// mode also pair 0 so, with the same step and offset.
+__device__ __forceinline__ bool pair64_taken(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                             int64_t units, int64_t p, int mode)
+{
+    if (mode == kPatchNone || patches == nullptr || 2 * p + 1 >= units) return false;
+    if (cls[2 * p] != kClassLines || cls[2 * p + 1] != kClassLines || patches[2 * p].x != 2) return false;
+    if (mode == kPatchFormed || p == 0) return true;
+    if (cls[0] != kClassLines || cls[1] != kClassLines || patches[0].x != 2) return false;
+    const int4 r0 = patches[0], r1 = patches[1], a0 = patches[2 * p], a1 = patches[2 * p + 1];
+    return r0.y == a0.y && r1.x == a1.x && r1.y == a1.y && r1.z == a1.z;
+}
+
+// Whether quad q is taken by the line-pair instance in `mode`.
+__device__ __forceinline__ bool patch_taken(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                            int64_t units, int64_t q, int mode)
+{
+    if (mode == kPatchNone || !patch_quad(cls, patches, units, q)) return false;
+    if (mode == kPatchFormed) return true;
+    if (q == 0) return true;
+    if (!patch_quad(cls, patches, units, 0)) return false;
+    const int4 r0 = patches[0], r1 = patches[1], a0 = patches[4 * q], a1 = patches[4 * q + 1];
+    return r0.y == a0.y && r1.x == a1.x && r1.y == a1.y && r1.z == a1.z;
+}
+
+// ---------------------------------------------------------------------------
 // Lines on the matrix cores
 // ---------------------------------------------------------------------------
 // In a unit of class kClassLines the voxels of a line pair up about its
@@ -798,10 +869,11 @@ static_assert(kLinesBlock / 64 == 2, "wave 0 forms B_C, wave 1 B_S");
 template <bool F16>
 __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_lines_kernel(
     const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
-    const int *__restrict__ info, const float *__restrict__ x, const float *__restrict__ y,
-    const float *__restrict__ z, float *__restrict__ out_r, float *__restrict__ out_i, int N)
+    const int4 *__restrict__ patches, int64_t units, int patch_mode, const int *__restrict__ info,
+    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
+    float *__restrict__ out_r, float *__restrict__ out_i, int N)
 {
-    if (cls[blockIdx.x] != kClassLines) return;
+    if (cls[blockIdx.x] != kClassLines || pair64_taken(cls, patches, units, blockIdx.x / 2, patch_mode)) return;
     __shared__ float4 stage[2][kLinesStageVec4];
     // [buffer][B_C hi, B_C lo, B_S hi, B_S lo][k half][pair]: one lane's
     // 8-sample operand each; a half-wave reads 32 consecutive entries
@@ -929,37 +1001,6 @@ __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))
     }
 }
 
-// Whether quad q (units 4q .. 4q + 3) is taken by the line-pair instance:
-// both of its unit pairs are long pairs with the line-pair structure, the
-// same step and the same offset (records from the classification, two
-// int4 per unit pair).
-__device__ __forceinline__ bool patch_quad(const int *__restrict__ cls, const int4 *__restrict__ patches,
-                                           int64_t units, int64_t q)
-{
-    if (patches == nullptr || 4 * q + 3 >= units) return false;
-    if (cls[4 * q] != kClassLongPair || cls[4 * q + 2] != kClassLongPair) return false;
-    const int4 a0 = patches[4 * q], a1 = patches[4 * q + 1], b0 = patches[4 * q + 2], b1 = patches[4 * q + 3];
-    return a0.x != 0 && b0.x != 0 && a0.y == b0.y && a1.x == b1.x && a1.y == b1.y && a1.z == b1.z;
-}
-
-// How the line-pair instance runs in a call: not at all, with a B table
-// formed for quad 0's step and offset (it then takes the quads that share
-// them; the long-line instance takes the other long pairs), or forming
-// each step's B operands itself (it takes every quad).
-enum : int { kPatchNone = 0, kPatchTable = 1, kPatchFormed = 2 };
-
-// Whether quad q is taken by the line-pair instance in `mode`.
-__device__ __forceinline__ bool patch_taken(const int *__restrict__ cls, const int4 *__restrict__ patches,
-                                            int64_t units, int64_t q, int mode)
-{
-    if (mode == kPatchNone || !patch_quad(cls, patches, units, q)) return false;
-    if (mode == kPatchFormed) return true;
-    if (q == 0) return true;
-    if (!patch_quad(cls, patches, units, 0)) return false;
-    const int4 r0 = patches[0], r1 = patches[1], a0 = patches[4 * q], a1 = patches[4 * q + 1];
-    return r0.y == a0.y && r1.x == a1.x && r1.y == a1.y && r1.z == a1.z;
-}
-
 // ---------------------------------------------------------------------------
 // Long lines on the matrix cores
 // ---------------------------------------------------------------------------
@@ -1032,22 +1073,114 @@ __device__ __forceinline__ void long_step_b(const float (&f)[kFields][kChunk], f
     dst[2 * part + 1][t0 + 1][quarter_k][col] = (u32x4){l1[0], l1[1], l1[2], l1[3]};
 }
 
+constexpr int kQuadVox = 2 * kPairVox;              // voxels of a quad
+constexpr int kPatchBlock = 256;                    // 4 waves of 16 line pairs
+
+// The line-pair instance for lines of LINE voxels (128: quads of long
+// pairs; 64: unit pairs of 64-voxel lines, as on a grid with rows of 64):
+// a workgroup takes 64 line pairs, 128 LINE voxels, with LINE pair
+// columns (LINE / 2 per side) in LINE / 16 tiles. B operands of one step:
+// [B_C hi, B_C lo, B_S hi, B_S lo][tile][k quarter][column in tile], one
+// lane's 8 fp16 or bf16 each: 32 KB (LINE 128) or 16 KB (64).
+template <int LINE>
+struct PatchShape {
+    static constexpr int kHalf = LINE / 2;          // pairs per side
+    static constexpr int kTiles = LINE / 16;
+    static constexpr int kGroupVox = 128 * LINE;
+    static constexpr int kStepVec4 = 4 * kTiles * 4 * 16;
+    typedef u32x4 StepB[4][kTiles][4][16];
+    struct Step {
+        StepB b;
+        float4 chunks[kLongStepChunkVec4];
+    };
+};
+static_assert(PatchShape<kLongLineVox>::kGroupVox == kQuadVox, "a 128-voxel line-pair workgroup is a quad");
+static_assert(PatchShape<kLineVox>::kGroupVox == kPairVox, "a 64-voxel line-pair workgroup is a unit pair");
+constexpr int kPatchStepVec4 = PatchShape<kLongLineVox>::kStepVec4;
+constexpr int kPatch64StepVec4 = PatchShape<kLineVox>::kStepVec4;
+static_assert(kPatch64StepVec4 == kLongStepVec4, "the 64-voxel line-pair B shares the long-line table");
+
+// Lane (wave w, lane l) of a step's B: B_C (w < 2) or B_S (w >= 2, as a
+// cosine a quarter turn later) of the pair tiles of side w % 2 (columns at
+// +d/2 for side 0, -d/2 for side 1), column l % 16 of each, samples
+// 8 (l / 16) .. + 7 (f: their chunk; dx and d: the group's step and
+// offset; sh: the amplitudes' scaling in the fp16 form), split and stored
+// at their place in `dst`.
+template <bool F16, int LINE>
+__device__ __forceinline__ void patch_step_b(const float (&f)[kFields][kChunk], float dx, float ddx, float ddy,
+                                             float ddz, int wave, int quarter_k, int col, int sh,
+                                             typename PatchShape<LINE>::StepB &dst)
+{
+    constexpr int kSideTiles = PatchShape<LINE>::kTiles / 2;
+    const int part = wave >> 1, side = wave & 1, t0 = kSideTiles * side;
+    const float turn = part == 0 ? 0.0f : -0.25f;
+#pragma unroll
+    for (int tt = 0; tt < kSideTiles; ++tt) {
+        const int j = 16 * tt + col;
+        const float tj = (float)(2 * j + 1) * (0.5f * dx);
+        float b[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const float hd = 0.5f * __builtin_fmaf(f[0][i], ddx, __builtin_fmaf(f[1][i], ddy, f[2][i] * ddz));
+            const float amp = scale_amp<F16>(f[4][i], sh);
+            b[i] = amp * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj, (side == 0 ? hd : -hd) + turn));
+        }
+        unsigned h[4], l[4];
+        split_parts<F16, kChunk>(b, h, l);
+        dst[2 * part + 0][t0 + tt][quarter_k][col] = (u32x4){h[0], h[1], h[2], h[3]};
+        dst[2 * part + 1][t0 + tt][quarter_k][col] = (u32x4){l[0], l[1], l[2], l[3]};
+    }
+}
+
+// Step g of the B table for a group's step and offset (the records at
+// rec[0], rec[1]): chunks past the stream's end as zeros.
+template <bool F16, int LINE>
+__device__ __forceinline__ void patch_table_step(const float *__restrict__ packed, int nchunks,
+                                                 const int4 *__restrict__ rec, const int *__restrict__ info,
+                                                 float4 *__restrict__ table)
+{
+    const float dx = __int_as_float(rec[0].y);
+    const int4 d = rec[1];
+    const int sh = F16 ? read_amp_shift(info) : 0;
+    const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t chunk = (int64_t)blockIdx.x * kLongGroup + quarter_k;
+    float f[kFields][kChunk];
+    if (chunk < nchunks) {
+        load_chunk(reinterpret_cast<const float4 *>(packed) + chunk * kChunkVec4, f);
+    } else {
+#pragma unroll
+        for (int q = 0; q < kFields; ++q)
+#pragma unroll
+            for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
+    }
+    patch_step_b<F16, LINE>(
+        f, dx, __int_as_float(d.x), __int_as_float(d.y), __int_as_float(d.z), wave, quarter_k, col, sh,
+        *reinterpret_cast<typename PatchShape<LINE>::StepB *>(table + (int64_t)blockIdx.x * PatchShape<LINE>::kStepVec4));
+}
+
 // The B operands of every product step of the sample stream, formed once per
 // call for the step of the first pair of units when that pair is of class
 // kClassLongPair (info[0] = 1, info[1] = its step's bits, as the classify
 // kernel records them) and not taken by the line-pair instance (which then
 // most likely takes every long pair): step g at table + g kLongStepVec4,
-// chunks past the
-// stream's end as zeros. The long-line workgroups whose lines have that
-// step copy them into LDS instead of forming them (same arithmetic, same
-// bits).
+// chunks past the stream's end as zeros. The long-line workgroups whose
+// lines have that step copy them into LDS instead of forming them (same
+// arithmetic, same bits). When pair 0 is instead taken by the 64-voxel
+// line-pair instance (in table mode), the same buffer gets that instance's
+// B operands for pair 0's step and offset (the same size per step).
 template <bool F16>
 __global__ __launch_bounds__(kLongBlock) void fhd_long_table_kernel(const float *__restrict__ packed, int nchunks,
                                                                     const int *__restrict__ cls,
                                                                     const int4 *__restrict__ patches, int64_t units,
-                                                                    int patch_mode, const int *__restrict__ info,
+                                                                    int patch_mode, int pair64_mode,
+                                                                    const int *__restrict__ info,
                                                                     float4 *__restrict__ table)
 {
+    if (pair64_mode == kPatchTable && pair64_taken(cls, patches, units, 0, kPatchTable)) {
+        patch_table_step<F16, kLineVox>(packed, nchunks, patches, info, table);
+        return;
+    }
     if (info[0] == 0 || patch_taken(cls, patches, units, 0, patch_mode)) return;
     const float dx = __int_as_float(info[1]);
     const int sh = F16 ? read_amp_shift(info) : 0;
@@ -1265,56 +1398,11 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
 // 32 KB (formed once per call into a table, or by the workgroup itself),
 // double buffered with the step's four sample chunks: 66.8 KB of LDS, two
 // workgroups (8 waves) per CU.
-constexpr int kQuadVox = 2 * kPairVox;              // voxels per workgroup
-constexpr int kPatchPairs = 2 * kLongPairs;         // 128 pair columns
-constexpr int kPatchTiles = kPatchPairs / 16;       // 8
-constexpr int kPatchBlock = 256;                    // 4 waves of 16 line pairs
-static_assert(kQuadVox == 2 * kLongLineVox * 16 * (kPatchBlock / 64), "a wave takes 16 line pairs");
-static_assert(kPatchTiles == 8 && kPatchBlock / 64 == 4, "each wave forms 4 tiles of B_C or B_S");
-
-// B operands of one step: [B_C hi, B_C lo, B_S hi, B_S lo][tile][k
-// quarter][column in tile], one lane's 8 fp16 or bf16 each. 32 KB.
-constexpr int kPatchStepVec4 = 4 * kPatchTiles * 4 * 16;
-typedef u32x4 PatchStepB[4][kPatchTiles][4][16];
-struct PatchStep {
-    PatchStepB b;
-    float4 chunks[kLongStepChunkVec4];
-};
-
-// Lane (wave w, lane l) of a step's B: B_C (w < 2) or B_S (w >= 2, as a
-// cosine a quarter turn later) of pair tiles 4 (w % 2) .. 4 (w % 2) + 3,
-// column l % 16 of each, samples 8 (l / 16) .. + 7 (f: their chunk; dx and
-// d: the quad's step and offset; sh: the amplitudes' scaling in the fp16
-// form), split and stored at their place in `dst`.
-template <bool F16>
-__device__ __forceinline__ void patch_step_b(const float (&f)[kFields][kChunk], float dx, float ddx, float ddy,
-                                             float ddz, int wave, int quarter_k, int col, int sh, PatchStepB &dst)
-{
-    const int part = wave >> 1, side = wave & 1, t0 = 4 * side;
-    const float turn = part == 0 ? 0.0f : -0.25f;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int j = 16 * tt + col;
-        const float tj = (float)(2 * j + 1) * (0.5f * dx);
-        float b[kChunk];
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            const float hd = 0.5f * __builtin_fmaf(f[0][i], ddx, __builtin_fmaf(f[1][i], ddy, f[2][i] * ddz));
-            const float amp = scale_amp<F16>(f[4][i], sh);
-            b[i] = amp * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj, (side == 0 ? hd : -hd) + turn));
-        }
-        unsigned h[4], l[4];
-        split_parts<F16, kChunk>(b, h, l);
-        dst[2 * part + 0][t0 + tt][quarter_k][col] = (u32x4){h[0], h[1], h[2], h[3]};
-        dst[2 * part + 1][t0 + tt][quarter_k][col] = (u32x4){l[0], l[1], l[2], l[3]};
-    }
-}
-
 // The B operands of every step of the sample stream for quad 0's step and
-// offset, formed once per call when quad 0 is taken by the line-pair
-// instance: step g at table + g kPatchStepVec4, chunks past the stream's end
-// as zeros. Quads with that step and offset copy them into LDS instead of
-// forming them (same arithmetic, same bits).
+// offset, formed once per call when quad 0 is taken by the 128-voxel
+// line-pair instance: step g at table + g kPatchStepVec4. Quads with that
+// step and offset copy them into LDS instead of forming them (same
+// arithmetic, same bits).
 template <bool F16>
 __global__ __launch_bounds__(kPatchBlock) void fhd_patch_table_kernel(const float *__restrict__ packed, int nchunks,
                                                                       const int *__restrict__ cls,
@@ -1323,61 +1411,43 @@ __global__ __launch_bounds__(kPatchBlock) void fhd_patch_table_kernel(const floa
                                                                       float4 *__restrict__ table)
 {
     if (!patch_quad(cls, patches, units, 0)) return;
-    const float dx = __int_as_float(patches[0].y);
-    const int4 d = patches[1];
-    const int sh = F16 ? read_amp_shift(info) : 0;
-    const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t chunk = (int64_t)blockIdx.x * kLongGroup + quarter_k;
-    float f[kFields][kChunk];
-    if (chunk < nchunks) {
-        load_chunk(reinterpret_cast<const float4 *>(packed) + chunk * kChunkVec4, f);
-    } else {
-#pragma unroll
-        for (int q = 0; q < kFields; ++q)
-#pragma unroll
-            for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
-    }
-    patch_step_b<F16>(f, dx, __int_as_float(d.x), __int_as_float(d.y), __int_as_float(d.z), wave, quarter_k, col, sh,
-                      *reinterpret_cast<PatchStepB *>(table + (int64_t)blockIdx.x * kPatchStepVec4));
+    patch_table_step<F16, kLongLineVox>(packed, nchunks, patches, info, table);
 }
 
-// TABLE: the B operands come from the table (mode kPatchTable, the quads
-// that share quad 0's step and offset); else the workgroup forms them
-// (mode kPatchFormed, every quad; two separate instances, so the table
-// form's register allocation does not carry the forming code's).
-template <bool F16, bool TABLE>
-__global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(2))) void fhd_gather_patch_kernel(
-    const float *__restrict__ packed, int nchunks, int splits, int64_t quads, int64_t units,
-    const int *__restrict__ cls, const int4 *__restrict__ patches, const int *__restrict__ info,
-    const float4 *__restrict__ table, const float *__restrict__ x, const float *__restrict__ y,
-    const float *__restrict__ z, float *__restrict__ out_r, float *__restrict__ out_i, int N)
+// One workgroup of the line-pair instance for lines of LINE voxels: group
+// `group` (a quad for 128, a unit pair for 64), sample split `split` of
+// `splits`. TABLE: the B operands come from `table`; else the workgroup
+// forms them (the same arithmetic).
+template <bool F16, bool TABLE, int LINE>
+__device__ __forceinline__ void patch_group(const float *__restrict__ packed, int nchunks, int splits, int64_t group,
+                                            int split, const int4 *__restrict__ rec, const int *__restrict__ info,
+                                            const float4 *__restrict__ table, const float *__restrict__ x,
+                                            const float *__restrict__ y, const float *__restrict__ z,
+                                            float *__restrict__ out_r, float *__restrict__ out_i, int N,
+                                            typename PatchShape<LINE>::Step &buf0,
+                                            typename PatchShape<LINE>::Step &buf1)
 {
-    // workgroup -> (quad, split), split-major over the XCDs (see xcd_unit)
-    const int64_t unit = xcd_unit(blockIdx.x, quads * splits);
-    const int64_t quad = unit % quads;
-    const int split = (int)(unit / quads);
-    if (!patch_taken(cls, patches, units, quad, TABLE ? kPatchTable : kPatchFormed)) return;
-    // two step buffers used alternately, as in the long-line instance
-    __shared__ PatchStep buf0, buf1;
+    using Shape = PatchShape<LINE>;
+    using Step = typename Shape::Step;
+    constexpr int kTiles = Shape::kTiles, kHalf = Shape::kHalf;
     const float4 *src = reinterpret_cast<const float4 *>(packed);
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sh = F16 ? read_amp_shift(info) : 0;
-    const float dx = __int_as_float(patches[4 * quad].y);
-    const int4 dbits = patches[4 * quad + 1];
+    const float dx = __int_as_float(rec[0].y);
+    const int4 dbits = rec[1];
     const float ddx = __int_as_float(dbits.x), ddy = __int_as_float(dbits.y), ddz = __int_as_float(dbits.z);
 
-    // line pair 16 wave + col of the quad: lines 2 lp and 2 lp + 1
-    const int64_t base = quad * kQuadVox;
-    const int64_t first = base + (int64_t)(2 * (16 * wave + col)) * kLongLineVox;
+    // line pair 16 wave + col of the group: lines 2 lp and 2 lp + 1
+    const int64_t base = group * Shape::kGroupVox;
+    const int64_t first = base + (int64_t)(2 * (16 * wave + col)) * LINE;
     const float x0 = x[first], ly = y[first], lz = z[first];
-    const float cx = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x0) + 0.5f * ddx;
+    const float cx = __builtin_fmaf(0.5f * (float)(LINE - 1), dx, x0) + 0.5f * ddx;
     const float cy = ly + 0.5f * ddy, cz = lz + 0.5f * ddz;
 
-    float4v prc[kPatchTiles], pic[kPatchTiles], pis[kPatchTiles], prs[kPatchTiles];
+    float4v prc[kTiles], pic[kTiles], pis[kTiles], prs[kTiles];
 #pragma unroll
-    for (int t = 0; t < kPatchTiles; ++t)
+    for (int t = 0; t < kTiles; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             prc[t][r] = 0.0f;
@@ -1392,27 +1462,26 @@ __global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(2))
     src += (int64_t)c0 * kChunkVec4;
     const int64_t total_vec4 = (int64_t)nch * kChunkVec4;
     const int nsteps = (nch + kLongGroup - 1) / kLongGroup;
-    const int64_t table_vec4 = (((int64_t)nchunks + kLongGroup - 1) / kLongGroup) * kPatchStepVec4;
+    const int64_t table_vec4 = (((int64_t)nchunks + kLongGroup - 1) / kLongGroup) * Shape::kStepVec4;
     const int g0 = c0 / kLongGroup;
 
-    auto copy_step = [&](int i, PatchStep &dst, auto from_table) __attribute__((always_inline)) {
+    auto copy_step = [&](int i, Step &dst) __attribute__((always_inline)) {
         issue_stage_load<kPatchBlock, kLongStepChunkVec4>(src, total_vec4, i, dst.chunks);
-        if constexpr (decltype(from_table)::value)
-            issue_stage_load<kPatchBlock, kPatchStepVec4>(table, table_vec4, g0 + i,
-                                                           reinterpret_cast<float4 *>(&dst.b));
+        if constexpr (TABLE)
+            issue_stage_load<kPatchBlock, Shape::kStepVec4>(table, table_vec4, g0 + i,
+                                                             reinterpret_cast<float4 *>(&dst.b));
     };
 
     // step i in `cur` (see the long-line instance's step for the order of
     // waits, barriers and copies)
-    auto step = [&](int i, PatchStep &cur, PatchStep &next, auto from_table) __attribute__((always_inline)) {
-        constexpr bool kTable = decltype(from_table)::value;
+    auto step = [&](int i, Step &cur, Step &next) __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         lds_barrier();
-        if (i + 1 < nsteps) copy_step(i + 1, next, from_table);
+        if (i + 1 < nsteps) copy_step(i + 1, next);
         float f[kFields][kChunk];
         load_chunk(cur.chunks + quarter_k * kChunkVec4, f);
-        if constexpr (!kTable) {
-            patch_step_b<F16>(f, dx, ddx, ddy, ddz, wave, quarter_k, col, sh, cur.b);
+        if constexpr (!TABLE) {
+            patch_step_b<F16, LINE>(f, dx, ddx, ddy, ddz, wave, quarter_k, col, sh, cur.b);
             lds_barrier();
         }
         float ur[kChunk], ui[kChunk];
@@ -1429,7 +1498,7 @@ __global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(2))
         const u32x4 aih = {wa[2][0], wa[2][1], wa[2][2], wa[2][3]}, ail = {wa[3][0], wa[3][1], wa[3][2], wa[3][3]};
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int t = 0; t < kPatchTiles; ++t) {
+        for (int t = 0; t < kTiles; ++t) {
             const u32x4 bch = cur.b[0][t][quarter_k][col], bcl = cur.b[1][t][quarter_k][col];
             const u32x4 bsh = cur.b[2][t][quarter_k][col], bsl = cur.b[3][t][quarter_k][col];
             prc[t] = mfma16<F16>(arh, bch, prc[t]);
@@ -1448,34 +1517,74 @@ __global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(2))
         __builtin_amdgcn_s_setprio(0);
     };
 
-    auto walk = [&](auto from_table) __attribute__((always_inline)) {
-        if (nsteps > 0) copy_step(0, buf0, from_table);
-        int i = 0;
-        for (; i + 1 < nsteps; i += 2) {
-            step(i, buf0, buf1, from_table);
-            step(i + 1, buf1, buf0, from_table);
-        }
-        if (i < nsteps) step(i, buf0, buf1, from_table);
-    };
-    walk(std::integral_constant<bool, TABLE>{});
+    if (nsteps > 0) copy_step(0, buf0);
+    int i = 0;
+    for (; i + 1 < nsteps; i += 2) {
+        step(i, buf0, buf1);
+        step(i + 1, buf1, buf0);
+    }
+    if (i < nsteps) step(i, buf0, buf1);
 
     // unfold: row 4 (l / 16) + r of the wave's 16 line pairs, pair column
-    // 16 t + l % 16 (side t / 4, j = 16 (t % 4) + l % 16)
+    // 16 t + l % 16 (side t / (kTiles / 2), j = 16 (t % (kTiles / 2)) + l % 16)
     float *dst_r = out_r + (int64_t)split * N, *dst_i = out_i + (int64_t)split * N;
 #pragma unroll
-    for (int t = 0; t < kPatchTiles; ++t)
+    for (int t = 0; t < kTiles; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t line_a = base + (int64_t)(2 * (16 * wave + 4 * quarter_k + r)) * kLongLineVox;
-            const int64_t line_b = line_a + kLongLineVox;
-            const int j = 16 * (t % 4) + col;
-            const int64_t plus = (t < 4 ? line_b : line_a) + kLongPairs + j;
-            const int64_t minus = (t < 4 ? line_a : line_b) + kLongPairs - 1 - j;
+            const int64_t line_a = base + (int64_t)(2 * (16 * wave + 4 * quarter_k + r)) * LINE;
+            const int64_t line_b = line_a + LINE;
+            const bool side0 = t < kTiles / 2;
+            const int j = 16 * (t % (kTiles / 2)) + col;
+            const int64_t plus = (side0 ? line_b : line_a) + kHalf + j;
+            const int64_t minus = (side0 ? line_a : line_b) + kHalf - 1 - j;
             dst_r[plus] = unscale<F16>(prc[t][r] - pis[t][r], sh);
             dst_i[plus] = unscale<F16>(pic[t][r] + prs[t][r], sh);
             dst_r[minus] = unscale<F16>(prc[t][r] + pis[t][r], sh);
             dst_i[minus] = unscale<F16>(pic[t][r] - prs[t][r], sh);
         }
+}
+
+// The 128-voxel line-pair instance: quads. TABLE: the B operands come
+// from the table (mode kPatchTable, the quads that share quad 0's step and
+// offset); else the workgroup forms them (mode kPatchFormed, every quad;
+// two separate instances, so the table form's register allocation does
+// not carry the forming code's).
+template <bool F16, bool TABLE>
+__global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(2))) void fhd_gather_patch_kernel(
+    const float *__restrict__ packed, int nchunks, int splits, int64_t quads, int64_t units,
+    const int *__restrict__ cls, const int4 *__restrict__ patches, const int *__restrict__ info,
+    const float4 *__restrict__ table, const float *__restrict__ x, const float *__restrict__ y,
+    const float *__restrict__ z, float *__restrict__ out_r, float *__restrict__ out_i, int N)
+{
+    // workgroup -> (quad, split), split-major over the XCDs (see xcd_unit)
+    const int64_t unit = xcd_unit(blockIdx.x, quads * splits);
+    const int64_t quad = unit % quads;
+    const int split = (int)(unit / quads);
+    if (!patch_taken(cls, patches, units, quad, TABLE ? kPatchTable : kPatchFormed)) return;
+    // two step buffers used alternately, as in the long-line instance
+    __shared__ PatchShape<kLongLineVox>::Step buf0, buf1;
+    patch_group<F16, TABLE, kLongLineVox>(packed, nchunks, splits, quad, split, patches + 4 * quad, info, table, x, y,
+                                          z, out_r, out_i, N, buf0, buf1);
+}
+
+// The 64-voxel line-pair instance: unit pairs whose 64-voxel lines pair up
+// (record flag 2), with the B table (16 KB per step, in the long-line
+// table's buffer) for pair 0's step and offset, or formed.
+template <bool F16, bool TABLE>
+__global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_patch64_kernel(
+    const float *__restrict__ packed, int nchunks, int splits, int64_t pairs, int64_t units,
+    const int *__restrict__ cls, const int4 *__restrict__ patches, const int *__restrict__ info,
+    const float4 *__restrict__ table, const float *__restrict__ x, const float *__restrict__ y,
+    const float *__restrict__ z, float *__restrict__ out_r, float *__restrict__ out_i, int N)
+{
+    const int64_t unit = xcd_unit(blockIdx.x, pairs * splits);
+    const int64_t pair = unit % pairs;
+    const int split = (int)(unit / pairs);
+    if (!pair64_taken(cls, patches, units, pair, TABLE ? kPatchTable : kPatchFormed)) return;
+    __shared__ PatchShape<kLineVox>::Step buf0, buf1;
+    patch_group<F16, TABLE, kLineVox>(packed, nchunks, splits, pair, split, patches + 2 * pair, info, table, x, y, z,
+                                      out_r, out_i, N, buf0, buf1);
 }
 
 }  // namespace
@@ -1561,9 +1670,11 @@ int launch_line_instances(const GatherPlan &g, const int *cls, const int4 *patch
         }
         rc = launch_status("fhd_gather_patch_kernel launch");
     }
+    // the 64-voxel line-pair instance shares the long-line table's buffer
+    const int mode64 = !long_pairs ? kPatchNone : long_table ? kPatchTable : kPatchFormed;
     if (rc == FHD_OK && long_pairs && long_table) {
         fhd_long_table_kernel<F16><<<dim3((unsigned)g.steps), dim3(kLongBlock), 0, stream>>>(
-            packed, g.nchunks, cls, patches, g.blocks, mode, info, long_table);
+            packed, g.nchunks, cls, patches, g.blocks, mode, mode64, info, long_table);
         rc = launch_status("fhd_long_table_kernel launch");
     }
     if (rc == FHD_OK && long_pairs) {
@@ -1573,12 +1684,34 @@ int launch_line_instances(const GatherPlan &g, const int *cls, const int4 *patch
             direct_long ? rho_r : part_r, direct_long ? rho_i : part_i, N);
         rc = launch_status("fhd_gather_long_lines_kernel launch");
     }
+    // the 64-voxel line-pair and line instances share one split count
+    // (both take units of class kClassLines)
+    const bool direct_lines = g.s_lines == 1;
+    if (rc == FHD_OK && long_pairs) {
+        const dim3 grid((unsigned)(g.pairs * g.s_lines));
+        float *out_r = direct_lines ? rho_r : part_r, *out_i = direct_lines ? rho_i : part_i;
+        if (mode64 == kPatchTable) {
+            TimedLaunch timed(F16 ? "fhd_gather_patch64_kernel<true, true>" : "fhd_gather_patch64_kernel<false, true>",
+                              stream);
+            fhd_gather_patch64_kernel<F16, true><<<grid, dim3(kPatchBlock), 0, stream>>>(
+                packed, g.nchunks, g.s_lines, g.pairs, g.blocks, cls, patches, info, long_table, x, y, z, out_r,
+                out_i, N);
+        } else {
+            TimedLaunch timed(F16 ? "fhd_gather_patch64_kernel<true, false>"
+                                  : "fhd_gather_patch64_kernel<false, false>",
+                              stream);
+            fhd_gather_patch64_kernel<F16, false><<<grid, dim3(kPatchBlock), 0, stream>>>(
+                packed, g.nchunks, g.s_lines, g.pairs, g.blocks, cls, patches, info, nullptr, x, y, z, out_r, out_i,
+                N);
+        }
+        rc = launch_status("fhd_gather_patch64_kernel launch");
+    }
     if (rc == FHD_OK && whole_unit) {
-        const bool direct = g.s_lines == 1;
         TimedLaunch timed(F16 ? "fhd_gather_lines_kernel<true>" : "fhd_gather_lines_kernel<false>", stream);
         fhd_gather_lines_kernel<F16><<<dim3((unsigned)g.blocks, (unsigned)g.s_lines), dim3(kLinesBlock), 0,
-                                        stream>>>(packed, g.nchunks, g.s_lines, cls, info, x, y, z,
-                                                  direct ? rho_r : part_r, direct ? rho_i : part_i, N);
+                                        stream>>>(packed, g.nchunks, g.s_lines, cls, patches, g.blocks, mode64, info,
+                                                  x, y, z, direct_lines ? rho_r : part_r,
+                                                  direct_lines ? rho_i : part_i, N);
         rc = launch_status("fhd_gather_lines_kernel launch");
     }
     return rc;
@@ -1657,7 +1790,15 @@ GatherPlan plan_gather(int M, int N, int paths, bool with_table)
                                blocks_per_cu<1>(reinterpret_cast<const void *>(fhd_gather_long_lines_kernel<true>),
                                                 kLongBlock),
                                kLinesStageChunks);
-    if (whole_unit)
+    // the lines' split count: sized for the 64-voxel line-pair instance
+    // where unit pairs exist (on grids with rows of 64 it takes them all),
+    // else for the line one
+    if (long_pairs)
+        g.s_lines = split_count(g.pairs, g.nchunks,
+                                blocks_per_cu<5>(reinterpret_cast<const void *>(fhd_gather_patch64_kernel<true, true>),
+                                                 kPatchBlock),
+                                kLinesStageChunks);
+    else if (whole_unit)
         g.s_lines = split_count(g.blocks, g.nchunks,
                                 blocks_per_cu<3>(reinterpret_cast<const void *>(fhd_gather_lines_kernel<true>),
                                                  kLinesBlock),

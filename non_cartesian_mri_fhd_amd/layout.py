@@ -146,6 +146,54 @@ def line_pair_quads(x, y, z, cls=None, block: int = 256, vox: int = 16, long_lin
     return quad & np.all(key[0::2] == key[0], axis=1)
 
 
+def line_pair64_pairs(x, y, z, cls=None, block: int = 256, vox: int = 16, line: int = 64,
+                      formed: bool = False):
+    """Per unit pair (units 2p, 2p + 1, both present), whether the F^H D
+    64-voxel line-pair instance takes it, by the classify kernel's record:
+    both units of class 2 with one step for the pair (bitwise), in the pair
+    the lines 2i + 1 of `line` voxels the lines 2i moved by one common
+    offset d (bitwise equal fp32 differences of their first voxels' x, y,
+    z, all finite; d from the pair's lines 0 and 1); and, unless `formed`,
+    pair 0 so too with the same step and d."""
+    x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
+    unit = block * vox
+    if cls is None:
+        cls = gather_unit_classes(x, y, z, block, vox)[0]
+    pairs = cls.size // 2
+    if pairs == 0:
+        return np.zeros(0, bool)
+    nl = 2 * unit // line                          # lines per unit pair
+    first = np.arange(pairs * nl) * line
+    ok_first = first + 1 < x.size
+    if not ok_first.all():
+        return np.zeros(pairs, bool)
+    fx, fy, fz = x[first], y[first], z[first]
+    step = (x[first + 1] - fx).astype(np.float32).view(np.uint32).reshape(pairs, nl)
+    sx = (fx[1::2] - fx[0::2]).astype(np.float32)
+    sy = (fy[1::2] - fy[0::2]).astype(np.float32)
+    sz = (fz[1::2] - fz[0::2]).astype(np.float32)
+    lp = nl // 2
+
+    def bits(a):
+        return a.view(np.uint32).reshape(pairs, lp)
+
+    SX, SY, SZ = bits(sx), bits(sy), bits(sz)
+    fin = (np.isfinite(sx) & np.isfinite(sy) & np.isfinite(sz)).reshape(pairs, lp)
+    shifted = (fin.all(axis=1) & np.all(SX == SX[:, :1], axis=1) & np.all(SY == SY[:, :1], axis=1)
+               & np.all(SZ == SZ[:, :1], axis=1))
+    both = (cls[0:2 * pairs:2] == 2) & (cls[1:2 * pairs:2] == 2)
+    # one step for the pair: the two units' first lines (each unit's lines
+    # share its step, as class 2 says)
+    common = step[:, 0] == step[:, nl // 2]
+    ok = both & common & shifted
+    if formed:
+        return ok
+    if not ok[0]:
+        return np.zeros(pairs, bool)
+    key = np.stack([step[:, 0], SX[:, 0], SY[:, 0], SZ[:, 0]], axis=1)
+    return ok & np.all(key == key[0], axis=1)
+
+
 def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16,
                          allow_lines: bool = True) -> tuple[float, float, float]:
     """Fractions of voxels by the F^H D gather path their unit takes (see

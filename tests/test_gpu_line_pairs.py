@@ -1,14 +1,16 @@
-"""The line-pair matrix-core instance of F^H D, through the C ABI.
+"""The line-pair matrix-core instances of F^H D, through the C ABI.
 
 Quads of four units whose lines of 128 voxels, two by two, are one line and
 the same line moved by a common offset d (rows of a grid along y, or the
 two halves of rows of 256 along x) are summed about each line pair's
-centre. Each case states which quads the instance takes (the host mirror
-of the classification, layout.line_pair_quads) and checks every voxel
-against the oracle; quads that break the structure fall back to the
-long-line instance. fhd_compute_noalloc forms the B operands itself and
-takes every quad with the structure: where both forms take the same quads
-its output is bitwise fhd_compute's.
+centre; so are unit pairs whose lines of 64 voxels pair up (rows of 64).
+Each case states which quads or pairs the instances take (the host mirror
+of the classification, layout.line_pair_quads / line_pair64_pairs) and
+checks every voxel against the oracle; groups that break the structure
+fall back to the long-line (or 64-voxel line) instance.
+fhd_compute_noalloc forms the B operands itself and takes every group with
+the structure: where both forms take the same groups its output is
+bitwise fhd_compute's.
 """
 import numpy as np
 import pytest
@@ -53,14 +55,26 @@ def run(case, dev, paths=binding.FHD_GATHER_ALL, noalloc=False):
     return rr.cpu().numpy(), ri.cpu().numpy()
 
 
-def bend_rows(case, first_line, count, amount):
-    """Moves lines first_line .. first_line + count - 1 (of 128 voxels) by
-    `amount` along y, breaking the common line-pair offset there."""
+def bend_rows(case, first_line, count, amount, line=128):
+    """Moves lines first_line .. first_line + count - 1 (of `line` voxels)
+    by `amount` along y, breaking the common line-pair offset there."""
     y = case["y"].copy()
     for ln in range(first_line, first_line + count):
-        y[ln * 128:(ln + 1) * 128] += np.float32(amount)
+        y[ln * line:(ln + 1) * line] += np.float32(amount)
     case["y"] = y
     return case
+
+
+def cases64():
+    # unit pairs of 64-voxel lines (the 64-voxel line-pair instance): one
+    # pair; two pairs, the second bent (the line instance there); the first
+    # bent (no pair in the table form, the second in the formed one)
+    yield "64x32x4", grid_case((64, 32, 4), 3001, 970), [True], [True]
+    yield "64x64x4", grid_case((64, 64, 4), 2048, 971), [True, True], [True, True]
+    c = bend_rows(grid_case((64, 64, 4), 2048, 972), 128 + 1, 1, 1.0 / 512, line=64)
+    yield "second pair bent", c, [True, False], [True, False]
+    c = bend_rows(grid_case((64, 64, 4), 2048, 973), 3, 1, 1.0 / 512, line=64)
+    yield "first pair bent", c, [False, False], [False, True]
 
 
 def cases():
@@ -107,3 +121,22 @@ def test_line_pairs_split_sums_repeatable(dev):
     ref = oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"],
                      case["x"][idx], case["y"][idx], case["z"][idx])
     assert metrics.rel_l2(a[0][idx], a[1][idx], *ref) <= TOL
+
+
+@pytest.mark.parametrize("name,case,taken,formed", list(cases64()), ids=[c[0] for c in cases64()])
+def test_64_voxel_line_pairs_match_the_oracle(dev, name, case, taken, formed):
+    cls = layout.gather_unit_classes(case["x"], case["y"], case["z"])[0]
+    assert np.all(cls == 2), (name, cls)
+    assert layout.line_pair64_pairs(case["x"], case["y"], case["z"], cls).tolist() == taken, name
+    assert layout.line_pair64_pairs(case["x"], case["y"], case["z"], cls, formed=True).tolist() == formed, name
+    ref = oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"], case["x"], case["y"], case["z"])
+    print("64-voxel line pairs: %s" % name, flush=True)
+    got = run(case, dev)
+    e = metrics.rel_l2(*got, *ref)
+    bf = metrics.rel_l2(*run(case, dev, binding.FHD_GATHER_BF16X3), *ref)
+    na = run(case, dev, noalloc=True)
+    e_na = metrics.rel_l2(*na, *ref)
+    print("  rel-L2 default %.3g, bf16x3 %.3g, noalloc %.3g" % (e, bf, e_na), flush=True)
+    assert e <= TOL and e_na <= TOL and bf <= TOL
+    if taken == formed:
+        assert np.array_equal(got[0], na[0]) and np.array_equal(got[1], na[1]), name

@@ -156,10 +156,25 @@ def test_lines_zero_step_and_degenerate_angles(dev):
     x, y, z = inputs.coords_from_axis(64, 16, 8, AX64)
     c = dict(kx=kx, ky=ky, kz=kz, Dr=Dr, Di=Di, x=x, y=y, z=z)
     check("degenerate angles", c, *gpu_fhd(c, dev))
+    # two units whose lines pair up (the 64-voxel line-pair instance): the
+    # voxels of a line are equal in exact arithmetic; the two halves of a
+    # line come from pair columns at +d/2 and -d/2, so they agree to
+    # rounding only
     c0 = dict(c, x=np.full_like(x, np.float32(0.125)))
     assert classes(c0) == [2, 2]
+    assert layout.line_pair64_pairs(c0["x"], c0["y"], c0["z"]).tolist() == [True]
     rr, ri = gpu_fhd(c0, dev)
-    check("zero step", c0, rr, ri)
+    check("zero step, line pairs", c0, rr, ri)
+    scale = np.sqrt(np.mean(rr.astype(np.float64) ** 2 + ri.astype(np.float64) ** 2))
+    assert np.max(np.abs(rr.reshape(-1, 64) - rr.reshape(-1, 64)[:, :1])) <= 1e-5 * scale
+    assert np.max(np.abs(ri.reshape(-1, 64) - ri.reshape(-1, 64)[:, :1])) <= 1e-5 * scale
+    # one unit (the 64-voxel line instance): every pair column has the same
+    # operands, so a line's voxels are equal bit for bit
+    xs, ys, zs = inputs.coords_from_axis(64, 16, 4, AX64)
+    c1 = dict(c, x=np.full_like(xs, np.float32(0.125)), y=ys, z=zs)
+    assert classes(c1) == [2]
+    rr, ri = gpu_fhd(c1, dev)
+    check("zero step, single unit", c1, rr, ri)
     assert np.all(rr.reshape(-1, 64) == rr.reshape(-1, 64)[:, :1])
     assert np.all(ri.reshape(-1, 64) == ri.reshape(-1, 64)[:, :1])
 

@@ -30,6 +30,8 @@ REL_L2_TOL = 5e-4
 LINES128 = ((128, 16, 4), (-0.5, 1.0 / 128, -0.5, 1.0 / 16, -0.5, 0.25))
 # 64 x 16 x 8: two units of 64-voxel lines (the 64-voxel instance)
 LINES64 = ((64, 16, 8), (-0.5, 1.0 / 64, -0.5, 1.0 / 16, -0.5, 0.125))
+# one unit of 64-voxel lines, no pair (the 64-voxel line instance)
+LINES64_SOLO = ((64, 16, 4), (-0.5, 1.0 / 64, -0.5, 1.0 / 16, -0.5, 0.25))
 # one quad of four units whose lines pair up (the line-pair instance):
 # rows of 128 one step apart along y, and rows of 256 (halves along x)
 PAIRS_Y = ((128, 32, 4), (-0.5, 1.0 / 128, -0.5, 1.0 / 32, -0.5, 0.25))
@@ -83,12 +85,16 @@ def forward(case, img, dev, paths):
     return Dr.cpu().numpy(), Di.cpu().numpy()
 
 
-@pytest.mark.parametrize("grid,cls,quads", [(LINES128, [3, 3], []), (LINES64, [2, 2], []),
-                                            (PAIRS_Y, [3, 3, 3, 3], [True]), (PAIRS_X, [3, 3, 3, 3], [True])])
-def test_adjoint_line_form_is_fp32_class(dev, grid, cls, quads):
+@pytest.mark.parametrize("grid,cls,quads,pairs64", [(LINES128, [3, 3], [], [False]),
+                                                    (LINES64, [2, 2], [], [True]),
+                                                    (LINES64_SOLO, [2], [], []),
+                                                    (PAIRS_Y, [3, 3, 3, 3], [True], [False, False]),
+                                                    (PAIRS_X, [3, 3, 3, 3], [True], [False, False])])
+def test_adjoint_line_form_is_fp32_class(dev, grid, cls, quads, pairs64):
     c = exact_phase_case(grid, 3001, seed=910)
     assert layout.gather_unit_classes(c["x"], c["y"], c["z"])[0].tolist() == cls
     assert layout.line_pair_quads(c["x"], c["y"], c["z"]).tolist() == quads
+    assert layout.line_pair64_pairs(c["x"], c["y"], c["z"]).tolist() == pairs64
     ref = oracle.fhd(c["kx"], c["ky"], c["kz"], c["Dr"], c["Di"], c["x"], c["y"], c["z"])
     err = {}
     for p in PATHS:
@@ -119,7 +125,7 @@ def test_forward_line_form_is_fp32_class(dev):
     assert err["bf16x3"] > 2.0 * err["vector"], err
 
 
-@pytest.mark.parametrize("grid", [LINES128, LINES64, PAIRS_Y])
+@pytest.mark.parametrize("grid", [LINES128, LINES64, LINES64_SOLO, PAIRS_Y])
 def test_amplitude_scaling_is_exact(dev, grid):
     """F^H (2^e D) = 2^e F^H D bit for bit on every path, for scales that
     move the largest |D| far outside fp16's range in both directions."""
