@@ -135,14 +135,14 @@ TRAFFIC = {
     "fhd_gather_kernel<16, true>": {
         "workload": "spiral128", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
         "bytes_per_launch": (54788.0 * 2.0 + 92160.0 * 1.0) * 1024},
+    "fhd_forward_pairs_kernel<true>": {
+        "workload": "spiral128", "sources": ["fhd_forward.hip", "fhd_internal.h"],
+        "sha256": "6b3fb860a684ab50eb8d4420ab7134edee83d3e2bfd0b54c31d83cf0a718fcc6",
+        "bytes_per_launch": (73924.4 * 2.0 + 5468.75 * 1.0) * 1024},
     "fhd_gather_patch64_kernel<true, true>": {
         "workload": "radial64", "sources": _GATHER_SRC,
         "sha256": "e1ee16a4e91cc4340cb87c2fdf1a00d467c7495ce78841ff9fff32ced098aca5",
         "bytes_per_launch": (20186.5 * 2.0 + 65536.0 * 1.0) * 1024},
-    "fhd_forward_lines_kernel<true>": {
-        "workload": "spiral128", "sources": ["fhd_forward.hip", "fhd_internal.h"],
-        "sha256": "180b23387c0e9b8650ba365c5376dbed83a7ab2e6d12011a9aa858a9d9722062",
-        "bytes_per_launch": (74996.0 * 2.0 + 8594.0 * 1.0) * 1024},
 }
 
 
@@ -230,7 +230,7 @@ def roofline_for(kernel: str, terms: float, kernel_ms: float, traffic, fractions
     rate = terms / (kernel_ms * 1e-3)
     out = {"kernel": kernel, "achieved": FLOP_PER_TERM * rate / 1e12, "unit": "TFLOP/s",
            "traffic": traffic, "flop_per_term": FLOP_PER_TERM}
-    if "lines" in kernel or "patch" in kernel:
+    if "lines" in kernel or "patch" in kernel or "pairs" in kernel:
         out.update(bound="mfma", peak=P_MFMA_F16 / 1e12,
                    executed={"flop_per_term": LINES_EXEC_FLOP_PER_TERM,
                              "tflops": LINES_EXEC_FLOP_PER_TERM * rate / 1e12,
@@ -513,11 +513,13 @@ def bench_other(args) -> int:
     axis = inputs.grid_axis_of(L)
     split = "false" if args.paths == "bf16x3" else "true"
     f_lines = args.paths != "vector" and layout.forward_lines_form(w["x"], w["y"], w["z"])
+    f_pairs = f_lines and layout.forward_pairs_form(w["x"], w["y"], w["z"])
     cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
     lp = layout.line_pair_quads(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
     lp64 = layout.line_pair64_pairs(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
     adj_kernel, adj_share = adjoint_kernel(cls, counts, args.paths, lp, lp64)
-    fwd_kernel = "fhd_forward_lines_kernel<%s>" % split if f_lines else "fhd_forward_gather_kernel<2>"
+    fwd_kernel = ("fhd_forward_pairs_kernel<%s>" % split if f_pairs else
+                  "fhd_forward_lines_kernel<%s>" % split if f_lines else "fhd_forward_gather_kernel<2>")
     out_r = torch.empty(max(N, M), device=dev)
     out_i = torch.empty(max(N, M), device=dev)
     grid_op = args.op in ("grid", "grid_bf16x3", "forward_grid", "normal_grid", "cg_grid")

@@ -220,8 +220,13 @@ int fhd_gather_paths(const void *packed, int M,
  * v dx rounded once; any x-fastest grid whose rows are a multiple of 128
  * voxels and whose voxel count is a multiple of 8192), F runs on the
  * matrix cores with fp32-class split-fp16 products (FHD_GATHER_ALL; each
- * line's operands scaled by its own power of two); otherwise on the
- * vector ALUs in fp32 (the form fhd_forward_pack / fhd_forward_gather
+ * line's operands scaled by its own power of two). When, beyond that, the
+ * lines 2i + 1 of every unit are the lines 2i moved by one common offset
+ * (bitwise equal differences of their first voxels' x, y, z; any such grid
+ * with an even number of rows per slice, or rows of 256), F sums each such
+ * line pair about its centre (one phasor per line pair and sample; each
+ * tile of 16 line pairs scaled by one power of two). Otherwise F runs on
+ * the vector ALUs in fp32 (the form fhd_forward_pack / fhd_forward_gather
  * always take). The choice is made on the device; the library allocates
  * its stream-ordered workspaces on `stream`.
  * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
@@ -234,8 +239,9 @@ int fhd_forward(const float *kx, const float *ky, const float *kz,
 /*
  * fhd_forward with a choice of paths: FHD_GATHER_ALL (identical to
  * fhd_forward), FHD_GATHER_VECTOR (the vector form always) or
- * FHD_GATHER_BF16X3 (the line form in split bf16 where it applies). Any
- * other value is FHD_ERR_INVALID_ARG; otherwise as fhd_forward.
+ * FHD_GATHER_BF16X3 (the line-pair or line form in split bf16 where it
+ * applies). Any other value is FHD_ERR_INVALID_ARG; otherwise as
+ * fhd_forward.
  */
 int fhd_forward_paths(const float *kx, const float *ky, const float *kz,
                       const float *x, const float *y, const float *z,
@@ -483,6 +489,7 @@ int fhd_compute_noalloc(const float *kx, const float *ky, const float *kz,
  * for 64-voxel line pairs), "fhd_gather_long_lines_kernel<true>" (split
  * fp16) or "<false>" (split bf16), "fhd_gather_lines_kernel<true>"/"<false>",
  * "fhd_gather_kernel<16, true>" (one-step ramps) or "<16, false>",
+ * "fhd_forward_pairs_kernel<true>"/"<false>" (line pairs),
  * "fhd_forward_lines_kernel<true>"/"<false>",
  * "fhd_forward_gather_kernel<2>", "fhd_grid_kernel",
  * "fhd_grid_bf16x3_kernel<4>"/"<2>", "fhd_forward_grid_bf16x3_kernel".

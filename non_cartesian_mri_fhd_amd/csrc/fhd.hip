@@ -543,8 +543,8 @@ __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (
 // gather instances) per unit, both tested at once: cls[u] = the class of
 // unit u (never a matrix-core class unless allow_lines); the first pair's
 // workgroup also records whether that pair is of class kClassLongPair
-// (info[0]) and its lines' step (info[1], bits), and clears info[2] (a flag
-// the forward operator's line pre-pass sets). Two barriers: one to publish
+// (info[0]) and its lines' step (info[1], bits), and clears info[2] and
+// info[3] (flags the forward operator's line and line-pair pre-passes set). Two barriers: one to publish
 // each unit's first-lane steps, one to combine the waves' votes.
 //
 // With `patches` set, the workgroup also records in patches[2 b] and
@@ -689,6 +689,7 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
             info[0] = pair ? 1 : 0;
             info[1] = (int)__float_as_uint(wg_step[0][2]);
             info[2] = 0;
+            info[3] = 0;
         }
         if (patches) {
             // 1: 128-voxel line pairs (a long pair); 2: 64-voxel line pairs

@@ -441,6 +441,7 @@ __global__ __launch_bounds__(kFwdBlock) void fhd_forward_lines_pack_kernel(
     const float *__restrict__ rho_r, const float *__restrict__ rho_i, const int *__restrict__ cls,
     int *__restrict__ info, u32x4 *__restrict__ tiles)
 {
+    if (pairs_form_ran(info)) return;   // the line-pair form took F
     const int s = threadIdx.x >> 6, lane = threadIdx.x & 63, row = lane & 15, quarter_k = lane >> 4;
     const int64_t base = ((int64_t)blockIdx.x * kFwdTileLines + row) * kLongLineVox;
     const bool sine = s >= kFwdKSteps / 2;   // K >= 64: the S part
@@ -510,7 +511,8 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
     float *__restrict__ out_r, float *__restrict__ out_i, int M)
 {
-    if (!lines_form_ran(info)) return;   // the vector form takes F
+    // the vector form takes F, or the line-pair form took it
+    if (!lines_form_ran(info) || pairs_form_ran(info)) return;
     __shared__ u32x4 stage[2][kFwdTileVec4];
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -648,6 +650,275 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// F on line pairs, on the matrix cores
+// ---------------------------------------------------------------------------
+// When, beyond the line form's rule, the lines 2i + 1 of every unit are
+// the lines 2i moved by one offset d, the same throughout (the line-pair
+// records of the classification: flag 1 in every unit pair, with pair 0's
+// step and offset), each line pair sums about its centre c = x_c(2i) +
+// d / 2. Its voxels lie at c + sigma (d / 2 + o_j) and c - sigma (d / 2 +
+// o_j) with o_j = (j + 1/2) dx e_x, j < 64, and sigma = +1 (side 0: line
+// 2i + 1 from its centre up, line 2i from its centre down) or -1 (side 1:
+// the other halves). With rho+ and rho- the two voxels of (side, j),
+//
+//   D_m = sum_pairs conj(V) sum_{side, j} (P C - i Q S),
+//   V = exp(i 2 pi k_m . c),  P, Q = rho+ +- rho-,
+//   C, S = cos, sin(2 pi k_m . (sigma d / 2 + o_j)),
+//
+// the line form's products with K = 2 x 128 per line pair instead of
+// 2 x 64 per line: the same matrix-core work per term, and half the phasor
+// work (one V per line pair and sample).
+//
+// fhd_forward_pairs_pack_kernel forms A in tiles of 16 line pairs (one
+// unit; K = 32 s + 8 (l / 16) + i: cos part for K < 128, then sin; side
+// (K / 64) % 2; j = K % 64) and checks the rule; fhd_forward_pairs_kernel
+// walks the tiles with each wave's B (both sides) in registers. In the
+// fp16 form a tile's operands share one power-of-two scale (the tile's
+// largest |value| times 2^sh in [2^14, 2^15)), undone once per tile.
+constexpr int kFwpTilePairs = 16;
+constexpr int kFwpKSteps = 2 * 2 * kFwdPairs / 32;      // 8 products of K = 32
+constexpr int kFwpOpsVec4 = kFwpKSteps * 4 * 64;
+constexpr int kFwpTileVec4 = kFwpOpsVec4 + kFwpTilePairs;   // then (c_x, c_y, c_z, sh) per pair
+static_assert(2 * kFwpTilePairs * kLongLineVox == kUnitVox, "a tile of line pairs is one unit");
+static_assert(kFwpKSteps == 2 * (kFwdBlock / 64), "two k steps per pre-pass wave");
+
+// One workgroup per unit (tile): wave w forms k steps 2 w and 2 w + 1
+// (lane l: line pair l % 16), the first 16 lanes of wave 0 the pairs'
+// centres; the first lane checks the unit's record against pair 0's and,
+// when they differ, sets info[3] (the line-pair form then stands aside).
+template <bool F16>
+__global__ __launch_bounds__(kFwdBlock) void fhd_forward_pairs_pack_kernel(
+    const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
+    const float *__restrict__ rho_r, const float *__restrict__ rho_i, const int *__restrict__ cls,
+    const int4 *__restrict__ patches, int *__restrict__ info, u32x4 *__restrict__ tiles)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, row = lane & 15, quarter_k = lane >> 4;
+    const int64_t unit = blockIdx.x;
+    const int64_t line_a = unit * kUnitVox + (int64_t)(2 * row) * kLongLineVox, line_b = line_a + kLongLineVox;
+    float re[2][kChunk], im[2][kChunk];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int s = 2 * w + h;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const int K = 32 * s + 8 * quarter_k + i;
+            const bool sine = K >= 2 * kFwdPairs, side1 = ((K / kFwdPairs) & 1) != 0;
+            const int j = K % kFwdPairs;
+            const int64_t up = (side1 ? line_a : line_b) + kFwdPairs + j;
+            const int64_t dn = (side1 ? line_b : line_a) + kFwdPairs - 1 - j;
+            const float ur = rho_r[up], ui = rho_i[up], dr = rho_r[dn], di = rho_i[dn];
+            re[h][i] = sine ? ui - di : ur + dr;   // Q_i | P_r
+            im[h][i] = sine ? dr - ur : ui + di;   // -Q_r | P_i
+        }
+    }
+    int sh = 0;
+    if constexpr (F16) {
+        // the tile's largest magnitude: the lane's values, the wave, the
+        // four waves (LDS)
+        __shared__ unsigned wave_max[kFwdBlock / 64];
+        unsigned m = 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const unsigned a = __float_as_uint(re[h][i]) & 0x7fffffffu;
+                const unsigned b = __float_as_uint(im[h][i]) & 0x7fffffffu;
+                m = a > m ? a : m;
+                m = b > m ? b : m;
+            }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned t = (unsigned)__shfl_xor((int)m, o);
+            m = t > m ? t : m;
+        }
+        if (lane == 0) wave_max[w] = m;
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < kFwdBlock / 64; ++v) m = wave_max[v] > m ? wave_max[v] : m;
+        sh = amp_shift(m);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                re[h][i] = __builtin_ldexpf(re[h][i], sh);
+                im[h][i] = __builtin_ldexpf(im[h][i], sh);
+            }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        unsigned rh[4], rl[4], ih[4], il[4];
+        split_parts<F16, kChunk>(re[h], rh, rl);
+        split_parts<F16, kChunk>(im[h], ih, il);
+        u32x4 *t = tiles + unit * kFwpTileVec4 + (2 * w + h) * 4 * 64 + lane;
+        t[0 * 64] = (u32x4){rh[0], rh[1], rh[2], rh[3]};
+        t[1 * 64] = (u32x4){rl[0], rl[1], rl[2], rl[3]};
+        t[2 * 64] = (u32x4){ih[0], ih[1], ih[2], ih[3]};
+        t[3 * 64] = (u32x4){il[0], il[1], il[2], il[3]};
+    }
+    const int4 r0 = patches[2 * (unit / 2)], r1 = patches[2 * (unit / 2) + 1];
+    if (w == 0 && quarter_k == 0) {
+        const float dx = __int_as_float(r0.y);
+        const float cx = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x[line_a]) + 0.5f * __int_as_float(r1.x);
+        const float cy = y[line_a] + 0.5f * __int_as_float(r1.y), cz = z[line_a] + 0.5f * __int_as_float(r1.z);
+        tiles[unit * kFwpTileVec4 + kFwpOpsVec4 + row] =
+            (u32x4){__float_as_uint(cx), __float_as_uint(cy), __float_as_uint(cz), (unsigned)sh};
+    }
+    if (threadIdx.x == 0) {
+        const int4 q0 = patches[0], q1 = patches[1];
+        const bool ok = info[0] != 0 && cls[unit] == kClassLongPair && r0.x == 1 && q0.x == 1 &&
+                        r0.y == info[1] && r0.y == q0.y && r1.x == q1.x && r1.y == q1.y && r1.z == q1.z;
+        if (!ok) atomicOr(&info[3], 1);
+    }
+}
+
+// Workgroup b, split s: samples b kFwdBlockSamples .. + 127 as in the line
+// form (wave w the 32 from 32 w, two 16-sample columns), the tiles of
+// split s of the line-pair stream, staged into LDS by buffer loads (two
+// buffers); writes D (splits == 1) or its partial sums at out + s M.
+template <bool F16>
+__global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(2))) void fhd_forward_pairs_kernel(
+    const u32x4 *__restrict__ tiles, int ntiles, int splits, const int *__restrict__ info,
+    const int4 *__restrict__ patches, const float *__restrict__ kx, const float *__restrict__ ky,
+    const float *__restrict__ kz, float *__restrict__ out_r, float *__restrict__ out_i, int M)
+{
+    if (!pairs_form_ran(info)) return;
+    __shared__ u32x4 stage[2][kFwpTileVec4];
+    const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int4 r0 = patches[0], r1 = patches[1];
+    const float hdx = 0.5f * __int_as_float(r0.y);
+    const float ddx = __int_as_float(r1.x), ddy = __int_as_float(r1.y), ddz = __int_as_float(r1.z);
+
+    int64_t m[kFwdColumns];
+    float skx[kFwdColumns], sky[kFwdColumns], skz[kFwdColumns];
+#pragma unroll
+    for (int t = 0; t < kFwdColumns; ++t) {
+        m[t] = (int64_t)blockIdx.x * kFwdBlockSamples + wave * 16 * kFwdColumns + t * 16 + col;
+        const bool live = m[t] < M;   // samples past M compute with k = 0 and are not stored
+        skx[t] = live ? kx[m[t]] : 0.0f;
+        sky[t] = live ? ky[m[t]] : 0.0f;
+        skz[t] = live ? kz[m[t]] : 0.0f;
+    }
+    // B operands, held for the whole walk: K = 32 s + 8 (l / 16) + i,
+    // cos (K < 128) or sin of 2 pi (kx (j + 1/2) dx +- k . d / 2), j = K % 64,
+    // + for side 0 ((K / 64) % 2 == 0)
+    u32x4 bh[kFwdColumns][kFwpKSteps], bl[kFwdColumns][kFwpKSteps];
+#pragma unroll
+    for (int t = 0; t < kFwdColumns; ++t) {
+        const float hd = 0.5f * __builtin_fmaf(skx[t], ddx, __builtin_fmaf(sky[t], ddy, skz[t] * ddz));
+#pragma unroll
+        for (int s = 0; s < kFwpKSteps; ++s) {
+            float v[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const int K = 32 * s + 8 * quarter_k + i;
+                const int j = K % kFwdPairs;
+                const bool side1 = ((K / kFwdPairs) & 1) != 0;
+                const float a = __builtin_fmaf(skx[t], (float)(2 * j + 1) * hdx, side1 ? -hd : hd);
+                v[i] = K < 2 * kFwdPairs ? __builtin_amdgcn_cosf(a) : __builtin_amdgcn_sinf(a);
+            }
+            unsigned h[4], l[4];
+            split_parts<F16, kChunk>(v, h, l);
+            bh[t][s] = (u32x4){h[0], h[1], h[2], h[3]};
+            bl[t][s] = (u32x4){l[0], l[1], l[2], l[3]};
+        }
+    }
+
+    float dr[kFwdColumns], di[kFwdColumns];
+#pragma unroll
+    for (int t = 0; t < kFwdColumns; ++t) {
+        dr[t] = 0.0f;
+        di[t] = 0.0f;
+    }
+    const int per = (ntiles + splits - 1) / splits;
+    const int t0 = min(ntiles, (int)blockIdx.y * per), t1 = min(ntiles, t0 + per);
+    const float4 *src = reinterpret_cast<const float4 *>(tiles);
+    const int64_t total_vec4 = (int64_t)ntiles * kFwpTileVec4;
+    if (t0 < t1) issue_stage_load<kFwdBlock, kFwpTileVec4>(src, total_vec4, t0, reinterpret_cast<float4 *>(stage[0]));
+    int b = 0;
+    for (int tau = t0; tau < t1; ++tau) {
+        // tile tau is in stage[b] once every wave's copies have landed; the
+        // other buffer was last read before this barrier
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        if (tau + 1 < t1)
+            issue_stage_load<kFwdBlock, kFwpTileVec4>(src, total_vec4, tau + 1,
+                                                      reinterpret_cast<float4 *>(stage[b ^ 1]));
+        float4v tre[kFwdColumns], tim[kFwdColumns];
+#pragma unroll
+        for (int t = 0; t < kFwdColumns; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                tre[t][r] = 0.0f;
+                tim[t][r] = 0.0f;
+            }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < kFwpKSteps; ++s) {
+            const u32x4 *op = &stage[b][s * 4 * 64 + lane];
+            const u32x4 arh = op[0 * 64], arl = op[1 * 64], aih = op[2 * 64], ail = op[3 * 64];
+#pragma unroll
+            for (int t = 0; t < kFwdColumns; ++t) {
+                tre[t] = mfma16<F16>(arh, bh[t][s], tre[t]);
+                tim[t] = mfma16<F16>(aih, bh[t][s], tim[t]);
+                tre[t] = mfma16<F16>(arh, bl[t][s], tre[t]);
+                tim[t] = mfma16<F16>(aih, bl[t][s], tim[t]);
+                tre[t] = mfma16<F16>(arl, bh[t][s], tre[t]);
+                tim[t] = mfma16<F16>(ail, bh[t][s], tim[t]);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        // D += 2^-sh conj(V) T over rows 4 (l / 16) + r (line pairs), V of
+        // each pair's centre
+        float tdr[kFwdColumns], tdi[kFwdColumns];
+#pragma unroll
+        for (int t = 0; t < kFwdColumns; ++t) {
+            tdr[t] = 0.0f;
+            tdi[t] = 0.0f;
+        }
+        int sh = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const u32x4 c = stage[b][kFwpOpsVec4 + 4 * quarter_k + r];
+            const float cx = __uint_as_float(c.x), cy = __uint_as_float(c.y), cz = __uint_as_float(c.z);
+            sh = (int)c.w;
+#pragma unroll
+            for (int t = 0; t < kFwdColumns; ++t) {
+                const float p = __builtin_fmaf(skx[t], cx, __builtin_fmaf(sky[t], cy, skz[t] * cz));
+                const float vc = __builtin_amdgcn_cosf(p), vs = __builtin_amdgcn_sinf(p);
+                tdr[t] = __builtin_fmaf(vc, tre[t][r], __builtin_fmaf(vs, tim[t][r], tdr[t]));
+                tdi[t] = __builtin_fmaf(vc, tim[t][r], __builtin_fmaf(-vs, tre[t][r], tdi[t]));
+            }
+        }
+        const float scale = unscale<F16>(1.0f, sh);
+#pragma unroll
+        for (int t = 0; t < kFwdColumns; ++t) {
+            dr[t] = __builtin_fmaf(tdr[t], scale, dr[t]);
+            di[t] = __builtin_fmaf(tdi[t], scale, di[t]);
+        }
+        b ^= 1;
+    }
+
+    // each column's four row groups (lanes col + 16 q) add up
+#pragma unroll
+    for (int t = 0; t < kFwdColumns; ++t) {
+        dr[t] += __shfl_xor(dr[t], 16);
+        di[t] += __shfl_xor(di[t], 16);
+        dr[t] += __shfl_xor(dr[t], 32);
+        di[t] += __shfl_xor(di[t], 32);
+    }
+    if (quarter_k == 0) {
+        float *dst_r = out_r + (int64_t)blockIdx.y * M, *dst_i = out_i + (int64_t)blockIdx.y * M;
+#pragma unroll
+        for (int t = 0; t < kFwdColumns; ++t)
+            if (m[t] < M) {
+                dst_r[m[t]] = dr[t];
+                dst_i[m[t]] = di[t];
+            }
+    }
+}
+
 }  // namespace
 
 int launch_forward_pack(const float *x, const float *y, const float *z, const float *rho_r,
@@ -695,6 +966,26 @@ int launch_forward_gather(const float *packed, int N, const float *kx, const flo
 }
 
 
+// The line-pair form's pre-pass and gather of one split type (F16: fp16
+// parts).
+template <bool F16>
+int launch_forward_pairs(const float *x, const float *y, const float *z, const float *rho_r,
+                         const float *rho_i, const int *cls, const int4 *patches, int *info, u32x4 *tiles,
+                         int64_t units, int64_t blocks, int splits, const float *kx, const float *ky,
+                         const float *kz, float *part_r, float *part_i, int M, hipStream_t stream)
+{
+    fhd_forward_pairs_pack_kernel<F16><<<dim3((unsigned)units), dim3(kFwdBlock), 0, stream>>>(
+        x, y, z, rho_r, rho_i, cls, patches, info, tiles);
+    int rc = launch_status("fhd_forward_pairs_pack_kernel launch");
+    if (rc == FHD_OK) {
+        TimedLaunch timed(F16 ? "fhd_forward_pairs_kernel<true>" : "fhd_forward_pairs_kernel<false>", stream);
+        fhd_forward_pairs_kernel<F16><<<dim3((unsigned)blocks, (unsigned)splits), dim3(kFwdBlock), 0, stream>>>(
+            tiles, (int)units, splits, info, patches, kx, ky, kz, part_r, part_i, M);
+        rc = launch_status("fhd_forward_pairs_kernel launch");
+    }
+    return rc;
+}
+
 // The line form's pre-pass and gather of one split type (F16: fp16 parts).
 template <bool F16>
 int launch_forward_lines(const float *x, const float *y, const float *z, const float *rho_r,
@@ -726,46 +1017,60 @@ int launch_forward(const float *x, const float *y, const float *z, const float *
     }
     const int64_t units = N / kUnitVox, ntiles = N / kFwdTileVox;
     const int64_t blocks = ((int64_t)M + kFwdBlockSamples - 1) / kFwdBlockSamples;
+    // workgroups per CU of the line-pair gather (the split count's, shared
+    // with the line form, which stands in when the line-pair rule fails)
     static int per_cu_cache[64] = {0};
-    int dev = 0, per_cu = 3;
+    int dev = 0, per_cu = 2;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
         if (per_cu_cache[dev] == 0) {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, reinterpret_cast<const void *>(fhd_forward_lines_kernel<true>), kFwdBlock, 0) != hipSuccess ||
+                    &n, reinterpret_cast<const void *>(fhd_forward_pairs_kernel<true>), kFwdBlock, 0) != hipSuccess ||
                 n < 1)
-                n = 3;
+                n = 2;
             per_cu_cache[dev] = n;
         }
         per_cu = per_cu_cache[dev];
     }
-    // cut the line stream so the sample blocks fill whole rounds (each part
-    // at least one tile)
-    const int splits = split_count(blocks, (int)(ntiles * kStageChunks), per_cu);
-    // one workspace: unit classes and the flag words | line tiles | partials
+    // cut the tile stream so the sample blocks fill whole rounds (each part
+    // at least one line-pair tile, two line tiles)
+    const int splits = split_count(blocks, (int)(units * kStageChunks), per_cu);
+    // one workspace: unit classes and the flag words | line-pair records |
+    // tiles (either form's) | partials
     const size_t cls_bytes = ((size_t)units * sizeof(int) + kInfoWords * sizeof(int) + 255) / 256 * 256;
-    const size_t tile_bytes = (size_t)ntiles * kFwdTileVec4 * sizeof(u32x4);
+    const size_t rec_bytes = ((size_t)units * sizeof(int4) + 255) / 256 * 256;
+    const size_t line_tile_bytes = (size_t)ntiles * kFwdTileVec4 * sizeof(u32x4);
+    const size_t pair_tile_bytes = (size_t)units * kFwpTileVec4 * sizeof(u32x4);
+    const size_t tile_bytes = line_tile_bytes > pair_tile_bytes ? line_tile_bytes : pair_tile_bytes;
     const size_t part_bytes = splits > 1 ? (size_t)splits * 2 * M * sizeof(float) : 0;
     StreamBuffer buf(stream, kSlotForward);
     char *work = nullptr;
-    int rc = buf.get(cls_bytes + tile_bytes + part_bytes, &work);
+    int rc = buf.get(cls_bytes + rec_bytes + tile_bytes + part_bytes, &work);
     if (rc != FHD_OK) return rc;
     int *cls = reinterpret_cast<int *>(work), *info = cls + units;
-    u32x4 *tiles = reinterpret_cast<u32x4 *>(work + cls_bytes);
+    int4 *patches = reinterpret_cast<int4 *>(work + cls_bytes);
+    u32x4 *tiles = reinterpret_cast<u32x4 *>(work + cls_bytes + rec_bytes);
     float *part_r = Dr, *part_i = Di;
     if (splits > 1) {
-        part_r = reinterpret_cast<float *>(work + cls_bytes + tile_bytes);
+        part_r = reinterpret_cast<float *>(work + cls_bytes + rec_bytes + tile_bytes);
         part_i = part_r + (int64_t)splits * M;
     }
-    rc = launch_classify(x, y, z, N, true, cls, info, stream);
+    rc = launch_classify(x, y, z, N, true, cls, info, stream, false, nullptr, 0, patches);
+    // the line-pair form, else the line form (each stands aside when the
+    // other runs or its rule fails), with one split count
+    const bool f16 = paths != FHD_GATHER_BF16X3;
     if (rc == FHD_OK)
-        rc = paths == FHD_GATHER_BF16X3
-                 ? launch_forward_lines<false>(x, y, z, rho_r, rho_i, cls, info, tiles, ntiles, blocks, splits, kx,
-                                               ky, kz, part_r, part_i, M, stream)
-                 : launch_forward_lines<true>(x, y, z, rho_r, rho_i, cls, info, tiles, ntiles, blocks, splits, kx,
-                                              ky, kz, part_r, part_i, M, stream);
+        rc = f16 ? launch_forward_pairs<true>(x, y, z, rho_r, rho_i, cls, patches, info, tiles, units, blocks,
+                                              splits, kx, ky, kz, part_r, part_i, M, stream)
+                 : launch_forward_pairs<false>(x, y, z, rho_r, rho_i, cls, patches, info, tiles, units, blocks,
+                                               splits, kx, ky, kz, part_r, part_i, M, stream);
+    if (rc == FHD_OK)
+        rc = f16 ? launch_forward_lines<true>(x, y, z, rho_r, rho_i, cls, info, tiles, ntiles, blocks, splits, kx,
+                                              ky, kz, part_r, part_i, M, stream)
+                 : launch_forward_lines<false>(x, y, z, rho_r, rho_i, cls, info, tiles, ntiles, blocks, splits, kx,
+                                               ky, kz, part_r, part_i, M, stream);
     if (rc == FHD_OK && splits > 1) rc = launch_reduce(part_r, part_i, splits, M, Dr, Di, stream, info, true);
-    // the vector form, which stands aside when the line form ran
+    // the vector form, which stands aside when either matrix-core form ran
     if (rc == FHD_OK) rc = launch_forward_pack(x, y, z, rho_r, rho_i, N, vox, stream, info);
     if (rc == FHD_OK) rc = launch_forward_gather(vox, N, kx, ky, kz, Dr, Di, M, stream, info);
     const int f = buf.finish();

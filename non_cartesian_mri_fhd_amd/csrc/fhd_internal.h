@@ -439,10 +439,15 @@ int launch_pack(const float *kx, const float *ky, const float *kz, const float *
 // stand aside): info as launch_classify leaves it, with info[2] set by the
 // line pre-pass when some line breaks the rule.
 __device__ __forceinline__ bool lines_form_ran(const int *info) { return info[0] != 0 && info[2] == 0; }
+// Whether its line-pair form ran (the line form then stands aside too):
+// info[3] set by the line-pair pre-pass when some unit breaks that form's
+// rule.
+__device__ __forceinline__ bool pairs_form_ran(const int *info) { return info[0] != 0 && info[3] == 0; }
 
 // Classes of the ceil(N / kUnitVox) units into cls; info[0] = 1 if the
 // first pair is of class kClassLongPair, info[1] its step's bits, info[2]
-// = 0 (stream-ordered; allow_lines = false gives no matrix-core class).
+// = info[3] = 0 (stream-ordered; allow_lines = false gives no matrix-core
+// class).
 // With amp_slots, also the amplitude slots info[4 .. 4 + kAmpSlots) of
 // the packed k-space of M samples (zeros when M = 0; info holds kInfoWords
 // words). With patches (two int4 per unit pair), also each pair's

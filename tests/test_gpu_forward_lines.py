@@ -1,11 +1,16 @@
-"""GPU parity of the forward operator F in its matrix-core line form (every
-aligned pair of 4096-voxel units is lines of 128 voxels along x with one
-step) against the fp64 oracle, against the vector form on the same voxels,
-and through adjointness with F^H D.
+"""GPU parity of the forward operator F in its matrix-core forms against
+the fp64 oracle, against each other and the vector form on the same
+voxels, and through adjointness with F^H D. The line form takes F when
+every aligned pair of 4096-voxel units is lines of 128 voxels along x with
+one step; the line-pair form when, beyond that, the lines 2i + 1 are the
+lines 2i moved by one common offset (rows one step apart, or the halves of
+rows of 256). Swapping the rows two by two keeps the line form's rule and
+breaks the line-pair form's.
 
 Gate as in test_gpu_parity: relative L2 <= 5e-4 and every element within
-10x that bound times the reference's rms. The line form computes in split
-bf16 (three bf16 products per fp32 product, fp32 accumulation).
+10x that bound times the reference's rms. Both forms compute in split
+fp16 by default (three fp16 products per fp32 product, fp32
+accumulation).
 """
 import numpy as np
 import pytest
@@ -58,24 +63,57 @@ def all_long_pairs(x, y, z):
     return cls.size > 0 and bool(np.all(cls == 3))
 
 
+def swap_rows(n):
+    """Voxel order with the 128-voxel rows swapped two by two (rows 0, 1,
+    3, 2, 4, 5, 7, 6, ...): line pairs (2i, 2i + 1) then alternate between
+    two offsets."""
+    rows = np.arange(n // 128)
+    rows[2::4], rows[3::4] = rows[3::4].copy(), rows[2::4].copy()
+    return (rows[:, None] * 128 + np.arange(128)).reshape(-1)
+
+
+@pytest.mark.parametrize("form", ["pairs", "lines"])
 @pytest.mark.parametrize("shape,axis,M", [
     ((128, 16, 4), AX128, 3000),                                           # one pair of units
     ((256, 16, 6), (-0.5, 1.0 / 256, -0.5, 1.0 / 16, -0.5, 1.0 / 6), 1000),   # 3 pairs, half rows
     ((128, 32, 2), (0.25, -1.0 / 128, -0.5, 1.0 / 32, 0.0, 0.5), 129),      # negative step, ragged M
     ((128, 16, 4), AX128, 1),
 ])
-def test_forward_lines_grids(dev, shape, axis, M):
+def test_forward_lines_grids(dev, shape, axis, M, form):
     x, y, z = inputs.coords_from_axis(*shape, axis)
+    if form == "lines":
+        perm = swap_rows(x.size)
+        x, y, z = x[perm], y[perm], z[perm]
     assert all_long_pairs(x, y, z)
+    assert layout.forward_pairs_form(x, y, z) == (form == "pairs")
     k = inputs.random_case(1, M, seed=sum(shape) + M, kmax=shape[0] / 2.0)
     img = inputs.random_image(x.size, seed=M + 5)
-    check("forward lines %s M=%d" % (shape, M), k, x, y, z, img, *gpu_forward(k, x, y, z, img, dev))
+    check("forward %s %s M=%d" % (form, shape, M), k, x, y, z, img, *gpu_forward(k, x, y, z, img, dev))
+
+
+def test_forward_pairs_against_line_form(dev):
+    """The same voxels and image in row order (the line-pair form) and with
+    the rows swapped two by two (the line form) give the same D to
+    rounding, not bitwise (one phasor per line pair against one per line)."""
+    k = inputs.make_kspace("spiral32")
+    x, y, z = inputs.coords_from_axis(128, 32, 4, (-0.5, 1.0 / 128, -0.5, 1.0 / 32, -0.5, 0.25))
+    img = inputs.random_image(x.size, seed=33)
+    perm = swap_rows(x.size)
+    assert layout.forward_pairs_form(x, y, z)
+    assert layout.forward_lines_form(x[perm], y[perm], z[perm])
+    assert not layout.forward_pairs_form(x[perm], y[perm], z[perm])
+    a = gpu_forward(k, x, y, z, img, dev)
+    b = gpu_forward(k, x[perm], y[perm], z[perm], (img[0][perm], img[1][perm]), dev)
+    check("line-pair form", k, x, y, z, img, *a)
+    diff = metrics.rel_l2(a[0], a[1], b[0].astype(np.float64), b[1].astype(np.float64))
+    print("line-pair vs line form: rel diff %.2e" % diff)
+    assert 0 < diff < 2e-5
 
 
 def test_forward_lines_against_vector_form(dev):
-    """Rows of 128 (the line form) and the same voxels with the two halves
-    of every row swapped (64-voxel lines only: the vector form) meet the
-    oracle gate and agree to rounding, not bitwise."""
+    """Rows of 128 (the line-pair form) and the same voxels with the two
+    halves of every row swapped (64-voxel lines only: the vector form) meet
+    the oracle gate and agree to rounding, not bitwise."""
     k = inputs.make_kspace("spiral32")
     x, y, z = inputs.coords_from_axis(128, 16, 4, AX128)
     perm = np.arange(x.size).reshape(-1, 2, 64)[:, ::-1, :].reshape(-1)
@@ -84,10 +122,10 @@ def test_forward_lines_against_vector_form(dev):
     assert all_long_pairs(x, y, z) and not all_long_pairs(x[perm], y[perm], z[perm])
     a = gpu_forward(k, x, y, z, img, dev)
     b = gpu_forward(k, x[perm], y[perm], z[perm], pimg, dev)
-    check("line form", k, x, y, z, img, *a)
+    check("line-pair form", k, x, y, z, img, *a)
     check("vector form", k, x[perm], y[perm], z[perm], pimg, *b)
     diff = metrics.rel_l2(a[0], a[1], b[0].astype(np.float64), b[1].astype(np.float64))
-    print("line vs vector form: rel diff %.2e" % diff)
+    print("line-pair vs vector form: rel diff %.2e" % diff)
     assert 0 < diff < 1e-4
 
 
@@ -110,8 +148,9 @@ def test_forward_lines_fall_back_on_a_second_step(dev):
 
 
 def test_forward_lines_adjointness_and_normal(dev):
-    """<F^H D, rho> = <D, F rho> with both operators in their line forms,
-    and F^H F p against the oracle's composition."""
+    """<F^H D, rho> = <D, F rho> with both operators in their line forms
+    (F in its line-pair form), and F^H F p against the oracle's
+    composition."""
     x, y, z = inputs.coords_from_axis(128, 16, 4, AX128)
     c = inputs.random_case(1, 2000, seed=41, kmax=32.0)
     img = inputs.random_image(x.size, seed=42)

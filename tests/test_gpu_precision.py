@@ -108,9 +108,18 @@ def test_adjoint_line_form_is_fp32_class(dev, grid, cls, quads, pairs64):
     assert err["bf16x3"] > 2.0 * err["vector"], err
 
 
-def test_forward_line_form_is_fp32_class(dev):
+@pytest.mark.parametrize("form", ["pairs", "lines"])
+def test_forward_line_form_is_fp32_class(dev, form):
     c = exact_phase_case(LINES128, 2003, seed=911)
+    if form == "lines":
+        # rows swapped two by two: the line form (the line-pair form's
+        # common offset broken)
+        rows = np.arange(c["x"].size // 128)
+        rows[2::4], rows[3::4] = rows[3::4].copy(), rows[2::4].copy()
+        perm = (rows[:, None] * 128 + np.arange(128)).reshape(-1)
+        c = dict(c, x=c["x"][perm], y=c["y"][perm], z=c["z"][perm])
     assert layout.forward_lines_form(c["x"], c["y"], c["z"])
+    assert layout.forward_pairs_form(c["x"], c["y"], c["z"]) == (form == "pairs")
     # an image of dyadic values: rho enters the sums exactly
     rng = np.random.default_rng(912)
     img = tuple((rng.integers(-512, 512, c["x"].size) / 256.0).astype(np.float32) for _ in range(2))
@@ -119,7 +128,7 @@ def test_forward_line_form_is_fp32_class(dev):
     for p in PATHS:
         Dr, Di = forward(c, img, dev, p)
         err[p] = metrics.rel_l2(Dr, Di, *ref)
-    print("exact phases, F on 128-voxel lines: rel-L2 %s" % err, flush=True)
+    print("exact phases, F on 128-voxel lines (%s form): rel-L2 %s" % (form, err), flush=True)
     assert max(err.values()) <= REL_L2_TOL
     assert err["all"] <= 2.0 * err["vector"], err
     assert err["bf16x3"] > 2.0 * err["vector"], err

@@ -126,3 +126,27 @@ def test_forward_lines_form_mirror():
     xx, yy, zz = (np.concatenate((a, b)) for a, b in zip((x, y, z), gb))
     assert not layout.forward_lines_form(xx, yy, zz)
     assert not layout.forward_lines_form(x[:4096], y[:4096], z[:4096])
+
+
+def test_forward_pairs_form_mirror():
+    """fhd_forward's line-pair form: the line form, and lines 2i + 1 the
+    lines 2i moved by one offset throughout (rows one step apart along y,
+    or the halves of rows of 256); rows swapped two by two, a bent row or a
+    second offset fall back to the line form."""
+    from non_cartesian_mri_fhd_amd import inputs
+    ax = (-0.5, 1.0 / 128, -0.5, 1.0 / 16, 0.0, 0.25)
+    x, y, z = inputs.coords_from_axis(128, 16, 4, ax)
+    assert layout.forward_pairs_form(x, y, z)
+    h = inputs.coords_from_axis(256, 16, 2, (-0.5, 1.0 / 256, -0.5, 1.0 / 16, 0.0, 0.5))
+    assert layout.forward_pairs_form(*h)
+    rows = np.arange(x.size // 128)
+    rows[2::4], rows[3::4] = rows[3::4].copy(), rows[2::4].copy()
+    perm = (rows[:, None] * 128 + np.arange(128)).reshape(-1)
+    xs, ys, zs = x[perm], y[perm], z[perm]
+    assert layout.forward_lines_form(xs, ys, zs) and not layout.forward_pairs_form(xs, ys, zs)
+    yb = y.copy()
+    yb[5 * 128:6 * 128] += np.float32(1.0 / 512)
+    assert layout.forward_lines_form(x, yb, z) and not layout.forward_pairs_form(x, yb, z)
+    g2 = inputs.coords_from_axis(128, 16, 4, (-0.5, 1.0 / 128, -0.5, 1.0 / 32, 0.0, 0.25))
+    xx, yy, zz = (np.concatenate((a, b)) for a, b in zip((x, y, z), g2))
+    assert layout.forward_lines_form(xx, yy, zz) and not layout.forward_pairs_form(xx, yy, zz)
