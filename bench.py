@@ -127,22 +127,21 @@ PATH_DTYPE = {
 # until the counters are taken again.
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 _GATHER_SRC = ["fhd.hip", "fhd_internal.h"]
-_GATHER_SHA = "b05bd53763c9b3bac95677f067709916b560d937b1fee421cd5c70fffa13cede"
+_GATHER_SHA = "8b8d10af332b78a238db7ad7c2e724b61a106434e580a65f6d0f66263543ebe5"
 TRAFFIC = {
     "fhd_gather_patch_kernel<true, true>": {
         "workload": "spiral128", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
-        "bytes_per_launch": (108286.0 * 2.0 + 65771.0 * 1.0) * 1024},
+        "bytes_per_launch": (108297.0 * 2.0 + 65755.0 * 1.0) * 1024},
     "fhd_gather_kernel<16, true>": {
         "workload": "spiral128", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
-        "bytes_per_launch": (54788.0 * 2.0 + 92160.0 * 1.0) * 1024},
+        "bytes_per_launch": (52931.4 * 2.0 + 87040.3 * 1.0) * 1024},
+    "fhd_gather_patch64_kernel<true, true>": {
+        "workload": "radial64", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
+        "bytes_per_launch": (20184.5 * 2.0 + 65536.1 * 1.0) * 1024},
     "fhd_forward_pairs_kernel<true>": {
         "workload": "spiral128", "sources": ["fhd_forward.hip", "fhd_internal.h"],
-        "sha256": "6b3fb860a684ab50eb8d4420ab7134edee83d3e2bfd0b54c31d83cf0a718fcc6",
-        "bytes_per_launch": (73924.4 * 2.0 + 5468.75 * 1.0) * 1024},
-    "fhd_gather_patch64_kernel<true, true>": {
-        "workload": "radial64", "sources": _GATHER_SRC,
-        "sha256": "e1ee16a4e91cc4340cb87c2fdf1a00d467c7495ce78841ff9fff32ced098aca5",
-        "bytes_per_launch": (20186.5 * 2.0 + 65536.0 * 1.0) * 1024},
+        "sha256": "315294ad4d584c3fb6b3dd1c63f84b9d1539da5ef195be38b1855f31ce035ab4",
+        "bytes_per_launch": (74313.4 * 2.0 + 5468.75 * 1.0) * 1024},
 }
 
 

@@ -106,10 +106,17 @@ __device__ __forceinline__ void issue_stage_load(const float4 *__restrict__ src,
 {
     static_assert(BLOCK % 64 == 0, "workgroup must be whole wave64s");
     constexpr int loads = (STAGE_VEC4 + BLOCK - 1) / BLOCK;
-    const int wave_base = threadIdx.x & ~63;
+    // the wave's LDS base in a scalar register, so that the LDS addresses
+    // (M0) are scalar arithmetic
+    const int wave_base = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
     const int64_t first = (int64_t)st * STAGE_VEC4;
-    const int64_t left = total_vec4 - first;   // callers pass st with left > 0
-    const int bytes = (int)(left <= 0 ? 0 : left < STAGE_VEC4 ? left : STAGE_VEC4) * 16;
+    // callers pass st with total_vec4 - first > 0; the clamp to one stage
+    // in 32-bit halves (scalar compares; 64-bit ordered compares would
+    // take vector instructions)
+    const uint64_t left = (uint64_t)(total_vec4 - first);
+    unsigned left_hi = (unsigned)(left >> 32), left_lo = (unsigned)left;
+    asm("" : "+s"(left_hi), "+s"(left_lo));   // kept apart (no 64-bit compare)
+    const int bytes = (left_hi != 0u || left_lo >= (unsigned)STAGE_VEC4 ? STAGE_VEC4 : (int)left_lo) * 16;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)(src + first), (short)0, bytes, 0x00020000);
 #pragma unroll
