@@ -129,17 +129,18 @@ CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 _GATHER_SRC = ["fhd.hip", "fhd_internal.h"]
 _GATHER_SHA = "8b8d10af332b78a238db7ad7c2e724b61a106434e580a65f6d0f66263543ebe5"
 TRAFFIC = {
-    "fhd_gather_patch_kernel<true, true>": {
-        "workload": "spiral128", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
+    ("fhd_gather_patch_kernel<true, true>", "spiral128"): {
+        "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
         "bytes_per_launch": (108297.0 * 2.0 + 65755.0 * 1.0) * 1024},
-    "fhd_gather_kernel<16, true>": {
-        "workload": "spiral128", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
+    ("fhd_gather_kernel<16, true>", "spiral128"): {
+        "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
         "bytes_per_launch": (52931.4 * 2.0 + 87040.3 * 1.0) * 1024},
-    "fhd_gather_patch64_kernel<true, true>": {
-        "workload": "radial64", "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
-        "bytes_per_launch": (20184.5 * 2.0 + 65536.1 * 1.0) * 1024},
-    "fhd_forward_pairs_kernel<true>": {
-        "workload": "spiral128", "sources": ["fhd_forward.hip", "fhd_internal.h"],
+    ("fhd_gather_patch_kernel<true, true>", "radial64"): {
+        "sources": _GATHER_SRC,
+        "sha256": "c6d15134c31e40f9e1c69d34de5c5fa321d115bff07ef9cbf600f83d2a11f908",
+        "bytes_per_launch": (35071.8 * 2.0 + 69324.2 * 1.0) * 1024},
+    ("fhd_forward_pairs_kernel<true>", "spiral128"): {
+        "sources": ["fhd_forward.hip", "fhd_internal.h"],
         "sha256": "315294ad4d584c3fb6b3dd1c63f84b9d1539da5ef195be38b1855f31ce035ab4",
         "bytes_per_launch": (74313.4 * 2.0 + 5468.75 * 1.0) * 1024},
 }
@@ -148,14 +149,28 @@ TRAFFIC = {
 def measured_traffic(kernel: str, workload: str):
     """Measured HBM bytes per launch of `kernel` on `workload`, when the
     counters were taken on the current sources (else None)."""
-    entry = TRAFFIC.get(kernel)
-    if entry is None or workload != entry["workload"]:
+    entry = TRAFFIC.get((kernel, workload))
+    if entry is None:
         return None
     h = hashlib.sha256()
     for name in entry["sources"]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return entry["bytes_per_launch"] if h.hexdigest() == entry["sha256"] else None
+
+
+def line_instance_masks(w: dict, cls: np.ndarray, paths: str):
+    """The quads the line-pair instance takes (128-voxel line pairs or
+    four-line groups of 64-voxel lines) and the unit pairs the 64-voxel
+    line-pair instance takes, as the layout mirror gives them."""
+    from non_cartesian_mri_fhd_amd import layout
+    if paths == "vector":
+        return None, None
+    q128 = layout.line_pair_quads(w["x"], w["y"], w["z"], cls)
+    q64 = layout.line_group64_quads(w["x"], w["y"], w["z"], cls)
+    n = min(q128.size, q64.size) if q64.size else q128.size
+    quads = q128[:n] | (q64[:n] if q64.size else False)
+    return quads, layout.line_pair64_pairs(w["x"], w["y"], w["z"], cls)
 
 
 def adjoint_kernel(cls: np.ndarray, counts: np.ndarray, paths: str, quads=None,
@@ -395,8 +410,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
-    lp = layout.line_pair_quads(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
-    lp64 = layout.line_pair64_pairs(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
+    lp, lp64 = line_instance_masks(w, cls, args.paths)
     kernel, kernel_share = adjoint_kernel(cls, counts, args.paths, lp, lp64)
     timer = binding.KernelTimer(kernel, args.steps, dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -463,8 +477,7 @@ def main(argv=None) -> int:
             continue
         gather(p)
         c2, _, n2 = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=p != "vector")
-        lp2 = layout.line_pair_quads(w["x"], w["y"], w["z"], c2) if p != "vector" else None
-        lq2 = layout.line_pair64_pairs(w["x"], w["y"], w["z"], c2) if p != "vector" else None
+        lp2, lq2 = line_instance_masks(w, c2, p)
         k2, share2 = adjoint_kernel(c2, n2, p, lp2, lq2)
         call_ms, kms = timed_calls(lambda: gather(p), 3, stream, k2, 1, dev)
         fr2, _ = adjoint_ceiling(w, p != "vector")
@@ -514,8 +527,7 @@ def bench_other(args) -> int:
     f_lines = args.paths != "vector" and layout.forward_lines_form(w["x"], w["y"], w["z"])
     f_pairs = f_lines and layout.forward_pairs_form(w["x"], w["y"], w["z"])
     cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
-    lp = layout.line_pair_quads(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
-    lp64 = layout.line_pair64_pairs(w["x"], w["y"], w["z"], cls) if args.paths != "vector" else None
+    lp, lp64 = line_instance_masks(w, cls, args.paths)
     adj_kernel, adj_share = adjoint_kernel(cls, counts, args.paths, lp, lp64)
     fwd_kernel = ("fhd_forward_pairs_kernel<%s>" % split if f_pairs else
                   "fhd_forward_lines_kernel<%s>" % split if f_lines else "fhd_forward_gather_kernel<2>")

@@ -63,7 +63,10 @@ extern "C" {
  * (lines of 64), the lines also come two by two as one line and that line
  * moved by one offset (the rows of a grid), F^H D pairs the voxels of each
  * two lines about their common centre instead, with half the per-line
- * work. Every other unit is summed on the vector ALUs in fp32.
+ * work; where, in four units of lines of 64, they come four by four at
+ * offsets 0, d, e and e + d from the first (rows y .. y + 3), about the
+ * four lines' common centre, with a quarter. Every other unit is summed on
+ * the vector ALUs in fp32.
  *
  *   FHD_GATHER_ALL    (the default of fhd_compute, fhd_gather, fhd_forward,
  *                     fhd_normal, fhd_cg) lines on the matrix cores with
@@ -463,9 +466,11 @@ void fhd_gather_config(int *voxels_per_lane, int *samples_per_chunk, int *block_
  *     operands inside each workgroup instead of from a per-call table
  *     (slower), with the same arithmetic: the results equal
  *     fhd_compute_paths' bit for bit except on grids where some quads of
- *     line pairs differ from the first quad's step or offset, which
- *     fhd_compute_paths sums as long lines and this entry point as line
- *     pairs (both within the same bound).
+ *     line pairs (or four-line groups, or unit pairs of 64-voxel line
+ *     pairs) differ from the first one's step or offsets, which
+ *     fhd_compute_paths sums in the next form down (long lines, 64-voxel
+ *     line pairs or lines) and this entry point as they are (both within
+ *     the same bound).
  * Errors: FHD_ERR_INVALID_ARG (also for a workspace beyond the array),
  * FHD_ERR_HIP.
  */
@@ -483,10 +488,11 @@ int fhd_compute_noalloc(const float *kx, const float *ky, const float *kz,
  * events[2*i + 1] just after it, so hipEventElapsedTime(events[2*i],
  * events[2*i + 1]) is that launch's duration on the GPU. Names are the
  * kernels' as a profiler lists them, with template arguments:
- * "fhd_gather_patch_kernel<true, true>" (line pairs, split fp16, B table)
- * or "<false, true>" (split bf16), "<true, false>"/"<false, false>" (B
- * formed in the workgroups), "fhd_gather_patch64_kernel<...>" (the same
- * for 64-voxel line pairs), "fhd_gather_long_lines_kernel<true>" (split
+ * "fhd_gather_patch_kernel<true, true>" (quads of 128-voxel line pairs or
+ * of four-line groups of 64-voxel lines, split fp16, B table) or "<false,
+ * true>" (split bf16), "<true, false>"/"<false, false>" (B formed in the
+ * workgroups), "fhd_gather_patch64_kernel<...>" (the same for unit pairs
+ * of 64-voxel line pairs), "fhd_gather_long_lines_kernel<true>" (split
  * fp16) or "<false>" (split bf16), "fhd_gather_lines_kernel<true>"/"<false>",
  * "fhd_gather_kernel<16, true>" (one-step ramps) or "<16, false>",
  * "fhd_forward_pairs_kernel<true>"/"<false>" (line pairs),

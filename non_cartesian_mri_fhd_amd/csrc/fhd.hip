@@ -551,9 +551,12 @@ __device__ __forceinline__ bool lane_on_line(const float (&px)[V], const float (
 // patches[2 b + 1] whether the pair's lines, taken two by two (lines 2i
 // and 2i + 1), are all one line and that line moved by one common offset d
 // (bitwise the same difference of their first voxels' x, y and z), with
-// the lines' step dx and d (bits): {flag, dx, 0, 0} and {d.x, d.y, d.z,
-// 0}; flag 1 for the 64 lines of 128 voxels of a long pair, 2 for the 128
-// lines of 64 voxels of two units of class kClassLines with one step.
+// the lines' step dx and d (bits): {flag, dx, e.x, e.y} and {d.x, d.y,
+// d.z, e.z}; flag 1 for the 64 lines of 128 voxels of a long pair, 2 for
+// the 128 lines of 64 voxels of two units of class kClassLines with one
+// step, 3 for those when, beyond that, the lines 4i + 2 are the lines 4i
+// moved by one common offset e (so lines 4i .. 4i + 3 sit at 0, d, e and
+// e + d from line 4i).
 //
 // When the grid holds kAmpSlots more workgroups than pairs, workgroup
 // pairs + s instead writes slot s (info[4 + s]) with the largest amplitude
@@ -600,8 +603,8 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
         return;
     }
     __shared__ float wg_step[2][3];                // each unit's first lane's ramp and line steps
-    __shared__ float wg_shift[2][3];               // the pair's first two lines' offset (128, 64)
-    __shared__ int votes[2 * kWavesPerUnit][5];    // per wave: one step, 64-lines, 128-lines, shifts
+    __shared__ float wg_shift[3][3];               // the pair's first lines' offsets (128, 64, 64 by 2)
+    __shared__ int votes[2 * kWavesPerUnit][6];    // per wave: one step, 64-lines, 128-lines, shifts
     const int half = threadIdx.x / kBlock, t = threadIdx.x % kBlock;
     const int64_t u = 2 * (int64_t)blockIdx.x + half;
     const bool present = u < units;   // the grid's last pair may hold one unit
@@ -616,6 +619,7 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
     static_assert(kLineLanes == 8 && 64 % (2 * kLineLanes) == 0, "a wave holds whole line pairs");
     static_assert(kLine64Lanes == 4, "a 64-voxel line pair is 8 lanes");
     float sx = 0.0f, sy = 0.0f, sz = 0.0f, sx64 = 0.0f, sy64 = 0.0f, sz64 = 0.0f;
+    float ex64 = 0.0f, ey64 = 0.0f, ez64 = 0.0f;
     if (present) {   // uniform over each wave
         float px[kVox], py[kVox], pz[kVox];
         load_lane_voxels<kVox, true>(x, y, z, N, n0, px, py, pz);
@@ -632,6 +636,12 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
         sx64 = __shfl(px[0], a64 + kLine64Lanes) - __shfl(px[0], a64);
         sy64 = __shfl(py[0], a64 + kLine64Lanes) - __shfl(py[0], a64);
         sz64 = __shfl(pz[0], a64 + kLine64Lanes) - __shfl(pz[0], a64);
+        // this lane's group of four 64-voxel lines (16 lanes): line 4i + 2's
+        // offset from line 4i
+        const int a4 = (threadIdx.x & 63) & ~(4 * kLine64Lanes - 1);
+        ex64 = __shfl(px[0], a4 + 2 * kLine64Lanes) - __shfl(px[0], a4);
+        ey64 = __shfl(py[0], a4 + 2 * kLine64Lanes) - __shfl(py[0], a4);
+        ez64 = __shfl(pz[0], a4 + 2 * kLine64Lanes) - __shfl(pz[0], a4);
         if (t == 0) {
             wg_step[half][0] = dx;
             wg_step[half][1] = d64;
@@ -643,6 +653,9 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
                 wg_shift[1][0] = sx64;
                 wg_shift[1][1] = sy64;
                 wg_shift[1][2] = sz64;
+                wg_shift[2][0] = ex64;
+                wg_shift[2][1] = ey64;
+                wg_shift[2][2] = ez64;
             }
         }
     }
@@ -658,27 +671,33 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
                            __builtin_isfinite(sz64) && __float_as_uint(sx64) == __float_as_uint(wg_shift[1][0]) &&
                            __float_as_uint(sy64) == __float_as_uint(wg_shift[1][1]) &&
                            __float_as_uint(sz64) == __float_as_uint(wg_shift[1][2]);
+    const bool grouped64 = shifted64 && __builtin_isfinite(ex64) && __builtin_isfinite(ey64) &&
+                           __builtin_isfinite(ez64) && __float_as_uint(ex64) == __float_as_uint(wg_shift[2][0]) &&
+                           __float_as_uint(ey64) == __float_as_uint(wg_shift[2][1]) &&
+                           __float_as_uint(ez64) == __float_as_uint(wg_shift[2][2]);
     const int wave = threadIdx.x / 64;
     const bool all_one = __all(one), all64 = __all(l64), all128 = __all(l128), all_shift = __all(shifted);
-    const bool all_shift64 = __all(shifted64);
+    const bool all_shift64 = __all(shifted64), all_group64 = __all(grouped64);
     if ((threadIdx.x & 63) == 0) {
         votes[wave][0] = all_one;
         votes[wave][1] = all64;
         votes[wave][2] = all128;
         votes[wave][3] = all_shift;
         votes[wave][4] = all_shift64;
+        votes[wave][5] = all_group64;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int c[2], lng[2], shf = 1, shf64 = 1;
+        int c[2], lng[2], shf = 1, shf64 = 1, grp64 = 1;
         for (int k = 0; k < 2; ++k) {
-            int v[5] = {1, 1, 1, 1, 1};
+            int v[6] = {1, 1, 1, 1, 1, 1};
             for (int w = 0; w < kWavesPerUnit; ++w)
-                for (int q = 0; q < 5; ++q) v[q] &= votes[k * kWavesPerUnit + w][q];
+                for (int q = 0; q < 6; ++q) v[q] &= votes[k * kWavesPerUnit + w][q];
             c[k] = allow_lines && v[1] ? kClassLines : v[0] ? kClassOneStep : kClassGeneral;
             lng[k] = v[2];
             shf &= v[3];
             shf64 &= v[4];
+            grp64 &= v[5];
         }
         const bool has_second = 2 * (int64_t)blockIdx.x + 1 < units;
         const bool pair = allow_lines && has_second && lng[0] && lng[1] &&
@@ -693,16 +712,18 @@ __global__ __launch_bounds__(kClassifyBlock) void fhd_classify_kernel(const floa
         }
         if (patches) {
             // 1: 128-voxel line pairs (a long pair); 2: 64-voxel line pairs
-            // (both units of class kClassLines with one step for the pair)
+            // (both units of class kClassLines with one step for the pair);
+            // 3: those in groups of four lines with one second offset
             const bool pair64 = !pair && has_second && c[0] == kClassLines && c[1] == kClassLines &&
                                 __float_as_uint(wg_step[0][1]) == __float_as_uint(wg_step[1][1]) && shf64;
-            const int flag = pair && shf ? 1 : pair64 ? 2 : 0;
-            const int sel = flag == 2 ? 1 : 0;
+            const int flag = pair && shf ? 1 : pair64 && grp64 ? 3 : pair64 ? 2 : 0;
+            const int sel = flag >= 2 ? 1 : 0;
             patches[2 * (int64_t)blockIdx.x] =
-                make_int4(flag, (int)__float_as_uint(wg_step[0][flag == 2 ? 1 : 2]), 0, 0);
+                make_int4(flag, (int)__float_as_uint(wg_step[0][flag >= 2 ? 1 : 2]),
+                          (int)__float_as_uint(wg_shift[2][0]), (int)__float_as_uint(wg_shift[2][1]));
             patches[2 * (int64_t)blockIdx.x + 1] =
                 make_int4((int)__float_as_uint(wg_shift[sel][0]), (int)__float_as_uint(wg_shift[sel][1]),
-                          (int)__float_as_uint(wg_shift[sel][2]), 0);
+                          (int)__float_as_uint(wg_shift[sel][2]), (int)__float_as_uint(wg_shift[2][2]));
         }
     }
 }
@@ -794,27 +815,69 @@ __device__ __forceinline__ bool patch_quad(const int *__restrict__ cls, const in
 }
 
 // How the line-pair instance runs in a call: not at all, with a B table
-// formed for quad 0's step and offset (it then takes the quads that share
-// them; the long-line instance takes the other long pairs), or forming
-// each step's B operands itself (it takes every quad).
+// formed for quad 0's step and offsets (it then takes the quads of quad
+// 0's kind that share them; the long-line and 64-voxel line-pair
+// instances take the other unit pairs), or forming each step's B operands
+// itself (it takes every quad of either kind).
 enum : int { kPatchNone = 0, kPatchTable = 1, kPatchFormed = 2 };
 
-// Whether unit pair p (units 2p, 2p + 1) is taken by the 64-voxel
-// line-pair instance in `mode`: both units of class kClassLines and the
-// pair's record says its 64-voxel lines pair up (flag 2); in the table
-// mode also pair 0 so, with the same step and offset.
-__device__ __forceinline__ bool pair64_taken(const int *__restrict__ cls, const int4 *__restrict__ patches,
-                                             int64_t units, int64_t p, int mode)
+// Whether quad q (units 4q .. 4q + 3) is one of four-line groups of
+// 64-voxel lines: all four units of class kClassLines, both unit pairs'
+// records flag 3, with the same step and offsets.
+__device__ __forceinline__ bool group64_quad(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                             int64_t units, int64_t q)
 {
-    if (mode == kPatchNone || patches == nullptr || 2 * p + 1 >= units) return false;
-    if (cls[2 * p] != kClassLines || cls[2 * p + 1] != kClassLines || patches[2 * p].x != 2) return false;
+    if (patches == nullptr || 4 * q + 3 >= units) return false;
+    if (cls[4 * q] != kClassLines || cls[4 * q + 1] != kClassLines || cls[4 * q + 2] != kClassLines ||
+        cls[4 * q + 3] != kClassLines)
+        return false;
+    const int4 a0 = patches[4 * q], a1 = patches[4 * q + 1], b0 = patches[4 * q + 2], b1 = patches[4 * q + 3];
+    return a0.x == 3 && b0.x == 3 && a0.y == b0.y && a0.z == b0.z && a0.w == b0.w && a1.x == b1.x &&
+           a1.y == b1.y && a1.z == b1.z && a1.w == b1.w;
+}
+
+// Whether quad q is taken by the line-pair instance as four-line groups
+// of 64-voxel lines in `mode` (in the table mode: quad 0 so too, with the
+// same step and offsets).
+__device__ __forceinline__ bool group64_taken(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                              int64_t units, int64_t q, int mode)
+{
+    if (mode == kPatchNone || !group64_quad(cls, patches, units, q)) return false;
+    if (mode == kPatchFormed || q == 0) return true;
+    if (!group64_quad(cls, patches, units, 0)) return false;
+    const int4 r0 = patches[0], r1 = patches[1], a0 = patches[4 * q], a1 = patches[4 * q + 1];
+    return r0.y == a0.y && r0.z == a0.z && r0.w == a0.w && r1.x == a1.x && r1.y == a1.y && r1.z == a1.z &&
+           r1.w == a1.w;
+}
+
+// Whether unit pair p (units 2p, 2p + 1) is one the 64-voxel line-pair
+// instance may take: both units of class kClassLines, the pair's record
+// says its 64-voxel lines pair up (flag 2 or 3), and its quad is not
+// taken as four-line groups in the line-pair instance's mode.
+__device__ __forceinline__ bool pair64_open(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                            int64_t units, int64_t p, int quad_mode)
+{
+    if (patches == nullptr || 2 * p + 1 >= units) return false;
+    if (cls[2 * p] != kClassLines || cls[2 * p + 1] != kClassLines) return false;
+    if (patches[2 * p].x != 2 && patches[2 * p].x != 3) return false;
+    return !group64_taken(cls, patches, units, p / 2, quad_mode);
+}
+
+// Whether unit pair p is taken by the 64-voxel line-pair instance in
+// `mode` (in the table mode also pair 0 so, with the same step and
+// offset), the line-pair instance running in `quad_mode`.
+__device__ __forceinline__ bool pair64_taken(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                             int64_t units, int64_t p, int mode, int quad_mode)
+{
+    if (mode == kPatchNone || !pair64_open(cls, patches, units, p, quad_mode)) return false;
     if (mode == kPatchFormed || p == 0) return true;
-    if (cls[0] != kClassLines || cls[1] != kClassLines || patches[0].x != 2) return false;
+    if (!pair64_open(cls, patches, units, 0, quad_mode)) return false;
     const int4 r0 = patches[0], r1 = patches[1], a0 = patches[2 * p], a1 = patches[2 * p + 1];
     return r0.y == a0.y && r1.x == a1.x && r1.y == a1.y && r1.z == a1.z;
 }
 
-// Whether quad q is taken by the line-pair instance in `mode`.
+// Whether quad q is taken by the line-pair instance in `mode` as 128-voxel
+// line pairs.
 __device__ __forceinline__ bool patch_taken(const int *__restrict__ cls, const int4 *__restrict__ patches,
                                             int64_t units, int64_t q, int mode)
 {
@@ -870,11 +933,14 @@ static_assert(kLinesBlock / 64 == 2, "wave 0 forms B_C, wave 1 B_S");
 template <bool F16>
 __global__ __launch_bounds__(kLinesBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_lines_kernel(
     const float *__restrict__ packed, int nchunks, int splits, const int *__restrict__ cls,
-    const int4 *__restrict__ patches, int64_t units, int patch_mode, const int *__restrict__ info,
+    const int4 *__restrict__ patches, int64_t units, int pair_mode, int quad_mode, const int *__restrict__ info,
     const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
     float *__restrict__ out_r, float *__restrict__ out_i, int N)
 {
-    if (cls[blockIdx.x] != kClassLines || pair64_taken(cls, patches, units, blockIdx.x / 2, patch_mode)) return;
+    // units the line-pair or 64-voxel line-pair instance takes are theirs
+    if (cls[blockIdx.x] != kClassLines || group64_taken(cls, patches, units, blockIdx.x / 4, quad_mode) ||
+        pair64_taken(cls, patches, units, blockIdx.x / 2, pair_mode, quad_mode))
+        return;
     __shared__ float4 stage[2][kLinesStageVec4];
     // [buffer][B_C hi, B_C lo, B_S hi, B_S lo][k half][pair]: one lane's
     // 8-sample operand each; a half-wave reads 32 consecutive entries
@@ -1075,73 +1141,117 @@ __device__ __forceinline__ void long_step_b(const float (&f)[kFields][kChunk], f
 }
 
 constexpr int kQuadVox = 2 * kPairVox;              // voxels of a quad
-constexpr int kPatchBlock = 256;                    // 4 waves of 16 line pairs
+constexpr int kPatchBlock = 256;                    // 4 waves of 16 rows
 
-// The line-pair instance for lines of LINE voxels (128: quads of long
-// pairs; 64: unit pairs of 64-voxel lines, as on a grid with rows of 64):
-// a workgroup takes 64 line pairs, 128 LINE voxels, with LINE pair
-// columns (LINE / 2 per side) in LINE / 16 tiles. B operands of one step:
-// [B_C hi, B_C lo, B_S hi, B_S lo][tile][k quarter][column in tile], one
-// lane's 8 fp16 or bf16 each: 32 KB (LINE 128) or 16 KB (64).
-template <int LINE>
+// The line-pair instance for groups of SIDES lines of LINE voxels
+// symmetric about a centre c (128, 2: a line and the line moved by d, the
+// quads of long pairs; 64, 4: lines at 0, d, e, e + d, four-line groups of
+// 64-voxel lines; 64, 2: unit pairs of 64-voxel lines). A group is one row
+// of the products; its voxels pair up by point reflection about c, one
+// column per pair: side s (sigma_1, sigma_2) = (s & 1 ? -1 : 1, s & 2 ?
+// -1 : 1) and j < LINE / 2 hold the voxel at c + sigma_1 d / 2 + sigma_2 e
+// / 2 + o_j (line SIDES - 1 - s of the group, voxel LINE / 2 + j) and its
+// reflection (line s, voxel LINE / 2 - 1 - j), o_j = (j + 1/2) dx e_x. A
+// workgroup takes 64 rows with SIDES LINE / 2 columns in kTiles tiles of
+// 16. B operands of one step: [B_C hi, B_C lo, B_S hi, B_S lo][tile][k
+// quarter][column in tile], one lane's 8 fp16 or bf16 each: 32 KB for 8
+// tiles, 16 KB for 4.
+template <int TILES>
+struct PatchStep {
+    u32x4 b[4][TILES][4][16];
+    float4 chunks[kLongStepChunkVec4];
+};
+template <int LINE, int SIDES>
 struct PatchShape {
-    static constexpr int kHalf = LINE / 2;          // pairs per side
-    static constexpr int kTiles = LINE / 16;
-    static constexpr int kGroupVox = 128 * LINE;
+    static constexpr int kHalf = LINE / 2;                  // columns per side
+    static constexpr int kTiles = SIDES * kHalf / 16;
+    static constexpr int kSideTiles = kHalf / 16;
+    static constexpr int kGroupVox = 64 * SIDES * LINE;
     static constexpr int kStepVec4 = 4 * kTiles * 4 * 16;
     typedef u32x4 StepB[4][kTiles][4][16];
-    struct Step {
-        StepB b;
-        float4 chunks[kLongStepChunkVec4];
-    };
+    typedef PatchStep<kTiles> Step;
 };
-static_assert(PatchShape<kLongLineVox>::kGroupVox == kQuadVox, "a 128-voxel line-pair workgroup is a quad");
-static_assert(PatchShape<kLineVox>::kGroupVox == kPairVox, "a 64-voxel line-pair workgroup is a unit pair");
-constexpr int kPatchStepVec4 = PatchShape<kLongLineVox>::kStepVec4;
-constexpr int kPatch64StepVec4 = PatchShape<kLineVox>::kStepVec4;
-static_assert(kPatch64StepVec4 == kLongStepVec4, "the 64-voxel line-pair B shares the long-line table");
+typedef PatchShape<kLongLineVox, 2> PairShape128;
+typedef PatchShape<kLineVox, 4> GroupShape64;
+typedef PatchShape<kLineVox, 2> PairShape64;
+static_assert(PairShape128::kGroupVox == kQuadVox, "a 128-voxel line-pair workgroup is a quad");
+static_assert(GroupShape64::kGroupVox == kQuadVox, "a 64-voxel four-line-group workgroup is a quad");
+static_assert(PairShape64::kGroupVox == kPairVox, "a 64-voxel line-pair workgroup is a unit pair");
+static_assert(PairShape128::kTiles == GroupShape64::kTiles, "both quad kinds share one step layout");
+constexpr int kPatchStepVec4 = PairShape128::kStepVec4;
+static_assert(PairShape64::kStepVec4 == kLongStepVec4, "the 64-voxel line-pair B shares the long-line table");
+
+// The offsets of a group (from its records): d and, for four sides, e.
+struct GroupOffsets {
+    float dx, d[3], e[3];
+};
+__device__ __forceinline__ GroupOffsets group_offsets(const int4 *__restrict__ rec)
+{
+    const int4 a = rec[0], b = rec[1];
+    GroupOffsets o;
+    o.dx = __int_as_float(a.y);
+    o.d[0] = __int_as_float(b.x);
+    o.d[1] = __int_as_float(b.y);
+    o.d[2] = __int_as_float(b.z);
+    o.e[0] = __int_as_float(a.z);
+    o.e[1] = __int_as_float(a.w);
+    o.e[2] = __int_as_float(b.w);
+    return o;
+}
 
 // Lane (wave w, lane l) of a step's B: B_C (w < 2) or B_S (w >= 2, as a
-// cosine a quarter turn later) of the pair tiles of side w % 2 (columns at
-// +d/2 for side 0, -d/2 for side 1), column l % 16 of each, samples
-// 8 (l / 16) .. + 7 (f: their chunk; dx and d: the group's step and
-// offset; sh: the amplitudes' scaling in the fp16 form), split and stored
-// at their place in `dst`.
-template <bool F16, int LINE>
-__device__ __forceinline__ void patch_step_b(const float (&f)[kFields][kChunk], float dx, float ddx, float ddy,
-                                             float ddz, int wave, int quarter_k, int col, int sh,
-                                             typename PatchShape<LINE>::StepB &dst)
+// cosine a quarter turn later) of the tiles of sides (w & 1) SIDES / 2 ..
+// + SIDES / 2 - 1, column l % 16 of each, samples 8 (l / 16) .. + 7 (f:
+// their chunk; sh: the amplitudes' scaling in the fp16 form), split and
+// stored at their place in `dst`.
+template <bool F16, int LINE, int SIDES>
+__device__ __forceinline__ void patch_step_b(const float (&f)[kFields][kChunk], const GroupOffsets &o, int wave,
+                                             int quarter_k, int col, int sh,
+                                             typename PatchShape<LINE, SIDES>::StepB &dst)
 {
-    constexpr int kSideTiles = PatchShape<LINE>::kTiles / 2;
-    const int part = wave >> 1, side = wave & 1, t0 = kSideTiles * side;
+    using Shape = PatchShape<LINE, SIDES>;
+    constexpr int kSidesPerWave = SIDES / 2;
+    const int part = wave >> 1;
     const float turn = part == 0 ? 0.0f : -0.25f;
+    float hd[kChunk], he[kChunk];
 #pragma unroll
-    for (int tt = 0; tt < kSideTiles; ++tt) {
-        const int j = 16 * tt + col;
-        const float tj = (float)(2 * j + 1) * (0.5f * dx);
-        float b[kChunk];
+    for (int i = 0; i < kChunk; ++i) {
+        hd[i] = 0.5f * __builtin_fmaf(f[0][i], o.d[0], __builtin_fmaf(f[1][i], o.d[1], f[2][i] * o.d[2]));
+        he[i] = SIDES == 4 ? 0.5f * __builtin_fmaf(f[0][i], o.e[0], __builtin_fmaf(f[1][i], o.e[1], f[2][i] * o.e[2]))
+                           : 0.0f;
+    }
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            const float hd = 0.5f * __builtin_fmaf(f[0][i], ddx, __builtin_fmaf(f[1][i], ddy, f[2][i] * ddz));
-            const float amp = scale_amp<F16>(f[4][i], sh);
-            b[i] = amp * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj, (side == 0 ? hd : -hd) + turn));
+    for (int q = 0; q < kSidesPerWave; ++q) {
+        const int side = (wave & 1) * kSidesPerWave + q;
+        const float s1 = (side & 1) ? -1.0f : 1.0f, s2 = (side & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int tt = 0; tt < Shape::kSideTiles; ++tt) {
+            const int j = 16 * tt + col, t = side * Shape::kSideTiles + tt;
+            const float tj = (float)(2 * j + 1) * (0.5f * o.dx);
+            float b[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                const float off = SIDES == 4 ? __builtin_fmaf(s2, he[i], s1 * hd[i]) : s1 * hd[i];
+                const float amp = scale_amp<F16>(f[4][i], sh);
+                b[i] = amp * __builtin_amdgcn_cosf(__builtin_fmaf(f[0][i], tj, off + turn));
+            }
+            unsigned h[4], l[4];
+            split_parts<F16, kChunk>(b, h, l);
+            dst[2 * part + 0][t][quarter_k][col] = (u32x4){h[0], h[1], h[2], h[3]};
+            dst[2 * part + 1][t][quarter_k][col] = (u32x4){l[0], l[1], l[2], l[3]};
         }
-        unsigned h[4], l[4];
-        split_parts<F16, kChunk>(b, h, l);
-        dst[2 * part + 0][t0 + tt][quarter_k][col] = (u32x4){h[0], h[1], h[2], h[3]};
-        dst[2 * part + 1][t0 + tt][quarter_k][col] = (u32x4){l[0], l[1], l[2], l[3]};
     }
 }
 
-// Step g of the B table for a group's step and offset (the records at
+// Step g of the B table for a group's step and offsets (the records at
 // rec[0], rec[1]): chunks past the stream's end as zeros.
-template <bool F16, int LINE>
+template <bool F16, int LINE, int SIDES>
 __device__ __forceinline__ void patch_table_step(const float *__restrict__ packed, int nchunks,
                                                  const int4 *__restrict__ rec, const int *__restrict__ info,
                                                  float4 *__restrict__ table)
 {
-    const float dx = __int_as_float(rec[0].y);
-    const int4 d = rec[1];
+    using Shape = PatchShape<LINE, SIDES>;
+    const GroupOffsets o = group_offsets(rec);
     const int sh = F16 ? read_amp_shift(info) : 0;
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1155,9 +1265,9 @@ __device__ __forceinline__ void patch_table_step(const float *__restrict__ packe
 #pragma unroll
             for (int u = 0; u < kChunk; ++u) f[q][u] = 0.0f;
     }
-    patch_step_b<F16, LINE>(
-        f, dx, __int_as_float(d.x), __int_as_float(d.y), __int_as_float(d.z), wave, quarter_k, col, sh,
-        *reinterpret_cast<typename PatchShape<LINE>::StepB *>(table + (int64_t)blockIdx.x * PatchShape<LINE>::kStepVec4));
+    patch_step_b<F16, LINE, SIDES>(
+        f, o, wave, quarter_k, col, sh,
+        *reinterpret_cast<typename Shape::StepB *>(table + (int64_t)blockIdx.x * Shape::kStepVec4));
 }
 
 // The B operands of every product step of the sample stream, formed once per
@@ -1178,8 +1288,8 @@ __global__ __launch_bounds__(kLongBlock) void fhd_long_table_kernel(const float 
                                                                     const int *__restrict__ info,
                                                                     float4 *__restrict__ table)
 {
-    if (pair64_mode == kPatchTable && pair64_taken(cls, patches, units, 0, kPatchTable)) {
-        patch_table_step<F16, kLineVox>(packed, nchunks, patches, info, table);
+    if (pair64_mode == kPatchTable && pair64_taken(cls, patches, units, 0, kPatchTable, patch_mode)) {
+        patch_table_step<F16, kLineVox, 2>(packed, nchunks, patches, info, table);
         return;
     }
     if (info[0] == 0 || patch_taken(cls, patches, units, 0, patch_mode)) return;
@@ -1399,11 +1509,12 @@ __global__ __launch_bounds__(kLongBlock) __attribute__((amdgpu_waves_per_eu(3)))
 // 32 KB (formed once per call into a table, or by the workgroup itself),
 // double buffered with the step's four sample chunks: 66.8 KB of LDS, two
 // workgroups (8 waves) per CU.
-// The B operands of every step of the sample stream for quad 0's step and
-// offset, formed once per call when quad 0 is taken by the 128-voxel
-// line-pair instance: step g at table + g kPatchStepVec4. Quads with that
-// step and offset copy them into LDS instead of forming them (same
-// arithmetic, same bits).
+// The B operands of every step of the sample stream for quad 0's kind,
+// step and offsets, formed once per call when quad 0 is taken by the
+// line-pair instance (as 128-voxel line pairs or as four-line groups of
+// 64-voxel lines): step g at table + g kPatchStepVec4. Quads of that kind
+// with that step and those offsets copy them into LDS instead of forming
+// them (same arithmetic, same bits).
 template <bool F16>
 __global__ __launch_bounds__(kPatchBlock) void fhd_patch_table_kernel(const float *__restrict__ packed, int nchunks,
                                                                       const int *__restrict__ cls,
@@ -1411,40 +1522,47 @@ __global__ __launch_bounds__(kPatchBlock) void fhd_patch_table_kernel(const floa
                                                                       int64_t units, const int *__restrict__ info,
                                                                       float4 *__restrict__ table)
 {
-    if (!patch_quad(cls, patches, units, 0)) return;
-    patch_table_step<F16, kLongLineVox>(packed, nchunks, patches, info, table);
+    if (patch_quad(cls, patches, units, 0))
+        patch_table_step<F16, kLongLineVox, 2>(packed, nchunks, patches, info, table);
+    else if (group64_quad(cls, patches, units, 0))
+        patch_table_step<F16, kLineVox, 4>(packed, nchunks, patches, info, table);
 }
 
-// One workgroup of the line-pair instance for lines of LINE voxels: group
-// `group` (a quad for 128, a unit pair for 64), sample split `split` of
-// `splits`. TABLE: the B operands come from `table`; else the workgroup
-// forms them (the same arithmetic).
-template <bool F16, bool TABLE, int LINE>
+// One workgroup of the line-pair instance for groups of SIDES lines of LINE
+// voxels: group `group` (a quad for PairShape128 and GroupShape64, a unit
+// pair for PairShape64), sample split `split` of `splits`. TABLE: the B
+// operands come from `table`; else the workgroup forms them (the same
+// arithmetic).
+template <bool F16, bool TABLE, int LINE, int SIDES>
 __device__ __forceinline__ void patch_group(const float *__restrict__ packed, int nchunks, int splits, int64_t group,
                                             int split, const int4 *__restrict__ rec, const int *__restrict__ info,
                                             const float4 *__restrict__ table, const float *__restrict__ x,
                                             const float *__restrict__ y, const float *__restrict__ z,
                                             float *__restrict__ out_r, float *__restrict__ out_i, int N,
-                                            typename PatchShape<LINE>::Step &buf0,
-                                            typename PatchShape<LINE>::Step &buf1)
+                                            typename PatchShape<LINE, SIDES>::Step &buf0,
+                                            typename PatchShape<LINE, SIDES>::Step &buf1)
 {
-    using Shape = PatchShape<LINE>;
+    using Shape = PatchShape<LINE, SIDES>;
     using Step = typename Shape::Step;
     constexpr int kTiles = Shape::kTiles, kHalf = Shape::kHalf;
     const float4 *src = reinterpret_cast<const float4 *>(packed);
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sh = F16 ? read_amp_shift(info) : 0;
-    const float dx = __int_as_float(rec[0].y);
-    const int4 dbits = rec[1];
-    const float ddx = __int_as_float(dbits.x), ddy = __int_as_float(dbits.y), ddz = __int_as_float(dbits.z);
+    const GroupOffsets o = group_offsets(rec);
 
-    // line pair 16 wave + col of the group: lines 2 lp and 2 lp + 1
+    // row 16 wave + col of the group: its lines SIDES row .. + SIDES - 1,
+    // centre x_c(line 0) + d / 2 (+ e / 2)
     const int64_t base = group * Shape::kGroupVox;
-    const int64_t first = base + (int64_t)(2 * (16 * wave + col)) * LINE;
+    const int64_t first = base + (int64_t)(SIDES * (16 * wave + col)) * LINE;
     const float x0 = x[first], ly = y[first], lz = z[first];
-    const float cx = __builtin_fmaf(0.5f * (float)(LINE - 1), dx, x0) + 0.5f * ddx;
-    const float cy = ly + 0.5f * ddy, cz = lz + 0.5f * ddz;
+    float cx = __builtin_fmaf(0.5f * (float)(LINE - 1), o.dx, x0) + 0.5f * o.d[0];
+    float cy = ly + 0.5f * o.d[1], cz = lz + 0.5f * o.d[2];
+    if constexpr (SIDES == 4) {
+        cx += 0.5f * o.e[0];
+        cy += 0.5f * o.e[1];
+        cz += 0.5f * o.e[2];
+    }
 
     float4v prc[kTiles], pic[kTiles], pis[kTiles], prs[kTiles];
 #pragma unroll
@@ -1482,7 +1600,7 @@ __device__ __forceinline__ void patch_group(const float *__restrict__ packed, in
         float f[kFields][kChunk];
         load_chunk(cur.chunks + quarter_k * kChunkVec4, f);
         if constexpr (!TABLE) {
-            patch_step_b<F16, LINE>(f, dx, ddx, ddy, ddz, wave, quarter_k, col, sh, cur.b);
+            patch_step_b<F16, LINE, SIDES>(f, o, wave, quarter_k, col, sh, cur.b);
             lds_barrier();
         }
         float ur[kChunk], ui[kChunk];
@@ -1526,19 +1644,20 @@ __device__ __forceinline__ void patch_group(const float *__restrict__ packed, in
     }
     if (i < nsteps) step(i, buf0, buf1);
 
-    // unfold: row 4 (l / 16) + r of the wave's 16 line pairs, pair column
-    // 16 t + l % 16 (side t / (kTiles / 2), j = 16 (t % (kTiles / 2)) + l % 16)
+    // unfold: row 4 (l / 16) + r of the wave's 16 rows, column 16 t + l % 16
+    // (side t / kSideTiles, j = 16 (t % kSideTiles) + l % 16): the voxel of
+    // the side's line SIDES - 1 - side at kHalf + j and its reflection on
+    // line `side` at kHalf - 1 - j
     float *dst_r = out_r + (int64_t)split * N, *dst_i = out_i + (int64_t)split * N;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t line_a = base + (int64_t)(2 * (16 * wave + 4 * quarter_k + r)) * LINE;
-            const int64_t line_b = line_a + LINE;
-            const bool side0 = t < kTiles / 2;
-            const int j = 16 * (t % (kTiles / 2)) + col;
-            const int64_t plus = (side0 ? line_b : line_a) + kHalf + j;
-            const int64_t minus = (side0 ? line_a : line_b) + kHalf - 1 - j;
+            const int64_t row0 = base + (int64_t)(SIDES * (16 * wave + 4 * quarter_k + r)) * LINE;
+            const int side = t / Shape::kSideTiles;
+            const int j = 16 * (t % Shape::kSideTiles) + col;
+            const int64_t plus = row0 + (int64_t)(SIDES - 1 - side) * LINE + kHalf + j;
+            const int64_t minus = row0 + (int64_t)side * LINE + kHalf - 1 - j;
             dst_r[plus] = unscale<F16>(prc[t][r] - pis[t][r], sh);
             dst_i[plus] = unscale<F16>(pic[t][r] + prs[t][r], sh);
             dst_r[minus] = unscale<F16>(prc[t][r] + pis[t][r], sh);
@@ -1546,35 +1665,50 @@ __device__ __forceinline__ void patch_group(const float *__restrict__ packed, in
         }
 }
 
-// The 128-voxel line-pair instance: quads. TABLE: the B operands come
-// from the table (mode kPatchTable, the quads that share quad 0's step and
-// offset); else the workgroup forms them (mode kPatchFormed, every quad;
-// two separate instances, so the table form's register allocation does
-// not carry the forming code's).
+// The line-pair instance on quads: quads of long pairs whose lines pair up
+// (128-voxel line pairs, splits_long sample splits, into out_long) and
+// quads of 64-voxel lines in four-line groups (splits_lines splits, into
+// out_lines; the reduce sums class kClassLines units over that many rows).
+// TABLE: the B operands come from the table (mode kPatchTable, the quads of
+// quad 0's kind that share its step and offsets); else the workgroup
+// forms them (mode kPatchFormed, every quad; two separate instances, so
+// the table form's register allocation does not carry the forming code's).
+// The grid is quads x max(splits_long, splits_lines); a workgroup past its
+// kind's split count returns.
 template <bool F16, bool TABLE>
 __global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(2))) void fhd_gather_patch_kernel(
-    const float *__restrict__ packed, int nchunks, int splits, int64_t quads, int64_t units,
+    const float *__restrict__ packed, int nchunks, int splits_long, int splits_lines, int64_t quads, int64_t units,
     const int *__restrict__ cls, const int4 *__restrict__ patches, const int *__restrict__ info,
     const float4 *__restrict__ table, const float *__restrict__ x, const float *__restrict__ y,
-    const float *__restrict__ z, float *__restrict__ out_r, float *__restrict__ out_i, int N)
+    const float *__restrict__ z, float *__restrict__ out_long_r, float *__restrict__ out_long_i,
+    float *__restrict__ out_lines_r, float *__restrict__ out_lines_i, int N)
 {
     // workgroup -> (quad, split), split-major over the XCDs (see xcd_unit)
+    const int splits = splits_long > splits_lines ? splits_long : splits_lines;
     const int64_t unit = xcd_unit(blockIdx.x, quads * splits);
     const int64_t quad = unit % quads;
     const int split = (int)(unit / quads);
-    if (!patch_taken(cls, patches, units, quad, TABLE ? kPatchTable : kPatchFormed)) return;
+    constexpr int kMode = TABLE ? kPatchTable : kPatchFormed;
     // two step buffers used alternately, as in the long-line instance
-    __shared__ PatchShape<kLongLineVox>::Step buf0, buf1;
-    patch_group<F16, TABLE, kLongLineVox>(packed, nchunks, splits, quad, split, patches + 4 * quad, info, table, x, y,
-                                          z, out_r, out_i, N, buf0, buf1);
+    __shared__ PairShape128::Step buf0, buf1;
+    if (patch_taken(cls, patches, units, quad, kMode)) {
+        if (split >= splits_long) return;
+        patch_group<F16, TABLE, kLongLineVox, 2>(packed, nchunks, splits_long, quad, split, patches + 4 * quad, info,
+                                                 table, x, y, z, out_long_r, out_long_i, N, buf0, buf1);
+    } else if (group64_taken(cls, patches, units, quad, kMode)) {
+        if (split >= splits_lines) return;
+        patch_group<F16, TABLE, kLineVox, 4>(packed, nchunks, splits_lines, quad, split, patches + 4 * quad, info,
+                                             table, x, y, z, out_lines_r, out_lines_i, N, buf0, buf1);
+    }
 }
 
 // The 64-voxel line-pair instance: unit pairs whose 64-voxel lines pair up
-// (record flag 2), with the B table (16 KB per step, in the long-line
-// table's buffer) for pair 0's step and offset, or formed.
+// (record flag 2 or 3, outside the quads taken as four-line groups in
+// quad_mode), with the B table (16 KB per step, in the long-line table's
+// buffer) for pair 0's step and offset, or formed.
 template <bool F16, bool TABLE>
 __global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(3))) void fhd_gather_patch64_kernel(
-    const float *__restrict__ packed, int nchunks, int splits, int64_t pairs, int64_t units,
+    const float *__restrict__ packed, int nchunks, int splits, int64_t pairs, int64_t units, int quad_mode,
     const int *__restrict__ cls, const int4 *__restrict__ patches, const int *__restrict__ info,
     const float4 *__restrict__ table, const float *__restrict__ x, const float *__restrict__ y,
     const float *__restrict__ z, float *__restrict__ out_r, float *__restrict__ out_i, int N)
@@ -1582,10 +1716,10 @@ __global__ __launch_bounds__(kPatchBlock) __attribute__((amdgpu_waves_per_eu(3))
     const int64_t unit = xcd_unit(blockIdx.x, pairs * splits);
     const int64_t pair = unit % pairs;
     const int split = (int)(unit / pairs);
-    if (!pair64_taken(cls, patches, units, pair, TABLE ? kPatchTable : kPatchFormed)) return;
-    __shared__ PatchShape<kLineVox>::Step buf0, buf1;
-    patch_group<F16, TABLE, kLineVox>(packed, nchunks, splits, pair, split, patches + 2 * pair, info, table, x, y, z,
-                                      out_r, out_i, N, buf0, buf1);
+    if (!pair64_taken(cls, patches, units, pair, TABLE ? kPatchTable : kPatchFormed, quad_mode)) return;
+    __shared__ PairShape64::Step buf0, buf1;
+    patch_group<F16, TABLE, kLineVox, 2>(packed, nchunks, splits, pair, split, patches + 2 * pair, info, table, x,
+                                         y, z, out_r, out_i, N, buf0, buf1);
 }
 
 }  // namespace
@@ -1646,7 +1780,7 @@ int launch_line_instances(const GatherPlan &g, const int *cls, const int4 *patch
     // units no unit can take the line-pair (long-line, line) instance,
     // which is not launched
     const bool quads = g.quads > 0, long_pairs = (int64_t)N >= 2 * (int64_t)kUnitVox, whole_unit = N >= kUnitVox;
-    const bool direct_long = g.s_long == 1;
+    const bool direct_long = g.s_long == 1, direct_lines = g.s_lines == 1;
     if (quads && patch_table) {
         fhd_patch_table_kernel<F16><<<dim3((unsigned)g.steps), dim3(kPatchBlock), 0, stream>>>(
             packed, g.nchunks, cls, patches, g.blocks, info, patch_table);
@@ -1654,20 +1788,24 @@ int launch_line_instances(const GatherPlan &g, const int *cls, const int4 *patch
     }
     const int mode = !quads ? kPatchNone : patch_table ? kPatchTable : kPatchFormed;
     if (rc == FHD_OK && quads) {
-        const dim3 grid((unsigned)(g.quads * g.s_long));
-        float *out_r = direct_long ? rho_r : part_r, *out_i = direct_long ? rho_i : part_i;
+        // quads of long pairs take the long pairs' split count, four-line
+        // groups of 64-voxel lines the lines' one
+        const int s_quad = g.s_long > g.s_lines ? g.s_long : g.s_lines;
+        const dim3 grid((unsigned)(g.quads * s_quad));
+        float *long_r = direct_long ? rho_r : part_r, *long_i = direct_long ? rho_i : part_i;
+        float *lines_r = direct_lines ? rho_r : part_r, *lines_i = direct_lines ? rho_i : part_i;
         if (mode == kPatchTable) {
             TimedLaunch timed(F16 ? "fhd_gather_patch_kernel<true, true>" : "fhd_gather_patch_kernel<false, true>",
                               stream);
             fhd_gather_patch_kernel<F16, true><<<grid, dim3(kPatchBlock), 0, stream>>>(
-                packed, g.nchunks, g.s_long, g.quads, g.blocks, cls, patches, info, patch_table, x, y, z, out_r,
-                out_i, N);
+                packed, g.nchunks, g.s_long, g.s_lines, g.quads, g.blocks, cls, patches, info, patch_table, x, y, z,
+                long_r, long_i, lines_r, lines_i, N);
         } else {
             TimedLaunch timed(F16 ? "fhd_gather_patch_kernel<true, false>" : "fhd_gather_patch_kernel<false, false>",
                               stream);
             fhd_gather_patch_kernel<F16, false><<<grid, dim3(kPatchBlock), 0, stream>>>(
-                packed, g.nchunks, g.s_long, g.quads, g.blocks, cls, patches, info, nullptr, x, y, z, out_r, out_i,
-                N);
+                packed, g.nchunks, g.s_long, g.s_lines, g.quads, g.blocks, cls, patches, info, nullptr, x, y, z,
+                long_r, long_i, lines_r, lines_i, N);
         }
         rc = launch_status("fhd_gather_patch_kernel launch");
     }
@@ -1685,9 +1823,8 @@ int launch_line_instances(const GatherPlan &g, const int *cls, const int4 *patch
             direct_long ? rho_r : part_r, direct_long ? rho_i : part_i, N);
         rc = launch_status("fhd_gather_long_lines_kernel launch");
     }
-    // the 64-voxel line-pair and line instances share one split count
-    // (both take units of class kClassLines)
-    const bool direct_lines = g.s_lines == 1;
+    // the four-line groups, the 64-voxel line-pair and the line instances
+    // share one split count (all take units of class kClassLines)
     if (rc == FHD_OK && long_pairs) {
         const dim3 grid((unsigned)(g.pairs * g.s_lines));
         float *out_r = direct_lines ? rho_r : part_r, *out_i = direct_lines ? rho_i : part_i;
@@ -1695,23 +1832,23 @@ int launch_line_instances(const GatherPlan &g, const int *cls, const int4 *patch
             TimedLaunch timed(F16 ? "fhd_gather_patch64_kernel<true, true>" : "fhd_gather_patch64_kernel<false, true>",
                               stream);
             fhd_gather_patch64_kernel<F16, true><<<grid, dim3(kPatchBlock), 0, stream>>>(
-                packed, g.nchunks, g.s_lines, g.pairs, g.blocks, cls, patches, info, long_table, x, y, z, out_r,
-                out_i, N);
+                packed, g.nchunks, g.s_lines, g.pairs, g.blocks, mode, cls, patches, info, long_table, x, y, z,
+                out_r, out_i, N);
         } else {
             TimedLaunch timed(F16 ? "fhd_gather_patch64_kernel<true, false>"
                                   : "fhd_gather_patch64_kernel<false, false>",
                               stream);
             fhd_gather_patch64_kernel<F16, false><<<grid, dim3(kPatchBlock), 0, stream>>>(
-                packed, g.nchunks, g.s_lines, g.pairs, g.blocks, cls, patches, info, nullptr, x, y, z, out_r, out_i,
-                N);
+                packed, g.nchunks, g.s_lines, g.pairs, g.blocks, mode, cls, patches, info, nullptr, x, y, z, out_r,
+                out_i, N);
         }
         rc = launch_status("fhd_gather_patch64_kernel launch");
     }
     if (rc == FHD_OK && whole_unit) {
         TimedLaunch timed(F16 ? "fhd_gather_lines_kernel<true>" : "fhd_gather_lines_kernel<false>", stream);
         fhd_gather_lines_kernel<F16><<<dim3((unsigned)g.blocks, (unsigned)g.s_lines), dim3(kLinesBlock), 0,
-                                        stream>>>(packed, g.nchunks, g.s_lines, cls, patches, g.blocks, mode64, info,
-                                                  x, y, z, direct_lines ? rho_r : part_r,
+                                        stream>>>(packed, g.nchunks, g.s_lines, cls, patches, g.blocks, mode64, mode,
+                                                  info, x, y, z, direct_lines ? rho_r : part_r,
                                                   direct_lines ? rho_i : part_i, N);
         rc = launch_status("fhd_gather_lines_kernel launch");
     }

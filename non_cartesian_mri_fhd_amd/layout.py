@@ -146,52 +146,94 @@ def line_pair_quads(x, y, z, cls=None, block: int = 256, vox: int = 16, long_lin
     return quad & np.all(key[0::2] == key[0], axis=1)
 
 
-def line_pair64_pairs(x, y, z, cls=None, block: int = 256, vox: int = 16, line: int = 64,
-                      formed: bool = False):
-    """Per unit pair (units 2p, 2p + 1, both present), whether the F^H D
-    64-voxel line-pair instance takes it, by the classify kernel's record:
-    both units of class 2 with one step for the pair (bitwise), in the pair
-    the lines 2i + 1 of `line` voxels the lines 2i moved by one common
-    offset d (bitwise equal fp32 differences of their first voxels' x, y,
-    z, all finite; d from the pair's lines 0 and 1); and, unless `formed`,
-    pair 0 so too with the same step and d."""
-    x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
+def _pair64_records(x, y, z, cls, block: int, vox: int, line: int):
+    """Per unit pair, the classify kernel's 64-voxel records as the host
+    sees them: (flag 2 or 3, flag 3, key = step, d and e bits). Flag 2:
+    both units of class 2 with one step for the pair (bitwise), the lines
+    2i + 1 the lines 2i moved by one common offset d (bitwise equal fp32
+    differences of their first voxels' x, y, z, all finite; d from the
+    pair's lines 0 and 1). Flag 3: beyond that, the lines 4i + 2 the lines
+    4i moved by one common offset e (e from the pair's lines 0 and 2)."""
     unit = block * vox
-    if cls is None:
-        cls = gather_unit_classes(x, y, z, block, vox)[0]
     pairs = cls.size // 2
-    if pairs == 0:
-        return np.zeros(0, bool)
     nl = 2 * unit // line                          # lines per unit pair
     first = np.arange(pairs * nl) * line
-    ok_first = first + 1 < x.size
-    if not ok_first.all():
-        return np.zeros(pairs, bool)
+    if pairs == 0 or not (first + 1 < x.size).all():
+        z0 = np.zeros(pairs, bool)
+        return z0, z0, np.zeros((pairs, 7), np.uint32)
     fx, fy, fz = x[first], y[first], z[first]
     step = (x[first + 1] - fx).astype(np.float32).view(np.uint32).reshape(pairs, nl)
-    sx = (fx[1::2] - fx[0::2]).astype(np.float32)
-    sy = (fy[1::2] - fy[0::2]).astype(np.float32)
-    sz = (fz[1::2] - fz[0::2]).astype(np.float32)
-    lp = nl // 2
 
-    def bits(a):
-        return a.view(np.uint32).reshape(pairs, lp)
+    def offsets(k, per):
+        # line (per i + k) minus line (per i), per group of `per` lines
+        out = []
+        for a in (fx, fy, fz):
+            g = a.reshape(-1, per)
+            out.append((g[:, k] - g[:, 0]).astype(np.float32))
+        fin = np.isfinite(out[0]) & np.isfinite(out[1]) & np.isfinite(out[2])
+        bits = [o.view(np.uint32).reshape(pairs, nl // per) for o in out]
+        same = fin.reshape(pairs, -1).all(axis=1)
+        for b in bits:
+            same &= np.all(b == b[:, :1], axis=1)
+        return same, [b[:, 0] for b in bits]
 
-    SX, SY, SZ = bits(sx), bits(sy), bits(sz)
-    fin = (np.isfinite(sx) & np.isfinite(sy) & np.isfinite(sz)).reshape(pairs, lp)
-    shifted = (fin.all(axis=1) & np.all(SX == SX[:, :1], axis=1) & np.all(SY == SY[:, :1], axis=1)
-               & np.all(SZ == SZ[:, :1], axis=1))
+    shifted, d = offsets(1, 2)
+    grouped, e = offsets(2, 4)
     both = (cls[0:2 * pairs:2] == 2) & (cls[1:2 * pairs:2] == 2)
     # one step for the pair: the two units' first lines (each unit's lines
     # share its step, as class 2 says)
     common = step[:, 0] == step[:, nl // 2]
     ok = both & common & shifted
+    key = np.stack([step[:, 0], *d, *e], axis=1)
+    return ok, ok & grouped, key
+
+
+def line_group64_quads(x, y, z, cls=None, block: int = 256, vox: int = 16, line: int = 64,
+                       formed: bool = False):
+    """Per quad of four units (all present), whether the F^H D line-pair
+    instance takes it as four-line groups of 64-voxel lines: both unit
+    pairs' records flag 3 (see _pair64_records) with the same step, d and
+    e; and, unless `formed`, quad 0 so too with the same step and
+    offsets."""
+    x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
+    if cls is None:
+        cls = gather_unit_classes(x, y, z, block, vox)[0]
+    quads = cls.size // 4
+    if quads == 0:
+        return np.zeros(0, bool)
+    _, grp, key = _pair64_records(x, y, z, cls, block, vox, line)
+    grp, key = grp[:2 * quads], key[:2 * quads]
+    quad = grp[0::2] & grp[1::2] & np.all(key[0::2] == key[1::2], axis=1)
+    if formed:
+        return quad
+    if not quad[0]:
+        return np.zeros(quads, bool)
+    return quad & np.all(key[0::2] == key[0], axis=1)
+
+
+def line_pair64_pairs(x, y, z, cls=None, block: int = 256, vox: int = 16, line: int = 64,
+                      formed: bool = False):
+    """Per unit pair (units 2p, 2p + 1, both present), whether the F^H D
+    64-voxel line-pair instance takes it: its record is flag 2 or 3 (see
+    _pair64_records), its quad is not taken as four-line groups (in the
+    same mode, line_group64_quads); and, unless `formed`, pair 0 so too
+    with the same step and d."""
+    x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
+    if cls is None:
+        cls = gather_unit_classes(x, y, z, block, vox)[0]
+    pairs = cls.size // 2
+    if pairs == 0:
+        return np.zeros(0, bool)
+    ok, _, key = _pair64_records(x, y, z, cls, block, vox, line)
+    groups = line_group64_quads(x, y, z, cls, block, vox, line, formed)
+    in_group = np.zeros(pairs, bool)
+    in_group[:2 * groups.size] = np.repeat(groups, 2)
+    ok = ok & ~in_group
     if formed:
         return ok
     if not ok[0]:
         return np.zeros(pairs, bool)
-    key = np.stack([step[:, 0], SX[:, 0], SY[:, 0], SZ[:, 0]], axis=1)
-    return ok & np.all(key == key[0], axis=1)
+    return ok & np.all(key[:, :4] == key[0, :4], axis=1)
 
 
 def ramp_voxel_fractions(x, y, z, block: int = 256, vox: int = 16,

@@ -18,23 +18,24 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_only_for_the_profiled_workload():
-    for kernel, entry in bench.TRAFFIC.items():
-        other = "vdrandom256" if entry["workload"] != "vdrandom256" else "spiral128"
-        assert bench.measured_traffic(kernel, other) is None
+    for (kernel, workload), entry in bench.TRAFFIC.items():
+        other = "vdrandom256" if workload != "vdrandom256" else "spiral128"
+        if (kernel, other) not in bench.TRAFFIC:
+            assert bench.measured_traffic(kernel, other) is None
     assert bench.measured_traffic("fhd_grid_kernel", "spiral128") is None
 
 
 def test_traffic_follows_the_sources(tmp_path, monkeypatch):
     """A recorded figure holds only for the sources it was taken on."""
-    kernel, entry = next(iter(bench.TRAFFIC.items()))
+    (kernel, workload), entry = next(iter(bench.TRAFFIC.items()))
     src = tmp_path / "csrc"
     src.mkdir()
     for name in entry["sources"]:
         (src / name).write_bytes(open(os.path.join(bench.CSRC, name), "rb").read())
     monkeypatch.setattr(bench, "CSRC", str(src))
-    same = bench.measured_traffic(kernel, entry["workload"])
+    same = bench.measured_traffic(kernel, workload)
     (src / entry["sources"][0]).write_bytes(b"// edited\n" + (src / entry["sources"][0]).read_bytes())
-    assert bench.measured_traffic(kernel, entry["workload"]) is None
+    assert bench.measured_traffic(kernel, workload) is None
     if same is not None:
         assert same == entry["bytes_per_launch"]
 

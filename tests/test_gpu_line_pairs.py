@@ -3,11 +3,14 @@
 Quads of four units whose lines of 128 voxels, two by two, are one line and
 the same line moved by a common offset d (rows of a grid along y, or the
 two halves of rows of 256 along x) are summed about each line pair's
-centre; so are unit pairs whose lines of 64 voxels pair up (rows of 64).
-Each case states which quads or pairs the instances take (the host mirror
-of the classification, layout.line_pair_quads / line_pair64_pairs) and
+centre; so are quads of 64-voxel lines in groups of four at 0, d, e and
+e + d (rows of 64: rows y .. y + 3), about each group's centre, and unit
+pairs whose lines of 64 voxels only pair up. Each case states which quads
+or pairs the instances take (the host mirror of the classification,
+layout.line_pair_quads / line_group64_quads / line_pair64_pairs) and
 checks every voxel against the oracle; groups that break the structure
-fall back to the long-line (or 64-voxel line) instance.
+fall back to the long-line (or 64-voxel line-pair, or 64-voxel line)
+instance.
 fhd_compute_noalloc forms the B operands itself and takes every group with
 the structure: where both forms take the same groups its output is
 bitwise fhd_compute's.
@@ -57,7 +60,8 @@ def run(case, dev, paths=binding.FHD_GATHER_ALL, noalloc=False):
 
 def bend_rows(case, first_line, count, amount, line=128):
     """Moves lines first_line .. first_line + count - 1 (of `line` voxels)
-    by `amount` along y, breaking the common line-pair offset there."""
+    by `amount` along y, breaking the common line-pair offset there (or,
+    moving a whole line pair, only the four-line groups' second offset)."""
     y = case["y"].copy()
     for ln in range(first_line, first_line + count):
         y[ln * line:(ln + 1) * line] += np.float32(amount)
@@ -66,15 +70,26 @@ def bend_rows(case, first_line, count, amount, line=128):
 
 
 def cases64():
-    # unit pairs of 64-voxel lines (the 64-voxel line-pair instance): one
-    # pair; two pairs, the second bent (the line instance there); the first
-    # bent (no pair in the table form, the second in the formed one)
-    yield "64x32x4", grid_case((64, 32, 4), 3001, 970), [True], [True]
-    yield "64x64x4", grid_case((64, 64, 4), 2048, 971), [True, True], [True, True]
-    c = bend_rows(grid_case((64, 64, 4), 2048, 972), 128 + 1, 1, 1.0 / 512, line=64)
-    yield "second pair bent", c, [True, False], [True, False]
-    c = bend_rows(grid_case((64, 64, 4), 2048, 973), 3, 1, 1.0 / 512, line=64)
-    yield "first pair bent", c, [False, False], [False, True]
+    # 64-voxel lines: (name, case, four-line groups taken by quad, in the
+    # table form and formed; unit pairs taken by the 64-voxel line-pair
+    # instance, in the table form and formed). One unit pair (no quad);
+    # one quad; two quads; the second quad's first pair bent in one line
+    # (its other pair goes to the 64-voxel line-pair instance in the formed
+    # form; in the table form that instance's pair 0, inside a group, takes
+    # no table, so the line instance takes both); the first quad so bent
+    # (no group and no pair in the table forms; quad 1 and pair 1 in the
+    # formed ones); one group's second pair moved together (its quad's
+    # records flag 2 only: the 64-voxel line-pair instance takes both pairs)
+    yield "64x32x4", grid_case((64, 32, 4), 3001, 970), [], [], [True], [True]
+    yield "64x64x4", grid_case((64, 64, 4), 2048, 971), [True], [True], [False, False], [False, False]
+    yield ("64x64x8", grid_case((64, 64, 8), 2048, 974), [True, True], [True, True],
+           [False] * 4, [False] * 4)
+    c = bend_rows(grid_case((64, 64, 8), 2048, 972), 256 + 1, 1, 1.0 / 512, line=64)
+    yield "second quad bent", c, [True, False], [True, False], [False] * 4, [False, False, False, True]
+    c = bend_rows(grid_case((64, 64, 8), 2048, 973), 3, 1, 1.0 / 512, line=64)
+    yield "first quad bent", c, [False, False], [False, True], [False] * 4, [False, True, False, False]
+    c = bend_rows(grid_case((64, 64, 4), 2048, 975), 2, 2, 1.0 / 512, line=64)
+    yield "second offset broken", c, [False], [False], [True, True], [True, True]
 
 
 def cases():
@@ -123,14 +138,17 @@ def test_line_pairs_split_sums_repeatable(dev):
     assert metrics.rel_l2(a[0][idx], a[1][idx], *ref) <= TOL
 
 
-@pytest.mark.parametrize("name,case,taken,formed", list(cases64()), ids=[c[0] for c in cases64()])
-def test_64_voxel_line_pairs_match_the_oracle(dev, name, case, taken, formed):
+@pytest.mark.parametrize("name,case,groups,groups_f,pairs,pairs_f", list(cases64()),
+                         ids=[c[0] for c in cases64()])
+def test_64_voxel_line_groups_and_pairs_match_the_oracle(dev, name, case, groups, groups_f, pairs, pairs_f):
     cls = layout.gather_unit_classes(case["x"], case["y"], case["z"])[0]
     assert np.all(cls == 2), (name, cls)
-    assert layout.line_pair64_pairs(case["x"], case["y"], case["z"], cls).tolist() == taken, name
-    assert layout.line_pair64_pairs(case["x"], case["y"], case["z"], cls, formed=True).tolist() == formed, name
+    assert layout.line_group64_quads(case["x"], case["y"], case["z"], cls).tolist() == groups, name
+    assert layout.line_group64_quads(case["x"], case["y"], case["z"], cls, formed=True).tolist() == groups_f, name
+    assert layout.line_pair64_pairs(case["x"], case["y"], case["z"], cls).tolist() == pairs, name
+    assert layout.line_pair64_pairs(case["x"], case["y"], case["z"], cls, formed=True).tolist() == pairs_f, name
     ref = oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"], case["x"], case["y"], case["z"])
-    print("64-voxel line pairs: %s" % name, flush=True)
+    print("64-voxel lines: %s" % name, flush=True)
     got = run(case, dev)
     e = metrics.rel_l2(*got, *ref)
     bf = metrics.rel_l2(*run(case, dev, binding.FHD_GATHER_BF16X3), *ref)
@@ -138,5 +156,19 @@ def test_64_voxel_line_pairs_match_the_oracle(dev, name, case, taken, formed):
     e_na = metrics.rel_l2(*na, *ref)
     print("  rel-L2 default %.3g, bf16x3 %.3g, noalloc %.3g" % (e, bf, e_na), flush=True)
     assert e <= TOL and e_na <= TOL and bf <= TOL
-    if taken == formed:
+    if groups == groups_f and pairs == pairs_f:
         assert np.array_equal(got[0], na[0]) and np.array_equal(got[1], na[1]), name
+
+
+def test_64_voxel_line_groups_split_sums_repeatable(dev):
+    """Four-line groups over several sample splits: the same call twice
+    gives the same bits, and sampled voxels match the oracle."""
+    case = grid_case((64, 64, 32), 20000, 976, kmax=32.0)
+    assert layout.line_group64_quads(case["x"], case["y"], case["z"]).all()
+    a = run(case, dev)
+    b = run(case, dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    idx = inputs.voxel_subset(case["x"].size, 600, seed=977)
+    ref = oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"],
+                     case["x"][idx], case["y"][idx], case["z"][idx])
+    assert metrics.rel_l2(a[0][idx], a[1][idx], *ref) <= TOL

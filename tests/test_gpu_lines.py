@@ -168,6 +168,17 @@ def test_lines_zero_step_and_degenerate_angles(dev):
     scale = np.sqrt(np.mean(rr.astype(np.float64) ** 2 + ri.astype(np.float64) ** 2))
     assert np.max(np.abs(rr.reshape(-1, 64) - rr.reshape(-1, 64)[:, :1])) <= 1e-5 * scale
     assert np.max(np.abs(ri.reshape(-1, 64) - ri.reshape(-1, 64)[:, :1])) <= 1e-5 * scale
+    # four units in four-line groups (the line-pair instance's 64-voxel
+    # form): likewise equal to rounding
+    xg, yg, zg = inputs.coords_from_axis(64, 32, 8, AX64)
+    cg = dict(c, x=np.full_like(xg, np.float32(0.125)), y=yg, z=zg)
+    assert classes(cg) == [2, 2, 2, 2]
+    assert layout.line_group64_quads(cg["x"], cg["y"], cg["z"]).tolist() == [True]
+    rr, ri = gpu_fhd(cg, dev)
+    check("zero step, four-line groups", cg, rr, ri)
+    scale = np.sqrt(np.mean(rr.astype(np.float64) ** 2 + ri.astype(np.float64) ** 2))
+    assert np.max(np.abs(rr.reshape(-1, 64) - rr.reshape(-1, 64)[:, :1])) <= 1e-5 * scale
+    assert np.max(np.abs(ri.reshape(-1, 64) - ri.reshape(-1, 64)[:, :1])) <= 1e-5 * scale
     # one unit (the 64-voxel line instance): every pair column has the same
     # operands, so a line's voxels are equal bit for bit
     xs, ys, zs = inputs.coords_from_axis(64, 16, 4, AX64)

@@ -30,6 +30,9 @@ REL_L2_TOL = 5e-4
 LINES128 = ((128, 16, 4), (-0.5, 1.0 / 128, -0.5, 1.0 / 16, -0.5, 0.25))
 # 64 x 16 x 8: two units of 64-voxel lines (the 64-voxel instance)
 LINES64 = ((64, 16, 8), (-0.5, 1.0 / 64, -0.5, 1.0 / 16, -0.5, 0.125))
+# four units of 64-voxel lines in four-line groups (rows y .. y + 3: the
+# line-pair instance's 64-voxel form)
+GROUPS64 = ((64, 32, 8), (-0.5, 1.0 / 64, -0.5, 1.0 / 32, -0.5, 0.125))
 # one unit of 64-voxel lines, no pair (the 64-voxel line instance)
 LINES64_SOLO = ((64, 16, 4), (-0.5, 1.0 / 64, -0.5, 1.0 / 16, -0.5, 0.25))
 # one quad of four units whose lines pair up (the line-pair instance):
@@ -87,6 +90,7 @@ def forward(case, img, dev, paths):
 
 @pytest.mark.parametrize("grid,cls,quads,pairs64", [(LINES128, [3, 3], [], [False]),
                                                     (LINES64, [2, 2], [], [True]),
+                                                    (GROUPS64, [2, 2, 2, 2], [False], [False, False]),
                                                     (LINES64_SOLO, [2], [], []),
                                                     (PAIRS_Y, [3, 3, 3, 3], [True], [False, False]),
                                                     (PAIRS_X, [3, 3, 3, 3], [True], [False, False])])
@@ -95,6 +99,8 @@ def test_adjoint_line_form_is_fp32_class(dev, grid, cls, quads, pairs64):
     assert layout.gather_unit_classes(c["x"], c["y"], c["z"])[0].tolist() == cls
     assert layout.line_pair_quads(c["x"], c["y"], c["z"]).tolist() == quads
     assert layout.line_pair64_pairs(c["x"], c["y"], c["z"]).tolist() == pairs64
+    groups = layout.line_group64_quads(c["x"], c["y"], c["z"]).tolist()
+    assert groups == ([True] if grid is GROUPS64 else [False] * len(groups))
     ref = oracle.fhd(c["kx"], c["ky"], c["kz"], c["Dr"], c["Di"], c["x"], c["y"], c["z"])
     err = {}
     for p in PATHS:
@@ -134,7 +140,7 @@ def test_forward_line_form_is_fp32_class(dev, form):
     assert err["bf16x3"] > 2.0 * err["vector"], err
 
 
-@pytest.mark.parametrize("grid", [LINES128, LINES64, LINES64_SOLO, PAIRS_Y])
+@pytest.mark.parametrize("grid", [LINES128, LINES64, LINES64_SOLO, PAIRS_Y, GROUPS64])
 def test_amplitude_scaling_is_exact(dev, grid):
     """F^H (2^e D) = 2^e F^H D bit for bit on every path, for scales that
     move the largest |D| far outside fp16's range in both directions."""

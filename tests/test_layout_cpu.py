@@ -150,3 +150,29 @@ def test_forward_pairs_form_mirror():
     g2 = inputs.coords_from_axis(128, 16, 4, (-0.5, 1.0 / 128, -0.5, 1.0 / 32, 0.0, 0.25))
     xx, yy, zz = (np.concatenate((a, b)) for a, b in zip((x, y, z), g2))
     assert layout.forward_lines_form(xx, yy, zz) and not layout.forward_pairs_form(xx, yy, zz)
+
+
+def test_line_group64_mirror():
+    """Four-line groups of 64-voxel lines: rows y .. y + 3 of a grid with
+    rows of 64 (or two rows by two slices); a line moved in one group
+    breaks its quad (its unit pairs then pair up or not), a pair of lines
+    moved together keeps the pairs but breaks the group."""
+    from non_cartesian_mri_fhd_amd import inputs
+    ax = (-0.5, 1.0 / 64, -0.5, 1.0 / 64, -0.5, 0.25)
+    x, y, z = inputs.coords_from_axis(64, 64, 8, ax)
+    assert layout.line_group64_quads(x, y, z).tolist() == [True, True]
+    assert layout.line_pair64_pairs(x, y, z).tolist() == [False] * 4
+    x2, y2, z2 = inputs.coords_from_axis(64, 2, 128, (-0.5, 1.0 / 64, -0.5, 0.5, -0.5, 1.0 / 128))
+    assert layout.line_group64_quads(x2, y2, z2).tolist() == [True]
+    yb = y.copy()
+    yb[2 * 64:4 * 64] += np.float32(1.0 / 512)          # lines 2, 3 together
+    assert layout.line_group64_quads(x, yb, z).tolist() == [False, False]
+    assert layout.line_group64_quads(x, yb, z, formed=True).tolist() == [False, True]
+    # in the table form no quad is a group (quad 0 is not), so every pair
+    # with pair 0's step and d is the 64-voxel line-pair instance's
+    assert layout.line_pair64_pairs(x, yb, z).tolist() == [True] * 4
+    assert layout.line_pair64_pairs(x, yb, z, formed=True).tolist() == [True, True, False, False]
+    yc = y.copy()
+    yc[3 * 64:4 * 64] += np.float32(1.0 / 512)          # line 3 alone
+    assert layout.line_pair64_pairs(x, yc, z, formed=True).tolist() == [False, True, False, False]
+    assert layout.line_group64_quads(x[:8192], y[:8192], z[:8192]).tolist() == []
