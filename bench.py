@@ -525,7 +525,7 @@ def bench_other(args) -> int:
     axis = inputs.grid_axis_of(L)
     split = "false" if args.paths == "bf16x3" else "true"
     f_lines = args.paths != "vector" and layout.forward_lines_form(w["x"], w["y"], w["z"])
-    f_pairs = f_lines and layout.forward_pairs_form(w["x"], w["y"], w["z"])
+    f_pairs = args.paths != "vector" and layout.forward_pairs_form(w["x"], w["y"], w["z"])
     cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
     lp, lp64 = line_instance_masks(w, cls, args.paths)
     adj_kernel, adj_share = adjoint_kernel(cls, counts, args.paths, lp, lp64)
@@ -601,7 +601,7 @@ def bench_other(args) -> int:
         if n_adj:
             parts.append("F^H: " + path_dtype(args.paths, lines_adj))
         if n_fwd:
-            parts.append("F: " + path_dtype(args.paths, 1.0 if f_lines else 0.0))
+            parts.append("F: " + path_dtype(args.paths, 1.0 if f_lines or f_pairs else 0.0))
         dtype = "; ".join(parts)
     out = {
         "metric": "%s voxel-sample terms/s (%s)" % (args.op, args.workload),

@@ -228,9 +228,12 @@ int fhd_gather_paths(const void *packed, int M,
  * (bitwise equal differences of their first voxels' x, y, z; any such grid
  * with an even number of rows per slice, or rows of 256), F sums each such
  * line pair about its centre (one phasor per line pair and sample; each
- * tile of 16 line pairs scaled by one power of two). Otherwise F runs on
- * the vector ALUs in fp32 (the form fhd_forward_pack / fhd_forward_gather
- * always take). The choice is made on the device; the library allocates
+ * tile of 16 line pairs scaled by one power of two). Units of lines of 64
+ * voxels with one step take the same form where their lines come four by
+ * four at offsets 0, d, e and e + d from the first, common to all units
+ * (rows y .. y + 3 of a grid with rows of 64): one phasor per four lines.
+ * Otherwise F runs on the vector ALUs in fp32 (the form fhd_forward_pack
+ * / fhd_forward_gather always take). The choice is made on the device; the library allocates
  * its stream-ordered workspaces on `stream`.
  * Errors: FHD_ERR_INVALID_ARG, FHD_ERR_ALLOC, FHD_ERR_HIP.
  */

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kPackBlock) void fhd_forward_pack_kernel(
     const float *__restrict__ rho_r, const float *__restrict__ rho_i,
     float *__restrict__ packed, int N, int64_t N_pad, const int *__restrict__ gate)
 {
-    if (gate != nullptr && lines_form_ran(gate)) return;   // the line form took F
+    if (gate != nullptr && lines_form_ran(gate)) return;   // a matrix-core form took F
     // every lane stays to the end: the ramp test exchanges values between
     // the 8 lanes of a chunk (a chunk never straddles N_pad or a wave)
     const int64_t n = (int64_t)blockIdx.x * kPackBlock + threadIdx.x;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
     float *__restrict__ out_r, float *__restrict__ out_i, int M, const int *__restrict__ gate)
 {
-    if (gate != nullptr && lines_form_ran(gate)) return;   // the line form took F
+    if (gate != nullptr && lines_form_ran(gate)) return;   // a matrix-core form took F
     __shared__ float4 stage[2][kStageVec4];
     const float4 *src = reinterpret_cast<const float4 *>(packed);
 
@@ -511,8 +511,8 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) 
     const float *__restrict__ kx, const float *__restrict__ ky, const float *__restrict__ kz,
     float *__restrict__ out_r, float *__restrict__ out_i, int M)
 {
-    // the vector form takes F, or the line-pair form took it
-    if (!lines_form_ran(info) || pairs_form_ran(info)) return;
+    // the line-pair form took F, or the vector form takes it
+    if (pairs_form_ran(info) || !lines_form_ran(info)) return;
     __shared__ u32x4 stage[2][kFwdTileVec4];
     const int lane = threadIdx.x & 63, quarter_k = lane >> 4, col = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -670,23 +670,69 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(3))) 
 // 2 x 64 per line: the same matrix-core work per term, and half the phasor
 // work (one V per line pair and sample).
 //
-// fhd_forward_pairs_pack_kernel forms A in tiles of 16 line pairs (one
-// unit; K = 32 s + 8 (l / 16) + i: cos part for K < 128, then sin; side
-// (K / 64) % 2; j = K % 64) and checks the rule; fhd_forward_pairs_kernel
-// walks the tiles with each wave's B (both sides) in registers. In the
-// fp16 form a tile's operands share one power-of-two scale (the tile's
-// largest |value| times 2^sh in [2^14, 2^15)), undone once per tile.
+// Units of 64-voxel lines (class kClassLines) whose lines come four by
+// four at 0, d, e and e + d from line 4i (record flag 3 in every unit
+// pair, pair 0's step and offsets throughout; rows y .. y + 3 of a grid
+// with rows of 64) take the same form with four sides of 32 columns: the
+// group's voxels at c + sigma_1 d / 2 + sigma_2 e / 2 + o_j (line 3 - s of
+// the group) and their reflections (line s), side s = (sigma_1, sigma_2)
+// = (s & 1 ? -1 : 1, s & 2 ? -1 : 1), j < 32, c = x_c(4i) + d / 2 + e / 2;
+// again K = 2 x 128 per group and sample.
+//
+// fhd_forward_pairs_pack_kernel forms A in tiles of 16 groups (one unit;
+// K = 32 s + 8 (l / 16) + i: cos part for K < 128, then sin; within a
+// part, side (K % 128) / (LINE / 2), j = K % (LINE / 2)) and checks the
+// rule; fhd_forward_pairs_kernel walks the tiles with each wave's B (all
+// sides) in registers. In the fp16 form a tile's operands share one
+// power-of-two scale (the tile's largest |value| times 2^sh in [2^14,
+// 2^15)), undone once per tile.
 constexpr int kFwpTilePairs = 16;
 constexpr int kFwpKSteps = 2 * 2 * kFwdPairs / 32;      // 8 products of K = 32
 constexpr int kFwpOpsVec4 = kFwpKSteps * 4 * 64;
 constexpr int kFwpTileVec4 = kFwpOpsVec4 + kFwpTilePairs;   // then (c_x, c_y, c_z, sh) per pair
 static_assert(2 * kFwpTilePairs * kLongLineVox == kUnitVox, "a tile of line pairs is one unit");
+static_assert(4 * kFwpTilePairs * kLineVox == kUnitVox, "a tile of four-line groups is one unit");
+
+// The group kind of a call, from pair 0's record: 128-voxel line pairs
+// (flag 1) or four-line groups of 64-voxel lines (flag 3); else none.
+enum : int { kFwpNone = 0, kFwpPairs128 = 1, kFwpGroups64 = 3 };
+__device__ __forceinline__ int fwp_kind(const int4 *__restrict__ patches)
+{
+    const int f = patches[0].x;
+    return f == kFwpPairs128 || f == kFwpGroups64 ? f : kFwpNone;
+}
+
+// Whether unit `unit` has the group structure of the call's kind, with
+// pair 0's step and offsets.
+__device__ __forceinline__ bool fwp_unit_ok(const int *__restrict__ cls, const int4 *__restrict__ patches,
+                                            const int *__restrict__ info, int64_t unit, int kind)
+{
+    const int4 r0 = patches[2 * (unit / 2)], r1 = patches[2 * (unit / 2) + 1], q0 = patches[0], q1 = patches[1];
+    const bool same = r0.x == q0.x && r0.y == q0.y && r1.x == q1.x && r1.y == q1.y && r1.z == q1.z;
+    if (kind == kFwpPairs128) return info[0] != 0 && cls[unit] == kClassLongPair && same && r0.y == info[1];
+    if (kind == kFwpGroups64)
+        return cls[unit] == kClassLines && same && r0.z == q0.z && r0.w == q0.w && r1.w == q1.w;
+    return false;
+}
+
+// Unit `unit`'s voxels of row `row` (a group of SIDES lines of LINE) and
+// column K of the operand, as the pre-pass pairs them.
+template <int LINE, int SIDES>
+__device__ __forceinline__ void fwp_voxels(int64_t unit, int row, int K, int64_t *up, int64_t *dn)
+{
+    constexpr int kHalf = LINE / 2;
+    const int kk = K % (2 * kFwdPairs), side = kk / kHalf, j = kk % kHalf;
+    const int64_t row0 = unit * kUnitVox + (int64_t)(SIDES * row) * LINE;
+    *up = row0 + (int64_t)(SIDES - 1 - side) * LINE + kHalf + j;
+    *dn = row0 + (int64_t)side * LINE + kHalf - 1 - j;
+}
 static_assert(kFwpKSteps == 2 * (kFwdBlock / 64), "two k steps per pre-pass wave");
 
 // One workgroup per unit (tile): wave w forms k steps 2 w and 2 w + 1
-// (lane l: line pair l % 16), the first 16 lanes of wave 0 the pairs'
-// centres; the first lane checks the unit's record against pair 0's and,
-// when they differ, sets info[3] (the line-pair form then stands aside).
+// (lane l: row l % 16, a line pair or a four-line group), the first 16
+// lanes of wave 0 the rows' centres; the first lane checks the unit
+// against pair 0's record and, when it differs (or pair 0 has no group
+// kind), sets info[3] (the line-pair form then stands aside).
 template <bool F16>
 __global__ __launch_bounds__(kFwdBlock) void fhd_forward_pairs_pack_kernel(
     const float *__restrict__ x, const float *__restrict__ y, const float *__restrict__ z,
@@ -695,7 +741,11 @@ __global__ __launch_bounds__(kFwdBlock) void fhd_forward_pairs_pack_kernel(
 {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, row = lane & 15, quarter_k = lane >> 4;
     const int64_t unit = blockIdx.x;
-    const int64_t line_a = unit * kUnitVox + (int64_t)(2 * row) * kLongLineVox, line_b = line_a + kLongLineVox;
+    const int kind = fwp_kind(patches);   // uniform
+    if (threadIdx.x == 0 && !fwp_unit_ok(cls, patches, info, unit, kind)) atomicOr(&info[3], 1);
+    if (kind == kFwpNone) return;
+    const bool pairs = kind == kFwpPairs128;
+    const int line = pairs ? kLongLineVox : kLineVox, sides = pairs ? 2 : 4;
     float re[2][kChunk], im[2][kChunk];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -703,10 +753,12 @@ __global__ __launch_bounds__(kFwdBlock) void fhd_forward_pairs_pack_kernel(
 #pragma unroll
         for (int i = 0; i < kChunk; ++i) {
             const int K = 32 * s + 8 * quarter_k + i;
-            const bool sine = K >= 2 * kFwdPairs, side1 = ((K / kFwdPairs) & 1) != 0;
-            const int j = K % kFwdPairs;
-            const int64_t up = (side1 ? line_a : line_b) + kFwdPairs + j;
-            const int64_t dn = (side1 ? line_b : line_a) + kFwdPairs - 1 - j;
+            const bool sine = K >= 2 * kFwdPairs;
+            int64_t up, dn;
+            if (pairs)
+                fwp_voxels<kLongLineVox, 2>(unit, row, K, &up, &dn);
+            else
+                fwp_voxels<kLineVox, 4>(unit, row, K, &up, &dn);
             const float ur = rho_r[up], ui = rho_i[up], dr = rho_r[dn], di = rho_i[dn];
             re[h][i] = sine ? ui - di : ur + dr;   // Q_i | P_r
             im[h][i] = sine ? dr - ur : ui + di;   // -Q_r | P_i
@@ -756,19 +808,20 @@ __global__ __launch_bounds__(kFwdBlock) void fhd_forward_pairs_pack_kernel(
         t[2 * 64] = (u32x4){ih[0], ih[1], ih[2], ih[3]};
         t[3 * 64] = (u32x4){il[0], il[1], il[2], il[3]};
     }
-    const int4 r0 = patches[2 * (unit / 2)], r1 = patches[2 * (unit / 2) + 1];
     if (w == 0 && quarter_k == 0) {
+        // the row's centre: x_c of its first line plus d / 2 (plus e / 2)
+        const int4 r0 = patches[2 * (unit / 2)], r1 = patches[2 * (unit / 2) + 1];
         const float dx = __int_as_float(r0.y);
-        const float cx = __builtin_fmaf(0.5f * (float)(kLongLineVox - 1), dx, x[line_a]) + 0.5f * __int_as_float(r1.x);
-        const float cy = y[line_a] + 0.5f * __int_as_float(r1.y), cz = z[line_a] + 0.5f * __int_as_float(r1.z);
+        const int64_t first = unit * kUnitVox + (int64_t)(sides * row) * line;
+        float cx = __builtin_fmaf(0.5f * (float)(line - 1), dx, x[first]) + 0.5f * __int_as_float(r1.x);
+        float cy = y[first] + 0.5f * __int_as_float(r1.y), cz = z[first] + 0.5f * __int_as_float(r1.z);
+        if (!pairs) {
+            cx += 0.5f * __int_as_float(r0.z);
+            cy += 0.5f * __int_as_float(r0.w);
+            cz += 0.5f * __int_as_float(r1.w);
+        }
         tiles[unit * kFwpTileVec4 + kFwpOpsVec4 + row] =
             (u32x4){__float_as_uint(cx), __float_as_uint(cy), __float_as_uint(cz), (unsigned)sh};
-    }
-    if (threadIdx.x == 0) {
-        const int4 q0 = patches[0], q1 = patches[1];
-        const bool ok = info[0] != 0 && cls[unit] == kClassLongPair && r0.x == 1 && q0.x == 1 &&
-                        r0.y == info[1] && r0.y == q0.y && r1.x == q1.x && r1.y == q1.y && r1.z == q1.z;
-        if (!ok) atomicOr(&info[3], 1);
     }
 }
 
@@ -800,22 +853,27 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(2))) 
         sky[t] = live ? ky[m[t]] : 0.0f;
         skz[t] = live ? kz[m[t]] : 0.0f;
     }
-    // B operands, held for the whole walk: K = 32 s + 8 (l / 16) + i,
-    // cos (K < 128) or sin of 2 pi (kx (j + 1/2) dx +- k . d / 2), j = K % 64,
-    // + for side 0 ((K / 64) % 2 == 0)
+    // B operands, held for the whole walk: K = 32 s + 8 (l / 16) + i, cos
+    // (K < 128) or sin of 2 pi (kx (j + 1/2) dx + sigma_1 k . d / 2 +
+    // sigma_2 k . e / 2) for side (K % 128) / (LINE / 2), j = K % (LINE / 2)
+    const bool pairs = r0.x == kFwpPairs128;   // uniform
+    const int half = pairs ? kFwdPairs : kLineVox / 2;
+    const float hex = __int_as_float(r0.z), hey = __int_as_float(r0.w), hez = __int_as_float(r1.w);
     u32x4 bh[kFwdColumns][kFwpKSteps], bl[kFwdColumns][kFwpKSteps];
 #pragma unroll
     for (int t = 0; t < kFwdColumns; ++t) {
         const float hd = 0.5f * __builtin_fmaf(skx[t], ddx, __builtin_fmaf(sky[t], ddy, skz[t] * ddz));
+        const float he = pairs ? 0.0f : 0.5f * __builtin_fmaf(skx[t], hex, __builtin_fmaf(sky[t], hey, skz[t] * hez));
 #pragma unroll
         for (int s = 0; s < kFwpKSteps; ++s) {
             float v[kChunk];
 #pragma unroll
             for (int i = 0; i < kChunk; ++i) {
-                const int K = 32 * s + 8 * quarter_k + i;
-                const int j = K % kFwdPairs;
-                const bool side1 = ((K / kFwdPairs) & 1) != 0;
-                const float a = __builtin_fmaf(skx[t], (float)(2 * j + 1) * hdx, side1 ? -hd : hd);
+                const int K = 32 * s + 8 * quarter_k + i, kk = K % (2 * kFwdPairs);
+                const int side = kk / half, j = kk % half;
+                const float s1 = (side & 1) ? -1.0f : 1.0f, s2 = (side & 2) ? -1.0f : 1.0f;
+                const float off = pairs ? s1 * hd : __builtin_fmaf(s2, he, s1 * hd);
+                const float a = __builtin_fmaf(skx[t], (float)(2 * j + 1) * hdx, off);
                 v[i] = K < 2 * kFwdPairs ? __builtin_amdgcn_cosf(a) : __builtin_amdgcn_sinf(a);
             }
             unsigned h[4], l[4];

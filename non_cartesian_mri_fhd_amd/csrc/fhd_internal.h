@@ -442,14 +442,18 @@ int launch_reduce(const float *part_r, const float *part_i, int splits, int64_t 
 // fhd.hip: adjoint F^H D
 int launch_pack(const float *kx, const float *ky, const float *kz, const float *Dr, const float *Di,
                 int M, float *packed, hipStream_t stream);
-// Whether the forward operator's line form ran (and the vector form is to
-// stand aside): info as launch_classify leaves it, with info[2] set by the
-// line pre-pass when some line breaks the rule.
-__device__ __forceinline__ bool lines_form_ran(const int *info) { return info[0] != 0 && info[2] == 0; }
-// Whether its line-pair form ran (the line form then stands aside too):
-// info[3] set by the line-pair pre-pass when some unit breaks that form's
-// rule.
-__device__ __forceinline__ bool pairs_form_ran(const int *info) { return info[0] != 0 && info[3] == 0; }
+// Whether the forward operator's line-pair form ran (its line form then
+// stands aside): info as launch_classify leaves it, with info[3] set by
+// the line-pair pre-pass (which runs first on that path) when some unit
+// breaks that form's rule.
+__device__ __forceinline__ bool pairs_form_ran(const int *info) { return info[3] == 0; }
+// Whether one of its matrix-core forms ran (and the vector form is to
+// stand aside): the line-pair form, or the line form, info[2] set by the
+// line pre-pass when some line breaks that form's rule.
+__device__ __forceinline__ bool lines_form_ran(const int *info)
+{
+    return pairs_form_ran(info) || (info[0] != 0 && info[2] == 0);
+}
 
 // Classes of the ceil(N / kUnitVox) units into cls; info[0] = 1 if the
 // first pair is of class kClassLongPair, info[1] its step's bits, info[2]

@@ -262,26 +262,36 @@ def forward_lines_form(x, y, z, block: int = 256, vox: int = 16, long_line: int 
     return bool(np.all(cls == 3) and dx.size and np.all(dx.view(np.uint32) == dx.view(np.uint32)[0]))
 
 
-def forward_pairs_form(x, y, z, block: int = 256, vox: int = 16, long_line: int = 128) -> bool:
-    """Whether fhd_forward takes its matrix-core line-pair form: the line
-    form's rule, and in every unit pair the lines 2i + 1 the lines 2i moved
-    by one offset d (bitwise equal fp32 differences of their first voxels'
-    x, y, z, all finite), with pair 0's step and d throughout (the classify
-    kernel's line-pair records, flag 1)."""
-    if not forward_lines_form(x, y, z, block, vox, long_line):
-        return False
+def forward_pairs_form(x, y, z, block: int = 256, vox: int = 16, long_line: int = 128,
+                       line: int = 64) -> bool:
+    """Whether fhd_forward takes its matrix-core line-pair form: either the
+    line form's rule and, in every unit pair, the lines 2i + 1 the lines
+    2i moved by one offset d (bitwise equal fp32 differences of their first
+    voxels' x, y, z, all finite), with pair 0's step and d throughout (the
+    classify kernel's records, flag 1); or every unit of class 2, a whole
+    number of unit pairs, and every pair's 64-voxel lines in four-line
+    groups with pair 0's step, d and e (flag 3, see _pair64_records)."""
     x, y, z = (np.asarray(a, np.float32) for a in (x, y, z))
-    pairs = x.size // (2 * block * vox)
-    nl = 2 * block * vox // long_line              # lines per unit pair
-    first = np.arange(pairs * nl) * long_line
-    fx, fy, fz = x[first], y[first], z[first]
-    d = [(a[1::2] - a[0::2]).astype(np.float32) for a in (fx, fy, fz)]
-    if not all(np.all(np.isfinite(a)) for a in d):
+    N = x.size
+    if N == 0 or N % (2 * block * vox) != 0:
         return False
-    bits = [a.view(np.uint32).reshape(pairs, nl // 2) for a in d]
-    # within each pair (the record), then pair 0's throughout (the step is
-    # one throughout by the line form's rule)
-    return bool(all(np.all(b == b[0, 0]) for b in bits))
+    if forward_lines_form(x, y, z, block, vox, long_line):
+        pairs = N // (2 * block * vox)
+        nl = 2 * block * vox // long_line              # lines per unit pair
+        first = np.arange(pairs * nl) * long_line
+        fx, fy, fz = x[first], y[first], z[first]
+        d = [(a[1::2] - a[0::2]).astype(np.float32) for a in (fx, fy, fz)]
+        if not all(np.all(np.isfinite(a)) for a in d):
+            return False
+        bits = [a.view(np.uint32).reshape(pairs, nl // 2) for a in d]
+        # within each pair (the record), then pair 0's throughout (the step
+        # is one throughout by the line form's rule)
+        return bool(all(np.all(b == b[0, 0]) for b in bits))
+    cls = gather_unit_classes(x, y, z, block, vox)[0]
+    if not np.all(cls == 2):
+        return False
+    _, grp, key = _pair64_records(x, y, z, cls, block, vox, line)
+    return bool(grp.all() and np.all(key == key[0]))
 
 
 def ramp_voxel_fraction(x, y, z, block: int = 256, vox: int = 16) -> float:

@@ -122,17 +122,20 @@ def test_cg_tolerance_stop_inside_a_batch(dev, stop):
     check("cg stop at %d" % stop, rr, ri, ref.real, ref.imag)
 
 
-@pytest.mark.parametrize("paths", ["all", "bf16x3", "vector"])
-def test_cg_line_form_matches_oracle_cg(dev, paths):
-    """CG with both operators in their matrix-core line form: 128 x 16 x 4
+@pytest.mark.parametrize("shape,paths", [((128, 16, 4), "all"), ((128, 16, 4), "bf16x3"),
+                                         ((128, 16, 4), "vector"), ((64, 32, 4), "all")])
+def test_cg_line_form_matches_oracle_cg(dev, shape, paths):
+    """CG with both operators in their matrix-core forms: 128 x 16 x 4
     voxels (an aligned pair of units of 128-voxel lines, so F^H takes the
-    long-line instance and F its line form), 12,000 random samples in the
-    grid's Nyquist box, 20 iterations, against the oracle's fp64 CG; the
-    vector paths and the split-bf16 form on the same case."""
-    shape, axis = (128, 16, 4), (-0.5, 1.0 / 128, -0.5, 1.0 / 16, -0.5, 0.25)
+    long-line instance and F its line-pair form) or 64 x 32 x 4 (a unit
+    pair of 64-voxel lines: F^H as line pairs, F as four-line groups),
+    12,000 random samples in the grid's Nyquist box, 20 iterations, against
+    the oracle's fp64 CG; the vector paths and the split-bf16 form on the
+    first case."""
+    axis = (-0.5, 1.0 / shape[0], -0.5, 1.0 / shape[1], -0.5, 1.0 / shape[2])
     x, y, z = inputs.coords_from_axis(*shape, axis)
-    assert layout.gather_unit_classes(x, y, z)[0].tolist() == [3, 3]
-    assert layout.forward_lines_form(x, y, z)
+    assert layout.gather_unit_classes(x, y, z)[0].tolist() == ([3, 3] if shape[0] == 128 else [2, 2])
+    assert layout.forward_pairs_form(x, y, z)
     rng = np.random.default_rng(75)
     M = 12000
     k = np.stack([rng.uniform(-n / 2, n / 2, M) for n in shape]).astype(np.float32)
@@ -144,6 +147,6 @@ def test_cg_line_form_matches_oracle_cg(dev, paths):
     rr, ri, done, res = run(case, dev, iters, paths=code)
     ref, ref_res = oracle.cg(k[0], k[1], k[2], D[0], D[1], x, y, z, iters=iters)
     assert done == iters == len(ref_res) - 1
-    check("cg line form (%s), %d iterations" % (paths, iters), rr, ri, ref.real, ref.imag)
+    check("cg line form %s (%s), %d iterations" % (shape, paths, iters), rr, ri, ref.real, ref.imag)
     assert np.allclose(res, ref_res, rtol=2e-3, atol=0), (res, ref_res)
 

@@ -4,8 +4,10 @@ voxels, and through adjointness with F^H D. The line form takes F when
 every aligned pair of 4096-voxel units is lines of 128 voxels along x with
 one step; the line-pair form when, beyond that, the lines 2i + 1 are the
 lines 2i moved by one common offset (rows one step apart, or the halves of
-rows of 256). Swapping the rows two by two keeps the line form's rule and
-breaks the line-pair form's.
+rows of 256), and also when the units are 64-voxel lines in four-line
+groups at 0, d, e and e + d (rows y .. y + 3 of a grid with rows of 64).
+Swapping the rows two by two keeps the line form's rule and breaks the
+line-pair form's.
 
 Gate as in test_gpu_parity: relative L2 <= 5e-4 and every element within
 10x that bound times the reference's rms. Both forms compute in split
@@ -89,6 +91,43 @@ def test_forward_lines_grids(dev, shape, axis, M, form):
     k = inputs.random_case(1, M, seed=sum(shape) + M, kmax=shape[0] / 2.0)
     img = inputs.random_image(x.size, seed=M + 5)
     check("forward %s %s M=%d" % (form, shape, M), k, x, y, z, img, *gpu_forward(k, x, y, z, img, dev))
+
+
+@pytest.mark.parametrize("shape,M", [((64, 32, 4), 3000),   # one unit pair of groups
+                                     ((64, 64, 8), 1500),   # four unit pairs
+                                     ((64, 2, 64), 777)])   # groups across two slices
+def test_forward_groups_of_64_voxel_lines(dev, shape, M):
+    axis = (-0.5, 1.0 / shape[0], -0.5, 1.0 / shape[1], -0.5, 1.0 / shape[2])
+    x, y, z = inputs.coords_from_axis(*shape, axis)
+    assert np.all(layout.gather_unit_classes(x, y, z)[0] == 2)
+    assert layout.forward_pairs_form(x, y, z) and not layout.forward_lines_form(x, y, z)
+    k = inputs.random_case(1, M, seed=sum(shape) + M, kmax=shape[0] / 2.0)
+    img = inputs.random_image(x.size, seed=M + 7)
+    check("forward groups %s M=%d" % (shape, M), k, x, y, z, img, *gpu_forward(k, x, y, z, img, dev))
+
+
+def test_forward_groups_against_vector_form(dev):
+    """Rows of 64 in four-line groups (the line-pair form) and the same
+    voxels with one group's second line pair moved apart from the rest in
+    the order (groups broken: the vector form) give the same D to
+    rounding; a grid whose groups differ from pair 0's takes the vector
+    form too."""
+    k = inputs.make_kspace("spiral32")
+    x, y, z = inputs.coords_from_axis(64, 32, 8, (-0.5, 1.0 / 64, -0.5, 1.0 / 32, -0.5, 0.125))
+    img = inputs.random_image(x.size, seed=35)
+    # lines 2, 3 after lines 4 .. 7: the first two groups' e are then +4
+    # and -4 rows
+    perm = np.arange(x.size).reshape(-1, 64)
+    perm = np.concatenate([perm[:2], perm[4:8], perm[2:4], perm[8:]]).reshape(-1)
+    assert layout.forward_pairs_form(x, y, z)
+    assert not layout.forward_pairs_form(x[perm], y[perm], z[perm])
+    a = gpu_forward(k, x, y, z, img, dev)
+    b = gpu_forward(k, x[perm], y[perm], z[perm], (img[0][perm], img[1][perm]), dev)
+    check("groups", k, x, y, z, img, *a)
+    check("groups broken", k, x[perm], y[perm], z[perm], (img[0][perm], img[1][perm]), *b)
+    diff = metrics.rel_l2(a[0], a[1], b[0].astype(np.float64), b[1].astype(np.float64))
+    print("groups vs vector form: rel diff %.2e" % diff)
+    assert 0 < diff < 2e-5
 
 
 def test_forward_pairs_against_line_form(dev):

@@ -114,9 +114,9 @@ def test_adjoint_line_form_is_fp32_class(dev, grid, cls, quads, pairs64):
     assert err["bf16x3"] > 2.0 * err["vector"], err
 
 
-@pytest.mark.parametrize("form", ["pairs", "lines"])
+@pytest.mark.parametrize("form", ["pairs", "lines", "groups"])
 def test_forward_line_form_is_fp32_class(dev, form):
-    c = exact_phase_case(LINES128, 2003, seed=911)
+    c = exact_phase_case(GROUPS64 if form == "groups" else LINES128, 2003, seed=911)
     if form == "lines":
         # rows swapped two by two: the line form (the line-pair form's
         # common offset broken)
@@ -124,8 +124,8 @@ def test_forward_line_form_is_fp32_class(dev, form):
         rows[2::4], rows[3::4] = rows[3::4].copy(), rows[2::4].copy()
         perm = (rows[:, None] * 128 + np.arange(128)).reshape(-1)
         c = dict(c, x=c["x"][perm], y=c["y"][perm], z=c["z"][perm])
-    assert layout.forward_lines_form(c["x"], c["y"], c["z"])
-    assert layout.forward_pairs_form(c["x"], c["y"], c["z"]) == (form == "pairs")
+    assert layout.forward_lines_form(c["x"], c["y"], c["z"]) == (form != "groups")
+    assert layout.forward_pairs_form(c["x"], c["y"], c["z"]) == (form != "lines")
     # an image of dyadic values: rho enters the sums exactly
     rng = np.random.default_rng(912)
     img = tuple((rng.integers(-512, 512, c["x"].size) / 256.0).astype(np.float32) for _ in range(2))
