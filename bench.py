@@ -113,7 +113,7 @@ def roof_terms(parts) -> float:
 # (vector-ALU terms are fp32 on every choice).
 PATH_DTYPE = {
     "all": "f16x3: fp32 operands split into fp16 hi + lo, 3 fp16 products per fp32 product, "
-           "fp32 accumulation (fp32-class, ~2^-22 per product)",
+           "fp32 accumulation (fp32-class, within 2^-21 per product)",
     "bf16x3": "bf16x3: fp32 operands split into bf16 hi + lo, 3 bf16 products per fp32 product, "
               "fp32 accumulation (16-bit operands, ~2^-16 per product)",
     "vector": "f32",

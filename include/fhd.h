@@ -75,9 +75,10 @@ extern "C" {
  *                     bits together; amplitudes scaled by a power of two
  *                     into fp16's range first, and the sums scaled back),
  *                     three fp16 products per fp32 product with fp32
- *                     accumulation: per product within about 3 x 2^-24
- *                     relative of the fp32 product, the same order as fp32
- *                     rounding and below the hardware sine's error.
+ *                     accumulation: per product within 2^-21 relative of
+ *                     the exact product at worst and about 2^-24 on
+ *                     average, the order of fp32's own rounding (2^-24)
+ *                     and below the hardware sine's error (about 2^-21).
  *   FHD_GATHER_VECTOR every unit on the vector ALUs in fp32.
  *   FHD_GATHER_BF16X3 lines on the matrix cores as above but with bf16 parts
  *                     (16 significant bits together): per product within
