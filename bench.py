@@ -127,22 +127,25 @@ PATH_DTYPE = {
 # until the counters are taken again.
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 _GATHER_SRC = ["fhd.hip", "fhd_internal.h"]
-_GATHER_SHA = "8b8d10af332b78a238db7ad7c2e724b61a106434e580a65f6d0f66263543ebe5"
+_GATHER_SHA = "cba32e94859672a2f0d1e19f25045710c65063d17b4930119218f8b2e90852eb"
+_FORWARD_SRC = ["fhd_forward.hip", "fhd_internal.h"]
+_FORWARD_SHA = "8c440b35b20c688261902ca9077eae637251504a0f197779fa1aaf9fd35bfd1f"
 TRAFFIC = {
     ("fhd_gather_patch_kernel<true, true>", "spiral128"): {
         "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
-        "bytes_per_launch": (108297.0 * 2.0 + 65755.0 * 1.0) * 1024},
+        "bytes_per_launch": (108264.9 * 2.0 + 65678.8 * 1.0) * 1024},
     ("fhd_gather_kernel<16, true>", "spiral128"): {
         "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
-        "bytes_per_launch": (52931.4 * 2.0 + 87040.3 * 1.0) * 1024},
+        "bytes_per_launch": (52915.8 * 2.0 + 87040.0 * 1.0) * 1024},
     ("fhd_gather_patch_kernel<true, true>", "radial64"): {
-        "sources": _GATHER_SRC,
-        "sha256": "c6d15134c31e40f9e1c69d34de5c5fa321d115bff07ef9cbf600f83d2a11f908",
-        "bytes_per_launch": (35071.8 * 2.0 + 69324.2 * 1.0) * 1024},
+        "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
+        "bytes_per_launch": (35071.8 * 2.0 + 69286.5 * 1.0) * 1024},
     ("fhd_forward_pairs_kernel<true>", "spiral128"): {
-        "sources": ["fhd_forward.hip", "fhd_internal.h"],
-        "sha256": "315294ad4d584c3fb6b3dd1c63f84b9d1539da5ef195be38b1855f31ce035ab4",
-        "bytes_per_launch": (74313.4 * 2.0 + 5468.75 * 1.0) * 1024},
+        "sources": _FORWARD_SRC, "sha256": _FORWARD_SHA,
+        "bytes_per_launch": (74359.9 * 2.0 + 5468.8 * 1.0) * 1024},
+    ("fhd_forward_pairs_kernel<true>", "radial64"): {
+        "sources": _FORWARD_SRC, "sha256": _FORWARD_SHA,
+        "bytes_per_launch": (8707.0 * 2.0 + 512.0 * 1.0) * 1024},
 }
 
 

@@ -41,6 +41,7 @@
 #include <cmath>
 #include <cstdint>
 #include <string>
+#include <type_traits>
 
 #include "fhd_internal.h"
 
@@ -747,23 +748,26 @@ __global__ __launch_bounds__(kFwdBlock) void fhd_forward_pairs_pack_kernel(
     const bool pairs = kind == kFwpPairs128;
     const int line = pairs ? kLongLineVox : kLineVox, sides = pairs ? 2 : 4;
     float re[2][kChunk], im[2][kChunk];
+    auto gather_rows = [&](auto line_c, auto sides_c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int s = 2 * w + h;
+        for (int h = 0; h < 2; ++h) {
+            const int s = 2 * w + h;
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            const int K = 32 * s + 8 * quarter_k + i;
-            const bool sine = K >= 2 * kFwdPairs;
-            int64_t up, dn;
-            if (pairs)
-                fwp_voxels<kLongLineVox, 2>(unit, row, K, &up, &dn);
-            else
-                fwp_voxels<kLineVox, 4>(unit, row, K, &up, &dn);
-            const float ur = rho_r[up], ui = rho_i[up], dr = rho_r[dn], di = rho_i[dn];
-            re[h][i] = sine ? ui - di : ur + dr;   // Q_i | P_r
-            im[h][i] = sine ? dr - ur : ui + di;   // -Q_r | P_i
+            for (int i = 0; i < kChunk; ++i) {
+                const int K = 32 * s + 8 * quarter_k + i;
+                const bool sine = K >= 2 * kFwdPairs;
+                int64_t up, dn;
+                fwp_voxels<decltype(line_c)::value, decltype(sides_c)::value>(unit, row, K, &up, &dn);
+                const float ur = rho_r[up], ui = rho_i[up], dr = rho_r[dn], di = rho_i[dn];
+                re[h][i] = sine ? ui - di : ur + dr;   // Q_i | P_r
+                im[h][i] = sine ? dr - ur : ui + di;   // -Q_r | P_i
+            }
         }
-    }
+    };
+    if (pairs)   // uniform
+        gather_rows(std::integral_constant<int, kLongLineVox>(), std::integral_constant<int, 2>());
+    else
+        gather_rows(std::integral_constant<int, kLineVox>(), std::integral_constant<int, 4>());
     int sh = 0;
     if constexpr (F16) {
         // the tile's largest magnitude: the lane's values, the wave, the
@@ -856,32 +860,39 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(2))) 
     // B operands, held for the whole walk: K = 32 s + 8 (l / 16) + i, cos
     // (K < 128) or sin of 2 pi (kx (j + 1/2) dx + sigma_1 k . d / 2 +
     // sigma_2 k . e / 2) for side (K % 128) / (LINE / 2), j = K % (LINE / 2)
-    const bool pairs = r0.x == kFwpPairs128;   // uniform
-    const int half = pairs ? kFwdPairs : kLineVox / 2;
     const float hex = __int_as_float(r0.z), hey = __int_as_float(r0.w), hez = __int_as_float(r1.w);
     u32x4 bh[kFwdColumns][kFwpKSteps], bl[kFwdColumns][kFwpKSteps];
+    auto form_b = [&](auto half_c) __attribute__((always_inline)) {
+        constexpr int kHalf = decltype(half_c)::value;
+        constexpr bool kPairs = kHalf == kFwdPairs;
 #pragma unroll
-    for (int t = 0; t < kFwdColumns; ++t) {
-        const float hd = 0.5f * __builtin_fmaf(skx[t], ddx, __builtin_fmaf(sky[t], ddy, skz[t] * ddz));
-        const float he = pairs ? 0.0f : 0.5f * __builtin_fmaf(skx[t], hex, __builtin_fmaf(sky[t], hey, skz[t] * hez));
+        for (int t = 0; t < kFwdColumns; ++t) {
+            const float hd = 0.5f * __builtin_fmaf(skx[t], ddx, __builtin_fmaf(sky[t], ddy, skz[t] * ddz));
+            const float he =
+                kPairs ? 0.0f : 0.5f * __builtin_fmaf(skx[t], hex, __builtin_fmaf(sky[t], hey, skz[t] * hez));
 #pragma unroll
-        for (int s = 0; s < kFwpKSteps; ++s) {
-            float v[kChunk];
+            for (int s = 0; s < kFwpKSteps; ++s) {
+                float v[kChunk];
 #pragma unroll
-            for (int i = 0; i < kChunk; ++i) {
-                const int K = 32 * s + 8 * quarter_k + i, kk = K % (2 * kFwdPairs);
-                const int side = kk / half, j = kk % half;
-                const float s1 = (side & 1) ? -1.0f : 1.0f, s2 = (side & 2) ? -1.0f : 1.0f;
-                const float off = pairs ? s1 * hd : __builtin_fmaf(s2, he, s1 * hd);
-                const float a = __builtin_fmaf(skx[t], (float)(2 * j + 1) * hdx, off);
-                v[i] = K < 2 * kFwdPairs ? __builtin_amdgcn_cosf(a) : __builtin_amdgcn_sinf(a);
+                for (int i = 0; i < kChunk; ++i) {
+                    const int K = 32 * s + 8 * quarter_k + i, kk = K % (2 * kFwdPairs);
+                    const int side = kk / kHalf, j = kk % kHalf;
+                    const float s1 = (side & 1) ? -1.0f : 1.0f, s2 = (side & 2) ? -1.0f : 1.0f;
+                    const float off = kPairs ? s1 * hd : __builtin_fmaf(s2, he, s1 * hd);
+                    const float a = __builtin_fmaf(skx[t], (float)(2 * j + 1) * hdx, off);
+                    v[i] = K < 2 * kFwdPairs ? __builtin_amdgcn_cosf(a) : __builtin_amdgcn_sinf(a);
+                }
+                unsigned h[4], l[4];
+                split_parts<F16, kChunk>(v, h, l);
+                bh[t][s] = (u32x4){h[0], h[1], h[2], h[3]};
+                bl[t][s] = (u32x4){l[0], l[1], l[2], l[3]};
             }
-            unsigned h[4], l[4];
-            split_parts<F16, kChunk>(v, h, l);
-            bh[t][s] = (u32x4){h[0], h[1], h[2], h[3]};
-            bl[t][s] = (u32x4){l[0], l[1], l[2], l[3]};
         }
-    }
+    };
+    if (r0.x == kFwpPairs128)   // uniform
+        form_b(std::integral_constant<int, kFwdPairs>());
+    else
+        form_b(std::integral_constant<int, kLineVox / 2>());
 
     float dr[kFwdColumns], di[kFwdColumns];
 #pragma unroll
