@@ -172,3 +172,43 @@ def test_64_voxel_line_groups_split_sums_repeatable(dev):
     ref = oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"],
                      case["x"][idx], case["y"][idx], case["z"][idx])
     assert metrics.rel_l2(a[0][idx], a[1][idx], *ref) <= TOL
+
+
+def test_mixed_quad_kinds_in_one_call(dev):
+    """A quad of 128-voxel line pairs followed by a quad of four-line
+    groups of 64-voxel lines: in the table form the table serves quad 0's
+    kind, so the groups fall to the 64-voxel line instance (pair 0, a long
+    pair, opens no 64-voxel pair table); fhd_compute_noalloc forms both
+    kinds in the one line-pair launch, each with its own split count. Both
+    match the oracle, and so does F (pair 0's kind fails for the second
+    quad: the vector form)."""
+    a = grid_case((128, 32, 4), 10, 980)
+    b = grid_case((64, 64, 4), 10, 981)
+    rng = np.random.default_rng(982)
+    M = 2500
+    k = {n: rng.uniform(-16, 16, M).astype(np.float32) for n in ("kx", "ky", "kz")}
+    D = {n: rng.standard_normal(M).astype(np.float32) for n in ("Dr", "Di")}
+    case = dict(k, **D, **{n: np.concatenate((a[n], b[n])) for n in ("x", "y", "z")})
+    x, y, z = case["x"], case["y"], case["z"]
+    cls = layout.gather_unit_classes(x, y, z)[0]
+    assert cls.tolist() == [3, 3, 3, 3, 2, 2, 2, 2]
+    assert layout.line_pair_quads(x, y, z, cls).tolist() == [True, False]
+    assert layout.line_group64_quads(x, y, z, cls).tolist() == [False, False]
+    assert layout.line_group64_quads(x, y, z, cls, formed=True).tolist() == [False, True]
+    assert layout.line_pair64_pairs(x, y, z, cls).tolist() == [False] * 4
+    ref = oracle.fhd(case["kx"], case["ky"], case["kz"], case["Dr"], case["Di"], x, y, z)
+    got = run(case, dev)
+    na = run(case, dev, noalloc=True)
+    e, e_na = metrics.rel_l2(*got, *ref), metrics.rel_l2(*na, *ref)
+    print("mixed quad kinds: rel-L2 default %.3g, noalloc %.3g" % (e, e_na), flush=True)
+    assert e <= TOL and e_na <= TOL
+    img = inputs.random_image(x.size, seed=983)
+    assert not layout.forward_pairs_form(x, y, z) and not layout.forward_lines_form(x, y, z)
+    t = [torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+         for v in (case["kx"], case["ky"], case["kz"], x, y, z, img[0], img[1])]
+    Dr, Di = binding.fhd_forward(*t)
+    torch.cuda.synchronize(dev)
+    fr = oracle.forward(case["kx"], case["ky"], case["kz"], img[0], img[1], x, y, z)
+    ef = metrics.rel_l2(Dr.cpu().numpy(), Di.cpu().numpy(), *fr)
+    print("mixed quad kinds, F: rel-L2 %.3g" % ef, flush=True)
+    assert ef <= TOL
