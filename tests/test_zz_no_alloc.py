@@ -51,10 +51,13 @@ def noalloc(lib, t, paths, dev):
 def test_noalloc_matches_compute_on_calls_of_shrinking_size(lib, paths):
     """128^3 x 100,000 (about 70 MiB of workspace on the line forms, whose
     line-pair workgroups form their B operands themselves here; 86 MB on
-    the vector paths), then smaller calls on the same scratch."""
+    the vector paths), then smaller calls on the same scratch: 64^3 x
+    65,536 (four-line groups of 64-voxel lines, formed here too), 32^3 and
+    a ragged case."""
     dev = torch.device("cuda:0")
     first = "spiral128"
     cases = [(first, inputs.make_workload(first)),
+             ("radial64", inputs.make_workload("radial64")),
              ("spiral32", inputs.make_workload("spiral32")),
              ("ragged 5000 x 123", inputs.random_case(5000, 123, seed=931))]
     for name, c in cases:
