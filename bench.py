@@ -129,7 +129,7 @@ CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 _GATHER_SRC = ["fhd.hip", "fhd_internal.h"]
 _GATHER_SHA = "cba32e94859672a2f0d1e19f25045710c65063d17b4930119218f8b2e90852eb"
 _FORWARD_SRC = ["fhd_forward.hip", "fhd_internal.h"]
-_FORWARD_SHA = "8c440b35b20c688261902ca9077eae637251504a0f197779fa1aaf9fd35bfd1f"
+_FORWARD_SHA = "d7592fbbc091a58520ffcc51161a1b2de87c2cb4b3a6fa2117cf8c2e5bc8ce34"
 TRAFFIC = {
     ("fhd_gather_patch_kernel<true, true>", "spiral128"): {
         "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
@@ -142,10 +142,10 @@ TRAFFIC = {
         "bytes_per_launch": (35071.8 * 2.0 + 69286.5 * 1.0) * 1024},
     ("fhd_forward_pairs_kernel<true>", "spiral128"): {
         "sources": _FORWARD_SRC, "sha256": _FORWARD_SHA,
-        "bytes_per_launch": (74359.9 * 2.0 + 5468.8 * 1.0) * 1024},
+        "bytes_per_launch": (74787.1 * 2.0 + 5468.8 * 1.0) * 1024},
     ("fhd_forward_pairs_kernel<true>", "radial64"): {
         "sources": _FORWARD_SRC, "sha256": _FORWARD_SHA,
-        "bytes_per_launch": (8707.0 * 2.0 + 512.0 * 1.0) * 1024},
+        "bytes_per_launch": (8734.5 * 2.0 + 512.0 * 1.0) * 1024},
 }
 
 

@@ -905,8 +905,50 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(2))) 
     const float4 *src = reinterpret_cast<const float4 *>(tiles);
     const int64_t total_vec4 = (int64_t)ntiles * kFwpTileVec4;
     if (t0 < t1) issue_stage_load<kFwdBlock, kFwpTileVec4>(src, total_vec4, t0, reinterpret_cast<float4 *>(stage[0]));
-    int b = 0;
-    for (int tau = t0; tau < t1; ++tau) {
+
+    // V = exp(i 2 pi k . c) of a tile's rows 4 (l / 16) + r and the lane's
+    // columns, and the tile's scale 2^-sh
+    struct Phasors {
+        float c[4][kFwdColumns], s[4][kFwdColumns];
+        float scale;
+    };
+    auto phasors = [&](const u32x4 *st, Phasors &v) __attribute__((always_inline)) {
+        int sh = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const u32x4 c = st[kFwpOpsVec4 + 4 * quarter_k + r];
+            const float cx = __uint_as_float(c.x), cy = __uint_as_float(c.y), cz = __uint_as_float(c.z);
+            sh = (int)c.w;
+#pragma unroll
+            for (int t = 0; t < kFwdColumns; ++t) {
+                const float p = __builtin_fmaf(skx[t], cx, __builtin_fmaf(sky[t], cy, skz[t] * cz));
+                v.c[r][t] = __builtin_amdgcn_cosf(p);
+                v.s[r][t] = __builtin_amdgcn_sinf(p);
+            }
+        }
+        v.scale = unscale<F16>(1.0f, sh);
+    };
+    // D += 2^-sh conj(V) T over the lane's four rows
+    float4v tre[kFwdColumns], tim[kFwdColumns];
+    auto accumulate = [&](const Phasors &v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < kFwdColumns; ++t) {
+            float tdr = 0.0f, tdi = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                tdr = __builtin_fmaf(v.c[r][t], tre[t][r], __builtin_fmaf(v.s[r][t], tim[t][r], tdr));
+                tdi = __builtin_fmaf(v.c[r][t], tim[t][r], __builtin_fmaf(-v.s[r][t], tre[t][r], tdi));
+            }
+            dr[t] = __builtin_fmaf(tdr, v.scale, dr[t]);
+            di[t] = __builtin_fmaf(tdi, v.scale, di[t]);
+        }
+    };
+
+    // Tile tau (in stage[b]): its phasors go to `cur` first, while the
+    // previous tile's products (tre / tim) drain; those are then folded
+    // into D with the previous tile's phasors `prev`, and tile tau's
+    // products start. So the phasor work never waits on the matrix cores.
+    auto tile = [&](int tau, int b, Phasors &cur, const Phasors &prev) __attribute__((always_inline)) {
         // tile tau is in stage[b] once every wave's copies have landed; the
         // other buffer was last read before this barrier
         __builtin_amdgcn_s_waitcnt(0);
@@ -914,7 +956,14 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(2))) 
         if (tau + 1 < t1)
             issue_stage_load<kFwdBlock, kFwpTileVec4>(src, total_vec4, tau + 1,
                                                       reinterpret_cast<float4 *>(stage[b ^ 1]));
-        float4v tre[kFwdColumns], tim[kFwdColumns];
+        phasors(stage[b], cur);
+        // formed here, not sunk towards their use a tile later
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int t = 0; t < kFwdColumns; ++t) asm volatile("" : "+v"(cur.c[r][t]), "+v"(cur.s[r][t]));
+        __builtin_amdgcn_sched_barrier(0);   // keep the phasors ahead of the fold
+        accumulate(prev);
 #pragma unroll
         for (int t = 0; t < kFwdColumns; ++t)
 #pragma unroll
@@ -938,35 +987,30 @@ __global__ __launch_bounds__(kFwdBlock) __attribute__((amdgpu_waves_per_eu(2))) 
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        // D += 2^-sh conj(V) T over rows 4 (l / 16) + r (line pairs), V of
-        // each pair's centre
-        float tdr[kFwdColumns], tdi[kFwdColumns];
+    };
+
+    // the fold before the first tile adds zeros
+    Phasors va, vb;
 #pragma unroll
-        for (int t = 0; t < kFwdColumns; ++t) {
-            tdr[t] = 0.0f;
-            tdi[t] = 0.0f;
-        }
-        int sh = 0;
+    for (int t = 0; t < kFwdColumns; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const u32x4 c = stage[b][kFwpOpsVec4 + 4 * quarter_k + r];
-            const float cx = __uint_as_float(c.x), cy = __uint_as_float(c.y), cz = __uint_as_float(c.z);
-            sh = (int)c.w;
-#pragma unroll
-            for (int t = 0; t < kFwdColumns; ++t) {
-                const float p = __builtin_fmaf(skx[t], cx, __builtin_fmaf(sky[t], cy, skz[t] * cz));
-                const float vc = __builtin_amdgcn_cosf(p), vs = __builtin_amdgcn_sinf(p);
-                tdr[t] = __builtin_fmaf(vc, tre[t][r], __builtin_fmaf(vs, tim[t][r], tdr[t]));
-                tdi[t] = __builtin_fmaf(vc, tim[t][r], __builtin_fmaf(-vs, tre[t][r], tdi[t]));
-            }
+            tre[t][r] = 0.0f;
+            tim[t][r] = 0.0f;
+            vb.c[r][t] = 0.0f;
+            vb.s[r][t] = 0.0f;
         }
-        const float scale = unscale<F16>(1.0f, sh);
-#pragma unroll
-        for (int t = 0; t < kFwdColumns; ++t) {
-            dr[t] = __builtin_fmaf(tdr[t], scale, dr[t]);
-            di[t] = __builtin_fmaf(tdi[t], scale, di[t]);
-        }
-        b ^= 1;
+    vb.scale = 0.0f;
+    int tau = t0;
+    for (; tau + 1 < t1; tau += 2) {
+        tile(tau, 0, va, vb);
+        tile(tau + 1, 1, vb, va);
+    }
+    if (tau < t1) {
+        tile(tau, 0, va, vb);
+        accumulate(va);
+    } else if (t0 < t1) {
+        accumulate(vb);
     }
 
     // each column's four row groups (lanes col + 16 q) add up
