@@ -44,7 +44,8 @@ def gpu_forward(case, img, dev):
 
 
 @pytest.mark.parametrize("name,samples", [("random16", None), ("spiral32", None),
-                                          ("radial64", 1024), ("spiral128", 384)])
+                                          ("radial64", 1024), ("spiral128", 384),
+                                          ("vdrandom256", 32)])
 def test_forward_workloads(dev, name, samples):
     w = inputs.make_workload(name)
     img = inputs.random_image(w["N"], seed=inputs.WORKLOADS[name].seed + 7)
