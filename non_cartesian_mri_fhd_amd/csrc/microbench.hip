@@ -21,7 +21,13 @@
 // independent neighbours. The forms separate what decides the FP32 issue
 // rate on gfx950: operand source (VGPR, inline constant, literal, SGPR),
 // encoding (VOP2, VOP3), v_fract_f32, the transcendental unit, and the
-// gather kernel's own mix of 2 transcendentals and 5 FMAs.
+// gather kernel's own mix of 2 transcendentals and 5 FMAs. One more form
+// reads the LDS (ds_read_b128, conflict-free, eight reads in flight per
+// wave) to give the LDS read bandwidth per CU that the matrix-core kernels'
+// operand reads share; four more time v_mfma_f32_16x16x32_f16 alone and
+// each followed by independent work (4 FMAs; a v_sin_f32 and an FMA; one
+// ds_read_b128), at one and at two waves per SIMD, to show what a wave's
+// other instructions cost its matrix products.
 //
 // The kernels also read the shader clock counter (clock64) and the constant
 // wall clock (wall_clock64) at the start and end of each workgroup, so the
@@ -35,6 +41,8 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kStreams = 8;
+typedef unsigned mb_u32x4 __attribute__((ext_vector_type(4)));
+typedef float mb_f32x4 __attribute__((ext_vector_type(4)));
 
 template <int A, int B>
 __global__ __launch_bounds__(kBlock) void mix_kernel(float *__restrict__ out,
@@ -119,6 +127,9 @@ __global__ __launch_bounds__(kBlock) void form_kernel(float *__restrict__ out,
           a6 = a0 + 6, a7 = a0 + 7;
     float t0 = 0, t1 = 0, t2 = 0, t3 = 0, t4 = 0, t5 = 0, t6 = 0, t7 = 0;
     const float x = threadIdx.x * 0.001f, y = x + 0.5f;
+    // matrix-core forms: eight independent 16x16x32 fp16 accumulators
+    mb_f32x4 m0 = {0, 0, 0, 0}, m1 = m0, m2 = m0, m3 = m0, m4 = m0, m5 = m0, m6 = m0, m7 = m0;
+    const mb_u32x4 ma = {threadIdx.x, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u}, mb = {0x3c003c00u, 1u, 2u, 3u};
     const long long c0 = clock64(), w0 = wall_clock64();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
@@ -171,6 +182,77 @@ __global__ __launch_bounds__(kBlock) void form_kernel(float *__restrict__ out,
 #define FHDMB_I(i) asm volatile("v_mov_b32_dpp %0, %1 row_newbcast:5 row_mask:0xf bank_mask:0xf" : "=v"(t##i) : "v"(a##i));
                 FHDMB_R8(FHDMB_I)
 #undef FHDMB_I
+            } else if constexpr (F == 12) {   // ds_read_b128, 1 KB per wave and read, no bank conflicts
+                // 16 KB per workgroup: its 256 lanes' 16 B at 4 offsets
+                __shared__ uint4 lds[4 * kBlock];
+                if (it == 0 && r == 0) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) lds[k * kBlock + threadIdx.x] = make_uint4(threadIdx.x, k, 1, 2);
+                    __syncthreads();
+                }
+                // the LDS offset of this lane's 16 B (the low half of its flat address)
+                const unsigned addr = (unsigned)reinterpret_cast<uintptr_t>(&lds[threadIdx.x]);
+                mb_u32x4 q0, q1, q2, q3, q4, q5, q6, q7;
+                asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(q0) : "v"(addr) : "memory");
+                asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(q1) : "v"(addr) : "memory");
+                asm volatile("ds_read_b128 %0, %1 offset:8192" : "=v"(q2) : "v"(addr) : "memory");
+                asm volatile("ds_read_b128 %0, %1 offset:12288" : "=v"(q3) : "v"(addr) : "memory");
+                asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(q4) : "v"(addr) : "memory");
+                asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(q5) : "v"(addr) : "memory");
+                asm volatile("ds_read_b128 %0, %1 offset:8192" : "=v"(q6) : "v"(addr) : "memory");
+                asm volatile("ds_read_b128 %0, %1 offset:12288" : "=v"(q7) : "v"(addr) : "memory");
+                // the waits tie the loaded registers, so nothing reads them before
+                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3)::"memory");
+                asm volatile("" : "+v"(q4), "+v"(q5), "+v"(q6), "+v"(q7));
+                t0 = __uint_as_float(__float_as_uint(t0) ^ q0.x);
+                t1 = __uint_as_float(__float_as_uint(t1) ^ q1.y);
+                t2 = __uint_as_float(__float_as_uint(t2) ^ q2.z);
+                t3 = __uint_as_float(__float_as_uint(t3) ^ q3.w);
+                t4 = __uint_as_float(__float_as_uint(t4) ^ q4.x);
+                t5 = __uint_as_float(__float_as_uint(t5) ^ q5.y);
+                t6 = __uint_as_float(__float_as_uint(t6) ^ q6.z);
+                t7 = __uint_as_float(__float_as_uint(t7) ^ q7.w);
+            } else if constexpr (F == 13) {   // v_mfma_f32_16x16x32_f16 alone
+#define FHDMB_I(i) asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(m##i) : "v"(ma), "v"(mb));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 14) {   // each MFMA followed by 4 independent VGPR FMAs
+#define FHDMB_I(i)                                                                            \
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(m##i) : "v"(ma), "v"(mb));   \
+    asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a0) : "v"(y), "v"(x));                     \
+    asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a1) : "v"(y), "v"(x));                     \
+    asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a2) : "v"(y), "v"(x));                     \
+    asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a3) : "v"(y), "v"(x));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 15) {   // each MFMA followed by a v_sin_f32 and an FMA
+#define FHDMB_I(i)                                                                            \
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(m##i) : "v"(ma), "v"(mb));   \
+    asm volatile("v_sin_f32_e32 %0, %1" : "+v"(t##i) : "v"(a##i));                             \
+    asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a##i) : "v"(y), "v"(x));
+                FHDMB_R8(FHDMB_I)
+#undef FHDMB_I
+            } else if constexpr (F == 16) {   // each MFMA followed by one ds_read_b128
+                __shared__ uint4 lds2[4 * kBlock];
+                if (it == 0 && r == 0) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) lds2[k * kBlock + threadIdx.x] = make_uint4(threadIdx.x, k, 1, 2);
+                    __syncthreads();
+                }
+                // the LDS offset of this lane's 16 B (the low half of its flat address)
+                const unsigned addr = (unsigned)reinterpret_cast<uintptr_t>(&lds2[threadIdx.x]);
+                mb_u32x4 q0, q1, q2, q3, q4, q5, q6, q7;
+#define FHDMB_I(i, off)                                                                       \
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(m##i) : "v"(ma), "v"(mb));   \
+    asm volatile("ds_read_b128 %0, %1 offset:" #off : "=v"(q##i) : "v"(addr) : "memory");
+                FHDMB_I(0, 0) FHDMB_I(1, 4096) FHDMB_I(2, 8192) FHDMB_I(3, 12288)
+                FHDMB_I(4, 0) FHDMB_I(5, 4096) FHDMB_I(6, 8192) FHDMB_I(7, 12288)
+#undef FHDMB_I
+                // the wait ties the loaded registers, so nothing reads them before;
+                // one of them is used (one vector instruction per 8 MFMAs)
+                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3)::"memory");
+                asm volatile("" : "+v"(q4), "+v"(q5), "+v"(q6), "+v"(q7));
+                t0 = __uint_as_float(__float_as_uint(t0) ^ q0.x);
             } else if constexpr (F == 9) {   // gather mix with SGPR operands
                 asm volatile("v_sin_f32_e32 %0, %1" : "+v"(t0) : "v"(x));
                 asm volatile("v_cos_f32_e32 %0, %1" : "+v"(t1) : "v"(x));
@@ -183,8 +265,9 @@ __global__ __launch_bounds__(kBlock) void form_kernel(float *__restrict__ out,
         }
     }
     const long long c1 = clock64(), w1 = wall_clock64();
+    const mb_f32x4 m = m0 + m1 + m2 + m3 + m4 + m5 + m6 + m7;
     out[(size_t)blockIdx.x * kBlock + threadIdx.x] =
-        a0 + a1 + a2 + a3 + a4 + a5 + a6 + a7 + t0 + t1 + t2 + t3 + t4 + t5 + t6 + t7;
+        a0 + a1 + a2 + a3 + a4 + a5 + a6 + a7 + t0 + t1 + t2 + t3 + t4 + t5 + t6 + t7 + m[0] + m[1] + m[2] + m[3];
     if (threadIdx.x == 0) {
         clocks[4 * blockIdx.x + 0] = c0;
         clocks[4 * blockIdx.x + 1] = c1;
@@ -207,6 +290,9 @@ const FormEntry kForms[] = {
     {"fract", 8, form_kernel<6>}, {"sin", 8, form_kernel<7>},
     {"mix_2trans_5fma_vgpr", 7, form_kernel<8>}, {"mix_2trans_5fma_sgpr", 7, form_kernel<9>},
     {"fmac_vop2_dpp_row_bcast", 8, form_kernel<10>}, {"mov_dpp_row_bcast", 8, form_kernel<11>},
+    {"lds_read_b128", 8, form_kernel<12>},
+    {"mfma_f16_16x16x32", 8, form_kernel<13>}, {"mfma_f16_plus_4fma", 8, form_kernel<14>},
+    {"mfma_f16_plus_sin_fma", 8, form_kernel<15>}, {"mfma_f16_plus_lds_read_b128", 8, form_kernel<16>},
 };
 
 }  // namespace

@@ -9,7 +9,13 @@ JSON line per measurement:
 * ``form`` lines: one exact VALU instruction form (inline assembly, eight
   independent chains), as SIMD cycles per wave64 instruction, both at the
   clock the kernel measured and at the 2.4 GHz peak clock;
-* a ``summary`` line: fma_cycles (VGPR FMA), sgpr_fma_cycles, trans_cycles.
+* the ``lds_read_b128`` form also as LDS bytes per clock and CU (conflict-
+  free 16-byte reads, eight in flight per wave);
+* ``mfma_form`` lines: v_mfma_f32_16x16x32_f16 alone and each followed by
+  independent vector instructions or an LDS read, at one and two waves per
+  SIMD, as SIMD cycles per MFMA;
+* a ``summary`` line: fma_cycles (VGPR FMA), sgpr_fma_cycles, trans_cycles,
+  lds_bytes_per_clk_per_cu.
 
 Cycle counts are per SIMD: elapsed time x clock x SIMDs / wave64
 instructions. Each launch keeps every SIMD at 8 resident waves.
@@ -79,11 +85,34 @@ def run_forms(lib, cus: int, iters: int, waves_per_simd: int = 8) -> list[dict]:
     for i in range(lib.fhdmb_form_count()):
         ms, mhz, chk = _time(lib.fhdmb_form, i, blocks, iters)
         per_simd = waves_per_simd * iters * 4 * lib.fhdmb_form_instrs(i)
-        rows.append(dict(kind="form", form=lib.fhdmb_form_name(i).decode(), ms=ms,
-                         sclk_mhz=mhz,
-                         cycles_per_instr=ms * 1e-3 * mhz * 1e6 / per_simd,
-                         cycles_per_instr_at_peak_clock=ms * 1e-3 * PEAK_CLOCK_HZ / per_simd,
-                         checksum=chk))
+        row = dict(kind="form", form=lib.fhdmb_form_name(i).decode(), ms=ms, sclk_mhz=mhz,
+                   cycles_per_instr=ms * 1e-3 * mhz * 1e6 / per_simd,
+                   cycles_per_instr_at_peak_clock=ms * 1e-3 * PEAK_CLOCK_HZ / per_simd,
+                   checksum=chk)
+        if row["form"] == "lds_read_b128":
+            # 1 KB per wave64 read, four SIMDs per CU
+            per_cu = 4 * per_simd * 1024.0
+            row["lds_bytes_per_clk_per_cu"] = per_cu / (ms * 1e-3 * mhz * 1e6)
+        rows.append(row)
+    return rows
+
+
+MFMA_FORMS = ("mfma_f16_16x16x32", "mfma_f16_plus_4fma", "mfma_f16_plus_sin_fma",
+              "mfma_f16_plus_lds_read_b128")
+
+
+def run_mfma_forms(lib, cus: int, iters: int) -> list[dict]:
+    """The matrix-core forms at one and two waves per SIMD: cycles per
+    MFMA (with its vector instructions) per SIMD."""
+    names = [lib.fhdmb_form_name(i).decode() for i in range(lib.fhdmb_form_count())]
+    rows = []
+    for waves in (1, 2):
+        for name in MFMA_FORMS:
+            i = names.index(name)
+            ms, mhz, chk = _time(lib.fhdmb_form, i, cus * waves, iters)
+            per_simd = waves * iters * 4 * lib.fhdmb_form_instrs(i)
+            rows.append(dict(kind="mfma_form", form=name, waves_per_simd=waves, ms=ms, sclk_mhz=mhz,
+                             cycles_per_mfma=ms * 1e-3 * mhz * 1e6 / per_simd, checksum=chk))
     return rows
 
 
@@ -98,6 +127,7 @@ def main(argv=None) -> int:
     lib = load()
     rows = [] if args.forms_only else run_mixes(lib, cus, args.mix_iters)
     rows += run_forms(lib, cus, args.iters)
+    rows += run_mfma_forms(lib, cus, args.iters)
     for r in rows:
         print(json.dumps(r), flush=True)
     forms = {r["form"]: r for r in rows if r["kind"] == "form"}
@@ -107,6 +137,7 @@ def main(argv=None) -> int:
         sgpr_fma_cycles=forms["fmac_vop2_sgpr"]["cycles_per_instr"],
         trans_cycles=forms["sin"]["cycles_per_instr"],
         fract_cycles=forms["fract"]["cycles_per_instr"],
+        lds_bytes_per_clk_per_cu=forms["lds_read_b128"]["lds_bytes_per_clk_per_cu"],
     )
     print(json.dumps({"summary": summary}), flush=True)
     return 0
