@@ -375,7 +375,7 @@ def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the F^H D path shards over voxels "
-              "with no exchange, and this build measures one GPU's share only "
+              "with no exchange, and this benchmark measures one GPU's share only "
               "(got --gpus %d)" % args.gpus, file=sys.stderr)
         return 2
     if args.op != "fhd":
