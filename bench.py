@@ -265,8 +265,11 @@ def roofline_for(kernel: str, terms: float, kernel_ms: float, traffic, fractions
 def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 20, or 3 for the multi-call cg, cg_grid and "
+                         "scatter steps): after an idle spell the shader clock settles over about ten "
+                         "calls of the 128^3 operators")
     ap.add_argument("--workload", default="spiral128")
     ap.add_argument("--op", default="fhd", choices=["fhd", "forward", "normal", "cg", "grid", "grid_bf16x3",
                                                        "forward_grid", "normal_grid", "cg_grid", "scatter"])
@@ -275,7 +278,10 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
-    return ap.parse_args(argv)
+    args = ap.parse_args(argv)
+    if args.warmup is None:
+        args.warmup = 3 if args.op in ("cg", "cg_grid", "scatter") else 20
+    return args
 
 
 def cpu_model() -> str:
@@ -407,14 +413,18 @@ def main(argv=None) -> int:
     def gather(p):
         binding.fhd_gather(packed, M, t["x"], t["y"], t["z"], *rho[p], paths=PATHS[p])
 
+    # the host's mirror of the kernels' path tests (seconds of CPU work at
+    # 128^3) runs before the warm-up, so the GPU goes from the warm-up
+    # straight into the timed steps
+    cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
+    lp, lp64 = line_instance_masks(w, cls, args.paths)
+    kernel, kernel_share = adjoint_kernel(cls, counts, args.paths, lp, lp64)
+
     for _ in range(args.warmup):
         pack()
         gather(args.paths)
     torch.cuda.synchronize()
 
-    cls, _, counts = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=args.paths != "vector")
-    lp, lp64 = line_instance_masks(w, cls, args.paths)
-    kernel, kernel_share = adjoint_kernel(cls, counts, args.paths, lp, lp64)
     timer = binding.KernelTimer(kernel, args.steps, dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -478,11 +488,13 @@ def main(argv=None) -> int:
     for p in PATHS:
         if p == args.paths:
             continue
-        gather(p)
         c2, _, n2 = layout.gather_unit_classes(w["x"], w["y"], w["z"], allow_lines=p != "vector")
         lp2, lq2 = line_instance_masks(w, c2, p)
         k2, share2 = adjoint_kernel(c2, n2, p, lp2, lq2)
-        call_ms, kms = timed_calls(lambda: gather(p), 3, stream, k2, 1, dev)
+        for _ in range(args.warmup):
+            gather(p)
+        torch.cuda.synchronize()
+        call_ms, kms = timed_calls(lambda: gather(p), 5, stream, k2, 1, dev)
         fr2, _ = adjoint_ceiling(w, p != "vector")
         others[p] = {"dtype": path_dtype(p, fr2[0]), "fhd_gather_call": summary(call_ms),
                      "kernel_ms": {"kernel": k2, **summary(kms)},
