@@ -147,7 +147,7 @@ int device_cus()
     return cus_cached[device];
 }
 
-int split_count(int64_t blocks, int nchunks, int per_cu, int granule)
+int split_count(int64_t blocks, int nchunks, int per_cu, int granule, double slack)
 {
     const int cus = device_cus();
     if (cus <= 0) return 1;
@@ -159,8 +159,8 @@ int split_count(int64_t blocks, int nchunks, int per_cu, int granule)
     // Cutting the stream s ways makes every workgroup's work 1/s as long and
     // the launch ceil(s blocks / resident) rounds of them: time ~ rounds / s,
     // bounded below by blocks / resident. Take the fewest ways (at most one
-    // per granule, and at most 16 or two rounds' worth) that come within 3 %
-    // of the best.
+    // per granule, and at most 16 or two rounds' worth) that come within
+    // `slack` of the best.
     // s ways give every split ceil(stages / s) granules, so only
     // ceil(stages / that) of them have any: count those
     auto ways = [&](int64_t s) {
@@ -177,7 +177,7 @@ int split_count(int64_t blocks, int nchunks, int per_cu, int granule)
     double lowest = cost(1);
     for (int64_t s = 2; s <= most; ++s) lowest = cost(s) < lowest ? cost(s) : lowest;
     for (int64_t s = 1; s <= most; ++s)
-        if (cost(s) <= 1.03 * lowest) return (int)ways(s);
+        if (cost(s) <= slack * lowest) return (int)ways(s);
     return 1;
 }
 

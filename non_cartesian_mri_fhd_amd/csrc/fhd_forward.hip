@@ -1146,8 +1146,12 @@ int launch_forward(const float *x, const float *y, const float *z, const float *
         per_cu = per_cu_cache[dev];
     }
     // cut the tile stream so the sample blocks fill whole rounds (each part
-    // at least one line-pair tile, two line tiles)
-    const int splits = split_count(blocks, (int)(units * kStageChunks), per_cu);
+    // at least one line-pair tile, two line tiles), within 0.5 % of the
+    // cheapest count: a part's own cost (its workgroups form their B
+    // operands, one row of partial sums of D) is small against a walk of
+    // tens of tiles (at 128^3 x 100k: 13 parts rather than 7; 11 or 15
+    // parts ran 0.8 % faster than 7, interleaved on one machine)
+    const int splits = split_count(blocks, (int)(units * kStageChunks), per_cu, kStageChunks, 1.005);
     // one workspace: unit classes and the flag words | line-pair records |
     // tiles (either form's) | partials
     const size_t cls_bytes = ((size_t)units * sizeof(int) + kInfoWords * sizeof(int) + 255) / 256 * 256;

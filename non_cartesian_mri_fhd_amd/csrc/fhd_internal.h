@@ -425,8 +425,10 @@ struct TimedLaunch {
 // whose output needs `blocks` workgroups of which `per_cu` fit on a CU at
 // once: below one round, enough parts to fill it (at least `granule`
 // chunks per part); above, a few parts where that evens out a partly
-// filled last round.
-int split_count(int64_t blocks, int nchunks, int per_cu = 4, int granule = kStageChunks);
+// filled last round. `slack`: the fewest parts whose priced time is within
+// this factor of the cheapest are taken (a part costs its workgroups'
+// set-up and one more row of partial sums).
+int split_count(int64_t blocks, int nchunks, int per_cu = 4, int granule = kStageChunks, double slack = 1.03);
 // Compute units of the current device (cached per device); 0 on error.
 int device_cus();
 
