@@ -127,22 +127,22 @@ PATH_DTYPE = {
 # until the counters are taken again.
 CSRC = os.path.join(ROOT, "non_cartesian_mri_fhd_amd", "csrc")
 _GATHER_SRC = ["fhd.hip", "fhd_internal.h"]
-_GATHER_SHA = "cba32e94859672a2f0d1e19f25045710c65063d17b4930119218f8b2e90852eb"
+_GATHER_SHA = "6292fa24e0e3bd5b1a8145097191074396175d6a7e2047eef0ccc084b8aa300c"
 _FORWARD_SRC = ["fhd_forward.hip", "fhd_internal.h"]
-_FORWARD_SHA = "d7592fbbc091a58520ffcc51161a1b2de87c2cb4b3a6fa2117cf8c2e5bc8ce34"
+_FORWARD_SHA = "e1130f81255b284b83e9650dfa21ccf7cec954127d270b614c092c7775cee3ed"
 TRAFFIC = {
     ("fhd_gather_patch_kernel<true, true>", "spiral128"): {
         "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
-        "bytes_per_launch": (108264.9 * 2.0 + 65678.8 * 1.0) * 1024},
+        "bytes_per_launch": (108288.0 * 2.0 + 65710.3 * 1.0) * 1024},
     ("fhd_gather_kernel<16, true>", "spiral128"): {
         "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
-        "bytes_per_launch": (52915.8 * 2.0 + 87040.0 * 1.0) * 1024},
+        "bytes_per_launch": (52924.4 * 2.0 + 87040.0 * 1.0) * 1024},
     ("fhd_gather_patch_kernel<true, true>", "radial64"): {
         "sources": _GATHER_SRC, "sha256": _GATHER_SHA,
-        "bytes_per_launch": (35071.8 * 2.0 + 69286.5 * 1.0) * 1024},
+        "bytes_per_launch": (35071.0 * 2.0 + 69234.4 * 1.0) * 1024},
     ("fhd_forward_pairs_kernel<true>", "spiral128"): {
         "sources": _FORWARD_SRC, "sha256": _FORWARD_SHA,
-        "bytes_per_launch": (74787.1 * 2.0 + 5468.8 * 1.0) * 1024},
+        "bytes_per_launch": (75520.6 * 2.0 + 10156.2 * 1.0) * 1024},
     ("fhd_forward_pairs_kernel<true>", "radial64"): {
         "sources": _FORWARD_SRC, "sha256": _FORWARD_SHA,
         "bytes_per_launch": (8734.5 * 2.0 + 512.0 * 1.0) * 1024},
